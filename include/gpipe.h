@@ -1,0 +1,191 @@
+/*
+ * gpipe.h - one GPipe pipeline cell's training step on an AMD Instinct MI355X.
+ *
+ * Source of the method: the GPipe technical review page (zzz0906.github.io,
+ * "GPipe：微批次流水线并行的大规模模型训练 — 深度技术评审"), section "GPipe algorithm in
+ * detail".  A model is a sequence of L layers; GPipe cuts it into K contiguous
+ * cells ("minimal interface design"), splits each mini-batch of N into M
+ * micro-batches, runs the forward pass keeping only the cells' boundary
+ * activations, re-computes each micro-batch's forward during the backward pass
+ * (re-materialization), sums the micro-batch gradients and applies them in one
+ * synchronous update ("pipeline execution flow", phases 1-3).
+ *
+ * This library runs one cell of L/K identical pre-LN Transformer layers
+ * (LayerNorm, multi-head attention, GeLU FFN) on one GPU.
+ *
+ * Conventions for every entry point
+ *  - Plain C types only.  Device pointers are HIP device addresses (for
+ *    example from torch tensors on a ROCm device); the library never allocates
+ *    or frees device memory and never keeps a pointer beyond what is stated.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Device work is only
+ *    enqueued on it; calls return without waiting, so buffers must stay alive
+ *    until the caller has synchronised the stream.
+ *  - Errors are return codes.  On any error no device work has been enqueued
+ *    and no output has been written, except GPIPE_ERR_DEVICE (a HIP launch
+ *    failed part-way; outputs are then undefined).
+ *  - Activations (x, target, y, dx) are row-major [N, S, D], token-major;
+ *    their element type is the cell's precision (float32, or bf16 stored as
+ *    uint16), and they must be 16-byte aligned.
+ */
+#ifndef GPIPE_H
+#define GPIPE_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gpipe_cell gpipe_cell; /* opaque; host-side metadata only */
+
+typedef enum {
+  GPIPE_OK = 0,
+  GPIPE_ERR_INVALID = 1,     /* an argument is out of range or misaligned      */
+  GPIPE_ERR_OOM = 2,         /* the plan does not fit the device's free memory */
+  GPIPE_ERR_DEVICE = 3,      /* a HIP call failed                              */
+  GPIPE_ERR_UNSUPPORTED = 4, /* a shape outside what the kernels implement     */
+  GPIPE_ERR_STATE = 5        /* e.g. step before bind                          */
+} gpipe_status;
+
+typedef enum {
+  GPIPE_FP32 = 0, /* everything in float32                                        */
+  GPIPE_BF16 = 1  /* bf16 activations and weight copy; fp32 accumulation, master
+                     weights, gradients, optimizer state and normalisation stats */
+} gpipe_precision;
+
+/* Per-layer tensors, in their order inside the flat parameter vector (layer
+ * major: all tensors of layer 0, then layer 1, ...).  Matrices are
+ * [out_features, in_features] row-major, y = x W^T + b.  w_qkv rows 0..D-1
+ * produce q, D..2D-1 k, 2D..3D-1 v; head h owns columns h*D/H .. (h+1)*D/H-1. */
+typedef enum {
+  GPIPE_LN1_G = 0, GPIPE_LN1_B, GPIPE_W_QKV, GPIPE_B_QKV, GPIPE_W_O, GPIPE_B_O,
+  GPIPE_LN2_G, GPIPE_LN2_B, GPIPE_W_1, GPIPE_B_1, GPIPE_W_2, GPIPE_B_2,
+  GPIPE_N_TENSORS
+} gpipe_tensor;
+
+/* Saved activations of one layer for one micro-batch of T = (N/M)*S tokens
+ * (what re-materialization rebuilds; "preliminaries 5").  Element type is the
+ * cell's precision except the LayerNorm statistics (float32 pairs mean, rstd). */
+typedef enum {
+  GPIPE_SAVED_X = 0, /* layer input [T, D] (layer 0: the caller's x)          */
+  GPIPE_SAVED_H1,    /* LN1 output [T, D]                                     */
+  GPIPE_SAVED_ST1,   /* LN1 (mean, rstd) [T, 2] float32                       */
+  GPIPE_SAVED_QKV,   /* [T, 3D]                                               */
+  GPIPE_SAVED_P,     /* softmax [N/M, H, S, ldS], ldS = S rounded up to 8     */
+  GPIPE_SAVED_CTX,   /* attention output before the projection [T, D]         */
+  GPIPE_SAVED_X1,    /* residual after attention [T, D]                        */
+  GPIPE_SAVED_H2,    /* LN2 output [T, D]                                     */
+  GPIPE_SAVED_ST2,   /* LN2 (mean, rstd) [T, 2] float32                       */
+  GPIPE_SAVED_U,     /* FFN pre-activation [T, F]                             */
+  GPIPE_SAVED_G,     /* GeLU(u) [T, F]                                        */
+  GPIPE_N_SAVED
+} gpipe_saved;
+
+/* Creates a cell of `layers` (= L/K) identical pre-LN Transformer layers:
+ * x1 = x + MHA(LN1(x)), y = x1 + W2 GeLU(W1 LN2(x1) + b1) + b2, attention
+ * scale 1/sqrt(d_model/heads), causal mask if `causal`, LayerNorm eps 1e-5,
+ * exact-erf GeLU.  Requirements: all sizes > 0; d_model, d_ff and
+ * d_model/heads multiples of 8; d_model <= 8192; seq <= 4096.
+ * Errors: GPIPE_ERR_INVALID for a non-positive size or heads not dividing
+ * d_model; GPIPE_ERR_UNSUPPORTED for the other requirements.  *out is set
+ * only on success; free it with gpipe_cell_destroy. */
+gpipe_status gpipe_cell_create(int layers, int d_model, int heads, int d_ff, int seq, int causal,
+                               gpipe_precision prec, gpipe_cell **out);
+
+gpipe_status gpipe_cell_destroy(gpipe_cell *cell); /* NULL is accepted */
+
+/* Number of parameters P of the cell (= layers * (4D^2 + 2DF + 9D + F)). */
+gpipe_status gpipe_cell_param_count(const gpipe_cell *cell, size_t *n_params);
+
+/* Element offset and element count of tensor `tensor` of layer `layer` in the
+ * flat parameter vector (and in the gradient and optimizer-state vectors,
+ * which share the layout). */
+gpipe_status gpipe_cell_param_offset(const gpipe_cell *cell, int layer, int tensor,
+                                     size_t *offset, size_t *count);
+
+/* Hands the cell its parameter state; the caller owns all four buffers and
+ * keeps them alive while the cell is used.  Each holds P elements:
+ *   master  float32 weights (read by fp32 cells, updated by gpipe_apply_update)
+ *   w_lowp  bf16 copy of master used by bf16 cells' GEMMs (NULL for fp32 cells;
+ *           required for bf16 cells; the caller initialises it, the update
+ *           rewrites it)
+ *   grad    float32 gradient accumulator (written by gpipe_cell_step)
+ *   ms      float32 RMSProp mean-square state, zero-initialised by the caller
+ * This is the "~12 bytes per parameter" optimizer footprint of the pages'
+ * preliminaries section 2 (fp32: 12 B; bf16 adds the 2 B copy).
+ * All four must be 16-byte aligned. */
+gpipe_status gpipe_cell_bind(gpipe_cell *cell, float *master, void *w_lowp, float *grad,
+                             float *ms);
+
+/* Writes w_lowp <- bf16(master) (round to nearest even) for a bf16 cell, so
+ * the copy the GEMMs read starts equal to the master weights; a no-op for
+ * fp32 cells.  Errors: GPIPE_ERR_STATE if not bound. */
+gpipe_status gpipe_cell_sync_lowp(gpipe_cell *cell, void *stream);
+
+/* Exact device workspace needed by gpipe_cell_step(N, M, remat): one
+ * micro-batch's saved activations of all layers when remat != 0 (the pages'
+ * O(N + L/K * N/M) activation bound: the boundary tensors are the caller's
+ * x / y), all M micro-batches' when remat == 0, plus one layer's backward
+ * transients and the reduction partials.  GPIPE_ERR_INVALID unless
+ * N > 0, M > 0 and N % M == 0. */
+gpipe_status gpipe_cell_workspace_bytes(const gpipe_cell *cell, int N, int M, int remat,
+                                        size_t *bytes);
+
+/* Byte offset inside the workspace of saved tensor `which` of layer `layer`
+ * for micro-batch `micro`, as laid out for gpipe_cell_step(N, M, remat).
+ * With remat != 0 only one micro-batch set exists (micro must be 0) and it
+ * holds the last re-materialized micro-batch when the step ends.  For
+ * GPIPE_SAVED_X of layer 0 (the caller's x) it returns GPIPE_ERR_INVALID.
+ * Meant for inspection and tests. */
+gpipe_status gpipe_cell_saved_offset(const gpipe_cell *cell, int N, int M, int remat, int micro,
+                                     int layer, int which, size_t *offset, size_t *bytes);
+
+/* One training step of the cell, phases 1 and 2 of "pipeline execution flow":
+ *  - split x [N, S, D] into M micro-batches of N/M sequences (views);
+ *  - forward phase: run every micro-batch through the cell, writing its
+ *    boundary output into y; with remat != 0 the layer intermediates are
+ *    dropped (overwritten by the next micro-batch);
+ *  - backward phase, micro-batches m = 0 .. M-1 in order: with remat != 0
+ *    rebuild the intermediates by re-running the forward (bitwise identical
+ *    to the forward phase), take the loss against target, backpropagate,
+ *    and accumulate the parameter gradients in float32: micro-batch 0 stores
+ *    into grad, the others add.
+ * Loss: loss = sum((y - target)^2) / (N*S*D), gradient 2(y - target)/(N*S*D)
+ * for every micro-batch, so the summed gradients are the full mini-batch's.
+ * Outputs: y [N,S,D]; dx [N,S,D] (gradient w.r.t. x; NULL to skip); *loss_dev
+ * (a float32 on the device); grad (the bound accumulator).  x, target, y and
+ * dx must not overlap the workspace.  The workspace (ws_bytes >=
+ * gpipe_cell_workspace_bytes) is owned by the caller; its contents on entry
+ * are ignored.  Errors: GPIPE_ERR_STATE if not bound; GPIPE_ERR_INVALID for
+ * bad N/M, misaligned pointers or too small a workspace. */
+gpipe_status gpipe_cell_step(gpipe_cell *cell, const void *x, const void *target, void *y,
+                             void *dx, int N, int M, int remat, void *workspace, size_t ws_bytes,
+                             void *stream, float *loss_dev);
+
+/* Phase 3, the single synchronous update: RMSProp over all P parameters,
+ *   ms <- decay*ms + (1-decay)*grad^2;  master <- master - lr*grad/(sqrt(ms)+eps)
+ * and, for bf16 cells, w_lowp <- bf16(master) (round to nearest even).
+ * grad is read, not cleared.  Errors: GPIPE_ERR_STATE if not bound;
+ * GPIPE_ERR_INVALID if decay is outside [0, 1) or lr/eps are negative or
+ * not finite. */
+gpipe_status gpipe_apply_update(gpipe_cell *cell, float lr, float decay, float eps, void *stream);
+
+/* The cell partition of "minimal interface design": split L layers with
+ * estimated costs costs[0..L-1] (finite, >= 0) into K contiguous non-empty
+ * cells minimising the variance of the cells' summed costs.  Writes
+ * bounds[0..K] (bounds[0] = 0, bounds[K] = L, cell k = layers
+ * bounds[k] .. bounds[k+1]-1) and the variance (1/K) sum_k (C_k - mean)^2.
+ * Exact minimum by dynamic programming over prefix sums, O(K L^2); among
+ * equal minima the lexicographically smallest bounds.  Host only.
+ * Errors: GPIPE_ERR_INVALID if L < 1, K < 1, K > L or a cost is negative or
+ * not finite. */
+gpipe_status gpipe_partition(const double *costs, int L, int K, int *bounds, double *variance);
+
+/* Static string naming a status code. */
+const char *gpipe_status_string(gpipe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPIPE_H */

@@ -1,0 +1,566 @@
+// C-ABI of the GPipe cell library: cell metadata, the activation-workspace
+// plan, the partition, and the step / update drivers that enqueue the kernels.
+//
+// Schedule (GPipe technical review page, "GPipe algorithm in detail / pipeline
+// execution flow"): forward phase over the M micro-batches keeping only the
+// boundary output, backward phase re-materializing each micro-batch's
+// intermediates and accumulating float32 gradients, then one update.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <limits>
+#include <new>
+#include <vector>
+
+#include "../../include/gpipe.h"
+#include "kernels.hpp"
+
+using namespace gp;
+
+struct gpipe_cell {
+  int L, D, H, F, S, causal;
+  gpipe_precision prec;
+  float ln_eps;
+  size_t n_params;
+  size_t per_layer;
+  size_t rel_off[GPIPE_N_TENSORS];  // offsets inside one layer
+  size_t count[GPIPE_N_TENSORS];
+  float* master;
+  void* w_lowp;
+  float* grad;
+  float* ms;
+  bool bound;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ----------------------------------------------------------------- workspace plan
+// Byte layout of the workspace for one (N, M, remat):
+//   sets:   remat ? 1 : M micro-batch sets; each set holds, for every layer,
+//           the saved tensors of gpipe_saved (layer 0 has no X slot)
+//   yre:    output of the re-materialized forward [T, D] (remat only)
+//   scores: float32 [B*H, S, ldS]  (forward scores, backward dP)
+//   ds:     act [B*H, S, ldS]
+//   r0, r1, dm: float32 [T, D]   (residual-stream gradients, LN input grads)
+//   a0, a1, dctx: act [T, D]
+//   du: act [T, F];  dqkv: act [T, 3D]
+//   colpart: float32 [colsum chunks, max(3D, F)]
+//   lnpart:  float32 [LN blocks, 2D]
+//   msepart: float32 [M, mse blocks]
+struct Plan {
+  int N, M, B, T, ldS;
+  size_t eb;
+  size_t saved_off[GPIPE_N_SAVED];  // inside one layer's slot
+  size_t saved_bytes[GPIPE_N_SAVED];
+  size_t layer_bytes, set_bytes;
+  int nsets;
+  size_t yre, scores, ds, r0, r1, dm, a0, a1, dctx, du, dqkv, colpart, lnpart, msepart;
+  int mse_nblk;
+  size_t total;
+};
+
+bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
+  if (N <= 0 || M <= 0 || N % M) return false;
+  p->N = N;
+  p->M = M;
+  p->B = N / M;
+  const size_t S = c->S, D = c->D, F = c->F, H = c->H;
+  const size_t B = p->B;
+  const size_t T = B * S;
+  if (T > size_t(std::numeric_limits<int>::max())) return false;
+  p->T = int(T);
+  p->ldS = int(align_up(S, 8));
+  const size_t eb = c->prec == GPIPE_BF16 ? 2 : 4;
+  p->eb = eb;
+  const size_t pbytes = B * H * S * size_t(p->ldS);
+  const size_t sizes[GPIPE_N_SAVED] = {
+      T * D * eb, T * D * eb, T * 2 * 4, T * 3 * D * eb, pbytes * eb, T * D * eb,
+      T * D * eb, T * D * eb, T * 2 * 4, T * F * eb, T * F * eb};
+  size_t off = 0;
+  for (int i = 0; i < GPIPE_N_SAVED; ++i) {
+    p->saved_off[i] = off;
+    p->saved_bytes[i] = sizes[i];
+    off += align_up(sizes[i], kAlign);
+  }
+  p->layer_bytes = off;
+  // layer 0 has no X slot: the set is L layer slots minus one X slot
+  p->set_bytes = size_t(c->L) * p->layer_bytes;
+  p->nsets = remat ? 1 : M;
+  size_t o = size_t(p->nsets) * p->set_bytes;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes, kAlign);
+    return at;
+  };
+  p->yre = take(remat ? T * D * eb : 0);
+  p->scores = take(pbytes * 4);
+  p->ds = take(pbytes * eb);
+  p->r0 = take(T * D * 4);
+  p->r1 = take(T * D * 4);
+  p->dm = take(T * D * 4);
+  p->a0 = take(T * D * eb);
+  p->a1 = take(T * D * eb);
+  p->dctx = take(T * D * eb);
+  p->du = take(T * F * eb);
+  p->dqkv = take(T * 3 * D * eb);
+  p->colpart = take(size_t(colsum_chunks(int(T))) * std::max(3 * D, F) * 4);
+  p->lnpart = take(size_t(layernorm_bwd_blocks(int(T))) * 2 * D * 4);
+  p->mse_nblk = mse_blocks(int64_t(T) * int64_t(D));
+  p->msepart = take(size_t(M) * size_t(p->mse_nblk) * 4);
+  p->total = o;
+  return true;
+}
+
+// Offset of a saved tensor of (set, layer).  Layer 0's X slot exists in the
+// layout but is never used (its input is the caller's x).
+inline size_t saved_at(const Plan& p, int set, int layer, int which) {
+  return size_t(set) * p.set_bytes + size_t(layer) * p.layer_bytes + p.saved_off[which];
+}
+
+#define GP_CHECK(expr)                              \
+  do {                                              \
+    if ((expr) != hipSuccess) return GPIPE_ERR_DEVICE; \
+  } while (0)
+
+struct Ctx {
+  const gpipe_cell* c;
+  const Plan* p;
+  char* ws;
+  hipStream_t s;
+  bool bf16;
+  const void* wmat(int layer, int t) const {
+    const size_t off = size_t(layer) * c->per_layer + c->rel_off[t];
+    if (bf16) return static_cast<const uint16_t*>(c->w_lowp) + off;
+    return c->master + off;
+  }
+  const float* wf32(int layer, int t) const {
+    return c->master + size_t(layer) * c->per_layer + c->rel_off[t];
+  }
+  float* grad(int layer, int t) const {
+    return c->grad + size_t(layer) * c->per_layer + c->rel_off[t];
+  }
+  void* at(size_t off) const { return ws + off; }
+  void* act(const void* base, size_t elems) const {
+    return const_cast<char*>(static_cast<const char*>(base)) + elems * p->eb;
+  }
+};
+
+GemmParams gp0() {
+  GemmParams g;
+  memset(&g, 0, sizeof(g));
+  g.hdiv = 1;
+  g.alpha = 1.0f;
+  return g;
+}
+
+// Plain 2-D product, no batching.
+hipError_t mm(const Ctx& x, int la, int lb, int epi, int M, int N, int K, const void* A, int64_t lda,
+              const void* B, int64_t ldb, void* C, int64_t ldc, const float* bias = nullptr,
+              const void* R = nullptr, int64_t ldr = 0, void* U = nullptr, int64_t ldu = 0,
+              int beta = 0) {
+  GemmParams g = gp0();
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda;
+  g.B = B; g.ldb = ldb;
+  g.C = C; g.ldc = ldc;
+  g.bias = bias; g.R = R; g.ldr = ldr; g.U = U; g.ldu = ldu; g.beta = beta;
+  return gemm(x.bf16, la, lb, epi, g, 1, x.s);
+}
+
+// Batched over (sequence b, head h) of one micro-batch.
+struct Bat {
+  const void* ptr;
+  int64_t ld, sb, sh;
+};
+hipError_t bmm(const Ctx& x, int la, int lb, int epi, int M, int N, int K, Bat A, Bat B, Bat C,
+               int causal, float alpha) {
+  GemmParams g = gp0();
+  g.M = M; g.N = N; g.K = K;
+  g.A = A.ptr; g.lda = A.ld; g.sAb = A.sb; g.sAh = A.sh;
+  g.B = B.ptr; g.ldb = B.ld; g.sBb = B.sb; g.sBh = B.sh;
+  g.C = const_cast<void*>(C.ptr); g.ldc = C.ld; g.sCb = C.sb; g.sCh = C.sh;
+  g.hdiv = x.c->H;
+  g.causal = causal;
+  g.alpha = alpha;
+  return gemm(x.bf16, la, lb, epi, g, x.p->B * x.c->H, x.s);
+}
+
+// Column sums of x [T, cols] added (beta) or stored into out[cols].
+hipError_t colsum_into(const Ctx& x, int xtype, const void* src, int64_t ld, int cols, float* out,
+                       int beta) {
+  int nch = 0;
+  float* part = static_cast<float*>(x.at(x.p->colpart));
+  hipError_t e = colsum_partial(xtype, src, ld, x.p->T, cols, part, &nch, x.s);
+  if (e != hipSuccess) return e;
+  return sum_partials(part, nch, cols, cols, out, beta, x.s);
+}
+
+// Forward of layer l for one micro-batch: input xin, saved tensors in `set`,
+// output xout (all act [T, D]).
+gpipe_status layer_forward(const Ctx& x, int set, int l, const void* xin, void* xout) {
+  const gpipe_cell* c = x.c;
+  const Plan& p = *x.p;
+  const int T = p.T, D = c->D, F = c->F, S = c->S, H = c->H, dh = D / H;
+  const int64_t ldS = p.ldS;
+  void* h1 = x.at(saved_at(p, set, l, GPIPE_SAVED_H1));
+  float* st1 = static_cast<float*>(x.at(saved_at(p, set, l, GPIPE_SAVED_ST1)));
+  void* qkv = x.at(saved_at(p, set, l, GPIPE_SAVED_QKV));
+  void* P = x.at(saved_at(p, set, l, GPIPE_SAVED_P));
+  void* ctx = x.at(saved_at(p, set, l, GPIPE_SAVED_CTX));
+  void* x1 = x.at(saved_at(p, set, l, GPIPE_SAVED_X1));
+  void* h2 = x.at(saved_at(p, set, l, GPIPE_SAVED_H2));
+  float* st2 = static_cast<float*>(x.at(saved_at(p, set, l, GPIPE_SAVED_ST2)));
+  void* u = x.at(saved_at(p, set, l, GPIPE_SAVED_U));
+  void* g = x.at(saved_at(p, set, l, GPIPE_SAVED_G));
+  float* scores = static_cast<float*>(x.at(p.scores));
+
+  GP_CHECK(layernorm_fwd(x.bf16, xin, h1, st1, x.wf32(l, GPIPE_LN1_G), x.wf32(l, GPIPE_LN1_B), T, D,
+                         c->ln_eps, x.s));
+  GP_CHECK(mm(x, LAY_K, LAY_K, EPI_BIAS, T, 3 * D, D, h1, D, x.wmat(l, GPIPE_W_QKV), D, qkv, 3 * D,
+              x.wf32(l, GPIPE_B_QKV)));
+  const int64_t sq = int64_t(S) * 3 * D;       // per-sequence stride inside qkv
+  const int64_t sp = int64_t(H) * S * ldS;     // per-sequence stride inside P / scores
+  const float scale = 1.0f / sqrtf(float(dh));
+  Bat Q{qkv, 3 * D, sq, dh}, K{x.act(qkv, D), 3 * D, sq, dh}, V{x.act(qkv, 2 * D), 3 * D, sq, dh};
+  Bat SC{scores, ldS, sp, int64_t(S) * ldS};
+  Bat PP{P, ldS, sp, int64_t(S) * ldS};
+  Bat CX{ctx, D, int64_t(S) * D, dh};
+  GP_CHECK(bmm(x, LAY_K, LAY_K, EPI_STORE_F32, S, S, dh, Q, K, SC,
+               c->causal ? CAUSAL_SKIP_UPPER : CAUSAL_NONE, scale));
+  GP_CHECK(softmax_fwd(x.bf16, scores, P, int64_t(p.B) * H * S, S, ldS, c->causal, x.s));
+  GP_CHECK(bmm(x, LAY_K, LAY_MN, EPI_STORE, S, dh, S, PP, V, CX,
+               c->causal ? CAUSAL_K_UPTO_M : CAUSAL_NONE, 1.0f));
+  GP_CHECK(mm(x, LAY_K, LAY_K, EPI_BIAS_RESID, T, D, D, ctx, D, x.wmat(l, GPIPE_W_O), D, x1, D,
+              x.wf32(l, GPIPE_B_O), xin, D));
+  GP_CHECK(layernorm_fwd(x.bf16, x1, h2, st2, x.wf32(l, GPIPE_LN2_G), x.wf32(l, GPIPE_LN2_B), T, D,
+                         c->ln_eps, x.s));
+  GP_CHECK(mm(x, LAY_K, LAY_K, EPI_BIAS_GELU, T, F, D, h2, D, x.wmat(l, GPIPE_W_1), D, g, F,
+              x.wf32(l, GPIPE_B_1), nullptr, 0, u, F));
+  GP_CHECK(mm(x, LAY_K, LAY_K, EPI_BIAS_RESID, T, D, F, g, F, x.wmat(l, GPIPE_W_2), F, xout, D,
+              x.wf32(l, GPIPE_B_2), x1, D));
+  return GPIPE_OK;
+}
+
+gpipe_status cell_forward(const Ctx& x, int set, const void* xin, void* yout) {
+  const int L = x.c->L;
+  for (int l = 0; l < L; ++l) {
+    const void* in = l == 0 ? xin : x.at(saved_at(*x.p, set, l, GPIPE_SAVED_X));
+    void* out = l == L - 1 ? yout : x.at(saved_at(*x.p, set, l + 1, GPIPE_SAVED_X));
+    gpipe_status st = layer_forward(x, set, l, in, out);
+    if (st != GPIPE_OK) return st;
+  }
+  return GPIPE_OK;
+}
+
+// Backward of layer l.  On entry r0 (f32) / a0 (act) hold the gradient w.r.t.
+// the layer output; on exit they hold the gradient w.r.t. its input (a0, or
+// dx_out when given, receives the act copy).
+gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int beta, void* dx_out) {
+  const gpipe_cell* c = x.c;
+  const Plan& p = *x.p;
+  const int T = p.T, D = c->D, F = c->F, S = c->S, H = c->H, dh = D / H;
+  const int64_t ldS = p.ldS;
+  const bool bf = x.bf16;
+  const int xt_act = bf ? XT_BF16 : XT_F32;
+  void* h1 = x.at(saved_at(p, set, l, GPIPE_SAVED_H1));
+  const float* st1 = static_cast<const float*>(x.at(saved_at(p, set, l, GPIPE_SAVED_ST1)));
+  void* qkv = x.at(saved_at(p, set, l, GPIPE_SAVED_QKV));
+  void* P = x.at(saved_at(p, set, l, GPIPE_SAVED_P));
+  void* ctx = x.at(saved_at(p, set, l, GPIPE_SAVED_CTX));
+  void* x1 = x.at(saved_at(p, set, l, GPIPE_SAVED_X1));
+  void* h2 = x.at(saved_at(p, set, l, GPIPE_SAVED_H2));
+  const float* st2 = static_cast<const float*>(x.at(saved_at(p, set, l, GPIPE_SAVED_ST2)));
+  void* u = x.at(saved_at(p, set, l, GPIPE_SAVED_U));
+  void* g = x.at(saved_at(p, set, l, GPIPE_SAVED_G));
+  float* r0 = static_cast<float*>(x.at(p.r0));
+  float* r1 = static_cast<float*>(x.at(p.r1));
+  float* dm = static_cast<float*>(x.at(p.dm));
+  void* a0 = x.at(p.a0);
+  void* a1 = x.at(p.a1);
+  void* dctx = x.at(p.dctx);
+  void* du = x.at(p.du);
+  void* dqkv = x.at(p.dqkv);
+  float* dP = static_cast<float*>(x.at(p.scores));
+  void* dS = x.at(p.ds);
+  float* lnpart = static_cast<float*>(x.at(p.lnpart));
+
+  // FFN: y = x1 + g W2^T + b2,  g = gelu(u),  u = h2 W1^T + b1
+  GP_CHECK(mm(x, LAY_K, LAY_MN, EPI_GELU_BWD, T, F, D, a0, D, x.wmat(l, GPIPE_W_2), F, du, F,
+              nullptr, nullptr, 0, u, F));
+  GP_CHECK(mm(x, LAY_MN, LAY_MN, EPI_ACC_F32, D, F, T, a0, D, g, F, x.grad(l, GPIPE_W_2), F,
+              nullptr, nullptr, 0, nullptr, 0, beta));
+  GP_CHECK(colsum_into(x, XT_F32, r0, D, D, x.grad(l, GPIPE_B_2), beta));
+  GP_CHECK(mm(x, LAY_K, LAY_MN, EPI_STORE_F32, T, D, F, du, F, x.wmat(l, GPIPE_W_1), D, dm, D));
+  GP_CHECK(mm(x, LAY_MN, LAY_MN, EPI_ACC_F32, F, D, T, du, F, h2, D, x.grad(l, GPIPE_W_1), D,
+              nullptr, nullptr, 0, nullptr, 0, beta));
+  GP_CHECK(colsum_into(x, xt_act, du, F, F, x.grad(l, GPIPE_B_1), beta));
+  int nblk = 0;
+  GP_CHECK(layernorm_bwd(bf, dm, x1, st2, x.wf32(l, GPIPE_LN2_G), r0, r1, a1, lnpart, T, D, &nblk,
+                         x.s));
+  GP_CHECK(sum_partials(lnpart, nblk, 2 * D, D, x.grad(l, GPIPE_LN2_G), beta, x.s));
+  GP_CHECK(sum_partials(lnpart + D, nblk, 2 * D, D, x.grad(l, GPIPE_LN2_B), beta, x.s));
+
+  // attention: x1 = x + ctx Wo^T + bo
+  GP_CHECK(mm(x, LAY_K, LAY_MN, EPI_STORE, T, D, D, a1, D, x.wmat(l, GPIPE_W_O), D, dctx, D));
+  GP_CHECK(mm(x, LAY_MN, LAY_MN, EPI_ACC_F32, D, D, T, a1, D, ctx, D, x.grad(l, GPIPE_W_O), D,
+              nullptr, nullptr, 0, nullptr, 0, beta));
+  GP_CHECK(colsum_into(x, XT_F32, r1, D, D, x.grad(l, GPIPE_B_O), beta));
+  const int64_t sq = int64_t(S) * 3 * D;
+  const int64_t sp = int64_t(H) * S * ldS;
+  const int64_t sd = int64_t(S) * D;
+  const float scale = 1.0f / sqrtf(float(dh));
+  Bat Q{qkv, 3 * D, sq, dh}, K{x.act(qkv, D), 3 * D, sq, dh}, V{x.act(qkv, 2 * D), 3 * D, sq, dh};
+  Bat dQ{dqkv, 3 * D, sq, dh}, dK{x.act(dqkv, D), 3 * D, sq, dh}, dV{x.act(dqkv, 2 * D), 3 * D, sq, dh};
+  Bat PP{P, ldS, sp, int64_t(S) * ldS}, DP{dP, ldS, sp, int64_t(S) * ldS}, DS{dS, ldS, sp, int64_t(S) * ldS};
+  Bat DC{dctx, D, sd, dh};
+  const int cz = c->causal;
+  GP_CHECK(bmm(x, LAY_K, LAY_K, EPI_STORE_F32, S, S, dh, DC, V, DP,
+               cz ? CAUSAL_SKIP_UPPER : CAUSAL_NONE, 1.0f));
+  GP_CHECK(bmm(x, LAY_MN, LAY_MN, EPI_STORE, S, dh, S, PP, DC, dV,
+               cz ? CAUSAL_K_FROM_M : CAUSAL_NONE, 1.0f));
+  GP_CHECK(softmax_bwd(bf, P, dP, dS, int64_t(p.B) * H * S, S, ldS, cz, scale, x.s));
+  GP_CHECK(bmm(x, LAY_K, LAY_MN, EPI_STORE, S, dh, S, DS, K, dQ,
+               cz ? CAUSAL_K_UPTO_M : CAUSAL_NONE, 1.0f));
+  GP_CHECK(bmm(x, LAY_MN, LAY_MN, EPI_STORE, S, dh, S, DS, Q, dK,
+               cz ? CAUSAL_K_FROM_M : CAUSAL_NONE, 1.0f));
+
+  // qkv = h1 Wqkv^T + bqkv,  h1 = LN1(x)
+  GP_CHECK(mm(x, LAY_K, LAY_MN, EPI_STORE_F32, T, D, 3 * D, dqkv, 3 * D, x.wmat(l, GPIPE_W_QKV), D,
+              dm, D));
+  GP_CHECK(mm(x, LAY_MN, LAY_MN, EPI_ACC_F32, 3 * D, D, T, dqkv, 3 * D, h1, D,
+              x.grad(l, GPIPE_W_QKV), D, nullptr, nullptr, 0, nullptr, 0, beta));
+  GP_CHECK(colsum_into(x, xt_act, dqkv, 3 * D, 3 * D, x.grad(l, GPIPE_B_QKV), beta));
+  GP_CHECK(layernorm_bwd(bf, dm, xin, st1, x.wf32(l, GPIPE_LN1_G), r1, r0, dx_out ? dx_out : a0,
+                         lnpart, T, D, &nblk, x.s));
+  GP_CHECK(sum_partials(lnpart, nblk, 2 * D, D, x.grad(l, GPIPE_LN1_G), beta, x.s));
+  GP_CHECK(sum_partials(lnpart + D, nblk, 2 * D, D, x.grad(l, GPIPE_LN1_B), beta, x.s));
+  return GPIPE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gpipe_status_string(gpipe_status s) {
+  switch (s) {
+    case GPIPE_OK: return "ok";
+    case GPIPE_ERR_INVALID: return "invalid argument";
+    case GPIPE_ERR_OOM: return "out of device memory";
+    case GPIPE_ERR_DEVICE: return "HIP device error";
+    case GPIPE_ERR_UNSUPPORTED: return "unsupported shape";
+    case GPIPE_ERR_STATE: return "invalid state";
+  }
+  return "unknown status";
+}
+
+gpipe_status gpipe_cell_create(int layers, int d_model, int heads, int d_ff, int seq, int causal,
+                               gpipe_precision prec, gpipe_cell** out) {
+  if (!out) return GPIPE_ERR_INVALID;
+  if (layers <= 0 || d_model <= 0 || heads <= 0 || d_ff <= 0 || seq <= 0) return GPIPE_ERR_INVALID;
+  if (d_model % heads) return GPIPE_ERR_INVALID;
+  if (prec != GPIPE_FP32 && prec != GPIPE_BF16) return GPIPE_ERR_INVALID;
+  const int dh = d_model / heads;
+  if (d_model % 8 || d_ff % 8 || dh % 8 || d_model > 8192 || seq > 4096)
+    return GPIPE_ERR_UNSUPPORTED;
+  gpipe_cell* c = new (std::nothrow) gpipe_cell();
+  if (!c) return GPIPE_ERR_INVALID;
+  c->L = layers; c->D = d_model; c->H = heads; c->F = d_ff; c->S = seq;
+  c->causal = causal ? 1 : 0;
+  c->prec = prec;
+  c->ln_eps = 1e-5f;
+  const size_t D = d_model, F = d_ff;
+  const size_t cnt[GPIPE_N_TENSORS] = {D, D, 3 * D * D, 3 * D, D * D, D, D, D, F * D, F, D * F, D};
+  size_t off = 0;
+  for (int t = 0; t < GPIPE_N_TENSORS; ++t) {
+    c->rel_off[t] = off;
+    c->count[t] = cnt[t];
+    off += cnt[t];
+  }
+  c->per_layer = off;
+  c->n_params = off * size_t(layers);
+  *out = c;
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_cell_destroy(gpipe_cell* c) {
+  delete c;
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_cell_param_count(const gpipe_cell* c, size_t* n) {
+  if (!c || !n) return GPIPE_ERR_INVALID;
+  *n = c->n_params;
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_cell_param_offset(const gpipe_cell* c, int layer, int tensor, size_t* offset,
+                                     size_t* count) {
+  if (!c || !offset || !count || layer < 0 || layer >= c->L || tensor < 0 ||
+      tensor >= GPIPE_N_TENSORS)
+    return GPIPE_ERR_INVALID;
+  *offset = size_t(layer) * c->per_layer + c->rel_off[tensor];
+  *count = c->count[tensor];
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_cell_bind(gpipe_cell* c, float* master, void* w_lowp, float* grad, float* ms) {
+  if (!c || !master || !grad || !ms) return GPIPE_ERR_INVALID;
+  if ((c->prec == GPIPE_BF16) != (w_lowp != nullptr)) return GPIPE_ERR_INVALID;
+  if (!aligned16(master) || !aligned16(grad) || !aligned16(ms) || (w_lowp && !aligned16(w_lowp)))
+    return GPIPE_ERR_INVALID;
+  c->master = master;
+  c->w_lowp = w_lowp;
+  c->grad = grad;
+  c->ms = ms;
+  c->bound = true;
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_cell_sync_lowp(gpipe_cell* c, void* stream) {
+  if (!c) return GPIPE_ERR_INVALID;
+  if (!c->bound) return GPIPE_ERR_STATE;
+  if (c->prec != GPIPE_BF16) return GPIPE_OK;
+  GP_CHECK(to_bf16(c->master, c->w_lowp, int64_t(c->n_params), static_cast<hipStream_t>(stream)));
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_cell_workspace_bytes(const gpipe_cell* c, int N, int M, int remat, size_t* bytes) {
+  if (!c || !bytes) return GPIPE_ERR_INVALID;
+  Plan p;
+  if (!make_plan(c, N, M, remat, &p)) return GPIPE_ERR_INVALID;
+  *bytes = p.total;
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_cell_saved_offset(const gpipe_cell* c, int N, int M, int remat, int micro,
+                                     int layer, int which, size_t* offset, size_t* bytes) {
+  if (!c || !offset || !bytes) return GPIPE_ERR_INVALID;
+  Plan p;
+  if (!make_plan(c, N, M, remat, &p)) return GPIPE_ERR_INVALID;
+  if (micro < 0 || micro >= p.nsets || layer < 0 || layer >= c->L || which < 0 ||
+      which >= GPIPE_N_SAVED || (layer == 0 && which == GPIPE_SAVED_X))
+    return GPIPE_ERR_INVALID;
+  *offset = saved_at(p, micro, layer, which);
+  *bytes = p.saved_bytes[which];
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, void* y, void* dx,
+                             int N, int M, int remat, void* workspace, size_t ws_bytes,
+                             void* stream, float* loss_dev) {
+  if (!c) return GPIPE_ERR_INVALID;
+  if (!c->bound) return GPIPE_ERR_STATE;
+  Plan p;
+  if (!make_plan(c, N, M, remat, &p)) return GPIPE_ERR_INVALID;
+  if (!x || !target || !y || !workspace || !loss_dev || ws_bytes < p.total) return GPIPE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(target) || !aligned16(y) || (dx && !aligned16(dx)) ||
+      !aligned16(workspace))
+    return GPIPE_ERR_INVALID;
+  Ctx cx{c, &p, static_cast<char*>(workspace), static_cast<hipStream_t>(stream),
+         c->prec == GPIPE_BF16};
+  const size_t mb = size_t(p.T) * c->D;  // elements per micro-batch
+  const float inv_denom = float(1.0 / (double(N) * c->S * c->D));
+  float* msepart = static_cast<float*>(cx.at(p.msepart));
+
+  // phase 1: forward, boundary output only (intermediates are overwritten)
+  for (int m = 0; m < M; ++m) {
+    const int set = remat ? 0 : m;
+    gpipe_status st = cell_forward(cx, set, cx.act(x, m * mb), cx.act(y, m * mb));
+    if (st != GPIPE_OK) return st;
+  }
+  // phase 2: backward with re-materialization and float32 accumulation
+  for (int m = 0; m < M; ++m) {
+    const int set = remat ? 0 : m;
+    const void* xm = cx.act(x, m * mb);
+    const void* ym = cx.act(y, m * mb);
+    if (remat) {
+      void* yre = cx.at(p.yre);
+      gpipe_status st = cell_forward(cx, set, xm, yre);
+      if (st != GPIPE_OK) return st;
+      ym = yre;
+    }
+    int nblk = 0;
+    GP_CHECK(mse_fwd_bwd(cx.bf16, ym, cx.act(target, m * mb), static_cast<float*>(cx.at(p.r0)),
+                         cx.at(p.a0), msepart + size_t(m) * p.mse_nblk, int64_t(mb), inv_denom,
+                         &nblk, cx.s));
+    for (int l = c->L - 1; l >= 0; --l) {
+      const void* xin = l == 0 ? xm : cx.at(saved_at(p, set, l, GPIPE_SAVED_X));
+      void* dxo = (l == 0 && dx) ? cx.act(dx, m * mb) : nullptr;
+      gpipe_status st = layer_backward(cx, set, l, xin, m > 0 ? 1 : 0, dxo);
+      if (st != GPIPE_OK) return st;
+    }
+  }
+  GP_CHECK(sum_partials(msepart, M * p.mse_nblk, 1, 1, loss_dev, 0, cx.s));
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_apply_update(gpipe_cell* c, float lr, float decay, float eps, void* stream) {
+  if (!c) return GPIPE_ERR_INVALID;
+  if (!c->bound) return GPIPE_ERR_STATE;
+  if (!(decay >= 0.f && decay < 1.f) || !(lr >= 0.f) || !(eps >= 0.f) || !isfinite(lr) ||
+      !isfinite(eps))
+    return GPIPE_ERR_INVALID;
+  GP_CHECK(rmsprop(c->master, c->grad, c->ms, c->prec == GPIPE_BF16 ? c->w_lowp : nullptr,
+                   int64_t(c->n_params), lr, decay, eps, static_cast<hipStream_t>(stream)));
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_partition(const double* costs, int L, int K, int* bounds, double* variance) {
+  if (!costs || !bounds || L < 1 || K < 1 || K > L) return GPIPE_ERR_INVALID;
+  for (int i = 0; i < L; ++i)
+    if (!(costs[i] >= 0.0) || !isfinite(costs[i])) return GPIPE_ERR_INVALID;
+  // Minimising the variance of the K cell sums C_k is minimising sum_k C_k^2
+  // (their total is fixed).  g[k][i]: least sum of squares splitting layers
+  // i..L-1 into k non-empty cells; the cuts are then read from the front,
+  // always taking the earliest optimal cut, which gives the
+  // lexicographically smallest bounds among the optima.
+  std::vector<double> pre(L + 1, 0.0);
+  for (int i = 0; i < L; ++i) pre[i + 1] = pre[i] + costs[i];
+  const double inf = std::numeric_limits<double>::infinity();
+  std::vector<double> g(size_t(K + 1) * (L + 1), inf);
+  auto G = [&](int k, int i) -> double& { return g[size_t(k) * (L + 1) + i]; };
+  G(0, L) = 0.0;
+  for (int k = 1; k <= K; ++k)
+    for (int i = 0; i <= L - k; ++i) {
+      double best = inf;
+      for (int j = i + 1; j <= L - (k - 1); ++j) {
+        const double cj = pre[j] - pre[i];
+        const double v = cj * cj + G(k - 1, j);
+        if (v < best) best = v;
+      }
+      G(k, i) = best;
+    }
+  bounds[0] = 0;
+  int i = 0;
+  for (int k = K; k >= 1; --k) {
+    int pick = -1;
+    for (int j = i + 1; j <= L - (k - 1); ++j) {
+      const double cj = pre[j] - pre[i];
+      if (cj * cj + G(k - 1, j) == G(k, i)) {
+        pick = j;
+        break;
+      }
+    }
+    if (pick < 0) return GPIPE_ERR_INVALID;  // unreachable for finite costs
+    bounds[K - k + 1] = pick;
+    i = pick;
+  }
+  if (variance) {
+    const double mean = pre[L] / K;
+    double v = 0.0;
+    for (int k = 0; k < K; ++k) {
+      const double ck = pre[bounds[k + 1]] - pre[bounds[k]] - mean;
+      v += ck * ck;
+    }
+    *variance = v / K;
+  }
+  return GPIPE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Host-callable launchers of the cell's HIP kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gp {
+
+// ---------------------------------------------------------------- GEMM
+enum { LAY_K = 0, LAY_MN = 1 };
+
+enum {
+  EPI_STORE = 0,       // C(act) = alpha * acc
+  EPI_BIAS = 1,        // C(act) = acc + bias[n]
+  EPI_BIAS_RESID = 2,  // C(act) = acc + bias[n] + R(act)[m, n]
+  EPI_BIAS_GELU = 3,   // U(act) = acc + bias[n];  C(act) = gelu(U)
+  EPI_GELU_BWD = 4,    // C(act) = acc * gelu'(U(act)[m, n])
+  EPI_STORE_F32 = 5,   // C(f32) = alpha * acc
+  EPI_ACC_F32 = 6,     // C(f32) = (beta ? C : 0) + acc
+};
+
+// Causal structure of the attention products (rows i, keys j, j <= i kept):
+//   SKIP_UPPER:  output tiles entirely above the diagonal are not computed
+//   K_UPTO_M:    reduction over k < (tile's last row + 1)   (P.V, dS.K)
+//   K_FROM_M:    reduction over k >= tile's first row       (P^T.dC, dS^T.Q)
+// The masked entries of P and dS are stored as exact zeros, so the partial
+// k-tiles these modes keep contribute nothing extra.
+enum { CAUSAL_NONE = 0, CAUSAL_SKIP_UPPER = 1, CAUSAL_K_UPTO_M = 2, CAUSAL_K_FROM_M = 3 };
+
+struct GemmParams {
+  int M, N, K;
+  const void* A; int64_t lda, sAb, sAh;   // element strides; batch z -> (z / hdiv, z % hdiv)
+  const void* B; int64_t ldb, sBb, sBh;
+  void* C; int64_t ldc, sCb, sCh;
+  int hdiv;
+  int causal;
+  const float* bias;
+  const void* R; int64_t ldr;
+  void* U; int64_t ldu;
+  float alpha;
+  int beta;
+};
+
+hipError_t gemm(bool bf16, int la, int lb, int epi, const GemmParams& g, int batch, hipStream_t s);
+int gemm_tile_m(bool bf16);
+
+// ---------------------------------------------------------------- row kernels
+// LayerNorm forward over rows of length D: y(act) = gamma*(x-mu)*rstd + beta, stats[2*row] = (mu, rstd).
+hipError_t layernorm_fwd(bool bf16, const void* x, void* y, float* stats, const float* gamma,
+                         const float* beta, int rows, int d, float eps, hipStream_t s);
+
+// LayerNorm backward.  dh: f32 [rows, d] gradient w.r.t. the LN output; x: act input;
+// res_in: f32 residual gradient added to dx; writes dx_f32 (may alias res_in) and dx_act;
+// per-block partial sums of dgamma and dbeta into part[nblk][2][d]; returns nblk via *nblk.
+hipError_t layernorm_bwd(bool bf16, const float* dh, const void* x, const float* stats,
+                         const float* gamma, const float* res_in, float* dx_f32, void* dx_act,
+                         float* part, int rows, int d, int* nblk, hipStream_t s);
+int layernorm_bwd_blocks(int rows);
+
+// Softmax forward of scores (f32, already scaled) into P(act); rows of length n, row pitch ld,
+// optional causal mask (key j > row index i within its [n x n] block); masked entries -> 0.
+hipError_t softmax_fwd(bool bf16, const float* scores, void* p, int64_t rows, int n, int64_t ld,
+                       int causal, hipStream_t s);
+// Softmax backward: dS(act) = scale * P * (dP - rowsum(P*dP)); masked entries -> 0.
+hipError_t softmax_bwd(bool bf16, const void* p, const float* dp, void* ds, int64_t rows, int n,
+                       int64_t ld, int causal, float scale, hipStream_t s);
+
+// MSE: r = y - t over `count` elements; dy = 2 r / denom into dy_f32 and dy_act;
+// per-block partial sums of r^2 / denom into part[nblk].
+hipError_t mse_fwd_bwd(bool bf16, const void* y, const void* t, float* dy_f32, void* dy_act,
+                       float* part, int64_t count, float inv_denom, int* nblk, hipStream_t s);
+int mse_blocks(int64_t count);
+
+// Column sums: part[chunk][c] = sum over the rows of chunk of x[r, c] (x is f32 or act).
+hipError_t colsum_partial(int xtype, const void* x, int64_t ld, int rows, int cols, float* part,
+                          int* nchunk, hipStream_t s);
+int colsum_chunks(int rows);
+// out[c] = (beta ? out[c] : 0) + sum_p part[p * stride + c], p = 0 .. nparts-1 in order.
+hipError_t sum_partials(const float* part, int nparts, int64_t stride, int cols, float* out,
+                        int beta, hipStream_t s);
+
+// RMSProp over n parameters; writes the bf16 copy when w_lowp is non-null.
+hipError_t rmsprop(float* w, const float* g, float* ms, void* w_lowp, int64_t n, float lr,
+                   float decay, float eps, hipStream_t s);
+
+// dst = bf16(src), n elements.
+hipError_t to_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
+
+enum { XT_F32 = 0, XT_BF16 = 2 };
+
+}  // namespace gp

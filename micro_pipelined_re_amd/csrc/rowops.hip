@@ -1,0 +1,509 @@
+// Memory-bound kernels of the cell step: LayerNorm, softmax, MSE, column sums,
+// RMSProp.  Every reduction has a fixed combination order (no float atomics),
+// so a step is bitwise reproducible and re-materialization rebuilds exactly
+// the activations of the forward phase.
+//
+// Rows are processed in chunks of 8 elements (one 16-byte bf16 vector or two
+// float4), so row lengths must be multiples of 8.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gp {
+
+// ------------------------------------------------------------ 8-element chunks
+template <typename T> __device__ __forceinline__ void load8(const T* p, float* v);
+template <> __device__ __forceinline__ void load8<float>(const float* p, float* v) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <> __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float* v) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <typename T> __device__ __forceinline__ void store8(T* p, const float* v);
+template <> __device__ __forceinline__ void store8<float>(float* p, const float* v) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+template <> __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float* v) {
+  uint4 a;
+  a.x = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
+  a.y = uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16);
+  a.z = uint32_t(f2bf(v[4])) | (uint32_t(f2bf(v[5])) << 16);
+  a.w = uint32_t(f2bf(v[6])) | (uint32_t(f2bf(v[7])) << 16);
+  *reinterpret_cast<uint4*>(p) = a;
+}
+
+// Sum over the 256 threads of a block, fixed order; every thread gets the result.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// ------------------------------------------------------------ LayerNorm forward
+// One wave per row; lane owns chunks lane, lane+64, ... (NV of them).
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void ln_fwd_kernel(const T* __restrict__ x, T* __restrict__ y,
+                                                     float* __restrict__ stats,
+                                                     const float* __restrict__ gamma,
+                                                     const float* __restrict__ beta, int rows,
+                                                     int d, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int nch = d >> 3;
+  const T* xr = x + int64_t(row) * d;
+  float v[NV][8];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      load8<T>(xr + c * 8, v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += v[i][e];
+    }
+  }
+  const float mu = wave_sum(s) / float(d);
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = v[i][e] - mu;
+        q += t * t;
+      }
+    }
+  }
+  const float var = wave_sum(q) / float(d);
+  const float rstd = 1.0f / sqrtf(var + eps);
+  T* yr = y + int64_t(row) * d;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (v[i][e] - mu) * rstd * gamma[c * 8 + e] + beta[c * 8 + e];
+      store8<T>(yr + c * 8, o);
+    }
+  }
+  if (lane == 0) {
+    stats[2 * row] = mu;
+    stats[2 * row + 1] = rstd;
+  }
+}
+
+template <typename T>
+static hipError_t ln_fwd_t(const void* x, void* y, float* stats, const float* g, const float* b,
+                           int rows, int d, float eps, hipStream_t s) {
+  const int nch = d / 8;
+  dim3 grid((rows + 3) / 4), blk(256);
+  const T* xp = static_cast<const T*>(x);
+  T* yp = static_cast<T*>(y);
+  if (nch <= 64) hipLaunchKernelGGL((ln_fwd_kernel<T, 1>), grid, blk, 0, s, xp, yp, stats, g, b, rows, d, eps);
+  else if (nch <= 128) hipLaunchKernelGGL((ln_fwd_kernel<T, 2>), grid, blk, 0, s, xp, yp, stats, g, b, rows, d, eps);
+  else if (nch <= 256) hipLaunchKernelGGL((ln_fwd_kernel<T, 4>), grid, blk, 0, s, xp, yp, stats, g, b, rows, d, eps);
+  else if (nch <= 512) hipLaunchKernelGGL((ln_fwd_kernel<T, 8>), grid, blk, 0, s, xp, yp, stats, g, b, rows, d, eps);
+  else if (nch <= 1024) hipLaunchKernelGGL((ln_fwd_kernel<T, 16>), grid, blk, 0, s, xp, yp, stats, g, b, rows, d, eps);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t layernorm_fwd(bool bf16, const void* x, void* y, float* stats, const float* gamma,
+                         const float* beta, int rows, int d, float eps, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  return bf16 ? ln_fwd_t<bf16_t>(x, y, stats, gamma, beta, rows, d, eps, s)
+              : ln_fwd_t<float>(x, y, stats, gamma, beta, rows, d, eps, s);
+}
+
+// ------------------------------------------------------------ LayerNorm backward
+// A block of 256 threads takes kLnRows consecutive rows; thread owns chunks
+// tid, tid+256, ... of every row, so it also owns those columns' dgamma/dbeta
+// partial sums, which it writes once for the whole block.
+constexpr int kLnRows = 8;
+
+template <typename T, int NVB>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ dh,
+                                                     const T* __restrict__ x,
+                                                     const float* __restrict__ stats,
+                                                     const float* __restrict__ gamma,
+                                                     const float* res_in, float* dx_f32,
+                                                     T* __restrict__ dx_act,
+                                                     float* __restrict__ part, int rows, int d) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int nch = d >> 3;
+  float pg[NVB][8], pb[NVB][8];
+#pragma unroll
+  for (int i = 0; i < NVB; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pg[i][e] = pb[i][e] = 0.f;
+  const int r0 = blockIdx.x * kLnRows;
+  const int r1 = min(rows, r0 + kLnRows);
+  for (int row = r0; row < r1; ++row) {
+    const float mu = stats[2 * row], rstd = stats[2 * row + 1];
+    float xh[NVB][8], dxh[NVB][8];
+    float sa = 0.f, sb = 0.f;
+#pragma unroll
+    for (int i = 0; i < NVB; ++i) {
+      const int c = tid + 256 * i;
+      if (c < nch) {
+        float xv[8], gv[8];
+        load8<T>(x + int64_t(row) * d + c * 8, xv);
+        load8<float>(dh + int64_t(row) * d + c * 8, gv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xh[i][e] = (xv[e] - mu) * rstd;
+          dxh[i][e] = gv[e] * gamma[c * 8 + e];
+          sa += dxh[i][e];
+          sb += dxh[i][e] * xh[i][e];
+          pg[i][e] += gv[e] * xh[i][e];
+          pb[i][e] += gv[e];
+        }
+      }
+    }
+    const float ma = block_sum(sa, red) / float(d);
+    const float mb = block_sum(sb, red) / float(d);
+#pragma unroll
+    for (int i = 0; i < NVB; ++i) {
+      const int c = tid + 256 * i;
+      if (c < nch) {
+        float rv[8], o[8];
+        load8<float>(res_in + int64_t(row) * d + c * 8, rv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = rv[e] + rstd * (dxh[i][e] - ma - xh[i][e] * mb);
+        store8<float>(dx_f32 + int64_t(row) * d + c * 8, o);
+        store8<T>(dx_act + int64_t(row) * d + c * 8, o);
+      }
+    }
+  }
+  float* pgo = part + int64_t(blockIdx.x) * 2 * d;
+#pragma unroll
+  for (int i = 0; i < NVB; ++i) {
+    const int c = tid + 256 * i;
+    if (c < nch) {
+      store8<float>(pgo + c * 8, pg[i]);
+      store8<float>(pgo + d + c * 8, pb[i]);
+    }
+  }
+}
+
+int layernorm_bwd_blocks(int rows) { return (rows + kLnRows - 1) / kLnRows; }
+
+template <typename T>
+static hipError_t ln_bwd_t(const float* dh, const void* x, const float* stats, const float* gamma,
+                           const float* res_in, float* dx_f32, void* dx_act, float* part,
+                           int rows, int d, hipStream_t s) {
+  const int nch = d / 8;
+  dim3 grid(layernorm_bwd_blocks(rows)), blk(256);
+  const T* xp = static_cast<const T*>(x);
+  T* op = static_cast<T*>(dx_act);
+  if (nch <= 256) hipLaunchKernelGGL((ln_bwd_kernel<T, 1>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d);
+  else if (nch <= 512) hipLaunchKernelGGL((ln_bwd_kernel<T, 2>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d);
+  else if (nch <= 1024) hipLaunchKernelGGL((ln_bwd_kernel<T, 4>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t layernorm_bwd(bool bf16, const float* dh, const void* x, const float* stats,
+                         const float* gamma, const float* res_in, float* dx_f32, void* dx_act,
+                         float* part, int rows, int d, int* nblk, hipStream_t s) {
+  *nblk = layernorm_bwd_blocks(rows);
+  if (rows == 0) return hipSuccess;
+  return bf16 ? ln_bwd_t<bf16_t>(dh, x, stats, gamma, res_in, dx_f32, dx_act, part, rows, d, s)
+              : ln_bwd_t<float>(dh, x, stats, gamma, res_in, dx_f32, dx_act, part, rows, d, s);
+}
+
+// ------------------------------------------------------------ softmax
+// One wave per row of length n (row pitch ld >= n rounded up to 8); rows are
+// grouped in [n x n] blocks, so the query index of a row is row % n.  Causal
+// rows keep keys j <= i; the other entries of P, and the row padding, are
+// written as zeros.
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void softmax_fwd_kernel(const float* __restrict__ sc,
+                                                          T* __restrict__ p, int64_t rows, int n,
+                                                          int64_t ld, int causal) {
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int valid = causal ? int(row % n) + 1 : n;
+  const int nch = (n + 7) >> 3;  // the last chunk may run into the row padding
+  const float* sr = sc + row * ld;
+  float v[NV][8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch && c * 8 < valid) {
+      load8<float>(sr + c * 8, v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (c * 8 + e >= valid) v[i][e] = -INFINITY;
+        mx = fmaxf(mx, v[i][e]);
+      }
+    }
+  }
+  mx = wave_max(mx);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch && c * 8 < valid) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[i][e] = (c * 8 + e < valid) ? expf(v[i][e] - mx) : 0.f;
+        sum += v[i][e];
+      }
+    }
+  }
+  const float inv = 1.0f / wave_sum(sum);
+  T* pr = p + row * ld;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      float o[8];
+      const bool live = c * 8 < valid;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = live ? v[i][e] * inv : 0.f;
+      store8<T>(pr + c * 8, o);
+    }
+  }
+}
+
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void softmax_bwd_kernel(const T* __restrict__ p,
+                                                          const float* __restrict__ dp,
+                                                          T* __restrict__ ds, int64_t rows, int n,
+                                                          int64_t ld, int causal, float scale) {
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int valid = causal ? int(row % n) + 1 : n;
+  const int nch = (n + 7) >> 3;  // the last chunk may run into the row padding
+  float pv[NV][8], gv[NV][8];
+  float r = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch && c * 8 < valid) {
+      load8<T>(p + row * ld + c * 8, pv[i]);
+      load8<float>(dp + row * ld + c * 8, gv[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (c * 8 + e >= valid) pv[i][e] = gv[i][e] = 0.f;
+        r += pv[i][e] * gv[i][e];
+      }
+    }
+  }
+  r = wave_sum(r);
+  T* dr = ds + row * ld;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      float o[8];
+      const bool live = c * 8 < valid;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = live ? scale * pv[i][e] * (gv[i][e] - r) : 0.f;
+      store8<T>(dr + c * 8, o);
+    }
+  }
+}
+
+#define GP_SOFTMAX_DISPATCH(KERNEL, T, ...)                                                    \
+  do {                                                                                         \
+    const int nch_ = (n + 7) / 8;                                                              \
+    dim3 grid_((unsigned)((rows + 3) / 4)), blk_(256);                                         \
+    if (nch_ <= 64) hipLaunchKernelGGL((KERNEL<T, 1>), grid_, blk_, 0, s, __VA_ARGS__);        \
+    else if (nch_ <= 128) hipLaunchKernelGGL((KERNEL<T, 2>), grid_, blk_, 0, s, __VA_ARGS__);  \
+    else if (nch_ <= 256) hipLaunchKernelGGL((KERNEL<T, 4>), grid_, blk_, 0, s, __VA_ARGS__);  \
+    else if (nch_ <= 512) hipLaunchKernelGGL((KERNEL<T, 8>), grid_, blk_, 0, s, __VA_ARGS__);  \
+    else return hipErrorInvalidValue;                                                          \
+  } while (0)
+
+hipError_t softmax_fwd(bool bf16, const float* scores, void* p, int64_t rows, int n, int64_t ld,
+                       int causal, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (bf16) GP_SOFTMAX_DISPATCH(softmax_fwd_kernel, bf16_t, scores, static_cast<bf16_t*>(p), rows, n, ld, causal);
+  else GP_SOFTMAX_DISPATCH(softmax_fwd_kernel, float, scores, static_cast<float*>(p), rows, n, ld, causal);
+  return hipGetLastError();
+}
+
+hipError_t softmax_bwd(bool bf16, const void* p, const float* dp, void* ds, int64_t rows, int n,
+                       int64_t ld, int causal, float scale, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (bf16) GP_SOFTMAX_DISPATCH(softmax_bwd_kernel, bf16_t, static_cast<const bf16_t*>(p), dp, static_cast<bf16_t*>(ds), rows, n, ld, causal, scale);
+  else GP_SOFTMAX_DISPATCH(softmax_bwd_kernel, float, static_cast<const float*>(p), dp, static_cast<float*>(ds), rows, n, ld, causal, scale);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ MSE
+constexpr int kMseBlocks = 256;
+int mse_blocks(int64_t count) {
+  const int64_t chunks = count / 8;
+  return int(chunks < kMseBlocks * 256 ? (chunks + 255) / 256 : kMseBlocks);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void mse_kernel(const T* __restrict__ y, const T* __restrict__ t,
+                                                  float* __restrict__ dy_f32, T* __restrict__ dy_act,
+                                                  float* __restrict__ part, int64_t nch,
+                                                  float inv_denom, float two_inv_denom) {
+  __shared__ float red[4];
+  float acc = 0.f;
+  for (int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x; c < nch; c += int64_t(gridDim.x) * 256) {
+    float yv[8], tv[8], o[8];
+    load8<T>(y + c * 8, yv);
+    load8<T>(t + c * 8, tv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float r = yv[e] - tv[e];
+      acc += r * r;
+      o[e] = two_inv_denom * r;
+    }
+    store8<float>(dy_f32 + c * 8, o);
+    store8<T>(dy_act + c * 8, o);
+  }
+  const float tot = block_sum(acc, red);
+  if (threadIdx.x == 0) part[blockIdx.x] = tot * inv_denom;
+}
+
+hipError_t mse_fwd_bwd(bool bf16, const void* y, const void* t, float* dy_f32, void* dy_act,
+                       float* part, int64_t count, float inv_denom, int* nblk, hipStream_t s) {
+  *nblk = mse_blocks(count);
+  if (count == 0) return hipSuccess;
+  const float k = 2.0f * inv_denom;
+  if (bf16)
+    hipLaunchKernelGGL(mse_kernel<bf16_t>, dim3(*nblk), dim3(256), 0, s, static_cast<const bf16_t*>(y),
+                       static_cast<const bf16_t*>(t), dy_f32, static_cast<bf16_t*>(dy_act), part, count / 8, inv_denom, k);
+  else
+    hipLaunchKernelGGL(mse_kernel<float>, dim3(*nblk), dim3(256), 0, s, static_cast<const float*>(y),
+                       static_cast<const float*>(t), dy_f32, static_cast<float*>(dy_act), part, count / 8, inv_denom, k);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ column sums
+constexpr int kColRows = 64;
+int colsum_chunks(int rows) { return (rows + kColRows - 1) / kColRows; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void colsum_kernel(const T* __restrict__ x, int64_t ld, int rows,
+                                                     int cols, float* __restrict__ part) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= cols) return;
+  const int r0 = blockIdx.y * kColRows, r1 = min(rows, r0 + kColRows);
+  float s = 0.f;
+  for (int r = r0; r < r1; ++r) s += to_f<T>(x[int64_t(r) * ld + c]);
+  part[int64_t(blockIdx.y) * cols + c] = s;
+}
+
+hipError_t colsum_partial(int xtype, const void* x, int64_t ld, int rows, int cols, float* part,
+                          int* nchunk, hipStream_t s) {
+  *nchunk = colsum_chunks(rows);
+  if (rows == 0 || cols == 0) return hipSuccess;
+  dim3 grid((cols + 255) / 256, *nchunk);
+  if (xtype == XT_BF16)
+    hipLaunchKernelGGL(colsum_kernel<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t*>(x), ld, rows, cols, part);
+  else
+    hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(x), ld, rows, cols, part);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restrict__ part, int nparts,
+                                                           int64_t stride, int cols,
+                                                           float* __restrict__ out, int beta) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= cols) return;
+  float s = 0.f;
+  for (int p = 0; p < nparts; ++p) s += part[int64_t(p) * stride + c];
+  out[c] = beta ? out[c] + s : s;
+}
+
+hipError_t sum_partials(const float* part, int nparts, int64_t stride, int cols, float* out,
+                        int beta, hipStream_t s) {
+  if (cols == 0) return hipSuccess;
+  hipLaunchKernelGGL(sum_partials_kernel, dim3((cols + 255) / 256), dim3(256), 0, s, part, nparts,
+                     stride, cols, out, beta);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ RMSProp
+__global__ __launch_bounds__(256) void rmsprop_kernel(float* __restrict__ w, const float* __restrict__ g,
+                                                      float* __restrict__ ms, bf16_t* __restrict__ wl,
+                                                      int64_t n, float lr, float decay, float eps) {
+  const float keep = decay, mix = 1.0f - decay;
+  const int64_t n4 = n / 4;
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += stride) {
+    float4 wv = reinterpret_cast<float4*>(w)[i];
+    const float4 gv = reinterpret_cast<const float4*>(g)[i];
+    float4 mv = reinterpret_cast<float4*>(ms)[i];
+    mv.x = keep * mv.x + mix * gv.x * gv.x;
+    mv.y = keep * mv.y + mix * gv.y * gv.y;
+    mv.z = keep * mv.z + mix * gv.z * gv.z;
+    mv.w = keep * mv.w + mix * gv.w * gv.w;
+    wv.x -= lr * gv.x / (sqrtf(mv.x) + eps);
+    wv.y -= lr * gv.y / (sqrtf(mv.y) + eps);
+    wv.z -= lr * gv.z / (sqrtf(mv.z) + eps);
+    wv.w -= lr * gv.w / (sqrtf(mv.w) + eps);
+    reinterpret_cast<float4*>(ms)[i] = mv;
+    reinterpret_cast<float4*>(w)[i] = wv;
+    if (wl) {
+      uint2 o;
+      o.x = uint32_t(f2bf(wv.x)) | (uint32_t(f2bf(wv.y)) << 16);
+      o.y = uint32_t(f2bf(wv.z)) | (uint32_t(f2bf(wv.w)) << 16);
+      reinterpret_cast<uint2*>(wl)[i] = o;
+    }
+  }
+  // tail (n % 4 elements)
+  for (int64_t i = n4 * 4 + int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) {
+    const float gv = g[i];
+    const float mv = keep * ms[i] + mix * gv * gv;
+    const float wv = w[i] - lr * gv / (sqrtf(mv) + eps);
+    ms[i] = mv;
+    w[i] = wv;
+    if (wl) wl[i] = f2bf(wv);
+  }
+}
+
+hipError_t rmsprop(float* w, const float* g, float* ms, void* w_lowp, int64_t n, float lr,
+                   float decay, float eps, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t n4 = (n + 3) / 4;
+  const int64_t want = (n4 + 255) / 256;
+  const int blocks = int(want < 256 * 32 ? want : 256 * 32);
+  hipLaunchKernelGGL(rmsprop_kernel, dim3(blocks), dim3(256), 0, s, w, g, ms,
+                     static_cast<bf16_t*>(w_lowp), n, lr, decay, eps);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ src,
+                                                      bf16_t* __restrict__ dst, int64_t n) {
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) dst[i] = f2bf(src[i]);
+}
+
+hipError_t to_bf16(const float* src, void* dst, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  const int blocks = int(want < 256 * 32 ? want : 256 * 32);
+  hipLaunchKernelGGL(to_bf16_kernel, dim3(blocks), dim3(256), 0, s, src, static_cast<bf16_t*>(dst), n);
+  return hipGetLastError();
+}
+
+}  // namespace gp

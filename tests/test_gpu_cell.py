@@ -1,0 +1,156 @@
+"""Parity of the HIP cell step (through the C-ABI) with the oracle.
+
+Tolerances: relative L2 <= 1e-4 in fp32 mode and <= 2e-2 in bf16 mode with
+fp32 accumulation, per tensor for y, dx and every gradient, on the whole
+parameter vector for the updated weights and RMSProp state.
+"""
+import numpy as np
+import pytest
+
+from micro_pipelined_re_amd import configs, gpipe, inputs
+from oracle import transformer_cell as tc
+from tests.gpu_common import compare_step, make_cell, rel_l2, run_gpu, say, to_host
+
+pytestmark = pytest.mark.gpu
+
+FP32_TOL = 1e-4
+BF16_TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gpipe.lib()
+    yield
+
+
+def oracle_step(cfg, params, x, t, M, remat=True):
+    return tc.train_step(params, x, t, M, cfg.heads, cfg.causal, cfg.lr, cfg.decay, cfg.eps,
+                         ln_eps=cfg.ln_eps, remat=remat)
+
+
+def check(cfg, N=None, M=None, remat=True, tol=None, seed_params=None):
+    N = cfg.batch if N is None else N
+    M = cfg.micro if M is None else M
+    params = inputs.cell_params(cfg)
+    x, t = inputs.cell_data(cfg, batch=N)
+    gpu = run_gpu(cfg, params, x, t, N, M, remat=remat)
+    ref = oracle_step(cfg, params, x, t, M)
+    tol = tol or (FP32_TOL if cfg.precision == "fp32" else BF16_TOL)
+    report, bad = compare_step(gpu, ref, tol)
+    assert not bad, bad
+    return gpu, ref
+
+
+def test_tiny_fp32_saved_activations_match_oracle():
+    """No-remat run: every saved intermediate of every micro-batch vs the oracle's."""
+    import torch
+    cfg = configs.TINY
+    params = inputs.cell_params(cfg)
+    x, t = inputs.cell_data(cfg)
+    N, M = cfg.batch, cfg.micro
+    cell = make_cell(cfg, params)
+    gpu = run_gpu(cfg, params, x, t, N, M, remat=False, update=False, cell=cell)
+    ref = tc.cell_step(params, x, t, M, cfg.heads, cfg.causal, remat=False, record=True)
+    ws = cell._ws.cpu().numpy()
+    b, T, D, S, H = N // M, (N // M) * cfg.seq, cfg.d_model, cfg.seq, cfg.heads
+    lds = -(-S // 8) * 8
+    shapes = {"x": (T, D), "h1": (T, D), "qkv": (T, 3 * D), "ctx": (T, D), "x1": (T, D),
+              "h2": (T, D), "u": (T, cfg.d_ff), "g": (T, cfg.d_ff), "p": (b, H, S, lds)}
+    for m in range(M):
+        for l in range(cfg.layers):
+            sv = ref["forward_saved"][m][l]
+            for w, name in enumerate(gpipe.SAVED):
+                if name in ("st1", "st2") or (l == 0 and name == "x"):
+                    continue
+                off, nb = gpipe.gpipe_cell_saved_offset(cell.handle, N, M, False, m, l, w)
+                a = ws[off:off + nb].view(np.float32).reshape(shapes[name])
+                if name == "p":
+                    a = a[..., :S]
+                    r = sv["prob"]
+                else:
+                    r = sv[name].reshape(shapes[name])
+                e = rel_l2(a, r)
+                assert e < FP32_TOL, (m, l, name, e)
+            for w, name, key in ((2, "st1", ("mu1", "rstd1")), (8, "st2", ("mu2", "rstd2"))):
+                off, nb = gpipe.gpipe_cell_saved_offset(cell.handle, N, M, False, m, l, w)
+                a = ws[off:off + nb].view(np.float32).reshape(T, 2)
+                assert rel_l2(a[:, 0], sv[key[0]].ravel()) < 1e-4
+                assert rel_l2(a[:, 1], sv[key[1]].ravel()) < 1e-4
+    assert rel_l2(gpu["y"], ref["y"]) < FP32_TOL
+
+
+def test_tiny_fp32_step_and_update():
+    check(configs.TINY)
+
+
+def test_tiny_fp32_causal():
+    check(configs.TINY.with_(causal=True))
+
+
+@pytest.mark.parametrize("M", [1, 2, 8])
+def test_tiny_fp32_micro_batch_counts(M):
+    check(configs.TINY, M=M)
+
+
+def test_ragged_shapes_fp32():
+    """T = 3*40 = 120 tokens (not a tile multiple), S = 40 (ragged attention tiles)."""
+    cfg = configs.TINY.with_(name="ragged_fp32", seq=40, batch=6, micro=2, d_model=96, heads=6,
+                             d_ff=200)
+    check(cfg)
+    check(cfg.with_(causal=True))
+
+
+def test_odd_sequence_length_fp32():
+    """S = 13: rows of the attention matrices are not a multiple of 8."""
+    cfg = configs.TINY.with_(name="s13_fp32", seq=13, batch=4, micro=2, causal=True)
+    check(cfg)
+
+
+def test_single_token_sequences_fp32():
+    cfg = configs.TINY.with_(name="s1_fp32", seq=1, batch=8, micro=4)
+    check(cfg)
+
+
+def test_single_head_fp32():
+    cfg = configs.TINY.with_(name="h1_fp32", heads=1, seq=24, batch=4, micro=2)
+    check(cfg)
+
+
+def test_remat_bitwise_equals_stored_fp32():
+    cfg = configs.TINY.with_(causal=True)
+    params = inputs.cell_params(cfg)
+    x, t = inputs.cell_data(cfg)
+    a = run_gpu(cfg, params, x, t, cfg.batch, cfg.micro, remat=True, update=False)
+    b = run_gpu(cfg, params, x, t, cfg.batch, cfg.micro, remat=False, update=False)
+    assert np.array_equal(a["y"], b["y"])
+    assert np.array_equal(a["dx"], b["dx"])
+    assert a["loss"] == b["loss"]
+    for ga, gb in zip(a["grad"], b["grad"]):
+        for n in gpipe.TENSORS:
+            assert np.array_equal(ga[n], gb[n]), n
+
+
+def test_step_is_deterministic_bf16():
+    cfg = configs.SMALL.with_(name="small_2l", layers=2, batch=8, micro=4)
+    params = inputs.cell_params(cfg)
+    x, t = inputs.cell_data(cfg, batch=8)
+    a = run_gpu(cfg, params, x, t, 8, 4, update=False)
+    b = run_gpu(cfg, params, x, t, 8, 4, update=False, remat=False)
+    c = run_gpu(cfg, params, x, t, 8, 4, update=False)
+    for o in (b, c):
+        assert np.array_equal(a["y"], o["y"]) and np.array_equal(a["dx"], o["dx"])
+        for ga, gb in zip(a["grad"], o["grad"]):
+            for n in gpipe.TENSORS:
+                assert np.array_equal(ga[n], gb[n]), n
+
+
+def test_small_bf16_reduced():
+    """The small cell's layer shapes (D=512, H=8, F=2048, S=128) at 2 layers, N=8, M=4."""
+    check(configs.SMALL.with_(name="small_2l", layers=2, batch=8, micro=4))
+
+
+def test_small_bf16_causal_reduced():
+    check(configs.SMALL.with_(name="small_2l_causal", layers=2, batch=4, micro=2, causal=True))

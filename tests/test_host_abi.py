@@ -1,0 +1,219 @@
+"""Host logic of the C-ABI library, on the CPU: exports, layout, planner, partition, errors.
+
+No device work is launched here.
+"""
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+from micro_pipelined_re_amd import configs, gpipe, inputs
+from oracle.partition import partition_bruteforce
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "gpipe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gpipe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gpipe.lib()
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(gpipe.EXPORTS) == names
+
+
+def test_status_strings():
+    assert gpipe.gpipe_status_string(0) == "ok"
+    assert "memory" in gpipe.gpipe_status_string(2)
+
+
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.SMALL, configs.CELL_2048, configs.MEMORY_4096])
+def test_param_layout_matches_documented_order(cfg):
+    h = gpipe.gpipe_cell_create(cfg.layers, cfg.d_model, cfg.heads, cfg.d_ff, cfg.seq,
+                                cfg.causal, gpipe.GPIPE_BF16)
+    try:
+        n = gpipe.gpipe_cell_param_count(h)
+        assert n == cfg.param_count()
+        shapes = inputs.param_shapes(cfg.d_model, cfg.d_ff)
+        expect = 0
+        for l in range(cfg.layers):
+            for t, name in enumerate(gpipe.TENSORS):
+                off, cnt = gpipe.gpipe_cell_param_offset(h, l, t)
+                assert off == expect and cnt == int(np.prod(shapes[name]))
+                assert off % 8 == 0
+                expect += cnt
+        assert expect == n
+        assert tuple(gpipe.TENSORS) == inputs.PARAM_NAMES
+    finally:
+        gpipe.gpipe_cell_destroy(h)
+
+
+def test_param_counts_of_the_workloads():
+    # tiny: 2 * (4*64^2 + 2*64*256 + 9*64 + 256) = 99,968
+    assert configs.TINY.param_count() == 99968
+    assert configs.CELL_2048.param_count() == 402_866_176
+    assert abs(configs.MEMORY_4096.param_count() - 9.666e9) < 1e7
+
+
+def saved_set_bytes_formula(cfg, n, m, eb):
+    """Per micro-batch set: L * T * ((8D + H*S' + 2F) * eb + 16) bytes, S' = S rounded to 8."""
+    b = n // m
+    t = b * cfg.seq
+    lds = -(-cfg.seq // 8) * 8
+    return cfg.layers * t * ((8 * cfg.d_model + cfg.heads * lds + 2 * cfg.d_ff) * eb + 16)
+
+
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.SMALL, configs.CELL_2048, configs.MEMORY_4096])
+def test_workspace_tracks_the_activation_bound(cfg):
+    """Remat keeps one micro-batch's saved set, no-remat keeps M of them.
+
+    The pages put re-materialized peak activations at O(N + L/K * N/M): the N
+    term is the boundary (the caller's x / y), the second term one saved set.
+    """
+    eb = 4 if cfg.precision == "fp32" else 2
+    prec = gpipe.GPIPE_FP32 if eb == 4 else gpipe.GPIPE_BF16
+    h = gpipe.gpipe_cell_create(cfg.layers, cfg.d_model, cfg.heads, cfg.d_ff, cfg.seq,
+                                cfg.causal, prec)
+    try:
+        n, m = cfg.batch, cfg.micro
+        remat = gpipe.gpipe_cell_workspace_bytes(h, n, m, True)
+        keep = gpipe.gpipe_cell_workspace_bytes(h, n, m, False)
+        formula = saved_set_bytes_formula(cfg, n, m, eb)
+        set_bytes = (gpipe.gpipe_cell_saved_offset(h, n, m, False, 1, 0, 1)[0]
+                     - gpipe.gpipe_cell_saved_offset(h, n, m, False, 0, 0, 1)[0])
+        # the set is the formula up to 256-byte padding of its 11 tensors per layer
+        assert formula <= set_bytes <= formula + 256 * 11 * cfg.layers
+        yre = -(-(n // m) * cfg.seq * cfg.d_model * eb // 256) * 256
+        assert keep - remat == (m - 1) * set_bytes - yre
+        # transients are one layer's worth, small next to the set for the big cells
+        transient = remat - set_bytes
+        assert transient > 0
+        if cfg.layers >= 6:
+            assert transient < 0.5 * set_bytes
+        # halving the micro-batch halves the set
+        if n % (2 * m) == 0:
+            assert gpipe.gpipe_cell_workspace_bytes(h, n, 2 * m, True) < 0.6 * remat + transient
+    finally:
+        gpipe.gpipe_cell_destroy(h)
+
+
+def test_memory_cell_at_one_micro_batch_exceeds_one_gpu():
+    """48 layers of d_model 4096, N=32: M=1 needs ~309 GB of saved activations (> 288 GB)."""
+    cfg = configs.MEMORY_4096
+    h = gpipe.gpipe_cell_create(cfg.layers, cfg.d_model, cfg.heads, cfg.d_ff, cfg.seq, False,
+                                gpipe.GPIPE_BF16)
+    try:
+        m1 = gpipe.gpipe_cell_workspace_bytes(h, 32, 1, True)
+        m32 = gpipe.gpipe_cell_workspace_bytes(h, 32, 32, True)
+        assert m1 > 288e9
+        assert 9.5e9 < m32 < 12e9
+    finally:
+        gpipe.gpipe_cell_destroy(h)
+
+
+def test_create_validation():
+    E = gpipe.GpipeError
+    with pytest.raises(E) as e:
+        gpipe.gpipe_cell_create(2, 64, 3, 256, 32, 0, 0)       # heads do not divide d_model
+    assert e.value.code == 1
+    with pytest.raises(E) as e:
+        gpipe.gpipe_cell_create(0, 64, 4, 256, 32, 0, 0)
+    assert e.value.code == 1
+    with pytest.raises(E) as e:
+        gpipe.gpipe_cell_create(2, 60, 4, 256, 32, 0, 0)       # d_model not a multiple of 8
+    assert e.value.code == 4
+    with pytest.raises(E) as e:
+        gpipe.gpipe_cell_create(2, 64, 4, 256, 5000, 0, 0)     # seq too long
+    assert e.value.code == 4
+
+
+def test_workspace_and_step_validation_without_device():
+    h = gpipe.gpipe_cell_create(2, 64, 4, 256, 32, 0, gpipe.GPIPE_FP32)
+    try:
+        with pytest.raises(gpipe.GpipeError):
+            gpipe.gpipe_cell_workspace_bytes(h, 8, 3, True)      # N % M != 0
+        with pytest.raises(gpipe.GpipeError):
+            gpipe.gpipe_cell_workspace_bytes(h, 0, 1, True)
+        # stepping an unbound cell is a state error; nothing is launched
+        with pytest.raises(gpipe.GpipeError) as e:
+            gpipe.gpipe_cell_step(h, 16, 16, 16, None, 8, 4, True, 16, 1 << 30, 0, 16)
+        assert e.value.code == 5
+        with pytest.raises(gpipe.GpipeError) as e:
+            gpipe.gpipe_apply_update(h, 1e-3, 0.9, 1e-8, 0)
+        assert e.value.code == 5
+        # bf16 cells need the low-precision copy; fp32 cells must not get one
+        with pytest.raises(gpipe.GpipeError):
+            gpipe.gpipe_cell_bind(h, 256, 256, 256, 256)
+        # misaligned pointers are rejected
+        with pytest.raises(gpipe.GpipeError):
+            gpipe.gpipe_cell_bind(h, 258, None, 256, 256)
+        gpipe.gpipe_cell_bind(h, 256, None, 512, 768)            # host-side bookkeeping only
+        ws = gpipe.gpipe_cell_workspace_bytes(h, 8, 4, True)
+        with pytest.raises(gpipe.GpipeError) as e:               # workspace too small
+            gpipe.gpipe_cell_step(h, 16, 16, 16, None, 8, 4, True, 16, ws - 1, 0, 16)
+        assert e.value.code == 1
+        with pytest.raises(gpipe.GpipeError) as e:               # misaligned x
+            gpipe.gpipe_cell_step(h, 18, 16, 16, None, 8, 4, True, 16, ws, 0, 16)
+        assert e.value.code == 1
+        with pytest.raises(gpipe.GpipeError):                    # bad decay
+            gpipe.gpipe_apply_update(h, 1e-3, 1.0, 1e-8, 0)
+    finally:
+        gpipe.gpipe_cell_destroy(h)
+
+
+def test_saved_offsets_are_disjoint_and_inside_the_workspace():
+    cfg = configs.TINY
+    h = gpipe.gpipe_cell_create(cfg.layers, cfg.d_model, cfg.heads, cfg.d_ff, cfg.seq, 0, 0)
+    try:
+        for remat in (True, False):
+            ws = gpipe.gpipe_cell_workspace_bytes(h, 8, 4, remat)
+            spans = []
+            for m in range(1 if remat else 4):
+                for l in range(cfg.layers):
+                    for w in range(len(gpipe.SAVED)):
+                        if l == 0 and w == 0:
+                            with pytest.raises(gpipe.GpipeError):
+                                gpipe.gpipe_cell_saved_offset(h, 8, 4, remat, m, l, w)
+                            continue
+                        off, nb = gpipe.gpipe_cell_saved_offset(h, 8, 4, remat, m, l, w)
+                        assert off % 256 == 0 and off + nb <= ws
+                        spans.append((off, off + nb))
+            spans.sort()
+            for a, b in zip(spans, spans[1:]):
+                assert a[1] <= b[0]
+    finally:
+        gpipe.gpipe_cell_destroy(h)
+
+
+def test_partition_matches_bruteforce_oracle():
+    rng = random.Random(7)
+    for _ in range(300):
+        L = rng.randint(1, 12)
+        K = rng.randint(1, L)
+        costs = [float(rng.randint(0, 20)) for _ in range(L)]
+        b, v = gpipe.gpipe_partition(costs, K)
+        ob, ov = partition_bruteforce(costs, K)
+        assert b == ob, (costs, K)
+        assert v == pytest.approx(float(ov), rel=1e-12, abs=1e-12)
+
+
+def test_partition_uniform_and_large():
+    b, v = gpipe.gpipe_partition([1.0] * 128, 16)
+    assert b == list(range(0, 129, 8)) and v == 0.0
+    costs = [float(c) for c in np.random.default_rng(1).integers(1, 100, 200)]
+    b, v = gpipe.gpipe_partition(costs, 16)
+    assert b[0] == 0 and b[-1] == 200 and all(x < y for x, y in zip(b, b[1:]))
+
+
+def test_partition_validation():
+    for costs, k in [([1.0, 2.0], 3), ([1.0, -1.0], 1), ([float("nan")], 1), ([1.0], 0)]:
+        with pytest.raises(gpipe.GpipeError):
+            gpipe.gpipe_partition(costs, k)
