@@ -181,6 +181,33 @@ gpipe_status gpipe_apply_update(gpipe_cell *cell, float lr, float decay, float e
  * not finite. */
 gpipe_status gpipe_partition(const double *costs, int L, int K, int *bounds, double *variance);
 
+/* Kernel roles of a step, for gpipe_cell_profile.  One role is one kind of
+ * launch (e.g. the FFN up-projection GEMM of the forward and re-materialized
+ * passes); its launches all have the same shape within a step. */
+typedef enum {
+  GPIPE_ROLE_LN1_FWD = 0, GPIPE_ROLE_QKV_FWD, GPIPE_ROLE_SCORES_FWD, GPIPE_ROLE_SOFTMAX_FWD,
+  GPIPE_ROLE_PV_FWD, GPIPE_ROLE_OUT_FWD, GPIPE_ROLE_LN2_FWD, GPIPE_ROLE_FFN1_FWD,
+  GPIPE_ROLE_FFN2_FWD, GPIPE_ROLE_MSE, GPIPE_ROLE_FFN2_DGRAD, GPIPE_ROLE_FFN2_WGRAD,
+  GPIPE_ROLE_FFN1_DGRAD, GPIPE_ROLE_FFN1_WGRAD, GPIPE_ROLE_LN2_BWD, GPIPE_ROLE_OUT_DGRAD,
+  GPIPE_ROLE_OUT_WGRAD, GPIPE_ROLE_DP, GPIPE_ROLE_DV, GPIPE_ROLE_SOFTMAX_BWD, GPIPE_ROLE_DQ,
+  GPIPE_ROLE_DK, GPIPE_ROLE_QKV_DGRAD, GPIPE_ROLE_QKV_WGRAD, GPIPE_ROLE_LN1_BWD,
+  GPIPE_ROLE_BIAS_GRAD, GPIPE_ROLE_NORM_GRAD, GPIPE_ROLE_LOSS_REDUCE, GPIPE_ROLE_RMSPROP,
+  GPIPE_N_ROLES
+} gpipe_role;
+
+/* Event timing of selected kernel roles.  With bit r of role_mask set, every
+ * later launch of role r by gpipe_cell_step / gpipe_apply_update is
+ * bracketed by two HIP events recorded on the call's stream.  Calling it
+ * again (any mask, 0 switches timing off) discards what was recorded.  The
+ * cell creates the events it needs and destroys them in gpipe_cell_destroy.
+ * Errors: GPIPE_ERR_DEVICE if events cannot be created. */
+gpipe_status gpipe_cell_profile(gpipe_cell *cell, unsigned long long role_mask);
+
+/* Total milliseconds and number of launches of `role` recorded since the last
+ * gpipe_cell_profile call; waits for the recorded events to complete. */
+gpipe_status gpipe_cell_profile_read(gpipe_cell *cell, int role, double *total_ms,
+                                     long long *launches);
+
 /* Static string naming a status code. */
 const char *gpipe_status_string(gpipe_status status);
 

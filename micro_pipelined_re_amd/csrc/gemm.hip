@@ -20,6 +20,7 @@
 // consecutive instructions, k = 4*(lane/16)+s (fp32); A and B use the same
 // lane->k assignment, which is all the contraction needs.
 // Accumulator layout (16x16 block): lane l holds column l%16, rows 4*(l/16)+v.
+#include "../../include/gpipe.h"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -162,7 +163,8 @@ struct TileLoader {
   }
 };
 
-template <typename T, int LA, int LB, int EPI>
+// ROLE only names the instance (one kernel symbol per role of the step).
+template <typename T, int LA, int LB, int EPI, int ROLE>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams g) {
   using Tl = Tile<T>;
   constexpr int BM = Tl::BM, BN = Tl::BN, BK = Tl::BK, LDP = Tl::BK + Tl::PAD;
@@ -293,35 +295,50 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams g) {
   }
 }
 
-template <typename T, int LA, int LB, int EPI>
+template <typename T, int LA, int LB, int EPI, int ROLE>
 static hipError_t launch(const GemmParams& g, int batch, hipStream_t s) {
   using Tl = Tile<T>;
   const int tiles = ((g.M + Tl::BM - 1) / Tl::BM) * ((g.N + Tl::BN - 1) / Tl::BN);
   if (tiles == 0 || batch == 0) return hipSuccess;
   dim3 grid(tiles, 1, batch);
-  hipLaunchKernelGGL((gemm_kernel<T, LA, LB, EPI>), grid, dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((gemm_kernel<T, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 
+// Operand layouts and epilogue of every GEMM role of the step.
+//   forward linears          C = A W^T (+ epilogue)          A: K, B: K
+//   input-gradient products  dA = dC W                      A: K, B: MN
+//   weight gradients         G (+)= dC^T A  (over tokens)    A: MN, B: MN
 template <typename T>
-static hipError_t dispatch(int la, int lb, int epi, const GemmParams& g, int batch, hipStream_t s) {
-#define GP_CASE(LA_, LB_, EPI_) \
-  if (la == LA_ && lb == LB_ && epi == EPI_) return launch<T, LA_, LB_, EPI_>(g, batch, s);
-  GP_CASE(LAY_K, LAY_K, EPI_BIAS)
-  GP_CASE(LAY_K, LAY_K, EPI_BIAS_RESID)
-  GP_CASE(LAY_K, LAY_K, EPI_BIAS_GELU)
-  GP_CASE(LAY_K, LAY_K, EPI_STORE_F32)
-  GP_CASE(LAY_K, LAY_MN, EPI_STORE)
-  GP_CASE(LAY_K, LAY_MN, EPI_GELU_BWD)
-  GP_CASE(LAY_K, LAY_MN, EPI_STORE_F32)
-  GP_CASE(LAY_MN, LAY_MN, EPI_ACC_F32)
-  GP_CASE(LAY_MN, LAY_MN, EPI_STORE)
-#undef GP_CASE
-  return hipErrorInvalidValue;
+static hipError_t dispatch(int role, const GemmParams& g, int batch, hipStream_t s) {
+#define GP_ROLE(R, LA_, LB_, EPI_) \
+  case R: return launch<T, LA_, LB_, EPI_, R>(g, batch, s);
+  switch (role) {
+    GP_ROLE(GPIPE_ROLE_QKV_FWD, LAY_K, LAY_K, EPI_BIAS)
+    GP_ROLE(GPIPE_ROLE_SCORES_FWD, LAY_K, LAY_K, EPI_STORE_F32)
+    GP_ROLE(GPIPE_ROLE_PV_FWD, LAY_K, LAY_MN, EPI_STORE)
+    GP_ROLE(GPIPE_ROLE_OUT_FWD, LAY_K, LAY_K, EPI_BIAS_RESID)
+    GP_ROLE(GPIPE_ROLE_FFN1_FWD, LAY_K, LAY_K, EPI_BIAS_GELU)
+    GP_ROLE(GPIPE_ROLE_FFN2_FWD, LAY_K, LAY_K, EPI_BIAS_RESID)
+    GP_ROLE(GPIPE_ROLE_FFN2_DGRAD, LAY_K, LAY_MN, EPI_GELU_BWD)
+    GP_ROLE(GPIPE_ROLE_FFN2_WGRAD, LAY_MN, LAY_MN, EPI_ACC_F32)
+    GP_ROLE(GPIPE_ROLE_FFN1_DGRAD, LAY_K, LAY_MN, EPI_STORE_F32)
+    GP_ROLE(GPIPE_ROLE_FFN1_WGRAD, LAY_MN, LAY_MN, EPI_ACC_F32)
+    GP_ROLE(GPIPE_ROLE_OUT_DGRAD, LAY_K, LAY_MN, EPI_STORE)
+    GP_ROLE(GPIPE_ROLE_OUT_WGRAD, LAY_MN, LAY_MN, EPI_ACC_F32)
+    GP_ROLE(GPIPE_ROLE_DP, LAY_K, LAY_K, EPI_STORE_F32)
+    GP_ROLE(GPIPE_ROLE_DV, LAY_MN, LAY_MN, EPI_STORE)
+    GP_ROLE(GPIPE_ROLE_DQ, LAY_K, LAY_MN, EPI_STORE)
+    GP_ROLE(GPIPE_ROLE_DK, LAY_MN, LAY_MN, EPI_STORE)
+    GP_ROLE(GPIPE_ROLE_QKV_DGRAD, LAY_K, LAY_MN, EPI_STORE_F32)
+    GP_ROLE(GPIPE_ROLE_QKV_WGRAD, LAY_MN, LAY_MN, EPI_ACC_F32)
+    default: return hipErrorInvalidValue;
+  }
+#undef GP_ROLE
 }
 
-hipError_t gemm(bool bf16, int la, int lb, int epi, const GemmParams& g, int batch, hipStream_t s) {
-  return bf16 ? dispatch<bf16_t>(la, lb, epi, g, batch, s) : dispatch<float>(la, lb, epi, g, batch, s);
+hipError_t gemm(bool bf16, int role, const GemmParams& g, int batch, hipStream_t s) {
+  return bf16 ? dispatch<bf16_t>(role, g, batch, s) : dispatch<float>(role, g, batch, s);
 }
 
 int gemm_tile_m(bool bf16) { return bf16 ? Tile<bf16_t>::BM : Tile<float>::BM; }

@@ -32,6 +32,10 @@ struct gpipe_cell {
   float* grad;
   float* ms;
   bool bound;
+  // event timing of selected kernel roles (gpipe_cell_profile)
+  unsigned long long prof_mask = 0;
+  std::vector<hipEvent_t> prof_events;  // pool, pairs (start, end), reused
+  std::vector<int> prof_roles;          // role of each recorded pair
 };
 
 namespace {
@@ -128,8 +132,36 @@ inline size_t saved_at(const Plan& p, int set, int layer, int which) {
     if ((expr) != hipSuccess) return GPIPE_ERR_DEVICE; \
   } while (0)
 
+// Next (start, end) event pair of the cell's pool for a launch of `role`.
+bool prof_pair(gpipe_cell* c, int role, hipEvent_t* e0, hipEvent_t* e1) {
+  const size_t k = 2 * c->prof_roles.size();
+  while (c->prof_events.size() < k + 2) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return false;
+    c->prof_events.push_back(e);
+  }
+  *e0 = c->prof_events[k];
+  *e1 = c->prof_events[k + 1];
+  c->prof_roles.push_back(role);
+  return true;
+}
+
+// Launches `expr`; when `role` is being timed, brackets it with two events
+// recorded on the context's stream.
+#define GP_RUN(ctx, role, expr)                                                         \
+  do {                                                                                 \
+    hipEvent_t e0_ = nullptr, e1_ = nullptr;                                           \
+    if ((ctx).prof && (((ctx).prof->prof_mask >> (role)) & 1ull)) {                   \
+      if (!prof_pair((ctx).prof, (role), &e0_, &e1_)) return GPIPE_ERR_DEVICE;          \
+      if (hipEventRecord(e0_, (ctx).s) != hipSuccess) return GPIPE_ERR_DEVICE;         \
+    }                                                                                  \
+    if ((expr) != hipSuccess) return GPIPE_ERR_DEVICE;                                 \
+    if (e1_ && hipEventRecord(e1_, (ctx).s) != hipSuccess) return GPIPE_ERR_DEVICE;    \
+  } while (0)
+
 struct Ctx {
   const gpipe_cell* c;
+  gpipe_cell* prof;  // non-null when some role is being timed
   const Plan* p;
   char* ws;
   hipStream_t s;
@@ -160,7 +192,7 @@ GemmParams gp0() {
 }
 
 // Plain 2-D product, no batching.
-hipError_t mm(const Ctx& x, int la, int lb, int epi, int M, int N, int K, const void* A, int64_t lda,
+hipError_t mm(const Ctx& x, int role, int M, int N, int K, const void* A, int64_t lda,
               const void* B, int64_t ldb, void* C, int64_t ldc, const float* bias = nullptr,
               const void* R = nullptr, int64_t ldr = 0, void* U = nullptr, int64_t ldu = 0,
               int beta = 0) {
@@ -170,7 +202,7 @@ hipError_t mm(const Ctx& x, int la, int lb, int epi, int M, int N, int K, const 
   g.B = B; g.ldb = ldb;
   g.C = C; g.ldc = ldc;
   g.bias = bias; g.R = R; g.ldr = ldr; g.U = U; g.ldu = ldu; g.beta = beta;
-  return gemm(x.bf16, la, lb, epi, g, 1, x.s);
+  return gemm(x.bf16, role, g, 1, x.s);
 }
 
 // Batched over (sequence b, head h) of one micro-batch.
@@ -178,7 +210,7 @@ struct Bat {
   const void* ptr;
   int64_t ld, sb, sh;
 };
-hipError_t bmm(const Ctx& x, int la, int lb, int epi, int M, int N, int K, Bat A, Bat B, Bat C,
+hipError_t bmm(const Ctx& x, int role, int M, int N, int K, Bat A, Bat B, Bat C,
                int causal, float alpha) {
   GemmParams g = gp0();
   g.M = M; g.N = N; g.K = K;
@@ -188,7 +220,7 @@ hipError_t bmm(const Ctx& x, int la, int lb, int epi, int M, int N, int K, Bat A
   g.hdiv = x.c->H;
   g.causal = causal;
   g.alpha = alpha;
-  return gemm(x.bf16, la, lb, epi, g, x.p->B * x.c->H, x.s);
+  return gemm(x.bf16, role, g, x.p->B * x.c->H, x.s);
 }
 
 // Column sums of x [T, cols] added (beta) or stored into out[cols].
@@ -220,9 +252,9 @@ gpipe_status layer_forward(const Ctx& x, int set, int l, const void* xin, void* 
   void* g = x.at(saved_at(p, set, l, GPIPE_SAVED_G));
   float* scores = static_cast<float*>(x.at(p.scores));
 
-  GP_CHECK(layernorm_fwd(x.bf16, xin, h1, st1, x.wf32(l, GPIPE_LN1_G), x.wf32(l, GPIPE_LN1_B), T, D,
+  GP_RUN(x, GPIPE_ROLE_LN1_FWD, layernorm_fwd(x.bf16, xin, h1, st1, x.wf32(l, GPIPE_LN1_G), x.wf32(l, GPIPE_LN1_B), T, D,
                          c->ln_eps, x.s));
-  GP_CHECK(mm(x, LAY_K, LAY_K, EPI_BIAS, T, 3 * D, D, h1, D, x.wmat(l, GPIPE_W_QKV), D, qkv, 3 * D,
+  GP_RUN(x, GPIPE_ROLE_QKV_FWD, mm(x, GPIPE_ROLE_QKV_FWD, T, 3 * D, D, h1, D, x.wmat(l, GPIPE_W_QKV), D, qkv, 3 * D,
               x.wf32(l, GPIPE_B_QKV)));
   const int64_t sq = int64_t(S) * 3 * D;       // per-sequence stride inside qkv
   const int64_t sp = int64_t(H) * S * ldS;     // per-sequence stride inside P / scores
@@ -231,18 +263,18 @@ gpipe_status layer_forward(const Ctx& x, int set, int l, const void* xin, void* 
   Bat SC{scores, ldS, sp, int64_t(S) * ldS};
   Bat PP{P, ldS, sp, int64_t(S) * ldS};
   Bat CX{ctx, D, int64_t(S) * D, dh};
-  GP_CHECK(bmm(x, LAY_K, LAY_K, EPI_STORE_F32, S, S, dh, Q, K, SC,
+  GP_RUN(x, GPIPE_ROLE_SCORES_FWD, bmm(x, GPIPE_ROLE_SCORES_FWD, S, S, dh, Q, K, SC,
                c->causal ? CAUSAL_SKIP_UPPER : CAUSAL_NONE, scale));
-  GP_CHECK(softmax_fwd(x.bf16, scores, P, int64_t(p.B) * H * S, S, ldS, c->causal, x.s));
-  GP_CHECK(bmm(x, LAY_K, LAY_MN, EPI_STORE, S, dh, S, PP, V, CX,
+  GP_RUN(x, GPIPE_ROLE_SOFTMAX_FWD, softmax_fwd(x.bf16, scores, P, int64_t(p.B) * H * S, S, ldS, c->causal, x.s));
+  GP_RUN(x, GPIPE_ROLE_PV_FWD, bmm(x, GPIPE_ROLE_PV_FWD, S, dh, S, PP, V, CX,
                c->causal ? CAUSAL_K_UPTO_M : CAUSAL_NONE, 1.0f));
-  GP_CHECK(mm(x, LAY_K, LAY_K, EPI_BIAS_RESID, T, D, D, ctx, D, x.wmat(l, GPIPE_W_O), D, x1, D,
+  GP_RUN(x, GPIPE_ROLE_OUT_FWD, mm(x, GPIPE_ROLE_OUT_FWD, T, D, D, ctx, D, x.wmat(l, GPIPE_W_O), D, x1, D,
               x.wf32(l, GPIPE_B_O), xin, D));
-  GP_CHECK(layernorm_fwd(x.bf16, x1, h2, st2, x.wf32(l, GPIPE_LN2_G), x.wf32(l, GPIPE_LN2_B), T, D,
+  GP_RUN(x, GPIPE_ROLE_LN2_FWD, layernorm_fwd(x.bf16, x1, h2, st2, x.wf32(l, GPIPE_LN2_G), x.wf32(l, GPIPE_LN2_B), T, D,
                          c->ln_eps, x.s));
-  GP_CHECK(mm(x, LAY_K, LAY_K, EPI_BIAS_GELU, T, F, D, h2, D, x.wmat(l, GPIPE_W_1), D, g, F,
+  GP_RUN(x, GPIPE_ROLE_FFN1_FWD, mm(x, GPIPE_ROLE_FFN1_FWD, T, F, D, h2, D, x.wmat(l, GPIPE_W_1), D, g, F,
               x.wf32(l, GPIPE_B_1), nullptr, 0, u, F));
-  GP_CHECK(mm(x, LAY_K, LAY_K, EPI_BIAS_RESID, T, D, F, g, F, x.wmat(l, GPIPE_W_2), F, xout, D,
+  GP_RUN(x, GPIPE_ROLE_FFN2_FWD, mm(x, GPIPE_ROLE_FFN2_FWD, T, D, F, g, F, x.wmat(l, GPIPE_W_2), F, xout, D,
               x.wf32(l, GPIPE_B_2), x1, D));
   return GPIPE_OK;
 }
@@ -291,26 +323,26 @@ gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int b
   float* lnpart = static_cast<float*>(x.at(p.lnpart));
 
   // FFN: y = x1 + g W2^T + b2,  g = gelu(u),  u = h2 W1^T + b1
-  GP_CHECK(mm(x, LAY_K, LAY_MN, EPI_GELU_BWD, T, F, D, a0, D, x.wmat(l, GPIPE_W_2), F, du, F,
+  GP_RUN(x, GPIPE_ROLE_FFN2_DGRAD, mm(x, GPIPE_ROLE_FFN2_DGRAD, T, F, D, a0, D, x.wmat(l, GPIPE_W_2), F, du, F,
               nullptr, nullptr, 0, u, F));
-  GP_CHECK(mm(x, LAY_MN, LAY_MN, EPI_ACC_F32, D, F, T, a0, D, g, F, x.grad(l, GPIPE_W_2), F,
+  GP_RUN(x, GPIPE_ROLE_FFN2_WGRAD, mm(x, GPIPE_ROLE_FFN2_WGRAD, D, F, T, a0, D, g, F, x.grad(l, GPIPE_W_2), F,
               nullptr, nullptr, 0, nullptr, 0, beta));
-  GP_CHECK(colsum_into(x, XT_F32, r0, D, D, x.grad(l, GPIPE_B_2), beta));
-  GP_CHECK(mm(x, LAY_K, LAY_MN, EPI_STORE_F32, T, D, F, du, F, x.wmat(l, GPIPE_W_1), D, dm, D));
-  GP_CHECK(mm(x, LAY_MN, LAY_MN, EPI_ACC_F32, F, D, T, du, F, h2, D, x.grad(l, GPIPE_W_1), D,
+  GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r0, D, D, x.grad(l, GPIPE_B_2), beta));
+  GP_RUN(x, GPIPE_ROLE_FFN1_DGRAD, mm(x, GPIPE_ROLE_FFN1_DGRAD, T, D, F, du, F, x.wmat(l, GPIPE_W_1), D, dm, D));
+  GP_RUN(x, GPIPE_ROLE_FFN1_WGRAD, mm(x, GPIPE_ROLE_FFN1_WGRAD, F, D, T, du, F, h2, D, x.grad(l, GPIPE_W_1), D,
               nullptr, nullptr, 0, nullptr, 0, beta));
-  GP_CHECK(colsum_into(x, xt_act, du, F, F, x.grad(l, GPIPE_B_1), beta));
+  GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, du, F, F, x.grad(l, GPIPE_B_1), beta));
   int nblk = 0;
-  GP_CHECK(layernorm_bwd(bf, dm, x1, st2, x.wf32(l, GPIPE_LN2_G), r0, r1, a1, lnpart, T, D, &nblk,
+  GP_RUN(x, GPIPE_ROLE_LN2_BWD, layernorm_bwd(bf, dm, x1, st2, x.wf32(l, GPIPE_LN2_G), r0, r1, a1, lnpart, T, D, &nblk,
                          x.s));
-  GP_CHECK(sum_partials(lnpart, nblk, 2 * D, D, x.grad(l, GPIPE_LN2_G), beta, x.s));
-  GP_CHECK(sum_partials(lnpart + D, nblk, 2 * D, D, x.grad(l, GPIPE_LN2_B), beta, x.s));
+  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(lnpart, nblk, 2 * D, D, x.grad(l, GPIPE_LN2_G), beta, x.s));
+  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(lnpart + D, nblk, 2 * D, D, x.grad(l, GPIPE_LN2_B), beta, x.s));
 
   // attention: x1 = x + ctx Wo^T + bo
-  GP_CHECK(mm(x, LAY_K, LAY_MN, EPI_STORE, T, D, D, a1, D, x.wmat(l, GPIPE_W_O), D, dctx, D));
-  GP_CHECK(mm(x, LAY_MN, LAY_MN, EPI_ACC_F32, D, D, T, a1, D, ctx, D, x.grad(l, GPIPE_W_O), D,
+  GP_RUN(x, GPIPE_ROLE_OUT_DGRAD, mm(x, GPIPE_ROLE_OUT_DGRAD, T, D, D, a1, D, x.wmat(l, GPIPE_W_O), D, dctx, D));
+  GP_RUN(x, GPIPE_ROLE_OUT_WGRAD, mm(x, GPIPE_ROLE_OUT_WGRAD, D, D, T, a1, D, ctx, D, x.grad(l, GPIPE_W_O), D,
               nullptr, nullptr, 0, nullptr, 0, beta));
-  GP_CHECK(colsum_into(x, XT_F32, r1, D, D, x.grad(l, GPIPE_B_O), beta));
+  GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r1, D, D, x.grad(l, GPIPE_B_O), beta));
   const int64_t sq = int64_t(S) * 3 * D;
   const int64_t sp = int64_t(H) * S * ldS;
   const int64_t sd = int64_t(S) * D;
@@ -320,26 +352,26 @@ gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int b
   Bat PP{P, ldS, sp, int64_t(S) * ldS}, DP{dP, ldS, sp, int64_t(S) * ldS}, DS{dS, ldS, sp, int64_t(S) * ldS};
   Bat DC{dctx, D, sd, dh};
   const int cz = c->causal;
-  GP_CHECK(bmm(x, LAY_K, LAY_K, EPI_STORE_F32, S, S, dh, DC, V, DP,
+  GP_RUN(x, GPIPE_ROLE_DP, bmm(x, GPIPE_ROLE_DP, S, S, dh, DC, V, DP,
                cz ? CAUSAL_SKIP_UPPER : CAUSAL_NONE, 1.0f));
-  GP_CHECK(bmm(x, LAY_MN, LAY_MN, EPI_STORE, S, dh, S, PP, DC, dV,
+  GP_RUN(x, GPIPE_ROLE_DV, bmm(x, GPIPE_ROLE_DV, S, dh, S, PP, DC, dV,
                cz ? CAUSAL_K_FROM_M : CAUSAL_NONE, 1.0f));
-  GP_CHECK(softmax_bwd(bf, P, dP, dS, int64_t(p.B) * H * S, S, ldS, cz, scale, x.s));
-  GP_CHECK(bmm(x, LAY_K, LAY_MN, EPI_STORE, S, dh, S, DS, K, dQ,
+  GP_RUN(x, GPIPE_ROLE_SOFTMAX_BWD, softmax_bwd(bf, P, dP, dS, int64_t(p.B) * H * S, S, ldS, cz, scale, x.s));
+  GP_RUN(x, GPIPE_ROLE_DQ, bmm(x, GPIPE_ROLE_DQ, S, dh, S, DS, K, dQ,
                cz ? CAUSAL_K_UPTO_M : CAUSAL_NONE, 1.0f));
-  GP_CHECK(bmm(x, LAY_MN, LAY_MN, EPI_STORE, S, dh, S, DS, Q, dK,
+  GP_RUN(x, GPIPE_ROLE_DK, bmm(x, GPIPE_ROLE_DK, S, dh, S, DS, Q, dK,
                cz ? CAUSAL_K_FROM_M : CAUSAL_NONE, 1.0f));
 
   // qkv = h1 Wqkv^T + bqkv,  h1 = LN1(x)
-  GP_CHECK(mm(x, LAY_K, LAY_MN, EPI_STORE_F32, T, D, 3 * D, dqkv, 3 * D, x.wmat(l, GPIPE_W_QKV), D,
+  GP_RUN(x, GPIPE_ROLE_QKV_DGRAD, mm(x, GPIPE_ROLE_QKV_DGRAD, T, D, 3 * D, dqkv, 3 * D, x.wmat(l, GPIPE_W_QKV), D,
               dm, D));
-  GP_CHECK(mm(x, LAY_MN, LAY_MN, EPI_ACC_F32, 3 * D, D, T, dqkv, 3 * D, h1, D,
+  GP_RUN(x, GPIPE_ROLE_QKV_WGRAD, mm(x, GPIPE_ROLE_QKV_WGRAD, 3 * D, D, T, dqkv, 3 * D, h1, D,
               x.grad(l, GPIPE_W_QKV), D, nullptr, nullptr, 0, nullptr, 0, beta));
-  GP_CHECK(colsum_into(x, xt_act, dqkv, 3 * D, 3 * D, x.grad(l, GPIPE_B_QKV), beta));
-  GP_CHECK(layernorm_bwd(bf, dm, xin, st1, x.wf32(l, GPIPE_LN1_G), r1, r0, dx_out ? dx_out : a0,
+  GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, dqkv, 3 * D, 3 * D, x.grad(l, GPIPE_B_QKV), beta));
+  GP_RUN(x, GPIPE_ROLE_LN1_BWD, layernorm_bwd(bf, dm, xin, st1, x.wf32(l, GPIPE_LN1_G), r1, r0, dx_out ? dx_out : a0,
                          lnpart, T, D, &nblk, x.s));
-  GP_CHECK(sum_partials(lnpart, nblk, 2 * D, D, x.grad(l, GPIPE_LN1_G), beta, x.s));
-  GP_CHECK(sum_partials(lnpart + D, nblk, 2 * D, D, x.grad(l, GPIPE_LN1_B), beta, x.s));
+  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(lnpart, nblk, 2 * D, D, x.grad(l, GPIPE_LN1_G), beta, x.s));
+  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(lnpart + D, nblk, 2 * D, D, x.grad(l, GPIPE_LN1_B), beta, x.s));
   return GPIPE_OK;
 }
 
@@ -389,6 +421,8 @@ gpipe_status gpipe_cell_create(int layers, int d_model, int heads, int d_ff, int
 }
 
 gpipe_status gpipe_cell_destroy(gpipe_cell* c) {
+  if (c)
+    for (hipEvent_t e : c->prof_events) (void)hipEventDestroy(e);
   delete c;
   return GPIPE_OK;
 }
@@ -462,8 +496,8 @@ gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, v
   if (!aligned16(x) || !aligned16(target) || !aligned16(y) || (dx && !aligned16(dx)) ||
       !aligned16(workspace))
     return GPIPE_ERR_INVALID;
-  Ctx cx{c, &p, static_cast<char*>(workspace), static_cast<hipStream_t>(stream),
-         c->prec == GPIPE_BF16};
+  Ctx cx{c, c->prof_mask ? c : nullptr, &p, static_cast<char*>(workspace),
+         static_cast<hipStream_t>(stream), c->prec == GPIPE_BF16};
   const size_t mb = size_t(p.T) * c->D;  // elements per micro-batch
   const float inv_denom = float(1.0 / (double(N) * c->S * c->D));
   float* msepart = static_cast<float*>(cx.at(p.msepart));
@@ -486,7 +520,7 @@ gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, v
       ym = yre;
     }
     int nblk = 0;
-    GP_CHECK(mse_fwd_bwd(cx.bf16, ym, cx.act(target, m * mb), static_cast<float*>(cx.at(p.r0)),
+    GP_RUN(cx, GPIPE_ROLE_MSE, mse_fwd_bwd(cx.bf16, ym, cx.act(target, m * mb), static_cast<float*>(cx.at(p.r0)),
                          cx.at(p.a0), msepart + size_t(m) * p.mse_nblk, int64_t(mb), inv_denom,
                          &nblk, cx.s));
     for (int l = c->L - 1; l >= 0; --l) {
@@ -496,7 +530,7 @@ gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, v
       if (st != GPIPE_OK) return st;
     }
   }
-  GP_CHECK(sum_partials(msepart, M * p.mse_nblk, 1, 1, loss_dev, 0, cx.s));
+  GP_RUN(cx, GPIPE_ROLE_LOSS_REDUCE, sum_partials(msepart, M * p.mse_nblk, 1, 1, loss_dev, 0, cx.s));
   return GPIPE_OK;
 }
 
@@ -506,8 +540,36 @@ gpipe_status gpipe_apply_update(gpipe_cell* c, float lr, float decay, float eps,
   if (!(decay >= 0.f && decay < 1.f) || !(lr >= 0.f) || !(eps >= 0.f) || !isfinite(lr) ||
       !isfinite(eps))
     return GPIPE_ERR_INVALID;
-  GP_CHECK(rmsprop(c->master, c->grad, c->ms, c->prec == GPIPE_BF16 ? c->w_lowp : nullptr,
-                   int64_t(c->n_params), lr, decay, eps, static_cast<hipStream_t>(stream)));
+  Ctx cx{c, c->prof_mask ? c : nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream),
+         c->prec == GPIPE_BF16};
+  GP_RUN(cx, GPIPE_ROLE_RMSPROP,
+         rmsprop(c->master, c->grad, c->ms, c->prec == GPIPE_BF16 ? c->w_lowp : nullptr,
+                 int64_t(c->n_params), lr, decay, eps, cx.s));
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_cell_profile(gpipe_cell* c, unsigned long long role_mask) {
+  if (!c) return GPIPE_ERR_INVALID;
+  c->prof_mask = role_mask;
+  c->prof_roles.clear();
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_cell_profile_read(gpipe_cell* c, int role, double* total_ms, long long* launches) {
+  if (!c || !total_ms || !launches || role < 0 || role >= GPIPE_N_ROLES) return GPIPE_ERR_INVALID;
+  double t = 0.0;
+  long long n = 0;
+  for (size_t i = 0; i < c->prof_roles.size(); ++i) {
+    if (c->prof_roles[i] != role) continue;
+    float ms = 0.f;
+    if (hipEventSynchronize(c->prof_events[2 * i + 1]) != hipSuccess) return GPIPE_ERR_DEVICE;
+    if (hipEventElapsedTime(&ms, c->prof_events[2 * i], c->prof_events[2 * i + 1]) != hipSuccess)
+      return GPIPE_ERR_DEVICE;
+    t += ms;
+    ++n;
+  }
+  *total_ms = t;
+  *launches = n;
   return GPIPE_OK;
 }
 

@@ -40,7 +40,9 @@ struct GemmParams {
   int beta;
 };
 
-hipError_t gemm(bool bf16, int la, int lb, int epi, const GemmParams& g, int batch, hipStream_t s);
+// role: a gpipe_role of a GEMM launch; it fixes the operand layouts and the
+// epilogue (see gemm.hip) and names the kernel instance in profiles.
+hipError_t gemm(bool bf16, int role, const GemmParams& g, int batch, hipStream_t s);
 int gemm_tile_m(bool bf16);
 
 // ---------------------------------------------------------------- row kernels

@@ -22,7 +22,13 @@ SAVED = ("x", "h1", "st1", "qkv", "p", "ctx", "x1", "h2", "st2", "u", "g")
 EXPORTS = ("gpipe_cell_create", "gpipe_cell_destroy", "gpipe_cell_param_count",
            "gpipe_cell_param_offset", "gpipe_cell_bind", "gpipe_cell_sync_lowp",
            "gpipe_cell_workspace_bytes", "gpipe_cell_saved_offset", "gpipe_cell_step",
-           "gpipe_apply_update", "gpipe_partition", "gpipe_status_string")
+           "gpipe_apply_update", "gpipe_partition", "gpipe_status_string",
+           "gpipe_cell_profile", "gpipe_cell_profile_read")
+
+ROLES = ("ln1_fwd", "qkv_fwd", "scores_fwd", "softmax_fwd", "pv_fwd", "out_fwd", "ln2_fwd",
+         "ffn1_fwd", "ffn2_fwd", "mse", "ffn2_dgrad", "ffn2_wgrad", "ffn1_dgrad", "ffn1_wgrad",
+         "ln2_bwd", "out_dgrad", "out_wgrad", "dp", "dv", "softmax_bwd", "dq", "dk", "qkv_dgrad",
+         "qkv_wgrad", "ln1_bwd", "bias_grad", "norm_grad", "loss_reduce", "rmsprop")
 
 
 class GpipeError(RuntimeError):
@@ -57,6 +63,9 @@ def lib() -> ctypes.CDLL:
             "gpipe_apply_update": [_vp, ctypes.c_float, ctypes.c_float, ctypes.c_float, _vp],
             "gpipe_partition": [ctypes.POINTER(ctypes.c_double), _i, _i, ctypes.POINTER(_i),
                                 ctypes.POINTER(ctypes.c_double)],
+            "gpipe_cell_profile": [_vp, ctypes.c_ulonglong],
+            "gpipe_cell_profile_read": [_vp, _i, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_longlong)],
         }
         for name, argtypes in sig.items():
             f = getattr(L, name)
@@ -168,6 +177,17 @@ def gpipe_partition(costs, K: int):
            lib().gpipe_partition(c.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), int(c.size), K,
                                  bounds, ctypes.byref(var)))
     return list(bounds), var.value
+
+
+def gpipe_cell_profile(cell, role_mask: int) -> None:
+    _check("gpipe_cell_profile", lib().gpipe_cell_profile(cell, role_mask))
+
+
+def gpipe_cell_profile_read(cell, role: int):
+    ms, n = ctypes.c_double(), ctypes.c_longlong()
+    _check("gpipe_cell_profile_read",
+           lib().gpipe_cell_profile_read(cell, role, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 # ---------------------------------------------------------------- convenience
