@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libgpipe_cell.so")
-SOURCES = ["gemm.hip", "rowops.hip", "gpipe_api.hip"]
+SOURCES = ["gemm.hip", "gemm_fwd.hip", "gemm_dgrad.hip", "gemm_wgrad.hip", "gemm_attn.hip",
+           "gemm_f32.hip", "rowops.hip", "gpipe_api.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

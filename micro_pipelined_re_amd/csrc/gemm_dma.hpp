@@ -1,0 +1,355 @@
+// bf16 GEMM with HBM -> LDS direct loads (gfx950 global_load_lds_dwordx4).
+//
+// No staging registers: each wave's load instruction writes 64 x 16 bytes to
+// a contiguous kilobyte of LDS (lane l at +16*l), and the global address each
+// lane fetches is chosen so that the kilobyte holds the tile in its swizzled
+// layout.  S LDS stages keep S-1 k-tiles in flight.
+//
+// Tile layouts in LDS (k-tile depth BK = 64 or 32):
+//   k-contiguous operand  [rows][BK]: rows of BK/8 16-byte chunks; chunk c of
+//       row r stored at position c ^ ((r ^ r>>3) & 7) (BK 64) or
+//       c ^ ((r >> 2) & 3) (BK 32); MFMA fragments are one ds_read_b128
+//       (16 rows x one chunk, conflict-free within each 8-lane phase).
+//   m-contiguous operand  [64 k][R]: rows of R elements in 32-byte granules,
+//       granule q of k-row r stored at q ^ (r & 7) (R >= 128) or q ^ (r & 3)
+//       (R = 64); fragments are two ds_read_b64_tr_b16: within a group of 16
+//       lanes, lane s points at (k0 + s/4, m0 + 4*(s%4)) and lane i receives
+//       the four k-rows k0..k0+3 of column m0 + i.
+// Rows past the operand's extent are read from its last row (valid memory;
+// those results are never stored).  k must be a multiple of 64.
+#pragma once
+#include "gemm_impl.hpp"
+
+namespace gp {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+
+__device__ __forceinline__ void dma16(const void* g, bf16_t* lds_block) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_block, 16, 0, 0);
+}
+
+// Workgroup barrier without a memory fence: the waves have already waited for
+// their own LDS loads (vmcnt), and a fence would also drain the loads of the
+// younger k-tiles still in flight.  The asm's memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+#define LPT_CHECK(lpt, stages) ((lpt) * ((stages) - 2) < 64)
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// granule swizzle of an m-contiguous tile with R elements per k-row
+template <int R>
+__device__ __forceinline__ int mn_off(int k, int m) {
+  constexpr int mask = (R >= 128) ? 7 : 3;
+  return k * R + ((((m >> 4) ^ (k & mask))) << 4) + (m & 15);
+}
+
+// element offset of (row, 16-byte chunk) in a swizzled k-contiguous tile
+template <int BK>
+__device__ __forceinline__ int kswz_off(int row, int chunk) {
+  if constexpr (BK == 64) return row * 64 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 3);
+  else return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3);
+}
+
+template <int ROWS, int BK, int LAY>
+struct DmaOperand {
+  static constexpr int ELEMS = ROWS * BK;          // per stage
+  static constexpr int KB_PER_STAGE = ELEMS * 2 / 1024;
+  static constexpr int PER_WAVE = KB_PER_STAGE / 4;  // load instructions per wave per stage
+  static_assert(PER_WAVE >= 1 && KB_PER_STAGE % 4 == 0, "tile too small for four waves");
+  int64_t off[PER_WAVE];  // element offsets of this lane's source (at k-tile 0)
+  int64_t kstep;          // element step per k-tile
+
+  __device__ __forceinline__ void init(int64_t ld, int row0, int rows_total, int kbeg, int wave,
+                                       int lane) {
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q) {
+      const int blk = q * 4 + wave;  // kilobyte of the stage this instruction fills
+      if constexpr (LAY == LAY_K) {
+        constexpr int CPR = BK / 8;          // chunks per row
+        constexpr int RPK = 1024 / (BK * 2); // rows per kilobyte
+        const int r = blk * RPK + lane / CPR;
+        const int p = lane % CPR;
+        const int c = (BK == 64) ? (p ^ ((r ^ (r >> 3)) & 7)) : (p ^ ((r >> 2) & 3));
+        const int gr = min(row0 + r, rows_total - 1);
+        off[q] = int64_t(gr) * ld + kbeg + c * 8;
+      } else {
+        constexpr int mask = (ROWS >= 128) ? 7 : 3;
+        const int byte = blk * 1024 + lane * 16;
+        const int kr = byte / (ROWS * 2);
+        const int within = byte % (ROWS * 2);
+        const int p = within >> 5, h = (within >> 4) & 1;
+        const int m = ((p ^ (kr & mask)) << 4) + h * 8;
+        const int gm = min(row0 + m, rows_total - 8);
+        off[q] = int64_t(kbeg + kr) * ld + gm;
+      }
+    }
+    kstep = (LAY == LAY_K) ? BK : int64_t(BK) * ld;
+  }
+
+  __device__ __forceinline__ void issue(const bf16_t* base, int kt, bf16_t* stage, int wave) const {
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q) dma16(base + off[q] + kt * kstep, stage + (q * 4 + wave) * 512);
+  }
+
+  // MFMA fragment (8 bf16, k = ks*32 + 8*(lane/16) + e) of tile rows row16 .. row16+15
+  __device__ __forceinline__ bf16x8_t frag(const bf16_t* stage, int row16, int lane, int ks) const {
+    if constexpr (LAY == LAY_K) {
+      const int r = row16 + (lane & 15);
+      return *reinterpret_cast<const bf16x8_t*>(stage + kswz_off<BK>(r, ks * 4 + (lane >> 4)));
+    } else {
+      const int s = lane & 15, g = lane >> 4;
+      const int k0 = ks * 32 + g * 8 + (s >> 2);
+      const int m = row16 + 4 * (s & 3);
+      const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4_t*)(stage + mn_off<ROWS>(k0, m)));
+      const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4_t*)(stage + mn_off<ROWS>(k0 + 4, m)));
+      typedef short short8_t __attribute__((ext_vector_type(8)));
+      const short8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+};
+
+// Waits until at most n (<= MAXN) younger k-tiles of LPT loads each are in flight.
+template <int LPT, int MAXN>
+__device__ __forceinline__ void wait_tiles(int n) {
+  if (n >= MAXN) {
+    wait_vmcnt<MAXN * LPT>();
+  } else if constexpr (MAXN > 0) {
+    wait_tiles<LPT, MAXN - 1>(n);
+  }
+}
+
+// Tile configuration of the direct-to-LDS kernel.
+template <int BM_, int BN_, int BK_, int STAGES_, int OCC_>
+struct DCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, OCC = OCC_;
+  static constexpr int WTM = BM / 2, WTN = BN / 2;
+  static constexpr int FM = WTM / 16, FN = WTN / 16;
+};
+
+// Epilogue of eight consecutive columns (col .. col+7) of one row, all in range.
+template <int EPI>
+__device__ __forceinline__ void epi_store8(const GemmParams& g, int row, int col, const float* a,
+                                           int64_t coff, float* P) {
+  if (P) {  // split-K partial sums
+    float* dst = P + int64_t(row) * g.N + col;
+    reinterpret_cast<float4*>(dst)[0] = make_float4(a[0], a[1], a[2], a[3]);
+    reinterpret_cast<float4*>(dst)[1] = make_float4(a[4], a[5], a[6], a[7]);
+    return;
+  }
+  const int64_t ci = coff + int64_t(row) * g.ldc + col;
+  float o[8];
+  if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_ACC_F32) {
+    float* dst = static_cast<float*>(g.C) + ci;
+    if (EPI == EPI_ACC_F32 && g.beta) {
+      const float4 c0 = reinterpret_cast<const float4*>(dst)[0];
+      const float4 c1 = reinterpret_cast<const float4*>(dst)[1];
+      o[0] = c0.x + a[0]; o[1] = c0.y + a[1]; o[2] = c0.z + a[2]; o[3] = c0.w + a[3];
+      o[4] = c1.x + a[4]; o[5] = c1.y + a[5]; o[6] = c1.z + a[6]; o[7] = c1.w + a[7];
+    } else {
+      const float k = (EPI == EPI_STORE_F32) ? g.alpha : 1.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = k * a[e];
+    }
+    reinterpret_cast<float4*>(dst)[0] = make_float4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<float4*>(dst)[1] = make_float4(o[4], o[5], o[6], o[7]);
+    return;
+  } else {
+    auto ld8 = [](const bf16_t* p, float* v) {
+      const uint4 u = *reinterpret_cast<const uint4*>(p);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    };
+    auto st8 = [](bf16_t* p, const float* v) {
+      uint4 u;
+      u.x = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
+      u.y = uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16);
+      u.z = uint32_t(f2bf(v[4])) | (uint32_t(f2bf(v[5])) << 16);
+      u.w = uint32_t(f2bf(v[6])) | (uint32_t(f2bf(v[7])) << 16);
+      *reinterpret_cast<uint4*>(p) = u;
+    };
+    float b[8];
+    if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU) {
+      const float4 b0 = reinterpret_cast<const float4*>(g.bias + col)[0];
+      const float4 b1 = reinterpret_cast<const float4*>(g.bias + col)[1];
+      b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w;
+      b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+    }
+    if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = g.alpha * a[e];
+    } else if constexpr (EPI == EPI_BIAS) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = a[e] + b[e];
+    } else if constexpr (EPI == EPI_BIAS_RESID) {
+      float r[8];
+      ld8(static_cast<const bf16_t*>(g.R) + int64_t(row) * g.ldr + col, r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = a[e] + b[e] + r[e];
+    } else if constexpr (EPI == EPI_BIAS_GELU) {
+      float u[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        u[e] = a[e] + b[e];
+        o[e] = gelu_f(u[e]);
+      }
+      st8(static_cast<bf16_t*>(g.U) + int64_t(row) * g.ldu + col, u);
+    } else if constexpr (EPI == EPI_GELU_BWD) {
+      float u[8];
+      ld8(static_cast<const bf16_t*>(g.U) + int64_t(row) * g.ldu + col, u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = a[e] * gelu_grad_f(u[e]);
+    }
+    st8(static_cast<bf16_t*>(g.C) + ci, o);
+  }
+}
+
+template <class C, int LA, int LB, int EPI, int ROLE>
+__global__ __launch_bounds__(kThreads, C::OCC) void gemm_dma_kernel(GemmParams g) {
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, STAGES = C::STAGES, FM = C::FM, FN = C::FN;
+  using OA = DmaOperand<BM, BK, LA>;
+  using OB = DmaOperand<BN, BK, LB>;
+  static_assert(LPT_CHECK(OA::PER_WAVE + OB::PER_WAVE, STAGES), "vmcnt range");
+  constexpr int LPT = OA::PER_WAVE + OB::PER_WAVE;  // load instructions per wave per k-tile
+  // pipeline stages; after the k loop the same memory holds the fp32 tile
+  constexpr int PIPE = STAGES * (BM + BN) * BK * 2, TP = BN + 4;  // TP: tile row pitch (floats)
+  constexpr int SMEM = (PIPE > BM * TP * 4) ? PIPE : BM * TP * 4;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[SMEM / 2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int z = blockIdx.z, zb = z / g.hdiv, zh = z % g.hdiv;
+  int kbeg, kend;
+  if (!causal_range(g, m0, n0, BM, BK, &kbeg, &kend)) return;
+  const int split = blockIdx.y;
+  if (gridDim.y > 1) {
+    kbeg = max(kbeg, split * g.kchunk);
+    kend = min(kend, (split + 1) * g.kchunk);
+  }
+  const bf16_t* A = static_cast<const bf16_t*>(g.A) + zb * g.sAb + zh * g.sAh;
+  const bf16_t* B = static_cast<const bf16_t*>(g.B) + zb * g.sBb + zh * g.sBh;
+  OA oa;
+  OB ob;
+  oa.init(g.lda, m0, g.M, kbeg, wave, lane);
+  ob.init(g.ldb, n0, g.N, kbeg, wave, lane);
+  auto sa = [&](int st) { return smem + st * (BM + BN) * BK; };
+  auto sb = [&](int st) { return smem + st * (BM + BN) * BK + BM * BK; };
+
+  floatx4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  const int wm0 = (wave >> 1) * C::WTM, wn0 = (wave & 1) * C::WTN;
+  const int nkt = kend > kbeg ? (kend - kbeg) / BK : 0;
+
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nkt) {
+      oa.issue(A, s, sa(s), wave);
+      ob.issue(B, s, sb(s), wave);
+    }
+  int st = 0;
+  for (int kt = 0; kt < nkt; ++kt) {
+    // tile kt must have landed; up to STAGES-2 younger tiles may still be in flight
+    wait_tiles<LPT, STAGES - 2>(min(STAGES - 2, nkt - 1 - kt));
+    barrier_nofence();
+    if (kt + STAGES - 1 < nkt) {
+      const int ns = (st + STAGES - 1) % STAGES;
+      oa.issue(A, kt + STAGES - 1, sa(ns), wave);
+      ob.issue(B, kt + STAGES - 1, sb(ns), wave);
+    }
+    const bf16_t* as = sa(st);
+    const bf16_t* bs = sb(st);
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      bf16x8_t af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = oa.frag(as, wm0 + i * 16, lane, ks);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = ob.frag(bs, wn0 + j * 16, lane, ks);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    st = (st + 1 == STAGES) ? 0 : st + 1;
+  }
+
+  // Epilogue through LDS: each wave writes its accumulators into a [BM][BN+4]
+  // fp32 tile (conflict-free: the four row groups of a write land 16 banks
+  // apart), then each thread takes 8 consecutive columns of a row and does
+  // 16-byte loads and stores.
+  barrier_nofence();
+  float* tile = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        tile[(wm0 + i * 16 + (lane >> 4) * 4 + v) * TP + wn0 + j * 16 + (lane & 15)] = acc[i][j][v];
+  barrier_nofence();
+  float* P = gridDim.y > 1 ? g.P + int64_t(split) * g.M * g.N : nullptr;
+  const int64_t coff = zb * g.sCb + zh * g.sCh;
+  constexpr int CH = BN / 8;  // 8-column chunks per row
+  for (int idx = tid; idx < BM * CH; idx += kThreads) {
+    const int r = idx / CH, c = (idx % CH) * 8;
+    const int row = m0 + r, col = n0 + c;
+    if (row >= g.M || col >= g.N) continue;
+    const float4 t0 = *reinterpret_cast<const float4*>(tile + r * TP + c);
+    const float4 t1 = *reinterpret_cast<const float4*>(tile + r * TP + c + 4);
+    const float a[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+    if (col + 8 <= g.N) {
+      epi_store8<EPI>(g, row, col, a, coff, P);
+    } else {
+      for (int e = 0; e < 8 && col + e < g.N; ++e) {
+        if (P) P[int64_t(row) * g.N + col + e] = a[e];
+        else epi_store<bf16_t, EPI>(g, row, col + e, a[e], coff);
+      }
+    }
+  }
+}
+
+// path 0: direct-to-LDS kernel with configuration DC; path 1: register-staged
+// kernel with tile RC (for k not a multiple of 64).
+template <class DC, class RC, int LA, int LB, int EPI, int ROLE>
+hipError_t launch_bf16(int path, const GemmParams& g, int batch, int splits, hipStream_t s) {
+  const int bm = path == 0 ? DC::BM : RC::BM, bn = path == 0 ? DC::BN : RC::BN;
+  const int tiles = ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
+  if (tiles == 0 || batch == 0) return hipSuccess;
+  const dim3 grid(tiles, splits, batch);
+  if (path == 0)
+    hipLaunchKernelGGL((gemm_dma_kernel<DC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<RC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t n = int64_t(g.M) * g.N;
+  const int64_t want = (n + 255) / 256;
+  const int blocks = int(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI>), dim3(blocks), dim3(256), 0, s, g, splits);
+  return hipGetLastError();
+}
+
+}  // namespace gp

@@ -64,7 +64,7 @@ struct Plan {
   size_t saved_bytes[GPIPE_N_SAVED];
   size_t layer_bytes, set_bytes;
   int nsets;
-  size_t yre, scores, ds, r0, r1, dm, a0, a1, dctx, du, dqkv, colpart, lnpart, msepart;
+  size_t yre, scores, ds, r0, r1, dm, a0, a1, dctx, du, dqkv, colpart, lnpart, msepart, splitk;
   int mse_nblk;
   size_t total;
 };
@@ -117,6 +117,16 @@ bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
   p->lnpart = take(size_t(layernorm_bwd_blocks(int(T))) * 2 * D * 4);
   p->mse_nblk = mse_blocks(int64_t(T) * int64_t(D));
   p->msepart = take(size_t(M) * size_t(p->mse_nblk) * 4);
+  // split-K partials of the largest split GEMM of a layer (none for fp32 cells)
+  const bool bf = c->prec == GPIPE_BF16;
+  const int Ti = int(T), Di = c->D, Fi = c->F;
+  const int shapes[][4] = {{GPIPE_ROLE_QKV_FWD, Ti, 3 * Di, Di}, {GPIPE_ROLE_OUT_FWD, Ti, Di, Di},
+                           {GPIPE_ROLE_FFN1_FWD, Ti, Fi, Di},     {GPIPE_ROLE_FFN2_FWD, Ti, Di, Fi},
+                           {GPIPE_ROLE_FFN2_DGRAD, Ti, Fi, Di},   {GPIPE_ROLE_FFN1_DGRAD, Ti, Di, Fi},
+                           {GPIPE_ROLE_OUT_DGRAD, Ti, Di, Di},    {GPIPE_ROLE_QKV_DGRAD, Ti, Di, 3 * Di}};
+  size_t sk = 0;
+  for (const auto& r : shapes) sk = std::max(sk, gemm_partial_floats(r[0], bf, r[1], r[2], r[3], 1));
+  p->splitk = take(sk * 4);
   p->total = o;
   return true;
 }
@@ -202,6 +212,7 @@ hipError_t mm(const Ctx& x, int role, int M, int N, int K, const void* A, int64_
   g.B = B; g.ldb = ldb;
   g.C = C; g.ldc = ldc;
   g.bias = bias; g.R = R; g.ldr = ldr; g.U = U; g.ldu = ldu; g.beta = beta;
+  g.P = static_cast<float*>(x.at(x.p->splitk));
   return gemm(x.bf16, role, g, 1, x.s);
 }
 
@@ -335,8 +346,8 @@ gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int b
   int nblk = 0;
   GP_RUN(x, GPIPE_ROLE_LN2_BWD, layernorm_bwd(bf, dm, x1, st2, x.wf32(l, GPIPE_LN2_G), r0, r1, a1, lnpart, T, D, &nblk,
                          x.s));
-  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(lnpart, nblk, 2 * D, D, x.grad(l, GPIPE_LN2_G), beta, x.s));
-  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(lnpart + D, nblk, 2 * D, D, x.grad(l, GPIPE_LN2_B), beta, x.s));
+  // gamma and beta are adjacent in the parameter layout: one pass over 2D columns
+  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(lnpart, nblk, 2 * D, 2 * D, x.grad(l, GPIPE_LN2_G), beta, x.s));
 
   // attention: x1 = x + ctx Wo^T + bo
   GP_RUN(x, GPIPE_ROLE_OUT_DGRAD, mm(x, GPIPE_ROLE_OUT_DGRAD, T, D, D, a1, D, x.wmat(l, GPIPE_W_O), D, dctx, D));
@@ -370,8 +381,7 @@ gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int b
   GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, dqkv, 3 * D, 3 * D, x.grad(l, GPIPE_B_QKV), beta));
   GP_RUN(x, GPIPE_ROLE_LN1_BWD, layernorm_bwd(bf, dm, xin, st1, x.wf32(l, GPIPE_LN1_G), r1, r0, dx_out ? dx_out : a0,
                          lnpart, T, D, &nblk, x.s));
-  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(lnpart, nblk, 2 * D, D, x.grad(l, GPIPE_LN1_G), beta, x.s));
-  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(lnpart + D, nblk, 2 * D, D, x.grad(l, GPIPE_LN1_B), beta, x.s));
+  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(lnpart, nblk, 2 * D, 2 * D, x.grad(l, GPIPE_LN1_G), beta, x.s));
   return GPIPE_OK;
 }
 

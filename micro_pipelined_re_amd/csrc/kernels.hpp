@@ -38,12 +38,23 @@ struct GemmParams {
   void* U; int64_t ldu;
   float alpha;
   int beta;
+  float* P;     // split-K partials [splits][M][N] (f32), required when the plan splits
+  int kchunk;   // split-K: k extent of one split (set by gemm())
 };
+
+// Macro tile and split-K chosen for one GEMM launch.
+struct GemmPlan {
+  int cfg;      // tile configuration (gemm_impl.hpp), -1 for the fp32 kernel
+  int splits;   // k-splits reduced in a fixed order by a second kernel
+  int kchunk;
+};
+GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch);
+// Floats of split-K partials the launch needs (0 if it does not split).
+size_t gemm_partial_floats(int role, bool bf16, int M, int N, int K, int batch);
 
 // role: a gpipe_role of a GEMM launch; it fixes the operand layouts and the
 // epilogue (see gemm.hip) and names the kernel instance in profiles.
 hipError_t gemm(bool bf16, int role, const GemmParams& g, int batch, hipStream_t s);
-int gemm_tile_m(bool bf16);
 
 // ---------------------------------------------------------------- row kernels
 // LayerNorm forward over rows of length D: y(act) = gamma*(x-mu)*rstd + beta, stats[2*row] = (mu, rstd).

@@ -398,18 +398,38 @@ hipError_t mse_fwd_bwd(bool bf16, const void* y, const void* t, float* dy_f32, v
 }
 
 // ------------------------------------------------------------ column sums
-constexpr int kColRows = 64;
+// A block covers 256 columns x kColRows rows: thread (g, c) sums 8 consecutive
+// columns over rows g, g+8, ... of the chunk; the 8 row groups are then added
+// in order through LDS.  Columns must be a multiple of 8.
+constexpr int kColRows = 128;
 int colsum_chunks(int rows) { return (rows + kColRows - 1) / kColRows; }
 
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_kernel(const T* __restrict__ x, int64_t ld, int rows,
                                                      int cols, float* __restrict__ part) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= cols) return;
+  __shared__ float red[8][257];
+  const int cg = threadIdx.x & 31, rg = threadIdx.x >> 5;
+  const int c0 = blockIdx.x * 256 + cg * 8;
   const int r0 = blockIdx.y * kColRows, r1 = min(rows, r0 + kColRows);
-  float s = 0.f;
-  for (int r = r0; r < r1; ++r) s += to_f<T>(x[int64_t(r) * ld + c]);
-  part[int64_t(blockIdx.y) * cols + c] = s;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (c0 < cols) {
+    for (int r = r0 + rg; r < r1; r += 8) {
+      float v[8];
+      load8<T>(x + int64_t(r) * ld + c0, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] += v[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rg][cg * 8 + e] = s[e];
+  __syncthreads();
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c < cols) {
+    float t = red[0][threadIdx.x];
+#pragma unroll
+    for (int g = 1; g < 8; ++g) t += red[g][threadIdx.x];
+    part[int64_t(blockIdx.y) * cols + c] = t;
+  }
 }
 
 hipError_t colsum_partial(int xtype, const void* x, int64_t ld, int rows, int cols, float* part,
@@ -424,21 +444,39 @@ hipError_t colsum_partial(int xtype, const void* x, int64_t ld, int rows, int co
   return hipGetLastError();
 }
 
+// out[c] (+)= sum_p part[p * stride + c].  CW columns per block, 256/CW
+// threads per column each summing every (256/CW)-th part, then a fixed-order
+// combination in LDS.
+template <int CW>
 __global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restrict__ part, int nparts,
                                                            int64_t stride, int cols,
                                                            float* __restrict__ out, int beta) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= cols) return;
+  constexpr int G = 256 / CW;
+  __shared__ float red[256];
+  const int cl = threadIdx.x % CW, pg = threadIdx.x / CW;
+  const int c = blockIdx.x * CW + cl;
   float s = 0.f;
-  for (int p = 0; p < nparts; ++p) s += part[int64_t(p) * stride + c];
-  out[c] = beta ? out[c] + s : s;
+  if (c < cols)
+    for (int p = pg; p < nparts; p += G) s += part[int64_t(p) * stride + c];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  // tree over the G groups of this column, fixed pairing
+  for (int h = G / 2; h > 0; h >>= 1) {
+    if (pg < h) red[pg * CW + cl] += red[(pg + h) * CW + cl];
+    __syncthreads();
+  }
+  if (pg == 0 && c < cols) out[c] = beta ? out[c] + red[cl] : red[cl];
 }
 
 hipError_t sum_partials(const float* part, int nparts, int64_t stride, int cols, float* out,
                         int beta, hipStream_t s) {
   if (cols == 0) return hipSuccess;
-  hipLaunchKernelGGL(sum_partials_kernel, dim3((cols + 255) / 256), dim3(256), 0, s, part, nparts,
-                     stride, cols, out, beta);
+  if (cols >= 32)
+    hipLaunchKernelGGL(sum_partials_kernel<32>, dim3((cols + 31) / 32), dim3(256), 0, s, part,
+                       nparts, stride, cols, out, beta);
+  else
+    hipLaunchKernelGGL(sum_partials_kernel<1>, dim3(cols), dim3(256), 0, s, part, nparts, stride,
+                       cols, out, beta);
   return hipGetLastError();
 }
 

@@ -215,13 +215,15 @@ def cast_params(params, dtype):
 
 
 def cell_step(params, x, t, micro, heads, causal, ln_eps=LN_EPS, remat=True,
-              dtype=np.float64, record=False):
+              dtype=np.float64, record=False, denom=None):
     """One GPipe training step of the cell without the update (phases 1 and 2).
 
     x, t: [N, S, D].  micro: M, must divide N.  remat=True drops the layer
     intermediates in the forward phase and rebuilds them per micro-batch in
     the backward phase; remat=False keeps every micro-batch's intermediates.
     Micro-batches are processed in order m = 0 .. M-1 in both phases.
+    denom is the loss normaliser, N*S*D of x unless given (a caller taking
+    some sequences of a larger mini-batch passes that mini-batch's N*S*D).
     Returns dict(y, loss, dx, grads) plus, if record, the forward phase's and
     the backward phase's intermediates for each micro-batch.
     """
@@ -232,7 +234,7 @@ def cell_step(params, x, t, micro, heads, causal, ln_eps=LN_EPS, remat=True,
     params = cast_params(params, dtype)
     x = np.asarray(x, dtype=dtype)
     t = np.asarray(t, dtype=dtype)
-    denom = x.size
+    denom = x.size if denom is None else denom
     y = np.empty_like(x)
     kept = []
     # phase 1: forward, keeping the boundary output (and, without remat, everything)

@@ -154,3 +154,54 @@ def test_small_bf16_reduced():
 
 def test_small_bf16_causal_reduced():
     check(configs.SMALL.with_(name="small_2l_causal", layers=2, batch=4, micro=2, causal=True))
+
+
+def test_ragged_shapes_bf16():
+    """bf16 tiles with ragged edges: T = 80, D = 96 (head_dim 24), F = 200, S = 40."""
+    cfg = configs.SMALL.with_(name="ragged_bf16", layers=2, d_model=96, heads=4, d_ff=200, seq=40,
+                              batch=4, micro=2)
+    check(cfg)
+    check(cfg.with_(causal=True))
+
+
+def test_small_bf16_full():
+    """The small cell as specified: 6 layers, N=64, M=8."""
+    check(configs.SMALL)
+
+
+def test_small_bf16_one_micro_batch_matches_eight():
+    """M=1 (the full-batch step) and M=8 agree with the oracle and with each other."""
+    cfg = configs.SMALL
+    params = inputs.cell_params(cfg)
+    x, t = inputs.cell_data(cfg)
+    g1 = run_gpu(cfg, params, x, t, cfg.batch, 1, update=False)
+    g8 = run_gpu(cfg, params, x, t, cfg.batch, 8, update=False)
+    # the tile / split-K plan depends on the rows per micro-batch, so the two runs
+    # sum in different orders: equal up to bf16 rounding, not bitwise
+    assert rel_l2(g1["y"], g8["y"]) < 1e-2
+    for a, b in zip(g1["grad"], g8["grad"]):
+        for n in gpipe.TENSORS:
+            assert rel_l2(a[n], b[n]) < 1e-2, n
+
+
+def test_cell_2048_layer_shapes_bf16():
+    """The 2048-wide causal cell's layers at their real micro-batch (2 sequences, 1024
+    tokens): two micro-batches, so every GEMM, split and tile is the one the
+    benchmark runs.  Oracle in float32 for time."""
+    cfg = configs.CELL_2048.with_(name="cell2048_n4", batch=4, micro=2)
+    params = inputs.cell_params(cfg)
+    x, t = inputs.cell_data(cfg, batch=4)
+    gpu = run_gpu(cfg, params, x, t, 4, 2)
+    ref = tc.train_step(params, x, t, 2, cfg.heads, cfg.causal, cfg.lr, cfg.decay, cfg.eps,
+                        dtype=np.float32)
+    report, bad = compare_step(gpu, ref, BF16_TOL)
+    assert not bad, bad
+
+
+def test_ragged_tiles_direct_lds_path_bf16():
+    """k extents multiples of 64 (the direct-to-LDS GEMM) with ragged M / N edges:
+    T = 192 rows per micro-batch, D = 320, F = 832, S = 192, head_dim 64."""
+    cfg = configs.SMALL.with_(name="dma_ragged_bf16", layers=2, d_model=320, heads=5, d_ff=832,
+                              seq=192, batch=2, micro=2)
+    check(cfg)
+    check(cfg.with_(causal=True))
