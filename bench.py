@@ -172,7 +172,13 @@ def main():
         ms_tot, cnt = gpipe.gpipe_cell_profile_read(cell.handle, r)
         if cnt:
             prof[name] = (ms_tot, cnt)
-    dominant = max(prof, key=lambda k: prof[k][0])
+    # the dominant kernel: the role with the most time whose launch is a single kernel
+    # (a split-K GEMM role is two kernels: the split products and their ordered sum)
+    def single_kernel(name):
+        if name not in work or name in ("bias_grad", "norm_grad", "loss_reduce"):
+            return False
+        return gpipe.gpipe_cell_gemm_plan(cell.handle, n, m, gpipe.ROLES.index(name))[2] <= 1
+    dominant = max((k for k in prof if single_kernel(k)), key=lambda k: prof[k][0])
     dom_idx = gpipe.ROLES.index(dominant)
 
     # timed region: K steps; the dominant role's launches are bracketed by events
@@ -207,6 +213,10 @@ def main():
         kind, per = work.get(name, (None, None))
         e = {"ms_per_step": round(ms_tot, 4), "launches_per_step": cnt,
              "avg_us": round(ms_tot / cnt * 1e3, 3)}
+        if name in gpipe.ROLES:
+            _, _, sp_ = gpipe.gpipe_cell_gemm_plan(cell.handle, n, m, gpipe.ROLES.index(name))
+            if sp_ > 1:
+                e["split_k"] = sp_
         if kind == "mfma":
             tf = per / (ms_tot / cnt * 1e-3) / 1e12
             e.update(tflops=round(tf, 1), frac_bf16_peak=round(tf / PEAK_BF16_TFLOPS, 4))
@@ -228,6 +238,8 @@ def main():
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
     roof["kernel"] = dominant
+    tm_, tn_, sp_ = gpipe.gpipe_cell_gemm_plan(cell.handle, n, m, dom_idx)
+    roof["kernel_tile"] = [tm_, tn_] if tm_ else None
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
     roof["work_per_launch"] = per
 

@@ -208,6 +208,14 @@ gpipe_status gpipe_cell_profile(gpipe_cell *cell, unsigned long long role_mask);
 gpipe_status gpipe_cell_profile_read(gpipe_cell *cell, int role, double *total_ms,
                                      long long *launches);
 
+/* The GEMM plan a role uses in gpipe_cell_step(N, M) of this cell: macro
+ * tile rows / columns and the number of k-splits (a split GEMM launches a
+ * second kernel that sums the splits in order).  For roles that are not
+ * GEMMs all three are 0.  Inspection only; host side, no device work.
+ * Errors: GPIPE_ERR_INVALID for bad N/M or role. */
+gpipe_status gpipe_cell_gemm_plan(const gpipe_cell *cell, int N, int M, int role, int *tile_m,
+                                  int *tile_n, int *splits);
+
 /* Static string naming a status code. */
 const char *gpipe_status_string(gpipe_status status);
 

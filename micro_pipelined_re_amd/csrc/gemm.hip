@@ -84,6 +84,9 @@ GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch) {
   return p;
 }
 
+int gemm_cfg_bm(int cfg) { return kCfgBM[cfg]; }
+int gemm_cfg_bn(int cfg) { return kCfgBN[cfg]; }
+
 size_t gemm_partial_floats(int role, bool bf16, int M, int N, int K, int batch) {
   const GemmPlan p = plan_gemm(role, bf16, M, N, K, batch);
   return p.splits > 1 ? size_t(p.splits) * M * N : 0;

@@ -37,6 +37,12 @@ __device__ __forceinline__ void dma16(const void* g, bf16_t* lds_block) {
 // compiler from moving LDS accesses across it.
 __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
 
+// Barrier after ordinary LDS writes: s_barrier alone does not wait for a
+// wave's outstanding LDS operations, so drain them (lgkmcnt) first.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 #define LPT_CHECK(lpt, stages) ((lpt) * ((stages) - 2) < 64)
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
@@ -300,7 +306,7 @@ __global__ __launch_bounds__(kThreads, C::OCC) void gemm_dma_kernel(GemmParams g
   // fp32 tile (conflict-free: the four row groups of a write land 16 banks
   // apart), then each thread takes 8 consecutive columns of a row and does
   // 16-byte loads and stores.
-  barrier_nofence();
+  barrier_lds();
   float* tile = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(kThreads, C::OCC) void gemm_dma_kernel(GemmParams g
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         tile[(wm0 + i * 16 + (lane >> 4) * 4 + v) * TP + wn0 + j * 16 + (lane & 15)] = acc[i][j][v];
-  barrier_nofence();
+  barrier_lds();
   float* P = gridDim.y > 1 ? g.P + int64_t(split) * g.M * g.N : nullptr;
   const int64_t coff = zb * g.sCb + zh * g.sCh;
   constexpr int CH = BN / 8;  // 8-column chunks per row

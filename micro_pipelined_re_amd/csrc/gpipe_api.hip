@@ -583,6 +583,47 @@ gpipe_status gpipe_cell_profile_read(gpipe_cell* c, int role, double* total_ms, 
   return GPIPE_OK;
 }
 
+gpipe_status gpipe_cell_gemm_plan(const gpipe_cell* c, int N, int M, int role, int* tile_m,
+                                  int* tile_n, int* splits) {
+  if (!c || !tile_m || !tile_n || !splits || role < 0 || role >= GPIPE_N_ROLES)
+    return GPIPE_ERR_INVALID;
+  Plan p;
+  if (!make_plan(c, N, M, 1, &p)) return GPIPE_ERR_INVALID;
+  const int T = p.T, D = c->D, F = c->F, S = c->S, dh = c->D / c->H, bh = p.B * c->H;
+  int mnk[4] = {0, 0, 0, 0};  // M, N, K, batch
+  switch (role) {
+    case GPIPE_ROLE_QKV_FWD: mnk[0] = T; mnk[1] = 3 * D; mnk[2] = D; break;
+    case GPIPE_ROLE_OUT_FWD: mnk[0] = T; mnk[1] = D; mnk[2] = D; break;
+    case GPIPE_ROLE_FFN1_FWD: mnk[0] = T; mnk[1] = F; mnk[2] = D; break;
+    case GPIPE_ROLE_FFN2_FWD: mnk[0] = T; mnk[1] = D; mnk[2] = F; break;
+    case GPIPE_ROLE_FFN2_DGRAD: mnk[0] = T; mnk[1] = F; mnk[2] = D; break;
+    case GPIPE_ROLE_FFN1_DGRAD: mnk[0] = T; mnk[1] = D; mnk[2] = F; break;
+    case GPIPE_ROLE_OUT_DGRAD: mnk[0] = T; mnk[1] = D; mnk[2] = D; break;
+    case GPIPE_ROLE_QKV_DGRAD: mnk[0] = T; mnk[1] = D; mnk[2] = 3 * D; break;
+    case GPIPE_ROLE_FFN2_WGRAD: mnk[0] = D; mnk[1] = F; mnk[2] = T; break;
+    case GPIPE_ROLE_FFN1_WGRAD: mnk[0] = F; mnk[1] = D; mnk[2] = T; break;
+    case GPIPE_ROLE_OUT_WGRAD: mnk[0] = D; mnk[1] = D; mnk[2] = T; break;
+    case GPIPE_ROLE_QKV_WGRAD: mnk[0] = 3 * D; mnk[1] = D; mnk[2] = T; break;
+    case GPIPE_ROLE_SCORES_FWD: case GPIPE_ROLE_DP: mnk[0] = S; mnk[1] = S; mnk[2] = dh; break;
+    case GPIPE_ROLE_PV_FWD: case GPIPE_ROLE_DV: case GPIPE_ROLE_DQ: case GPIPE_ROLE_DK:
+      mnk[0] = S; mnk[1] = dh; mnk[2] = S; break;
+    default:
+      *tile_m = *tile_n = *splits = 0;
+      return GPIPE_OK;
+  }
+  const bool attn = role == GPIPE_ROLE_SCORES_FWD || role == GPIPE_ROLE_DP || role == GPIPE_ROLE_PV_FWD ||
+                    role == GPIPE_ROLE_DV || role == GPIPE_ROLE_DQ || role == GPIPE_ROLE_DK;
+  const GemmPlan g = plan_gemm(role, c->prec == GPIPE_BF16, mnk[0], mnk[1], mnk[2], attn ? bh : 1);
+  if (g.cfg < 0) {  // fp32 kernel
+    *tile_m = *tile_n = 64;
+  } else {
+    *tile_m = gemm_cfg_bm(g.cfg);
+    *tile_n = gemm_cfg_bn(g.cfg);
+  }
+  *splits = g.splits;
+  return GPIPE_OK;
+}
+
 gpipe_status gpipe_partition(const double* costs, int L, int K, int* bounds, double* variance) {
   if (!costs || !bounds || L < 1 || K < 1 || K > L) return GPIPE_ERR_INVALID;
   for (int i = 0; i < L; ++i)

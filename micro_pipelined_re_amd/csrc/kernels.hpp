@@ -49,6 +49,8 @@ struct GemmPlan {
   int kchunk;
 };
 GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch);
+int gemm_cfg_bm(int cfg);
+int gemm_cfg_bn(int cfg);
 // Floats of split-K partials the launch needs (0 if it does not split).
 size_t gemm_partial_floats(int role, bool bf16, int M, int N, int K, int batch);
 

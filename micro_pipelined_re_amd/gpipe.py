@@ -23,7 +23,7 @@ EXPORTS = ("gpipe_cell_create", "gpipe_cell_destroy", "gpipe_cell_param_count",
            "gpipe_cell_param_offset", "gpipe_cell_bind", "gpipe_cell_sync_lowp",
            "gpipe_cell_workspace_bytes", "gpipe_cell_saved_offset", "gpipe_cell_step",
            "gpipe_apply_update", "gpipe_partition", "gpipe_status_string",
-           "gpipe_cell_profile", "gpipe_cell_profile_read")
+           "gpipe_cell_profile", "gpipe_cell_profile_read", "gpipe_cell_gemm_plan")
 
 ROLES = ("ln1_fwd", "qkv_fwd", "scores_fwd", "softmax_fwd", "pv_fwd", "out_fwd", "ln2_fwd",
          "ffn1_fwd", "ffn2_fwd", "mse", "ffn2_dgrad", "ffn2_wgrad", "ffn1_dgrad", "ffn1_wgrad",
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
             "gpipe_partition": [ctypes.POINTER(ctypes.c_double), _i, _i, ctypes.POINTER(_i),
                                 ctypes.POINTER(ctypes.c_double)],
             "gpipe_cell_profile": [_vp, ctypes.c_ulonglong],
+            "gpipe_cell_gemm_plan": [_vp, _i, _i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i),
+                                     ctypes.POINTER(_i)],
             "gpipe_cell_profile_read": [_vp, _i, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_longlong)],
         }
@@ -188,6 +190,14 @@ def gpipe_cell_profile_read(cell, role: int):
     _check("gpipe_cell_profile_read",
            lib().gpipe_cell_profile_read(cell, role, ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def gpipe_cell_gemm_plan(cell, N: int, M: int, role: int):
+    tm, tn, sp = _i(), _i(), _i()
+    _check("gpipe_cell_gemm_plan",
+           lib().gpipe_cell_gemm_plan(cell, N, M, role, ctypes.byref(tm), ctypes.byref(tn),
+                                      ctypes.byref(sp)))
+    return tm.value, tn.value, sp.value
 
 
 # ---------------------------------------------------------------- convenience
