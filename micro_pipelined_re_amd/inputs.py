@@ -111,3 +111,42 @@ def unflatten_params(flat: np.ndarray, n_layers: int, d_model: int, d_ff: int) -
         out.append(d)
     assert off == flat.size, (off, flat.size)
     return out
+
+
+# ---------------------------------------------------------------- convolutional cell
+CONV_NAMES = ("w1", "bn1_g", "bn1_b", "w2", "bn2_g", "bn2_b")
+_CONV_MATRIX_ID = {"w1": 10, "w2": 11}
+
+
+def conv_param_shapes(channels: int) -> dict:
+    c = channels
+    return {"w1": (c, 3, 3, c), "bn1_g": (c,), "bn1_b": (c,),
+            "w2": (c, 3, 3, c), "bn2_g": (c,), "bn2_b": (c,)}
+
+
+def conv_block_params(seed: int, block: int, channels: int, bf16: bool = False) -> dict:
+    """He-normal conv weights (std sqrt(2 / (9 C))), BN gamma 1, beta 0."""
+    std = float(np.sqrt(2.0 / (9 * channels)))
+    out = {}
+    for name, shape in conv_param_shapes(channels).items():
+        if name in _CONV_MATRIX_ID:
+            out[name] = normal(seed, block, _CONV_MATRIX_ID[name], shape, std, bf16)
+        elif name.endswith("_g"):
+            out[name] = np.ones(shape, np.float32)
+        else:
+            out[name] = np.zeros(shape, np.float32)
+    return out
+
+
+def conv_cell_params(cfg, bf16: bool | None = None) -> list:
+    bf = (cfg.precision == "bf16") if bf16 is None else bf16
+    return [conv_block_params(cfg.seed, l, cfg.channels, bf) for l in range(cfg.blocks)]
+
+
+def conv_cell_data(cfg, bf16: bool | None = None, batch: int | None = None):
+    """x and target [N, H, W, C] (NHWC), ~N(0, 1)."""
+    bf = (cfg.precision == "bf16") if bf16 is None else bf16
+    n = cfg.batch if batch is None else batch
+    shape = (n, cfg.height, cfg.width, cfg.channels)
+    return (normal(cfg.seed, _GROUP_DATA, 2, shape, 1.0, bf),
+            normal(cfg.seed, _GROUP_DATA, 3, shape, 1.0, bf))
