@@ -81,6 +81,53 @@ typedef enum {
   GPIPE_N_SAVED
 } gpipe_saved;
 
+/* ---------------------------------------------------------------------------
+ * Convolutional cells with micro-batch BatchNorm ("algorithm / BatchNorm
+ * handling": during training each micro-batch is normalised with its own
+ * statistics, and moving averages over the whole mini-batch are kept for
+ * evaluation).  A conv cell is `blocks` residual blocks
+ *     a = conv3x3(x, W1); r = ReLU(BN1(a)); z = conv3x3(r, W2); y = x + BN2(z)
+ * (pad 1, stride 1, no conv bias, BN eps 1e-5, biased variance), activations
+ * NHWC [N, H, W, C].  The same entry points as for Transformer cells apply
+ * (param_count, param_offset with gpipe_conv_tensor, bind, sync_lowp,
+ * workspace_bytes, saved_offset with gpipe_conv_saved, step, apply_update,
+ * gemm_plan); the step additionally updates the moving averages bound with
+ * gpipe_cell_bind_running once, after its forward phase, from the pooled
+ * micro-batch moments (mean = mean of the micro-batch means; variance = mean
+ * of (var_m + mu_m^2) minus mean^2, made unbiased with n/(n-1), n = N*H*W):
+ *     running <- momentum * running + (1 - momentum) * statistic.
+ * The re-materialized forward never touches them.
+ * ------------------------------------------------------------------------- */
+typedef enum {
+  GPIPE_CONV_W1 = 0, /* [C_out, 3, 3, C_in] */
+  GPIPE_CONV_BN1_G, GPIPE_CONV_BN1_B,
+  GPIPE_CONV_W2,
+  GPIPE_CONV_BN2_G, GPIPE_CONV_BN2_B,
+  GPIPE_CONV_N_TENSORS
+} gpipe_conv_tensor;
+
+typedef enum {
+  GPIPE_CONV_SAVED_X = 0, /* block input [P, C], P = (N/M)*H*W (block 0: the caller's x) */
+  GPIPE_CONV_SAVED_A,     /* conv1 output [P, C] */
+  GPIPE_CONV_SAVED_ST1,   /* BN1 (mean[C], rstd[C]) float32 */
+  GPIPE_CONV_SAVED_R,     /* ReLU(BN1(a)) [P, C] */
+  GPIPE_CONV_SAVED_Z,     /* conv2 output [P, C] */
+  GPIPE_CONV_SAVED_ST2,   /* BN2 (mean[C], rstd[C]) float32 */
+  GPIPE_CONV_N_SAVED
+} gpipe_conv_saved;
+
+/* Creates a conv cell.  Requirements: blocks, height, width > 0; channels a
+ * positive multiple of 8; 0 <= bn_momentum < 1.  Errors as for
+ * gpipe_cell_create. */
+gpipe_status gpipe_conv_cell_create(int blocks, int channels, int height, int width,
+                                    float bn_momentum, gpipe_precision prec, gpipe_cell **out);
+
+/* Binds the moving averages of a conv cell: float32 [blocks][2 BNs][mean[C], var[C]],
+ * 16-byte aligned, owned and initialised by the caller (for example mean 0,
+ * var 1).  Required before gpipe_cell_step on a conv cell.
+ * Errors: GPIPE_ERR_INVALID for a Transformer cell or a misaligned pointer. */
+gpipe_status gpipe_cell_bind_running(gpipe_cell *cell, float *running);
+
 /* Creates a cell of `layers` (= L/K) identical pre-LN Transformer layers:
  * x1 = x + MHA(LN1(x)), y = x1 + W2 GeLU(W1 LN2(x1) + b1) + b2, attention
  * scale 1/sqrt(d_model/heads), causal mask if `causal`, LayerNorm eps 1e-5,
@@ -192,6 +239,10 @@ typedef enum {
   GPIPE_ROLE_OUT_WGRAD, GPIPE_ROLE_DP, GPIPE_ROLE_DV, GPIPE_ROLE_SOFTMAX_BWD, GPIPE_ROLE_DQ,
   GPIPE_ROLE_DK, GPIPE_ROLE_QKV_DGRAD, GPIPE_ROLE_QKV_WGRAD, GPIPE_ROLE_LN1_BWD,
   GPIPE_ROLE_BIAS_GRAD, GPIPE_ROLE_NORM_GRAD, GPIPE_ROLE_LOSS_REDUCE, GPIPE_ROLE_RMSPROP,
+  /* convolutional cells */
+  GPIPE_ROLE_CONV_FWD, GPIPE_ROLE_CONV_DGRAD, GPIPE_ROLE_CONV_WGRAD, GPIPE_ROLE_IM2COL,
+  GPIPE_ROLE_COL2IM, GPIPE_ROLE_BN_STATS, GPIPE_ROLE_BN_APPLY, GPIPE_ROLE_BN_BWD,
+  GPIPE_ROLE_BN_RUNNING,
   GPIPE_N_ROLES
 } gpipe_role;
 

@@ -66,6 +66,16 @@ class ConvCellConfig:
     eps: float = 1e-8
     seed: int = 0
 
+    def param_count(self) -> int:
+        c = self.channels
+        return self.blocks * (2 * 9 * c * c + 4 * c)
+
+    def pixels(self) -> int:
+        return self.batch * self.height * self.width
+
+    def with_(self, **kw) -> "ConvCellConfig":
+        return replace(self, **kw)
+
 
 # Tiny fp32 cell: the small case every oracle check runs in seconds.
 TINY = CellConfig("tiny_fp32", layers=2, d_model=64, heads=4, d_ff=256, seq=32,
@@ -88,8 +98,14 @@ MEMORY_4096 = CellConfig("cell_d4096_L48", layers=48, d_model=4096, heads=32,
                          d_ff=16384, seq=1024, batch=32, micro=32, causal=False,
                          precision="bf16")
 
-# Convolutional cell with micro-batch BatchNorm.
+# Convolutional cells with micro-batch BatchNorm: a tiny fp32 case, a small
+# bf16 case whose GEMMs take the tiled MFMA path, and the throughput workload.
+CONV_TINY = ConvCellConfig("conv_tiny_fp32", blocks=2, channels=16, height=8, width=8,
+                           batch=8, micro=4, precision="fp32")
+CONV_SMALL = ConvCellConfig("conv_small_bf16", blocks=2, channels=64, height=16, width=16,
+                            batch=16, micro=4, precision="bf16")
 CONV_CELL = ConvCellConfig("conv_c256_b8", blocks=8, channels=256, height=32, width=32,
                            batch=256, micro=16, precision="bf16")
 
 ALL = {c.name: c for c in (TINY, SMALL, CELL_2048, MEMORY_4096)}
+CONV_ALL = {c.name: c for c in (CONV_TINY, CONV_SMALL, CONV_CELL)}

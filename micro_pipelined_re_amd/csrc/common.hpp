@@ -53,4 +53,45 @@ __device__ __forceinline__ float gelu_grad_f(float u) {
   return cdf + u * pdf;
 }
 
+// ------------------------------------------------------------ 8-element chunks
+template <typename T> __device__ __forceinline__ void load8(const T* p, float* v);
+template <> __device__ __forceinline__ void load8<float>(const float* p, float* v) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <> __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float* v) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <typename T> __device__ __forceinline__ void store8(T* p, const float* v);
+template <> __device__ __forceinline__ void store8<float>(float* p, const float* v) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+template <> __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float* v) {
+  uint4 a;
+  a.x = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
+  a.y = uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16);
+  a.z = uint32_t(f2bf(v[4])) | (uint32_t(f2bf(v[5])) << 16);
+  a.w = uint32_t(f2bf(v[6])) | (uint32_t(f2bf(v[7])) << 16);
+  *reinterpret_cast<uint4*>(p) = a;
+}
+
+// Sum over the 256 threads of a block, fixed order; every thread gets the result.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 }  // namespace gp

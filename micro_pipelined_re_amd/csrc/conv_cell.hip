@@ -1,0 +1,325 @@
+// Driver of the convolutional cell with micro-batch BatchNorm.
+//
+// Schedule (GPipe technical review page, "GPipe algorithm in detail"):
+// forward phase over the M micro-batches keeping the boundary output, each
+// micro-batch normalised with its own BatchNorm statistics ("BatchNorm
+// handling"), whose moments are recorded; the moving averages are updated
+// once from them; backward phase re-materializing each micro-batch and
+// accumulating float32 gradients; the update is gpipe_apply_update.
+#include "cell.hpp"
+
+namespace gp {
+namespace {
+
+// Byte layout of a conv-cell workspace for one (N, M, remat):
+//   sets:  remat ? 1 : M micro-batch sets, each L blocks of the saved tensors
+//          of gpipe_conv_saved (block 0 has no X slot in use)
+//   yre:   output of the re-materialized forward [P, C] (remat only)
+//   col:   im2col matrix [P, 9C] (act);  dcol: its gradient [P, 9C] (f32)
+//   r0:    residual-stream gradient [P, C] (f32);  r1: ReLU-input gradient (f32)
+//   dz:    BN input gradient [P, C] (act, GEMM operand)
+//   part, sums: BN reduction partials;  rec: forward-phase moments [M][2L][2][C]
+//   msepart, splitk
+struct CPlan {
+  int N, M, B;
+  int64_t P;  // pixels per micro-batch
+  size_t eb;
+  size_t saved_off[GPIPE_CONV_N_SAVED], saved_bytes[GPIPE_CONV_N_SAVED];
+  size_t block_bytes, set_bytes;
+  int nsets;
+  size_t yre, col, dcol, r0, r1, dz, part, sums, rec, msepart, splitk;
+  int mse_nblk;
+  size_t total;
+};
+
+bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
+  if (N <= 0 || M <= 0 || N % M) return false;
+  p->N = N;
+  p->M = M;
+  p->B = N / M;
+  const size_t C = c->C;
+  const size_t P = size_t(p->B) * c->Hc * c->Wc;
+  if (P * 9 * C > size_t(1) << 40) return false;
+  p->P = int64_t(P);
+  const size_t eb = c->prec == GPIPE_BF16 ? 2 : 4;
+  p->eb = eb;
+  const size_t sizes[GPIPE_CONV_N_SAVED] = {P * C * eb, P * C * eb, 2 * C * 4,
+                                            P * C * eb, P * C * eb, 2 * C * 4};
+  size_t off = 0;
+  for (int i = 0; i < GPIPE_CONV_N_SAVED; ++i) {
+    p->saved_off[i] = off;
+    p->saved_bytes[i] = sizes[i];
+    off += align_up(sizes[i], kAlign);
+  }
+  p->block_bytes = off;
+  p->set_bytes = size_t(c->L) * off;
+  p->nsets = remat ? 1 : M;
+  size_t o = size_t(p->nsets) * p->set_bytes;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes, kAlign);
+    return at;
+  };
+  p->yre = take(remat ? P * C * eb : 0);
+  p->col = take(P * 9 * C * eb);
+  p->dcol = take(P * 9 * C * 4);
+  p->r0 = take(P * C * 4);
+  p->r1 = take(P * C * 4);
+  p->dz = take(P * C * eb);
+  p->part = take(size_t(bn_chunks(int64_t(P))) * 2 * C * 4);
+  p->sums = take(2 * C * 4);
+  p->rec = take(size_t(M) * 2 * c->L * 2 * C * 4);
+  p->mse_nblk = mse_blocks(int64_t(P * C));
+  p->msepart = take(size_t(M) * p->mse_nblk * 4);
+  const bool bf = c->prec == GPIPE_BF16;
+  const int Pi = int(P), Ci = int(C);
+  const size_t sk = std::max({gemm_partial_floats(GPIPE_ROLE_CONV_FWD, bf, Pi, Ci, 9 * Ci, 1),
+                              gemm_partial_floats(GPIPE_ROLE_CONV_DGRAD, bf, Pi, 9 * Ci, Ci, 1),
+                              gemm_partial_floats(GPIPE_ROLE_CONV_WGRAD, bf, Ci, 9 * Ci, Pi, 1)});
+  p->splitk = take(sk * 4);
+  p->total = o;
+  return true;
+}
+
+inline size_t csaved_at(const CPlan& p, int set, int block, int which) {
+  return size_t(set) * p.set_bytes + size_t(block) * p.block_bytes + p.saved_off[which];
+}
+
+struct CCtx {
+  const gpipe_cell* c;
+  gpipe_cell* prof;
+  const CPlan* p;
+  char* ws;
+  hipStream_t s;
+  bool bf16;
+  const void* wmat(int block, int t) const {
+    const size_t off = size_t(block) * c->per_layer + c->rel_off[t];
+    if (bf16) return static_cast<const uint16_t*>(c->w_lowp) + off;
+    return c->master + off;
+  }
+  const float* wf32(int block, int t) const {
+    return c->master + size_t(block) * c->per_layer + c->rel_off[t];
+  }
+  float* grad(int block, int t) const {
+    return c->grad + size_t(block) * c->per_layer + c->rel_off[t];
+  }
+  void* at(size_t off) const { return ws + off; }
+  float* f(size_t off) const { return reinterpret_cast<float*>(ws + off); }
+  void* act(const void* base, size_t elems) const {
+    return const_cast<char*>(static_cast<const char*>(base)) + elems * p->eb;
+  }
+};
+
+hipError_t cmm(const CCtx& x, int role, int M, int N, int K, const void* A, int64_t lda,
+               const void* B, int64_t ldb, void* C, int64_t ldc, int beta = 0) {
+  GemmParams g;
+  memset(&g, 0, sizeof(g));
+  g.hdiv = 1;
+  g.alpha = 1.0f;
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda;
+  g.B = B; g.ldb = ldb;
+  g.C = C; g.ldc = ldc;
+  g.beta = beta;
+  g.P = x.f(x.p->splitk);
+  return gemm(x.bf16, role, g, 1, x.s);
+}
+
+// One block forward of one micro-batch; rec (nullable) receives the BN
+// moments [2][2][C] of this block (forward phase only).
+gpipe_status block_forward(const CCtx& x, int set, int l, const void* xin, void* xout, float* rec) {
+  const gpipe_cell* c = x.c;
+  const CPlan& p = *x.p;
+  const int C = c->C, B = p.B, H = c->Hc, W = c->Wc;
+  const int64_t P = p.P;
+  void* col = x.at(p.col);
+  void* a = x.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_A));
+  float* st1 = x.f(csaved_at(p, set, l, GPIPE_CONV_SAVED_ST1));
+  void* r = x.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_R));
+  void* z = x.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_Z));
+  float* st2 = x.f(csaved_at(p, set, l, GPIPE_CONV_SAVED_ST2));
+  float* part = x.f(p.part);
+  GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, xin, col, B, H, W, C, x.s));
+  GP_RUN(x, GPIPE_ROLE_CONV_FWD, cmm(x, GPIPE_ROLE_CONV_FWD, int(P), C, 9 * C, col, 9 * C,
+                                     x.wmat(l, GPIPE_CONV_W1), 9 * C, a, C));
+  GP_RUN(x, GPIPE_ROLE_BN_STATS, bn_stats(x.bf16, a, P, C, c->bn_eps, part, st1, rec, x.s));
+  GP_RUN(x, GPIPE_ROLE_BN_APPLY, bn_apply(x.bf16, 0, a, st1, x.wf32(l, GPIPE_CONV_BN1_G),
+                                          x.wf32(l, GPIPE_CONV_BN1_B), nullptr, r, P, C, x.s));
+  GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, r, col, B, H, W, C, x.s));
+  GP_RUN(x, GPIPE_ROLE_CONV_FWD, cmm(x, GPIPE_ROLE_CONV_FWD, int(P), C, 9 * C, col, 9 * C,
+                                     x.wmat(l, GPIPE_CONV_W2), 9 * C, z, C));
+  GP_RUN(x, GPIPE_ROLE_BN_STATS,
+         bn_stats(x.bf16, z, P, C, c->bn_eps, part, st2, rec ? rec + 2 * C : nullptr, x.s));
+  GP_RUN(x, GPIPE_ROLE_BN_APPLY, bn_apply(x.bf16, 1, z, st2, x.wf32(l, GPIPE_CONV_BN2_G),
+                                          x.wf32(l, GPIPE_CONV_BN2_B), xin, xout, P, C, x.s));
+  return GPIPE_OK;
+}
+
+gpipe_status cell_forward(const CCtx& x, int set, const void* xin, void* yout, float* rec) {
+  const int L = x.c->L, C = x.c->C;
+  for (int l = 0; l < L; ++l) {
+    const void* in = l == 0 ? xin : x.at(csaved_at(*x.p, set, l, GPIPE_CONV_SAVED_X));
+    void* out = l == L - 1 ? yout : x.at(csaved_at(*x.p, set, l + 1, GPIPE_CONV_SAVED_X));
+    gpipe_status st = block_forward(x, set, l, in, out, rec ? rec + size_t(l) * 4 * C : nullptr);
+    if (st != GPIPE_OK) return st;
+  }
+  return GPIPE_OK;
+}
+
+// Backward of block l.  r0 holds the gradient w.r.t. the block output and is
+// overwritten in place with the gradient w.r.t. its input (dx_out, if given,
+// receives the act copy).
+gpipe_status block_backward(const CCtx& x, int set, int l, const void* xin, int beta, void* dx_out) {
+  const gpipe_cell* c = x.c;
+  const CPlan& p = *x.p;
+  const int C = c->C, B = p.B, H = c->Hc, W = c->Wc;
+  const int64_t P = p.P;
+  const void* a = x.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_A));
+  const float* st1 = x.f(csaved_at(p, set, l, GPIPE_CONV_SAVED_ST1));
+  const void* r = x.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_R));
+  const void* z = x.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_Z));
+  const float* st2 = x.f(csaved_at(p, set, l, GPIPE_CONV_SAVED_ST2));
+  void* col = x.at(p.col);
+  float* dcol = x.f(p.dcol);
+  float* r0 = x.f(p.r0);
+  float* r1 = x.f(p.r1);
+  void* dz = x.at(p.dz);
+  float* part = x.f(p.part);
+  float* sums = x.f(p.sums);
+  int nch = 0;
+  // y = x + BN2(z)
+  GP_RUN(x, GPIPE_ROLE_BN_BWD, bn_bwd(x.bf16, 0, r0, nullptr, z, st2, x.wf32(l, GPIPE_CONV_BN2_G),
+                                      part, sums, dz, P, C, &nch, x.s));
+  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(part, nch, 2 * C, 2 * C, x.grad(l, GPIPE_CONV_BN2_G),
+                                               beta, x.s));
+  // z = conv(r, W2)
+  GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, r, col, B, H, W, C, x.s));
+  GP_RUN(x, GPIPE_ROLE_CONV_WGRAD, cmm(x, GPIPE_ROLE_CONV_WGRAD, C, 9 * C, int(P), dz, C, col,
+                                       9 * C, x.grad(l, GPIPE_CONV_W2), 9 * C, beta));
+  GP_RUN(x, GPIPE_ROLE_CONV_DGRAD, cmm(x, GPIPE_ROLE_CONV_DGRAD, int(P), 9 * C, C, dz, C,
+                                       x.wmat(l, GPIPE_CONV_W2), 9 * C, dcol, 9 * C));
+  GP_RUN(x, GPIPE_ROLE_COL2IM, col2im(x.bf16, dcol, nullptr, r1, nullptr, B, H, W, C, x.s));
+  // r = ReLU(BN1(a))
+  GP_RUN(x, GPIPE_ROLE_BN_BWD, bn_bwd(x.bf16, 1, r1, r, a, st1, x.wf32(l, GPIPE_CONV_BN1_G), part,
+                                      sums, dz, P, C, &nch, x.s));
+  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(part, nch, 2 * C, 2 * C, x.grad(l, GPIPE_CONV_BN1_G),
+                                               beta, x.s));
+  // a = conv(x, W1); the residual gradient r0 is added in col2im (in place)
+  GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, xin, col, B, H, W, C, x.s));
+  GP_RUN(x, GPIPE_ROLE_CONV_WGRAD, cmm(x, GPIPE_ROLE_CONV_WGRAD, C, 9 * C, int(P), dz, C, col,
+                                       9 * C, x.grad(l, GPIPE_CONV_W1), 9 * C, beta));
+  GP_RUN(x, GPIPE_ROLE_CONV_DGRAD, cmm(x, GPIPE_ROLE_CONV_DGRAD, int(P), 9 * C, C, dz, C,
+                                       x.wmat(l, GPIPE_CONV_W1), 9 * C, dcol, 9 * C));
+  GP_RUN(x, GPIPE_ROLE_COL2IM, col2im(x.bf16, dcol, r0, r0, dx_out, B, H, W, C, x.s));
+  return GPIPE_OK;
+}
+
+}  // namespace
+
+gpipe_status conv_cell_init(gpipe_cell* c) {
+  const size_t C = c->C;
+  const size_t cnt[GPIPE_CONV_N_TENSORS] = {9 * C * C, C, C, 9 * C * C, C, C};
+  size_t off = 0;
+  for (int t = 0; t < GPIPE_CONV_N_TENSORS; ++t) {
+    c->rel_off[t] = off;
+    c->count[t] = cnt[t];
+    off += cnt[t];
+  }
+  c->per_layer = off;
+  c->n_params = off * size_t(c->L);
+  return GPIPE_OK;
+}
+
+bool conv_workspace_bytes(const gpipe_cell* c, int N, int M, int remat, size_t* bytes) {
+  CPlan p;
+  if (!make_cplan(c, N, M, remat, &p)) return false;
+  *bytes = p.total;
+  return true;
+}
+
+bool conv_saved_offset(const gpipe_cell* c, int N, int M, int remat, int micro, int block,
+                       int which, size_t* offset, size_t* bytes) {
+  CPlan p;
+  if (!make_cplan(c, N, M, remat, &p)) return false;
+  if (micro < 0 || micro >= p.nsets || block < 0 || block >= c->L || which < 0 ||
+      which >= GPIPE_CONV_N_SAVED || (block == 0 && which == GPIPE_CONV_SAVED_X))
+    return false;
+  *offset = csaved_at(p, micro, block, which);
+  *bytes = p.saved_bytes[which];
+  return true;
+}
+
+gpipe_status conv_gemm_plan(const gpipe_cell* c, int N, int M, int role, int* tile_m, int* tile_n,
+                            int* splits) {
+  CPlan p;
+  if (!make_cplan(c, N, M, 1, &p)) return GPIPE_ERR_INVALID;
+  const int P = int(p.P), C = c->C;
+  int m = 0, n = 0, k = 0;
+  switch (role) {
+    case GPIPE_ROLE_CONV_FWD: m = P; n = C; k = 9 * C; break;
+    case GPIPE_ROLE_CONV_DGRAD: m = P; n = 9 * C; k = C; break;
+    case GPIPE_ROLE_CONV_WGRAD: m = C; n = 9 * C; k = P; break;
+    default:
+      *tile_m = *tile_n = *splits = 0;
+      return GPIPE_OK;
+  }
+  const GemmPlan g = plan_gemm(role, c->prec == GPIPE_BF16, m, n, k, 1);
+  *tile_m = g.cfg < 0 ? 64 : gemm_cfg_bm(g.cfg);
+  *tile_n = g.cfg < 0 ? 64 : gemm_cfg_bn(g.cfg);
+  *splits = g.splits;
+  return GPIPE_OK;
+}
+
+gpipe_status conv_cell_step(gpipe_cell* c, const void* x, const void* target, void* y, void* dx,
+                            int N, int M, int remat, void* workspace, size_t ws_bytes,
+                            hipStream_t stream, float* loss_dev) {
+  CPlan p;
+  if (!make_cplan(c, N, M, remat, &p)) return GPIPE_ERR_INVALID;
+  if (!c->running) return GPIPE_ERR_STATE;
+  if (!x || !target || !y || !workspace || !loss_dev || ws_bytes < p.total) return GPIPE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(target) || !aligned16(y) || (dx && !aligned16(dx)) ||
+      !aligned16(workspace))
+    return GPIPE_ERR_INVALID;
+  CCtx cx{c, c->prof_mask ? c : nullptr, &p, static_cast<char*>(workspace), stream,
+          c->prec == GPIPE_BF16};
+  const size_t mb = size_t(p.P) * c->C;
+  const float inv_denom = float(1.0 / (double(N) * c->Hc * c->Wc * c->C));
+  float* rec = cx.f(p.rec);
+  float* msepart = cx.f(p.msepart);
+  const size_t rec_mb = size_t(2) * c->L * 2 * c->C;
+  // phase 1: forward; each micro-batch normalised with its own statistics
+  for (int m = 0; m < M; ++m) {
+    gpipe_status st = cell_forward(cx, remat ? 0 : m, cx.act(x, m * mb), cx.act(y, m * mb),
+                                   rec + m * rec_mb);
+    if (st != GPIPE_OK) return st;
+  }
+  // the moving averages, once per step, from the forward phase's moments
+  GP_RUN(cx, GPIPE_ROLE_BN_RUNNING, bn_running(rec, M, 2 * c->L, c->C,
+                                              int64_t(N) * c->Hc * c->Wc, c->bn_momentum,
+                                              c->running, stream));
+  // phase 2: re-materialize and backpropagate each micro-batch
+  for (int m = 0; m < M; ++m) {
+    const int set = remat ? 0 : m;
+    const void* xm = cx.act(x, m * mb);
+    const void* ym = cx.act(y, m * mb);
+    if (remat) {
+      gpipe_status st = cell_forward(cx, set, xm, cx.at(p.yre), nullptr);
+      if (st != GPIPE_OK) return st;
+      ym = cx.at(p.yre);
+    }
+    int nblk = 0;
+    GP_RUN(cx, GPIPE_ROLE_MSE, mse_fwd_bwd(cx.bf16, ym, cx.act(target, m * mb), cx.f(p.r0),
+                                           cx.at(p.dz), msepart + size_t(m) * p.mse_nblk,
+                                           int64_t(mb), inv_denom, &nblk, stream));
+    for (int l = c->L - 1; l >= 0; --l) {
+      const void* xin = l == 0 ? xm : cx.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_X));
+      void* dxo = (l == 0 && dx) ? cx.act(dx, m * mb) : nullptr;
+      gpipe_status st = block_backward(cx, set, l, xin, m > 0 ? 1 : 0, dxo);
+      if (st != GPIPE_OK) return st;
+    }
+  }
+  GP_RUN(cx, GPIPE_ROLE_LOSS_REDUCE, sum_partials(msepart, M * p.mse_nblk, 1, 1, loss_dev, 0, stream));
+  return GPIPE_OK;
+}
+
+}  // namespace gp

@@ -1,0 +1,398 @@
+// Kernels of the convolutional cell with micro-batch BatchNorm (GPipe
+// technical review page, "GPipe algorithm in detail / BatchNorm handling":
+// each micro-batch normalises with its own statistics; moving averages over
+// the mini-batch are kept for evaluation).
+//
+// Activations are NHWC [B, H, W, C]; a 3x3 convolution (pad 1, stride 1) is
+// a GEMM over the im2col matrix [B*H*W, 9*C] (column (kh*3 + kw)*C + c).
+// Channels are processed in chunks of 8 (C must be a multiple of 8).  Every
+// reduction has a fixed order, so re-materialization is bitwise.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gp {
+
+// ------------------------------------------------------------ im2col / col2im
+template <typename T>
+__global__ __launch_bounds__(256) void im2col_kernel(const T* __restrict__ x, T* __restrict__ col,
+                                                     int B, int H, int W, int C) {
+  const int cc8 = C >> 3;
+  const int64_t total = int64_t(B) * H * W * 9 * cc8;
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += stride) {
+    const int cc = int(i % cc8);
+    const int64_t rest = i / cc8;
+    const int tap = int(rest % 9);
+    const int64_t p = rest / 9;
+    const int w = int(p % W), h = int((p / W) % H), b = int(p / (int64_t(W) * H));
+    const int hs = h + tap / 3 - 1, ws = w + tap % 3 - 1;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (hs >= 0 && hs < H && ws >= 0 && ws < W)
+      load8<T>(x + ((int64_t(b) * H + hs) * W + ws) * C + cc * 8, v);
+    store8<T>(col + p * 9 * C + tap * C + cc * 8, v);
+  }
+}
+
+hipError_t im2col(bool bf16, const void* x, void* col, int B, int H, int W, int C, hipStream_t s) {
+  const int64_t total = int64_t(B) * H * W * 9 * (C / 8);
+  if (total == 0) return hipSuccess;
+  const int64_t want = (total + 255) / 256;
+  const int blocks = int(want < 16384 ? want : 16384);
+  if (bf16)
+    hipLaunchKernelGGL(im2col_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const bf16_t*>(x), static_cast<bf16_t*>(col), B, H, W, C);
+  else
+    hipLaunchKernelGGL(im2col_kernel<float>, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const float*>(x), static_cast<float*>(col), B, H, W, C);
+  return hipGetLastError();
+}
+
+// dx[p] = res[p] + sum over the nine taps t of dcol[p - offset(t)][t] (the
+// pixels whose tap t reads p), taps in order 0..8.
+template <typename T>
+__global__ __launch_bounds__(256) void col2im_kernel(const float* __restrict__ dcol,
+                                                     const float* res,  // may alias dx_f32
+                                                     float* dx_f32,
+                                                     T* __restrict__ dx_act, int B, int H, int W,
+                                                     int C) {
+  const int cc8 = C >> 3;
+  const int64_t total = int64_t(B) * H * W * cc8;
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += stride) {
+    const int cc = int(i % cc8);
+    const int64_t p = i / cc8;
+    const int w = int(p % W), h = int((p / W) % H), b = int(p / (int64_t(W) * H));
+    float acc[8];
+    if (res) load8<float>(res + p * C + cc * 8, acc);
+    else
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int tap = 0; tap < 9; ++tap) {
+      const int hs = h - (tap / 3 - 1), ws = w - (tap % 3 - 1);
+      if (hs < 0 || hs >= H || ws < 0 || ws >= W) continue;
+      float v[8];
+      load8<float>(dcol + ((int64_t(b) * H + hs) * W + ws) * 9 * C + tap * C + cc * 8, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += v[e];
+    }
+    store8<float>(dx_f32 + p * C + cc * 8, acc);
+    if (dx_act) store8<T>(dx_act + p * C + cc * 8, acc);
+  }
+}
+
+hipError_t col2im(bool bf16, const float* dcol, const float* res, float* dx_f32, void* dx_act,
+                  int B, int H, int W, int C, hipStream_t s) {
+  const int64_t total = int64_t(B) * H * W * (C / 8);
+  if (total == 0) return hipSuccess;
+  const int64_t want = (total + 255) / 256;
+  const int blocks = int(want < 16384 ? want : 16384);
+  if (bf16)
+    hipLaunchKernelGGL(col2im_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, dcol, res, dx_f32,
+                       static_cast<bf16_t*>(dx_act), B, H, W, C);
+  else
+    hipLaunchKernelGGL(col2im_kernel<float>, dim3(blocks), dim3(256), 0, s, dcol, res, dx_f32,
+                       static_cast<float*>(dx_act), B, H, W, C);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ BatchNorm statistics
+// Column partial sums over blocks of kBnRows rows: a block covers 256
+// channels x kBnRows rows; thread (g, c8) sums 8 channels over rows g, g+8, ...
+// of the block, the 8 row groups are combined in order through LDS.
+// mean == nullptr: sums x;  otherwise sums (x - mean)^2.
+constexpr int kBnRows = 128;
+int bn_chunks(int64_t rows) { return int((rows + kBnRows - 1) / kBnRows); }
+
+template <typename T>
+__global__ __launch_bounds__(256) void bn_partial_kernel(const T* __restrict__ x,
+                                                         const float* __restrict__ mean,
+                                                         float* __restrict__ part, int64_t rows,
+                                                         int C) {
+  __shared__ float red[8][257];
+  const int cg = threadIdx.x & 31, rg = threadIdx.x >> 5;
+  const int c0 = blockIdx.x * 256 + cg * 8;
+  const int64_t r0 = int64_t(blockIdx.y) * kBnRows;
+  const int64_t r1 = r0 + kBnRows < rows ? r0 + kBnRows : rows;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (c0 < C) {
+    float mu[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (mean) load8<float>(mean + c0, mu);
+    for (int64_t r = r0 + rg; r < r1; r += 8) {
+      float v[8];
+      load8<T>(x + r * C + c0, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = v[e] - mu[e];
+        s[e] += mean ? d * d : v[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rg][cg * 8 + e] = s[e];
+  __syncthreads();
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c < C) {
+    float t = red[0][threadIdx.x];
+#pragma unroll
+    for (int g = 1; g < 8; ++g) t += red[g][threadIdx.x];
+    part[int64_t(blockIdx.y) * C + c] = t;
+  }
+}
+
+// mode 0: out1 = sum/n (mean), copied to out2 if given.
+// mode 1: v = sum/n (biased variance): out1 = 1/sqrt(v + eps), out2 = v if given.
+__global__ __launch_bounds__(256) void bn_finalize_kernel(const float* __restrict__ part, int nchunk,
+                                                          int C, float inv_n, float eps, int mode,
+                                                          float* __restrict__ out1,
+                                                          float* __restrict__ out2) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= C) return;
+  float s = 0.f;
+  for (int k = 0; k < nchunk; ++k) s += part[int64_t(k) * C + c];
+  const float v = s * inv_n;
+  if (mode == 0) {
+    out1[c] = v;
+    if (out2) out2[c] = v;
+  } else {
+    out1[c] = 1.0f / sqrtf(v + eps);
+    if (out2) out2[c] = v;
+  }
+}
+
+// stats: [2][C] = (mean, rstd).  rec (optional): [2][C] = (mean, biased var).
+hipError_t bn_stats(bool bf16, const void* x, int64_t rows, int C, float eps, float* part,
+                    float* stats, float* rec, hipStream_t s) {
+  if (rows == 0 || C == 0) return hipSuccess;
+  const int nch = bn_chunks(rows);
+  dim3 grid((C + 255) / 256, nch);
+  const float inv_n = float(1.0 / double(rows));
+  for (int pass = 0; pass < 2; ++pass) {
+    const float* mean = pass == 0 ? nullptr : stats;
+    if (bf16)
+      hipLaunchKernelGGL(bn_partial_kernel<bf16_t>, grid, dim3(256), 0, s,
+                         static_cast<const bf16_t*>(x), mean, part, rows, C);
+    else
+      hipLaunchKernelGGL(bn_partial_kernel<float>, grid, dim3(256), 0, s,
+                         static_cast<const float*>(x), mean, part, rows, C);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    float* out1 = pass == 0 ? stats : stats + C;
+    float* out2 = rec ? (pass == 0 ? rec : rec + C) : nullptr;
+    hipLaunchKernelGGL(bn_finalize_kernel, dim3((C + 255) / 256), dim3(256), 0, s, part, nch, C,
+                       inv_n, eps, pass, out1, out2);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ------------------------------------------------------------ BatchNorm apply
+// y = gamma * (a - mean) * rstd + beta;  MODE 0: out = max(y, 0);  MODE 1: out = res + y.
+template <typename T, int MODE>
+__global__ __launch_bounds__(256) void bn_apply_kernel(const T* __restrict__ a,
+                                                       const float* __restrict__ stats,
+                                                       const float* __restrict__ gamma,
+                                                       const float* __restrict__ beta,
+                                                       const T* __restrict__ res,
+                                                       T* __restrict__ out, int64_t rows, int C) {
+  const int cc8 = C >> 3;
+  const int64_t total = rows * cc8;
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += stride) {
+    const int c0 = int(i % cc8) * 8;
+    const int64_t off = (i / cc8) * C + c0;
+    float v[8], o[8];
+    load8<T>(a + off, v);
+    float rv[8];
+    if (MODE == 1) load8<T>(res + off, rv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = c0 + e;
+      const float y = gamma[c] * (v[e] - stats[c]) * stats[C + c] + beta[c];
+      o[e] = MODE == 0 ? fmaxf(y, 0.f) : rv[e] + y;
+    }
+    store8<T>(out + off, o);
+  }
+}
+
+hipError_t bn_apply(bool bf16, int mode, const void* a, const float* stats, const float* gamma,
+                    const float* beta, const void* res, void* out, int64_t rows, int C,
+                    hipStream_t s) {
+  const int64_t total = rows * (C / 8);
+  if (total == 0) return hipSuccess;
+  const int64_t want = (total + 255) / 256;
+  const int blocks = int(want < 16384 ? want : 16384);
+#define GP_BN_APPLY(T, M)                                                                      \
+  hipLaunchKernelGGL((bn_apply_kernel<T, M>), dim3(blocks), dim3(256), 0, s,                  \
+                     static_cast<const T*>(a), stats, gamma, beta, static_cast<const T*>(res), \
+                     static_cast<T*>(out), rows, C)
+  if (bf16) {
+    if (mode == 0) GP_BN_APPLY(bf16_t, 0); else GP_BN_APPLY(bf16_t, 1);
+  } else {
+    if (mode == 0) GP_BN_APPLY(float, 0); else GP_BN_APPLY(float, 1);
+  }
+#undef GP_BN_APPLY
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ BatchNorm backward
+// dy = dy_src (MASK: times [r > 0], r the ReLU output), xhat = (a - mean) * rstd.
+// part[chunk][0:C] = sum dy*xhat, part[chunk][C:2C] = sum dy (gamma, beta order).
+template <typename T, int MASK>
+__global__ __launch_bounds__(256) void bn_bwd_partial_kernel(const float* __restrict__ dy_src,
+                                                             const T* __restrict__ r,
+                                                             const T* __restrict__ a,
+                                                             const float* __restrict__ stats,
+                                                             float* __restrict__ part,
+                                                             int64_t rows, int C) {
+  __shared__ float red[2][8][257];
+  const int cg = threadIdx.x & 31, rg = threadIdx.x >> 5;
+  const int c0 = blockIdx.x * 256 + cg * 8;
+  const int64_t r0 = int64_t(blockIdx.y) * kBnRows;
+  const int64_t r1 = r0 + kBnRows < rows ? r0 + kBnRows : rows;
+  float sg[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, sb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (c0 < C) {
+    float mu[8], rs[8];
+    load8<float>(stats + c0, mu);
+    load8<float>(stats + C + c0, rs);
+    for (int64_t row = r0 + rg; row < r1; row += 8) {
+      float g[8], av[8];
+      load8<float>(dy_src + row * C + c0, g);
+      load8<T>(a + row * C + c0, av);
+      if (MASK) {
+        float rv[8];
+        load8<T>(r + row * C + c0, rv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) g[e] = rv[e] > 0.f ? g[e] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sg[e] += g[e] * (av[e] - mu[e]) * rs[e];
+        sb[e] += g[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    red[0][rg][cg * 8 + e] = sg[e];
+    red[1][rg][cg * 8 + e] = sb[e];
+  }
+  __syncthreads();
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c < C) {
+    float tg = red[0][0][threadIdx.x], tb = red[1][0][threadIdx.x];
+#pragma unroll
+    for (int g = 1; g < 8; ++g) {
+      tg += red[0][g][threadIdx.x];
+      tb += red[1][g][threadIdx.x];
+    }
+    part[int64_t(blockIdx.y) * 2 * C + c] = tg;
+    part[int64_t(blockIdx.y) * 2 * C + C + c] = tb;
+  }
+}
+
+// da = gamma * rstd * (dy - sum(dy)/n - xhat * sum(dy*xhat)/n);  sums = [2][C] as in the partials.
+template <typename T, int MASK>
+__global__ __launch_bounds__(256) void bn_bwd_apply_kernel(const float* __restrict__ dy_src,
+                                                           const T* __restrict__ r,
+                                                           const T* __restrict__ a,
+                                                           const float* __restrict__ stats,
+                                                           const float* __restrict__ gamma,
+                                                           const float* __restrict__ sums,
+                                                           T* __restrict__ da, int64_t rows, int C,
+                                                           float inv_n) {
+  const int cc8 = C >> 3;
+  const int64_t total = rows * cc8;
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += stride) {
+    const int c0 = int(i % cc8) * 8;
+    const int64_t off = (i / cc8) * C + c0;
+    float g[8], av[8], o[8];
+    load8<float>(dy_src + off, g);
+    load8<T>(a + off, av);
+    if (MASK) {
+      float rv[8];
+      load8<T>(r + off, rv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[e] = rv[e] > 0.f ? g[e] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = c0 + e;
+      const float rs = stats[C + c];
+      const float xh = (av[e] - stats[c]) * rs;
+      o[e] = gamma[c] * rs * (g[e] - sums[C + c] * inv_n - xh * sums[c] * inv_n);
+    }
+    store8<T>(da + off, o);
+  }
+}
+
+hipError_t bn_bwd(bool bf16, int mask, const float* dy_src, const void* r, const void* a,
+                  const float* stats, const float* gamma, float* part, float* sums, void* da,
+                  int64_t rows, int C, int* nchunk, hipStream_t s) {
+  *nchunk = bn_chunks(rows);
+  if (rows == 0 || C == 0) return hipSuccess;
+  dim3 grid((C + 255) / 256, *nchunk);
+#define GP_BN_BWD_P(T, MK)                                                                    \
+  hipLaunchKernelGGL((bn_bwd_partial_kernel<T, MK>), grid, dim3(256), 0, s, dy_src,          \
+                     static_cast<const T*>(r), static_cast<const T*>(a), stats, part, rows, C)
+  if (bf16) {
+    if (mask) GP_BN_BWD_P(bf16_t, 1); else GP_BN_BWD_P(bf16_t, 0);
+  } else {
+    if (mask) GP_BN_BWD_P(float, 1); else GP_BN_BWD_P(float, 0);
+  }
+#undef GP_BN_BWD_P
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = sum_partials(part, *nchunk, 2 * C, 2 * C, sums, 0, s);
+  if (e != hipSuccess) return e;
+  const int64_t total = rows * (C / 8);
+  const int64_t want = (total + 255) / 256;
+  const int blocks = int(want < 16384 ? want : 16384);
+  const float inv_n = float(1.0 / double(rows));
+#define GP_BN_BWD_A(T, MK)                                                                   \
+  hipLaunchKernelGGL((bn_bwd_apply_kernel<T, MK>), dim3(blocks), dim3(256), 0, s, dy_src,   \
+                     static_cast<const T*>(r), static_cast<const T*>(a), stats, gamma, sums, \
+                     static_cast<T*>(da), rows, C, inv_n)
+  if (bf16) {
+    if (mask) GP_BN_BWD_A(bf16_t, 1); else GP_BN_BWD_A(bf16_t, 0);
+  } else {
+    if (mask) GP_BN_BWD_A(float, 1); else GP_BN_BWD_A(float, 0);
+  }
+#undef GP_BN_BWD_A
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ moving averages
+// rec: [M][nbn][2][C] = per micro-batch (mean, biased var); running: [nbn][2][C].
+// Pooled over the M equal micro-batches in order:
+//   mu = mean_m mu_m,  var = mean_m(var_m + mu_m^2) - mu^2,  unbiased * n/(n-1).
+__global__ __launch_bounds__(256) void bn_running_kernel(const float* __restrict__ rec, int M,
+                                                         int nbn, int C, float n_total,
+                                                         float momentum,
+                                                         float* __restrict__ running) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= nbn * C) return;
+  const int j = i / C, c = i % C;
+  double mu = 0.0, sq = 0.0;
+  for (int m = 0; m < M; ++m) {
+    const float* r = rec + (int64_t(m) * nbn + j) * 2 * C;
+    mu += r[c];
+    sq += double(r[C + c]) + double(r[c]) * double(r[c]);
+  }
+  mu /= M;
+  const double var = sq / M - mu * mu;
+  const double unbiased = n_total > 1.f ? var * n_total / (n_total - 1.0) : var;
+  float* run = running + int64_t(j) * 2 * C;
+  run[c] = float(momentum * run[c] + (1.0 - momentum) * mu);
+  run[C + c] = float(momentum * run[C + c] + (1.0 - momentum) * unbiased);
+}
+
+hipError_t bn_running(const float* rec, int M, int nbn, int C, int64_t n_total, float momentum,
+                      float* running, hipStream_t s) {
+  if (nbn * C == 0) return hipSuccess;
+  hipLaunchKernelGGL(bn_running_kernel, dim3((nbn * C + 255) / 256), dim3(256), 0, s, rec, M, nbn,
+                     C, float(n_total), momentum, running);
+  return hipGetLastError();
+}
+
+}  // namespace gp

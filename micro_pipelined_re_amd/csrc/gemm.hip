@@ -24,6 +24,9 @@ int group_of(int role) {
     case GPIPE_ROLE_FFN2_FWD: return 0;
     case GPIPE_ROLE_FFN2_DGRAD: case GPIPE_ROLE_FFN1_DGRAD: case GPIPE_ROLE_OUT_DGRAD:
     case GPIPE_ROLE_QKV_DGRAD: return 1;
+    case GPIPE_ROLE_CONV_FWD: return 0;
+    case GPIPE_ROLE_CONV_DGRAD: return 1;
+    case GPIPE_ROLE_CONV_WGRAD: return 2;
   }
   return is_wgrad(role) ? 2 : is_attention(role) ? 3 : -1;
 }
@@ -38,10 +41,11 @@ bool dma_ok(int role, const GemmParams& g) {
   if (g.K % 64 || g.M < 8 || g.N < 8 || g.N % 8 || g.ldc % 8 || g.ldr % 8 || g.ldu % 8) return false;
   const bool a_mn = role == GPIPE_ROLE_FFN2_WGRAD || role == GPIPE_ROLE_FFN1_WGRAD ||
                     role == GPIPE_ROLE_OUT_WGRAD || role == GPIPE_ROLE_QKV_WGRAD ||
-                    role == GPIPE_ROLE_DV || role == GPIPE_ROLE_DK;
+                    role == GPIPE_ROLE_DV || role == GPIPE_ROLE_DK || role == GPIPE_ROLE_CONV_WGRAD;
   const bool b_mn = role != GPIPE_ROLE_QKV_FWD && role != GPIPE_ROLE_SCORES_FWD &&
                     role != GPIPE_ROLE_OUT_FWD && role != GPIPE_ROLE_FFN1_FWD &&
-                    role != GPIPE_ROLE_FFN2_FWD && role != GPIPE_ROLE_DP;
+                    role != GPIPE_ROLE_FFN2_FWD && role != GPIPE_ROLE_DP &&
+                    role != GPIPE_ROLE_CONV_FWD;
   if (a_mn && g.M % 8) return false;
   if (b_mn && g.N % 8) return false;
   return true;
@@ -65,7 +69,10 @@ GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch) {
     p.cfg = -1;
     return p;
   }
-  const bool can_split = !is_attention(role) && !is_wgrad(role) && batch == 1;
+  // (the convolution's weight gradient is small -- C x 9C -- and reduces over
+  // every pixel of the micro-batch, so it does split)
+  const bool can_split = !is_attention(role) && (!is_wgrad(role) || role == GPIPE_ROLE_CONV_WGRAD) &&
+                         batch == 1;
   const int bm = kCfgBM[p.cfg], bn = kCfgBN[p.cfg];
   const long tiles = long((M + bm - 1) / bm) * ((N + bn - 1) / bn) * batch;
   if (can_split && tiles < kCUs && K >= 1024) {

@@ -23,6 +23,9 @@ hipError_t gemm_group_f32(int role, const GemmParams& g, int batch, hipStream_t 
     case GPIPE_ROLE_DK: return launch_f32<RoleSpec<GPIPE_ROLE_DK>::LA, RoleSpec<GPIPE_ROLE_DK>::LB, RoleSpec<GPIPE_ROLE_DK>::EPI, GPIPE_ROLE_DK>(g, batch, s);
     case GPIPE_ROLE_QKV_DGRAD: return launch_f32<RoleSpec<GPIPE_ROLE_QKV_DGRAD>::LA, RoleSpec<GPIPE_ROLE_QKV_DGRAD>::LB, RoleSpec<GPIPE_ROLE_QKV_DGRAD>::EPI, GPIPE_ROLE_QKV_DGRAD>(g, batch, s);
     case GPIPE_ROLE_QKV_WGRAD: return launch_f32<RoleSpec<GPIPE_ROLE_QKV_WGRAD>::LA, RoleSpec<GPIPE_ROLE_QKV_WGRAD>::LB, RoleSpec<GPIPE_ROLE_QKV_WGRAD>::EPI, GPIPE_ROLE_QKV_WGRAD>(g, batch, s);
+    case GPIPE_ROLE_CONV_FWD: return launch_f32<RoleSpec<GPIPE_ROLE_CONV_FWD>::LA, RoleSpec<GPIPE_ROLE_CONV_FWD>::LB, RoleSpec<GPIPE_ROLE_CONV_FWD>::EPI, GPIPE_ROLE_CONV_FWD>(g, batch, s);
+    case GPIPE_ROLE_CONV_DGRAD: return launch_f32<RoleSpec<GPIPE_ROLE_CONV_DGRAD>::LA, RoleSpec<GPIPE_ROLE_CONV_DGRAD>::LB, RoleSpec<GPIPE_ROLE_CONV_DGRAD>::EPI, GPIPE_ROLE_CONV_DGRAD>(g, batch, s);
+    case GPIPE_ROLE_CONV_WGRAD: return launch_f32<RoleSpec<GPIPE_ROLE_CONV_WGRAD>::LA, RoleSpec<GPIPE_ROLE_CONV_WGRAD>::LB, RoleSpec<GPIPE_ROLE_CONV_WGRAD>::EPI, GPIPE_ROLE_CONV_WGRAD>(g, batch, s);
   }
   return hipErrorInvalidValue;
 }

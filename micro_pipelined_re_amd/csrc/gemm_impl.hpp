@@ -526,6 +526,11 @@ GP_SPEC(GPIPE_ROLE_DQ, LAY_K, LAY_MN, EPI_STORE)
 GP_SPEC(GPIPE_ROLE_DK, LAY_MN, LAY_MN, EPI_STORE)
 GP_SPEC(GPIPE_ROLE_QKV_DGRAD, LAY_K, LAY_MN, EPI_STORE_F32)
 GP_SPEC(GPIPE_ROLE_QKV_WGRAD, LAY_MN, LAY_MN, EPI_ACC_F32)
+// 3x3 convolutions as GEMMs over the im2col matrix [P, 9C]:
+//   forward  a = col W^T;  input gradient dcol = da W (f32);  weight gradient G (+)= da^T col
+GP_SPEC(GPIPE_ROLE_CONV_FWD, LAY_K, LAY_K, EPI_STORE)
+GP_SPEC(GPIPE_ROLE_CONV_DGRAD, LAY_K, LAY_MN, EPI_STORE_F32)
+GP_SPEC(GPIPE_ROLE_CONV_WGRAD, LAY_MN, LAY_MN, EPI_ACC_F32)
 #undef GP_SPEC
 
 template <int BM, int BN, int BK, int ST, int OCC> struct DCfg;

@@ -9,6 +9,7 @@ hipError_t gemm_group_wgrad(int role, int path, int cfg, const GemmParams& g, in
     case GPIPE_ROLE_FFN1_WGRAD: return launch_role<GPIPE_ROLE_FFN1_WGRAD>(path, cfg, g, batch, splits, s);
     case GPIPE_ROLE_OUT_WGRAD: return launch_role<GPIPE_ROLE_OUT_WGRAD>(path, cfg, g, batch, splits, s);
     case GPIPE_ROLE_QKV_WGRAD: return launch_role<GPIPE_ROLE_QKV_WGRAD>(path, cfg, g, batch, splits, s);
+    case GPIPE_ROLE_CONV_WGRAD: return launch_role<GPIPE_ROLE_CONV_WGRAD>(path, cfg, g, batch, splits, s);
   }
   return hipErrorInvalidValue;
 }

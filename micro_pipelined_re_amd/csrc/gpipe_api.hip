@@ -14,35 +14,12 @@
 #include <new>
 #include <vector>
 
-#include "../../include/gpipe.h"
-#include "kernels.hpp"
+#include "cell.hpp"
 
 using namespace gp;
 
-struct gpipe_cell {
-  int L, D, H, F, S, causal;
-  gpipe_precision prec;
-  float ln_eps;
-  size_t n_params;
-  size_t per_layer;
-  size_t rel_off[GPIPE_N_TENSORS];  // offsets inside one layer
-  size_t count[GPIPE_N_TENSORS];
-  float* master;
-  void* w_lowp;
-  float* grad;
-  float* ms;
-  bool bound;
-  // event timing of selected kernel roles (gpipe_cell_profile)
-  unsigned long long prof_mask = 0;
-  std::vector<hipEvent_t> prof_events;  // pool, pairs (start, end), reused
-  std::vector<int> prof_roles;          // role of each recorded pair
-};
 
 namespace {
-
-constexpr size_t kAlign = 256;
-inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
-inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ----------------------------------------------------------------- workspace plan
 // Byte layout of the workspace for one (N, M, remat):
@@ -136,38 +113,6 @@ bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
 inline size_t saved_at(const Plan& p, int set, int layer, int which) {
   return size_t(set) * p.set_bytes + size_t(layer) * p.layer_bytes + p.saved_off[which];
 }
-
-#define GP_CHECK(expr)                              \
-  do {                                              \
-    if ((expr) != hipSuccess) return GPIPE_ERR_DEVICE; \
-  } while (0)
-
-// Next (start, end) event pair of the cell's pool for a launch of `role`.
-bool prof_pair(gpipe_cell* c, int role, hipEvent_t* e0, hipEvent_t* e1) {
-  const size_t k = 2 * c->prof_roles.size();
-  while (c->prof_events.size() < k + 2) {
-    hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return false;
-    c->prof_events.push_back(e);
-  }
-  *e0 = c->prof_events[k];
-  *e1 = c->prof_events[k + 1];
-  c->prof_roles.push_back(role);
-  return true;
-}
-
-// Launches `expr`; when `role` is being timed, brackets it with two events
-// recorded on the context's stream.
-#define GP_RUN(ctx, role, expr)                                                         \
-  do {                                                                                 \
-    hipEvent_t e0_ = nullptr, e1_ = nullptr;                                           \
-    if ((ctx).prof && (((ctx).prof->prof_mask >> (role)) & 1ull)) {                   \
-      if (!prof_pair((ctx).prof, (role), &e0_, &e1_)) return GPIPE_ERR_DEVICE;          \
-      if (hipEventRecord(e0_, (ctx).s) != hipSuccess) return GPIPE_ERR_DEVICE;         \
-    }                                                                                  \
-    if ((expr) != hipSuccess) return GPIPE_ERR_DEVICE;                                 \
-    if (e1_ && hipEventRecord(e1_, (ctx).s) != hipSuccess) return GPIPE_ERR_DEVICE;    \
-  } while (0)
 
 struct Ctx {
   const gpipe_cell* c;
@@ -412,6 +357,7 @@ gpipe_status gpipe_cell_create(int layers, int d_model, int heads, int d_ff, int
     return GPIPE_ERR_UNSUPPORTED;
   gpipe_cell* c = new (std::nothrow) gpipe_cell();
   if (!c) return GPIPE_ERR_INVALID;
+  c->kind = CELL_TRANSFORMER;
   c->L = layers; c->D = d_model; c->H = heads; c->F = d_ff; c->S = seq;
   c->causal = causal ? 1 : 0;
   c->prec = prec;
@@ -427,6 +373,35 @@ gpipe_status gpipe_cell_create(int layers, int d_model, int heads, int d_ff, int
   c->per_layer = off;
   c->n_params = off * size_t(layers);
   *out = c;
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_conv_cell_create(int blocks, int channels, int height, int width,
+                                    float bn_momentum, gpipe_precision prec, gpipe_cell** out) {
+  if (!out) return GPIPE_ERR_INVALID;
+  if (blocks <= 0 || channels <= 0 || height <= 0 || width <= 0) return GPIPE_ERR_INVALID;
+  if (!(bn_momentum >= 0.f && bn_momentum < 1.f)) return GPIPE_ERR_INVALID;
+  if (prec != GPIPE_FP32 && prec != GPIPE_BF16) return GPIPE_ERR_INVALID;
+  if (channels % 8 || channels > 8192 || size_t(height) * width > (size_t(1) << 24))
+    return GPIPE_ERR_UNSUPPORTED;
+  gpipe_cell* c = new (std::nothrow) gpipe_cell();
+  if (!c) return GPIPE_ERR_INVALID;
+  c->kind = CELL_CONV;
+  c->L = blocks;
+  c->C = channels;
+  c->Hc = height;
+  c->Wc = width;
+  c->bn_momentum = bn_momentum;
+  c->bn_eps = 1e-5f;
+  c->prec = prec;
+  conv_cell_init(c);
+  *out = c;
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_cell_bind_running(gpipe_cell* c, float* running) {
+  if (!c || !running || c->kind != CELL_CONV || !aligned16(running)) return GPIPE_ERR_INVALID;
+  c->running = running;
   return GPIPE_OK;
 }
 
@@ -446,7 +421,7 @@ gpipe_status gpipe_cell_param_count(const gpipe_cell* c, size_t* n) {
 gpipe_status gpipe_cell_param_offset(const gpipe_cell* c, int layer, int tensor, size_t* offset,
                                      size_t* count) {
   if (!c || !offset || !count || layer < 0 || layer >= c->L || tensor < 0 ||
-      tensor >= GPIPE_N_TENSORS)
+      tensor >= (c->kind == CELL_CONV ? int(GPIPE_CONV_N_TENSORS) : int(GPIPE_N_TENSORS)))
     return GPIPE_ERR_INVALID;
   *offset = size_t(layer) * c->per_layer + c->rel_off[tensor];
   *count = c->count[tensor];
@@ -476,6 +451,8 @@ gpipe_status gpipe_cell_sync_lowp(gpipe_cell* c, void* stream) {
 
 gpipe_status gpipe_cell_workspace_bytes(const gpipe_cell* c, int N, int M, int remat, size_t* bytes) {
   if (!c || !bytes) return GPIPE_ERR_INVALID;
+  if (c->kind == CELL_CONV)
+    return conv_workspace_bytes(c, N, M, remat, bytes) ? GPIPE_OK : GPIPE_ERR_INVALID;
   Plan p;
   if (!make_plan(c, N, M, remat, &p)) return GPIPE_ERR_INVALID;
   *bytes = p.total;
@@ -485,6 +462,9 @@ gpipe_status gpipe_cell_workspace_bytes(const gpipe_cell* c, int N, int M, int r
 gpipe_status gpipe_cell_saved_offset(const gpipe_cell* c, int N, int M, int remat, int micro,
                                      int layer, int which, size_t* offset, size_t* bytes) {
   if (!c || !offset || !bytes) return GPIPE_ERR_INVALID;
+  if (c->kind == CELL_CONV)
+    return conv_saved_offset(c, N, M, remat, micro, layer, which, offset, bytes) ? GPIPE_OK
+                                                                                 : GPIPE_ERR_INVALID;
   Plan p;
   if (!make_plan(c, N, M, remat, &p)) return GPIPE_ERR_INVALID;
   if (micro < 0 || micro >= p.nsets || layer < 0 || layer >= c->L || which < 0 ||
@@ -500,6 +480,9 @@ gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, v
                              void* stream, float* loss_dev) {
   if (!c) return GPIPE_ERR_INVALID;
   if (!c->bound) return GPIPE_ERR_STATE;
+  if (c->kind == CELL_CONV)
+    return conv_cell_step(c, x, target, y, dx, N, M, remat, workspace, ws_bytes,
+                          static_cast<hipStream_t>(stream), loss_dev);
   Plan p;
   if (!make_plan(c, N, M, remat, &p)) return GPIPE_ERR_INVALID;
   if (!x || !target || !y || !workspace || !loss_dev || ws_bytes < p.total) return GPIPE_ERR_INVALID;
@@ -587,6 +570,7 @@ gpipe_status gpipe_cell_gemm_plan(const gpipe_cell* c, int N, int M, int role, i
                                   int* tile_n, int* splits) {
   if (!c || !tile_m || !tile_n || !splits || role < 0 || role >= GPIPE_N_ROLES)
     return GPIPE_ERR_INVALID;
+  if (c->kind == CELL_CONV) return conv_gemm_plan(c, N, M, role, tile_m, tile_n, splits);
   Plan p;
   if (!make_plan(c, N, M, 1, &p)) return GPIPE_ERR_INVALID;
   const int T = p.T, D = c->D, F = c->F, S = c->S, dh = c->D / c->H, bh = p.B * c->H;

@@ -97,6 +97,29 @@ hipError_t sum_partials(const float* part, int nparts, int64_t stride, int cols,
 hipError_t rmsprop(float* w, const float* g, float* ms, void* w_lowp, int64_t n, float lr,
                    float decay, float eps, hipStream_t s);
 
+// ---------------------------------------------------------------- conv cell
+// col [B*H*W, 9*C] from x [B, H, W, C] (pad 1); column (kh*3 + kw)*C + c.
+hipError_t im2col(bool bf16, const void* x, void* col, int B, int H, int W, int C, hipStream_t s);
+// dx = res (optional) + adjoint of im2col applied to dcol (f32); writes f32 and (optional) act.
+hipError_t col2im(bool bf16, const float* dcol, const float* res, float* dx_f32, void* dx_act,
+                  int B, int H, int W, int C, hipStream_t s);
+int bn_chunks(int64_t rows);
+// Per-channel statistics over `rows` rows: stats = (mean[C], rstd[C]); rec (optional) = (mean, biased var).
+hipError_t bn_stats(bool bf16, const void* x, int64_t rows, int C, float eps, float* part,
+                    float* stats, float* rec, hipStream_t s);
+// mode 0: out = relu(bn(a));  mode 1: out = res + bn(a).
+hipError_t bn_apply(bool bf16, int mode, const void* a, const float* stats, const float* gamma,
+                    const float* beta, const void* res, void* out, int64_t rows, int C,
+                    hipStream_t s);
+// Backward of bn (mask: dy is multiplied by [r > 0]); sums = (sum dy*xhat, sum dy) of this
+// batch (part: [chunks][2C] scratch); da = input gradient (act).
+hipError_t bn_bwd(bool bf16, int mask, const float* dy_src, const void* r, const void* a,
+                  const float* stats, const float* gamma, float* part, float* sums, void* da,
+                  int64_t rows, int C, int* nchunk, hipStream_t s);
+// Moving averages from the M micro-batches' recorded moments.
+hipError_t bn_running(const float* rec, int M, int nbn, int C, int64_t n_total, float momentum,
+                      float* running, hipStream_t s);
+
 // dst = bf16(src), n elements.
 hipError_t to_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
 

@@ -18,17 +18,22 @@ GPIPE_FP32, GPIPE_BF16 = 0, 1
 TENSORS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o",
            "ln2_g", "ln2_b", "w_1", "b_1", "w_2", "b_2")
 SAVED = ("x", "h1", "st1", "qkv", "p", "ctx", "x1", "h2", "st2", "u", "g")
+CONV_TENSORS = ("w1", "bn1_g", "bn1_b", "w2", "bn2_g", "bn2_b")
+CONV_SAVED = ("x", "a", "st1", "r", "z", "st2")
 
 EXPORTS = ("gpipe_cell_create", "gpipe_cell_destroy", "gpipe_cell_param_count",
            "gpipe_cell_param_offset", "gpipe_cell_bind", "gpipe_cell_sync_lowp",
            "gpipe_cell_workspace_bytes", "gpipe_cell_saved_offset", "gpipe_cell_step",
            "gpipe_apply_update", "gpipe_partition", "gpipe_status_string",
-           "gpipe_cell_profile", "gpipe_cell_profile_read", "gpipe_cell_gemm_plan")
+           "gpipe_cell_profile", "gpipe_cell_profile_read", "gpipe_cell_gemm_plan",
+           "gpipe_conv_cell_create", "gpipe_cell_bind_running")
 
 ROLES = ("ln1_fwd", "qkv_fwd", "scores_fwd", "softmax_fwd", "pv_fwd", "out_fwd", "ln2_fwd",
          "ffn1_fwd", "ffn2_fwd", "mse", "ffn2_dgrad", "ffn2_wgrad", "ffn1_dgrad", "ffn1_wgrad",
          "ln2_bwd", "out_dgrad", "out_wgrad", "dp", "dv", "softmax_bwd", "dq", "dk", "qkv_dgrad",
-         "qkv_wgrad", "ln1_bwd", "bias_grad", "norm_grad", "loss_reduce", "rmsprop")
+         "qkv_wgrad", "ln1_bwd", "bias_grad", "norm_grad", "loss_reduce", "rmsprop",
+         "conv_fwd", "conv_dgrad", "conv_wgrad", "im2col", "col2im", "bn_stats", "bn_apply",
+         "bn_bwd", "bn_running")
 
 
 class GpipeError(RuntimeError):
@@ -68,6 +73,8 @@ def lib() -> ctypes.CDLL:
                                      ctypes.POINTER(_i)],
             "gpipe_cell_profile_read": [_vp, _i, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_longlong)],
+            "gpipe_conv_cell_create": [_i, _i, _i, _i, ctypes.c_float, _i, ctypes.POINTER(_vp)],
+            "gpipe_cell_bind_running": [_vp, _vp],
         }
         for name, argtypes in sig.items():
             f = getattr(L, name)
@@ -117,6 +124,18 @@ def gpipe_cell_create(layers, d_model, heads, d_ff, seq, causal, precision) -> i
            lib().gpipe_cell_create(layers, d_model, heads, d_ff, seq, int(bool(causal)),
                                    int(precision), ctypes.byref(h)))
     return h.value
+
+
+def gpipe_conv_cell_create(blocks, channels, height, width, bn_momentum, precision) -> int:
+    h = _vp()
+    _check("gpipe_conv_cell_create",
+           lib().gpipe_conv_cell_create(blocks, channels, height, width, float(bn_momentum),
+                                        int(precision), ctypes.byref(h)))
+    return h.value
+
+
+def gpipe_cell_bind_running(cell, running) -> None:
+    _check("gpipe_cell_bind_running", lib().gpipe_cell_bind_running(cell, _ptr(running)))
 
 
 def gpipe_cell_destroy(cell) -> None:
@@ -295,3 +314,47 @@ class Cell:
 
     def update(self, lr, decay, eps, stream=None):
         gpipe_apply_update(self.handle, lr, decay, eps, stream)
+
+
+class ConvCell(Cell):
+    """A conv cell (residual blocks with micro-batch BatchNorm) plus its buffers.
+
+    running: float32 [blocks][2][mean[C], var[C]], initialised to mean 0, var 1."""
+
+    def __init__(self, blocks, channels, height, width, bn_momentum, precision, device="cuda"):
+        import torch
+        self.torch = torch
+        self.layers, self.channels, self.height, self.width = blocks, channels, height, width
+        self.precision = precision
+        self.bf16 = precision in ("bf16", GPIPE_BF16)
+        self.device = device
+        self.handle = gpipe_conv_cell_create(blocks, channels, height, width, bn_momentum,
+                                             GPIPE_BF16 if self.bf16 else GPIPE_FP32)
+        self.n_params = gpipe_cell_param_count(self.handle)
+        self.act_dtype = torch.bfloat16 if self.bf16 else torch.float32
+        n = self.n_params
+        self.master = torch.zeros(n, dtype=torch.float32, device=device)
+        self.w_lowp = torch.zeros(n, dtype=torch.bfloat16, device=device) if self.bf16 else None
+        self.grad = torch.zeros(n, dtype=torch.float32, device=device)
+        self.ms = torch.zeros(n, dtype=torch.float32, device=device)
+        gpipe_cell_bind(self.handle, self.master, self.w_lowp, self.grad, self.ms)
+        self.running = torch.zeros(blocks, 2, 2, channels, dtype=torch.float32, device=device)
+        self.running[:, :, 1, :] = 1.0
+        gpipe_cell_bind_running(self.handle, self.running)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=device)
+        self._ws = None
+
+    @classmethod
+    def from_config(cls, cfg, device="cuda"):
+        return cls(cfg.blocks, cfg.channels, cfg.height, cfg.width, cfg.bn_momentum,
+                   cfg.precision, device)
+
+    def offsets(self):
+        return [[gpipe_cell_param_offset(self.handle, l, t) for t in range(len(CONV_TENSORS))]
+                for l in range(self.layers)]
+
+    def unflatten(self, flat):
+        from .inputs import conv_param_shapes
+        shapes = conv_param_shapes(self.channels)
+        return [{name: np.asarray(flat[o:o + c]).reshape(shapes[name])
+                 for name, (o, c) in zip(CONV_TENSORS, offs)} for offs in self.offsets()]

@@ -217,3 +217,118 @@ def test_partition_validation():
     for costs, k in [([1.0, 2.0], 3), ([1.0, -1.0], 1), ([float("nan")], 1), ([1.0], 0)]:
         with pytest.raises(gpipe.GpipeError):
             gpipe.gpipe_partition(costs, k)
+
+
+# ---------------------------------------------------------------- conv cells
+@pytest.mark.parametrize("cfg", [configs.CONV_TINY, configs.CONV_SMALL, configs.CONV_CELL])
+def test_conv_param_layout_matches_documented_order(cfg):
+    h = gpipe.gpipe_conv_cell_create(cfg.blocks, cfg.channels, cfg.height, cfg.width,
+                                     cfg.bn_momentum, gpipe.GPIPE_BF16)
+    try:
+        n = gpipe.gpipe_cell_param_count(h)
+        assert n == cfg.param_count()
+        shapes = inputs.conv_param_shapes(cfg.channels)
+        expect = 0
+        for l in range(cfg.blocks):
+            for t, name in enumerate(gpipe.CONV_TENSORS):
+                off, cnt = gpipe.gpipe_cell_param_offset(h, l, t)
+                assert off == expect and cnt == int(np.prod(shapes[name]))
+                expect += cnt
+            with pytest.raises(gpipe.GpipeError):
+                gpipe.gpipe_cell_param_offset(h, l, len(gpipe.CONV_TENSORS))
+        assert expect == n
+        assert tuple(gpipe.CONV_TENSORS) == inputs.CONV_NAMES
+    finally:
+        gpipe.gpipe_cell_destroy(h)
+
+
+def test_conv_param_count_of_the_workload():
+    # 8 blocks * (2 * 9 * 256^2 + 4 * 256) = 8 * 1,180,672
+    assert configs.CONV_CELL.param_count() == 9_445_376
+
+
+def test_conv_create_and_bind_validation():
+    E = gpipe.GpipeError
+    with pytest.raises(E) as e:
+        gpipe.gpipe_conv_cell_create(2, 12, 8, 8, 0.9, 0)        # channels not a multiple of 8
+    assert e.value.code == 4
+    for bad in ((0, 16, 8, 8, 0.9), (2, 16, 0, 8, 0.9), (2, 16, 8, 8, 1.0), (2, 16, 8, 8, -0.1)):
+        with pytest.raises(E) as e:
+            gpipe.gpipe_conv_cell_create(*bad, 0)
+        assert e.value.code == 1
+    t = gpipe.gpipe_cell_create(2, 64, 4, 256, 32, 0, 0)
+    try:
+        with pytest.raises(E) as e:                               # not a conv cell
+            gpipe.gpipe_cell_bind_running(t, 256)
+        assert e.value.code == 1
+    finally:
+        gpipe.gpipe_cell_destroy(t)
+    cfg = configs.CONV_TINY
+    h = gpipe.gpipe_conv_cell_create(cfg.blocks, cfg.channels, cfg.height, cfg.width, 0.9, 0)
+    try:
+        gpipe.gpipe_cell_bind(h, 256, None, 512, 768)            # host-side bookkeeping only
+        ws = gpipe.gpipe_cell_workspace_bytes(h, 8, 4, True)
+        with pytest.raises(E) as e:                               # moving averages not bound
+            gpipe.gpipe_cell_step(h, 16, 16, 16, None, 8, 4, True, 16, ws, 0, 16)
+        assert e.value.code == 5
+        with pytest.raises(E):                                    # misaligned running
+            gpipe.gpipe_cell_bind_running(h, 260)
+        gpipe.gpipe_cell_bind_running(h, 1024)
+        with pytest.raises(E) as e:                               # workspace too small
+            gpipe.gpipe_cell_step(h, 16, 16, 16, None, 8, 4, True, 16, ws - 1, 0, 16)
+        assert e.value.code == 1
+        with pytest.raises(E) as e:                               # N % M != 0
+            gpipe.gpipe_cell_step(h, 16, 16, 16, None, 8, 3, True, 16, ws, 0, 16)
+        assert e.value.code == 1
+    finally:
+        gpipe.gpipe_cell_destroy(h)
+
+
+def test_conv_saved_offsets_and_workspace_scaling():
+    cfg = configs.CONV_TINY
+    h = gpipe.gpipe_conv_cell_create(cfg.blocks, cfg.channels, cfg.height, cfg.width, 0.9, 0)
+    try:
+        P = (8 // 4) * cfg.height * cfg.width
+        for remat in (True, False):
+            ws = gpipe.gpipe_cell_workspace_bytes(h, 8, 4, remat)
+            spans = []
+            for m in range(1 if remat else 4):
+                for l in range(cfg.blocks):
+                    for w, name in enumerate(gpipe.CONV_SAVED):
+                        if l == 0 and w == 0:
+                            with pytest.raises(gpipe.GpipeError):
+                                gpipe.gpipe_cell_saved_offset(h, 8, 4, remat, m, l, w)
+                            continue
+                        off, nb = gpipe.gpipe_cell_saved_offset(h, 8, 4, remat, m, l, w)
+                        assert nb == (2 * cfg.channels * 4 if name.startswith("st")
+                                      else P * cfg.channels * 4)
+                        assert off % 256 == 0 and off + nb <= ws
+                        spans.append((off, off + nb))
+            spans.sort()
+            for a, b in zip(spans, spans[1:]):
+                assert a[1] <= b[0]
+        # re-materialization keeps one micro-batch's set (plus the re-computed
+        # output); without it every micro-batch's set is kept
+        r = [gpipe.gpipe_cell_workspace_bytes(h, 64, m, True) for m in (1, 2, 4)]
+        s = [gpipe.gpipe_cell_workspace_bytes(h, 64, m, False) for m in (1, 2, 4)]
+        assert r[0] > r[1] > r[2]
+        set_bytes = (gpipe.gpipe_cell_saved_offset(h, 64, 4, False, 1, 0, 1)[0]
+                     - gpipe.gpipe_cell_saved_offset(h, 64, 4, False, 0, 0, 1)[0])
+        y_bytes = 16 * cfg.height * cfg.width * cfg.channels * 4
+        assert s[2] - r[2] == 3 * set_bytes - y_bytes
+    finally:
+        gpipe.gpipe_cell_destroy(h)
+
+
+def test_conv_gemm_plan_of_the_workload():
+    cfg = configs.CONV_CELL
+    h = gpipe.gpipe_conv_cell_create(cfg.blocks, cfg.channels, cfg.height, cfg.width, 0.9,
+                                     gpipe.GPIPE_BF16)
+    try:
+        R = {n: i for i, n in enumerate(gpipe.ROLES)}
+        # weight gradient: [256 x 2304] reduced over 16384 pixels -> split-K
+        assert gpipe.gpipe_cell_gemm_plan(h, cfg.batch, cfg.micro, R["conv_wgrad"])[2] > 1
+        assert gpipe.gpipe_cell_gemm_plan(h, cfg.batch, cfg.micro, R["conv_fwd"])[:2] == (128, 128)
+        assert gpipe.gpipe_cell_gemm_plan(h, cfg.batch, cfg.micro, R["bn_stats"]) == (0, 0, 0)
+    finally:
+        gpipe.gpipe_cell_destroy(h)
