@@ -12,6 +12,11 @@ timed region starts.
 
 Prints one JSON line.  `value` is tokens per second of the full step
 (update included).
+
+--workload conv_c256_b8 times the convolutional cell instead: 8 residual
+blocks (3x3 conv, micro-batch BatchNorm, ReLU, 3x3 conv, BatchNorm, skip) of
+256 channels on 32 x 32 NHWC images, N = 256 in M = 16 micro-batches; its
+`value` is images per second.
 """
 from __future__ import annotations
 
@@ -73,6 +78,29 @@ def role_work(cfg, n, m):
     return w
 
 
+def conv_role_work(cfg, n, m):
+    """conv cell: ('mfma', flops) or ('hbm', bytes) per launch."""
+    P = (n // m) * cfg.height * cfg.width          # pixels per micro-batch
+    C = cfg.channels
+    eb = 2 if cfg.precision == "bf16" else 4
+    g = 2 * P * C * 9 * C
+    return {
+        "conv_fwd": ("mfma", g), "conv_dgrad": ("mfma", g), "conv_wgrad": ("mfma", g),
+        # im2col: read the image once, write the nine shifted copies
+        "im2col": ("hbm", P * C * eb * 10),
+        # col2im: read the f32 column gradient (and the f32 residual), write f32 (+ act)
+        "col2im": ("hbm", P * C * (36 + 4 + 4)),
+        # statistics: two passes over the input
+        "bn_stats": ("hbm", 2 * P * C * eb),
+        # apply: read the input (+ the residual half the time), write the output
+        "bn_apply": ("hbm", P * C * eb * 2.5),
+        # backward: two passes over dy (f32) and the input (+ the ReLU output), write da
+        "bn_bwd": ("hbm", P * C * (2 * 4 + 2 * eb + eb + eb)),
+        "mse": ("hbm", P * C * (3 * eb + 4)),
+        "rmsprop": ("hbm", cfg.param_count() * (20 + (2 if eb == 2 else 0))),
+    }
+
+
 # ------------------------------------------------------------------ CPU baseline (oracle)
 def cpu_baseline(cfg, n, m):
     """The oracle on one micro-batch of one layer (fwd + remat + bwd, fp64) plus that
@@ -105,6 +133,72 @@ def cpu_baseline(cfg, n, m):
             "sample_seconds": round(t2 - t0, 2)}
 
 
+def conv_cpu_baseline(cfg, n, m):
+    """The oracle on one micro-batch through one block (fwd + remat + bwd, fp64) plus
+    that block's RMSProp, scaled to the full step: M micro-batches x blocks + updates."""
+    from micro_pipelined_re_amd import inputs
+    from oracle import conv_cell as cc
+    from oracle import transformer_cell as tc
+    b = n // m
+    p = [inputs.conv_block_params(cfg.seed, 0, cfg.channels, bf16=cfg.precision == "bf16")]
+    x, t = inputs.conv_cell_data(cfg, batch=b)
+    t0 = time.perf_counter()
+    out = cc.cell_step(p, x, t, 1, eps=cfg.bn_eps, remat=True)
+    t1 = time.perf_counter()
+    for k in p[0]:
+        w = p[0][k].astype(np.float64)
+        tc.rmsprop(w, out["grads"][0][k], np.zeros_like(w), cfg.lr, cfg.decay, cfg.eps)
+    t2 = time.perf_counter()
+    step_s = m * cfg.blocks * (t1 - t0) + cfg.blocks * (t2 - t1)
+    threads = None
+    try:
+        import threadpoolctl
+        threads = max(i["num_threads"] for i in threadpoolctl.threadpool_info()) or None
+    except Exception:
+        pass
+    return {"value": n / step_s, "unit": "images/s",
+            "cores": threads or os.cpu_count(), "kind": "oracle",
+            "sample": (f"one micro-batch ({b} images of {cfg.height}x{cfg.width}x{cfg.channels}) "
+                       f"through one block (forward, re-materialized forward, backward; numpy "
+                       f"float64) plus that block's RMSProp, timed {t2 - t0:.1f} s, scaled by "
+                       f"{m} micro-batches x {cfg.blocks} blocks"),
+            "sample_seconds": round(t2 - t0, 2)}
+
+
+def setup_transformer(cfg, n, m, remat, dev):
+    import torch
+    from micro_pipelined_re_amd import gpipe, inputs
+    cell = gpipe.Cell.from_config(cfg, dev)
+    flat = np.empty(cell.n_params, np.float32)
+    for l, offs in enumerate(cell.offsets()):
+        lp = inputs.layer_params(cfg.seed, l, cfg.d_model, cfg.d_ff, bf16=True)
+        for name, (o, c) in zip(gpipe.TENSORS, offs):
+            flat[o:o + c] = lp[name].ravel()
+    cell.load_params(flat)
+    del flat
+    x_h, t_h = inputs.cell_data(cfg)
+    x, t = cell.to_device(x_h), cell.to_device(t_h)
+    del x_h, t_h
+    return cell, x, t
+
+
+def setup_conv(cfg, n, m, remat, dev):
+    from micro_pipelined_re_amd import gpipe, inputs
+    cell = gpipe.ConvCell.from_config(cfg, dev)
+    flat = np.empty(cell.n_params, np.float32)
+    bf = cfg.precision == "bf16"
+    for l, offs in enumerate(cell.offsets()):
+        lp = inputs.conv_block_params(cfg.seed, l, cfg.channels, bf16=bf)
+        for name, (o, c) in zip(gpipe.CONV_TENSORS, offs):
+            flat[o:o + c] = lp[name].ravel()
+    cell.load_params(flat)
+    del flat
+    x_h, t_h = inputs.conv_cell_data(cfg)
+    x, t = cell.to_device(x_h), cell.to_device(t_h)
+    del x_h, t_h
+    return cell, x, t
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -113,6 +207,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--micro", type=int, default=None, help="override M")
     ap.add_argument("--no-remat", action="store_true", help="keep every micro-batch's activations")
+    ap.add_argument("--workload", default="cell_d2048_L8_causal",
+                    choices=("cell_d2048_L8_causal", "conv_c256_b8"))
+    ap.add_argument("--precision", default=None, choices=("bf16", "fp32"),
+                    help="override the workload's precision")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-all", action="store_true",
                     help="time every kernel role inside the timed region")
@@ -125,27 +223,23 @@ def main():
     import torch
     from micro_pipelined_re_amd import configs, gpipe, inputs
 
-    cfg = configs.CELL_2048
+    conv = args.workload == "conv_c256_b8"
+    cfg = configs.CONV_CELL if conv else configs.CELL_2048
+    if args.precision:
+        cfg = cfg.with_(precision=args.precision)
     n = cfg.batch
     m = args.micro or cfg.micro
     remat = not args.no_remat
     dev = "cuda"
     torch.cuda.set_device(0)
-    log(f"[bench] {cfg.name}: L={cfg.layers} D={cfg.d_model} H={cfg.heads} F={cfg.d_ff} "
-        f"S={cfg.seq} N={n} M={m} remat={remat}")
-
-    cell = gpipe.Cell.from_config(cfg, dev)
+    if conv:
+        log(f"[bench] {cfg.name}: blocks={cfg.blocks} C={cfg.channels} {cfg.height}x{cfg.width} "
+            f"N={n} M={m} remat={remat} {cfg.precision}")
+    else:
+        log(f"[bench] {cfg.name}: L={cfg.layers} D={cfg.d_model} H={cfg.heads} F={cfg.d_ff} "
+            f"S={cfg.seq} N={n} M={m} remat={remat}")
     t0 = time.perf_counter()
-    flat = np.empty(cell.n_params, np.float32)
-    for l, offs in enumerate(cell.offsets()):
-        lp = inputs.layer_params(cfg.seed, l, cfg.d_model, cfg.d_ff, bf16=True)
-        for name, (o, c) in zip(gpipe.TENSORS, offs):
-            flat[o:o + c] = lp[name].ravel()
-    cell.load_params(flat)
-    del flat
-    x_h, t_h = inputs.cell_data(cfg)
-    x, t = cell.to_device(x_h), cell.to_device(t_h)
-    del x_h, t_h
+    cell, x, t = (setup_conv if conv else setup_transformer)(cfg, n, m, remat, dev)
     y = torch.empty_like(x)
     dx = torch.empty_like(x)
     ws, ws_bytes = cell.workspace(n, m, remat)
@@ -166,7 +260,7 @@ def main():
         step()
         torch.cuda.synchronize()
         log(f"[bench] warmup step {i} done, loss {cell.loss.item():.6f}")
-    work = role_work(cfg, n, m)
+    work = (conv_role_work if conv else role_work)(cfg, n, m)
     prof = {}
     for r, name in enumerate(gpipe.ROLES):
         ms_tot, cnt = gpipe.gpipe_cell_profile_read(cell.handle, r)
@@ -219,7 +313,8 @@ def main():
                 e["split_k"] = sp_
         if kind == "mfma":
             tf = per / (ms_tot / cnt * 1e-3) / 1e12
-            e.update(tflops=round(tf, 1), frac_bf16_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+            pk = PEAK_BF16_TFLOPS if cfg.precision == "bf16" else PEAK_FP32_TFLOPS
+            e.update(tflops=round(tf, 1), frac_mfma_peak=round(tf / pk, 4))
         elif kind == "hbm":
             gb = per / (ms_tot / cnt * 1e-3) / 1e9
             e.update(gbs=round(gb, 1), frac_hbm_peak=round(gb / PEAK_HBM_GBS, 4))
@@ -229,8 +324,9 @@ def main():
     kind, per = work[dominant]
     d_ms, d_cnt = src[dominant]
     avg_s = d_ms / d_cnt * 1e-3
+    peak_mfma = PEAK_BF16_TFLOPS if cfg.precision == "bf16" else PEAK_FP32_TFLOPS
     if kind == "mfma":
-        roof = {"bound": "mfma", "achieved": round(per / avg_s / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+        roof = {"bound": "mfma", "achieved": round(per / avg_s / 1e12, 2), "peak": peak_mfma,
                 "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": round(per / avg_s / 1e9, 1), "peak": PEAK_HBM_GBS,
@@ -245,23 +341,33 @@ def main():
 
     gemm_flops = sum(work[k][1] * src[k][1] for k in src if work.get(k, ("", 0))[0] == "mfma")
     gemm_ms = sum(src[k][0] for k in src if work.get(k, ("", 0))[0] == "mfma")
-    tokens = n * cfg.seq
     keep_bytes = gpipe.gpipe_cell_workspace_bytes(cell.handle, n, m, False)
     act_bytes = x.numel() * x.element_size()
+    if conv:
+        units, unit = n, "images/s"
+        config = {"workload": cfg.name, "blocks": cfg.blocks, "channels": cfg.channels,
+                  "height": cfg.height, "width": cfg.width, "global_batch": n,
+                  "micro_batches": m, "remat": remat, "bn_momentum": cfg.bn_momentum,
+                  "parallelism": "single-gpu cell"}
+        metric = "train images/sec per conv cell step (fwd+remat+bwd), MFMA util; peak act bytes"
+    else:
+        units, unit = n * cfg.seq, "tokens/s"
+        config = {"workload": cfg.name, "layers": cfg.layers, "d_model": cfg.d_model,
+                  "heads": cfg.heads, "d_ff": cfg.d_ff, "seq_len": cfg.seq, "causal": cfg.causal,
+                  "global_batch": n, "micro_batches": m, "remat": remat,
+                  "parallelism": "single-gpu cell"}
+        metric = METRIC
     out = {
-        "metric": METRIC,
-        "value": round(tokens / (ms_step * 1e-3), 1),
-        "unit": "tokens/s",
+        "metric": metric,
+        "value": round(units / (ms_step * 1e-3), 1),
+        "unit": unit,
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg.name, "layers": cfg.layers, "d_model": cfg.d_model,
-                   "heads": cfg.heads, "d_ff": cfg.d_ff, "seq_len": cfg.seq, "causal": cfg.causal,
-                   "global_batch": n, "micro_batches": m, "remat": remat,
-                   "parallelism": "single-gpu cell"},
+        "dtype": "bf16" if cfg.precision == "bf16" else "f32", "data": "synthetic",
+        "config": config,
         "roofline": roof,
-        "mfma_util_gemm": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        "mfma_util_gemm": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak_mfma, 4)
         if gemm_ms else None,
         "peak_act_bytes": {"workspace_plan": ws_bytes, "boundary_x_y_dx": 3 * act_bytes,
                            "total": ws_bytes + 3 * act_bytes,
@@ -272,7 +378,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a CPU sample ...")
-        out["cpu_baseline"] = cpu_baseline(cfg, n, m)
+        out["cpu_baseline"] = (conv_cpu_baseline if conv else cpu_baseline)(cfg, n, m)
     print(json.dumps(out), flush=True)
 
 

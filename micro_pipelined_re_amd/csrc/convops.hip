@@ -95,94 +95,140 @@ hipError_t col2im(bool bf16, const float* dcol, const float* res, float* dx_f32,
 }
 
 // ------------------------------------------------------------ BatchNorm statistics
-// Column partial sums over blocks of kBnRows rows: a block covers 256
-// channels x kBnRows rows; thread (g, c8) sums 8 channels over rows g, g+8, ...
-// of the block, the 8 row groups are combined in order through LDS.
-// mean == nullptr: sums x;  otherwise sums (x - mean)^2.
-constexpr int kBnRows = 128;
+// One pass over the input.  A block covers 256 channels x kBnRows rows (a
+// chunk); thread (rg, cg) holds rows rg, rg+8, ... of the chunk for channels
+// cg*8 .. cg*8+7 in registers.  Per chunk it writes the channel sums and the
+// sums of squared deviations from the chunk's own mean (M2); the finalize
+// merges the chunks with the exact pairwise formula
+//   mean = sum_k S_k / n,   M2 = sum_k (M2_k + n_k (S_k/n_k - mean)^2),
+// in a fixed order, so the result is reproducible bit for bit.
+constexpr int kBnRows = 32;
+constexpr int kBnRowsPerThread = kBnRows / 8;
 int bn_chunks(int64_t rows) { return int((rows + kBnRows - 1) / kBnRows); }
 
 template <typename T>
-__global__ __launch_bounds__(256) void bn_partial_kernel(const T* __restrict__ x,
-                                                         const float* __restrict__ mean,
+__global__ __launch_bounds__(256) void bn_moments_kernel(const T* __restrict__ x,
                                                          float* __restrict__ part, int64_t rows,
                                                          int C) {
   __shared__ float red[8][257];
+  __shared__ float mean_k[256];
   const int cg = threadIdx.x & 31, rg = threadIdx.x >> 5;
   const int c0 = blockIdx.x * 256 + cg * 8;
   const int64_t r0 = int64_t(blockIdx.y) * kBnRows;
-  const int64_t r1 = r0 + kBnRows < rows ? r0 + kBnRows : rows;
+  const int nk = int(r0 + kBnRows < rows ? kBnRows : rows - r0);
+  float v[kBnRowsPerThread][8];
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (c0 < C) {
-    float mu[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (mean) load8<float>(mean + c0, mu);
-    for (int64_t r = r0 + rg; r < r1; r += 8) {
-      float v[8];
-      load8<T>(x + r * C + c0, v);
+  const bool cok = c0 < C;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float d = v[e] - mu[e];
-        s[e] += mean ? d * d : v[e];
-      }
+  for (int i = 0; i < kBnRowsPerThread; ++i) {
+    const int r = rg + 8 * i;
+    if (cok && r < nk) {
+      load8<T>(x + (r0 + r) * C + c0, v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] += v[i][e];
     }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[rg][cg * 8 + e] = s[e];
   __syncthreads();
   const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c < C) {
-    float t = red[0][threadIdx.x];
+  float sum = red[0][threadIdx.x];
 #pragma unroll
-    for (int g = 1; g < 8; ++g) t += red[g][threadIdx.x];
-    part[int64_t(blockIdx.y) * C + c] = t;
+  for (int g = 1; g < 8; ++g) sum += red[g][threadIdx.x];
+  mean_k[threadIdx.x] = sum / float(nk);
+  __syncthreads();
+  float q[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kBnRowsPerThread; ++i) {
+    const int r = rg + 8 * i;
+    if (cok && r < nk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = v[i][e] - mean_k[cg * 8 + e];
+        q[e] += d * d;
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rg][cg * 8 + e] = q[e];
+  __syncthreads();
+  if (c < C) {
+    float m2 = red[0][threadIdx.x];
+#pragma unroll
+    for (int g = 1; g < 8; ++g) m2 += red[g][threadIdx.x];
+    part[int64_t(blockIdx.y) * 2 * C + c] = sum;
+    part[int64_t(blockIdx.y) * 2 * C + C + c] = m2;
   }
 }
 
-// mode 0: out1 = sum/n (mean), copied to out2 if given.
-// mode 1: v = sum/n (biased variance): out1 = 1/sqrt(v + eps), out2 = v if given.
-__global__ __launch_bounds__(256) void bn_finalize_kernel(const float* __restrict__ part, int nchunk,
-                                                          int C, float inv_n, float eps, int mode,
-                                                          float* __restrict__ out1,
-                                                          float* __restrict__ out2) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= C) return;
+// Block: 32 channels x 8 chunk groups.  stats = (mean, rstd); rec (optional)
+// = (mean, biased variance).
+__global__ __launch_bounds__(256) void bn_merge_kernel(const float* __restrict__ part, int nchunk,
+                                                       int64_t rows, int C, float eps,
+                                                       float* __restrict__ stats,
+                                                       float* __restrict__ rec) {
+  __shared__ float red[8][33];
+  __shared__ float mean_s[32];
+  const int cl = threadIdx.x & 31, g = threadIdx.x >> 5;
+  const int c = blockIdx.x * 32 + cl;
+  const bool ok = c < C;
   float s = 0.f;
-  for (int k = 0; k < nchunk; ++k) s += part[int64_t(k) * C + c];
-  const float v = s * inv_n;
-  if (mode == 0) {
-    out1[c] = v;
-    if (out2) out2[c] = v;
-  } else {
-    out1[c] = 1.0f / sqrtf(v + eps);
-    if (out2) out2[c] = v;
+  if (ok) {
+#pragma unroll 8
+    for (int k = g; k < nchunk; k += 8) s += part[int64_t(k) * 2 * C + c];
+  }
+  red[g][cl] = s;
+  __syncthreads();
+  if (g == 0) {
+    float t = red[0][cl];
+    for (int j = 1; j < 8; ++j) t += red[j][cl];
+    mean_s[cl] = t / float(rows);
+  }
+  __syncthreads();
+  const float mean = mean_s[cl];
+  float m2 = 0.f;
+  if (ok)
+#pragma unroll 8
+    for (int k = g; k < nchunk; k += 8) {
+      const float nk = float(int64_t(k) * kBnRows + kBnRows <= rows ? kBnRows
+                                                                    : rows - int64_t(k) * kBnRows);
+      const float d = part[int64_t(k) * 2 * C + c] / nk - mean;
+      m2 += part[int64_t(k) * 2 * C + C + c] + nk * d * d;
+    }
+  __syncthreads();
+  red[g][cl] = m2;
+  __syncthreads();
+  if (g == 0 && ok) {
+    float t = red[0][cl];
+    for (int j = 1; j < 8; ++j) t += red[j][cl];
+    const float var = t / float(rows);
+    stats[c] = mean;
+    stats[C + c] = 1.0f / sqrtf(var + eps);
+    if (rec) {
+      rec[c] = mean;
+      rec[C + c] = var;
+    }
   }
 }
 
 // stats: [2][C] = (mean, rstd).  rec (optional): [2][C] = (mean, biased var).
+// part: [bn_chunks(rows)][2C] scratch.
 hipError_t bn_stats(bool bf16, const void* x, int64_t rows, int C, float eps, float* part,
                     float* stats, float* rec, hipStream_t s) {
   if (rows == 0 || C == 0) return hipSuccess;
   const int nch = bn_chunks(rows);
-  dim3 grid((C + 255) / 256, nch);
-  const float inv_n = float(1.0 / double(rows));
-  for (int pass = 0; pass < 2; ++pass) {
-    const float* mean = pass == 0 ? nullptr : stats;
-    if (bf16)
-      hipLaunchKernelGGL(bn_partial_kernel<bf16_t>, grid, dim3(256), 0, s,
-                         static_cast<const bf16_t*>(x), mean, part, rows, C);
-    else
-      hipLaunchKernelGGL(bn_partial_kernel<float>, grid, dim3(256), 0, s,
-                         static_cast<const float*>(x), mean, part, rows, C);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    float* out1 = pass == 0 ? stats : stats + C;
-    float* out2 = rec ? (pass == 0 ? rec : rec + C) : nullptr;
-    hipLaunchKernelGGL(bn_finalize_kernel, dim3((C + 255) / 256), dim3(256), 0, s, part, nch, C,
-                       inv_n, eps, pass, out1, out2);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  const dim3 grid((C + 255) / 256, nch);
+  if (bf16)
+    hipLaunchKernelGGL(bn_moments_kernel<bf16_t>, grid, dim3(256), 0, s,
+                       static_cast<const bf16_t*>(x), part, rows, C);
+  else
+    hipLaunchKernelGGL(bn_moments_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(x), part, rows, C);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bn_merge_kernel, dim3((C + 31) / 32), dim3(256), 0, s, part, nch, rows, C, eps,
+                     stats, rec);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------ BatchNorm apply

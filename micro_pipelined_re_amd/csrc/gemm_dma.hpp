@@ -7,12 +7,17 @@
 //
 // Tile layouts in LDS (k-tile depth BK = 64 or 32):
 //   k-contiguous operand  [rows][BK]: rows of BK/8 16-byte chunks; chunk c of
-//       row r stored at position c ^ ((r ^ r>>3) & 7) (BK 64) or
-//       c ^ ((r >> 2) & 3) (BK 32); MFMA fragments are one ds_read_b128
-//       (16 rows x one chunk, conflict-free within each 8-lane phase).
+//       row r stored at position c ^ (r & 7) (BK 64) or c ^ ((r >> 2) & 3)
+//       (BK 32); MFMA fragments are one ds_read_b128 (16 rows x one chunk).
+//       Measured with the LDS bank-conflict counter on gfx950, the plain
+//       c ^ (r & 7) reads without conflicts where c ^ ((r ^ r>>3) & 7)
+//       spends a quarter of its LDS cycles in conflicts.
 //   m-contiguous operand  [64 k][R]: rows of R elements in 32-byte granules,
-//       granule q of k-row r stored at q ^ (r & 7) (R >= 128) or q ^ (r & 3)
-//       (R = 64); fragments are two ds_read_b64_tr_b16: within a group of 16
+//       granule q of k-row r stored at q ^ f(r), f(r) = (r & 3) | (r>>3 & 1) << 2
+//       (R >= 128) or (r>>1 & 1) | (r>>3 & 1) << 1 (R = 64), which the LDS
+//       bank-conflict counter shows conflict-free for the fragment reads (a
+//       plain r & 7 conflicts half of the time); fragments are two
+//       ds_read_b64_tr_b16: within a group of 16
 //       lanes, lane s points at (k0 + s/4, m0 + 4*(s%4)) and lane i receives
 //       the four k-rows k0..k0+3 of column m0 + i.
 // Rows past the operand's extent are read from its last row (valid memory;
@@ -54,15 +59,21 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // granule swizzle of an m-contiguous tile with R elements per k-row
 template <int R>
+__device__ __forceinline__ int mn_swz(int k) {
+  // one fragment read touches k-rows {0..3, 8..11, 16..19, 24..27} (+ 32 ks);
+  // these map to distinct 32-byte granule slots within each half wave
+  if constexpr (R >= 128) return (k & 3) | (((k >> 3) & 1) << 2);
+  else return ((k >> 1) & 1) | (((k >> 3) & 1) << 1);
+}
+template <int R>
 __device__ __forceinline__ int mn_off(int k, int m) {
-  constexpr int mask = (R >= 128) ? 7 : 3;
-  return k * R + ((((m >> 4) ^ (k & mask))) << 4) + (m & 15);
+  return k * R + (((m >> 4) ^ mn_swz<R>(k)) << 4) + (m & 15);
 }
 
 // element offset of (row, 16-byte chunk) in a swizzled k-contiguous tile
 template <int BK>
 __device__ __forceinline__ int kswz_off(int row, int chunk) {
-  if constexpr (BK == 64) return row * 64 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 3);
+  if constexpr (BK == 64) return row * 64 + ((chunk ^ (row & 7)) << 3);
   else return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3);
 }
 
@@ -85,16 +96,15 @@ struct DmaOperand {
         constexpr int RPK = 1024 / (BK * 2); // rows per kilobyte
         const int r = blk * RPK + lane / CPR;
         const int p = lane % CPR;
-        const int c = (BK == 64) ? (p ^ ((r ^ (r >> 3)) & 7)) : (p ^ ((r >> 2) & 3));
+        const int c = (BK == 64) ? (p ^ (r & 7)) : (p ^ ((r >> 2) & 3));
         const int gr = min(row0 + r, rows_total - 1);
         off[q] = int64_t(gr) * ld + kbeg + c * 8;
       } else {
-        constexpr int mask = (ROWS >= 128) ? 7 : 3;
         const int byte = blk * 1024 + lane * 16;
         const int kr = byte / (ROWS * 2);
         const int within = byte % (ROWS * 2);
         const int p = within >> 5, h = (within >> 4) & 1;
-        const int m = ((p ^ (kr & mask)) << 4) + h * 8;
+        const int m = ((p ^ mn_swz<ROWS>(kr)) << 4) + h * 8;
         const int gm = min(row0 + m, rows_total - 8);
         off[q] = int64_t(kbeg + kr) * ld + gm;
       }

@@ -121,7 +121,7 @@ struct Cfg {
 
 // element offset of (row, 8-element chunk) in a swizzled [rows][64] bf16 tile
 __device__ __forceinline__ int swz_off(int row, int chunk) {
-  return row * 64 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 3);
+  return row * 64 + ((chunk ^ (row & 7)) << 3);
 }
 
 template <int ROWS, int LAY>

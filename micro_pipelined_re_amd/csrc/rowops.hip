@@ -360,7 +360,7 @@ hipError_t mse_fwd_bwd(bool bf16, const void* y, const void* t, float* dy_f32, v
 // A block covers 256 columns x kColRows rows: thread (g, c) sums 8 consecutive
 // columns over rows g, g+8, ... of the chunk; the 8 row groups are then added
 // in order through LDS.  Columns must be a multiple of 8.
-constexpr int kColRows = 128;
+constexpr int kColRows = 32;
 int colsum_chunks(int rows) { return (rows + kColRows - 1) / kColRows; }
 
 template <typename T>
@@ -415,8 +415,10 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restri
   const int cl = threadIdx.x % CW, pg = threadIdx.x / CW;
   const int c = blockIdx.x * CW + cl;
   float s = 0.f;
-  if (c < cols)
+  if (c < cols) {
+#pragma unroll 8
     for (int p = pg; p < nparts; p += G) s += part[int64_t(p) * stride + c];
+  }
   red[threadIdx.x] = s;
   __syncthreads();
   // tree over the G groups of this column, fixed pairing
