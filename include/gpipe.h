@@ -71,7 +71,11 @@ typedef enum {
   GPIPE_SAVED_H1,    /* LN1 output [T, D]                                     */
   GPIPE_SAVED_ST1,   /* LN1 (mean, rstd) [T, 2] float32                       */
   GPIPE_SAVED_QKV,   /* [T, 3D]                                               */
-  GPIPE_SAVED_P,     /* softmax [N/M, H, S, ldS], ldS = S rounded up to 8     */
+  GPIPE_SAVED_P,     /* softmax [N/M, H, S, ldS], ldS = S rounded up to 8; in
+                      * bf16 cells with head dim 64 or 128 (fused attention)
+                      * instead the base-2 log-sum-exp of every query row,
+                      * float32 [N/M, H, S]: lse2 = log2 sum_k 2^(x_k),
+                      * x = (q . k) * log2(e) / sqrt(head dim)                 */
   GPIPE_SAVED_CTX,   /* attention output before the projection [T, D]         */
   GPIPE_SAVED_X1,    /* residual after attention [T, D]                        */
   GPIPE_SAVED_H2,    /* LN2 output [T, D]                                     */
@@ -243,6 +247,9 @@ typedef enum {
   GPIPE_ROLE_CONV_FWD, GPIPE_ROLE_CONV_DGRAD, GPIPE_ROLE_CONV_WGRAD, GPIPE_ROLE_IM2COL,
   GPIPE_ROLE_COL2IM, GPIPE_ROLE_BN_STATS, GPIPE_ROLE_BN_APPLY, GPIPE_ROLE_BN_BWD,
   GPIPE_ROLE_BN_RUNNING,
+  /* fused attention (bf16, head dim 64 or 128): forward; backward row sums
+   * of dO * O; dK and dV per key block; dQ per query block */
+  GPIPE_ROLE_ATTN_FWD, GPIPE_ROLE_ATTN_DELTA, GPIPE_ROLE_ATTN_DKDV, GPIPE_ROLE_ATTN_DQ,
   GPIPE_N_ROLES
 } gpipe_role;
 

@@ -18,7 +18,8 @@ PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libgpipe_cell.so")
 SOURCES = ["gemm.hip", "gemm_fwd.hip", "gemm_dgrad.hip", "gemm_wgrad.hip", "gemm_attn.hip",
-           "gemm_f32.hip", "rowops.hip", "convops.hip", "conv_cell.hip", "gpipe_api.hip"]
+           "gemm_f32.hip", "rowops.hip", "convops.hip", "conv_cell.hip", "attn.hip",
+           "gpipe_api.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

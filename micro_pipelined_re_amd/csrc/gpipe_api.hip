@@ -26,8 +26,9 @@ namespace {
 //   sets:   remat ? 1 : M micro-batch sets; each set holds, for every layer,
 //           the saved tensors of gpipe_saved (layer 0 has no X slot)
 //   yre:    output of the re-materialized forward [T, D] (remat only)
-//   scores: float32 [B*H, S, ldS]  (forward scores, backward dP)
-//   ds:     act [B*H, S, ldS]
+//   scores: float32 [B*H, S, ldS]  (forward scores, backward dP); with fused
+//           attention float32 [B*H, S], the row sums of dO * O
+//   ds:     act [B*H, S, ldS] (unfused attention only)
 //   r0, r1, dm: float32 [T, D]   (residual-stream gradients, LN input grads)
 //   a0, a1, dctx: act [T, D]
 //   du: act [T, F];  dqkv: act [T, 3D]
@@ -36,6 +37,7 @@ namespace {
 //   msepart: float32 [M, mse blocks]
 struct Plan {
   int N, M, B, T, ldS;
+  bool flash;  // fused attention kernels
   size_t eb;
   size_t saved_off[GPIPE_N_SAVED];  // inside one layer's slot
   size_t saved_bytes[GPIPE_N_SAVED];
@@ -60,8 +62,11 @@ bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
   const size_t eb = c->prec == GPIPE_BF16 ? 2 : 4;
   p->eb = eb;
   const size_t pbytes = B * H * S * size_t(p->ldS);
+  p->flash = flash_ok(c->prec == GPIPE_BF16, c->D / c->H);
+  // fused attention keeps the row log-sum-exp instead of the probabilities
+  const size_t p_saved = p->flash ? B * H * S * 4 : pbytes * eb;
   const size_t sizes[GPIPE_N_SAVED] = {
-      T * D * eb, T * D * eb, T * 2 * 4, T * 3 * D * eb, pbytes * eb, T * D * eb,
+      T * D * eb, T * D * eb, T * 2 * 4, T * 3 * D * eb, p_saved, T * D * eb,
       T * D * eb, T * D * eb, T * 2 * 4, T * F * eb, T * F * eb};
   size_t off = 0;
   for (int i = 0; i < GPIPE_N_SAVED; ++i) {
@@ -80,8 +85,9 @@ bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
     return at;
   };
   p->yre = take(remat ? T * D * eb : 0);
-  p->scores = take(pbytes * 4);
-  p->ds = take(pbytes * eb);
+  // unfused attention: scores / dP (f32) and dS; fused: the row sums of dO * O
+  p->scores = take(p->flash ? B * H * S * 4 : pbytes * 4);
+  p->ds = take(p->flash ? 0 : pbytes * eb);
   p->r0 = take(T * D * 4);
   p->r1 = take(T * D * 4);
   p->dm = take(T * D * 4);
@@ -219,11 +225,16 @@ gpipe_status layer_forward(const Ctx& x, int set, int l, const void* xin, void* 
   Bat SC{scores, ldS, sp, int64_t(S) * ldS};
   Bat PP{P, ldS, sp, int64_t(S) * ldS};
   Bat CX{ctx, D, int64_t(S) * D, dh};
-  GP_RUN(x, GPIPE_ROLE_SCORES_FWD, bmm(x, GPIPE_ROLE_SCORES_FWD, S, S, dh, Q, K, SC,
-               c->causal ? CAUSAL_SKIP_UPPER : CAUSAL_NONE, scale));
-  GP_RUN(x, GPIPE_ROLE_SOFTMAX_FWD, softmax_fwd(x.bf16, scores, P, int64_t(p.B) * H * S, S, ldS, c->causal, x.s));
-  GP_RUN(x, GPIPE_ROLE_PV_FWD, bmm(x, GPIPE_ROLE_PV_FWD, S, dh, S, PP, V, CX,
-               c->causal ? CAUSAL_K_UPTO_M : CAUSAL_NONE, 1.0f));
+  if (p.flash) {
+    GP_RUN(x, GPIPE_ROLE_ATTN_FWD, flash_fwd(qkv, ctx, static_cast<float*>(P), p.B, H, S, D,
+                                             c->causal, x.s));
+  } else {
+    GP_RUN(x, GPIPE_ROLE_SCORES_FWD, bmm(x, GPIPE_ROLE_SCORES_FWD, S, S, dh, Q, K, SC,
+                 c->causal ? CAUSAL_SKIP_UPPER : CAUSAL_NONE, scale));
+    GP_RUN(x, GPIPE_ROLE_SOFTMAX_FWD, softmax_fwd(x.bf16, scores, P, int64_t(p.B) * H * S, S, ldS, c->causal, x.s));
+    GP_RUN(x, GPIPE_ROLE_PV_FWD, bmm(x, GPIPE_ROLE_PV_FWD, S, dh, S, PP, V, CX,
+                 c->causal ? CAUSAL_K_UPTO_M : CAUSAL_NONE, 1.0f));
+  }
   GP_RUN(x, GPIPE_ROLE_OUT_FWD, mm(x, GPIPE_ROLE_OUT_FWD, T, D, D, ctx, D, x.wmat(l, GPIPE_W_O), D, x1, D,
               x.wf32(l, GPIPE_B_O), xin, D));
   GP_RUN(x, GPIPE_ROLE_LN2_FWD, layernorm_fwd(x.bf16, x1, h2, st2, x.wf32(l, GPIPE_LN2_G), x.wf32(l, GPIPE_LN2_B), T, D,
@@ -308,15 +319,22 @@ gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int b
   Bat PP{P, ldS, sp, int64_t(S) * ldS}, DP{dP, ldS, sp, int64_t(S) * ldS}, DS{dS, ldS, sp, int64_t(S) * ldS};
   Bat DC{dctx, D, sd, dh};
   const int cz = c->causal;
-  GP_RUN(x, GPIPE_ROLE_DP, bmm(x, GPIPE_ROLE_DP, S, S, dh, DC, V, DP,
-               cz ? CAUSAL_SKIP_UPPER : CAUSAL_NONE, 1.0f));
-  GP_RUN(x, GPIPE_ROLE_DV, bmm(x, GPIPE_ROLE_DV, S, dh, S, PP, DC, dV,
-               cz ? CAUSAL_K_FROM_M : CAUSAL_NONE, 1.0f));
-  GP_RUN(x, GPIPE_ROLE_SOFTMAX_BWD, softmax_bwd(bf, P, dP, dS, int64_t(p.B) * H * S, S, ldS, cz, scale, x.s));
-  GP_RUN(x, GPIPE_ROLE_DQ, bmm(x, GPIPE_ROLE_DQ, S, dh, S, DS, K, dQ,
-               cz ? CAUSAL_K_UPTO_M : CAUSAL_NONE, 1.0f));
-  GP_RUN(x, GPIPE_ROLE_DK, bmm(x, GPIPE_ROLE_DK, S, dh, S, DS, Q, dK,
-               cz ? CAUSAL_K_FROM_M : CAUSAL_NONE, 1.0f));
+  if (p.flash) {
+    const float* lse2 = static_cast<const float*>(P);
+    GP_RUN(x, GPIPE_ROLE_ATTN_DELTA, flash_bwd(qkv, ctx, dctx, lse2, dP, dqkv, p.B, H, S, D, cz, x.s, 0));
+    GP_RUN(x, GPIPE_ROLE_ATTN_DKDV, flash_bwd(qkv, ctx, dctx, lse2, dP, dqkv, p.B, H, S, D, cz, x.s, 1));
+    GP_RUN(x, GPIPE_ROLE_ATTN_DQ, flash_bwd(qkv, ctx, dctx, lse2, dP, dqkv, p.B, H, S, D, cz, x.s, 2));
+  } else {
+    GP_RUN(x, GPIPE_ROLE_DP, bmm(x, GPIPE_ROLE_DP, S, S, dh, DC, V, DP,
+                 cz ? CAUSAL_SKIP_UPPER : CAUSAL_NONE, 1.0f));
+    GP_RUN(x, GPIPE_ROLE_DV, bmm(x, GPIPE_ROLE_DV, S, dh, S, PP, DC, dV,
+                 cz ? CAUSAL_K_FROM_M : CAUSAL_NONE, 1.0f));
+    GP_RUN(x, GPIPE_ROLE_SOFTMAX_BWD, softmax_bwd(bf, P, dP, dS, int64_t(p.B) * H * S, S, ldS, cz, scale, x.s));
+    GP_RUN(x, GPIPE_ROLE_DQ, bmm(x, GPIPE_ROLE_DQ, S, dh, S, DS, K, dQ,
+                 cz ? CAUSAL_K_UPTO_M : CAUSAL_NONE, 1.0f));
+    GP_RUN(x, GPIPE_ROLE_DK, bmm(x, GPIPE_ROLE_DK, S, dh, S, DS, Q, dK,
+                 cz ? CAUSAL_K_FROM_M : CAUSAL_NONE, 1.0f));
+  }
 
   // qkv = h1 Wqkv^T + bqkv,  h1 = LN1(x)
   GP_RUN(x, GPIPE_ROLE_QKV_DGRAD, mm(x, GPIPE_ROLE_QKV_DGRAD, T, D, 3 * D, dqkv, 3 * D, x.wmat(l, GPIPE_W_QKV), D,

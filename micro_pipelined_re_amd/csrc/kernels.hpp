@@ -120,6 +120,17 @@ hipError_t bn_bwd(bool bf16, int mask, const float* dy_src, const void* r, const
 hipError_t bn_running(const float* rec, int M, int nbn, int C, int64_t n_total, float momentum,
                       float* running, hipStream_t s);
 
+// ---------------------------------------------------------------- fused attention
+// bf16 cells with head dim 64 or 128.  qkv [B*S][3D], ctx/dctx [B*S][D],
+// lse2/delta [B*H][S] float32, dqkv [B*S][3D].
+bool flash_ok(bool bf16, int dh);
+hipError_t flash_fwd(const void* qkv, void* ctx, float* lse2, int B, int H, int S, int D,
+                     int causal, hipStream_t s);
+// stage 0: delta = rowsum(dctx * ctx); 1: dK, dV; 2: dQ
+hipError_t flash_bwd(const void* qkv, const void* ctx, const void* dctx, const float* lse2,
+                     float* delta, void* dqkv, int B, int H, int S, int D, int causal,
+                     hipStream_t s, int stage);
+
 // dst = bf16(src), n elements.
 hipError_t to_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
 

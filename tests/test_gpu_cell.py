@@ -205,3 +205,29 @@ def test_ragged_tiles_direct_lds_path_bf16():
                               seq=192, batch=2, micro=2)
     check(cfg)
     check(cfg.with_(causal=True))
+
+
+@pytest.mark.parametrize("dh,seq", [(128, 100), (64, 70), (128, 64), (64, 1)])
+def test_fused_attention_ragged_sequences_bf16(dh, seq):
+    """The fused attention kernels (bf16, head dim 64 / 128) with sequence lengths
+    that are not multiples of their 64-row blocks, causal and not."""
+    heads = 2
+    cfg = configs.SMALL.with_(name=f"fused_dh{dh}_s{seq}", layers=2, d_model=dh * heads,
+                              heads=heads, d_ff=4 * dh, seq=seq, batch=6, micro=3)
+    check(cfg)
+    check(cfg.with_(causal=True))
+
+
+def test_fused_attention_remat_bitwise_bf16():
+    """Remat through the fused attention equals stored activations bit for bit."""
+    cfg = configs.SMALL.with_(name="fused_remat", layers=2, d_model=256, heads=2, d_ff=512,
+                              seq=100, batch=4, micro=2, causal=True)
+    params = inputs.cell_params(cfg)
+    x, t = inputs.cell_data(cfg)
+    a = run_gpu(cfg, params, x, t, cfg.batch, cfg.micro, remat=True, update=False)
+    b = run_gpu(cfg, params, x, t, cfg.batch, cfg.micro, remat=False, update=False)
+    assert np.array_equal(a["y"], b["y"])
+    assert np.array_equal(a["dx"], b["dx"])
+    for ga, gb in zip(a["grad"], b["grad"]):
+        for n in gpipe.TENSORS:
+            assert np.array_equal(ga[n], gb[n]), n
