@@ -42,6 +42,34 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# HBM traffic of the GEMM roles, measured with rocprofv3's FETCH_SIZE and
+# WRITE_SIZE counters (calibrated on a streaming kernel of known size) and
+# stored in a profile summary together with a digest of the GEMM sources; the
+# figures are used only while the sources still hash to that digest.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_cell_d2048_L8_causal.md")
+GEMM_SOURCES = ("common.hpp", "kernels.hpp", "gemm_impl.hpp", "gemm_dma.hpp", "gemm.hip",
+                "gemm_fwd.hip", "gemm_dgrad.hip", "gemm_wgrad.hip")
+
+
+def measured_traffic(role):
+    """(fetch_bytes, write_bytes) per launch of `role`, or None if not measured for these sources."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "micro_pipelined_re_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    m = re.search(r"gemm_source_digest: ([0-9a-f]+)", text)
+    if not m or m.group(1) != h.hexdigest():
+        return None
+    m = re.search(rf"traffic {re.escape(role)}: fetch_bytes=(\d+) write_bytes=(\d+)", text)
+    return (int(m.group(1)), int(m.group(2))) if m else None
+
+
 # ------------------------------------------------------------------ algorithmic work per role
 def role_work(cfg, n, m):
     """Per launch: ('mfma', flops) for the contractions, ('hbm', bytes) for the rest."""
@@ -110,13 +138,21 @@ def cpu_baseline(cfg, n, m):
     b = n // m
     p = [inputs.layer_params(cfg.seed, 0, cfg.d_model, cfg.d_ff, bf16=True)]
     x, t = inputs.cell_data(cfg, batch=b)
-    t0 = time.perf_counter()
-    out = tc.cell_step(p, x, t, 1, cfg.heads, cfg.causal, remat=True)
-    t1 = time.perf_counter()
-    ms = {k: np.zeros(v.shape) for k, v in p[0].items()}
-    for k in p[0]:
-        tc.rmsprop(p[0][k].astype(np.float64), out["grads"][0][k], ms[k], cfg.lr, cfg.decay, cfg.eps)
-    t2 = time.perf_counter()
+    # repeat the sample for about 10 s of CPU work; average the repetitions
+    reps, t_step, t_upd, t_start = 0, 0.0, 0.0, time.perf_counter()
+    while reps == 0 or time.perf_counter() - t_start < 10.0:
+        t0 = time.perf_counter()
+        out = tc.cell_step(p, x, t, 1, cfg.heads, cfg.causal, remat=True)
+        t1 = time.perf_counter()
+        ms = {k: np.zeros(v.shape) for k, v in p[0].items()}
+        for k in p[0]:
+            tc.rmsprop(p[0][k].astype(np.float64), out["grads"][0][k], ms[k], cfg.lr, cfg.decay,
+                       cfg.eps)
+        t2 = time.perf_counter()
+        t_step += t1 - t0
+        t_upd += t2 - t1
+        reps += 1
+    t1, t0, t2 = t_step / reps, 0.0, t_step / reps + t_upd / reps
     step_s = m * cfg.layers * (t1 - t0) + cfg.layers * (t2 - t1)
     threads = None
     try:
@@ -128,9 +164,9 @@ def cpu_baseline(cfg, n, m):
             "cores": threads or os.cpu_count(), "kind": "oracle",
             "sample": (f"one micro-batch ({b} sequences, {b * cfg.seq} tokens) through one layer "
                        f"(forward, re-materialized forward, backward; numpy float64) plus that "
-                       f"layer's RMSProp, timed {t2 - t0:.1f} s, scaled by {m} micro-batches x "
-                       f"{cfg.layers} layers"),
-            "sample_seconds": round(t2 - t0, 2)}
+                       f"layer's RMSProp, {reps} repetitions of {t2:.2f} s, scaled by {m} "
+                       f"micro-batches x {cfg.layers} layers"),
+            "sample_seconds": round(t2 * reps, 2)}
 
 
 def conv_cpu_baseline(cfg, n, m):
@@ -142,13 +178,19 @@ def conv_cpu_baseline(cfg, n, m):
     b = n // m
     p = [inputs.conv_block_params(cfg.seed, 0, cfg.channels, bf16=cfg.precision == "bf16")]
     x, t = inputs.conv_cell_data(cfg, batch=b)
-    t0 = time.perf_counter()
-    out = cc.cell_step(p, x, t, 1, eps=cfg.bn_eps, remat=True)
-    t1 = time.perf_counter()
-    for k in p[0]:
-        w = p[0][k].astype(np.float64)
-        tc.rmsprop(w, out["grads"][0][k], np.zeros_like(w), cfg.lr, cfg.decay, cfg.eps)
-    t2 = time.perf_counter()
+    reps, t_step, t_upd, t_start = 0, 0.0, 0.0, time.perf_counter()
+    while reps == 0 or time.perf_counter() - t_start < 10.0:
+        t0 = time.perf_counter()
+        out = cc.cell_step(p, x, t, 1, eps=cfg.bn_eps, remat=True)
+        t1 = time.perf_counter()
+        for k in p[0]:
+            w = p[0][k].astype(np.float64)
+            tc.rmsprop(w, out["grads"][0][k], np.zeros_like(w), cfg.lr, cfg.decay, cfg.eps)
+        t2 = time.perf_counter()
+        t_step += t1 - t0
+        t_upd += t2 - t1
+        reps += 1
+    t1, t0, t2 = t_step / reps, 0.0, t_step / reps + t_upd / reps
     step_s = m * cfg.blocks * (t1 - t0) + cfg.blocks * (t2 - t1)
     threads = None
     try:
@@ -160,9 +202,9 @@ def conv_cpu_baseline(cfg, n, m):
             "cores": threads or os.cpu_count(), "kind": "oracle",
             "sample": (f"one micro-batch ({b} images of {cfg.height}x{cfg.width}x{cfg.channels}) "
                        f"through one block (forward, re-materialized forward, backward; numpy "
-                       f"float64) plus that block's RMSProp, timed {t2 - t0:.1f} s, scaled by "
-                       f"{m} micro-batches x {cfg.blocks} blocks"),
-            "sample_seconds": round(t2 - t0, 2)}
+                       f"float64) plus that block's RMSProp, {reps} repetitions of {t2:.2f} s, "
+                       f"scaled by {m} micro-batches x {cfg.blocks} blocks"),
+            "sample_seconds": round(t2 * reps, 2)}
 
 
 def setup_transformer(cfg, n, m, remat, dev):
@@ -332,7 +374,11 @@ def main():
         roof = {"bound": "hbm", "achieved": round(per / avg_s / 1e9, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    tr = None if conv else measured_traffic(dominant)
+    roof["traffic"] = (tr[0] + tr[1]) if tr else None
+    if tr:
+        roof["traffic_detail"] = {"unit": "bytes per launch", "fetch": tr[0], "write": tr[1],
+                                  "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
     roof["kernel"] = dominant
     tm_, tn_, sp_ = gpipe.gpipe_cell_gemm_plan(cell.handle, n, m, dom_idx)
     roof["kernel_tile"] = [tm_, tn_] if tm_ else None

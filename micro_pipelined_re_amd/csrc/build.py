@@ -61,8 +61,16 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    # native driver of the C-ABI step (for profiling without an interpreter)
+    exe = os.path.join(PKG, "cell_bench")
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", exe + ".tmp", os.path.join(HERE, "cell_bench.cpp"),
+           f"-L{PKG}", "-lgpipe_cell", "-Wl,-rpath,$ORIGIN"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"cell_bench build failed:\n{r.stderr}")
+    os.replace(exe + ".tmp", exe)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {exe}")
     return LIB
 
 

@@ -161,47 +161,50 @@ __global__ __launch_bounds__(256) void bn_moments_kernel(const T* __restrict__ x
   }
 }
 
-// Block: 32 channels x 8 chunk groups.  stats = (mean, rstd); rec (optional)
-// = (mean, biased variance).
+// Block: 8 channels x 32 chunk groups; each group adds every 32nd chunk, the
+// groups are then combined by a fixed tree.  stats = (mean, rstd); rec
+// (optional) = (mean, biased variance).
+constexpr int kMergeCh = 8, kMergeGroups = 32;
+
+__device__ __forceinline__ float merge_tree(float v, float (*red)[kMergeCh + 1], int g, int cl) {
+  red[g][cl] = v;
+  __syncthreads();
+#pragma unroll
+  for (int h = kMergeGroups / 2; h > 0; h >>= 1) {
+    if (g < h) red[g][cl] += red[g + h][cl];
+    __syncthreads();
+  }
+  const float t = red[0][cl];
+  __syncthreads();
+  return t;
+}
+
 __global__ __launch_bounds__(256) void bn_merge_kernel(const float* __restrict__ part, int nchunk,
                                                        int64_t rows, int C, float eps,
                                                        float* __restrict__ stats,
                                                        float* __restrict__ rec) {
-  __shared__ float red[8][33];
-  __shared__ float mean_s[32];
-  const int cl = threadIdx.x & 31, g = threadIdx.x >> 5;
-  const int c = blockIdx.x * 32 + cl;
+  __shared__ float red[kMergeGroups][kMergeCh + 1];
+  const int cl = threadIdx.x % kMergeCh, g = threadIdx.x / kMergeCh;
+  const int c = blockIdx.x * kMergeCh + cl;
   const bool ok = c < C;
   float s = 0.f;
   if (ok) {
 #pragma unroll 8
-    for (int k = g; k < nchunk; k += 8) s += part[int64_t(k) * 2 * C + c];
+    for (int k = g; k < nchunk; k += kMergeGroups) s += part[int64_t(k) * 2 * C + c];
   }
-  red[g][cl] = s;
-  __syncthreads();
-  if (g == 0) {
-    float t = red[0][cl];
-    for (int j = 1; j < 8; ++j) t += red[j][cl];
-    mean_s[cl] = t / float(rows);
-  }
-  __syncthreads();
-  const float mean = mean_s[cl];
+  const float mean = merge_tree(s, red, g, cl) / float(rows);
   float m2 = 0.f;
-  if (ok)
+  if (ok) {
 #pragma unroll 8
-    for (int k = g; k < nchunk; k += 8) {
+    for (int k = g; k < nchunk; k += kMergeGroups) {
       const float nk = float(int64_t(k) * kBnRows + kBnRows <= rows ? kBnRows
                                                                     : rows - int64_t(k) * kBnRows);
       const float d = part[int64_t(k) * 2 * C + c] / nk - mean;
       m2 += part[int64_t(k) * 2 * C + C + c] + nk * d * d;
     }
-  __syncthreads();
-  red[g][cl] = m2;
-  __syncthreads();
+  }
+  const float var = merge_tree(m2, red, g, cl) / float(rows);
   if (g == 0 && ok) {
-    float t = red[0][cl];
-    for (int j = 1; j < 8; ++j) t += red[j][cl];
-    const float var = t / float(rows);
     stats[c] = mean;
     stats[C + c] = 1.0f / sqrtf(var + eps);
     if (rec) {
@@ -226,8 +229,8 @@ hipError_t bn_stats(bool bf16, const void* x, int64_t rows, int C, float eps, fl
                        static_cast<const float*>(x), part, rows, C);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bn_merge_kernel, dim3((C + 31) / 32), dim3(256), 0, s, part, nch, rows, C, eps,
-                     stats, rec);
+  hipLaunchKernelGGL(bn_merge_kernel, dim3((C + kMergeCh - 1) / kMergeCh), dim3(256), 0, s, part, nch,
+                     rows, C, eps, stats, rec);
   return hipGetLastError();
 }
 

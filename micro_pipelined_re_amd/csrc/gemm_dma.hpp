@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kThreads, C::OCC) void gemm_dma_kernel(GemmParams g
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   int tm, tn;
-  tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, &tm, &tn);
+  tile_of(blockIdx.x, tiles_m, tiles_n, BM, BN, &tm, &tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int z = blockIdx.z, zb = z / g.hdiv, zh = z % g.hdiv;
   int kbeg, kend;

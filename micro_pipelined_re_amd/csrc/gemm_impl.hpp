@@ -99,11 +99,33 @@ __device__ __forceinline__ bool causal_range(const GemmParams& g, int m0, int n0
 // robin; renumber so each XCD gets a contiguous range of tiles, walked with
 // the m-tile fastest, which keeps the operand panels a range shares in that
 // XCD's L2.
-__device__ __forceinline__ void tile_of(int bid, int ntile, int tiles_m, int* tm, int* tn) {
-  int t = bid;
-  if (ntile % 8 == 0) t = (bid % 8) * (ntile / 8) + bid / 8;
-  *tm = t % tiles_m;
-  *tn = t / tiles_m;
+// Workgroups are dealt to the eight XCDs round-robin (XCD = bid % 8), and
+// each XCD has its own L2.  Each XCD is given one rectangle of the tile grid:
+// tiles_m / a row tiles by tiles_n / (8 / a) column tiles, with a in
+// {1, 2, 4, 8} chosen to minimise the operand rows it touches,
+// (tiles_m / a) * bm + (tiles_n * a / 8) * bn; inside it, tm runs fastest.
+// Grids that do not split evenly keep the plain order.
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int bm, int bn, int* tm,
+                                        int* tn) {
+  int best = 0, cost = 0;
+  for (int a = 1; a <= 8; a *= 2) {
+    const int b = 8 / a;
+    if (tiles_m % a || tiles_n % b) continue;
+    const int c = (tiles_m / a) * bm + (tiles_n / b) * bn;
+    if (!best || c < cost) {
+      best = a;
+      cost = c;
+    }
+  }
+  if (!best) {
+    *tm = bid % tiles_m;
+    *tn = bid / tiles_m;
+    return;
+  }
+  const int xcd = bid % 8, j = bid / 8;
+  const int rm = tiles_m / best, rn = tiles_n / (8 / best);
+  *tm = (xcd / (8 / best)) * rm + j % rm;
+  *tn = (xcd % (8 / best)) * rn + j / rm;
 }
 
 // ---------------------------------------------------------------- bf16 kernel
@@ -227,7 +249,7 @@ __global__ __launch_bounds__(kThreads, C::OCC) void gemm_bf16_kernel(GemmParams 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   int tm, tn;
-  tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, &tm, &tn);
+  tile_of(blockIdx.x, tiles_m, tiles_n, BM, BN, &tm, &tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int z = blockIdx.z, zb = z / g.hdiv, zh = z % g.hdiv;
   int kbeg, kend;
@@ -415,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   int tm, tn;
-  tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, &tm, &tn);
+  tile_of(blockIdx.x, tiles_m, tiles_n, BM, BN, &tm, &tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int z = blockIdx.z, zb = z / g.hdiv, zh = z % g.hdiv;
   int kbeg, kend;
