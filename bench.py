@@ -241,6 +241,99 @@ def setup_conv(cfg, n, m, remat, dev):
     return cell, x, t
 
 
+# ------------------------------------------------------------------ memory scaling
+def run_memory(args):
+    """The 48-layer d_model-4096 cell: peak device bytes of one step at several M,
+    against the planner's O(N + L/K * N/M) figure and a run without
+    re-materialization at the largest N that fits.  Weights are drawn on the device
+    (seeded torch generator; matrices N(0, 0.02^2), gamma 1, beta and biases 0)."""
+    import torch
+    from micro_pipelined_re_amd import configs, gpipe
+    cfg = configs.MEMORY_4096
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    cell = gpipe.Cell.from_config(cfg, "cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(cfg.seed)
+    mats = {"w_qkv", "w_o", "w_1", "w_2"}
+    with torch.no_grad():
+        for l, offs in enumerate(cell.offsets()):
+            for name, (o, c) in zip(gpipe.TENSORS, offs):
+                v = cell.master[o:o + c]
+                if name in mats:
+                    v.normal_(0.0, 0.02, generator=gen)
+                else:
+                    v.fill_(1.0 if name.endswith("_g") else 0.0)
+    gpipe.gpipe_cell_sync_lowp(cell.handle)
+    torch.cuda.synchronize()
+    state = torch.cuda.memory_allocated()
+    total_mem = torch.cuda.get_device_properties(0).total_memory
+    log(f"[bench] {cfg.name}: params {cell.n_params}, state {state / 1e9:.1f} GB, "
+        f"device {total_mem / 1e9:.1f} GB, setup {time.perf_counter() - t0:.1f} s")
+    eb = 2
+    per_seq_io = cfg.seq * cfg.d_model * eb   # one sequence of x, y or dx
+
+    def one(n, m, remat):
+        x = torch.empty(n, cfg.seq, cfg.d_model, dtype=torch.bfloat16, device="cuda")
+        t = torch.empty_like(x)
+        x.normal_(0.0, 1.0, generator=gen)
+        t.normal_(0.0, 1.0, generator=gen)
+        y, dx = torch.empty_like(x), torch.empty_like(x)
+        plan = gpipe.gpipe_cell_workspace_bytes(cell.handle, n, m, remat)
+        ws = torch.empty(plan, dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gpipe.gpipe_cell_step(cell.handle, x, t, y, dx, n, m, remat, ws, plan, stream, cell.loss)
+        gpipe.gpipe_apply_update(cell.handle, cfg.lr, cfg.decay, cfg.eps, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated()
+        # one micro-batch's saved set: L layer slots of the plan
+        o0 = gpipe.gpipe_cell_saved_offset(cell.handle, n, m, remat, 0, 1, 1)[0]
+        o1 = gpipe.gpipe_cell_saved_offset(cell.handle, n, m, remat, 0, 2, 1)[0]
+        set_bytes = (o1 - o0) * cfg.layers
+        r = {"N": n, "M": m, "remat": remat, "ms_per_step": round(e0.elapsed_time(e1), 1),
+             "tokens_per_s": round(n * cfg.seq / (e0.elapsed_time(e1) * 1e-3), 1),
+             "activation_bytes_measured": peak - state,
+             "workspace_plan": plan, "boundary_x_t_y_dx": 4 * n * per_seq_io,
+             "saved_set_per_micro_batch": set_bytes, "peak_device_bytes": peak,
+             "loss": float(cell.loss.item())}
+        log(f"[bench] N={n} M={m} remat={remat}: {r['ms_per_step']} ms, activations "
+            f"{r['activation_bytes_measured'] / 1e9:.2f} GB (plan {plan / 1e9:.2f} GB)")
+        del x, t, y, dx, ws
+        torch.cuda.empty_cache()
+        return r
+
+    runs = []
+    n = cfg.batch
+    for m in (32, 8, 4):
+        runs.append(one(n, m, True))
+    # M = 1: the planner's figure alone (it does not fit next to the parameter state)
+    m1 = gpipe.gpipe_cell_workspace_bytes(cell.handle, n, 1, True)
+    # without re-materialization at the largest N (multiple of 8) that fits
+    per_seq_keep = gpipe.gpipe_cell_workspace_bytes(cell.handle, 16, 16, False) / 16
+    n_keep = int((0.97 * total_mem - state) // (per_seq_keep + 4 * per_seq_io)) // 8 * 8
+    keep = None
+    if n_keep >= 8:
+        keep = [one(n_keep, n_keep // 2, False), one(n_keep, n_keep // 2, True)]
+    out = {
+        "metric": "peak activation bytes vs O(N + L/K*N/M), 48-layer d4096 cell",
+        "value": runs[0]["activation_bytes_measured"], "unit": "bytes",
+        "higher_is_better": False, "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": cfg.layers, "d_model": cfg.d_model,
+                   "heads": cfg.heads, "d_ff": cfg.d_ff, "seq_len": cfg.seq,
+                   "global_batch": n, "causal": cfg.causal},
+        "parameter_state_bytes": state, "device_bytes": total_mem,
+        "remat_runs": runs,
+        "m1_workspace_plan": m1, "m1_fits": bool(state + m1 + 4 * n * per_seq_io < total_mem),
+        "no_remat_vs_remat_at_largest_n": keep,
+    }
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -250,13 +343,15 @@ def main():
     ap.add_argument("--micro", type=int, default=None, help="override M")
     ap.add_argument("--no-remat", action="store_true", help="keep every micro-batch's activations")
     ap.add_argument("--workload", default="cell_d2048_L8_causal",
-                    choices=("cell_d2048_L8_causal", "conv_c256_b8"))
+                    choices=("cell_d2048_L8_causal", "conv_c256_b8", "memory_4096"))
     ap.add_argument("--precision", default=None, choices=("bf16", "fp32"),
                     help="override the workload's precision")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-all", action="store_true",
                     help="time every kernel role inside the timed region")
     args = ap.parse_args()
+    if args.workload == "memory_4096" and args.gpus == 1:
+        return run_memory(args)
     if args.gpus != 1:
         print(f"bench.py runs one cell on one GPU; --gpus {args.gpus} is not supported "
               f"(the multi-GPU pipeline schedule is not part of this build)", file=sys.stderr)
