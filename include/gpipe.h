@@ -250,6 +250,10 @@ typedef enum {
   /* fused attention (bf16, head dim 64 or 128): forward; backward row sums
    * of dO * O; dK and dV per key block; dQ per query block */
   GPIPE_ROLE_ATTN_FWD, GPIPE_ROLE_ATTN_DELTA, GPIPE_ROLE_ATTN_DKDV, GPIPE_ROLE_ATTN_DQ,
+  /* conv cells in bf16 with channels a multiple of 64: implicit-GEMM
+   * convolution (the 3 x 3 neighbourhood gathered by the GEMM's loads) and the
+   * input gradient as the convolution of dz with tap-flipped weights */
+  GPIPE_ROLE_CONV_FWD_IMPLICIT, GPIPE_ROLE_CONV_DGRAD_IMPLICIT,
   GPIPE_N_ROLES
 } gpipe_role;
 

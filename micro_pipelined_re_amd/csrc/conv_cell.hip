@@ -15,19 +15,21 @@ namespace {
 //   sets:  remat ? 1 : M micro-batch sets, each L blocks of the saved tensors
 //          of gpipe_conv_saved (block 0 has no X slot in use)
 //   yre:   output of the re-materialized forward [P, C] (remat only)
-//   col:   im2col matrix [P, 9C] (act);  dcol: its gradient [P, 9C] (f32)
+//   col:   im2col matrix [P, 9C] (act);  dcol: its gradient [P, 9C] (f32, explicit path)
+//   wflip: tap-flipped transposed weights [L][2][C][9][C] (implicit path)
 //   r0:    residual-stream gradient [P, C] (f32);  r1: ReLU-input gradient (f32)
 //   dz:    BN input gradient [P, C] (act, GEMM operand)
 //   part, sums: BN reduction partials;  rec: forward-phase moments [M][2L][2][C]
 //   msepart, splitk
 struct CPlan {
   int N, M, B;
+  bool implicit;  // bf16, channels a multiple of 64: implicit-GEMM convolutions
   int64_t P;  // pixels per micro-batch
   size_t eb;
   size_t saved_off[GPIPE_CONV_N_SAVED], saved_bytes[GPIPE_CONV_N_SAVED];
   size_t block_bytes, set_bytes;
   int nsets;
-  size_t yre, col, dcol, r0, r1, dz, part, sums, rec, msepart, splitk;
+  size_t yre, col, dcol, r0, r1, dz, part, sums, rec, msepart, splitk, wflip;
   int mse_nblk;
   size_t total;
 };
@@ -60,9 +62,11 @@ bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
     o += align_up(bytes, kAlign);
     return at;
   };
+  p->implicit = c->prec == GPIPE_BF16 && C % 64 == 0;
   p->yre = take(remat ? P * C * eb : 0);
-  p->col = take(P * 9 * C * eb);
-  p->dcol = take(P * 9 * C * 4);
+  p->col = take(P * 9 * C * eb);                    // weight gradients (and the explicit path)
+  p->dcol = take(p->implicit ? 0 : P * 9 * C * 4);
+  p->wflip = take(p->implicit ? size_t(c->L) * 2 * 9 * C * C * 2 : 0);
   p->r0 = take(P * C * 4);
   p->r1 = take(P * C * 4);
   p->dz = take(P * C * eb);
@@ -75,7 +79,9 @@ bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
   const int Pi = int(P), Ci = int(C);
   const size_t sk = std::max({gemm_partial_floats(GPIPE_ROLE_CONV_FWD, bf, Pi, Ci, 9 * Ci, 1),
                               gemm_partial_floats(GPIPE_ROLE_CONV_DGRAD, bf, Pi, 9 * Ci, Ci, 1),
-                              gemm_partial_floats(GPIPE_ROLE_CONV_WGRAD, bf, Ci, 9 * Ci, Pi, 1)});
+                              gemm_partial_floats(GPIPE_ROLE_CONV_WGRAD, bf, Ci, 9 * Ci, Pi, 1),
+                              gemm_partial_floats(GPIPE_ROLE_CONV_FWD_IMPLICIT, bf, Pi, Ci, 9 * Ci, 1),
+                              gemm_partial_floats(GPIPE_ROLE_CONV_DGRAD_IMPLICIT, bf, Pi, Ci, 9 * Ci, 1)});
   p->splitk = take(sk * 4);
   p->total = o;
   return true;
@@ -108,6 +114,11 @@ struct CCtx {
   void* act(const void* base, size_t elems) const {
     return const_cast<char*>(static_cast<const char*>(base)) + elems * p->eb;
   }
+  // tap-flipped transposed weights of conv `which` (0: W1, 1: W2) of block l
+  const void* flipped(int block, int which) const {
+    const size_t n = size_t(9) * c->C * c->C;
+    return ws + p->wflip + (size_t(block) * 2 + which) * n * 2;
+  }
 };
 
 hipError_t cmm(const CCtx& x, int role, int M, int N, int K, const void* A, int64_t lda,
@@ -125,6 +136,24 @@ hipError_t cmm(const CCtx& x, int role, int M, int N, int K, const void* A, int6
   return gemm(x.bf16, role, g, 1, x.s);
 }
 
+// Implicit-GEMM convolution of an NHWC image [P, C] with [C][9C] weights
+// (k-contiguous): out[P, C] (beta: accumulate into an f32 output).
+hipError_t cconv(const CCtx& x, int role, const void* img, const void* w, void* out, int beta) {
+  GemmParams g;
+  memset(&g, 0, sizeof(g));
+  const int C = x.c->C;
+  g.hdiv = 1;
+  g.alpha = 1.0f;
+  g.M = int(x.p->P); g.N = C; g.K = 9 * C;
+  g.A = img; g.lda = C;
+  g.B = w; g.ldb = 9 * C;
+  g.C = out; g.ldc = C;
+  g.beta = beta;
+  g.conv_h = x.c->Hc; g.conv_w = x.c->Wc; g.conv_c = C;
+  g.P = x.f(x.p->splitk);
+  return gemm(true, role, g, 1, x.s);
+}
+
 // One block forward of one micro-batch; rec (nullable) receives the BN
 // moments [2][2][C] of this block (forward phase only).
 gpipe_status block_forward(const CCtx& x, int set, int l, const void* xin, void* xout, float* rec) {
@@ -139,15 +168,25 @@ gpipe_status block_forward(const CCtx& x, int set, int l, const void* xin, void*
   void* z = x.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_Z));
   float* st2 = x.f(csaved_at(p, set, l, GPIPE_CONV_SAVED_ST2));
   float* part = x.f(p.part);
-  GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, xin, col, B, H, W, C, x.s));
-  GP_RUN(x, GPIPE_ROLE_CONV_FWD, cmm(x, GPIPE_ROLE_CONV_FWD, int(P), C, 9 * C, col, 9 * C,
-                                     x.wmat(l, GPIPE_CONV_W1), 9 * C, a, C));
+  if (p.implicit) {
+    GP_RUN(x, GPIPE_ROLE_CONV_FWD_IMPLICIT,
+           cconv(x, GPIPE_ROLE_CONV_FWD_IMPLICIT, xin, x.wmat(l, GPIPE_CONV_W1), a, 0));
+  } else {
+    GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, xin, col, B, H, W, C, x.s));
+    GP_RUN(x, GPIPE_ROLE_CONV_FWD, cmm(x, GPIPE_ROLE_CONV_FWD, int(P), C, 9 * C, col, 9 * C,
+                                       x.wmat(l, GPIPE_CONV_W1), 9 * C, a, C));
+  }
   GP_RUN(x, GPIPE_ROLE_BN_STATS, bn_stats(x.bf16, a, P, C, c->bn_eps, part, st1, rec, x.s));
   GP_RUN(x, GPIPE_ROLE_BN_APPLY, bn_apply(x.bf16, 0, a, st1, x.wf32(l, GPIPE_CONV_BN1_G),
                                           x.wf32(l, GPIPE_CONV_BN1_B), nullptr, r, P, C, x.s));
-  GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, r, col, B, H, W, C, x.s));
-  GP_RUN(x, GPIPE_ROLE_CONV_FWD, cmm(x, GPIPE_ROLE_CONV_FWD, int(P), C, 9 * C, col, 9 * C,
-                                     x.wmat(l, GPIPE_CONV_W2), 9 * C, z, C));
+  if (p.implicit) {
+    GP_RUN(x, GPIPE_ROLE_CONV_FWD_IMPLICIT,
+           cconv(x, GPIPE_ROLE_CONV_FWD_IMPLICIT, r, x.wmat(l, GPIPE_CONV_W2), z, 0));
+  } else {
+    GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, r, col, B, H, W, C, x.s));
+    GP_RUN(x, GPIPE_ROLE_CONV_FWD, cmm(x, GPIPE_ROLE_CONV_FWD, int(P), C, 9 * C, col, 9 * C,
+                                       x.wmat(l, GPIPE_CONV_W2), 9 * C, z, C));
+  }
   GP_RUN(x, GPIPE_ROLE_BN_STATS,
          bn_stats(x.bf16, z, P, C, c->bn_eps, part, st2, rec ? rec + 2 * C : nullptr, x.s));
   GP_RUN(x, GPIPE_ROLE_BN_APPLY, bn_apply(x.bf16, 1, z, st2, x.wf32(l, GPIPE_CONV_BN2_G),
@@ -196,9 +235,14 @@ gpipe_status block_backward(const CCtx& x, int set, int l, const void* xin, int 
   GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, r, col, B, H, W, C, x.s));
   GP_RUN(x, GPIPE_ROLE_CONV_WGRAD, cmm(x, GPIPE_ROLE_CONV_WGRAD, C, 9 * C, int(P), dz, C, col,
                                        9 * C, x.grad(l, GPIPE_CONV_W2), 9 * C, beta));
-  GP_RUN(x, GPIPE_ROLE_CONV_DGRAD, cmm(x, GPIPE_ROLE_CONV_DGRAD, int(P), 9 * C, C, dz, C,
-                                       x.wmat(l, GPIPE_CONV_W2), 9 * C, dcol, 9 * C));
-  GP_RUN(x, GPIPE_ROLE_COL2IM, col2im(x.bf16, dcol, nullptr, r1, nullptr, B, H, W, C, x.s));
+  if (p.implicit) {
+    GP_RUN(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT,
+           cconv(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT, dz, x.flipped(l, 1), r1, 0));
+  } else {
+    GP_RUN(x, GPIPE_ROLE_CONV_DGRAD, cmm(x, GPIPE_ROLE_CONV_DGRAD, int(P), 9 * C, C, dz, C,
+                                         x.wmat(l, GPIPE_CONV_W2), 9 * C, dcol, 9 * C));
+    GP_RUN(x, GPIPE_ROLE_COL2IM, col2im(x.bf16, dcol, nullptr, r1, nullptr, B, H, W, C, x.s));
+  }
   // r = ReLU(BN1(a))
   GP_RUN(x, GPIPE_ROLE_BN_BWD, bn_bwd(x.bf16, 1, r1, r, a, st1, x.wf32(l, GPIPE_CONV_BN1_G), part,
                                       sums, dz, P, C, &nch, x.s));
@@ -208,9 +252,16 @@ gpipe_status block_backward(const CCtx& x, int set, int l, const void* xin, int 
   GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, xin, col, B, H, W, C, x.s));
   GP_RUN(x, GPIPE_ROLE_CONV_WGRAD, cmm(x, GPIPE_ROLE_CONV_WGRAD, C, 9 * C, int(P), dz, C, col,
                                        9 * C, x.grad(l, GPIPE_CONV_W1), 9 * C, beta));
-  GP_RUN(x, GPIPE_ROLE_CONV_DGRAD, cmm(x, GPIPE_ROLE_CONV_DGRAD, int(P), 9 * C, C, dz, C,
-                                       x.wmat(l, GPIPE_CONV_W1), 9 * C, dcol, 9 * C));
-  GP_RUN(x, GPIPE_ROLE_COL2IM, col2im(x.bf16, dcol, r0, r0, dx_out, B, H, W, C, x.s));
+  if (p.implicit) {
+    // the residual gradient already in r0 gets the convolution's input gradient added
+    GP_RUN(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT,
+           cconv(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT, dz, x.flipped(l, 0), r0, 1));
+    if (dx_out) GP_CHECK(to_bf16(r0, dx_out, P * C, x.s));
+  } else {
+    GP_RUN(x, GPIPE_ROLE_CONV_DGRAD, cmm(x, GPIPE_ROLE_CONV_DGRAD, int(P), 9 * C, C, dz, C,
+                                         x.wmat(l, GPIPE_CONV_W1), 9 * C, dcol, 9 * C));
+    GP_RUN(x, GPIPE_ROLE_COL2IM, col2im(x.bf16, dcol, r0, r0, dx_out, B, H, W, C, x.s));
+  }
   return GPIPE_OK;
 }
 
@@ -259,6 +310,8 @@ gpipe_status conv_gemm_plan(const gpipe_cell* c, int N, int M, int role, int* ti
     case GPIPE_ROLE_CONV_FWD: m = P; n = C; k = 9 * C; break;
     case GPIPE_ROLE_CONV_DGRAD: m = P; n = 9 * C; k = C; break;
     case GPIPE_ROLE_CONV_WGRAD: m = C; n = 9 * C; k = P; break;
+    case GPIPE_ROLE_CONV_FWD_IMPLICIT: case GPIPE_ROLE_CONV_DGRAD_IMPLICIT:
+      m = P; n = C; k = 9 * C; break;
     default:
       *tile_m = *tile_n = *splits = 0;
       return GPIPE_OK;
@@ -287,6 +340,13 @@ gpipe_status conv_cell_step(gpipe_cell* c, const void* x, const void* target, vo
   float* rec = cx.f(p.rec);
   float* msepart = cx.f(p.msepart);
   const size_t rec_mb = size_t(2) * c->L * 2 * c->C;
+  if (p.implicit)
+    for (int l = 0; l < c->L; ++l) {
+      GP_CHECK(conv_flip_weights(cx.wmat(l, GPIPE_CONV_W1), const_cast<void*>(cx.flipped(l, 0)),
+                                 c->C, stream));
+      GP_CHECK(conv_flip_weights(cx.wmat(l, GPIPE_CONV_W2), const_cast<void*>(cx.flipped(l, 1)),
+                                 c->C, stream));
+    }
   // phase 1: forward; each micro-batch normalised with its own statistics
   for (int m = 0; m < M; ++m) {
     gpipe_status st = cell_forward(cx, remat ? 0 : m, cx.act(x, m * mb), cx.act(y, m * mb),

@@ -411,6 +411,30 @@ hipError_t bn_bwd(bool bf16, int mask, const float* dy_src, const void* r, const
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ flipped weights
+// dst[c][t][o] = src[o][8 - t][c]: the input gradient of y = conv3x3(x, W) is
+// conv3x3(dy, dst) (the taps mirrored through the centre, in and out swapped).
+__global__ __launch_bounds__(256) void conv_flip_kernel(const bf16_t* __restrict__ src,
+                                                        bf16_t* __restrict__ dst, int C) {
+  const int64_t n = int64_t(9) * C * C;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    const int o = int(i % C);
+    const int t = int((i / C) % 9);
+    const int c = int(i / (int64_t(9) * C));
+    dst[i] = src[(int64_t(o) * 9 + (8 - t)) * C + c];
+  }
+}
+
+hipError_t conv_flip_weights(const void* src, void* dst, int C, hipStream_t s) {
+  const int64_t n = int64_t(9) * C * C;
+  if (n == 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  const int blocks = int(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(conv_flip_kernel, dim3(blocks), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(src), static_cast<bf16_t*>(dst), C);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ moving averages
 // rec: [M][nbn][2][C] = per micro-batch (mean, biased var); running: [nbn][2][C].
 // Pooled over the M equal micro-batches in order:

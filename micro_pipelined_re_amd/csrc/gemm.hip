@@ -24,8 +24,8 @@ int group_of(int role) {
     case GPIPE_ROLE_FFN2_FWD: return 0;
     case GPIPE_ROLE_FFN2_DGRAD: case GPIPE_ROLE_FFN1_DGRAD: case GPIPE_ROLE_OUT_DGRAD:
     case GPIPE_ROLE_QKV_DGRAD: return 1;
-    case GPIPE_ROLE_CONV_FWD: return 0;
-    case GPIPE_ROLE_CONV_DGRAD: return 1;
+    case GPIPE_ROLE_CONV_FWD: case GPIPE_ROLE_CONV_FWD_IMPLICIT: return 0;
+    case GPIPE_ROLE_CONV_DGRAD: case GPIPE_ROLE_CONV_DGRAD_IMPLICIT: return 1;
     case GPIPE_ROLE_CONV_WGRAD: return 2;
   }
   return is_wgrad(role) ? 2 : is_attention(role) ? 3 : -1;
@@ -45,7 +45,11 @@ bool dma_ok(int role, const GemmParams& g) {
   const bool b_mn = role != GPIPE_ROLE_QKV_FWD && role != GPIPE_ROLE_SCORES_FWD &&
                     role != GPIPE_ROLE_OUT_FWD && role != GPIPE_ROLE_FFN1_FWD &&
                     role != GPIPE_ROLE_FFN2_FWD && role != GPIPE_ROLE_DP &&
-                    role != GPIPE_ROLE_CONV_FWD;
+                    role != GPIPE_ROLE_CONV_FWD && role != GPIPE_ROLE_CONV_FWD_IMPLICIT &&
+                    role != GPIPE_ROLE_CONV_DGRAD_IMPLICIT;
+  const bool conv = role == GPIPE_ROLE_CONV_FWD_IMPLICIT || role == GPIPE_ROLE_CONV_DGRAD_IMPLICIT;
+  // a gathered operand needs every 64-deep k-tile inside one tap
+  if (conv && (g.conv_c % 64 || g.K != 9 * g.conv_c)) return false;
   if (a_mn && g.M % 8) return false;
   if (b_mn && g.N % 8) return false;
   return true;

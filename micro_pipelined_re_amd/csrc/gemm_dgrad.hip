@@ -10,6 +10,8 @@ hipError_t gemm_group_dgrad(int role, int path, int cfg, const GemmParams& g, in
     case GPIPE_ROLE_OUT_DGRAD: return launch_role<GPIPE_ROLE_OUT_DGRAD>(path, cfg, g, batch, splits, s);
     case GPIPE_ROLE_QKV_DGRAD: return launch_role<GPIPE_ROLE_QKV_DGRAD>(path, cfg, g, batch, splits, s);
     case GPIPE_ROLE_CONV_DGRAD: return launch_role<GPIPE_ROLE_CONV_DGRAD>(path, cfg, g, batch, splits, s);
+    case GPIPE_ROLE_CONV_DGRAD_IMPLICIT:
+      return launch_role<GPIPE_ROLE_CONV_DGRAD_IMPLICIT>(path, cfg, g, batch, splits, s);
   }
   return hipErrorInvalidValue;
 }

@@ -23,6 +23,8 @@
 // Rows past the operand's extent are read from its last row (valid memory;
 // those results are never stored).  k must be a multiple of 64.
 #pragma once
+#include <type_traits>
+
 #include "gemm_impl.hpp"
 
 namespace gp {
@@ -76,6 +78,63 @@ __device__ __forceinline__ int kswz_off(int row, int chunk) {
   if constexpr (BK == 64) return row * 64 + ((chunk ^ (row & 7)) << 3);
   else return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3);
 }
+
+// All-zero source for the loads of padding pixels of a LAY_CONV operand.
+static __device__ __attribute__((aligned(16))) bf16_t g_conv_zero[8];
+
+// A operand gathered from an NHWC image (LAY_CONV): the tile is stored like a
+// k-contiguous one; each load instruction's lane owns one pixel row and one
+// 16-byte chunk, and its source moves with the k-tile's tap.
+template <int ROWS, int BK>
+struct DmaConvOperand {
+  static_assert(BK == 64, "conv operands use 64-deep k-tiles");
+  static constexpr int ELEMS = ROWS * BK;
+  static constexpr int KB_PER_STAGE = ELEMS * 2 / 1024;
+  static constexpr int PER_WAVE = KB_PER_STAGE / 4;
+  int pix[PER_WAVE];     // pixel index (row of the operand, clamped into range)
+  short hh[PER_WAVE], ww[PER_WAVE];
+  short coff[PER_WAVE];  // element offset of the lane's chunk inside the k-tile
+  int H, W, C, kbeg;
+
+  __device__ __forceinline__ void init(const GemmParams& g, int row0, int rows_total, int kb,
+                                       int wave, int lane) {
+    H = g.conv_h;
+    W = g.conv_w;
+    C = g.conv_c;
+    kbeg = kb;
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q) {
+      const int blk = q * 4 + wave;
+      const int r = blk * 8 + lane / 8;       // 8 rows of 8 chunks per kilobyte
+      const int p = lane % 8;
+      const int c = p ^ (r & 7);
+      const int gr = min(row0 + r, rows_total - 1);
+      pix[q] = gr;
+      ww[q] = short(gr % W);
+      hh[q] = short((gr / W) % H);
+      coff[q] = short(c * 8);
+    }
+  }
+
+  __device__ __forceinline__ void issue(const bf16_t* img, int kt, bf16_t* stage, int wave) const {
+    const int k0 = kbeg + kt * BK;
+    const int tap = k0 / C, c0 = k0 - tap * C;
+    const int dh = tap / 3 - 1, dw = tap - (tap / 3) * 3 - 1;
+    const int shift = dh * W + dw;
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q) {
+      const int hs = hh[q] + dh, ws = ww[q] + dw;
+      const bool in = unsigned(hs) < unsigned(H) && unsigned(ws) < unsigned(W);
+      const bf16_t* src = in ? img + int64_t(pix[q] + shift) * C + c0 + coff[q] : g_conv_zero;
+      dma16(src, stage + (q * 4 + wave) * 512);
+    }
+  }
+
+  __device__ __forceinline__ bf16x8_t frag(const bf16_t* stage, int row16, int lane, int ks) const {
+    const int r = row16 + (lane & 15);
+    return *reinterpret_cast<const bf16x8_t*>(stage + kswz_off<BK>(r, ks * 4 + (lane >> 4)));
+  }
+};
 
 template <int ROWS, int BK, int LAY>
 struct DmaOperand {
@@ -239,7 +298,8 @@ __device__ __forceinline__ void epi_store8(const GemmParams& g, int row, int col
 template <class C, int LA, int LB, int EPI, int ROLE>
 __global__ __launch_bounds__(kThreads, C::OCC) void gemm_dma_kernel(GemmParams g) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, STAGES = C::STAGES, FM = C::FM, FN = C::FN;
-  using OA = DmaOperand<BM, BK, LA>;
+  using OA = typename std::conditional<LA == LAY_CONV, DmaConvOperand<BM, BK>,
+                                       DmaOperand<BM, BK, LA>>::type;
   using OB = DmaOperand<BN, BK, LB>;
   static_assert(LPT_CHECK(OA::PER_WAVE + OB::PER_WAVE, STAGES), "vmcnt range");
   constexpr int LPT = OA::PER_WAVE + OB::PER_WAVE;  // load instructions per wave per k-tile
@@ -265,7 +325,8 @@ __global__ __launch_bounds__(kThreads, C::OCC) void gemm_dma_kernel(GemmParams g
   const bf16_t* B = static_cast<const bf16_t*>(g.B) + zb * g.sBb + zh * g.sBh;
   OA oa;
   OB ob;
-  oa.init(g.lda, m0, g.M, kbeg, wave, lane);
+  if constexpr (LA == LAY_CONV) oa.init(g, m0, g.M, kbeg, wave, lane);
+  else oa.init(g.lda, m0, g.M, kbeg, wave, lane);
   ob.init(g.ldb, n0, g.N, kbeg, wave, lane);
   auto sa = [&](int st) { return smem + st * (BM + BN) * BK; };
   auto sb = [&](int st) { return smem + st * (BM + BN) * BK + BM * BK; };
@@ -355,10 +416,15 @@ hipError_t launch_bf16(int path, const GemmParams& g, int batch, int splits, hip
   const int tiles = ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
   if (tiles == 0 || batch == 0) return hipSuccess;
   const dim3 grid(tiles, splits, batch);
-  if (path == 0)
+  if constexpr (LA == LAY_CONV) {
+    // the gathered operand exists only on the direct-to-LDS path
+    if (path != 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_dma_kernel<DC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, g);
-  else
+  } else if (path == 0) {
+    hipLaunchKernelGGL((gemm_dma_kernel<DC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, g);
+  } else {
     hipLaunchKernelGGL((gemm_bf16_kernel<RC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, g);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const int64_t n = int64_t(g.M) * g.N;

@@ -553,6 +553,10 @@ GP_SPEC(GPIPE_ROLE_QKV_WGRAD, LAY_MN, LAY_MN, EPI_ACC_F32)
 GP_SPEC(GPIPE_ROLE_CONV_FWD, LAY_K, LAY_K, EPI_STORE)
 GP_SPEC(GPIPE_ROLE_CONV_DGRAD, LAY_K, LAY_MN, EPI_STORE_F32)
 GP_SPEC(GPIPE_ROLE_CONV_WGRAD, LAY_MN, LAY_MN, EPI_ACC_F32)
+// implicit GEMM: a = im2col(x) W^T with the column matrix gathered by the loads;
+// the input gradient (+)= im2col(dz) Wflip^T, Wflip the tap-flipped transposed weights
+GP_SPEC(GPIPE_ROLE_CONV_FWD_IMPLICIT, LAY_CONV, LAY_K, EPI_STORE)
+GP_SPEC(GPIPE_ROLE_CONV_DGRAD_IMPLICIT, LAY_CONV, LAY_K, EPI_ACC_F32)
 #undef GP_SPEC
 
 template <int BM, int BN, int BK, int ST, int OCC> struct DCfg;
@@ -562,6 +566,12 @@ template <int ROLE>
 hipError_t launch_role(int path, int cfg, const GemmParams& g, int batch, int splits, hipStream_t s) {
   using R = RoleSpec<ROLE>;
   using RB = Cfg<128, 128>;
+  if constexpr (R::LA == LAY_CONV) {
+    // one tile configuration for the gathered operand
+    if (cfg != CFG_128x128_K64) return hipErrorInvalidValue;
+    return launch_bf16<DCfg<128, 128, 64, 2, 2>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch,
+                                                                                splits, s);
+  } else {
   switch (cfg) {
     case CFG_256x128_K64: return launch_bf16<DCfg<256, 128, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
     case CFG_128x256_K64: return launch_bf16<DCfg<128, 256, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
@@ -571,6 +581,7 @@ hipError_t launch_role(int path, int cfg, const GemmParams& g, int batch, int sp
     case CFG_64x64_K64: return launch_bf16<DCfg<64, 64, 64, 3, 3>, Cfg<64, 64>, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
   }
   return hipErrorInvalidValue;
+  }
 }
 
 // Per-file group launchers (gemm_fwd.hip, gemm_dgrad.hip, gemm_wgrad.hip,

@@ -6,7 +6,10 @@
 namespace gp {
 
 // ---------------------------------------------------------------- GEMM
-enum { LAY_K = 0, LAY_MN = 1 };
+// LAY_CONV: the A operand is the 3 x 3 im2col matrix of an NHWC image that is
+// never materialised: row p, column tap*C + c reads pixel p shifted by the
+// tap's (dh, dw), or zero outside the image (A only, k-tiles within one tap).
+enum { LAY_K = 0, LAY_MN = 1, LAY_CONV = 2 };
 
 enum {
   EPI_STORE = 0,       // C(act) = alpha * acc
@@ -40,6 +43,7 @@ struct GemmParams {
   int beta;
   float* P;     // split-K partials [splits][M][N] (f32), required when the plan splits
   int kchunk;   // split-K: k extent of one split (set by gemm())
+  int conv_h, conv_w, conv_c;  // image geometry of a LAY_CONV operand
 };
 
 // Macro tile and split-K chosen for one GEMM launch.
@@ -130,6 +134,10 @@ hipError_t flash_fwd(const void* qkv, void* ctx, float* lse2, int B, int H, int 
 hipError_t flash_bwd(const void* qkv, const void* ctx, const void* dctx, const float* lse2,
                      float* delta, void* dqkv, int B, int H, int S, int D, int causal,
                      hipStream_t s, int stage);
+
+// Tap-flipped, transposed 3 x 3 weights: dst[c][t][o] = src[o][8 - t][c] (bf16, C x C x 9);
+// the input gradient of a convolution is the convolution of its output gradient with them.
+hipError_t conv_flip_weights(const void* src, void* dst, int C, hipStream_t s);
 
 // dst = bf16(src), n elements.
 hipError_t to_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
