@@ -97,7 +97,7 @@ bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
   p->du = take(T * F * eb);
   p->dqkv = take(T * 3 * D * eb);
   p->colpart = take(size_t(colsum_chunks(int(T))) * std::max(3 * D, F) * 4);
-  p->lnpart = take(size_t(layernorm_bwd_blocks(int(T))) * 2 * D * 4);
+  p->lnpart = take(size_t(layernorm_bwd_blocks(int(T), c->D)) * 2 * D * 4);
   p->mse_nblk = mse_blocks(int64_t(T) * int64_t(D));
   p->msepart = take(size_t(M) * size_t(p->mse_nblk) * 4);
   // split-K partials of the largest split GEMM of a layer (none for fp32 cells)

@@ -73,7 +73,7 @@ hipError_t layernorm_fwd(bool bf16, const void* x, void* y, float* stats, const 
 hipError_t layernorm_bwd(bool bf16, const float* dh, const void* x, const float* stats,
                          const float* gamma, const float* res_in, float* dx_f32, void* dx_act,
                          float* part, int rows, int d, int* nblk, hipStream_t s);
-int layernorm_bwd_blocks(int rows);
+int layernorm_bwd_blocks(int rows, int d);
 
 // Softmax forward of scores (f32, already scaled) into P(act); rows of length n, row pitch ld,
 // optional causal mask (key j > row index i within its [n x n] block); masked entries -> 0.

@@ -161,17 +161,112 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
   }
 }
 
-int layernorm_bwd_blocks(int rows) { return (rows + kLnRows - 1) / kLnRows; }
+// One wave per row, four rows per block (rows of up to 4096): the row's two
+// reductions are wave butterflies; the four rows' dgamma / dbeta partials are
+// added in row order through LDS and written once per block.
+constexpr int kLnWaveRows = 4;
+
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void ln_bwd_wave_kernel(const float* __restrict__ dh,
+                                                          const T* __restrict__ x,
+                                                          const float* __restrict__ stats,
+                                                          const float* __restrict__ gamma,
+                                                          const float* res_in, float* dx_f32,
+                                                          T* __restrict__ dx_act,
+                                                          float* __restrict__ part, int rows,
+                                                          int d) {
+  extern __shared__ float lds[];  // [4][d]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row = blockIdx.x * kLnWaveRows + w;
+  const int nch = d >> 3;
+  float pg[NV][8], pb[NV][8];
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pg[i][e] = pb[i][e] = 0.f;
+  if (row < rows) {
+    const float mu = stats[2 * row], rstd = stats[2 * row + 1];
+    float xh[NV][8], dxh[NV][8];
+    float sa = 0.f, sb = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nch) {
+        float xv[8], gv[8], gm[8];
+        load8<T>(x + int64_t(row) * d + c * 8, xv);
+        load8<float>(dh + int64_t(row) * d + c * 8, gv);
+        load8<float>(gamma + c * 8, gm);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xh[i][e] = (xv[e] - mu) * rstd;
+          dxh[i][e] = gv[e] * gm[e];
+          sa += dxh[i][e];
+          sb += dxh[i][e] * xh[i][e];
+          pg[i][e] = gv[e] * xh[i][e];
+          pb[i][e] = gv[e];
+        }
+      }
+    }
+    const float ma = wave_sum(sa) / float(d);
+    const float mb = wave_sum(sb) / float(d);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nch) {
+        float rv[8], o[8];
+        load8<float>(res_in + int64_t(row) * d + c * 8, rv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = rv[e] + rstd * (dxh[i][e] - ma - xh[i][e] * mb);
+        store8<float>(dx_f32 + int64_t(row) * d + c * 8, o);
+        store8<T>(dx_act + int64_t(row) * d + c * 8, o);
+      }
+    }
+  }
+  float* out = part + int64_t(blockIdx.x) * 2 * d;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nch) store8<float>(lds + w * d + c * 8, half ? pb[i] : pg[i]);
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < nch; c += 256) {
+      float s[8], v[8];
+      load8<float>(lds + c * 8, s);
+#pragma unroll
+      for (int r = 1; r < kLnWaveRows; ++r) {
+        load8<float>(lds + r * d + c * 8, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += v[e];
+      }
+      store8<float>(out + half * d + c * 8, s);
+    }
+    __syncthreads();
+  }
+}
+
+int layernorm_bwd_blocks(int rows, int d) {
+  const int per = (d / 8 <= 512) ? kLnWaveRows : kLnRows;
+  return (rows + per - 1) / per;
+}
 
 template <typename T>
 static hipError_t ln_bwd_t(const float* dh, const void* x, const float* stats, const float* gamma,
                            const float* res_in, float* dx_f32, void* dx_act, float* part,
                            int rows, int d, hipStream_t s) {
   const int nch = d / 8;
-  dim3 grid(layernorm_bwd_blocks(rows)), blk(256);
+  dim3 grid(layernorm_bwd_blocks(rows, d)), blk(256);
   const T* xp = static_cast<const T*>(x);
   T* op = static_cast<T*>(dx_act);
-  if (nch <= 256) hipLaunchKernelGGL((ln_bwd_kernel<T, 1>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d);
+  const size_t sh = size_t(kLnWaveRows) * d * 4;
+#define GP_LNW(NV) hipLaunchKernelGGL((ln_bwd_wave_kernel<T, NV>), grid, blk, sh, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d)
+  if (nch <= 64) GP_LNW(1);
+  else if (nch <= 128) GP_LNW(2);
+  else if (nch <= 256) GP_LNW(4);
+  else if (nch <= 512) GP_LNW(8);
+#undef GP_LNW
+  else if (nch <= 256) hipLaunchKernelGGL((ln_bwd_kernel<T, 1>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d);
   else if (nch <= 512) hipLaunchKernelGGL((ln_bwd_kernel<T, 2>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d);
   else if (nch <= 1024) hipLaunchKernelGGL((ln_bwd_kernel<T, 4>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d);
   else return hipErrorInvalidValue;
@@ -181,7 +276,7 @@ static hipError_t ln_bwd_t(const float* dh, const void* x, const float* stats, c
 hipError_t layernorm_bwd(bool bf16, const float* dh, const void* x, const float* stats,
                          const float* gamma, const float* res_in, float* dx_f32, void* dx_act,
                          float* part, int rows, int d, int* nblk, hipStream_t s) {
-  *nblk = layernorm_bwd_blocks(rows);
+  *nblk = layernorm_bwd_blocks(rows, d);
   if (rows == 0) return hipSuccess;
   return bf16 ? ln_bwd_t<bf16_t>(dh, x, stats, gamma, res_in, dx_f32, dx_act, part, rows, d, s)
               : ln_bwd_t<float>(dh, x, stats, gamma, res_in, dx_f32, dx_act, part, rows, d, s);
