@@ -18,6 +18,16 @@ bool is_wgrad(int role) {
   return role == GPIPE_ROLE_FFN2_WGRAD || role == GPIPE_ROLE_FFN1_WGRAD ||
          role == GPIPE_ROLE_OUT_WGRAD || role == GPIPE_ROLE_QKV_WGRAD;
 }
+bool is_conv(int role) {
+  return role == GPIPE_ROLE_CONV_FWD || role == GPIPE_ROLE_CONV_DGRAD ||
+         role == GPIPE_ROLE_CONV_WGRAD || role == GPIPE_ROLE_CONV_FWD_IMPLICIT ||
+         role == GPIPE_ROLE_CONV_DGRAD_IMPLICIT;
+}
+// B operand k-contiguous (the weight of a forward linear layer)
+bool b_k_contiguous(int role) {
+  return role == GPIPE_ROLE_QKV_FWD || role == GPIPE_ROLE_OUT_FWD || role == GPIPE_ROLE_FFN1_FWD ||
+         role == GPIPE_ROLE_FFN2_FWD;
+}
 int group_of(int role) {
   switch (role) {
     case GPIPE_ROLE_QKV_FWD: case GPIPE_ROLE_OUT_FWD: case GPIPE_ROLE_FFN1_FWD:
@@ -59,29 +69,27 @@ constexpr int kCUs = 256;
 
 }  // namespace
 
-// Tile and split choice, from sweeps of every role's shape on MI355X (the
-// k-contiguous and m-contiguous variants behave alike): 128 x 128 tiles with
-// two workgroups per CU win everywhere, because one workgroup's epilogue
-// overlaps the other's main loop; the attention products (K = 128 or 512,
-// 32 batches) take 64 x 64 tiles.  Split-K pays only when the output has
-// fewer tiles than CUs; it then aims at about two workgroups per CU with
-// splits at least 512 deep.  Weight gradients never split (their fp32
-// partials would double the accumulator traffic).
+// Tile and split choice, from per-role timings on MI355X with random
+// operands.  The linear layers' products (forward, input gradient, weight
+// gradient) take the specialised-wave kernel with 256 x 128 tiles (128 x 256
+// when both operands are k-contiguous and the output is wider than tall) as
+// soon as the output has 64 such tiles: against 128 x 128 tiles with two
+// workgroups per CU it ran 5-22% faster on every role of the 2048-wide layer.
+// When fewer than 192 of those tiles exist the k range is split, aiming at
+// one workgroup per CU with splits at least 1024 deep.  Weight gradients never
+// split (their fp32 partials would double the accumulator traffic).  The
+// attention products (K = 128 or 512, 32 batches) take 64 x 64 tiles, the
+// convolutions and small products 128 x 128 tiles, where split-K pays only
+// when the output has fewer tiles than CUs; it then aims at about two
+// workgroups per CU with splits at least 512 deep.
 GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch) {
   GemmPlan p{is_attention(role) ? CFG_64x64_K64 : CFG_128x128_K64, 1, K};
   if (!bf16) {
     p.cfg = -1;
     return p;
   }
-  // (the convolution's weight gradient is small -- C x 9C -- and reduces over
-  // every pixel of the micro-batch, so it does split)
-  const bool can_split = !is_attention(role) && (!is_wgrad(role) || role == GPIPE_ROLE_CONV_WGRAD) &&
-                         batch == 1;
-  const int bm = kCfgBM[p.cfg], bn = kCfgBN[p.cfg];
-  const long tiles = long((M + bm - 1) / bm) * ((N + bn - 1) / bn) * batch;
-  if (can_split && tiles < kCUs && K >= 1024) {
-    int s = int((2 * kCUs + tiles - 1) / tiles);
-    s = std::min(s, std::min(8, K / 512));
+  auto split_of = [&](int want, int min_depth) {
+    int s = std::min(want, std::min(8, K / min_depth));
     while (s > 1) {
       const int kc = ((K + s - 1) / s + 63) / 64 * 64;
       if ((s - 1) * kc < K) break;
@@ -91,7 +99,24 @@ GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch) {
       p.splits = s;
       p.kchunk = ((K + s - 1) / s + 63) / 64 * 64;
     }
+  };
+  const bool linear = group_of(role) >= 0 && group_of(role) <= 2 && !is_conv(role);
+  if (linear && batch == 1 && K >= 512) {
+    const int cfg = (b_k_contiguous(role) && N > M) ? CFG_128x256_K64 : CFG_256x128_K64;
+    const long tiles = long((M + kCfgBM[cfg] - 1) / kCfgBM[cfg]) * ((N + kCfgBN[cfg] - 1) / kCfgBN[cfg]);
+    if (tiles >= 64) {
+      p.cfg = cfg;
+      if (!is_wgrad(role) && tiles < 192) split_of(int((kCUs + tiles - 1) / tiles), 1024);
+      return p;
+    }
   }
+  // (the convolution's weight gradient is small -- C x 9C -- and reduces over
+  // every pixel of the micro-batch, so it does split)
+  const bool can_split = !is_attention(role) && (!is_wgrad(role) || role == GPIPE_ROLE_CONV_WGRAD) &&
+                         batch == 1;
+  const int bm = kCfgBM[p.cfg], bn = kCfgBN[p.cfg];
+  const long tiles = long((M + bm - 1) / bm) * ((N + bn - 1) / bn) * batch;
+  if (can_split && tiles < kCUs && K >= 1024) split_of(int((2 * kCUs + tiles - 1) / tiles), 512);
   return p;
 }
 
@@ -105,7 +130,11 @@ size_t gemm_partial_floats(int role, bool bf16, int M, int N, int K, int batch) 
 
 hipError_t gemm(bool bf16, int role, const GemmParams& g0, int batch, hipStream_t s) {
   if (!bf16) return gemm_group_f32(role, g0, batch, s);
-  const GemmPlan p = plan_gemm(role, true, g0.M, g0.N, g0.K, batch);
+  return gemm_with_plan(role, plan_gemm(role, true, g0.M, g0.N, g0.K, batch), g0, batch, s);
+}
+
+hipError_t gemm_with_plan(int role, const GemmPlan& p, const GemmParams& g0, int batch, hipStream_t s) {
+  if (p.cfg < 0 || p.cfg >= CFG_N || p.splits < 1) return hipErrorInvalidValue;
   GemmParams g = g0;
   g.kchunk = p.kchunk;
   if (p.splits > 1 && !g.P) return hipErrorInvalidValue;

@@ -408,8 +408,196 @@ __global__ __launch_bounds__(kThreads, C::OCC) void gemm_dma_kernel(GemmParams g
   }
 }
 
-// path 0: direct-to-LDS kernel with configuration DC; path 1: register-staged
-// kernel with tile RC (for k not a multiple of 64).
+// One workgroup per CU, 8 waves in two roles.  Waves 0-3 only read LDS and
+// issue MFMAs (2 x 2 grid, each a (BM/2) x (BN/2) block); waves 4-7 only
+// issue the direct-to-LDS loads.  A wave issues in order, and a load
+// instruction waits for the CU's texture unit: issued from the MFMA waves, the
+// loads of one k-tile stalled the MFMAs behind them for about 60% of the
+// k-tile's MFMA time on gfx950, so the loads live in waves of their own.
+// Three LDS stages: after barrier j of the k loop the stage of tile j is free
+// (its last fragments were read before the barrier) and the loader waves
+// refill it with tile j + 3; before barrier j they wait for tile j + 1.
+// MFMA waves keep the B fragments of both k-steps of a tile in registers and
+// stream the A fragments (A row block i of the next k-step is read as soon as
+// its MFMAs of the current one are issued), which fits in 256 VGPRs; the
+// scheduling hints interleave one LDS read with a few MFMAs.  LDS is dynamic
+// (set at launch) so that the register budget is that of two waves per SIMD.
+constexpr int kSpecThreads = 512;
+
+template <class C>
+constexpr int spec_smem_bytes() {
+  constexpr int pipe = 3 * (C::BM + C::BN) * 64 * 2, tile = C::BM * (C::BN + 4) * 4;
+  return pipe > tile ? pipe : tile;
+}
+
+template <class C, int LA, int LB, int EPI, int ROLE>
+__global__ __launch_bounds__(kSpecThreads, 1) void gemm_spec_kernel(GemmParams g) {
+  constexpr int BM = C::BM, BN = C::BN, BK = 64, FM = C::FM, FN = C::FN;
+  static_assert(C::BK == 64 && C::STAGES == 3, "specialised kernel: 64-deep k-tiles, 3 stages");
+  using OA = DmaOperand<BM, BK, LA>;
+  using OB = DmaOperand<BN, BK, LB>;
+  constexpr int LPT = OA::PER_WAVE + OB::PER_WAVE;  // loads per loader wave per k-tile
+  static_assert(LPT * 2 < 64, "vmcnt range");
+  constexpr int RA = LA == LAY_MN ? 2 : 1, RB = LB == LAY_MN ? 2 : 1;  // LDS reads per fragment
+  constexpr int STAGE = (BM + BN) * BK, TP = BN + 4;
+  extern __shared__ __attribute__((aligned(1024))) bf16_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, cw = wave & 3;
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, BM, BN, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int z = blockIdx.z, zb = z / g.hdiv, zh = z % g.hdiv;
+  int kbeg, kend;
+  if (!causal_range(g, m0, n0, BM, BK, &kbeg, &kend)) return;
+  const int split = blockIdx.y;
+  if (gridDim.y > 1) {
+    kbeg = max(kbeg, split * g.kchunk);
+    kend = min(kend, (split + 1) * g.kchunk);
+  }
+  const int nkt = kend > kbeg ? (kend - kbeg) / BK : 0;
+  auto sa = [&](int st) { return smem + st * STAGE; };
+  auto sb = [&](int st) { return smem + st * STAGE + BM * BK; };
+
+  floatx4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  const int wm0 = (cw >> 1) * C::WTM, wn0 = (cw & 1) * C::WTN;
+
+  if (wave >= 4) {
+    // ---- loader waves
+    const bf16_t* A = static_cast<const bf16_t*>(g.A) + zb * g.sAb + zh * g.sAh;
+    const bf16_t* B = static_cast<const bf16_t*>(g.B) + zb * g.sBb + zh * g.sBh;
+    OA oa;
+    OB ob;
+    oa.init(g.lda, m0, g.M, kbeg, cw, lane);
+    ob.init(g.ldb, n0, g.N, kbeg, cw, lane);
+    const int pre = min(3, nkt);
+    for (int t = 0; t < pre; ++t) {
+      oa.issue(A, t, sa(t), cw);
+      ob.issue(B, t, sb(t), cw);
+    }
+    wait_tiles<LPT, 2>(pre - 1);  // tile 0 has landed
+    barrier_nofence();
+    for (int kt = 0; kt < nkt; ++kt) {
+      wait_tiles<LPT, 1>(min(1, nkt - 2 - kt));  // tile kt + 1 has landed
+      barrier_nofence();
+      if (kt + 3 < nkt) {
+        const int st = kt % 3;
+        oa.issue(A, kt + 3, sa(st), cw);
+        ob.issue(B, kt + 3, sb(st), cw);
+      }
+    }
+    wait_vmcnt<0>();
+  } else {
+    // ---- MFMA waves
+    OA oa;  // fragment addressing only
+    OB ob;
+    bf16x8_t fa[FM], fb0[FN], fb1[FN];
+    barrier_nofence();
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = oa.frag(sa(0), wm0 + i * 16, lane, 0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb0[j] = ob.frag(sb(0), wn0 + j * 16, lane, 0);
+    constexpr int REST = FM * FN - 1 - FN * RB;
+    constexpr int PER_A = REST / FM;
+    int s_cur = 0;
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int s_nxt = s_cur == 2 ? 0 : s_cur + 1;
+      {  // k-step 0 of tile kt; read k-step 1
+        const bf16_t* as = sa(s_cur);
+        const bf16_t* bs = sb(s_cur);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb1[j] = ob.frag(bs, wn0 + j * 16, lane, 1);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb0[j], acc[i][j], 0, 0, 0);
+          fa[i] = oa.frag(as, wm0 + i * 16, lane, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+        for (int q = 0; q < FN * RB; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < FM; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, PER_A, 0);
+        }
+      }
+      // tile kt + 1 has landed; every wave is done reading tile kt's stage
+      barrier_lds();
+      {  // k-step 1 of tile kt; read k-step 0 of tile kt + 1
+        const bf16_t* as = sa(s_nxt);
+        const bf16_t* bs = sb(s_nxt);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb0[j] = ob.frag(bs, wn0 + j * 16, lane, 0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb1[j], acc[i][j], 0, 0, 0);
+          fa[i] = oa.frag(as, wm0 + i * 16, lane, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+        for (int q = 0; q < FN * RB; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < FM; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, PER_A, 0);
+        }
+      }
+      s_cur = s_nxt;
+    }
+  }
+
+  // Epilogue through LDS (every load has landed: the loader waves drained
+  // theirs before this barrier), then all 8 waves store.
+  barrier_lds();
+  float* tile = reinterpret_cast<float*>(smem);
+  if (wave < 4) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          tile[(wm0 + i * 16 + (lane >> 4) * 4 + v) * TP + wn0 + j * 16 + (lane & 15)] = acc[i][j][v];
+  }
+  barrier_lds();
+  float* P = gridDim.y > 1 ? g.P + int64_t(split) * g.M * g.N : nullptr;
+  const int64_t coff = zb * g.sCb + zh * g.sCh;
+  constexpr int CH = BN / 8;
+  for (int idx = tid; idx < BM * CH; idx += kSpecThreads) {
+    const int r = idx / CH, c = (idx % CH) * 8;
+    const int row = m0 + r, col = n0 + c;
+    if (row >= g.M || col >= g.N) continue;
+    const float4 t0 = *reinterpret_cast<const float4*>(tile + r * TP + c);
+    const float4 t1 = *reinterpret_cast<const float4*>(tile + r * TP + c + 4);
+    const float a[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+    if (col + 8 <= g.N) {
+      epi_store8<EPI>(g, row, col, a, coff, P);
+    } else {
+      for (int e = 0; e < 8 && col + e < g.N; ++e) {
+        if (P) P[int64_t(row) * g.N + col + e] = a[e];
+        else epi_store<bf16_t, EPI>(g, row, col + e, a[e], coff);
+      }
+    }
+  }
+}
+
+// path 0: direct-to-LDS kernel with configuration DC (the specialised-wave
+// kernel for the one-workgroup-per-CU 3-stage configurations); path 1:
+// register-staged kernel with tile RC (for k not a multiple of 64).
 template <class DC, class RC, int LA, int LB, int EPI, int ROLE>
 hipError_t launch_bf16(int path, const GemmParams& g, int batch, int splits, hipStream_t s) {
   const int bm = path == 0 ? DC::BM : RC::BM, bn = path == 0 ? DC::BN : RC::BN;
@@ -421,7 +609,17 @@ hipError_t launch_bf16(int path, const GemmParams& g, int batch, int splits, hip
     if (path != 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_dma_kernel<DC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, g);
   } else if (path == 0) {
-    hipLaunchKernelGGL((gemm_dma_kernel<DC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, g);
+    if constexpr (DC::OCC == 1 && DC::BK == 64 && DC::STAGES == 3) {
+      constexpr int smem = spec_smem_bytes<DC>();
+      static const hipError_t attr = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&gemm_spec_kernel<DC, LA, LB, EPI, ROLE>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+      if (attr != hipSuccess) return attr;
+      hipLaunchKernelGGL((gemm_spec_kernel<DC, LA, LB, EPI, ROLE>), grid, dim3(kSpecThreads), smem,
+                         s, g);
+    } else {
+      hipLaunchKernelGGL((gemm_dma_kernel<DC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, g);
+    }
   } else {
     hipLaunchKernelGGL((gemm_bf16_kernel<RC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, g);
   }

@@ -53,6 +53,10 @@ struct GemmPlan {
   int kchunk;
 };
 GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch);
+// bf16 GEMM with a given plan (the planner's choice is gemm(); this form lets
+// a benchmark compare tile configurations).  The partial buffer g.P must hold
+// splits * M * N floats when the plan splits.
+hipError_t gemm_with_plan(int role, const GemmPlan& plan, const GemmParams& g, int batch, hipStream_t s);
 int gemm_cfg_bm(int cfg);
 int gemm_cfg_bn(int cfg);
 // Floats of split-K partials the launch needs (0 if it does not split).

@@ -207,6 +207,16 @@ def test_ragged_tiles_direct_lds_path_bf16():
     check(cfg.with_(causal=True))
 
 
+def test_ragged_tiles_specialised_kernel_bf16():
+    """Outputs with at least 64 tiles of 256 x 128 take the specialised-wave GEMM
+    (loader and MFMA waves); here with ragged M / N edges on k-contiguous and
+    m-contiguous operands: T = 576 rows per micro-batch, D = 1152, F = 4160,
+    S = 288, head_dim 128 (the plans are checked on the host)."""
+    cfg = configs.SMALL.with_(name="spec_ragged_bf16", layers=1, d_model=1152, heads=9,
+                              d_ff=4160, seq=288, batch=2, micro=1)
+    check(cfg)
+
+
 @pytest.mark.parametrize("dh,seq", [(128, 100), (64, 70), (128, 64), (64, 1)])
 def test_fused_attention_ragged_sequences_bf16(dh, seq):
     """The fused attention kernels (bf16, head dim 64 / 128) with sequence lengths
