@@ -133,12 +133,26 @@ hipError_t gemm(bool bf16, int role, const GemmParams& g0, int batch, hipStream_
   return gemm_with_plan(role, plan_gemm(role, true, g0.M, g0.N, g0.K, batch), g0, batch, s);
 }
 
+namespace {
+bool spec_cfg(int cfg) { return cfg == CFG_256x128_K64 || cfg == CFG_128x256_K64; }
+}  // namespace
+
+int gemm_rowsum_parts(int role, const GemmParams& g, int batch) {
+  if (!is_wgrad(role) || batch != 1) return 0;
+  const GemmPlan p = plan_gemm(role, true, g.M, g.N, g.K, batch);
+  if (!(spec_cfg(p.cfg) && p.splits == 1 && dma_ok(role, g))) return 0;
+  return (g.N + kCfgBN[p.cfg] - 1) / kCfgBN[p.cfg];
+}
+
 hipError_t gemm_with_plan(int role, const GemmPlan& p, const GemmParams& g0, int batch, hipStream_t s) {
   if (p.cfg < 0 || p.cfg >= CFG_N || p.splits < 1) return hipErrorInvalidValue;
   GemmParams g = g0;
   g.kchunk = p.kchunk;
   if (p.splits > 1 && !g.P) return hipErrorInvalidValue;
   const int path = dma_ok(role, g) ? 0 : 1;
+  // row sums come only from the specialised kernel of a weight gradient, unsplit
+  if (g.rowsum && !(is_wgrad(role) && batch == 1 && spec_cfg(p.cfg) && p.splits == 1 && path == 0))
+    return hipErrorInvalidValue;
   int cfg = p.cfg;
   switch (group_of(role)) {
     case 0: return gemm_group_fwd(role, path, cfg, g, batch, p.splits, s);

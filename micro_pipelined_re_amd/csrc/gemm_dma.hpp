@@ -424,6 +424,19 @@ __global__ __launch_bounds__(kThreads, C::OCC) void gemm_dma_kernel(GemmParams g
 // (set at launch) so that the register budget is that of two waves per SIMD.
 constexpr int kSpecThreads = 512;
 
+// acc + the sum of a fragment's 8 bf16 values (pairs through the bf16 dot
+// product with (1, 1)), in a fixed order
+__device__ __forceinline__ float frag_sum(const bf16x8_t& v, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const bf16x2_t p = {v[e], v[e + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(p, one, acc, false);
+  }
+  return acc;
+}
+
 template <class C>
 constexpr int spec_smem_bytes() {
   constexpr int pipe = 3 * (C::BM + C::BN) * 64 * 2, tile = C::BM * (C::BN + 4) * 4;
@@ -440,6 +453,14 @@ __global__ __launch_bounds__(kSpecThreads, 1) void gemm_spec_kernel(GemmParams g
   static_assert(LPT * 2 < 64, "vmcnt range");
   constexpr int RA = LA == LAY_MN ? 2 : 1, RB = LB == LAY_MN ? 2 : 1;  // LDS reads per fragment
   constexpr int STAGE = (BM + BN) * BK, TP = BN + 4;
+  // Weight gradients can also sum A over k (the bias gradient).  The loader
+  // waves do it from the LDS tiles they loaded, with the MFMA fragment reads
+  // (lane l: 8 k-values of row l % 16) and bf16 dot products against (1, 1);
+  // each wave owns MB blocks of 16 rows.  Tile column tn sums its share of
+  // the k-tiles (the tile columns of one tile row see the same A) and writes
+  // partial sums for its rows; a second pass adds up the tile columns.
+  constexpr bool RS = EPI == EPI_ACC_F32 && LA == LAY_MN;
+  constexpr int MB = BM / 64;
   extern __shared__ __attribute__((aligned(1024))) bf16_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, cw = wave & 3;
@@ -481,9 +502,29 @@ __global__ __launch_bounds__(kSpecThreads, 1) void gemm_spec_kernel(GemmParams g
     }
     wait_tiles<LPT, 2>(pre - 1);  // tile 0 has landed
     barrier_nofence();
+    // row sums (RS): tile t is in LDS from barrier t-1 (the prologue barrier
+    // for t = 0) until barrier t; this wave's reads end before it arrives there
+    const bool do_rs = RS && g.rowsum;
+    const int rs_per = (nkt + tiles_n - 1) / tiles_n;
+    const int rs_lo = tn * rs_per, rs_hi = min(nkt, rs_lo + rs_per);  // this tile column's k-tiles
+    float rsum[MB];
+#pragma unroll
+    for (int j = 0; j < MB; ++j) rsum[j] = 0.f;
+    auto add_rows = [&](int st) {
+#pragma unroll
+      for (int j = 0; j < MB; ++j)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) rsum[j] = frag_sum(oa.frag(sa(st), (cw * MB + j) * 16, lane, ks), rsum[j]);
+      // the sums exist before the next barrier, so the reads behind them have
+      // completed (an lgkmcnt(0) there would also wait for the loads in flight)
+#pragma unroll
+      for (int j = 0; j < MB; ++j) asm volatile("" ::"v"(rsum[j]));
+    };
+    if (do_rs && rs_lo <= 0 && 0 < rs_hi) add_rows(0);
     for (int kt = 0; kt < nkt; ++kt) {
       wait_tiles<LPT, 1>(min(1, nkt - 2 - kt));  // tile kt + 1 has landed
       barrier_nofence();
+      if (do_rs && rs_lo <= kt + 1 && kt + 1 < rs_hi) add_rows((kt + 1) % 3);
       if (kt + 3 < nkt) {
         const int st = kt % 3;
         oa.issue(A, kt + 3, sa(st), cw);
@@ -491,6 +532,17 @@ __global__ __launch_bounds__(kSpecThreads, 1) void gemm_spec_kernel(GemmParams g
       }
     }
     wait_vmcnt<0>();
+    if (do_rs) {
+      // the four lane groups hold disjoint k-values of the same rows
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        float v = rsum[j];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        const int row = m0 + (cw * MB + j) * 16 + lane;
+        if (lane < 16 && row < g.M) g.rowsum[int64_t(tn) * g.M + row] = v;
+      }
+    }
   } else {
     // ---- MFMA waves
     OA oa;  // fragment addressing only

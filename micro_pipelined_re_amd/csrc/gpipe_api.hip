@@ -32,7 +32,8 @@ namespace {
 //   r0, r1, dm: float32 [T, D]   (residual-stream gradients, LN input grads)
 //   a0, a1, dctx: act [T, D]
 //   du: act [T, F];  dqkv: act [T, 3D]
-//   colpart: float32 [colsum chunks, max(3D, F)]
+//   colpart: float32 [colsum chunks, max(3D, F)], or the weight-gradient
+//            kernels' partial bias sums [N / 128, M], whichever is larger
 //   lnpart:  float32 [LN blocks, 2D]
 //   msepart: float32 [M, mse blocks]
 struct Plan {
@@ -44,6 +45,7 @@ struct Plan {
   size_t layer_bytes, set_bytes;
   int nsets;
   size_t yre, scores, ds, r0, r1, dm, a0, a1, dctx, du, dqkv, colpart, lnpart, msepart, splitk;
+  size_t colpart_floats;
   int mse_nblk;
   size_t total;
 };
@@ -96,7 +98,11 @@ bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
   p->dctx = take(T * D * eb);
   p->du = take(T * F * eb);
   p->dqkv = take(T * 3 * D * eb);
-  p->colpart = take(size_t(colsum_chunks(int(T))) * std::max(3 * D, F) * 4);
+  // (also the weight-gradient kernels' partial bias sums: [N / 128][M] at most)
+  p->colpart_floats = std::max(size_t(colsum_chunks(int(T))) * std::max(3 * D, F),
+                               std::max(size_t((D + 127) / 128) * std::max(3 * D, F),
+                                        size_t((F + 127) / 128) * D));
+  p->colpart = take(p->colpart_floats * 4);
   p->lnpart = take(size_t(layernorm_bwd_blocks(int(T), c->D)) * 2 * D * 4);
   p->mse_nblk = mse_blocks(int64_t(T) * int64_t(D));
   p->msepart = take(size_t(M) * size_t(p->mse_nblk) * 4);
@@ -165,6 +171,28 @@ hipError_t mm(const Ctx& x, int role, int M, int N, int K, const void* A, int64_
   g.bias = bias; g.R = R; g.ldr = ldr; g.U = U; g.ldu = ldu; g.beta = beta;
   g.P = static_cast<float*>(x.at(x.p->splitk));
   return gemm(x.bf16, role, g, 1, x.s);
+}
+
+// Weight gradient G (+)= A^T-product over tokens; where the launch supports it
+// the same kernel also sums A over tokens in partial vectors (the bias
+// gradient, added up here into bgrad) and *fused is set; otherwise the caller
+// sums the bias gradient.
+hipError_t mm_wgrad(const Ctx& x, int role, int M, int N, int K, const void* A, int64_t lda,
+                    const void* B, int64_t ldb, float* C, int64_t ldc, int beta, float* bgrad,
+                    bool* fused) {
+  GemmParams g = gp0();
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda;
+  g.B = B; g.ldb = ldb;
+  g.C = C; g.ldc = ldc;
+  g.beta = beta;
+  g.P = static_cast<float*>(x.at(x.p->splitk));
+  const int parts = x.bf16 ? gemm_rowsum_parts(role, g, 1) : 0;
+  *fused = parts > 0 && size_t(parts) * M <= x.p->colpart_floats;
+  if (*fused) g.rowsum = static_cast<float*>(x.at(x.p->colpart));
+  hipError_t e = gemm(x.bf16, role, g, 1, x.s);
+  if (e != hipSuccess || !*fused) return e;
+  return sum_partials(g.rowsum, parts, M, M, bgrad, beta, x.s);
 }
 
 // Batched over (sequence b, head h) of one micro-batch.
@@ -292,13 +320,16 @@ gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int b
   // FFN: y = x1 + g W2^T + b2,  g = gelu(u),  u = h2 W1^T + b1
   GP_RUN(x, GPIPE_ROLE_FFN2_DGRAD, mm(x, GPIPE_ROLE_FFN2_DGRAD, T, F, D, a0, D, x.wmat(l, GPIPE_W_2), F, du, F,
               nullptr, nullptr, 0, u, F));
-  GP_RUN(x, GPIPE_ROLE_FFN2_WGRAD, mm(x, GPIPE_ROLE_FFN2_WGRAD, D, F, T, a0, D, g, F, x.grad(l, GPIPE_W_2), F,
-              nullptr, nullptr, 0, nullptr, 0, beta));
-  GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r0, D, D, x.grad(l, GPIPE_B_2), beta));
+  // (bias gradients: from the weight-gradient kernel where it sums them --
+  // over the bf16 copy of the output gradient it reads -- else summed here)
+  bool fused = false;
+  GP_RUN(x, GPIPE_ROLE_FFN2_WGRAD, mm_wgrad(x, GPIPE_ROLE_FFN2_WGRAD, D, F, T, a0, D, g, F, x.grad(l, GPIPE_W_2),
+              F, beta, x.grad(l, GPIPE_B_2), &fused));
+  if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r0, D, D, x.grad(l, GPIPE_B_2), beta));
   GP_RUN(x, GPIPE_ROLE_FFN1_DGRAD, mm(x, GPIPE_ROLE_FFN1_DGRAD, T, D, F, du, F, x.wmat(l, GPIPE_W_1), D, dm, D));
-  GP_RUN(x, GPIPE_ROLE_FFN1_WGRAD, mm(x, GPIPE_ROLE_FFN1_WGRAD, F, D, T, du, F, h2, D, x.grad(l, GPIPE_W_1), D,
-              nullptr, nullptr, 0, nullptr, 0, beta));
-  GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, du, F, F, x.grad(l, GPIPE_B_1), beta));
+  GP_RUN(x, GPIPE_ROLE_FFN1_WGRAD, mm_wgrad(x, GPIPE_ROLE_FFN1_WGRAD, F, D, T, du, F, h2, D, x.grad(l, GPIPE_W_1),
+              D, beta, x.grad(l, GPIPE_B_1), &fused));
+  if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, du, F, F, x.grad(l, GPIPE_B_1), beta));
   int nblk = 0;
   GP_RUN(x, GPIPE_ROLE_LN2_BWD, layernorm_bwd(bf, dm, x1, st2, x.wf32(l, GPIPE_LN2_G), r0, r1, a1, lnpart, T, D, &nblk,
                          x.s));
@@ -307,9 +338,9 @@ gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int b
 
   // attention: x1 = x + ctx Wo^T + bo
   GP_RUN(x, GPIPE_ROLE_OUT_DGRAD, mm(x, GPIPE_ROLE_OUT_DGRAD, T, D, D, a1, D, x.wmat(l, GPIPE_W_O), D, dctx, D));
-  GP_RUN(x, GPIPE_ROLE_OUT_WGRAD, mm(x, GPIPE_ROLE_OUT_WGRAD, D, D, T, a1, D, ctx, D, x.grad(l, GPIPE_W_O), D,
-              nullptr, nullptr, 0, nullptr, 0, beta));
-  GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r1, D, D, x.grad(l, GPIPE_B_O), beta));
+  GP_RUN(x, GPIPE_ROLE_OUT_WGRAD, mm_wgrad(x, GPIPE_ROLE_OUT_WGRAD, D, D, T, a1, D, ctx, D, x.grad(l, GPIPE_W_O),
+              D, beta, x.grad(l, GPIPE_B_O), &fused));
+  if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r1, D, D, x.grad(l, GPIPE_B_O), beta));
   const int64_t sq = int64_t(S) * 3 * D;
   const int64_t sp = int64_t(H) * S * ldS;
   const int64_t sd = int64_t(S) * D;
@@ -339,9 +370,10 @@ gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int b
   // qkv = h1 Wqkv^T + bqkv,  h1 = LN1(x)
   GP_RUN(x, GPIPE_ROLE_QKV_DGRAD, mm(x, GPIPE_ROLE_QKV_DGRAD, T, D, 3 * D, dqkv, 3 * D, x.wmat(l, GPIPE_W_QKV), D,
               dm, D));
-  GP_RUN(x, GPIPE_ROLE_QKV_WGRAD, mm(x, GPIPE_ROLE_QKV_WGRAD, 3 * D, D, T, dqkv, 3 * D, h1, D,
-              x.grad(l, GPIPE_W_QKV), D, nullptr, nullptr, 0, nullptr, 0, beta));
-  GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, dqkv, 3 * D, 3 * D, x.grad(l, GPIPE_B_QKV), beta));
+  GP_RUN(x, GPIPE_ROLE_QKV_WGRAD, mm_wgrad(x, GPIPE_ROLE_QKV_WGRAD, 3 * D, D, T, dqkv, 3 * D, h1, D,
+              x.grad(l, GPIPE_W_QKV), D, beta, x.grad(l, GPIPE_B_QKV), &fused));
+  if (!fused)
+    GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, dqkv, 3 * D, 3 * D, x.grad(l, GPIPE_B_QKV), beta));
   GP_RUN(x, GPIPE_ROLE_LN1_BWD, layernorm_bwd(bf, dm, xin, st1, x.wf32(l, GPIPE_LN1_G), r1, r0, dx_out ? dx_out : a0,
                          lnpart, T, D, &nblk, x.s));
   GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(lnpart, nblk, 2 * D, 2 * D, x.grad(l, GPIPE_LN1_G), beta, x.s));

@@ -44,6 +44,10 @@ struct GemmParams {
   float* P;     // split-K partials [splits][M][N] (f32), required when the plan splits
   int kchunk;   // split-K: k extent of one split (set by gemm())
   int conv_h, conv_w, conv_c;  // image geometry of a LAY_CONV operand
+  // Optional (weight-gradient roles, where gemm_rowsum_parts() > 0): partial
+  // sums of A over k, rowsum[t * M + m] for tile column t; summed over t they
+  // give the row sums (each tile column adds up its own share of the k-tiles).
+  float* rowsum;
 };
 
 // Macro tile and split-K chosen for one GEMM launch.
@@ -57,6 +61,10 @@ GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch);
 // a benchmark compare tile configurations).  The partial buffer g.P must hold
 // splits * M * N floats when the plan splits.
 hipError_t gemm_with_plan(int role, const GemmPlan& plan, const GemmParams& g, int batch, hipStream_t s);
+// Number of partial row-sum vectors (GemmParams::rowsum) the bf16 launch of
+// this role and shape writes, 0 where it cannot: the bias gradient of a
+// weight-gradient product, from the tiles of the output gradient in LDS.
+int gemm_rowsum_parts(int role, const GemmParams& g, int batch);
 int gemm_cfg_bm(int cfg);
 int gemm_cfg_bn(int cfg);
 // Floats of split-K partials the launch needs (0 if it does not split).
