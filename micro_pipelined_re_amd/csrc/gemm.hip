@@ -71,13 +71,15 @@ constexpr int kCUs = 256;
 
 // Tile and split choice, from per-role timings on MI355X with random
 // operands.  The linear layers' products (forward, input gradient, weight
-// gradient) take the specialised-wave kernel with 256 x 128 tiles (128 x 256
-// when both operands are k-contiguous and the output is wider than tall) as
-// soon as the output has 64 such tiles: against 128 x 128 tiles with two
-// workgroups per CU it ran 5-22% faster on every role of the 2048-wide layer.
-// When fewer than 192 of those tiles exist the k range is split, aiming at
-// one workgroup per CU with splits at least 1024 deep.  Weight gradients never
-// split (their fp32 partials would double the accumulator traffic).  The
+// gradient) take the specialised-wave kernel: 256 x 128 tiles (128 x 256
+// when both operands are k-contiguous and the output is wider than tall)
+// when the output has at least 192 of them, else 128 x 128 tiles, split in
+// two for k >= 4096 (a 1024 x 2048 output: 18 us unsplit at k = 2048 against
+// 28 us for 256 x 128 tiles split in two, 45 us split in two at k = 8192
+// against 48 us split in four).  Against 128 x 128 tiles with two workgroups
+// per CU the specialised kernel ran 5-37% faster on every role of the
+// 2048-wide layer.  Weight gradients never split (their fp32 partials would
+// double the accumulator traffic).  The
 // attention products (K = 128 or 512, 32 batches) take 64 x 64 tiles, the
 // convolutions and small products 128 x 128 tiles, where split-K pays only
 // when the output has fewer tiles than CUs; it then aims at about two
@@ -104,9 +106,16 @@ GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch) {
   if (linear && batch == 1 && K >= 512) {
     const int cfg = (b_k_contiguous(role) && N > M) ? CFG_128x256_K64 : CFG_256x128_K64;
     const long tiles = long((M + kCfgBM[cfg] - 1) / kCfgBM[cfg]) * ((N + kCfgBN[cfg] - 1) / kCfgBN[cfg]);
-    if (tiles >= 64) {
+    if (tiles >= 192) {
       p.cfg = cfg;
-      if (!is_wgrad(role) && tiles < 192) split_of(int((kCUs + tiles - 1) / tiles), 1024);
+      return p;
+    }
+    const long t128 = long((M + 127) / 128) * ((N + 127) / 128);
+    if (t128 >= 64) {
+      // fewer big tiles than 3/4 of the CUs: 128 x 128 tiles, and for deep k
+      // two splits (the partial sums cost less than the idle CUs)
+      p.cfg = CFG_128x128_SPEC;
+      if (!is_wgrad(role) && K >= 4096 && t128 < 192) split_of(2, 1024);
       return p;
     }
   }
@@ -134,7 +143,9 @@ hipError_t gemm(bool bf16, int role, const GemmParams& g0, int batch, hipStream_
 }
 
 namespace {
-bool spec_cfg(int cfg) { return cfg == CFG_256x128_K64 || cfg == CFG_128x256_K64; }
+bool spec_cfg(int cfg) {
+  return cfg == CFG_256x128_K64 || cfg == CFG_128x256_K64 || cfg == CFG_128x128_SPEC;
+}
 }  // namespace
 
 int gemm_rowsum_parts(int role, const GemmParams& g, int batch) {
