@@ -540,7 +540,10 @@ __global__ __launch_bounds__(kSpecThreads, 1) void gemm_spec_kernel(GemmParams g
         v += __shfl_xor(v, 16);
         v += __shfl_xor(v, 32);
         const int row = m0 + (cw * MB + j) * 16 + lane;
-        if (lane < 16 && row < g.M) g.rowsum[int64_t(tn) * g.M + row] = v;
+        if (lane < 16 && row < g.M) {
+          float* dst = g.rowsum + int64_t(tn) * g.M + row;
+          *dst = g.beta ? *dst + v : v;
+        }
       }
     }
   } else {

@@ -32,10 +32,24 @@ namespace {
 //   r0, r1, dm: float32 [T, D]   (residual-stream gradients, LN input grads)
 //   a0, a1, dctx: act [T, D]
 //   du: act [T, F];  dqkv: act [T, 3D]
-//   colpart: float32 [colsum chunks, max(3D, F)], or the weight-gradient
-//            kernels' partial bias sums [N / 128, M], whichever is larger
-//   lnpart:  float32 [LN blocks, 2D]
+//   colpart: float32 [colsum chunks, max(3D, F)] (bias gradients summed by
+//            column sums: fp32 cells, or shapes the weight-gradient kernel
+//            does not sum)
+//   gpart:   per layer, float32 block partial sums that stay in place for the
+//            whole backward phase: LN1 and LN2 [LN blocks][2D] (gain, shift)
+//            and, where the weight-gradient kernel sums the bias gradient,
+//            its partial rows [parts][rows] for b_qkv, b_o, b_1, b_2.  Micro-
+//            batch 0 writes them, the others add; after the last micro-batch
+//            one fixed-order pass per tensor reduces them into G.
 //   msepart: float32 [M, mse blocks]
+enum { GPS_LN1, GPS_LN2, GPS_BQKV, GPS_BO, GPS_B1, GPS_B2, GPS_N };
+
+// Parameters of a weight-gradient product G[M][N] (+)= A^T-product over K
+// tokens; make_plan and mm_wgrad build them the same way, so the plan's
+// partial-row counts are the launches' counts.
+GemmParams wgrad_params(int M, int N, int K, const void* A, int64_t lda, const void* B,
+                        int64_t ldb, float* C, int64_t ldc, int beta);
+
 struct Plan {
   int N, M, B, T, ldS;
   bool flash;  // fused attention kernels
@@ -44,8 +58,11 @@ struct Plan {
   size_t saved_bytes[GPIPE_N_SAVED];
   size_t layer_bytes, set_bytes;
   int nsets;
-  size_t yre, scores, ds, r0, r1, dm, a0, a1, dctx, du, dqkv, colpart, lnpart, msepart, splitk;
+  size_t yre, scores, ds, r0, r1, dm, a0, a1, dctx, du, dqkv, colpart, gpart, msepart, splitk;
   size_t colpart_floats;
+  // gpart slots (GPS_*): offset inside a layer's block, partial rows, row length
+  size_t gp_off[GPS_N], gp_layer;
+  int gp_parts[GPS_N], gp_cols[GPS_N];
   int mse_nblk;
   size_t total;
 };
@@ -98,12 +115,36 @@ bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
   p->dctx = take(T * D * eb);
   p->du = take(T * F * eb);
   p->dqkv = take(T * 3 * D * eb);
-  // (also the weight-gradient kernels' partial bias sums: [N / 128][M] at most)
-  p->colpart_floats = std::max(size_t(colsum_chunks(int(T))) * std::max(3 * D, F),
-                               std::max(size_t((D + 127) / 128) * std::max(3 * D, F),
-                                        size_t((F + 127) / 128) * D));
+  p->colpart_floats = size_t(colsum_chunks(int(T))) * std::max(3 * D, F);
   p->colpart = take(p->colpart_floats * 4);
-  p->lnpart = take(size_t(layernorm_bwd_blocks(int(T), c->D)) * 2 * D * 4);
+  {
+    const int Ti = int(T), Di = c->D, Fi = c->F;
+    const int nbl = layernorm_bwd_blocks(Ti, Di);
+    // role, rows M, columns N, lda, ldb (= ldc) of the four weight gradients
+    const int wg[4][5] = {{GPIPE_ROLE_QKV_WGRAD, 3 * Di, Di, 3 * Di, Di},
+                          {GPIPE_ROLE_OUT_WGRAD, Di, Di, Di, Di},
+                          {GPIPE_ROLE_FFN1_WGRAD, Fi, Di, Fi, Di},
+                          {GPIPE_ROLE_FFN2_WGRAD, Di, Fi, Di, Fi}};
+    size_t lo = 0;
+    for (int k = 0; k < GPS_N; ++k) {
+      int parts = 0, cols = 0;
+      if (k <= GPS_LN2) {
+        parts = nbl;
+        cols = 2 * Di;
+      } else if (c->prec == GPIPE_BF16) {
+        const int* r = wg[k - GPS_BQKV];
+        const GemmParams g = wgrad_params(r[1], r[2], Ti, nullptr, r[3], nullptr, r[4], nullptr, r[4], 0);
+        parts = gemm_rowsum_parts(r[0], g, 1);
+        cols = r[1];
+      }
+      p->gp_off[k] = lo;
+      p->gp_parts[k] = parts;
+      p->gp_cols[k] = parts ? cols : 0;
+      lo += align_up(size_t(parts) * cols * 4, kAlign);
+    }
+    p->gp_layer = lo;
+    p->gpart = take(size_t(c->L) * lo);
+  }
   p->mse_nblk = mse_blocks(int64_t(T) * int64_t(D));
   p->msepart = take(size_t(M) * size_t(p->mse_nblk) * 4);
   // split-K partials of the largest split GEMM of a layer (none for fp32 cells)
@@ -124,6 +165,10 @@ bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
 // layout but is never used (its input is the caller's x).
 inline size_t saved_at(const Plan& p, int set, int layer, int which) {
   return size_t(set) * p.set_bytes + size_t(layer) * p.layer_bytes + p.saved_off[which];
+}
+
+inline size_t gpart_at(const Plan& p, int layer, int slot) {
+  return p.gpart + size_t(layer) * p.gp_layer + p.gp_off[slot];
 }
 
 struct Ctx {
@@ -173,26 +218,32 @@ hipError_t mm(const Ctx& x, int role, int M, int N, int K, const void* A, int64_
   return gemm(x.bf16, role, g, 1, x.s);
 }
 
-// Weight gradient G (+)= A^T-product over tokens; where the launch supports it
-// the same kernel also sums A over tokens in partial vectors (the bias
-// gradient, added up here into bgrad) and *fused is set; otherwise the caller
-// sums the bias gradient.
-hipError_t mm_wgrad(const Ctx& x, int role, int M, int N, int K, const void* A, int64_t lda,
-                    const void* B, int64_t ldb, float* C, int64_t ldc, int beta, float* bgrad,
-                    bool* fused) {
+GemmParams wgrad_params(int M, int N, int K, const void* A, int64_t lda, const void* B,
+                        int64_t ldb, float* C, int64_t ldc, int beta) {
   GemmParams g = gp0();
   g.M = M; g.N = N; g.K = K;
   g.A = A; g.lda = lda;
   g.B = B; g.ldb = ldb;
   g.C = C; g.ldc = ldc;
   g.beta = beta;
+  return g;
+}
+
+// Weight gradient G (+)= A^T-product over tokens.  Where the plan gives the
+// layer's bias a gpart slot (bf16 cells, shapes the specialised kernel
+// takes), the same kernel also sums A over tokens into that slot's partial
+// rows (written for micro-batch 0, added for the others; reduced into G
+// after the backward phase) and *fused is set; otherwise the caller sums the
+// bias gradient.
+hipError_t mm_wgrad(const Ctx& x, int role, int layer, int slot, int M, int N, int K,
+                    const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
+                    int64_t ldc, int beta, bool* fused) {
+  GemmParams g = wgrad_params(M, N, K, A, lda, B, ldb, C, ldc, beta);
   g.P = static_cast<float*>(x.at(x.p->splitk));
   const int parts = x.bf16 ? gemm_rowsum_parts(role, g, 1) : 0;
-  *fused = parts > 0 && size_t(parts) * M <= x.p->colpart_floats;
-  if (*fused) g.rowsum = static_cast<float*>(x.at(x.p->colpart));
-  hipError_t e = gemm(x.bf16, role, g, 1, x.s);
-  if (e != hipSuccess || !*fused) return e;
-  return sum_partials(g.rowsum, parts, M, M, bgrad, beta, x.s);
+  *fused = parts > 0 && parts == x.p->gp_parts[slot] && M == x.p->gp_cols[slot];
+  if (*fused) g.rowsum = static_cast<float*>(x.at(gpart_at(*x.p, layer, slot)));
+  return gemm(x.bf16, role, g, 1, x.s);
 }
 
 // Batched over (sequence b, head h) of one micro-batch.
@@ -315,7 +366,8 @@ gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int b
   void* dqkv = x.at(p.dqkv);
   float* dP = static_cast<float*>(x.at(p.scores));
   void* dS = x.at(p.ds);
-  float* lnpart = static_cast<float*>(x.at(p.lnpart));
+  float* ln1part = static_cast<float*>(x.at(gpart_at(p, l, GPS_LN1)));
+  float* ln2part = static_cast<float*>(x.at(gpart_at(p, l, GPS_LN2)));
 
   // FFN: y = x1 + g W2^T + b2,  g = gelu(u),  u = h2 W1^T + b1
   GP_RUN(x, GPIPE_ROLE_FFN2_DGRAD, mm(x, GPIPE_ROLE_FFN2_DGRAD, T, F, D, a0, D, x.wmat(l, GPIPE_W_2), F, du, F,
@@ -323,23 +375,21 @@ gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int b
   // (bias gradients: from the weight-gradient kernel where it sums them --
   // over the bf16 copy of the output gradient it reads -- else summed here)
   bool fused = false;
-  GP_RUN(x, GPIPE_ROLE_FFN2_WGRAD, mm_wgrad(x, GPIPE_ROLE_FFN2_WGRAD, D, F, T, a0, D, g, F, x.grad(l, GPIPE_W_2),
-              F, beta, x.grad(l, GPIPE_B_2), &fused));
+  GP_RUN(x, GPIPE_ROLE_FFN2_WGRAD, mm_wgrad(x, GPIPE_ROLE_FFN2_WGRAD, l, GPS_B2, D, F, T, a0, D, g, F,
+              x.grad(l, GPIPE_W_2), F, beta, &fused));
   if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r0, D, D, x.grad(l, GPIPE_B_2), beta));
   GP_RUN(x, GPIPE_ROLE_FFN1_DGRAD, mm(x, GPIPE_ROLE_FFN1_DGRAD, T, D, F, du, F, x.wmat(l, GPIPE_W_1), D, dm, D));
-  GP_RUN(x, GPIPE_ROLE_FFN1_WGRAD, mm_wgrad(x, GPIPE_ROLE_FFN1_WGRAD, F, D, T, du, F, h2, D, x.grad(l, GPIPE_W_1),
-              D, beta, x.grad(l, GPIPE_B_1), &fused));
+  GP_RUN(x, GPIPE_ROLE_FFN1_WGRAD, mm_wgrad(x, GPIPE_ROLE_FFN1_WGRAD, l, GPS_B1, F, D, T, du, F, h2, D,
+              x.grad(l, GPIPE_W_1), D, beta, &fused));
   if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, du, F, F, x.grad(l, GPIPE_B_1), beta));
   int nblk = 0;
-  GP_RUN(x, GPIPE_ROLE_LN2_BWD, layernorm_bwd(bf, dm, x1, st2, x.wf32(l, GPIPE_LN2_G), r0, r1, a1, lnpart, T, D, &nblk,
-                         x.s));
-  // gamma and beta are adjacent in the parameter layout: one pass over 2D columns
-  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(lnpart, nblk, 2 * D, 2 * D, x.grad(l, GPIPE_LN2_G), beta, x.s));
+  GP_RUN(x, GPIPE_ROLE_LN2_BWD, layernorm_bwd(bf, dm, x1, st2, x.wf32(l, GPIPE_LN2_G), r0, r1, a1, ln2part, T, D,
+                         beta, &nblk, x.s));
 
   // attention: x1 = x + ctx Wo^T + bo
   GP_RUN(x, GPIPE_ROLE_OUT_DGRAD, mm(x, GPIPE_ROLE_OUT_DGRAD, T, D, D, a1, D, x.wmat(l, GPIPE_W_O), D, dctx, D));
-  GP_RUN(x, GPIPE_ROLE_OUT_WGRAD, mm_wgrad(x, GPIPE_ROLE_OUT_WGRAD, D, D, T, a1, D, ctx, D, x.grad(l, GPIPE_W_O),
-              D, beta, x.grad(l, GPIPE_B_O), &fused));
+  GP_RUN(x, GPIPE_ROLE_OUT_WGRAD, mm_wgrad(x, GPIPE_ROLE_OUT_WGRAD, l, GPS_BO, D, D, T, a1, D, ctx, D,
+              x.grad(l, GPIPE_W_O), D, beta, &fused));
   if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r1, D, D, x.grad(l, GPIPE_B_O), beta));
   const int64_t sq = int64_t(S) * 3 * D;
   const int64_t sp = int64_t(H) * S * ldS;
@@ -370,13 +420,29 @@ gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int b
   // qkv = h1 Wqkv^T + bqkv,  h1 = LN1(x)
   GP_RUN(x, GPIPE_ROLE_QKV_DGRAD, mm(x, GPIPE_ROLE_QKV_DGRAD, T, D, 3 * D, dqkv, 3 * D, x.wmat(l, GPIPE_W_QKV), D,
               dm, D));
-  GP_RUN(x, GPIPE_ROLE_QKV_WGRAD, mm_wgrad(x, GPIPE_ROLE_QKV_WGRAD, 3 * D, D, T, dqkv, 3 * D, h1, D,
-              x.grad(l, GPIPE_W_QKV), D, beta, x.grad(l, GPIPE_B_QKV), &fused));
+  GP_RUN(x, GPIPE_ROLE_QKV_WGRAD, mm_wgrad(x, GPIPE_ROLE_QKV_WGRAD, l, GPS_BQKV, 3 * D, D, T, dqkv, 3 * D, h1,
+              D, x.grad(l, GPIPE_W_QKV), D, beta, &fused));
   if (!fused)
     GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, dqkv, 3 * D, 3 * D, x.grad(l, GPIPE_B_QKV), beta));
   GP_RUN(x, GPIPE_ROLE_LN1_BWD, layernorm_bwd(bf, dm, xin, st1, x.wf32(l, GPIPE_LN1_G), r1, r0, dx_out ? dx_out : a0,
-                         lnpart, T, D, &nblk, x.s));
-  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(lnpart, nblk, 2 * D, 2 * D, x.grad(l, GPIPE_LN1_G), beta, x.s));
+                         ln1part, T, D, beta, &nblk, x.s));
+  return GPIPE_OK;
+}
+
+// After the backward phase: reduce each layer's in-place partial sums (LN
+// gains and shifts -- adjacent in the parameter layout, so one pass over 2D
+// columns -- and the biases the weight-gradient kernels summed) into G.
+gpipe_status reduce_gparts(const Ctx& x) {
+  const Plan& p = *x.p;
+  const int grad_of[GPS_N] = {GPIPE_LN1_G, GPIPE_LN2_G, GPIPE_B_QKV, GPIPE_B_O, GPIPE_B_1, GPIPE_B_2};
+  for (int l = 0; l < x.c->L; ++l)
+    for (int k = 0; k < GPS_N; ++k) {
+      if (!p.gp_parts[k]) continue;
+      const int cols = p.gp_cols[k];
+      const float* part = static_cast<const float*>(x.at(gpart_at(p, l, k)));
+      GP_RUN(x, k <= GPS_LN2 ? GPIPE_ROLE_NORM_GRAD : GPIPE_ROLE_BIAS_GRAD,
+             sum_partials(part, p.gp_parts[k], cols, cols, x.grad(l, grad_of[k]), 0, x.s));
+    }
   return GPIPE_OK;
 }
 
@@ -572,6 +638,10 @@ gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, v
       gpipe_status st = layer_backward(cx, set, l, xin, m > 0 ? 1 : 0, dxo);
       if (st != GPIPE_OK) return st;
     }
+  }
+  {
+    gpipe_status st = reduce_gparts(cx);
+    if (st != GPIPE_OK) return st;
   }
   GP_RUN(cx, GPIPE_ROLE_LOSS_REDUCE, sum_partials(msepart, M * p.mse_nblk, 1, 1, loss_dev, 0, cx.s));
   return GPIPE_OK;

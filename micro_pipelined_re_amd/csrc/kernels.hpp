@@ -45,7 +45,8 @@ struct GemmParams {
   int kchunk;   // split-K: k extent of one split (set by gemm())
   int conv_h, conv_w, conv_c;  // image geometry of a LAY_CONV operand
   // Optional (weight-gradient roles, where gemm_rowsum_parts() > 0): partial
-  // sums of A over k, rowsum[t * M + m] for tile column t; summed over t they
+  // sums of A over k, rowsum[t * M + m] for tile column t, written (beta = 0)
+  // or added (beta = 1) like C; summed over t they
   // give the row sums (each tile column adds up its own share of the k-tiles).
   float* rowsum;
 };
@@ -81,10 +82,11 @@ hipError_t layernorm_fwd(bool bf16, const void* x, void* y, float* stats, const 
 
 // LayerNorm backward.  dh: f32 [rows, d] gradient w.r.t. the LN output; x: act input;
 // res_in: f32 residual gradient added to dx; writes dx_f32 (may alias res_in) and dx_act;
-// per-block partial sums of dgamma and dbeta into part[nblk][2][d]; returns nblk via *nblk.
+// per-block partial sums of dgamma and dbeta written (beta = 0) or added (beta = 1) to
+// part[nblk][2][d]; returns nblk via *nblk (at most 256 whatever the row count).
 hipError_t layernorm_bwd(bool bf16, const float* dh, const void* x, const float* stats,
                          const float* gamma, const float* res_in, float* dx_f32, void* dx_act,
-                         float* part, int rows, int d, int* nblk, hipStream_t s);
+                         float* part, int rows, int d, int beta, int* nblk, hipStream_t s);
 int layernorm_bwd_blocks(int rows, int d);
 
 // Softmax forward of scores (f32, already scaled) into P(act); rows of length n, row pitch ld,

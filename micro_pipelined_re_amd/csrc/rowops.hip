@@ -90,10 +90,13 @@ hipError_t layernorm_fwd(bool bf16, const void* x, void* y, float* stats, const 
 }
 
 // ------------------------------------------------------------ LayerNorm backward
-// A block of 256 threads takes kLnRows consecutive rows; thread owns chunks
-// tid, tid+256, ... of every row, so it also owns those columns' dgamma/dbeta
-// partial sums, which it writes once for the whole block.
+// A block of 256 threads takes chunks of kLnRows consecutive rows (chunk
+// blockIdx.x, then every gridDim.x-th); thread owns chunks tid, tid+256, ...
+// of every row, so it also owns those columns' dgamma/dbeta partial sums,
+// which it writes (beta = 0) or adds to the block's partial row (beta = 1)
+// once.  The grid is capped, so the partial rows do not grow with the rows.
 constexpr int kLnRows = 8;
+constexpr int kLnMaxBlocks = 256;
 
 template <typename T, int NVB>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ dh,
@@ -102,7 +105,8 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
                                                      const float* __restrict__ gamma,
                                                      const float* res_in, float* dx_f32,
                                                      T* __restrict__ dx_act,
-                                                     float* __restrict__ part, int rows, int d) {
+                                                     float* __restrict__ part, int rows, int d,
+                                                     int beta) {
   __shared__ float red[4];
   const int tid = threadIdx.x;
   const int nch = d >> 3;
@@ -111,9 +115,8 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
   for (int i = 0; i < NVB; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) pg[i][e] = pb[i][e] = 0.f;
-  const int r0 = blockIdx.x * kLnRows;
-  const int r1 = min(rows, r0 + kLnRows);
-  for (int row = r0; row < r1; ++row) {
+  for (int r0 = blockIdx.x * kLnRows; r0 < rows; r0 += gridDim.x * kLnRows)
+  for (int row = r0, r1 = min(rows, r0 + kLnRows); row < r1; ++row) {
     const float mu = stats[2 * row], rstd = stats[2 * row + 1];
     float xh[NVB][8], dxh[NVB][8];
     float sa = 0.f, sb = 0.f;
@@ -155,15 +158,27 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const float* __restrict__ d
   for (int i = 0; i < NVB; ++i) {
     const int c = tid + 256 * i;
     if (c < nch) {
+      if (beta) {
+        float og[8], ob[8];
+        load8<float>(pgo + c * 8, og);
+        load8<float>(pgo + d + c * 8, ob);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pg[i][e] += og[e];
+          pb[i][e] += ob[e];
+        }
+      }
       store8<float>(pgo + c * 8, pg[i]);
       store8<float>(pgo + d + c * 8, pb[i]);
     }
   }
 }
 
-// One wave per row, four rows per block (rows of up to 4096): the row's two
-// reductions are wave butterflies; the four rows' dgamma / dbeta partials are
-// added in row order through LDS and written once per block.
+// One wave per row, four rows per block at a time (rows of up to 4096): the
+// row's two reductions are wave butterflies.  Block b takes row groups b,
+// b + gridDim.x, ...; each wave sums its rows' dgamma / dbeta terms in
+// registers, the four waves' sums are added in wave order through LDS and
+// written (beta = 0) or added (beta = 1) to the block's partial row once.
 constexpr int kLnWaveRows = 4;
 
 template <typename T, int NV>
@@ -174,17 +189,16 @@ __global__ __launch_bounds__(256) void ln_bwd_wave_kernel(const float* __restric
                                                           const float* res_in, float* dx_f32,
                                                           T* __restrict__ dx_act,
                                                           float* __restrict__ part, int rows,
-                                                          int d) {
+                                                          int d, int beta) {
   extern __shared__ float lds[];  // [4][d]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int row = blockIdx.x * kLnWaveRows + w;
   const int nch = d >> 3;
   float pg[NV][8], pb[NV][8];
 #pragma unroll
   for (int i = 0; i < NV; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) pg[i][e] = pb[i][e] = 0.f;
-  if (row < rows) {
+  for (int row = blockIdx.x * kLnWaveRows + w; row < rows; row += gridDim.x * kLnWaveRows) {
     const float mu = stats[2 * row], rstd = stats[2 * row + 1];
     float xh[NV][8], dxh[NV][8];
     float sa = 0.f, sb = 0.f;
@@ -202,8 +216,8 @@ __global__ __launch_bounds__(256) void ln_bwd_wave_kernel(const float* __restric
           dxh[i][e] = gv[e] * gm[e];
           sa += dxh[i][e];
           sb += dxh[i][e] * xh[i][e];
-          pg[i][e] = gv[e] * xh[i][e];
-          pb[i][e] = gv[e];
+          pg[i][e] += gv[e] * xh[i][e];
+          pb[i][e] += gv[e];
         }
       }
     }
@@ -240,6 +254,11 @@ __global__ __launch_bounds__(256) void ln_bwd_wave_kernel(const float* __restric
 #pragma unroll
         for (int e = 0; e < 8; ++e) s[e] += v[e];
       }
+      if (beta) {
+        load8<float>(out + half * d + c * 8, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += v[e];
+      }
       store8<float>(out + half * d + c * 8, s);
     }
     __syncthreads();
@@ -248,38 +267,38 @@ __global__ __launch_bounds__(256) void ln_bwd_wave_kernel(const float* __restric
 
 int layernorm_bwd_blocks(int rows, int d) {
   const int per = (d / 8 <= 512) ? kLnWaveRows : kLnRows;
-  return (rows + per - 1) / per;
+  return std::min((rows + per - 1) / per, kLnMaxBlocks);
 }
 
 template <typename T>
 static hipError_t ln_bwd_t(const float* dh, const void* x, const float* stats, const float* gamma,
                            const float* res_in, float* dx_f32, void* dx_act, float* part,
-                           int rows, int d, hipStream_t s) {
+                           int rows, int d, int beta, hipStream_t s) {
   const int nch = d / 8;
   dim3 grid(layernorm_bwd_blocks(rows, d)), blk(256);
   const T* xp = static_cast<const T*>(x);
   T* op = static_cast<T*>(dx_act);
   const size_t sh = size_t(kLnWaveRows) * d * 4;
-#define GP_LNW(NV) hipLaunchKernelGGL((ln_bwd_wave_kernel<T, NV>), grid, blk, sh, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d)
+#define GP_LNW(NV) hipLaunchKernelGGL((ln_bwd_wave_kernel<T, NV>), grid, blk, sh, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d, beta)
   if (nch <= 64) GP_LNW(1);
   else if (nch <= 128) GP_LNW(2);
   else if (nch <= 256) GP_LNW(4);
   else if (nch <= 512) GP_LNW(8);
 #undef GP_LNW
-  else if (nch <= 256) hipLaunchKernelGGL((ln_bwd_kernel<T, 1>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d);
-  else if (nch <= 512) hipLaunchKernelGGL((ln_bwd_kernel<T, 2>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d);
-  else if (nch <= 1024) hipLaunchKernelGGL((ln_bwd_kernel<T, 4>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d);
+  else if (nch <= 256) hipLaunchKernelGGL((ln_bwd_kernel<T, 1>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d, beta);
+  else if (nch <= 512) hipLaunchKernelGGL((ln_bwd_kernel<T, 2>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d, beta);
+  else if (nch <= 1024) hipLaunchKernelGGL((ln_bwd_kernel<T, 4>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d, beta);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t layernorm_bwd(bool bf16, const float* dh, const void* x, const float* stats,
                          const float* gamma, const float* res_in, float* dx_f32, void* dx_act,
-                         float* part, int rows, int d, int* nblk, hipStream_t s) {
+                         float* part, int rows, int d, int beta, int* nblk, hipStream_t s) {
   *nblk = layernorm_bwd_blocks(rows, d);
   if (rows == 0) return hipSuccess;
-  return bf16 ? ln_bwd_t<bf16_t>(dh, x, stats, gamma, res_in, dx_f32, dx_act, part, rows, d, s)
-              : ln_bwd_t<float>(dh, x, stats, gamma, res_in, dx_f32, dx_act, part, rows, d, s);
+  return bf16 ? ln_bwd_t<bf16_t>(dh, x, stats, gamma, res_in, dx_f32, dx_act, part, rows, d, beta, s)
+              : ln_bwd_t<float>(dh, x, stats, gamma, res_in, dx_f32, dx_act, part, rows, d, beta, s);
 }
 
 // ------------------------------------------------------------ softmax
