@@ -2,7 +2,8 @@
 //
 // Forward, per (sequence, head) and block of 64 queries: stream the key/value
 // blocks through LDS, keep the running row maximum and row sum of the
-// softmax in registers, and accumulate the output; only the log-sum-exp of
+// softmax in registers, and accumulate the output (two wave groups, each
+// over half of the key blocks, combined at the end); only the log-sum-exp of
 // every query row is saved.  Backward recomputes the probabilities from it:
 // one kernel per key block accumulates dK and dV over the query blocks, one
 // per query block accumulates dQ over the key blocks, so every sum has a
@@ -67,36 +68,50 @@ __device__ __forceinline__ bf16x8_t frag_tr(const bf16_t* t, int rlo, int rhi, i
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// bf16x8 from 8 floats (round to nearest even)
+// bf16x8 from 8 floats, round to nearest even (v_cvt_pk_bf16_f32 per pair)
 __device__ __forceinline__ bf16x8_t pack8(const float* v) {
-  short8_t s;
+  typedef float float2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  bf16x8_t r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s[e] = short(f2bf(v[e]));
-  return __builtin_bit_cast(bf16x8_t, s);
+  for (int e = 0; e < 8; e += 2) {
+    const bf16x2v h = __builtin_convertvector((float2v{v[e], v[e + 1]}), bf16x2v);
+    r[e] = h[0];
+    r[e + 1] = h[1];
+  }
+  return r;
 }
 
-// A 64 x DH tile of a [rows][ld] bf16 matrix, staged through registers.
-// Rows >= nrows read as zeros.
+// 2^x without the library's range reduction (one v_exp_f32): the arguments
+// here are at most 0 and results below the fp32 normal range only scale
+// probabilities that are negligible next to the row's largest one (1).
+__device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A 64 x DH tile of a [rows][ld] bf16 matrix, staged through registers by
+// the 256 threads of one wave group (t = thread index inside the group).
+// Rows >= nrows read as zeros.  (Clamping the row instead, which removes the
+// branches, made the kernels 50% slower on gfx950: the compiler then waited
+// for each tile's loads right after issuing them.)
 template <int DH>
 struct TileLoad {
   static constexpr int CPR = DH / 8;                 // 16-byte chunks per row
   static constexpr int PER = kBlk * CPR / 256;       // per thread
   uint4 v[PER];
-  __device__ __forceinline__ void load(const bf16_t* base, int64_t ld, int r0, int nrows) {
+  __device__ __forceinline__ void load(const bf16_t* base, int64_t ld, int r0, int nrows, int t) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int cid = threadIdx.x + 256 * i;
+      const int cid = t + 256 * i;
       const int r = cid / CPR, c = cid % CPR;
       v[i] = make_uint4(0, 0, 0, 0);
       if (r0 + r < nrows) v[i] = *reinterpret_cast<const uint4*>(base + int64_t(r0 + r) * ld + c * 8);
     }
   }
-  __device__ __forceinline__ void store(bf16_t* t) const {
+  __device__ __forceinline__ void store(bf16_t* tl, int t) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int cid = threadIdx.x + 256 * i;
+      const int cid = t + 256 * i;
       const int r = cid / CPR, c = cid % CPR;
-      *reinterpret_cast<uint4*>(t + toff<DH>(r, c * 8)) = v[i];
+      *reinterpret_cast<uint4*>(tl + toff<DH>(r, c * 8)) = v[i];
     }
   }
 };
@@ -107,18 +122,42 @@ __device__ __forceinline__ bf16x8_t gfrag(const bf16_t* base, int64_t ld, int ro
   return *reinterpret_cast<const bf16x8_t*>(base + int64_t(row) * ld + c0);
 }
 
+// Every kernel below runs 8 waves in two groups of 4 that split the blocks
+// of its sequential loop: group 0 takes blocks 0, 2, 4, ... of the range,
+// group 1 blocks 1, 3, 5, ...  Each group keeps its own partial result in
+// registers; at the end group 1 hands its partial to group 0 through LDS
+// and group 0 combines the two (group 0's + group 1's, in that order).  With
+// one (sequence, head, 64-row block) per workgroup a single group would give
+// each SIMD one wave with every latency of its dependent chain exposed; two
+// groups double the waves per SIMD and halve the chain.  Both groups run the
+// same number of iterations (a group without a block in the last one only
+// joins the barrier), so every barrier is reached by all 512 threads.
+constexpr int kGroups = 2;
+
+// dynamic LDS of the kernels: [group][buffer][2 tiles] bf16, then (dK/dV
+// kernel) [group][buffer][2][64] float row statistics
+template <int DH>
+constexpr int attn_tile_elems() { return kBlk * DH; }
+template <int DH>
+constexpr int attn_smem_bytes() {
+  return kGroups * 2 * 2 * attn_tile_elems<DH>() * 2 + kGroups * 2 * 2 * kBlk * 4;
+}
+
+extern __shared__ __attribute__((aligned(16))) bf16_t attn_smem[];
+
 // ------------------------------------------------------------------ forward
 // grid (query blocks, B*H); qkv [B*S][3D], ctx [B*S][D], lse2 [B*H][S].
 template <int DH>
-__global__ __launch_bounds__(256) void flash_fwd_kernel(const bf16_t* __restrict__ qkv,
+__global__ __launch_bounds__(512) void flash_fwd_kernel(const bf16_t* __restrict__ qkv,
                                                         bf16_t* __restrict__ ctx,
                                                         float* __restrict__ lse2, int S, int H,
                                                         int D, int causal, float sl2) {
   constexpr int KS = DH / 32;   // k steps over the head dimension
   constexpr int DT = DH / 16;   // 16-column output tiles
-  __shared__ __attribute__((aligned(16))) bf16_t kt[2][kBlk * DH];
-  __shared__ __attribute__((aligned(16))) bf16_t vt[2][kBlk * DH];
+  constexpr int TE = attn_tile_elems<DH>();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, ln = lane & 15;
+  const int grp = w >> 2, wl = w & 3, gt = threadIdx.x & 255;
+  bf16_t* gbase = attn_smem + grp * 4 * TE;  // [buffer][K, V]
   const int nqb = (S + kBlk - 1) / kBlk;
   const int qb = nqb - 1 - int(blockIdx.x);  // longest causal rows first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -126,7 +165,7 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(const bf16_t* __restrict
   const bf16_t* Qg = qkv + int64_t(b) * S * ld + h * DH;
   const bf16_t* Kg = Qg + D;
   const bf16_t* Vg = Qg + 2 * D;
-  const int q = qb * kBlk + w * 16 + ln;  // this lane's query (column of S^T)
+  const int q = qb * kBlk + wl * 16 + ln;  // this lane's query (column of S^T)
   bf16x8_t qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qf[ks] = gfrag(Qg, ld, q, S, ks * 32 + 8 * g);
@@ -136,52 +175,75 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(const bf16_t* __restrict
   for (int i = 0; i < DT; ++i) o[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const int nkb = causal ? min(qb + 1, (S + kBlk - 1) / kBlk) : (S + kBlk - 1) / kBlk;
+  const int iters = (nkb + kGroups - 1) / kGroups;
   TileLoad<DH> lk, lv;
-  lk.load(Kg, ld, 0, S);
-  lv.load(Vg, ld, 0, S);
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    lk.store(kt[buf]);
-    lv.store(vt[buf]);
+  if (grp < nkb) {
+    lk.load(Kg, ld, grp * kBlk, S, gt);
+    lv.load(Vg, ld, grp * kBlk, S, gt);
+  }
+  for (int it = 0; it < iters; ++it) {
+    const int kb = kGroups * it + grp;
+    const bool have = kb < nkb;
+    bf16_t* kt = gbase + (it & 1) * 2 * TE;
+    bf16_t* vt = kt + TE;
+    if (have) {
+      lk.store(kt, gt);
+      lv.store(vt, gt);
+    }
     __syncthreads();
-    if (kb + 1 < nkb) {
-      lk.load(Kg, ld, (kb + 1) * kBlk, S);
-      lv.load(Vg, ld, (kb + 1) * kBlk, S);
+    if (kb + kGroups < nkb) {
+      lk.load(Kg, ld, (kb + kGroups) * kBlk, S, gt);
+      lv.load(Vg, ld, (kb + kGroups) * kBlk, S, gt);
     }
-    // S^T tile t: keys 16t + 4g + v, query q
+    if (!have) continue;
+    // S^T tile t: keys 16t + 4g + v, query q.  Every LDS read of the score
+    // product, and of the first 32 keys' V fragments, is issued before the
+    // first MFMA (otherwise each MFMA waits for its own read's round trip).
     floatx4_t st[4];
+    bf16x8_t kfr[4][KS], vfr[DT];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      st[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        st[t] = mfma(frag_row<DH>(kt[buf], t * 16 + ln, ks * 4 + g), qf[ks], st[t]);
-    }
+      for (int ks = 0; ks < KS; ++ks) kfr[t][ks] = frag_row<DH>(kt, t * 16 + ln, ks * 4 + g);
+#pragma unroll
+    for (int i = 0; i < DT; ++i) vfr[i] = frag_tr<DH>(vt, 0, 16, i * 16, lane);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) st[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) st[t] = mfma(kfr[t][ks], qf[ks], st[t]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * KS + 2 * DT, 0);  // the LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * KS, 0);           // then the MFMAs
     const int k0 = kb * kBlk;
     const bool full = (k0 + kBlk <= S) && (!causal || k0 + kBlk - 1 <= qb * kBlk);
+    if (!full)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int key = k0 + t * 16 + 4 * g + v;
+          if (key >= S || (causal && key > q)) st[t][v] = -INFINITY;
+        }
+    // the maximum of the raw scores times the (positive) scale is the
+    // maximum of the scaled scores
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float x = st[t][v] * sl2;
-        if (!full) {
-          const int key = k0 + t * 16 + 4 * g + v;
-          if (key >= S || (causal && key > q)) x = -INFINITY;
-        }
-        st[t][v] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, st[t][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
+    // every visited block holds an unmasked key of every row (its first key
+    // is below S and, causally, at most the row's query), so m_new is finite
+    const float m_new = fmaxf(m_run, mx * sl2);
+    const float alpha = exp2_raw(m_run - m_new);
     float ls = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float p = exp2f(st[t][v] - m_new);
+        const float p = exp2_raw(fmaf(st[t][v], sl2, -m_new));
         st[t][v] = p;
         ls += p;
       }
@@ -197,30 +259,62 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(const bf16_t* __restrict
     for (int i = 0; i < DT; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) o[i][v] *= av[v];
-    // O += P V over two 32-key halves
+    // O += P V over two 32-key halves (the second half's V fragments are
+    // read before the first half's MFMAs)
+    const float pv0[8] = {st[0][0], st[0][1], st[0][2], st[0][3], st[1][0], st[1][1], st[1][2], st[1][3]};
+    const float pv1[8] = {st[2][0], st[2][1], st[2][2], st[2][3], st[3][0], st[3][1], st[3][2], st[3][3]};
+    const bf16x8_t pa0 = pack8(pv0), pa1 = pack8(pv1);
+    bf16x8_t vfr1[DT];
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const float pv[8] = {st[2 * k2][0], st[2 * k2][1], st[2 * k2][2], st[2 * k2][3],
-                           st[2 * k2 + 1][0], st[2 * k2 + 1][1], st[2 * k2 + 1][2], st[2 * k2 + 1][3]};
-      const bf16x8_t pa = pack8(pv);
+    for (int i = 0; i < DT; ++i) vfr1[i] = frag_tr<DH>(vt, 32, 48, i * 16, lane);
 #pragma unroll
-      for (int i = 0; i < DT; ++i)
-        o[i] = mfma(pa, frag_tr<DH>(vt[buf], 32 * k2, 32 * k2 + 16, i * 16, lane), o[i]);
-    }
+    for (int i = 0; i < DT; ++i) o[i] = mfma(pa0, vfr[i], o[i]);
+#pragma unroll
+    for (int i = 0; i < DT; ++i) o[i] = mfma(pa1, vfr1[i], o[i]);
   }
-  // normalise and store: lane holds rows (queries) 4g+v, column i*16 + ln
-  float lv4[4];
+  // combine the groups: per wave slot [DT*4][64] group 1's output, then
+  // m[group][16], l[group][16] of the wave's 16 queries
+  __syncthreads();
+  float* slot = reinterpret_cast<float*>(attn_smem) + wl * (DT * 256 + 64);
+  float* stat = slot + DT * 256;
+  if (grp == 1)
 #pragma unroll
-  for (int v = 0; v < 4; ++v) lv4[v] = 1.0f / __shfl(l_run, 4 * g + v, 64);
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) slot[(i * 4 + v) * 64 + lane] = o[i][v];
+  if (g == 0) {
+    stat[grp * 16 + ln] = m_run;
+    stat[32 + grp * 16 + ln] = l_run;
+  }
+  __syncthreads();
+  if (grp != 0) return;
+  // rows (queries) 4g+v: the weights of the two partial outputs
+  float f0[4], f1[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int r = 4 * g + v;
+    const float a = stat[r], c = stat[16 + r];
+    const float mm = fmaxf(a, c);
+    const float e0 = exp2f(a - mm), e1 = exp2f(c - mm);
+    const float inv = 1.0f / (stat[32 + r] * e0 + stat[48 + r] * e1);
+    f0[v] = e0 * inv;
+    f1[v] = e1 * inv;
+  }
   bf16_t* Cg = ctx + int64_t(b) * S * D + h * DH;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int qr = qb * kBlk + w * 16 + 4 * g + v;
+    const int qr = qb * kBlk + wl * 16 + 4 * g + v;
     if (qr < S)
 #pragma unroll
-      for (int i = 0; i < DT; ++i) Cg[int64_t(qr) * D + i * 16 + ln] = f2bf(o[i][v] * lv4[v]);
+      for (int i = 0; i < DT; ++i)
+        Cg[int64_t(qr) * D + i * 16 + ln] =
+            f2bf(o[i][v] * f0[v] + slot[(i * 4 + v) * 64 + lane] * f1[v]);
   }
-  if (g == 0 && q < S) lse2[int64_t(bh) * S + q] = m_run + log2f(l_run);
+  if (g == 0 && q < S) {
+    const float a = stat[ln], c = stat[16 + ln];
+    const float mm = fmaxf(a, c);
+    lse2[int64_t(bh) * S + q] = mm + log2f(stat[32 + ln] * exp2f(a - mm) + stat[48 + ln] * exp2f(c - mm));
+  }
 }
 
 // ------------------------------------------------------------------ backward
@@ -248,18 +342,20 @@ __global__ __launch_bounds__(256) void flash_delta_kernel(const bf16_t* __restri
   delta[(int64_t(b) * H + h) * S + s] = acc;
 }
 
-// dK, dV for one key block: grid (key blocks, B*H)
+// dK, dV for one key block: grid (key blocks, B*H); the groups split the
+// query blocks.
 template <int DH>
-__global__ __launch_bounds__(256) void flash_dkdv_kernel(
+__global__ __launch_bounds__(512) void flash_dkdv_kernel(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dctx,
     const float* __restrict__ lse2, const float* __restrict__ delta, bf16_t* __restrict__ dqkv,
     int S, int H, int D, int causal, float sl2, float scale) {
   constexpr int KS = DH / 32;
   constexpr int DT = DH / 16;
-  __shared__ __attribute__((aligned(16))) bf16_t qt[2][kBlk * DH];
-  __shared__ __attribute__((aligned(16))) bf16_t ot[2][kBlk * DH];  // dO
-  __shared__ float ls_s[2][kBlk], dl_s[2][kBlk];
+  constexpr int TE = attn_tile_elems<DH>();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, ln = lane & 15;
+  const int grp = w >> 2, wl = w & 3, gt = threadIdx.x & 255;
+  bf16_t* gbase = attn_smem + grp * 4 * TE;  // [buffer][Q, dO]
+  float* sbase = reinterpret_cast<float*>(attn_smem + kGroups * 4 * TE) + grp * 4 * kBlk;  // [buffer][lse, delta][64]
   const int nb = (S + kBlk - 1) / kBlk;
   const int kbk = int(blockIdx.x);
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -270,7 +366,7 @@ __global__ __launch_bounds__(256) void flash_dkdv_kernel(
   const bf16_t* Og = dctx + int64_t(b) * S * D + h * DH;
   const float* Lg = lse2 + int64_t(bh) * S;
   const float* Dg = delta + int64_t(bh) * S;
-  const int key = kbk * kBlk + w * 16 + ln;  // this lane's key (column of S)
+  const int key = kbk * kBlk + wl * 16 + ln;  // this lane's key (column of S)
   bf16x8_t kf[KS], vf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -281,28 +377,39 @@ __global__ __launch_bounds__(256) void flash_dkdv_kernel(
 #pragma unroll
   for (int i = 0; i < DT; ++i) dk[i] = dv[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   const int q_first = causal ? kbk : 0;
+  const int nqb = nb - q_first;
+  const int iters = (nqb + kGroups - 1) / kGroups;
   TileLoad<DH> lq, lo;
   float lsv = 0.f, dlv = 0.f;
   auto load_blk = [&](int qb) {
-    lq.load(Qg, ld, qb * kBlk, S);
-    lo.load(Og, D, qb * kBlk, S);
-    if (threadIdx.x < kBlk) {
-      const int qq = qb * kBlk + threadIdx.x;
+    lq.load(Qg, ld, qb * kBlk, S, gt);
+    lo.load(Og, D, qb * kBlk, S, gt);
+    if (gt < kBlk) {
+      const int qq = qb * kBlk + gt;
       lsv = qq < S ? Lg[qq] : INFINITY;
       dlv = qq < S ? Dg[qq] : 0.f;
     }
   };
-  load_blk(q_first);
-  for (int qb = q_first; qb < nb; ++qb) {
-    const int buf = (qb - q_first) & 1;
-    lq.store(qt[buf]);
-    lo.store(ot[buf]);
-    if (threadIdx.x < kBlk) {
-      ls_s[buf][threadIdx.x] = lsv;
-      dl_s[buf][threadIdx.x] = dlv;
+  if (grp < nqb) load_blk(q_first + grp);
+  for (int it = 0; it < iters; ++it) {
+    const int qi = kGroups * it + grp;  // index into this key block's query blocks
+    const bool have = qi < nqb;
+    const int qb = q_first + qi;
+    bf16_t* qt = gbase + (it & 1) * 2 * TE;
+    bf16_t* ot = qt + TE;
+    float* ls_s = sbase + (it & 1) * 2 * kBlk;
+    float* dl_s = ls_s + kBlk;
+    if (have) {
+      lq.store(qt, gt);
+      lo.store(ot, gt);
+      if (gt < kBlk) {
+        ls_s[gt] = lsv;
+        dl_s[gt] = dlv;
+      }
     }
     __syncthreads();
-    if (qb + 1 < nb) load_blk(qb + 1);
+    if (qi + kGroups < nqb) load_blk(qb + kGroups);
+    if (!have) continue;
     // S and dP tiles t: rows (queries) 16t + 4g + v, column (key) `key`
     floatx4_t sp[4], dp[4];
 #pragma unroll
@@ -310,8 +417,8 @@ __global__ __launch_bounds__(256) void flash_dkdv_kernel(
       sp[t] = dp[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        sp[t] = mfma(frag_row<DH>(qt[buf], t * 16 + ln, ks * 4 + g), kf[ks], sp[t]);
-        dp[t] = mfma(frag_row<DH>(ot[buf], t * 16 + ln, ks * 4 + g), vf[ks], dp[t]);
+        sp[t] = mfma(frag_row<DH>(qt, t * 16 + ln, ks * 4 + g), kf[ks], sp[t]);
+        dp[t] = mfma(frag_row<DH>(ot, t * 16 + ln, ks * 4 + g), vf[ks], dp[t]);
       }
     }
     const int q0 = qb * kBlk;
@@ -321,10 +428,10 @@ __global__ __launch_bounds__(256) void flash_dkdv_kernel(
       for (int v = 0; v < 4; ++v) {
         const int r = t * 16 + 4 * g + v;
         const int qq = q0 + r;
-        float p = exp2f(sp[t][v] * sl2 - ls_s[buf][r]);
+        float p = exp2_raw(fmaf(sp[t][v], sl2, -ls_s[r]));
         if (key >= S || (causal && key > qq)) p = 0.f;
         sp[t][v] = p;                                   // P
-        dp[t][v] = p * (dp[t][v] - dl_s[buf][r]);       // dS (unscaled)
+        dp[t][v] = p * (dp[t][v] - dl_s[r]);            // dS (unscaled)
       }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
@@ -335,37 +442,53 @@ __global__ __launch_bounds__(256) void flash_dkdv_kernel(
       const bf16x8_t pa = pack8(pv), sa = pack8(sv);
 #pragma unroll
       for (int i = 0; i < DT; ++i) {
-        dv[i] = mfma(pa, frag_tr<DH>(ot[buf], 32 * k2, 32 * k2 + 16, i * 16, lane), dv[i]);
-        dk[i] = mfma(sa, frag_tr<DH>(qt[buf], 32 * k2, 32 * k2 + 16, i * 16, lane), dk[i]);
+        dv[i] = mfma(pa, frag_tr<DH>(ot, 32 * k2, 32 * k2 + 16, i * 16, lane), dv[i]);
+        dk[i] = mfma(sa, frag_tr<DH>(qt, 32 * k2, 32 * k2 + 16, i * 16, lane), dk[i]);
       }
     }
   }
+  // combine: group 1's dK, dV through LDS (per wave [2][DT*4][64]), added to group 0's
+  __syncthreads();
+  float* slot = reinterpret_cast<float*>(attn_smem) + wl * (2 * DT * 256);
+  if (grp == 1)
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        slot[(i * 4 + v) * 64 + lane] = dk[i][v];
+        slot[DT * 256 + (i * 4 + v) * 64 + lane] = dv[i][v];
+      }
+  __syncthreads();
+  if (grp != 0) return;
   // lane holds rows (keys) 4g+v of this wave, column i*16 + ln
   bf16_t* dKg = dqkv + int64_t(b) * S * ld + D + h * DH;
   bf16_t* dVg = dKg + D;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int kr = kbk * kBlk + w * 16 + 4 * g + v;
+    const int kr = kbk * kBlk + wl * 16 + 4 * g + v;
     if (kr < S)
 #pragma unroll
       for (int i = 0; i < DT; ++i) {
-        dKg[int64_t(kr) * ld + i * 16 + ln] = f2bf(dk[i][v] * scale);
-        dVg[int64_t(kr) * ld + i * 16 + ln] = f2bf(dv[i][v]);
+        const float k1 = slot[(i * 4 + v) * 64 + lane], v1 = slot[DT * 256 + (i * 4 + v) * 64 + lane];
+        dKg[int64_t(kr) * ld + i * 16 + ln] = f2bf((dk[i][v] + k1) * scale);
+        dVg[int64_t(kr) * ld + i * 16 + ln] = f2bf(dv[i][v] + v1);
       }
   }
 }
 
-// dQ for one query block: grid (query blocks, B*H)
+// dQ for one query block: grid (query blocks, B*H); the groups split the key
+// blocks.
 template <int DH>
-__global__ __launch_bounds__(256) void flash_dq_kernel(
+__global__ __launch_bounds__(512) void flash_dq_kernel(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dctx,
     const float* __restrict__ lse2, const float* __restrict__ delta, bf16_t* __restrict__ dqkv,
     int S, int H, int D, int causal, float sl2, float scale) {
   constexpr int KS = DH / 32;
   constexpr int DT = DH / 16;
-  __shared__ __attribute__((aligned(16))) bf16_t kt[2][kBlk * DH];
-  __shared__ __attribute__((aligned(16))) bf16_t vt[2][kBlk * DH];
+  constexpr int TE = attn_tile_elems<DH>();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, ln = lane & 15;
+  const int grp = w >> 2, wl = w & 3, gt = threadIdx.x & 255;
+  bf16_t* gbase = attn_smem + grp * 4 * TE;  // [buffer][K, V]
   const int nb = (S + kBlk - 1) / kBlk;
   const int qb = nb - 1 - int(blockIdx.x);
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -374,7 +497,7 @@ __global__ __launch_bounds__(256) void flash_dq_kernel(
   const bf16_t* Kg = Qg + D;
   const bf16_t* Vg = Qg + 2 * D;
   const bf16_t* Og = dctx + int64_t(b) * S * D + h * DH;
-  const int q = qb * kBlk + w * 16 + ln;  // this lane's query (column of S^T)
+  const int q = qb * kBlk + wl * 16 + ln;  // this lane's query (column of S^T)
   bf16x8_t qf[KS], of[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -387,18 +510,27 @@ __global__ __launch_bounds__(256) void flash_dq_kernel(
 #pragma unroll
   for (int i = 0; i < DT; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   const int nkb = causal ? min(qb + 1, nb) : nb;
+  const int iters = (nkb + kGroups - 1) / kGroups;
   TileLoad<DH> lk, lv;
-  lk.load(Kg, ld, 0, S);
-  lv.load(Vg, ld, 0, S);
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    lk.store(kt[buf]);
-    lv.store(vt[buf]);
-    __syncthreads();
-    if (kb + 1 < nkb) {
-      lk.load(Kg, ld, (kb + 1) * kBlk, S);
-      lv.load(Vg, ld, (kb + 1) * kBlk, S);
+  if (grp < nkb) {
+    lk.load(Kg, ld, grp * kBlk, S, gt);
+    lv.load(Vg, ld, grp * kBlk, S, gt);
+  }
+  for (int it = 0; it < iters; ++it) {
+    const int kb = kGroups * it + grp;
+    const bool have = kb < nkb;
+    bf16_t* kt = gbase + (it & 1) * 2 * TE;
+    bf16_t* vt = kt + TE;
+    if (have) {
+      lk.store(kt, gt);
+      lv.store(vt, gt);
     }
+    __syncthreads();
+    if (kb + kGroups < nkb) {
+      lk.load(Kg, ld, (kb + kGroups) * kBlk, S, gt);
+      lv.load(Vg, ld, (kb + kGroups) * kBlk, S, gt);
+    }
+    if (!have) continue;
     // S^T and dP^T tiles t: rows (keys) 16t + 4g + v, column (query) q
     floatx4_t st[4], dpt[4];
 #pragma unroll
@@ -406,8 +538,8 @@ __global__ __launch_bounds__(256) void flash_dq_kernel(
       st[t] = dpt[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        st[t] = mfma(frag_row<DH>(kt[buf], t * 16 + ln, ks * 4 + g), qf[ks], st[t]);
-        dpt[t] = mfma(frag_row<DH>(vt[buf], t * 16 + ln, ks * 4 + g), of[ks], dpt[t]);
+        st[t] = mfma(frag_row<DH>(kt, t * 16 + ln, ks * 4 + g), qf[ks], st[t]);
+        dpt[t] = mfma(frag_row<DH>(vt, t * 16 + ln, ks * 4 + g), of[ks], dpt[t]);
       }
     }
     const int k0 = kb * kBlk;
@@ -416,7 +548,7 @@ __global__ __launch_bounds__(256) void flash_dq_kernel(
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int key = k0 + t * 16 + 4 * g + v;
-        float p = exp2f(st[t][v] * sl2 - lq);
+        float p = exp2_raw(fmaf(st[t][v], sl2, -lq));
         if (key >= S || (causal && key > q)) p = 0.f;
         st[t][v] = p * (dpt[t][v] - dq_);   // dS^T (unscaled)
       }
@@ -427,17 +559,47 @@ __global__ __launch_bounds__(256) void flash_dq_kernel(
       const bf16x8_t sa = pack8(sv);
 #pragma unroll
       for (int i = 0; i < DT; ++i)
-        acc[i] = mfma(sa, frag_tr<DH>(kt[buf], 32 * k2, 32 * k2 + 16, i * 16, lane), acc[i]);
+        acc[i] = mfma(sa, frag_tr<DH>(kt, 32 * k2, 32 * k2 + 16, i * 16, lane), acc[i]);
     }
   }
+  // combine: group 1's dQ through LDS (per wave [DT*4][64]), added to group 0's
+  __syncthreads();
+  float* slot = reinterpret_cast<float*>(attn_smem) + wl * (DT * 256);
+  if (grp == 1)
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) slot[(i * 4 + v) * 64 + lane] = acc[i][v];
+  __syncthreads();
+  if (grp != 0) return;
   bf16_t* dQg = dqkv + int64_t(b) * S * ld + h * DH;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int qr = qb * kBlk + w * 16 + 4 * g + v;
+    const int qr = qb * kBlk + wl * 16 + 4 * g + v;
     if (qr < S)
 #pragma unroll
-      for (int i = 0; i < DT; ++i) dQg[int64_t(qr) * ld + i * 16 + ln] = f2bf(acc[i][v] * scale);
+      for (int i = 0; i < DT; ++i)
+        dQg[int64_t(qr) * ld + i * 16 + ln] = f2bf((acc[i][v] + slot[(i * 4 + v) * 64 + lane]) * scale);
   }
+}
+
+// Sets the dynamic-LDS limit of a kernel once.
+template <class K>
+hipError_t allow_smem(K kernel, int bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <int DH>
+hipError_t attn_attrs() {
+  static const hipError_t e = [] {
+    constexpr int sm = attn_smem_bytes<DH>();
+    hipError_t r = allow_smem(flash_fwd_kernel<DH>, sm);
+    if (r == hipSuccess) r = allow_smem(flash_dkdv_kernel<DH>, sm);
+    if (r == hipSuccess) r = allow_smem(flash_dq_kernel<DH>, sm);
+    return r;
+  }();
+  return e;
 }
 
 }  // namespace
@@ -452,12 +614,15 @@ hipError_t flash_fwd(const void* qkv, void* ctx, float* lse2, int B, int H, int 
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
   const bf16_t* q = static_cast<const bf16_t*>(qkv);
   bf16_t* c = static_cast<bf16_t*>(ctx);
-  if (dh == 128)
-    hipLaunchKernelGGL(flash_fwd_kernel<128>, grid, dim3(256), 0, s, q, c, lse2, S, H, D, causal, sl2);
-  else if (dh == 64)
-    hipLaunchKernelGGL(flash_fwd_kernel<64>, grid, dim3(256), 0, s, q, c, lse2, S, H, D, causal, sl2);
-  else
+  if (dh == 128) {
+    if (hipError_t e = attn_attrs<128>(); e != hipSuccess) return e;
+    hipLaunchKernelGGL(flash_fwd_kernel<128>, grid, dim3(512), attn_smem_bytes<128>(), s, q, c, lse2, S, H, D, causal, sl2);
+  } else if (dh == 64) {
+    if (hipError_t e = attn_attrs<64>(); e != hipSuccess) return e;
+    hipLaunchKernelGGL(flash_fwd_kernel<64>, grid, dim3(512), attn_smem_bytes<64>(), s, q, c, lse2, S, H, D, causal, sl2);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -482,20 +647,25 @@ hipError_t flash_bwd(const void* qkv, const void* ctx, const void* dctx, const f
     else
       hipLaunchKernelGGL(flash_delta_kernel<64>, dim3((rows + 255) / 256), dim3(256), 0, s, dO, o,
                          delta, S, H, D, rows);
-  } else if (stage == 1) {
-    if (dh == 128)
-      hipLaunchKernelGGL(flash_dkdv_kernel<128>, grid, dim3(256), 0, s, q, dO, lse2, delta, dq, S, H,
-                         D, causal, sl2, scale);
-    else
-      hipLaunchKernelGGL(flash_dkdv_kernel<64>, grid, dim3(256), 0, s, q, dO, lse2, delta, dq, S, H,
-                         D, causal, sl2, scale);
   } else {
-    if (dh == 128)
-      hipLaunchKernelGGL(flash_dq_kernel<128>, grid, dim3(256), 0, s, q, dO, lse2, delta, dq, S, H, D,
-                         causal, sl2, scale);
-    else
-      hipLaunchKernelGGL(flash_dq_kernel<64>, grid, dim3(256), 0, s, q, dO, lse2, delta, dq, S, H, D,
-                         causal, sl2, scale);
+    hipError_t e = dh == 128 ? attn_attrs<128>() : attn_attrs<64>();
+    if (e != hipSuccess) return e;
+    const int sm = dh == 128 ? attn_smem_bytes<128>() : attn_smem_bytes<64>();
+    if (stage == 1) {
+      if (dh == 128)
+        hipLaunchKernelGGL(flash_dkdv_kernel<128>, grid, dim3(512), sm, s, q, dO, lse2, delta, dq, S,
+                           H, D, causal, sl2, scale);
+      else
+        hipLaunchKernelGGL(flash_dkdv_kernel<64>, grid, dim3(512), sm, s, q, dO, lse2, delta, dq, S,
+                           H, D, causal, sl2, scale);
+    } else {
+      if (dh == 128)
+        hipLaunchKernelGGL(flash_dq_kernel<128>, grid, dim3(512), sm, s, q, dO, lse2, delta, dq, S, H,
+                           D, causal, sl2, scale);
+      else
+        hipLaunchKernelGGL(flash_dq_kernel<64>, grid, dim3(512), sm, s, q, dO, lse2, delta, dq, S, H,
+                           D, causal, sl2, scale);
+    }
   }
   return hipGetLastError();
 }
