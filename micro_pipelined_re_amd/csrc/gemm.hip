@@ -73,10 +73,14 @@ constexpr int kCUs = 256;
 // operands.  The linear layers' products (forward, input gradient, weight
 // gradient) take the specialised-wave kernel: 256 x 128 tiles (128 x 256
 // when both operands are k-contiguous and the output is wider than tall)
-// when the output has at least 192 of them, else 128 x 128 tiles, split in
-// two for k >= 4096 (a 1024 x 2048 output: 18 us unsplit at k = 2048 against
-// 28 us for 256 x 128 tiles split in two, 45 us split in two at k = 8192
-// against 48 us split in four).  Against 128 x 128 tiles with two workgroups
+// when the output has at least 192 of them; else, outside the weight
+// gradients and for k < 4096, 128 x 64 tiles when 128 x 128 ones would
+// number at most half the CUs and 128 x 64 ones at least 192 (a 1024 x 2048
+// output at k = 2048, inside the cell's step: 21.0 us against 24.6 us for
+// 128 x 128 tiles; at k = 8192 the narrow tiles re-read the operand that
+// the step brings in cold twice as often and took 60 us against 51 us for
+// 128 x 128 tiles split in two); else 128 x 128 tiles, split in two for
+// k >= 4096.  Against 128 x 128 tiles with two workgroups
 // per CU the specialised kernel ran 5-37% faster on every role of the
 // 2048-wide layer.  Weight gradients never split (their fp32 partials would
 // double the accumulator traffic).  The
@@ -111,6 +115,13 @@ GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch) {
       return p;
     }
     const long t128 = long((M + 127) / 128) * ((N + 127) / 128);
+    const long t64 = long((M + 127) / 128) * ((N + 63) / 64);
+    if (!is_wgrad(role) && K < 4096 && t128 <= kCUs / 2 && t64 >= 192) {
+      // 128 x 128 tiles would leave half the CUs idle: 128 x 64 tiles fill
+      // the chip (without split-K partials)
+      p.cfg = CFG_128x64_SPEC;
+      return p;
+    }
     if (t128 >= 64) {
       // fewer big tiles than 3/4 of the CUs: 128 x 128 tiles, and for deep k
       // two splits (the partial sums cost less than the idle CUs)
@@ -144,7 +155,8 @@ hipError_t gemm(bool bf16, int role, const GemmParams& g0, int batch, hipStream_
 
 namespace {
 bool spec_cfg(int cfg) {
-  return cfg == CFG_256x128_K64 || cfg == CFG_128x256_K64 || cfg == CFG_128x128_SPEC;
+  return cfg == CFG_256x128_K64 || cfg == CFG_128x256_K64 || cfg == CFG_128x128_SPEC ||
+         cfg == CFG_128x64_SPEC;
 }
 }  // namespace
 
