@@ -32,6 +32,13 @@ struct gpipe_cell {
   float* grad;
   float* ms;
   bool bound;
+  // Transformer cells: the second stream of the backward phase (the weight
+  // gradients) and the ring of events ordering it against the caller's
+  // stream; created at the first step, on the device current then.
+  hipStream_t aux = nullptr;
+  int aux_device = -1;
+  std::vector<hipEvent_t> sync_events;
+  size_t sync_next = 0;
   // event timing of selected kernel roles (gpipe_cell_profile)
   unsigned long long prof_mask = 0;
   std::vector<hipEvent_t> prof_events;  // pool, pairs (start, end), reused

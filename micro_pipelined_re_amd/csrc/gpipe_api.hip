@@ -195,6 +195,57 @@ struct Ctx {
   }
 };
 
+// Ordering of the backward phase's two streams.  The weight gradients do not
+// feed the input-gradient chain, so they run on the cell's second stream
+// (s2) and overlap the chain on the caller's stream (s1): each is enqueued
+// after a fork (s2 waits for everything s1 has enqueued: its operands
+// exist), and s1 joins (waits for the event recorded after a weight
+// gradient) before it overwrites a buffer that weight gradient reads.  s2
+// runs the weight gradients in issue order, so every gradient still sums the
+// micro-batches in order 0 .. M-1.
+struct Streams {
+  gpipe_cell* c;
+  hipStream_t s1, s2;
+  hipEvent_t next() { return c->sync_events[c->sync_next++ % c->sync_events.size()]; }
+  // s2 waits for the work enqueued so far on s1
+  bool fork() {
+    const hipEvent_t e = next();
+    return hipEventRecord(e, s1) == hipSuccess && hipStreamWaitEvent(s2, e, 0) == hipSuccess;
+  }
+  // event recorded on s2 after the work enqueued so far on it
+  bool mark(hipEvent_t* out) {
+    *out = next();
+    return hipEventRecord(*out, s2) == hipSuccess;
+  }
+  // s1 waits for an event of s2 (nullptr: nothing to wait for).  A ring
+  // event recorded again since only makes the wait longer, never shorter.
+  bool join(hipEvent_t e) { return !e || hipStreamWaitEvent(s1, e, 0) == hipSuccess; }
+  bool join_all() {
+    hipEvent_t e;
+    return mark(&e) && join(e);
+  }
+};
+
+// Events of s2 after the weight gradients of one layer's backward.
+struct WgradDone {
+  hipEvent_t ffn2 = nullptr, ffn1 = nullptr, out = nullptr, qkv = nullptr;
+};
+
+// Creates the second stream and the event ring at the first step.
+gpipe_status ensure_streams(gpipe_cell* c) {
+  int dev = -1;
+  GP_CHECK(hipGetDevice(&dev));
+  if (c->aux) return dev == c->aux_device ? GPIPE_OK : GPIPE_ERR_STATE;
+  GP_CHECK(hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking));
+  c->aux_device = dev;
+  for (int i = 0; i < 64; ++i) {
+    hipEvent_t e;
+    GP_CHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    c->sync_events.push_back(e);
+  }
+  return GPIPE_OK;
+}
+
 GemmParams gp0() {
   GemmParams g;
   memset(&g, 0, sizeof(g));
@@ -339,7 +390,10 @@ gpipe_status cell_forward(const Ctx& x, int set, const void* xin, void* yout) {
 // Backward of layer l.  On entry r0 (f32) / a0 (act) hold the gradient w.r.t.
 // the layer output; on exit they hold the gradient w.r.t. its input (a0, or
 // dx_out when given, receives the act copy).
-gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int beta, void* dx_out) {
+gpipe_status layer_backward(const Ctx& x, Streams& ss, const WgradDone& above, WgradDone* mine,
+                            int set, int l, const void* xin, int beta, void* dx_out) {
+  Ctx w = x;  // the weight gradients' context: the second stream
+  w.s = ss.s2;
   const gpipe_cell* c = x.c;
   const Plan& p = *x.p;
   const int T = p.T, D = c->D, F = c->F, S = c->S, H = c->H, dh = D / H;
@@ -370,26 +424,34 @@ gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int b
   float* ln2part = static_cast<float*>(x.at(gpart_at(p, l, GPS_LN2)));
 
   // FFN: y = x1 + g W2^T + b2,  g = gelu(u),  u = h2 W1^T + b1
-  GP_RUN(x, GPIPE_ROLE_FFN2_DGRAD, mm(x, GPIPE_ROLE_FFN2_DGRAD, T, F, D, a0, D, x.wmat(l, GPIPE_W_2), F, du, F,
-              nullptr, nullptr, 0, u, F));
   // (bias gradients: from the weight-gradient kernel where it sums them --
   // over the bf16 copy of the output gradient it reads -- else summed here)
   bool fused = false;
-  GP_RUN(x, GPIPE_ROLE_FFN2_WGRAD, mm_wgrad(x, GPIPE_ROLE_FFN2_WGRAD, l, GPS_B2, D, F, T, a0, D, g, F,
+  if (!ss.fork()) return GPIPE_ERR_DEVICE;  // a0 (and g) exist
+  GP_RUN(w, GPIPE_ROLE_FFN2_WGRAD, mm_wgrad(w, GPIPE_ROLE_FFN2_WGRAD, l, GPS_B2, D, F, T, a0, D, g, F,
               x.grad(l, GPIPE_W_2), F, beta, &fused));
+  if (!ss.mark(&mine->ffn2)) return GPIPE_ERR_DEVICE;
   if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r0, D, D, x.grad(l, GPIPE_B_2), beta));
-  GP_RUN(x, GPIPE_ROLE_FFN1_DGRAD, mm(x, GPIPE_ROLE_FFN1_DGRAD, T, D, F, du, F, x.wmat(l, GPIPE_W_1), D, dm, D));
-  GP_RUN(x, GPIPE_ROLE_FFN1_WGRAD, mm_wgrad(x, GPIPE_ROLE_FFN1_WGRAD, l, GPS_B1, F, D, T, du, F, h2, D,
+  if (!ss.join(above.ffn1)) return GPIPE_ERR_DEVICE;  // the layer above's FFN1 weight gradient read du
+  GP_RUN(x, GPIPE_ROLE_FFN2_DGRAD, mm(x, GPIPE_ROLE_FFN2_DGRAD, T, F, D, a0, D, x.wmat(l, GPIPE_W_2), F, du, F,
+              nullptr, nullptr, 0, u, F));
+  if (!ss.fork()) return GPIPE_ERR_DEVICE;  // du exists
+  GP_RUN(w, GPIPE_ROLE_FFN1_WGRAD, mm_wgrad(w, GPIPE_ROLE_FFN1_WGRAD, l, GPS_B1, F, D, T, du, F, h2, D,
               x.grad(l, GPIPE_W_1), D, beta, &fused));
+  if (!ss.mark(&mine->ffn1)) return GPIPE_ERR_DEVICE;
+  GP_RUN(x, GPIPE_ROLE_FFN1_DGRAD, mm(x, GPIPE_ROLE_FFN1_DGRAD, T, D, F, du, F, x.wmat(l, GPIPE_W_1), D, dm, D));
   if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, du, F, F, x.grad(l, GPIPE_B_1), beta));
   int nblk = 0;
+  if (!ss.join(above.out)) return GPIPE_ERR_DEVICE;  // the layer above's out-projection weight gradient read a1
   GP_RUN(x, GPIPE_ROLE_LN2_BWD, layernorm_bwd(bf, dm, x1, st2, x.wf32(l, GPIPE_LN2_G), r0, r1, a1, ln2part, T, D,
                          beta, &nblk, x.s));
 
   // attention: x1 = x + ctx Wo^T + bo
-  GP_RUN(x, GPIPE_ROLE_OUT_DGRAD, mm(x, GPIPE_ROLE_OUT_DGRAD, T, D, D, a1, D, x.wmat(l, GPIPE_W_O), D, dctx, D));
-  GP_RUN(x, GPIPE_ROLE_OUT_WGRAD, mm_wgrad(x, GPIPE_ROLE_OUT_WGRAD, l, GPS_BO, D, D, T, a1, D, ctx, D,
+  if (!ss.fork()) return GPIPE_ERR_DEVICE;  // a1 exists
+  GP_RUN(w, GPIPE_ROLE_OUT_WGRAD, mm_wgrad(w, GPIPE_ROLE_OUT_WGRAD, l, GPS_BO, D, D, T, a1, D, ctx, D,
               x.grad(l, GPIPE_W_O), D, beta, &fused));
+  if (!ss.mark(&mine->out)) return GPIPE_ERR_DEVICE;
+  GP_RUN(x, GPIPE_ROLE_OUT_DGRAD, mm(x, GPIPE_ROLE_OUT_DGRAD, T, D, D, a1, D, x.wmat(l, GPIPE_W_O), D, dctx, D));
   if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r1, D, D, x.grad(l, GPIPE_B_O), beta));
   const int64_t sq = int64_t(S) * 3 * D;
   const int64_t sp = int64_t(H) * S * ldS;
@@ -400,6 +462,7 @@ gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int b
   Bat PP{P, ldS, sp, int64_t(S) * ldS}, DP{dP, ldS, sp, int64_t(S) * ldS}, DS{dS, ldS, sp, int64_t(S) * ldS};
   Bat DC{dctx, D, sd, dh};
   const int cz = c->causal;
+  if (!ss.join(above.qkv)) return GPIPE_ERR_DEVICE;  // the layer above's QKV weight gradient read dqkv
   if (p.flash) {
     const float* lse2 = static_cast<const float*>(P);
     GP_RUN(x, GPIPE_ROLE_ATTN_DELTA, flash_bwd(qkv, ctx, dctx, lse2, dP, dqkv, p.B, H, S, D, cz, x.s, 0));
@@ -418,12 +481,15 @@ gpipe_status layer_backward(const Ctx& x, int set, int l, const void* xin, int b
   }
 
   // qkv = h1 Wqkv^T + bqkv,  h1 = LN1(x)
+  if (!ss.fork()) return GPIPE_ERR_DEVICE;  // dqkv exists
+  GP_RUN(w, GPIPE_ROLE_QKV_WGRAD, mm_wgrad(w, GPIPE_ROLE_QKV_WGRAD, l, GPS_BQKV, 3 * D, D, T, dqkv, 3 * D, h1,
+              D, x.grad(l, GPIPE_W_QKV), D, beta, &fused));
+  if (!ss.mark(&mine->qkv)) return GPIPE_ERR_DEVICE;
   GP_RUN(x, GPIPE_ROLE_QKV_DGRAD, mm(x, GPIPE_ROLE_QKV_DGRAD, T, D, 3 * D, dqkv, 3 * D, x.wmat(l, GPIPE_W_QKV), D,
               dm, D));
-  GP_RUN(x, GPIPE_ROLE_QKV_WGRAD, mm_wgrad(x, GPIPE_ROLE_QKV_WGRAD, l, GPS_BQKV, 3 * D, D, T, dqkv, 3 * D, h1,
-              D, x.grad(l, GPIPE_W_QKV), D, beta, &fused));
   if (!fused)
     GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, dqkv, 3 * D, 3 * D, x.grad(l, GPIPE_B_QKV), beta));
+  if (!ss.join(mine->ffn2)) return GPIPE_ERR_DEVICE;  // this layer's FFN2 weight gradient read a0
   GP_RUN(x, GPIPE_ROLE_LN1_BWD, layernorm_bwd(bf, dm, xin, st1, x.wf32(l, GPIPE_LN1_G), r1, r0, dx_out ? dx_out : a0,
                          ln1part, T, D, beta, &nblk, x.s));
   return GPIPE_OK;
@@ -522,8 +588,11 @@ gpipe_status gpipe_cell_bind_running(gpipe_cell* c, float* running) {
 }
 
 gpipe_status gpipe_cell_destroy(gpipe_cell* c) {
-  if (c)
+  if (c) {
     for (hipEvent_t e : c->prof_events) (void)hipEventDestroy(e);
+    for (hipEvent_t e : c->sync_events) (void)hipEventDestroy(e);
+    if (c->aux) (void)hipStreamDestroy(c->aux);
+  }
   delete c;
   return GPIPE_OK;
 }
@@ -605,8 +674,13 @@ gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, v
   if (!aligned16(x) || !aligned16(target) || !aligned16(y) || (dx && !aligned16(dx)) ||
       !aligned16(workspace))
     return GPIPE_ERR_INVALID;
+  {
+    const gpipe_status st = ensure_streams(c);
+    if (st != GPIPE_OK) return st;
+  }
   Ctx cx{c, c->prof_mask ? c : nullptr, &p, static_cast<char*>(workspace),
          static_cast<hipStream_t>(stream), c->prec == GPIPE_BF16};
+  Streams ss{c, cx.s, c->aux};
   const size_t mb = size_t(p.T) * c->D;  // elements per micro-batch
   const float inv_denom = float(1.0 / (double(N) * c->S * c->D));
   float* msepart = static_cast<float*>(cx.at(p.msepart));
@@ -622,6 +696,9 @@ gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, v
     const int set = remat ? 0 : m;
     const void* xm = cx.act(x, m * mb);
     const void* ym = cx.act(y, m * mb);
+    // every weight gradient of the previous micro-batch has read the saved
+    // activations and the transient gradients this one overwrites
+    if (m > 0 && !ss.join_all()) return GPIPE_ERR_DEVICE;
     if (remat) {
       void* yre = cx.at(p.yre);
       gpipe_status st = cell_forward(cx, set, xm, yre);
@@ -632,13 +709,18 @@ gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, v
     GP_RUN(cx, GPIPE_ROLE_MSE, mse_fwd_bwd(cx.bf16, ym, cx.act(target, m * mb), static_cast<float*>(cx.at(p.r0)),
                          cx.at(p.a0), msepart + size_t(m) * p.mse_nblk, int64_t(mb), inv_denom,
                          &nblk, cx.s));
+    WgradDone above;  // the top layer has none above it in this micro-batch
     for (int l = c->L - 1; l >= 0; --l) {
       const void* xin = l == 0 ? xm : cx.at(saved_at(p, set, l, GPIPE_SAVED_X));
       void* dxo = (l == 0 && dx) ? cx.act(dx, m * mb) : nullptr;
-      gpipe_status st = layer_backward(cx, set, l, xin, m > 0 ? 1 : 0, dxo);
+      WgradDone mine;
+      gpipe_status st = layer_backward(cx, ss, above, &mine, set, l, xin, m > 0 ? 1 : 0, dxo);
       if (st != GPIPE_OK) return st;
+      above = mine;
     }
   }
+  // the weight gradients (and their bias partial sums) are complete
+  if (!ss.join_all()) return GPIPE_ERR_DEVICE;
   {
     gpipe_status st = reduce_gparts(cx);
     if (st != GPIPE_OK) return st;
