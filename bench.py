@@ -37,11 +37,15 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
-# Roles the cell's step runs on its second stream, concurrently with the
-# input-gradient chain on the caller's stream: their event-bracketed times
-# include time shared with other kernels, so they are not per-kernel figures
-# and are left out of the dominant-kernel choice and of mfma_util_gemm.
-OVERLAPPED_ROLES = ("ffn2_wgrad", "ffn1_wgrad", "out_wgrad", "qkv_wgrad")
+# In the Transformer cell's backward phase the weight-gradient GEMMs run on a
+# second stream, concurrently with the input-gradient chain on the caller's
+# stream, so the event-bracketed times of every backward-phase launch include
+# time shared with other kernels: they are not per-kernel figures.  The
+# dominant kernel and mfma_util_gemm come from the roles of the forward phase
+# and the re-materialized forward, which run alone.
+SECOND_STREAM_ROLES = ("ffn2_wgrad", "ffn1_wgrad", "out_wgrad", "qkv_wgrad")
+ALONE_ROLES = ("ln1_fwd", "qkv_fwd", "scores_fwd", "softmax_fwd", "pv_fwd", "attn_fwd", "out_fwd",
+               "ln2_fwd", "ffn1_fwd", "ffn2_fwd", "mse")
 
 
 def log(*a):
@@ -415,7 +419,7 @@ def main():
     def single_kernel(name):
         if name not in work or name in ("bias_grad", "norm_grad", "loss_reduce"):
             return False
-        if not conv and name in OVERLAPPED_ROLES:
+        if not conv and name not in ALONE_ROLES:
             return False
         return gpipe.gpipe_cell_gemm_plan(cell.handle, n, m, gpipe.ROLES.index(name))[2] <= 1
     dominant = max((k for k in prof if single_kernel(k)), key=lambda k: prof[k][0])
@@ -457,8 +461,9 @@ def main():
             _, _, sp_ = gpipe.gpipe_cell_gemm_plan(cell.handle, n, m, gpipe.ROLES.index(name))
             if sp_ > 1:
                 e["split_k"] = sp_
-        if not conv and name in OVERLAPPED_ROLES:
-            e["stream"] = "second, overlapped with the input-gradient chain"
+        if not conv and name not in ALONE_ROLES and name not in ("loss_reduce", "rmsprop"):
+            e["overlapped"] = ("second stream" if name in SECOND_STREAM_ROLES
+                               else "caller's stream") + ", concurrent with the other stream"
         if kind == "mfma":
             tf = per / (ms_tot / cnt * 1e-3) / 1e12
             pk = PEAK_BF16_TFLOPS if cfg.precision == "bf16" else PEAK_FP32_TFLOPS
@@ -492,7 +497,7 @@ def main():
     roof["work_per_launch"] = per
 
     def clean(k):
-        return work.get(k, ("", 0))[0] == "mfma" and (conv or k not in OVERLAPPED_ROLES)
+        return work.get(k, ("", 0))[0] == "mfma" and (conv or k in ALONE_ROLES)
     gemm_flops = sum(work[k][1] * src[k][1] for k in src if clean(k))
     gemm_ms = sum(src[k][0] for k in src if clean(k))
     step_flops = sum(work[k][1] * src[k][1] for k in src if work.get(k, ("", 0))[0] == "mfma")

@@ -70,17 +70,27 @@ inline bool prof_pair(gpipe_cell* c, int role, hipEvent_t* e0, hipEvent_t* e1) {
   return true;
 }
 
-// Launches `expr`; when `role` is being timed, brackets it with two events
-// recorded on the context's stream.
+// Launches `expr`; when `role` is being timed, a GEMM role's launch records
+// two events in its own dispatch (launch_events()), any other role is
+// bracketed by two events recorded on the context's stream.
 #define GP_RUN(ctx, role, expr)                                                         \
   do {                                                                                 \
     hipEvent_t e0_ = nullptr, e1_ = nullptr;                                           \
+    const bool in_launch_ = gemm_role(role);                                           \
     if ((ctx).prof && (((ctx).prof->prof_mask >> (role)) & 1ull)) {                   \
       if (!prof_pair((ctx).prof, (role), &e0_, &e1_)) return GPIPE_ERR_DEVICE;          \
-      if (hipEventRecord(e0_, (ctx).s) != hipSuccess) return GPIPE_ERR_DEVICE;         \
+      if (in_launch_)                                                                  \
+        launch_events() = LaunchEvents{e0_, e1_};                                      \
+      else if (hipEventRecord(e0_, (ctx).s) != hipSuccess)                             \
+        return GPIPE_ERR_DEVICE;                                                       \
     }                                                                                  \
     if ((expr) != hipSuccess) return GPIPE_ERR_DEVICE;                                 \
-    if (e1_ && hipEventRecord(e1_, (ctx).s) != hipSuccess) return GPIPE_ERR_DEVICE;    \
+    if (e1_ && in_launch_ && (launch_events().start || launch_events().stop)) {        \
+      launch_events() = LaunchEvents{};                                                \
+      return GPIPE_ERR_STATE; /* a GEMM launch path did not take the events */         \
+    }                                                                                  \
+    if (e1_ && !in_launch_ && hipEventRecord(e1_, (ctx).s) != hipSuccess)              \
+      return GPIPE_ERR_DEVICE;                                                         \
   } while (0)
 
 // Conv-cell driver (conv_cell.hip).

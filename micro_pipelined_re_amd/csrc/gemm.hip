@@ -140,6 +140,13 @@ GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch) {
   return p;
 }
 
+LaunchEvents& launch_events() {
+  static thread_local LaunchEvents e;
+  return e;
+}
+
+bool gemm_role(int role) { return group_of(role) >= 0; }
+
 int gemm_cfg_bm(int cfg) { return kCfgBM[cfg]; }
 int gemm_cfg_bn(int cfg) { return kCfgBN[cfg]; }
 

@@ -703,12 +703,14 @@ template <class DC, class RC, int LA, int LB, int EPI, int ROLE>
 hipError_t launch_bf16(int path, const GemmParams& g, int batch, int splits, hipStream_t s) {
   const int bm = path == 0 ? DC::BM : RC::BM, bn = path == 0 ? DC::BN : RC::BN;
   const int tiles = ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
-  if (tiles == 0 || batch == 0) return hipSuccess;
+  if (tiles == 0 || batch == 0) return launch_nothing(s);
   const dim3 grid(tiles, splits, batch);
+  const bool one = splits == 1;  // the product is the whole launch
+  hipError_t e;
   if constexpr (LA == LAY_CONV) {
     // the gathered operand exists only on the direct-to-LDS path
     if (path != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_dma_kernel<DC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, g);
+    e = launch_timed((gemm_dma_kernel<DC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, true, one, g);
   } else if (path == 0) {
     if constexpr (DC::OCC == 1 && DC::BK == 64 && DC::STAGES == 3) {
       constexpr int smem = spec_smem_bytes<DC>();
@@ -716,21 +718,20 @@ hipError_t launch_bf16(int path, const GemmParams& g, int batch, int splits, hip
           reinterpret_cast<const void*>(&gemm_spec_kernel<DC, LA, LB, EPI, ROLE>),
           hipFuncAttributeMaxDynamicSharedMemorySize, smem);
       if (attr != hipSuccess) return attr;
-      hipLaunchKernelGGL((gemm_spec_kernel<DC, LA, LB, EPI, ROLE>), grid, dim3(kSpecThreads), smem,
-                         s, g);
+      e = launch_timed((gemm_spec_kernel<DC, LA, LB, EPI, ROLE>), grid, dim3(kSpecThreads), smem, s,
+                       true, one, g);
     } else {
-      hipLaunchKernelGGL((gemm_dma_kernel<DC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, g);
+      e = launch_timed((gemm_dma_kernel<DC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, true, one, g);
     }
   } else {
-    hipLaunchKernelGGL((gemm_bf16_kernel<RC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, g);
+    e = launch_timed((gemm_bf16_kernel<RC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, true, one, g);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
+  if (e != hipSuccess || one) return e;
   const int64_t n = int64_t(g.M) * g.N;
   const int64_t want = (n + 255) / 256;
   const int blocks = int(want < 4096 ? want : 4096);
-  hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI>), dim3(blocks), dim3(256), 0, s, g, splits);
-  return hipGetLastError();
+  return launch_timed((splitk_reduce_kernel<bf16_t, EPI>), dim3(blocks), dim3(256), 0, s, false,
+                      true, g, splits);
 }
 
 }  // namespace gp

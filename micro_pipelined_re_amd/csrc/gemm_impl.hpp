@@ -27,6 +27,8 @@
 // Accumulator layout (16x16 block): lane l holds column l%16, rows 4*(l/16)+v.
 #pragma once
 #include "../../include/gpipe.h"
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -592,13 +594,40 @@ hipError_t gemm_group_wgrad(int role, int path, int cfg, const GemmParams& g, in
 hipError_t gemm_group_attn(int role, int path, int cfg, const GemmParams& g, int batch, int splits, hipStream_t s);
 hipError_t gemm_group_f32(int role, const GemmParams& g, int batch, hipStream_t s);
 
+// Launches a kernel; `first` / `last`: it is the first / last kernel of its
+// GEMM launch, which then records the pending role-timing events
+// (launch_events()) in its dispatch and clears them.
+template <typename K, typename... A>
+hipError_t launch_timed(K kernel, dim3 grid, dim3 block, uint32_t smem, hipStream_t s, bool first,
+                        bool last, A... args) {
+  LaunchEvents& le = launch_events();
+  const hipEvent_t e0 = first ? le.start : nullptr, e1 = last ? le.stop : nullptr;
+  if (first) le.start = nullptr;
+  if (last) le.stop = nullptr;
+  if (e0 || e1)
+    hipExtLaunchKernelGGL(kernel, grid, block, smem, s, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, smem, s, args...);
+  return hipGetLastError();
+}
+
+// A GEMM launch with nothing to compute still takes the pending events:
+// both are recorded on the stream (an empty interval).
+inline hipError_t launch_nothing(hipStream_t s) {
+  LaunchEvents& le = launch_events();
+  hipError_t e = hipSuccess;
+  if (le.start) e = hipEventRecord(le.start, s);
+  if (le.stop && e == hipSuccess) e = hipEventRecord(le.stop, s);
+  le.start = le.stop = nullptr;
+  return e;
+}
+
 template <int LA, int LB, int EPI, int ROLE>
 hipError_t launch_f32(const GemmParams& g, int batch, hipStream_t s) {
   const int tiles = ((g.M + 63) / 64) * ((g.N + 63) / 64);
-  if (tiles == 0 || batch == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_f32_kernel<LA, LB, EPI, ROLE>), dim3(tiles, 1, batch), dim3(kThreads),
-                     0, s, g);
-  return hipGetLastError();
+  if (tiles == 0 || batch == 0) return launch_nothing(s);
+  return launch_timed((gemm_f32_kernel<LA, LB, EPI, ROLE>), dim3(tiles, 1, batch), dim3(kThreads),
+                      0, s, true, true, g);
 }
 
 }  // namespace gp

@@ -75,6 +75,18 @@ size_t gemm_partial_floats(int role, bool bf16, int M, int N, int K, int batch);
 // epilogue (see gemm.hip) and names the kernel instance in profiles.
 hipError_t gemm(bool bf16, int role, const GemmParams& g, int batch, hipStream_t s);
 
+// Role timing inside the dispatch.  When start / stop are set (host side, by
+// the step driver's role timing), the next GEMM launch records them in its
+// own dispatch packets -- start at the beginning of its first kernel, stop
+// at the end of its last -- and clears them, so the measured interval is the
+// kernels' execution, not the enqueue around it.  Per host thread.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();
+// true for the roles whose launch is a gemm() call (they take the events)
+bool gemm_role(int role);
+
 // ---------------------------------------------------------------- row kernels
 // LayerNorm forward over rows of length D: y(act) = gamma*(x-mu)*rstd + beta, stats[2*row] = (mu, rstd).
 hipError_t layernorm_fwd(bool bf16, const void* x, void* y, float* stats, const float* gamma,
