@@ -14,13 +14,14 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN.
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t(0x7fc0);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return bf16_t(u >> 16);
+// fp32 -> bf16, round to nearest even (NaN stays NaN): v_cvt_pk_bf16_f32,
+// two values per instruction.
+typedef float float2v_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v_t{lo, hi}), bf16x2v_t));
 }
+__device__ __forceinline__ bf16_t f2bf(float f) { return bf16_t(f2bf2(f, 0.0f) & 0xffffu); }
 
 template <typename T> __device__ __forceinline__ float to_f(T v);
 template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
@@ -68,14 +69,34 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
-// GeLU, exact form u * Phi(u), and its derivative Phi(u) + u * phi(u).
+// erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26: erf(|x|) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5))))
+// exp(-x^2), t = 1 / (1 + p |x|), |error| <= 1.5e-7 -- below the bf16
+// rounding of the activations it feeds.  Branch-free (one reciprocal, one
+// exponential; the library erff evaluates two branches in a divergent wave,
+// ~40 instructions).  *ex2 receives exp(-x^2).
+__device__ __forceinline__ float erf_as(float x, float* ex2) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  const float e = __builtin_amdgcn_exp2f((ax * ax) * -1.4426950408889634f);
+  float p = fmaf(t, 1.061405429f, -1.453152027f);
+  p = fmaf(t, p, 1.421413741f);
+  p = fmaf(t, p, -0.284496736f);
+  p = fmaf(t, p, 0.254829592f);
+  *ex2 = e;
+  return copysignf(fmaf(-(p * t), e, 1.0f), x);
+}
+
+// GeLU, exact form u * Phi(u), and its derivative Phi(u) + u * phi(u), with
+// Phi(u) = (1 + erf(u / sqrt 2)) / 2 and phi(u) = exp(-u^2 / 2) / sqrt(2 pi).
 __device__ __forceinline__ float gelu_f(float u) {
-  return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
+  float e;
+  return 0.5f * u * (1.0f + erf_as(u * 0.70710678118654752f, &e));
 }
 __device__ __forceinline__ float gelu_grad_f(float u) {
-  const float cdf = 0.5f * (1.0f + erff(u * 0.70710678118654752f));
-  const float pdf = expf(-0.5f * u * u) * 0.39894228040143268f;
-  return cdf + u * pdf;
+  float e;  // exp(-(u / sqrt 2)^2) = exp(-u^2 / 2)
+  const float cdf = 0.5f * (1.0f + erf_as(u * 0.70710678118654752f, &e));
+  return cdf + u * (e * 0.39894228040143268f);
 }
 
 // ------------------------------------------------------------ 8-element chunks
@@ -102,10 +123,10 @@ template <> __device__ __forceinline__ void store8<float>(float* p, const float*
 }
 template <> __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float* v) {
   uint4 a;
-  a.x = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
-  a.y = uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16);
-  a.z = uint32_t(f2bf(v[4])) | (uint32_t(f2bf(v[5])) << 16);
-  a.w = uint32_t(f2bf(v[6])) | (uint32_t(f2bf(v[7])) << 16);
+  a.x = f2bf2(v[0], v[1]);
+  a.y = f2bf2(v[2], v[3]);
+  a.z = f2bf2(v[4], v[5]);
+  a.w = f2bf2(v[6], v[7]);
   *reinterpret_cast<uint4*>(p) = a;
 }
 

@@ -80,7 +80,10 @@ constexpr int kCUs = 256;
 // 128 x 128 tiles; at k = 8192 the narrow tiles re-read the operand that
 // the step brings in cold twice as often and took 60 us against 51 us for
 // 128 x 128 tiles split in two); else 128 x 128 tiles, split in two for
-// k >= 4096.  Against 128 x 128 tiles with two workgroups
+// k >= 4096 in the forward products only (the input-gradient products run
+// while the weight gradients occupy the second stream, which fills the idle
+// CUs: unsplit, the step takes as long and the split-K reduction, which then
+// contends with the weight gradients' read-modify-write, disappears).  Against 128 x 128 tiles with two workgroups
 // per CU the specialised kernel ran 5-37% faster on every role of the
 // 2048-wide layer.  Weight gradients never split (their fp32 partials would
 // double the accumulator traffic).  The
@@ -126,7 +129,7 @@ GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch) {
       // fewer big tiles than 3/4 of the CUs: 128 x 128 tiles, and for deep k
       // two splits (the partial sums cost less than the idle CUs)
       p.cfg = CFG_128x128_SPEC;
-      if (!is_wgrad(role) && K >= 4096 && t128 < 192) split_of(2, 1024);
+      if (group_of(role) == 0 && K >= 4096 && t128 < 192) split_of(2, 1024);
       return p;
     }
   }

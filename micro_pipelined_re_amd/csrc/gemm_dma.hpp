@@ -253,10 +253,10 @@ __device__ __forceinline__ void epi_store8(const GemmParams& g, int row, int col
     };
     auto st8 = [](bf16_t* p, const float* v) {
       uint4 u;
-      u.x = uint32_t(f2bf(v[0])) | (uint32_t(f2bf(v[1])) << 16);
-      u.y = uint32_t(f2bf(v[2])) | (uint32_t(f2bf(v[3])) << 16);
-      u.z = uint32_t(f2bf(v[4])) | (uint32_t(f2bf(v[5])) << 16);
-      u.w = uint32_t(f2bf(v[6])) | (uint32_t(f2bf(v[7])) << 16);
+      u.x = f2bf2(v[0], v[1]);
+      u.y = f2bf2(v[2], v[3]);
+      u.z = f2bf2(v[4], v[5]);
+      u.w = f2bf2(v[6], v[7]);
       *reinterpret_cast<uint4*>(p) = u;
     };
     float b[8];

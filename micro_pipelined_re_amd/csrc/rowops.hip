@@ -578,8 +578,8 @@ __global__ __launch_bounds__(256) void rmsprop_kernel(float* __restrict__ w, con
     reinterpret_cast<float4*>(w)[i] = wv;
     if (wl) {
       uint2 o;
-      o.x = uint32_t(f2bf(wv.x)) | (uint32_t(f2bf(wv.y)) << 16);
-      o.y = uint32_t(f2bf(wv.z)) | (uint32_t(f2bf(wv.w)) << 16);
+      o.x = f2bf2(wv.x, wv.y);
+      o.y = f2bf2(wv.z, wv.w);
       reinterpret_cast<uint2*>(wl)[i] = o;
     }
   }
