@@ -5,9 +5,10 @@
 // softmax in registers, and accumulate the output (two wave groups, each
 // over half of the key blocks, combined at the end); only the log-sum-exp of
 // every query row is saved.  Backward recomputes the probabilities from it:
-// one kernel per key block accumulates dK and dV over the query blocks, one
-// per query block accumulates dQ over the key blocks, so every sum has a
-// fixed order (no atomics) and the result is reproducible.
+// one kernel per query block accumulates dQ over the key blocks (and first
+// computes the rows' sums of dO * O), then one kernel per key block
+// accumulates dK and dV over the query blocks, so every sum has a fixed
+// order (no atomics) and the result is reproducible.
 //
 // Scores live in base 2: x = (q . k) * scale * log2(e), p = 2^(x - lse2).
 //
@@ -318,30 +319,6 @@ __global__ __launch_bounds__(512) void flash_fwd_kernel(const bf16_t* __restrict
 }
 
 // ------------------------------------------------------------------ backward
-// delta[bh][s] = sum_d dO[s][h*DH + d] * O[s][h*DH + d]
-template <int DH>
-__global__ __launch_bounds__(256) void flash_delta_kernel(const bf16_t* __restrict__ dctx,
-                                                          const bf16_t* __restrict__ ctx,
-                                                          float* __restrict__ delta, int S, int H,
-                                                          int D, int rows) {
-  const int i = blockIdx.x * 256 + threadIdx.x;  // (token, head)
-  if (i >= rows) return;
-  const int t = i / H, h = i % H;
-  const int b = t / S, s = t % S;
-  const bf16_t* a = dctx + int64_t(t) * D + h * DH;
-  const bf16_t* c = ctx + int64_t(t) * D + h * DH;
-  float acc = 0.f;
-#pragma unroll
-  for (int k = 0; k < DH; k += 8) {
-    float x[8], y[8];
-    load8<bf16_t>(a + k, x);
-    load8<bf16_t>(c + k, y);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += x[e] * y[e];
-  }
-  delta[(int64_t(b) * H + h) * S + s] = acc;
-}
-
 // dK, dV for one key block: grid (key blocks, B*H); the groups split the
 // query blocks.
 template <int DH>
@@ -477,12 +454,15 @@ __global__ __launch_bounds__(512) void flash_dkdv_kernel(
 }
 
 // dQ for one query block: grid (query blocks, B*H); the groups split the key
-// blocks.
+// blocks.  It also computes the block's row sums delta = rowsum(dO * O) (each
+// lane a 32-column share of its query row, then the four lane groups added in
+// a fixed order), uses them and writes them for the dK / dV kernel, which runs
+// after it.
 template <int DH>
 __global__ __launch_bounds__(512) void flash_dq_kernel(
-    const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dctx,
-    const float* __restrict__ lse2, const float* __restrict__ delta, bf16_t* __restrict__ dqkv,
-    int S, int H, int D, int causal, float sl2, float scale) {
+    const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ ctx,
+    const bf16_t* __restrict__ dctx, const float* __restrict__ lse2, float* __restrict__ delta,
+    bf16_t* __restrict__ dqkv, int S, int H, int D, int causal, float sl2, float scale) {
   constexpr int KS = DH / 32;
   constexpr int DT = DH / 16;
   constexpr int TE = attn_tile_elems<DH>();
@@ -505,7 +485,19 @@ __global__ __launch_bounds__(512) void flash_dq_kernel(
     of[ks] = gfrag(Og, D, q, S, ks * 32 + 8 * g);
   }
   const float lq = q < S ? lse2[int64_t(bh) * S + q] : INFINITY;
-  const float dq_ = q < S ? delta[int64_t(bh) * S + q] : 0.f;
+  float dq_ = 0.f;  // delta of query q
+  {
+    const bf16_t* Cg = ctx + int64_t(b) * S * D + h * DH;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8_t o = gfrag(Cg, D, q, S, ks * 32 + 8 * g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dq_ = fmaf(float(of[ks][e]), float(o[e]), dq_);
+    }
+    dq_ += __shfl_xor(dq_, 16, 64);
+    dq_ += __shfl_xor(dq_, 32, 64);
+    if (grp == 0 && g == 0 && q < S) delta[int64_t(bh) * S + q] = dq_;
+  }
   floatx4_t acc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -638,34 +630,25 @@ hipError_t flash_bwd(const void* qkv, const void* ctx, const void* dctx, const f
   const bf16_t* o = static_cast<const bf16_t*>(ctx);
   const bf16_t* dO = static_cast<const bf16_t*>(dctx);
   bf16_t* dq = static_cast<bf16_t*>(dqkv);
-  const int rows = B * S * H;
   if (dh != 128 && dh != 64) return hipErrorInvalidValue;
-  if (stage == 0) {
+  if (stage != 1 && stage != 2) return hipErrorInvalidValue;
+  hipError_t e = dh == 128 ? attn_attrs<128>() : attn_attrs<64>();
+  if (e != hipSuccess) return e;
+  const int sm = dh == 128 ? attn_smem_bytes<128>() : attn_smem_bytes<64>();
+  if (stage == 1) {
     if (dh == 128)
-      hipLaunchKernelGGL(flash_delta_kernel<128>, dim3((rows + 255) / 256), dim3(256), 0, s, dO, o,
-                         delta, S, H, D, rows);
+      hipLaunchKernelGGL(flash_dkdv_kernel<128>, grid, dim3(512), sm, s, q, dO, lse2, delta, dq, S,
+                         H, D, causal, sl2, scale);
     else
-      hipLaunchKernelGGL(flash_delta_kernel<64>, dim3((rows + 255) / 256), dim3(256), 0, s, dO, o,
-                         delta, S, H, D, rows);
+      hipLaunchKernelGGL(flash_dkdv_kernel<64>, grid, dim3(512), sm, s, q, dO, lse2, delta, dq, S,
+                         H, D, causal, sl2, scale);
   } else {
-    hipError_t e = dh == 128 ? attn_attrs<128>() : attn_attrs<64>();
-    if (e != hipSuccess) return e;
-    const int sm = dh == 128 ? attn_smem_bytes<128>() : attn_smem_bytes<64>();
-    if (stage == 1) {
-      if (dh == 128)
-        hipLaunchKernelGGL(flash_dkdv_kernel<128>, grid, dim3(512), sm, s, q, dO, lse2, delta, dq, S,
-                           H, D, causal, sl2, scale);
-      else
-        hipLaunchKernelGGL(flash_dkdv_kernel<64>, grid, dim3(512), sm, s, q, dO, lse2, delta, dq, S,
-                           H, D, causal, sl2, scale);
-    } else {
-      if (dh == 128)
-        hipLaunchKernelGGL(flash_dq_kernel<128>, grid, dim3(512), sm, s, q, dO, lse2, delta, dq, S, H,
-                           D, causal, sl2, scale);
-      else
-        hipLaunchKernelGGL(flash_dq_kernel<64>, grid, dim3(512), sm, s, q, dO, lse2, delta, dq, S, H,
-                           D, causal, sl2, scale);
-    }
+    if (dh == 128)
+      hipLaunchKernelGGL(flash_dq_kernel<128>, grid, dim3(512), sm, s, q, o, dO, lse2, delta, dq, S,
+                         H, D, causal, sl2, scale);
+    else
+      hipLaunchKernelGGL(flash_dq_kernel<64>, grid, dim3(512), sm, s, q, o, dO, lse2, delta, dq, S,
+                         H, D, causal, sl2, scale);
   }
   return hipGetLastError();
 }

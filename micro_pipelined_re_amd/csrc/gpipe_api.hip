@@ -465,9 +465,9 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, const WgradDone& above, W
   if (!ss.join(above.qkv)) return GPIPE_ERR_DEVICE;  // the layer above's QKV weight gradient read dqkv
   if (p.flash) {
     const float* lse2 = static_cast<const float*>(P);
-    GP_RUN(x, GPIPE_ROLE_ATTN_DELTA, flash_bwd(qkv, ctx, dctx, lse2, dP, dqkv, p.B, H, S, D, cz, x.s, 0));
-    GP_RUN(x, GPIPE_ROLE_ATTN_DKDV, flash_bwd(qkv, ctx, dctx, lse2, dP, dqkv, p.B, H, S, D, cz, x.s, 1));
+    // dQ first: it also writes the row sums of dO * O that dK / dV read
     GP_RUN(x, GPIPE_ROLE_ATTN_DQ, flash_bwd(qkv, ctx, dctx, lse2, dP, dqkv, p.B, H, S, D, cz, x.s, 2));
+    GP_RUN(x, GPIPE_ROLE_ATTN_DKDV, flash_bwd(qkv, ctx, dctx, lse2, dP, dqkv, p.B, H, S, D, cz, x.s, 1));
   } else {
     GP_RUN(x, GPIPE_ROLE_DP, bmm(x, GPIPE_ROLE_DP, S, S, dh, DC, V, DP,
                  cz ? CAUSAL_SKIP_UPPER : CAUSAL_NONE, 1.0f));

@@ -156,7 +156,7 @@ hipError_t bn_running(const float* rec, int M, int nbn, int C, int64_t n_total, 
 bool flash_ok(bool bf16, int dh);
 hipError_t flash_fwd(const void* qkv, void* ctx, float* lse2, int B, int H, int S, int D,
                      int causal, hipStream_t s);
-// stage 0: delta = rowsum(dctx * ctx); 1: dK, dV; 2: dQ
+// stage 2: dQ, and delta = rowsum(dctx * ctx) (written); then stage 1: dK, dV (reads delta)
 hipError_t flash_bwd(const void* qkv, const void* ctx, const void* dctx, const float* lse2,
                      float* delta, void* dqkv, int B, int H, int S, int D, int causal,
                      hipStream_t s, int stage);
