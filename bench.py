@@ -37,12 +37,12 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
-# In the Transformer cell's backward phase the weight-gradient GEMMs run on a
-# second stream, concurrently with the input-gradient chain on the caller's
-# stream, so the event-bracketed times of every backward-phase launch include
-# time shared with other kernels: they are not per-kernel figures.  The
-# dominant kernel and mfma_util_gemm come from the roles of the forward phase
-# and the re-materialized forward, which run alone.
+# The Transformer cell's step runs two streams: in the forward phase even and
+# odd micro-batches (those launches are not role-timed), in the backward phase
+# the weight-gradient GEMMs beside the input-gradient chain, so the times of
+# every backward-phase launch include time shared with other kernels: they are
+# not per-kernel figures.  The dominant kernel and mfma_util_gemm come from the
+# roles of the re-materialized forward, which runs alone.
 SECOND_STREAM_ROLES = ("ffn2_wgrad", "ffn1_wgrad", "out_wgrad", "qkv_wgrad")
 ALONE_ROLES = ("ln1_fwd", "qkv_fwd", "scores_fwd", "softmax_fwd", "pv_fwd", "attn_fwd", "out_fwd",
                "ln2_fwd", "ffn1_fwd", "ffn2_fwd", "mse")
@@ -114,6 +114,17 @@ def role_work(cfg, n, m):
         "rmsprop": ("hbm", P * (20 + (2 if eb == 2 else 0))),
     }
     return w
+
+
+def step_mfma_flops(cfg, n, m):
+    """Algorithmic MFMA work of one Transformer-cell step: per layer and micro-batch
+    the forward and the re-materialized forward (linears + the two attention
+    products each), the input- and weight-gradient linears (twice the forward's)
+    and the four attention-gradient products."""
+    w = role_work(cfg, n, m)
+    lin = sum(w[k][1] for k in ("qkv_fwd", "out_fwd", "ffn1_fwd", "ffn2_fwd"))
+    attn = w["scores_fwd"][1]
+    return cfg.layers * m * (4 * lin + 8 * attn)
 
 
 def conv_role_work(cfg, n, m):
@@ -500,7 +511,9 @@ def main():
         return work.get(k, ("", 0))[0] == "mfma" and (conv or k in ALONE_ROLES)
     gemm_flops = sum(work[k][1] * src[k][1] for k in src if clean(k))
     gemm_ms = sum(src[k][0] for k in src if clean(k))
-    step_flops = sum(work[k][1] * src[k][1] for k in src if work.get(k, ("", 0))[0] == "mfma")
+    # (the Transformer cell's forward-phase launches are not role-timed: count its work directly)
+    step_flops = (sum(work[k][1] * src[k][1] for k in src if work.get(k, ("", 0))[0] == "mfma")
+                  if conv else step_mfma_flops(cfg, n, m))
     keep_bytes = gpipe.gpipe_cell_workspace_bytes(cell.handle, n, m, False)
     act_bytes = x.numel() * x.element_size()
     if conv:

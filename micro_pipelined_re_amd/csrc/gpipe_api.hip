@@ -58,7 +58,7 @@ struct Plan {
   size_t saved_bytes[GPIPE_N_SAVED];
   size_t layer_bytes, set_bytes;
   int nsets;
-  size_t yre, scores, ds, r0, r1, dm, a0, a1, dctx, du, dqkv, colpart, gpart, msepart, splitk;
+  size_t yre, scores, ds, r0, r1, dm, a0, a1, dctx, du, dqkv, colpart, gpart, msepart, splitk, splitk2;
   size_t colpart_floats;
   // gpart slots (GPS_*): offset inside a layer's block, partial rows, row length
   size_t gp_off[GPS_N], gp_layer;
@@ -157,6 +157,8 @@ bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
   size_t sk = 0;
   for (const auto& r : shapes) sk = std::max(sk, gemm_partial_floats(r[0], bf, r[1], r[2], r[3], 1));
   p->splitk = take(sk * 4);
+  // the forward phase's second lane (overlapped_forward) has its own partials
+  p->splitk2 = take(sk * 4);
   p->total = o;
   return true;
 }
@@ -178,6 +180,7 @@ struct Ctx {
   char* ws;
   hipStream_t s;
   bool bf16;
+  size_t splitk;     // workspace offset of this stream's split-K partials
   const void* wmat(int layer, int t) const {
     const size_t off = size_t(layer) * c->per_layer + c->rel_off[t];
     if (bf16) return static_cast<const uint16_t*>(c->w_lowp) + off;
@@ -265,7 +268,7 @@ hipError_t mm(const Ctx& x, int role, int M, int N, int K, const void* A, int64_
   g.B = B; g.ldb = ldb;
   g.C = C; g.ldc = ldc;
   g.bias = bias; g.R = R; g.ldr = ldr; g.U = U; g.ldu = ldu; g.beta = beta;
-  g.P = static_cast<float*>(x.at(x.p->splitk));
+  g.P = static_cast<float*>(x.at(x.splitk));
   return gemm(x.bf16, role, g, 1, x.s);
 }
 
@@ -290,7 +293,7 @@ hipError_t mm_wgrad(const Ctx& x, int role, int layer, int slot, int M, int N, i
                     const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
                     int64_t ldc, int beta, bool* fused) {
   GemmParams g = wgrad_params(M, N, K, A, lda, B, ldb, C, ldc, beta);
-  g.P = static_cast<float*>(x.at(x.p->splitk));
+  g.P = static_cast<float*>(x.at(x.splitk));
   const int parts = x.bf16 ? gemm_rowsum_parts(role, g, 1) : 0;
   *fused = parts > 0 && parts == x.p->gp_parts[slot] && M == x.p->gp_cols[slot];
   if (*fused) g.rowsum = static_cast<float*>(x.at(gpart_at(*x.p, layer, slot)));
@@ -327,21 +330,24 @@ hipError_t colsum_into(const Ctx& x, int xtype, const void* src, int64_t ld, int
 
 // Forward of layer l for one micro-batch: input xin, saved tensors in `set`,
 // output xout (all act [T, D]).
-gpipe_status layer_forward(const Ctx& x, int set, int l, const void* xin, void* xout) {
+// (slot: the layer slot of `set` that receives the intermediates; l: the
+// layer whose weights are applied -- the same except in the forward phase's
+// one-slot scratch)
+gpipe_status layer_forward(const Ctx& x, int set, int slot, int l, const void* xin, void* xout) {
   const gpipe_cell* c = x.c;
   const Plan& p = *x.p;
   const int T = p.T, D = c->D, F = c->F, S = c->S, H = c->H, dh = D / H;
   const int64_t ldS = p.ldS;
-  void* h1 = x.at(saved_at(p, set, l, GPIPE_SAVED_H1));
-  float* st1 = static_cast<float*>(x.at(saved_at(p, set, l, GPIPE_SAVED_ST1)));
-  void* qkv = x.at(saved_at(p, set, l, GPIPE_SAVED_QKV));
-  void* P = x.at(saved_at(p, set, l, GPIPE_SAVED_P));
-  void* ctx = x.at(saved_at(p, set, l, GPIPE_SAVED_CTX));
-  void* x1 = x.at(saved_at(p, set, l, GPIPE_SAVED_X1));
-  void* h2 = x.at(saved_at(p, set, l, GPIPE_SAVED_H2));
-  float* st2 = static_cast<float*>(x.at(saved_at(p, set, l, GPIPE_SAVED_ST2)));
-  void* u = x.at(saved_at(p, set, l, GPIPE_SAVED_U));
-  void* g = x.at(saved_at(p, set, l, GPIPE_SAVED_G));
+  void* h1 = x.at(saved_at(p, set, slot, GPIPE_SAVED_H1));
+  float* st1 = static_cast<float*>(x.at(saved_at(p, set, slot, GPIPE_SAVED_ST1)));
+  void* qkv = x.at(saved_at(p, set, slot, GPIPE_SAVED_QKV));
+  void* P = x.at(saved_at(p, set, slot, GPIPE_SAVED_P));
+  void* ctx = x.at(saved_at(p, set, slot, GPIPE_SAVED_CTX));
+  void* x1 = x.at(saved_at(p, set, slot, GPIPE_SAVED_X1));
+  void* h2 = x.at(saved_at(p, set, slot, GPIPE_SAVED_H2));
+  float* st2 = static_cast<float*>(x.at(saved_at(p, set, slot, GPIPE_SAVED_ST2)));
+  void* u = x.at(saved_at(p, set, slot, GPIPE_SAVED_U));
+  void* g = x.at(saved_at(p, set, slot, GPIPE_SAVED_G));
   float* scores = static_cast<float*>(x.at(p.scores));
 
   GP_RUN(x, GPIPE_ROLE_LN1_FWD, layernorm_fwd(x.bf16, xin, h1, st1, x.wf32(l, GPIPE_LN1_G), x.wf32(l, GPIPE_LN1_B), T, D,
@@ -381,10 +387,43 @@ gpipe_status cell_forward(const Ctx& x, int set, const void* xin, void* yout) {
   for (int l = 0; l < L; ++l) {
     const void* in = l == 0 ? xin : x.at(saved_at(*x.p, set, l, GPIPE_SAVED_X));
     void* out = l == L - 1 ? yout : x.at(saved_at(*x.p, set, l + 1, GPIPE_SAVED_X));
-    gpipe_status st = layer_forward(x, set, l, in, out);
+    gpipe_status st = layer_forward(x, set, l, l, in, out);
     if (st != GPIPE_OK) return st;
   }
   return GPIPE_OK;
+}
+
+// The forward phase with re-materialization keeps nothing but the boundary
+// output, so each micro-batch needs only one layer's intermediates, reused
+// layer after layer (the layer's output overwrites its input, which is last
+// read by the out-projection's residual add).  The micro-batches are
+// independent: even ones run on the caller's stream in slot 0 of the saved
+// set, odd ones on the second stream in slot 1 (with their own split-K
+// partials), so each stream's kernels fill the CUs and launch gaps the other
+// leaves; the set is free until the backward phase re-materializes into it,
+// after the streams join.  Launches here are not role-timed (their times
+// would include the other stream's).
+gpipe_status overlapped_forward(const Ctx& cx, Streams& ss, const void* x, void* y, int M,
+                                size_t mb) {
+  const Plan& p = *cx.p;
+  const int L = cx.c->L;
+  Ctx lane[2] = {cx, cx};
+  lane[0].prof = lane[1].prof = nullptr;
+  lane[1].s = ss.s2;
+  lane[1].splitk = p.splitk2;
+  if (!ss.fork()) return GPIPE_ERR_DEVICE;  // the inputs and weights exist
+  for (int m = 0; m < M; ++m) {
+    const Ctx& z = lane[m & 1];
+    const int slot = m & 1;
+    void* xs = z.at(saved_at(p, 0, slot, GPIPE_SAVED_X));
+    for (int l = 0; l < L; ++l) {
+      const void* in = l == 0 ? cx.act(x, m * mb) : xs;
+      void* out = l == L - 1 ? cx.act(y, m * mb) : xs;
+      gpipe_status st = layer_forward(z, 0, slot, l, in, out);
+      if (st != GPIPE_OK) return st;
+    }
+  }
+  return ss.join_all() ? GPIPE_OK : GPIPE_ERR_DEVICE;
 }
 
 // Backward of layer l.  On entry r0 (f32) / a0 (act) hold the gradient w.r.t.
@@ -679,17 +718,22 @@ gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, v
     if (st != GPIPE_OK) return st;
   }
   Ctx cx{c, c->prof_mask ? c : nullptr, &p, static_cast<char*>(workspace),
-         static_cast<hipStream_t>(stream), c->prec == GPIPE_BF16};
+         static_cast<hipStream_t>(stream), c->prec == GPIPE_BF16, p.splitk};
   Streams ss{c, cx.s, c->aux};
   const size_t mb = size_t(p.T) * c->D;  // elements per micro-batch
   const float inv_denom = float(1.0 / (double(N) * c->S * c->D));
   float* msepart = static_cast<float*>(cx.at(p.msepart));
 
   // phase 1: forward, boundary output only (intermediates are overwritten)
-  for (int m = 0; m < M; ++m) {
-    const int set = remat ? 0 : m;
-    gpipe_status st = cell_forward(cx, set, cx.act(x, m * mb), cx.act(y, m * mb));
+  if (remat && p.flash && c->L >= 2) {
+    gpipe_status st = overlapped_forward(cx, ss, x, y, M, mb);
     if (st != GPIPE_OK) return st;
+  } else {
+    for (int m = 0; m < M; ++m) {
+      const int set = remat ? 0 : m;
+      gpipe_status st = cell_forward(cx, set, cx.act(x, m * mb), cx.act(y, m * mb));
+      if (st != GPIPE_OK) return st;
+    }
   }
   // phase 2: backward with re-materialization and float32 accumulation
   for (int m = 0; m < M; ++m) {
@@ -736,7 +780,7 @@ gpipe_status gpipe_apply_update(gpipe_cell* c, float lr, float decay, float eps,
       !isfinite(eps))
     return GPIPE_ERR_INVALID;
   Ctx cx{c, c->prof_mask ? c : nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream),
-         c->prec == GPIPE_BF16};
+         c->prec == GPIPE_BF16, 0};
   GP_RUN(cx, GPIPE_ROLE_RMSPROP,
          rmsprop(c->master, c->grad, c->ms, c->prec == GPIPE_BF16 ? c->w_lowp : nullptr,
                  int64_t(c->n_params), lr, decay, eps, cx.s));
