@@ -412,17 +412,20 @@ gpipe_status overlapped_forward(const Ctx& cx, Streams& ss, const void* x, void*
   lane[1].s = ss.s2;
   lane[1].splitk = p.splitk2;
   if (!ss.fork()) return GPIPE_ERR_DEVICE;  // the inputs and weights exist
-  for (int m = 0; m < M; ++m) {
-    const Ctx& z = lane[m & 1];
-    const int slot = m & 1;
-    void* xs = z.at(saved_at(p, 0, slot, GPIPE_SAVED_X));
-    for (int l = 0; l < L; ++l) {
-      const void* in = l == 0 ? cx.act(x, m * mb) : xs;
-      void* out = l == L - 1 ? cx.act(y, m * mb) : xs;
-      gpipe_status st = layer_forward(z, 0, slot, l, in, out);
-      if (st != GPIPE_OK) return st;
-    }
-  }
+  // a pair of micro-batches is enqueued layer by layer, alternating the
+  // streams, so that both always have work queued (enqueueing a whole
+  // micro-batch per stream let each run dry while the host fed the other)
+  for (int m0 = 0; m0 < M; m0 += 2)
+    for (int l = 0; l < L; ++l)
+      for (int m = m0; m < std::min(M, m0 + 2); ++m) {
+        const Ctx& z = lane[m & 1];
+        const int slot = m & 1;
+        void* xs = z.at(saved_at(p, 0, slot, GPIPE_SAVED_X));
+        const void* in = l == 0 ? cx.act(x, m * mb) : xs;
+        void* out = l == L - 1 ? cx.act(y, m * mb) : xs;
+        gpipe_status st = layer_forward(z, 0, slot, l, in, out);
+        if (st != GPIPE_OK) return st;
+      }
   return ss.join_all() ? GPIPE_OK : GPIPE_ERR_DEVICE;
 }
 
