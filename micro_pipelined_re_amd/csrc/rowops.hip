@@ -23,13 +23,17 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const T* __restrict__ x, T*
   if (row >= rows) return;
   const int nch = d >> 3;
   const T* xr = x + int64_t(row) * d;
-  float v[NV][8];
+  // the gain and shift are loaded with the row, so the output needs no
+  // second memory round trip after the two reductions
+  float v[NV][8], gm[NV][8], bt[NV][8];
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = lane + 64 * i;
     if (c < nch) {
       load8<T>(xr + c * 8, v[i]);
+      load8<float>(gamma + c * 8, gm[i]);
+      load8<float>(beta + c * 8, bt[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += v[i][e];
     }
@@ -56,7 +60,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const T* __restrict__ x, T*
     if (c < nch) {
       float o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (v[i][e] - mu) * rstd * gamma[c * 8 + e] + beta[c * 8 + e];
+      for (int e = 0; e < 8; ++e) o[e] = (v[i][e] - mu) * rstd * gm[i][e] + bt[i][e];
       store8<T>(yr + c * 8, o);
     }
   }
@@ -200,7 +204,9 @@ __global__ __launch_bounds__(256) void ln_bwd_wave_kernel(const float* __restric
     for (int e = 0; e < 8; ++e) pg[i][e] = pb[i][e] = 0.f;
   for (int row = blockIdx.x * kLnWaveRows + w; row < rows; row += gridDim.x * kLnWaveRows) {
     const float mu = stats[2 * row], rstd = stats[2 * row + 1];
-    float xh[NV][8], dxh[NV][8];
+    // the residual gradient is loaded with the other inputs (no second
+    // memory round trip after the reductions)
+    float xh[NV][8], dxh[NV][8], rv[NV][8];
     float sa = 0.f, sb = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -210,6 +216,7 @@ __global__ __launch_bounds__(256) void ln_bwd_wave_kernel(const float* __restric
         load8<T>(x + int64_t(row) * d + c * 8, xv);
         load8<float>(dh + int64_t(row) * d + c * 8, gv);
         load8<float>(gamma + c * 8, gm);
+        load8<float>(res_in + int64_t(row) * d + c * 8, rv[i]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           xh[i][e] = (xv[e] - mu) * rstd;
@@ -227,10 +234,9 @@ __global__ __launch_bounds__(256) void ln_bwd_wave_kernel(const float* __restric
     for (int i = 0; i < NV; ++i) {
       const int c = lane + 64 * i;
       if (c < nch) {
-        float rv[8], o[8];
-        load8<float>(res_in + int64_t(row) * d + c * 8, rv);
+        float o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = rv[e] + rstd * (dxh[i][e] - ma - xh[i][e] * mb);
+        for (int e = 0; e < 8; ++e) o[e] = rv[i][e] + rstd * (dxh[i][e] - ma - xh[i][e] * mb);
         store8<float>(dx_f32 + int64_t(row) * d + c * 8, o);
         store8<T>(dx_act + int64_t(row) * d + c * 8, o);
       }
