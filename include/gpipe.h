@@ -208,7 +208,17 @@ gpipe_status gpipe_cell_saved_offset(const gpipe_cell *cell, int N, int M, int r
  * dx must not overlap the workspace.  The workspace (ws_bytes >=
  * gpipe_cell_workspace_bytes) is owned by the caller; its contents on entry
  * are ignored.  Errors: GPIPE_ERR_STATE if not bound; GPIPE_ERR_INVALID for
- * bad N/M, misaligned pointers or too small a workspace. */
+ * bad N/M, misaligned pointers or too small a workspace.
+ * Streams: all work is enqueued behind what the caller has enqueued on
+ * `stream` and the call returns after enqueueing; synchronising `stream`
+ * covers the whole step.  A Transformer cell also uses a second stream of
+ * its own (created at its first step, default priority, on the device
+ * current then; a later step on another device returns GPIPE_ERR_STATE): in
+ * the forward phase (remat != 0, bf16 with head dim 64 or 128, at least two
+ * layers) it runs the odd micro-batches, in the backward phase the weight-
+ * gradient GEMMs; events order it against `stream` both ways, the weight
+ * gradients still accumulate the micro-batches in order and the step is
+ * bitwise reproducible.  A cell must not run two steps at once. */
 gpipe_status gpipe_cell_step(gpipe_cell *cell, const void *x, const void *target, void *y,
                              void *dx, int N, int M, int remat, void *workspace, size_t ws_bytes,
                              void *stream, float *loss_dev);
