@@ -699,6 +699,31 @@ __global__ __launch_bounds__(kSpecThreads, 1) void gemm_spec_kernel(GemmParams g
 // path 0: direct-to-LDS kernel with configuration DC (the specialised-wave
 // kernel for the one-workgroup-per-CU 3-stage configurations); path 1:
 // register-staged kernel with tile RC (for k not a multiple of 64).
+// Split-K sum, eight consecutive columns per thread with 16-byte accesses:
+// the partials are added in split order (0 + p0 + p1 + ..., as the
+// per-element kernel does) and the role's epilogue is applied.  For outputs
+// whose rows are multiples of 8 elements (with 16-byte aligned pointers).
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce8_kernel(GemmParams g, int splits) {
+  const int cpr = g.N / 8;  // 8-column chunks per row
+  const int64_t n = int64_t(g.M) * g.N, nch = int64_t(g.M) * cpr;
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x; c < nch; c += stride) {
+    const int row = int(c / cpr), col = int(c % cpr) * 8;
+    const int64_t e = int64_t(row) * g.N + col;
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < splits; ++p) {
+      const float4* src = reinterpret_cast<const float4*>(g.P + int64_t(p) * n + e);
+      const float4 v0 = src[0], v1 = src[1];
+      a[0] += v0.x; a[1] += v0.y; a[2] += v0.z; a[3] += v0.w;
+      a[4] += v1.x; a[5] += v1.y; a[6] += v1.z; a[7] += v1.w;
+    }
+    epi_store8<EPI>(g, row, col, a, 0, nullptr);
+  }
+}
+
+inline bool aligned16_ptr(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 template <class DC, class RC, int LA, int LB, int EPI, int ROLE>
 hipError_t launch_bf16(int path, const GemmParams& g, int batch, int splits, hipStream_t s) {
   const int bm = path == 0 ? DC::BM : RC::BM, bn = path == 0 ? DC::BN : RC::BN;
@@ -728,6 +753,15 @@ hipError_t launch_bf16(int path, const GemmParams& g, int batch, int splits, hip
   }
   if (e != hipSuccess || one) return e;
   const int64_t n = int64_t(g.M) * g.N;
+  const bool vec = g.N % 8 == 0 && g.ldc % 8 == 0 && g.ldr % 8 == 0 && g.ldu % 8 == 0 &&
+                   aligned16_ptr(g.C) && aligned16_ptr(g.P) && (!g.R || aligned16_ptr(g.R)) &&
+                   (!g.U || aligned16_ptr(g.U)) && (!g.bias || aligned16_ptr(g.bias));
+  if (vec) {
+    const int64_t want = (n / 8 + 255) / 256;
+    const int blocks = int(want < (int64_t(1) << 30) ? want : (int64_t(1) << 30));
+    return launch_timed((splitk_reduce8_kernel<EPI>), dim3(blocks), dim3(256), 0, s, false, true,
+                        g, splits);
+  }
   const int64_t want = (n + 255) / 256;
   const int blocks = int(want < 4096 ? want : 4096);
   return launch_timed((splitk_reduce_kernel<bf16_t, EPI>), dim3(blocks), dim3(256), 0, s, false,
