@@ -133,6 +133,13 @@ GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch) {
       return p;
     }
   }
+  // implicit-GEMM convolutions with at least 192 tiles of 128 x 128: the
+  // specialised-wave kernel with the gathered-operand loader
+  if ((role == GPIPE_ROLE_CONV_FWD_IMPLICIT || role == GPIPE_ROLE_CONV_DGRAD_IMPLICIT) &&
+      batch == 1 && long((M + 127) / 128) * ((N + 127) / 128) >= 192) {
+    p.cfg = CFG_128x128_SPEC;
+    return p;
+  }
   // (the convolution's weight gradient is small -- C x 9C -- and reduces over
   // every pixel of the micro-batch, so it does split)
   const bool can_split = !is_attention(role) && (!is_wgrad(role) || role == GPIPE_ROLE_CONV_WGRAD) &&

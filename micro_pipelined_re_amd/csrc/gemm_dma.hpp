@@ -447,7 +447,9 @@ template <class C, int LA, int LB, int EPI, int ROLE>
 __global__ __launch_bounds__(kSpecThreads, 1) void gemm_spec_kernel(GemmParams g) {
   constexpr int BM = C::BM, BN = C::BN, BK = 64, FM = C::FM, FN = C::FN;
   static_assert(C::BK == 64 && C::STAGES == 3, "specialised kernel: 64-deep k-tiles, 3 stages");
-  using OA = DmaOperand<BM, BK, LA>;
+  // (A may be the gathered column matrix of a 3x3 convolution)
+  using OA = typename std::conditional<LA == LAY_CONV, DmaConvOperand<BM, BK>,
+                                       DmaOperand<BM, BK, LA>>::type;
   using OB = DmaOperand<BN, BK, LB>;
   constexpr int LPT = OA::PER_WAVE + OB::PER_WAVE;  // loads per loader wave per k-tile
   static_assert(LPT * 2 < 64, "vmcnt range");
@@ -493,7 +495,8 @@ __global__ __launch_bounds__(kSpecThreads, 1) void gemm_spec_kernel(GemmParams g
     const bf16_t* B = static_cast<const bf16_t*>(g.B) + zb * g.sBb + zh * g.sBh;
     OA oa;
     OB ob;
-    oa.init(g.lda, m0, g.M, kbeg, cw, lane);
+    if constexpr (LA == LAY_CONV) oa.init(g, m0, g.M, kbeg, cw, lane);
+    else oa.init(g.lda, m0, g.M, kbeg, cw, lane);
     ob.init(g.ldb, n0, g.N, kbeg, cw, lane);
     const int pre = min(3, nkt);
     for (int t = 0; t < pre; ++t) {
@@ -732,10 +735,8 @@ hipError_t launch_bf16(int path, const GemmParams& g, int batch, int splits, hip
   const dim3 grid(tiles, splits, batch);
   const bool one = splits == 1;  // the product is the whole launch
   hipError_t e;
-  if constexpr (LA == LAY_CONV) {
-    // the gathered operand exists only on the direct-to-LDS path
-    if (path != 0) return hipErrorInvalidValue;
-    e = launch_timed((gemm_dma_kernel<DC, LA, LB, EPI, ROLE>), grid, dim3(kThreads), 0, s, true, one, g);
+  if (LA == LAY_CONV && path != 0) {
+    return hipErrorInvalidValue;  // the gathered operand exists only on the direct-to-LDS path
   } else if (path == 0) {
     if constexpr (DC::OCC == 1 && DC::BK == 64 && DC::STAGES == 3) {
       constexpr int smem = spec_smem_bytes<DC>();
