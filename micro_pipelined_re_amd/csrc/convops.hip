@@ -13,37 +13,52 @@
 namespace gp {
 
 // ------------------------------------------------------------ im2col / col2im
-template <typename T>
+template <typename T, typename I>
 __global__ __launch_bounds__(256) void im2col_kernel(const T* __restrict__ x, T* __restrict__ col,
                                                      int B, int H, int W, int C) {
-  const int cc8 = C >> 3;
-  const int64_t total = int64_t(B) * H * W * 9 * cc8;
-  const int64_t stride = int64_t(gridDim.x) * 256;
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += stride) {
-    const int cc = int(i % cc8);
-    const int64_t rest = i / cc8;
-    const int tap = int(rest % 9);
-    const int64_t p = rest / 9;
-    const int w = int(p % W), h = int((p / W) % H), b = int(p / (int64_t(W) * H));
-    const int hs = h + tap / 3 - 1, ws = w + tap % 3 - 1;
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (hs >= 0 && hs < H && ws >= 0 && ws < W)
-      load8<T>(x + ((int64_t(b) * H + hs) * W + ws) * C + cc * 8, v);
-    store8<T>(col + p * 9 * C + tap * C + cc * 8, v);
+  // one 8-element chunk per thread, copied as raw 16-byte words (no
+  // conversion); I is the index type (32-bit whenever the count fits)
+  constexpr int WORDS = sizeof(T) * 8 / 16;
+  const I cc8 = I(C >> 3);
+  const I total = I(B) * H * W * 9 * cc8;
+  const I i = I(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= total) return;
+  const I cc = i % cc8;
+  const I rest = i / cc8;
+  const int tap = int(rest % 9);
+  const I p = rest / 9;
+  const int w = int(p % W), h = int((p / W) % H);
+  const I b = p / (I(W) * H);
+  const int hs = h + tap / 3 - 1, ws = w + tap % 3 - 1;
+  uint4 v[WORDS];
+#pragma unroll
+  for (int k = 0; k < WORDS; ++k) v[k] = make_uint4(0, 0, 0, 0);
+  if (hs >= 0 && hs < H && ws >= 0 && ws < W) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + ((int64_t(b) * H + hs) * W + ws) * C + cc * 8);
+#pragma unroll
+    for (int k = 0; k < WORDS; ++k) v[k] = src[k];
   }
+  uint4* dst = reinterpret_cast<uint4*>(col + int64_t(p) * 9 * C + tap * C + cc * 8);
+#pragma unroll
+  for (int k = 0; k < WORDS; ++k) dst[k] = v[k];
 }
 
 hipError_t im2col(bool bf16, const void* x, void* col, int B, int H, int W, int C, hipStream_t s) {
   const int64_t total = int64_t(B) * H * W * 9 * (C / 8);
   if (total == 0) return hipSuccess;
-  const int64_t want = (total + 255) / 256;
-  const int blocks = int(want < 16384 ? want : 16384);
-  if (bf16)
-    hipLaunchKernelGGL(im2col_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const bf16_t*>(x), static_cast<bf16_t*>(col), B, H, W, C);
-  else
-    hipLaunchKernelGGL(im2col_kernel<float>, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const float*>(x), static_cast<float*>(col), B, H, W, C);
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const bool small = total < (int64_t(1) << 31);
+#define GP_IM2COL(T, I) hipLaunchKernelGGL((im2col_kernel<T, I>), dim3(unsigned(blocks)), dim3(256), 0, s, \
+                                           static_cast<const T*>(x), static_cast<T*>(col), B, H, W, C)
+  if (bf16) {
+    if (small) GP_IM2COL(bf16_t, uint32_t);
+    else GP_IM2COL(bf16_t, uint64_t);
+  } else {
+    if (small) GP_IM2COL(float, uint32_t);
+    else GP_IM2COL(float, uint64_t);
+  }
+#undef GP_IM2COL
   return hipGetLastError();
 }
 
@@ -161,10 +176,11 @@ __global__ __launch_bounds__(256) void bn_moments_kernel(const T* __restrict__ x
   }
 }
 
-// Block: 8 channels x 32 chunk groups; each group adds every 32nd chunk, the
-// groups are then combined by a fixed tree.  stats = (mean, rstd); rec
-// (optional) = (mean, biased variance).
-constexpr int kMergeCh = 8, kMergeGroups = 32;
+// Block: 2 channels x 128 chunk groups; each group adds every 128th chunk,
+// the groups are then combined by a fixed tree.  stats = (mean, rstd); rec
+// (optional) = (mean, biased variance).  (With 8 channels x 32 groups a
+// 256-channel merge ran on 32 workgroups: 10.4 us for 512 chunks.)
+constexpr int kMergeCh = 2, kMergeGroups = 128;
 
 __device__ __forceinline__ float merge_tree(float v, float (*red)[kMergeCh + 1], int g, int cl) {
   red[g][cl] = v;
