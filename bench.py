@@ -136,6 +136,7 @@ def conv_role_work(cfg, n, m):
     return {
         "conv_fwd": ("mfma", g), "conv_dgrad": ("mfma", g), "conv_wgrad": ("mfma", g),
         "conv_fwd_implicit": ("mfma", g), "conv_dgrad_implicit": ("mfma", g),
+        "conv_wgrad_implicit": ("mfma", g),
         # im2col: read the image once, write the nine shifted copies
         "im2col": ("hbm", P * C * eb * 10),
         # col2im: read the f32 column gradient (and the f32 residual), write f32 (+ act)

@@ -262,8 +262,10 @@ typedef enum {
   GPIPE_ROLE_ATTN_FWD, GPIPE_ROLE_ATTN_DELTA, GPIPE_ROLE_ATTN_DKDV, GPIPE_ROLE_ATTN_DQ,
   /* conv cells in bf16 with channels a multiple of 64: implicit-GEMM
    * convolution (the 3 x 3 neighbourhood gathered by the GEMM's loads) and the
-   * input gradient as the convolution of dz with tap-flipped weights */
-  GPIPE_ROLE_CONV_FWD_IMPLICIT, GPIPE_ROLE_CONV_DGRAD_IMPLICIT,
+   * input gradient as the convolution of dz with tap-flipped weights; the
+   * weight gradient with the neighbourhood gathered along the pixels (when a
+   * micro-batch's pixel count is a multiple of 64 below 2^21) */
+  GPIPE_ROLE_CONV_FWD_IMPLICIT, GPIPE_ROLE_CONV_DGRAD_IMPLICIT, GPIPE_ROLE_CONV_WGRAD_IMPLICIT,
   GPIPE_N_ROLES
 } gpipe_role;
 

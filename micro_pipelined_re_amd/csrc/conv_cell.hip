@@ -15,7 +15,8 @@ namespace {
 //   sets:  remat ? 1 : M micro-batch sets, each L blocks of the saved tensors
 //          of gpipe_conv_saved (block 0 has no X slot in use)
 //   yre:   output of the re-materialized forward [P, C] (remat only)
-//   col:   im2col matrix [P, 9C] (act);  dcol: its gradient [P, 9C] (f32, explicit path)
+//   col:   im2col matrix [P, 9C] (act; explicit weight gradient and explicit path)
+//   dcol:  its gradient [P, 9C] (f32, explicit path)
 //   wflip: tap-flipped transposed weights [L][2][C][9][C] (implicit path)
 //   r0:    residual-stream gradient [P, C] (f32);  r1: ReLU-input gradient (f32)
 //   dz:    BN input gradient [P, C] (act, GEMM operand)
@@ -24,6 +25,7 @@ namespace {
 struct CPlan {
   int N, M, B;
   bool implicit;  // bf16, channels a multiple of 64: implicit-GEMM convolutions
+  bool implicit_wgrad;  // and the weight gradient too: pixels a multiple of 64, below 2^21
   int64_t P;  // pixels per micro-batch
   size_t eb;
   size_t saved_off[GPIPE_CONV_N_SAVED], saved_bytes[GPIPE_CONV_N_SAVED];
@@ -63,8 +65,10 @@ bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
     return at;
   };
   p->implicit = c->prec == GPIPE_BF16 && C % 64 == 0;
+  p->implicit_wgrad = p->implicit && P % 64 == 0 && P < (size_t(1) << 21) &&
+                      (P + 64) * C < (size_t(1) << 31);
   p->yre = take(remat ? P * C * eb : 0);
-  p->col = take(P * 9 * C * eb);                    // weight gradients (and the explicit path)
+  p->col = take(p->implicit_wgrad ? 0 : P * 9 * C * eb);
   p->dcol = take(p->implicit ? 0 : P * 9 * C * 4);
   p->wflip = take(p->implicit ? size_t(c->L) * 2 * 9 * C * C * 2 : 0);
   p->r0 = take(P * C * 4);
@@ -81,7 +85,8 @@ bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
                               gemm_partial_floats(GPIPE_ROLE_CONV_DGRAD, bf, Pi, 9 * Ci, Ci, 1),
                               gemm_partial_floats(GPIPE_ROLE_CONV_WGRAD, bf, Ci, 9 * Ci, Pi, 1),
                               gemm_partial_floats(GPIPE_ROLE_CONV_FWD_IMPLICIT, bf, Pi, Ci, 9 * Ci, 1),
-                              gemm_partial_floats(GPIPE_ROLE_CONV_DGRAD_IMPLICIT, bf, Pi, Ci, 9 * Ci, 1)});
+                              gemm_partial_floats(GPIPE_ROLE_CONV_DGRAD_IMPLICIT, bf, Pi, Ci, 9 * Ci, 1),
+                              gemm_partial_floats(GPIPE_ROLE_CONV_WGRAD_IMPLICIT, bf, Ci, 9 * Ci, Pi, 1)});
   p->splitk = take(sk * 4);
   p->total = o;
   return true;
@@ -154,6 +159,33 @@ hipError_t cconv(const CCtx& x, int role, const void* img, const void* w, void* 
   return gemm(true, role, g, 1, x.s);
 }
 
+// Weight gradient of a convolution: grad (+)= dz^T im2col(img), [C][9C] f32.
+gpipe_status cwgrad(const CCtx& x, const void* img, const void* dz, float* grad, int beta) {
+  const gpipe_cell* c = x.c;
+  const int C = c->C;
+  const int P = int(x.p->P);
+  if (!x.p->implicit_wgrad) {
+    void* col = x.at(x.p->col);
+    GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, img, col, x.p->B, c->Hc, c->Wc, C, x.s));
+    GP_RUN(x, GPIPE_ROLE_CONV_WGRAD,
+           cmm(x, GPIPE_ROLE_CONV_WGRAD, C, 9 * C, P, dz, C, col, 9 * C, grad, 9 * C, beta));
+    return GPIPE_OK;
+  }
+  GemmParams g;
+  memset(&g, 0, sizeof(g));
+  g.hdiv = 1;
+  g.alpha = 1.0f;
+  g.M = C; g.N = 9 * C; g.K = P;
+  g.A = dz; g.lda = C;
+  g.B = img; g.ldb = 9 * C;
+  g.C = grad; g.ldc = 9 * C;
+  g.beta = beta;
+  g.conv_h = c->Hc; g.conv_w = c->Wc; g.conv_c = C;
+  g.P = x.f(x.p->splitk);
+  GP_RUN(x, GPIPE_ROLE_CONV_WGRAD_IMPLICIT, gemm(true, GPIPE_ROLE_CONV_WGRAD_IMPLICIT, g, 1, x.s));
+  return GPIPE_OK;
+}
+
 // One block forward of one micro-batch; rec (nullable) receives the BN
 // moments [2][2][C] of this block (forward phase only).
 gpipe_status block_forward(const CCtx& x, int set, int l, const void* xin, void* xout, float* rec) {
@@ -218,7 +250,6 @@ gpipe_status block_backward(const CCtx& x, int set, int l, const void* xin, int 
   const void* r = x.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_R));
   const void* z = x.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_Z));
   const float* st2 = x.f(csaved_at(p, set, l, GPIPE_CONV_SAVED_ST2));
-  void* col = x.at(p.col);
   float* dcol = x.f(p.dcol);
   float* r0 = x.f(p.r0);
   float* r1 = x.f(p.r1);
@@ -232,9 +263,10 @@ gpipe_status block_backward(const CCtx& x, int set, int l, const void* xin, int 
   GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(part, nch, 2 * C, 2 * C, x.grad(l, GPIPE_CONV_BN2_G),
                                                beta, x.s));
   // z = conv(r, W2)
-  GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, r, col, B, H, W, C, x.s));
-  GP_RUN(x, GPIPE_ROLE_CONV_WGRAD, cmm(x, GPIPE_ROLE_CONV_WGRAD, C, 9 * C, int(P), dz, C, col,
-                                       9 * C, x.grad(l, GPIPE_CONV_W2), 9 * C, beta));
+  {
+    const gpipe_status st = cwgrad(x, r, dz, x.grad(l, GPIPE_CONV_W2), beta);
+    if (st != GPIPE_OK) return st;
+  }
   if (p.implicit) {
     GP_RUN(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT,
            cconv(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT, dz, x.flipped(l, 1), r1, 0));
@@ -249,9 +281,10 @@ gpipe_status block_backward(const CCtx& x, int set, int l, const void* xin, int 
   GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(part, nch, 2 * C, 2 * C, x.grad(l, GPIPE_CONV_BN1_G),
                                                beta, x.s));
   // a = conv(x, W1); the residual gradient r0 is added in col2im (in place)
-  GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, xin, col, B, H, W, C, x.s));
-  GP_RUN(x, GPIPE_ROLE_CONV_WGRAD, cmm(x, GPIPE_ROLE_CONV_WGRAD, C, 9 * C, int(P), dz, C, col,
-                                       9 * C, x.grad(l, GPIPE_CONV_W1), 9 * C, beta));
+  {
+    const gpipe_status st = cwgrad(x, xin, dz, x.grad(l, GPIPE_CONV_W1), beta);
+    if (st != GPIPE_OK) return st;
+  }
   if (p.implicit) {
     // the residual gradient already in r0 gets the convolution's input gradient added
     GP_RUN(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT,
@@ -309,7 +342,7 @@ gpipe_status conv_gemm_plan(const gpipe_cell* c, int N, int M, int role, int* ti
   switch (role) {
     case GPIPE_ROLE_CONV_FWD: m = P; n = C; k = 9 * C; break;
     case GPIPE_ROLE_CONV_DGRAD: m = P; n = 9 * C; k = C; break;
-    case GPIPE_ROLE_CONV_WGRAD: m = C; n = 9 * C; k = P; break;
+    case GPIPE_ROLE_CONV_WGRAD: case GPIPE_ROLE_CONV_WGRAD_IMPLICIT: m = C; n = 9 * C; k = P; break;
     case GPIPE_ROLE_CONV_FWD_IMPLICIT: case GPIPE_ROLE_CONV_DGRAD_IMPLICIT:
       m = P; n = C; k = 9 * C; break;
     default:

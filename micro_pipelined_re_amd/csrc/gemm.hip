@@ -21,7 +21,7 @@ bool is_wgrad(int role) {
 bool is_conv(int role) {
   return role == GPIPE_ROLE_CONV_FWD || role == GPIPE_ROLE_CONV_DGRAD ||
          role == GPIPE_ROLE_CONV_WGRAD || role == GPIPE_ROLE_CONV_FWD_IMPLICIT ||
-         role == GPIPE_ROLE_CONV_DGRAD_IMPLICIT;
+         role == GPIPE_ROLE_CONV_DGRAD_IMPLICIT || role == GPIPE_ROLE_CONV_WGRAD_IMPLICIT;
 }
 // B operand k-contiguous (the weight of a forward linear layer)
 bool b_k_contiguous(int role) {
@@ -36,7 +36,7 @@ int group_of(int role) {
     case GPIPE_ROLE_QKV_DGRAD: return 1;
     case GPIPE_ROLE_CONV_FWD: case GPIPE_ROLE_CONV_FWD_IMPLICIT: return 0;
     case GPIPE_ROLE_CONV_DGRAD: case GPIPE_ROLE_CONV_DGRAD_IMPLICIT: return 1;
-    case GPIPE_ROLE_CONV_WGRAD: return 2;
+    case GPIPE_ROLE_CONV_WGRAD: case GPIPE_ROLE_CONV_WGRAD_IMPLICIT: return 2;
   }
   return is_wgrad(role) ? 2 : is_attention(role) ? 3 : -1;
 }
@@ -51,7 +51,8 @@ bool dma_ok(int role, const GemmParams& g) {
   if (g.K % 64 || g.M < 8 || g.N < 8 || g.N % 8 || g.ldc % 8 || g.ldr % 8 || g.ldu % 8) return false;
   const bool a_mn = role == GPIPE_ROLE_FFN2_WGRAD || role == GPIPE_ROLE_FFN1_WGRAD ||
                     role == GPIPE_ROLE_OUT_WGRAD || role == GPIPE_ROLE_QKV_WGRAD ||
-                    role == GPIPE_ROLE_DV || role == GPIPE_ROLE_DK || role == GPIPE_ROLE_CONV_WGRAD;
+                    role == GPIPE_ROLE_DV || role == GPIPE_ROLE_DK || role == GPIPE_ROLE_CONV_WGRAD ||
+                    role == GPIPE_ROLE_CONV_WGRAD_IMPLICIT;
   const bool b_mn = role != GPIPE_ROLE_QKV_FWD && role != GPIPE_ROLE_SCORES_FWD &&
                     role != GPIPE_ROLE_OUT_FWD && role != GPIPE_ROLE_FFN1_FWD &&
                     role != GPIPE_ROLE_FFN2_FWD && role != GPIPE_ROLE_DP &&
@@ -60,6 +61,12 @@ bool dma_ok(int role, const GemmParams& g) {
   const bool conv = role == GPIPE_ROLE_CONV_FWD_IMPLICIT || role == GPIPE_ROLE_CONV_DGRAD_IMPLICIT;
   // a gathered operand needs every 64-deep k-tile inside one tap
   if (conv && (g.conv_c % 64 || g.K != 9 * g.conv_c)) return false;
+  // gathered along k: eight-column chunks inside one tap, pixel indices below
+  // 2^21, element offsets within 32 bits
+  if (role == GPIPE_ROLE_CONV_WGRAD_IMPLICIT &&
+      (g.conv_c % 8 || g.N != 9 * g.conv_c || g.K >= (1 << 21) || g.conv_h < 1 || g.conv_w < 1 ||
+       g.K % (g.conv_h * g.conv_w) || int64_t(g.K + 64) * g.conv_c >= (int64_t(1) << 31)))
+    return false;
   if (a_mn && g.M % 8) return false;
   if (b_mn && g.N % 8) return false;
   return true;
@@ -138,6 +145,15 @@ GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch) {
   if ((role == GPIPE_ROLE_CONV_FWD_IMPLICIT || role == GPIPE_ROLE_CONV_DGRAD_IMPLICIT) &&
       batch == 1 && long((M + 127) / 128) * ((N + 127) / 128) >= 192) {
     p.cfg = CFG_128x128_SPEC;
+    return p;
+  }
+  // the weight gradient with the gathered column matrix: C x 9C outputs
+  // reduced over every pixel of the micro-batch, split to about one
+  // workgroup per CU
+  if (role == GPIPE_ROLE_CONV_WGRAD_IMPLICIT) {
+    p.cfg = CFG_128x128_SPEC;
+    const long tiles = long((M + 127) / 128) * ((N + 127) / 128) * batch;
+    if (tiles < kCUs && K >= 1024) split_of(int(std::max(1L, kCUs / tiles)), 512);
     return p;
   }
   // (the convolution's weight gradient is small -- C x 9C -- and reduces over

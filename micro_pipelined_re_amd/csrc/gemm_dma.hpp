@@ -196,6 +196,75 @@ struct DmaOperand {
   }
 };
 
+// B operand gathered from an NHWC image with the pixels along k
+// (LAY_CONV_MN): stored like an m-contiguous tile.  Each load's lane owns
+// eight columns (channels c..c+7 of one tap) and one k-row.  The columns fix
+// the tap; the pixel of a k-row moves by 64 per k-tile, and its (h, w) are
+// carried along: found once by two divisions (products with rounded
+// reciprocals, exact for pixel indices below 2^21: the rounded quotient of
+// (p + 0.5) / W lies within 2^-23 relative of the true one, which is at
+// least 0.5 / W away from an integer), then advanced by (64 / W) mod H rows
+// and 64 mod W columns with one carry each.  issue() must be called for the
+// k-tiles 0, 1, 2, ... in order.
+template <int ROWS, int BK>
+struct DmaConvMnOperand : DmaOperand<ROWS, BK, LAY_MN> {
+  static_assert(BK == 64, "conv operands use 64-deep k-tiles");
+  static constexpr int PER_WAVE = DmaOperand<ROWS, BK, LAY_MN>::PER_WAVE;
+  int src[PER_WAVE];               // element offset of the shifted pixel's channels
+  int h[PER_WAVE], w[PER_WAVE];    // image row and column of the k-row's pixel
+  int hlo[PER_WAVE], wlo[PER_WAVE];        // the tap's pixel is inside the image
+  unsigned hcnt[PER_WAVE], wcnt[PER_WAVE];  // iff h - hlo < hcnt and w - wlo < wcnt
+  int H, W, step, dh64, dw64;
+
+  __device__ __forceinline__ void init(const GemmParams& g, int col0, int cols_total, int kb,
+                                       int wave, int lane) {
+    H = g.conv_h;
+    W = g.conv_w;
+    const int C = g.conv_c;
+    step = BK * C;
+    dh64 = (BK / W) % H;
+    dw64 = BK % W;
+    const float inv_w = 1.0f / float(W), inv_h = 1.0f / float(H);
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q) {
+      const int blk = q * 4 + wave;
+      const int byte = blk * 1024 + lane * 16;
+      const int r = byte / (ROWS * 2);
+      const int within = byte % (ROWS * 2);
+      const int gq = within >> 5, hf = (within >> 4) & 1;
+      const int m = ((gq ^ mn_swz<ROWS>(r)) << 4) + hf * 8;
+      const int gn = min(col0 + m, cols_total - 8);
+      const int tap = gn / C;
+      const int dh = tap / 3 - 1, dw = tap - (tap / 3) * 3 - 1;
+      const int p = kb + r;
+      const int pw = int((float(p) + 0.5f) * inv_w);  // p / W
+      const int ph = int((float(pw) + 0.5f) * inv_h);  // (p / W) / H
+      w[q] = p - pw * W;
+      h[q] = pw - ph * H;
+      src[q] = (p + dh * W + dw) * C + (gn - tap * C);
+      hlo[q] = dh < 0 ? 1 : 0;
+      wlo[q] = dw < 0 ? 1 : 0;
+      hcnt[q] = unsigned(H - (dh != 0 ? 1 : 0));
+      wcnt[q] = unsigned(W - (dw != 0 ? 1 : 0));
+    }
+  }
+
+  __device__ __forceinline__ void issue(const bf16_t* img, int, bf16_t* stage, int wave) {
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q) {
+      // (both tests evaluated: a select, no branch)
+      const bool in = (unsigned(h[q] - hlo[q]) < hcnt[q]) & (unsigned(w[q] - wlo[q]) < wcnt[q]);
+      dma16(in ? img + src[q] : g_conv_zero, stage + (q * 4 + wave) * 512);
+      src[q] += step;
+      w[q] += dw64;
+      const int carry = w[q] >= W ? 1 : 0;
+      w[q] -= carry * W;
+      h[q] += dh64 + carry;
+      if (h[q] >= H) h[q] -= H;
+    }
+  }
+};
+
 // Waits until at most n (<= MAXN) younger k-tiles of LPT loads each are in flight.
 template <int LPT, int MAXN>
 __device__ __forceinline__ void wait_tiles(int n) {
@@ -300,7 +369,8 @@ __global__ __launch_bounds__(kThreads, C::OCC) void gemm_dma_kernel(GemmParams g
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, STAGES = C::STAGES, FM = C::FM, FN = C::FN;
   using OA = typename std::conditional<LA == LAY_CONV, DmaConvOperand<BM, BK>,
                                        DmaOperand<BM, BK, LA>>::type;
-  using OB = DmaOperand<BN, BK, LB>;
+  using OB = typename std::conditional<LB == LAY_CONV_MN, DmaConvMnOperand<BN, BK>,
+                                       DmaOperand<BN, BK, LB>>::type;
   static_assert(LPT_CHECK(OA::PER_WAVE + OB::PER_WAVE, STAGES), "vmcnt range");
   constexpr int LPT = OA::PER_WAVE + OB::PER_WAVE;  // load instructions per wave per k-tile
   // pipeline stages; after the k loop the same memory holds the fp32 tile
@@ -327,7 +397,8 @@ __global__ __launch_bounds__(kThreads, C::OCC) void gemm_dma_kernel(GemmParams g
   OB ob;
   if constexpr (LA == LAY_CONV) oa.init(g, m0, g.M, kbeg, wave, lane);
   else oa.init(g.lda, m0, g.M, kbeg, wave, lane);
-  ob.init(g.ldb, n0, g.N, kbeg, wave, lane);
+  if constexpr (LB == LAY_CONV_MN) ob.init(g, n0, g.N, kbeg, wave, lane);
+  else ob.init(g.ldb, n0, g.N, kbeg, wave, lane);
   auto sa = [&](int st) { return smem + st * (BM + BN) * BK; };
   auto sb = [&](int st) { return smem + st * (BM + BN) * BK + BM * BK; };
 
@@ -450,10 +521,11 @@ __global__ __launch_bounds__(kSpecThreads, 1) void gemm_spec_kernel(GemmParams g
   // (A may be the gathered column matrix of a 3x3 convolution)
   using OA = typename std::conditional<LA == LAY_CONV, DmaConvOperand<BM, BK>,
                                        DmaOperand<BM, BK, LA>>::type;
-  using OB = DmaOperand<BN, BK, LB>;
+  using OB = typename std::conditional<LB == LAY_CONV_MN, DmaConvMnOperand<BN, BK>,
+                                       DmaOperand<BN, BK, LB>>::type;
   constexpr int LPT = OA::PER_WAVE + OB::PER_WAVE;  // loads per loader wave per k-tile
   static_assert(LPT * 2 < 64, "vmcnt range");
-  constexpr int RA = LA == LAY_MN ? 2 : 1, RB = LB == LAY_MN ? 2 : 1;  // LDS reads per fragment
+  constexpr int RA = LA == LAY_MN ? 2 : 1, RB = LB == LAY_MN || LB == LAY_CONV_MN ? 2 : 1;  // LDS reads per fragment
   constexpr int STAGE = (BM + BN) * BK, TP = BN + 4;
   // Weight gradients can also sum A over k (the bias gradient).  The loader
   // waves do it from the LDS tiles they loaded, with the MFMA fragment reads
@@ -467,13 +539,12 @@ __global__ __launch_bounds__(kSpecThreads, 1) void gemm_spec_kernel(GemmParams g
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, cw = wave & 3;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, BM, BN, &tm, &tn);
+  int tm, tn, split;
+  grid_tile(tiles_m, tiles_n, BM, BN, &tm, &tn, &split);
   const int m0 = tm * BM, n0 = tn * BN;
   const int z = blockIdx.z, zb = z / g.hdiv, zh = z % g.hdiv;
   int kbeg, kend;
   if (!causal_range(g, m0, n0, BM, BK, &kbeg, &kend)) return;
-  const int split = blockIdx.y;
   if (gridDim.y > 1) {
     kbeg = max(kbeg, split * g.kchunk);
     kend = min(kend, (split + 1) * g.kchunk);
@@ -497,7 +568,8 @@ __global__ __launch_bounds__(kSpecThreads, 1) void gemm_spec_kernel(GemmParams g
     OB ob;
     if constexpr (LA == LAY_CONV) oa.init(g, m0, g.M, kbeg, cw, lane);
     else oa.init(g.lda, m0, g.M, kbeg, cw, lane);
-    ob.init(g.ldb, n0, g.N, kbeg, cw, lane);
+    if constexpr (LB == LAY_CONV_MN) ob.init(g, n0, g.N, kbeg, cw, lane);
+    else ob.init(g.ldb, n0, g.N, kbeg, cw, lane);
     const int pre = min(3, nkt);
     for (int t = 0; t < pre; ++t) {
       oa.issue(A, t, sa(t), cw);
@@ -735,8 +807,8 @@ hipError_t launch_bf16(int path, const GemmParams& g, int batch, int splits, hip
   const dim3 grid(tiles, splits, batch);
   const bool one = splits == 1;  // the product is the whole launch
   hipError_t e;
-  if (LA == LAY_CONV && path != 0) {
-    return hipErrorInvalidValue;  // the gathered operand exists only on the direct-to-LDS path
+  if ((LA == LAY_CONV || LB == LAY_CONV_MN) && path != 0) {
+    return hipErrorInvalidValue;  // the gathered operands exist only on the direct-to-LDS path
   } else if (path == 0) {
     if constexpr (DC::OCC == 1 && DC::BK == 64 && DC::STAGES == 3) {
       constexpr int smem = spec_smem_bytes<DC>();

@@ -130,6 +130,30 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int b
   *tn = (xcd % (8 / best)) * rn + j / rm;
 }
 
+// Tile and k-split of a workgroup.  Workgroups go to the 8 XCDs round-robin
+// by linear id (x fastest).  Unsplit, or split with a tile count that is a
+// multiple of 8 (every split of a tile then shares its XCD), tile_of places
+// the tiles.  Otherwise the linear ids are renumbered so that each XCD holds
+// one contiguous run of (split, tile) pairs, split-major: the tiles of a
+// split, which read the same k-range of A (and of a gathered B), share one L2.
+__device__ __forceinline__ void grid_tile(int tiles_m, int tiles_n, int bm, int bn, int* tm,
+                                          int* tn, int* split) {
+  const int tiles = tiles_m * tiles_n;
+  if (gridDim.y == 1 || tiles % 8 == 0) {
+    tile_of(blockIdx.x, tiles_m, tiles_n, bm, bn, tm, tn);
+    *split = blockIdx.y;
+    return;
+  }
+  const int n = tiles * int(gridDim.y);
+  const int lin = int(blockIdx.y) * tiles + int(blockIdx.x);
+  const int xcd = lin % 8, i = lin / 8;
+  const int v = xcd * (n / 8) + min(xcd, n % 8) + i;  // XCD xcd owns (n - xcd + 7) / 8 ids
+  *split = v / tiles;
+  const int t = v % tiles;
+  *tm = t % tiles_m;
+  *tn = t / tiles_m;
+}
+
 // ---------------------------------------------------------------- bf16 kernel
 template <int BM_, int BN_>
 struct Cfg {
@@ -559,6 +583,8 @@ GP_SPEC(GPIPE_ROLE_CONV_WGRAD, LAY_MN, LAY_MN, EPI_ACC_F32)
 // the input gradient (+)= im2col(dz) Wflip^T, Wflip the tap-flipped transposed weights
 GP_SPEC(GPIPE_ROLE_CONV_FWD_IMPLICIT, LAY_CONV, LAY_K, EPI_STORE)
 GP_SPEC(GPIPE_ROLE_CONV_DGRAD_IMPLICIT, LAY_CONV, LAY_K, EPI_ACC_F32)
+// and the weight gradient G (+)= da^T im2col(x), the column matrix gathered along k
+GP_SPEC(GPIPE_ROLE_CONV_WGRAD_IMPLICIT, LAY_MN, LAY_CONV_MN, EPI_ACC_F32)
 #undef GP_SPEC
 
 template <int BM, int BN, int BK, int ST, int OCC> struct DCfg;
@@ -576,6 +602,14 @@ hipError_t launch_role(int path, int cfg, const GemmParams& g, int batch, int sp
     if (cfg != CFG_128x128_K64) return hipErrorInvalidValue;
     return launch_bf16<DCfg<128, 128, 64, 2, 2>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch,
                                                                                 splits, s);
+  } else if constexpr (R::LB == LAY_CONV_MN) {
+    // the specialised-wave tile configurations for the gathered B operand
+    switch (cfg) {
+      case CFG_256x128_K64: return launch_bf16<DCfg<256, 128, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
+      case CFG_128x128_SPEC: return launch_bf16<DCfg<128, 128, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
+      case CFG_128x64_SPEC: return launch_bf16<DCfg<128, 64, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
+    }
+    return hipErrorInvalidValue;
   } else {
   switch (cfg) {
     case CFG_256x128_K64: return launch_bf16<DCfg<256, 128, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);

@@ -10,6 +10,8 @@ hipError_t gemm_group_wgrad(int role, int path, int cfg, const GemmParams& g, in
     case GPIPE_ROLE_OUT_WGRAD: return launch_role<GPIPE_ROLE_OUT_WGRAD>(path, cfg, g, batch, splits, s);
     case GPIPE_ROLE_QKV_WGRAD: return launch_role<GPIPE_ROLE_QKV_WGRAD>(path, cfg, g, batch, splits, s);
     case GPIPE_ROLE_CONV_WGRAD: return launch_role<GPIPE_ROLE_CONV_WGRAD>(path, cfg, g, batch, splits, s);
+    case GPIPE_ROLE_CONV_WGRAD_IMPLICIT:
+      return launch_role<GPIPE_ROLE_CONV_WGRAD_IMPLICIT>(path, cfg, g, batch, splits, s);
   }
   return hipErrorInvalidValue;
 }

@@ -9,7 +9,10 @@ namespace gp {
 // LAY_CONV: the A operand is the 3 x 3 im2col matrix of an NHWC image that is
 // never materialised: row p, column tap*C + c reads pixel p shifted by the
 // tap's (dh, dw), or zero outside the image (A only, k-tiles within one tap).
-enum { LAY_K = 0, LAY_MN = 1, LAY_CONV = 2 };
+// LAY_CONV_MN: the B operand is that matrix with the pixels along k
+// (B(k, n) = im2col[k][n], n = tap*C + c), for the convolution's weight
+// gradient; the k extent (pixels) must stay below 2^21.
+enum { LAY_K = 0, LAY_MN = 1, LAY_CONV = 2, LAY_CONV_MN = 3 };
 
 enum {
   EPI_STORE = 0,       // C(act) = alpha * acc

@@ -34,7 +34,7 @@ ROLES = ("ln1_fwd", "qkv_fwd", "scores_fwd", "softmax_fwd", "pv_fwd", "out_fwd",
          "qkv_wgrad", "ln1_bwd", "bias_grad", "norm_grad", "loss_reduce", "rmsprop",
          "conv_fwd", "conv_dgrad", "conv_wgrad", "im2col", "col2im", "bn_stats", "bn_apply",
          "bn_bwd", "bn_running", "attn_fwd", "attn_delta", "attn_dkdv", "attn_dq",
-         "conv_fwd_implicit", "conv_dgrad_implicit")
+         "conv_fwd_implicit", "conv_dgrad_implicit", "conv_wgrad_implicit")
 
 
 class GpipeError(RuntimeError):

@@ -274,6 +274,23 @@ def test_conv_ragged_bf16_matches_oracle():
     check_conv(cfg)
 
 
+def test_conv_bf16_gathered_weight_gradient_odd_images():
+    """5 x 7 images, 64 channels, 2240 pixels per micro-batch (a multiple of
+    64): every GEMM gathers its column matrix, the weight gradient's k-tiles
+    straddle rows and images."""
+    cfg = configs.CONV_SMALL.with_(name="conv_odd_bf16", channels=64, height=5, width=7,
+                                   batch=128, micro=2)
+    check_conv(cfg)
+
+
+def test_conv_bf16_gathered_convolutions_explicit_weight_gradient():
+    """105 pixels per micro-batch: implicit convolutions, the weight gradient
+    through the column matrix."""
+    cfg = configs.CONV_SMALL.with_(name="conv_mixed_bf16", channels=64, height=5, width=7,
+                                   batch=6, micro=2)
+    check_conv(cfg)
+
+
 def test_conv_single_pixel_images():
     """1 x 1 images: only the centre tap of each 3 x 3 kernel sees data."""
     cfg = configs.CONV_TINY.with_(name="conv_1x1_fp32", height=1, width=1, batch=16, micro=2)

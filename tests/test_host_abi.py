@@ -334,6 +334,22 @@ def test_conv_saved_offsets_and_workspace_scaling():
         gpipe.gpipe_cell_destroy(h)
 
 
+def test_conv_workspace_drops_the_column_matrix_with_the_gathered_weight_gradient():
+    """bf16, channels a multiple of 64 and pixels per micro-batch a multiple of
+    64: no im2col matrix [P, 9C] in the workspace; with 105 pixels per
+    micro-batch the weight gradient takes the column matrix again."""
+    def ws(h, w, n, m):
+        hd = gpipe.gpipe_conv_cell_create(2, 64, h, w, 0.9, gpipe.GPIPE_BF16)
+        try:
+            return gpipe.gpipe_cell_workspace_bytes(hd, n, m, True)
+        finally:
+            gpipe.gpipe_cell_destroy(hd)
+    row = 9 * 64 * 2                         # one pixel's column-matrix row, bf16
+    a = ws(8, 8, 4, 4)                       # 64 pixels: gathered
+    b = ws(5, 7, 6, 2)                       # 105 pixels: explicit
+    assert b - a >= 105 * row
+
+
 def test_conv_gemm_plan_of_the_workload():
     cfg = configs.CONV_CELL
     h = gpipe.gpipe_conv_cell_create(cfg.blocks, cfg.channels, cfg.height, cfg.width, 0.9,
@@ -342,6 +358,9 @@ def test_conv_gemm_plan_of_the_workload():
         R = {n: i for i, n in enumerate(gpipe.ROLES)}
         # weight gradient: [256 x 2304] reduced over 16384 pixels -> split-K
         assert gpipe.gpipe_cell_gemm_plan(h, cfg.batch, cfg.micro, R["conv_wgrad"])[2] > 1
+        # the gathered weight gradient: 128 x 128 tiles, seven splits (252 workgroups)
+        assert gpipe.gpipe_cell_gemm_plan(h, cfg.batch, cfg.micro,
+                                          R["conv_wgrad_implicit"]) == (128, 128, 7)
         assert gpipe.gpipe_cell_gemm_plan(h, cfg.batch, cfg.micro, R["conv_fwd"])[:2] == (128, 128)
         assert gpipe.gpipe_cell_gemm_plan(h, cfg.batch, cfg.micro, R["bn_stats"]) == (0, 0, 0)
     finally:
