@@ -147,7 +147,7 @@ constexpr int attn_smem_bytes() {
 extern __shared__ __attribute__((aligned(16))) bf16_t attn_smem[];
 
 // ------------------------------------------------------------------ forward
-// grid (query blocks, B*H); qkv [B*S][3D], ctx [B*S][D], lse2 [B*H][S].
+// grid (B*H, query blocks); qkv [B*S][3D], ctx [B*S][D], lse2 [B*H][S].
 template <int DH>
 __global__ __launch_bounds__(512) void flash_fwd_kernel(const bf16_t* __restrict__ qkv,
                                                         bf16_t* __restrict__ ctx,
@@ -160,8 +160,8 @@ __global__ __launch_bounds__(512) void flash_fwd_kernel(const bf16_t* __restrict
   const int grp = w >> 2, wl = w & 3, gt = threadIdx.x & 255;
   bf16_t* gbase = attn_smem + grp * 4 * TE;  // [buffer][K, V]
   const int nqb = (S + kBlk - 1) / kBlk;
-  const int qb = nqb - 1 - int(blockIdx.x);  // longest causal rows first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int qb = nqb - 1 - int(blockIdx.y);  // longest causal rows first
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const int64_t ld = 3 * int64_t(D);
   const bf16_t* Qg = qkv + int64_t(b) * S * ld + h * DH;
   const bf16_t* Kg = Qg + D;
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(512) void flash_fwd_kernel(const bf16_t* __restrict
 }
 
 // ------------------------------------------------------------------ backward
-// dK, dV for one key block: grid (key blocks, B*H); the groups split the
+// dK, dV for one key block: grid (B*H, key blocks); the groups split the
 // query blocks.
 template <int DH>
 __global__ __launch_bounds__(512) void flash_dkdv_kernel(
@@ -334,8 +334,8 @@ __global__ __launch_bounds__(512) void flash_dkdv_kernel(
   bf16_t* gbase = attn_smem + grp * 4 * TE;  // [buffer][Q, dO]
   float* sbase = reinterpret_cast<float*>(attn_smem + kGroups * 4 * TE) + grp * 4 * kBlk;  // [buffer][lse, delta][64]
   const int nb = (S + kBlk - 1) / kBlk;
-  const int kbk = int(blockIdx.x);
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int kbk = int(blockIdx.y);
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const int64_t ld = 3 * int64_t(D);
   const bf16_t* Qg = qkv + int64_t(b) * S * ld + h * DH;
   const bf16_t* Kg = Qg + D;
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(512) void flash_dkdv_kernel(
   }
 }
 
-// dQ for one query block: grid (query blocks, B*H); the groups split the key
+// dQ for one query block: grid (B*H, query blocks); the groups split the key
 // blocks.  It also computes the block's row sums delta = rowsum(dO * O) (each
 // lane a 32-column share of its query row, then the four lane groups added in
 // a fixed order), uses them and writes them for the dK / dV kernel, which runs
@@ -470,8 +470,8 @@ __global__ __launch_bounds__(512) void flash_dq_kernel(
   const int grp = w >> 2, wl = w & 3, gt = threadIdx.x & 255;
   bf16_t* gbase = attn_smem + grp * 4 * TE;  // [buffer][K, V]
   const int nb = (S + kBlk - 1) / kBlk;
-  const int qb = nb - 1 - int(blockIdx.x);
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int qb = nb - 1 - int(blockIdx.y);
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const int64_t ld = 3 * int64_t(D);
   const bf16_t* Qg = qkv + int64_t(b) * S * ld + h * DH;
   const bf16_t* Kg = Qg + D;
@@ -602,7 +602,10 @@ hipError_t flash_fwd(const void* qkv, void* ctx, float* lse2, int B, int H, int 
                      int causal, hipStream_t s) {
   const int dh = D / H;
   const float sl2 = kLog2e / sqrtf(float(dh));
-  const dim3 grid((S + kBlk - 1) / kBlk, B * H);
+  // (sequence, head) along x: workgroups go to the XCDs round-robin by linear
+  // id, so with B*H a multiple of 8 every block of one (sequence, head) --
+  // which all read the same keys and values -- shares one XCD's L2
+  const dim3 grid(B * H, (S + kBlk - 1) / kBlk);
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
   const bf16_t* q = static_cast<const bf16_t*>(qkv);
   bf16_t* c = static_cast<bf16_t*>(ctx);
@@ -624,7 +627,10 @@ hipError_t flash_bwd(const void* qkv, const void* ctx, const void* dctx, const f
   const int dh = D / H;
   const float scale = 1.0f / sqrtf(float(dh));
   const float sl2 = kLog2e * scale;
-  const dim3 grid((S + kBlk - 1) / kBlk, B * H);
+  // (sequence, head) along x: workgroups go to the XCDs round-robin by linear
+  // id, so with B*H a multiple of 8 every block of one (sequence, head) --
+  // which all read the same keys and values -- shares one XCD's L2
+  const dim3 grid(B * H, (S + kBlk - 1) / kBlk);
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
   const bf16_t* q = static_cast<const bf16_t*>(qkv);
   const bf16_t* o = static_cast<const bf16_t*>(ctx);
