@@ -245,6 +245,25 @@ def test_fused_attention_ragged_sequences_bf16(dh, seq):
     check(cfg.with_(causal=True))
 
 
+@pytest.mark.parametrize("batch", [4, 6])
+def test_remat_with_split_products_bitwise_bf16(batch):
+    """With the FFN down-projection split over k (d_ff 4096) and the forward
+    phase on two streams, the re-materialized intermediates, and so every
+    gradient, equal the stored-activation run bit for bit."""
+    cfg = configs.SMALL.with_(name=f"remat_split_b{batch}", layers=2, d_model=512, heads=4,
+                              d_ff=4096, seq=128, batch=batch, micro=2, causal=True)
+    params = inputs.cell_params(cfg)
+    x, t = inputs.cell_data(cfg)
+    a = run_gpu(cfg, params, x, t, cfg.batch, cfg.micro, remat=True, update=False)
+    b = run_gpu(cfg, params, x, t, cfg.batch, cfg.micro, remat=False, update=False)
+    assert np.array_equal(a["y"], b["y"])
+    assert np.array_equal(a["dx"], b["dx"])
+    for ga, gb in zip(a["grad"], b["grad"]):
+        for n in gpipe.TENSORS:
+            assert np.array_equal(ga[n], gb[n]), n
+    check(cfg)
+
+
 def test_fused_attention_remat_bitwise_bf16():
     """Remat through the fused attention equals stored activations bit for bit."""
     cfg = configs.SMALL.with_(name="fused_remat", layers=2, d_model=256, heads=2, d_ff=512,
