@@ -37,12 +37,15 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
-# The Transformer cell's step runs two streams: in the forward phase even and
-# odd micro-batches (those launches are not role-timed), in the backward phase
-# the weight-gradient GEMMs beside the input-gradient chain, so the times of
-# every backward-phase launch include time shared with other kernels: they are
-# not per-kernel figures.  The dominant kernel and mfma_util_gemm come from the
-# roles of the re-materialized forward, which runs alone.
+# The Transformer cell's step runs several streams: in the forward phase even
+# and odd micro-batches, in the backward phase the weight-gradient GEMMs beside
+# the input-gradient chain and the next micro-batch's re-materialization on a
+# third stream (the launches of the forward phase and of those
+# re-materializations are not role-timed), so the times of every backward-
+# phase launch include time shared with other kernels: they are not per-kernel
+# figures.  Micro-batch 0 re-materializes on the caller's stream alone: the
+# dominant kernel and mfma_util_gemm come from those launches of the forward
+# roles.
 SECOND_STREAM_ROLES = ("ffn2_wgrad", "ffn1_wgrad", "out_wgrad", "qkv_wgrad")
 ALONE_ROLES = ("ln1_fwd", "qkv_fwd", "scores_fwd", "softmax_fwd", "pv_fwd", "attn_fwd", "out_fwd",
                "ln2_fwd", "ffn1_fwd", "ffn2_fwd", "mse")
@@ -434,7 +437,15 @@ def main():
         if not conv and name not in ALONE_ROLES:
             return False
         return gpipe.gpipe_cell_gemm_plan(cell.handle, n, m, gpipe.ROLES.index(name))[2] <= 1
-    dominant = max((k for k in prof if single_kernel(k)), key=lambda k: prof[k][0])
+    # (ranked by the role's time in a whole step: its average launch times its
+    # launches per step -- the forward roles are timed in one micro-batch's
+    # re-materialization but launch 2 L M times)
+    def step_launches(name, cnt):
+        if conv or name not in ALONE_ROLES or name == "mse":
+            return cnt
+        return 2 * cfg.layers * m
+    dominant = max((k for k in prof if single_kernel(k)),
+                   key=lambda k: prof[k][0] / prof[k][1] * step_launches(k, prof[k][1]))
     dom_idx = gpipe.ROLES.index(dominant)
 
     # timed region: K steps; the dominant role's launches are bracketed by events
@@ -475,7 +486,10 @@ def main():
                 e["split_k"] = sp_
         if not conv and name not in ALONE_ROLES and name not in ("loss_reduce", "rmsprop"):
             e["overlapped"] = ("second stream" if name in SECOND_STREAM_ROLES
-                               else "caller's stream") + ", concurrent with the other stream"
+                               else "caller's stream") + ", concurrent with the other streams"
+        if not conv and name in ALONE_ROLES and name != "mse":
+            e["timed"] = "micro-batch 0's re-materialization, caller's stream alone"
+            e["launches_per_step_all"] = 2 * cfg.layers * m
         if kind == "mfma":
             tf = per / (ms_tot / cnt * 1e-3) / 1e12
             pk = PEAK_BF16_TFLOPS if cfg.precision == "bf16" else PEAK_FP32_TFLOPS

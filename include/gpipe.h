@@ -184,8 +184,9 @@ gpipe_status gpipe_cell_workspace_bytes(const gpipe_cell *cell, int N, int M, in
 
 /* Byte offset inside the workspace of saved tensor `which` of layer `layer`
  * for micro-batch `micro`, as laid out for gpipe_cell_step(N, M, remat).
- * With remat != 0 only one micro-batch set exists (micro must be 0) and it
- * holds the last re-materialized micro-batch when the step ends.  For
+ * With remat != 0 only one micro-batch set exists (micro must be 0); it is
+ * the re-materialization's scratch, whose layer slots the step assigns as its
+ * schedule needs (their contents when the step ends are unspecified).  For
  * GPIPE_SAVED_X of layer 0 (the caller's x) it returns GPIPE_ERR_INVALID.
  * Meant for inspection and tests. */
 gpipe_status gpipe_cell_saved_offset(const gpipe_cell *cell, int N, int M, int remat, int micro,
@@ -211,14 +212,16 @@ gpipe_status gpipe_cell_saved_offset(const gpipe_cell *cell, int N, int M, int r
  * bad N/M, misaligned pointers or too small a workspace.
  * Streams: all work is enqueued behind what the caller has enqueued on
  * `stream` and the call returns after enqueueing; synchronising `stream`
- * covers the whole step.  A Transformer cell also uses a second stream of
- * its own (created at its first step, default priority, on the device
- * current then; a later step on another device returns GPIPE_ERR_STATE): in
- * the forward phase (remat != 0, bf16 with head dim 64 or 128, at least two
- * layers) it runs the odd micro-batches, in the backward phase the weight-
- * gradient GEMMs; events order it against `stream` both ways, the weight
- * gradients still accumulate the micro-batches in order and the step is
- * bitwise reproducible.  A cell must not run two steps at once. */
+ * covers the whole step.  A Transformer cell also uses two streams of its
+ * own (created at its first step, default priority, on the device current
+ * then; a later step on another device returns GPIPE_ERR_STATE).  The second
+ * runs the odd micro-batches of the forward phase (remat != 0, bf16 with
+ * head dim 64 or 128, at least two layers) and the weight-gradient GEMMs of
+ * the backward phase; the third (same conditions) re-materializes micro-
+ * batch m+1 layer by layer while micro-batch m's backward frees the saved
+ * set's layer slots.  Events order them against `stream` both ways, the
+ * weight gradients still accumulate the micro-batches in order and the step
+ * is bitwise reproducible.  A cell must not run two steps at once. */
 gpipe_status gpipe_cell_step(gpipe_cell *cell, const void *x, const void *target, void *y,
                              void *dx, int N, int M, int remat, void *workspace, size_t ws_bytes,
                              void *stream, float *loss_dev);

@@ -33,9 +33,10 @@ struct gpipe_cell {
   float* ms;
   bool bound;
   // Transformer cells: the second stream of the backward phase (the weight
-  // gradients) and the ring of events ordering it against the caller's
-  // stream; created at the first step, on the device current then.
-  hipStream_t aux = nullptr;
+  // gradients), the third (the next micro-batch's re-materialization) and
+  // the ring of events ordering them against the caller's stream; created at
+  // the first step, on the device current then.
+  hipStream_t aux = nullptr, aux2 = nullptr;
   int aux_device = -1;
   std::vector<hipEvent_t> sync_events;
   size_t sync_next = 0;

@@ -208,7 +208,7 @@ struct Ctx {
 // micro-batches in order 0 .. M-1.
 struct Streams {
   gpipe_cell* c;
-  hipStream_t s1, s2;
+  hipStream_t s1, s2, s3;
   hipEvent_t next() { return c->sync_events[c->sync_next++ % c->sync_events.size()]; }
   // s2 waits for the work enqueued so far on s1
   bool fork() {
@@ -227,6 +227,17 @@ struct Streams {
     hipEvent_t e;
     return mark(&e) && join(e);
   }
+  // s3 waits for the work enqueued so far on s1 and on s2
+  bool fork3() {
+    const hipEvent_t e1 = next(), e2 = next();
+    return hipEventRecord(e1, s1) == hipSuccess && hipEventRecord(e2, s2) == hipSuccess &&
+           hipStreamWaitEvent(s3, e1, 0) == hipSuccess && hipStreamWaitEvent(s3, e2, 0) == hipSuccess;
+  }
+  // s1 waits for the work enqueued so far on s3
+  bool join3() {
+    const hipEvent_t e = next();
+    return hipEventRecord(e, s3) == hipSuccess && hipStreamWaitEvent(s1, e, 0) == hipSuccess;
+  }
 };
 
 // Events of s2 after the weight gradients of one layer's backward.
@@ -240,6 +251,7 @@ gpipe_status ensure_streams(gpipe_cell* c) {
   GP_CHECK(hipGetDevice(&dev));
   if (c->aux) return dev == c->aux_device ? GPIPE_OK : GPIPE_ERR_STATE;
   GP_CHECK(hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking));
+  GP_CHECK(hipStreamCreateWithFlags(&c->aux2, hipStreamNonBlocking));
   c->aux_device = dev;
   for (int i = 0; i < 64; ++i) {
     hipEvent_t e;
@@ -429,11 +441,13 @@ gpipe_status overlapped_forward(const Ctx& cx, Streams& ss, const void* x, void*
   return ss.join_all() ? GPIPE_OK : GPIPE_ERR_DEVICE;
 }
 
-// Backward of layer l.  On entry r0 (f32) / a0 (act) hold the gradient w.r.t.
+// Backward of layer l (its saved tensors in layer slot `slot` of `set`).  On
+// entry r0 (f32) / a0 (act) hold the gradient w.r.t.
 // the layer output; on exit they hold the gradient w.r.t. its input (a0, or
 // dx_out when given, receives the act copy).
 gpipe_status layer_backward(const Ctx& x, Streams& ss, const WgradDone& above, WgradDone* mine,
-                            int set, int l, const void* xin, int beta, void* dx_out) {
+                            int set, int slot, int l, const void* xin, int beta,
+                            void* dx_out) {
   Ctx w = x;  // the weight gradients' context: the second stream
   w.s = ss.s2;
   const gpipe_cell* c = x.c;
@@ -442,16 +456,16 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, const WgradDone& above, W
   const int64_t ldS = p.ldS;
   const bool bf = x.bf16;
   const int xt_act = bf ? XT_BF16 : XT_F32;
-  void* h1 = x.at(saved_at(p, set, l, GPIPE_SAVED_H1));
-  const float* st1 = static_cast<const float*>(x.at(saved_at(p, set, l, GPIPE_SAVED_ST1)));
-  void* qkv = x.at(saved_at(p, set, l, GPIPE_SAVED_QKV));
-  void* P = x.at(saved_at(p, set, l, GPIPE_SAVED_P));
-  void* ctx = x.at(saved_at(p, set, l, GPIPE_SAVED_CTX));
-  void* x1 = x.at(saved_at(p, set, l, GPIPE_SAVED_X1));
-  void* h2 = x.at(saved_at(p, set, l, GPIPE_SAVED_H2));
-  const float* st2 = static_cast<const float*>(x.at(saved_at(p, set, l, GPIPE_SAVED_ST2)));
-  void* u = x.at(saved_at(p, set, l, GPIPE_SAVED_U));
-  void* g = x.at(saved_at(p, set, l, GPIPE_SAVED_G));
+  void* h1 = x.at(saved_at(p, set, slot, GPIPE_SAVED_H1));
+  const float* st1 = static_cast<const float*>(x.at(saved_at(p, set, slot, GPIPE_SAVED_ST1)));
+  void* qkv = x.at(saved_at(p, set, slot, GPIPE_SAVED_QKV));
+  void* P = x.at(saved_at(p, set, slot, GPIPE_SAVED_P));
+  void* ctx = x.at(saved_at(p, set, slot, GPIPE_SAVED_CTX));
+  void* x1 = x.at(saved_at(p, set, slot, GPIPE_SAVED_X1));
+  void* h2 = x.at(saved_at(p, set, slot, GPIPE_SAVED_H2));
+  const float* st2 = static_cast<const float*>(x.at(saved_at(p, set, slot, GPIPE_SAVED_ST2)));
+  void* u = x.at(saved_at(p, set, slot, GPIPE_SAVED_U));
+  void* g = x.at(saved_at(p, set, slot, GPIPE_SAVED_G));
   float* r0 = static_cast<float*>(x.at(p.r0));
   float* r1 = static_cast<float*>(x.at(p.r1));
   float* dm = static_cast<float*>(x.at(p.dm));
@@ -634,6 +648,7 @@ gpipe_status gpipe_cell_destroy(gpipe_cell* c) {
     for (hipEvent_t e : c->prof_events) (void)hipEventDestroy(e);
     for (hipEvent_t e : c->sync_events) (void)hipEventDestroy(e);
     if (c->aux) (void)hipStreamDestroy(c->aux);
+    if (c->aux2) (void)hipStreamDestroy(c->aux2);
   }
   delete c;
   return GPIPE_OK;
@@ -722,7 +737,7 @@ gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, v
   }
   Ctx cx{c, c->prof_mask ? c : nullptr, &p, static_cast<char*>(workspace),
          static_cast<hipStream_t>(stream), c->prec == GPIPE_BF16, p.splitk};
-  Streams ss{c, cx.s, c->aux};
+  Streams ss{c, cx.s, c->aux, c->aux2};
   const size_t mb = size_t(p.T) * c->D;  // elements per micro-batch
   const float inv_denom = float(1.0 / (double(N) * c->S * c->D));
   float* msepart = static_cast<float*>(cx.at(p.msepart));
@@ -738,7 +753,28 @@ gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, v
       if (st != GPIPE_OK) return st;
     }
   }
-  // phase 2: backward with re-materialization and float32 accumulation
+  // phase 2: backward with re-materialization and float32 accumulation.
+  // With fused attention the re-materialization of micro-batch m+1 runs on
+  // the third stream during the backward of micro-batch m, in the one saved
+  // set: the backward frees the layer slots from the top down and the
+  // re-materialization fills them from the bottom up, so micro-batch m+1
+  // puts layer j in the slot that layer L-1-j of micro-batch m held (odd
+  // micro-batches take the slots in reverse order), each layer enqueued
+  // after that slot's backward and weight gradients.  A layer's output goes
+  // to its own slot's X tensor (the next layer's input).  Micro-batch 0
+  // re-materializes on the caller's stream before its backward.
+  const int L = c->L;
+  const bool piped = remat && p.flash && L >= 2;
+  auto slot_of = [&](int m, int j) { return (piped && (m & 1)) ? L - 1 - j : j; };
+  Ctx cr = cx;  // the re-materialization's context on the third stream
+  cr.s = ss.s3;
+  cr.prof = nullptr;
+  cr.splitk = p.splitk2;
+  auto remat_layer = [&](const Ctx& z, int m, int j) {
+    const void* in = j == 0 ? cx.act(x, m * mb) : z.at(saved_at(p, 0, slot_of(m, j - 1), GPIPE_SAVED_X));
+    void* out = j == L - 1 ? z.at(p.yre) : z.at(saved_at(p, 0, slot_of(m, j), GPIPE_SAVED_X));
+    return layer_forward(z, 0, slot_of(m, j), j, in, out);
+  };
   for (int m = 0; m < M; ++m) {
     const int set = remat ? 0 : m;
     const void* xm = cx.act(x, m * mb);
@@ -746,7 +782,17 @@ gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, v
     // every weight gradient of the previous micro-batch has read the saved
     // activations and the transient gradients this one overwrites
     if (m > 0 && !ss.join_all()) return GPIPE_ERR_DEVICE;
-    if (remat) {
+    if (piped) {
+      if (m == 0) {
+        for (int j = 0; j < L; ++j) {
+          gpipe_status st = remat_layer(cx, 0, j);
+          if (st != GPIPE_OK) return st;
+        }
+      } else if (!ss.join3()) {  // this micro-batch's re-materialization is done
+        return GPIPE_ERR_DEVICE;
+      }
+      ym = cx.at(p.yre);
+    } else if (remat) {
       void* yre = cx.at(p.yre);
       gpipe_status st = cell_forward(cx, set, xm, yre);
       if (st != GPIPE_OK) return st;
@@ -757,13 +803,25 @@ gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, v
                          cx.at(p.a0), msepart + size_t(m) * p.mse_nblk, int64_t(mb), inv_denom,
                          &nblk, cx.s));
     WgradDone above;  // the top layer has none above it in this micro-batch
-    for (int l = c->L - 1; l >= 0; --l) {
-      const void* xin = l == 0 ? xm : cx.at(saved_at(p, set, l, GPIPE_SAVED_X));
+    for (int l = L - 1; l >= 0; --l) {
+      // (the layer's input: the output of layer l-1, in that layer's slot when
+      // pipelined, else in this layer's X tensor)
+      const void* xin = l == 0 ? xm
+                        : piped ? cx.at(saved_at(p, set, slot_of(m, l - 1), GPIPE_SAVED_X))
+                                : cx.at(saved_at(p, set, l, GPIPE_SAVED_X));
       void* dxo = (l == 0 && dx) ? cx.act(dx, m * mb) : nullptr;
       WgradDone mine;
-      gpipe_status st = layer_backward(cx, ss, above, &mine, set, l, xin, m > 0 ? 1 : 0, dxo);
+      gpipe_status st = layer_backward(cx, ss, above, &mine, set, slot_of(m, l), l, xin,
+                                       m > 0 ? 1 : 0, dxo);
       if (st != GPIPE_OK) return st;
       above = mine;
+      if (piped && m + 1 < M) {
+        // layer l's slot is free once its backward (s1) and weight gradients (s2)
+        // are done
+        if (!ss.fork3()) return GPIPE_ERR_DEVICE;
+        st = remat_layer(cr, m + 1, L - 1 - l);
+        if (st != GPIPE_OK) return st;
+      }
     }
   }
   // the weight gradients (and their bias partial sums) are complete
