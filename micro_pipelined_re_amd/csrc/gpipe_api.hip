@@ -58,7 +58,8 @@ struct Plan {
   size_t saved_bytes[GPIPE_N_SAVED];
   size_t layer_bytes, set_bytes;
   int nsets;
-  size_t yre, scores, ds, r0, r1, dm, a0, a1, dctx, du, dqkv, colpart, gpart, msepart, splitk, splitk2;
+  size_t yre, scores, ds, r0, r1, dm, a0, a1, dctx, du, dqkv, colpart, gpart, msepart, splitk, splitk2,
+      splitk3;
   size_t colpart_floats;
   // gpart slots (GPS_*): offset inside a layer's block, partial rows, row length
   size_t gp_off[GPS_N], gp_layer;
@@ -159,6 +160,8 @@ bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
   p->splitk = take(sk * 4);
   // the forward phase's second lane (overlapped_forward) has its own partials
   p->splitk2 = take(sk * 4);
+  // and its third lane (bf16 cells with fused attention and at least three layers)
+  p->splitk3 = take(remat && p->flash && c->L >= 3 ? sk * 4 : 0);
   p->total = o;
   return true;
 }
@@ -409,36 +412,40 @@ gpipe_status cell_forward(const Ctx& x, int set, const void* xin, void* yout) {
 // output, so each micro-batch needs only one layer's intermediates, reused
 // layer after layer (the layer's output overwrites its input, which is last
 // read by the out-projection's residual add).  The micro-batches are
-// independent: even ones run on the caller's stream in slot 0 of the saved
-// set, odd ones on the second stream in slot 1 (with their own split-K
-// partials), so each stream's kernels fill the CUs and launch gaps the other
-// leaves; the set is free until the backward phase re-materializes into it,
-// after the streams join.  Launches here are not role-timed (their times
-// would include the other stream's).
+// independent: micro-batch m runs on lane m mod K (K = 3 streams with at
+// least three layers, else 2) in slot m mod K of the saved set, the lanes
+// after the first with their own split-K partials, so each stream's kernels
+// fill the CUs and launch gaps the others leave; the set is free until the
+// backward phase re-materializes into it, after the streams join.  Launches
+// here are not role-timed (their times would include the other streams').
 gpipe_status overlapped_forward(const Ctx& cx, Streams& ss, const void* x, void* y, int M,
                                 size_t mb) {
   const Plan& p = *cx.p;
   const int L = cx.c->L;
-  Ctx lane[2] = {cx, cx};
-  lane[0].prof = lane[1].prof = nullptr;
+  const int K = L >= 3 ? 3 : 2;  // lanes (one layer slot each)
+  Ctx lane[3] = {cx, cx, cx};
+  for (Ctx& z : lane) z.prof = nullptr;
   lane[1].s = ss.s2;
   lane[1].splitk = p.splitk2;
-  if (!ss.fork()) return GPIPE_ERR_DEVICE;  // the inputs and weights exist
-  // a pair of micro-batches is enqueued layer by layer, alternating the
-  // streams, so that both always have work queued (enqueueing a whole
-  // micro-batch per stream let each run dry while the host fed the other)
-  for (int m0 = 0; m0 < M; m0 += 2)
+  lane[2].s = ss.s3;
+  lane[2].splitk = p.splitk3;
+  // the inputs and weights exist
+  if (!ss.fork() || (K == 3 && !ss.fork3())) return GPIPE_ERR_DEVICE;
+  // K micro-batches are enqueued layer by layer, alternating the streams, so
+  // that all always have work queued (enqueueing a whole micro-batch per
+  // stream let each run dry while the host fed the others)
+  for (int m0 = 0; m0 < M; m0 += K)
     for (int l = 0; l < L; ++l)
-      for (int m = m0; m < std::min(M, m0 + 2); ++m) {
-        const Ctx& z = lane[m & 1];
-        const int slot = m & 1;
+      for (int m = m0; m < std::min(M, m0 + K); ++m) {
+        const int slot = m % K;
+        const Ctx& z = lane[slot];
         void* xs = z.at(saved_at(p, 0, slot, GPIPE_SAVED_X));
         const void* in = l == 0 ? cx.act(x, m * mb) : xs;
         void* out = l == L - 1 ? cx.act(y, m * mb) : xs;
         gpipe_status st = layer_forward(z, 0, slot, l, in, out);
         if (st != GPIPE_OK) return st;
       }
-  return ss.join_all() ? GPIPE_OK : GPIPE_ERR_DEVICE;
+  return ss.join_all() && (K < 3 || ss.join3()) ? GPIPE_OK : GPIPE_ERR_DEVICE;
 }
 
 // Backward of layer l (its saved tensors in layer slot `slot` of `set`).  On
