@@ -160,8 +160,11 @@ bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
   p->splitk = take(sk * 4);
   // the forward phase's second lane (overlapped_forward) has its own partials
   p->splitk2 = take(sk * 4);
-  // and its third lane (bf16 cells with fused attention and at least three layers)
-  p->splitk3 = take(remat && p->flash && c->L >= 3 ? sk * 4 : 0);
+  // and its third lane (used with re-materialization by bf16 cells with
+  // fused attention and at least three layers; laid out whenever the cell
+  // could use it, like the second lane's, so that the two workspaces differ
+  // by the saved sets only)
+  p->splitk3 = take(p->flash && c->L >= 3 ? sk * 4 : 0);
   p->total = o;
   return true;
 }

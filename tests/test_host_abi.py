@@ -101,11 +101,12 @@ def test_workspace_tracks_the_activation_bound(cfg):
         assert formula <= set_bytes <= formula + 256 * 11 * cfg.layers
         yre = -(-(n // m) * cfg.seq * cfg.d_model * eb // 256) * 256
         assert keep - remat == (m - 1) * set_bytes - yre
-        # transients are one layer's worth, small next to the set for the big cells
+        # transients are one layer's worth plus each stream's split-K partials,
+        # small next to the set for the big cells
         transient = remat - set_bytes
         assert transient > 0
         if cfg.layers >= 6:
-            assert transient < 0.5 * set_bytes
+            assert transient < 0.6 * set_bytes
         # halving the micro-batch halves the set
         if n % (2 * m) == 0:
             assert gpipe.gpipe_cell_workspace_bytes(h, n, 2 * m, True) < 0.6 * remat + transient
