@@ -257,11 +257,10 @@ gpipe_status block_backward(const CCtx& x, int set, int l, const void* xin, int 
   float* part = x.f(p.part);
   float* sums = x.f(p.sums);
   int nch = 0;
-  // y = x + BN2(z)
+  // y = x + BN2(z) (the gain and shift gradients, adjacent, accumulate in the same pass)
   GP_RUN(x, GPIPE_ROLE_BN_BWD, bn_bwd(x.bf16, 0, r0, nullptr, z, st2, x.wf32(l, GPIPE_CONV_BN2_G),
-                                      part, sums, dz, P, C, &nch, x.s));
-  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(part, nch, 2 * C, 2 * C, x.grad(l, GPIPE_CONV_BN2_G),
-                                               beta, x.s));
+                                      part, sums, x.grad(l, GPIPE_CONV_BN2_G), beta, dz, P, C,
+                                      &nch, x.s));
   // z = conv(r, W2)
   {
     const gpipe_status st = cwgrad(x, r, dz, x.grad(l, GPIPE_CONV_W2), beta);
@@ -277,9 +276,8 @@ gpipe_status block_backward(const CCtx& x, int set, int l, const void* xin, int 
   }
   // r = ReLU(BN1(a))
   GP_RUN(x, GPIPE_ROLE_BN_BWD, bn_bwd(x.bf16, 1, r1, r, a, st1, x.wf32(l, GPIPE_CONV_BN1_G), part,
-                                      sums, dz, P, C, &nch, x.s));
-  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials(part, nch, 2 * C, 2 * C, x.grad(l, GPIPE_CONV_BN1_G),
-                                               beta, x.s));
+                                      sums, x.grad(l, GPIPE_CONV_BN1_G), beta, dz, P, C, &nch,
+                                      x.s));
   // a = conv(x, W1); the residual gradient r0 is added in col2im (in place)
   {
     const gpipe_status st = cwgrad(x, xin, dz, x.grad(l, GPIPE_CONV_W1), beta);

@@ -392,8 +392,8 @@ __global__ __launch_bounds__(256) void bn_bwd_apply_kernel(const float* __restri
 }
 
 hipError_t bn_bwd(bool bf16, int mask, const float* dy_src, const void* r, const void* a,
-                  const float* stats, const float* gamma, float* part, float* sums, void* da,
-                  int64_t rows, int C, int* nchunk, hipStream_t s) {
+                  const float* stats, const float* gamma, float* part, float* sums, float* grad,
+                  int grad_beta, void* da, int64_t rows, int C, int* nchunk, hipStream_t s) {
   *nchunk = bn_chunks(rows);
   if (rows == 0 || C == 0) return hipSuccess;
   dim3 grid((C + 255) / 256, *nchunk);
@@ -408,7 +408,7 @@ hipError_t bn_bwd(bool bf16, int mask, const float* dy_src, const void* r, const
 #undef GP_BN_BWD_P
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = sum_partials(part, *nchunk, 2 * C, 2 * C, sums, 0, s);
+  e = sum_partials(part, *nchunk, 2 * C, 2 * C, sums, 0, s, grad, grad_beta);
   if (e != hipSuccess) return e;
   const int64_t total = rows * (C / 8);
   const int64_t want = (total + 255) / 256;

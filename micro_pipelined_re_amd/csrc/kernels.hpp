@@ -122,9 +122,10 @@ int mse_blocks(int64_t count);
 hipError_t colsum_partial(int xtype, const void* x, int64_t ld, int rows, int cols, float* part,
                           int* nchunk, hipStream_t s);
 int colsum_chunks(int rows);
-// out[c] = (beta ? out[c] : 0) + sum_p part[p * stride + c], p = 0 .. nparts-1 in order.
+// out[c] = (beta ? out[c] : 0) + sum_p part[p * stride + c], p = 0 .. nparts-1 in order;
+// acc (optional) receives the same sum the same way under acc_beta.
 hipError_t sum_partials(const float* part, int nparts, int64_t stride, int cols, float* out,
-                        int beta, hipStream_t s);
+                        int beta, hipStream_t s, float* acc = nullptr, int acc_beta = 0);
 
 // RMSProp over n parameters; writes the bf16 copy when w_lowp is non-null.
 hipError_t rmsprop(float* w, const float* g, float* ms, void* w_lowp, int64_t n, float lr,
@@ -145,10 +146,11 @@ hipError_t bn_apply(bool bf16, int mode, const void* a, const float* stats, cons
                     const float* beta, const void* res, void* out, int64_t rows, int C,
                     hipStream_t s);
 // Backward of bn (mask: dy is multiplied by [r > 0]); sums = (sum dy*xhat, sum dy) of this
-// batch (part: [chunks][2C] scratch); da = input gradient (act).
+// batch (part: [chunks][2C] scratch), also stored (grad_beta = 0) or added into grad
+// [2C] (the gain and shift gradients); da = input gradient (act).
 hipError_t bn_bwd(bool bf16, int mask, const float* dy_src, const void* r, const void* a,
-                  const float* stats, const float* gamma, float* part, float* sums, void* da,
-                  int64_t rows, int C, int* nchunk, hipStream_t s);
+                  const float* stats, const float* gamma, float* part, float* sums, float* grad,
+                  int grad_beta, void* da, int64_t rows, int C, int* nchunk, hipStream_t s);
 // Moving averages from the M micro-batches' recorded moments.
 hipError_t bn_running(const float* rec, int M, int nbn, int C, int64_t n_total, float momentum,
                       float* running, hipStream_t s);

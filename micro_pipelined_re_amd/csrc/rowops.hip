@@ -529,7 +529,9 @@ hipError_t colsum_partial(int xtype, const void* x, int64_t ld, int rows, int co
 template <int CW>
 __global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restrict__ part, int nparts,
                                                            int64_t stride, int cols,
-                                                           float* __restrict__ out, int beta) {
+                                                           float* __restrict__ out, int beta,
+                                                           float* __restrict__ acc,
+                                                           int acc_beta) {
   constexpr int G = 256 / CW;
   __shared__ float red[256];
   const int cl = threadIdx.x % CW, pg = threadIdx.x / CW;
@@ -546,18 +548,21 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restri
     if (pg < h) red[pg * CW + cl] += red[(pg + h) * CW + cl];
     __syncthreads();
   }
-  if (pg == 0 && c < cols) out[c] = beta ? out[c] + red[cl] : red[cl];
+  if (pg == 0 && c < cols) {
+    out[c] = beta ? out[c] + red[cl] : red[cl];
+    if (acc) acc[c] = acc_beta ? acc[c] + red[cl] : red[cl];
+  }
 }
 
 hipError_t sum_partials(const float* part, int nparts, int64_t stride, int cols, float* out,
-                        int beta, hipStream_t s) {
+                        int beta, hipStream_t s, float* acc, int acc_beta) {
   if (cols == 0) return hipSuccess;
   if (cols >= 32)
     hipLaunchKernelGGL(sum_partials_kernel<32>, dim3((cols + 31) / 32), dim3(256), 0, s, part,
-                       nparts, stride, cols, out, beta);
+                       nparts, stride, cols, out, beta, acc, acc_beta);
   else
     hipLaunchKernelGGL(sum_partials_kernel<1>, dim3(cols), dim3(256), 0, s, part, nparts, stride,
-                       cols, out, beta);
+                       cols, out, beta, acc, acc_beta);
   return hipGetLastError();
 }
 
