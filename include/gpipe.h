@@ -260,8 +260,10 @@ typedef enum {
   GPIPE_ROLE_CONV_FWD, GPIPE_ROLE_CONV_DGRAD, GPIPE_ROLE_CONV_WGRAD, GPIPE_ROLE_IM2COL,
   GPIPE_ROLE_COL2IM, GPIPE_ROLE_BN_STATS, GPIPE_ROLE_BN_APPLY, GPIPE_ROLE_BN_BWD,
   GPIPE_ROLE_BN_RUNNING,
-  /* fused attention (bf16, head dim 64 or 128): forward; backward row sums
-   * of dO * O; dK and dV per key block; dQ per query block */
+  /* fused attention (bf16, head dim 64 or 128): ATTN_FWD the forward, ATTN_DQ
+   * the backward (dQ per query block and dK, dV per key block, in one
+   * launch); ATTN_DELTA and ATTN_DKDV are no longer launched (kept so that
+   * the later roles keep their values) */
   GPIPE_ROLE_ATTN_FWD, GPIPE_ROLE_ATTN_DELTA, GPIPE_ROLE_ATTN_DKDV, GPIPE_ROLE_ATTN_DQ,
   /* conv cells in bf16 with channels a multiple of 64: implicit-GEMM
    * convolution (the 3 x 3 neighbourhood gathered by the GEMM's loads) and the

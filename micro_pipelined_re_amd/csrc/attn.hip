@@ -319,13 +319,14 @@ __global__ __launch_bounds__(512) void flash_fwd_kernel(const bf16_t* __restrict
 }
 
 // ------------------------------------------------------------------ backward
-// dK, dV for one key block: grid (B*H, key blocks); the groups split the
-// query blocks.
+// dK, dV for key block kbk of (sequence, head) bh; the groups split the
+// query blocks, and each computes the row sums delta = rowsum(dO * O) of the
+// query blocks it visits from the dO and O tiles it loads.
 template <int DH>
-__global__ __launch_bounds__(512) void flash_dkdv_kernel(
-    const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dctx,
-    const float* __restrict__ lse2, const float* __restrict__ delta, bf16_t* __restrict__ dqkv,
-    int S, int H, int D, int causal, float sl2, float scale) {
+__device__ __forceinline__ void flash_dkdv_body(
+    const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ ctx,
+    const bf16_t* __restrict__ dctx, const float* __restrict__ lse2, bf16_t* __restrict__ dqkv,
+    int S, int H, int D, int causal, float sl2, float scale, int bh, int kbk) {
   constexpr int KS = DH / 32;
   constexpr int DT = DH / 16;
   constexpr int TE = attn_tile_elems<DH>();
@@ -334,15 +335,14 @@ __global__ __launch_bounds__(512) void flash_dkdv_kernel(
   bf16_t* gbase = attn_smem + grp * 4 * TE;  // [buffer][Q, dO]
   float* sbase = reinterpret_cast<float*>(attn_smem + kGroups * 4 * TE) + grp * 4 * kBlk;  // [buffer][lse, delta][64]
   const int nb = (S + kBlk - 1) / kBlk;
-  const int kbk = int(blockIdx.y);
-  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int b = bh / H, h = bh % H;
   const int64_t ld = 3 * int64_t(D);
   const bf16_t* Qg = qkv + int64_t(b) * S * ld + h * DH;
   const bf16_t* Kg = Qg + D;
   const bf16_t* Vg = Qg + 2 * D;
   const bf16_t* Og = dctx + int64_t(b) * S * D + h * DH;
   const float* Lg = lse2 + int64_t(bh) * S;
-  const float* Dg = delta + int64_t(bh) * S;
+  const bf16_t* Cg = ctx + int64_t(b) * S * D + h * DH;
   const int key = kbk * kBlk + wl * 16 + ln;  // this lane's key (column of S)
   bf16x8_t kf[KS], vf[KS];
 #pragma unroll
@@ -356,15 +356,15 @@ __global__ __launch_bounds__(512) void flash_dkdv_kernel(
   const int q_first = causal ? kbk : 0;
   const int nqb = nb - q_first;
   const int iters = (nqb + kGroups - 1) / kGroups;
-  TileLoad<DH> lq, lo;
-  float lsv = 0.f, dlv = 0.f;
+  TileLoad<DH> lq, lo, lc;  // Q, dO and O of a query block
+  float lsv = 0.f;
   auto load_blk = [&](int qb) {
     lq.load(Qg, ld, qb * kBlk, S, gt);
     lo.load(Og, D, qb * kBlk, S, gt);
+    lc.load(Cg, D, qb * kBlk, S, gt);
     if (gt < kBlk) {
       const int qq = qb * kBlk + gt;
       lsv = qq < S ? Lg[qq] : INFINITY;
-      dlv = qq < S ? Dg[qq] : 0.f;
     }
   };
   if (grp < nqb) load_blk(q_first + grp);
@@ -379,9 +379,24 @@ __global__ __launch_bounds__(512) void flash_dkdv_kernel(
     if (have) {
       lq.store(qt, gt);
       lo.store(ot, gt);
-      if (gt < kBlk) {
-        ls_s[gt] = lsv;
-        dl_s[gt] = dlv;
+      if (gt < kBlk) ls_s[gt] = lsv;
+      // delta = rowsum(dO * O) of the block's rows: chunk i of this thread is
+      // 8 columns of row (gt + 256 i) / CPR, the CPR consecutive threads of a
+      // row add their dot products in a fixed butterfly
+      constexpr int CPR = TileLoad<DH>::CPR;
+#pragma unroll
+      for (int i = 0; i < TileLoad<DH>::PER; ++i) {
+        const uint32_t av[4] = {lo.v[i].x, lo.v[i].y, lo.v[i].z, lo.v[i].w};
+        const uint32_t cv[4] = {lc.v[i].x, lc.v[i].y, lc.v[i].z, lc.v[i].w};
+        float dsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dsum = fmaf(__uint_as_float(av[e] << 16), __uint_as_float(cv[e] << 16), dsum);
+          dsum = fmaf(__uint_as_float(av[e] & 0xffff0000u), __uint_as_float(cv[e] & 0xffff0000u), dsum);
+        }
+#pragma unroll
+        for (int m = CPR / 2; m > 0; m >>= 1) dsum += __shfl_xor(dsum, m, 64);
+        if (gt % CPR == 0) dl_s[(gt + 256 * i) / CPR] = dsum;
       }
     }
     __syncthreads();
@@ -453,16 +468,13 @@ __global__ __launch_bounds__(512) void flash_dkdv_kernel(
   }
 }
 
-// dQ for one query block: grid (B*H, query blocks); the groups split the key
-// blocks.  It also computes the block's row sums delta = rowsum(dO * O) (each
-// lane a 32-column share of its query row, then the four lane groups added in
-// a fixed order), uses them and writes them for the dK / dV kernel, which runs
-// after it.
+// dQ for query block qb of (sequence, head) bh; the groups split the key
+// blocks.  Each computes the block's row sums delta = rowsum(dO * O) itself.
 template <int DH>
-__global__ __launch_bounds__(512) void flash_dq_kernel(
+__device__ __forceinline__ void flash_dq_body(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ ctx,
-    const bf16_t* __restrict__ dctx, const float* __restrict__ lse2, float* __restrict__ delta,
-    bf16_t* __restrict__ dqkv, int S, int H, int D, int causal, float sl2, float scale) {
+    const bf16_t* __restrict__ dctx, const float* __restrict__ lse2, bf16_t* __restrict__ dqkv,
+    int S, int H, int D, int causal, float sl2, float scale, int bh, int qb) {
   constexpr int KS = DH / 32;
   constexpr int DT = DH / 16;
   constexpr int TE = attn_tile_elems<DH>();
@@ -470,8 +482,7 @@ __global__ __launch_bounds__(512) void flash_dq_kernel(
   const int grp = w >> 2, wl = w & 3, gt = threadIdx.x & 255;
   bf16_t* gbase = attn_smem + grp * 4 * TE;  // [buffer][K, V]
   const int nb = (S + kBlk - 1) / kBlk;
-  const int qb = nb - 1 - int(blockIdx.y);
-  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int b = bh / H, h = bh % H;
   const int64_t ld = 3 * int64_t(D);
   const bf16_t* Qg = qkv + int64_t(b) * S * ld + h * DH;
   const bf16_t* Kg = Qg + D;
@@ -485,7 +496,7 @@ __global__ __launch_bounds__(512) void flash_dq_kernel(
     of[ks] = gfrag(Og, D, q, S, ks * 32 + 8 * g);
   }
   const float lq = q < S ? lse2[int64_t(bh) * S + q] : INFINITY;
-  float dq_ = 0.f;  // delta of query q
+  float dq_ = 0.f;  // delta of query q: each lane a 32-column share, the four lane groups added
   {
     const bf16_t* Cg = ctx + int64_t(b) * S * D + h * DH;
 #pragma unroll
@@ -496,7 +507,6 @@ __global__ __launch_bounds__(512) void flash_dq_kernel(
     }
     dq_ += __shfl_xor(dq_, 16, 64);
     dq_ += __shfl_xor(dq_, 32, 64);
-    if (grp == 0 && g == 0 && q < S) delta[int64_t(bh) * S + q] = dq_;
   }
   floatx4_t acc[DT];
 #pragma unroll
@@ -575,6 +585,24 @@ __global__ __launch_bounds__(512) void flash_dq_kernel(
   }
 }
 
+// The backward of the attention in one launch: grid (B*H, 2 * blocks); y <
+// blocks: dQ of query block blocks-1-y (longest causal rows first), else dK /
+// dV of key block y-blocks (key block 0, the longest, first).  The dQ and the
+// dK/dV blocks are independent, so a CU that finishes a short one takes the
+// next.
+template <int DH>
+__global__ __launch_bounds__(512) void flash_bwd_kernel(
+    const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ ctx,
+    const bf16_t* __restrict__ dctx, const float* __restrict__ lse2, bf16_t* __restrict__ dqkv,
+    int S, int H, int D, int causal, float sl2, float scale) {
+  const int nb = (S + kBlk - 1) / kBlk;
+  const int y = int(blockIdx.y), bh = int(blockIdx.x);
+  if (y < nb)
+    flash_dq_body<DH>(qkv, ctx, dctx, lse2, dqkv, S, H, D, causal, sl2, scale, bh, nb - 1 - y);
+  else
+    flash_dkdv_body<DH>(qkv, ctx, dctx, lse2, dqkv, S, H, D, causal, sl2, scale, bh, y - nb);
+}
+
 // Sets the dynamic-LDS limit of a kernel once.
 template <class K>
 hipError_t allow_smem(K kernel, int bytes) {
@@ -587,8 +615,7 @@ hipError_t attn_attrs() {
   static const hipError_t e = [] {
     constexpr int sm = attn_smem_bytes<DH>();
     hipError_t r = allow_smem(flash_fwd_kernel<DH>, sm);
-    if (r == hipSuccess) r = allow_smem(flash_dkdv_kernel<DH>, sm);
-    if (r == hipSuccess) r = allow_smem(flash_dq_kernel<DH>, sm);
+    if (r == hipSuccess) r = allow_smem(flash_bwd_kernel<DH>, sm);
     return r;
   }();
   return e;
@@ -622,40 +649,30 @@ hipError_t flash_fwd(const void* qkv, void* ctx, float* lse2, int B, int H, int 
 }
 
 hipError_t flash_bwd(const void* qkv, const void* ctx, const void* dctx, const float* lse2,
-                     float* delta, void* dqkv, int B, int H, int S, int D, int causal,
-                     hipStream_t s, int stage) {
+                     void* dqkv, int B, int H, int S, int D, int causal, hipStream_t s) {
   const int dh = D / H;
   const float scale = 1.0f / sqrtf(float(dh));
   const float sl2 = kLog2e * scale;
-  // (sequence, head) along x: workgroups go to the XCDs round-robin by linear
-  // id, so with B*H a multiple of 8 every block of one (sequence, head) --
-  // which all read the same keys and values -- shares one XCD's L2
-  const dim3 grid(B * H, (S + kBlk - 1) / kBlk);
-  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  const int nb = (S + kBlk - 1) / kBlk;
+  if (B * H == 0 || nb == 0) return hipSuccess;
   const bf16_t* q = static_cast<const bf16_t*>(qkv);
   const bf16_t* o = static_cast<const bf16_t*>(ctx);
   const bf16_t* dO = static_cast<const bf16_t*>(dctx);
   bf16_t* dq = static_cast<bf16_t*>(dqkv);
   if (dh != 128 && dh != 64) return hipErrorInvalidValue;
-  if (stage != 1 && stage != 2) return hipErrorInvalidValue;
   hipError_t e = dh == 128 ? attn_attrs<128>() : attn_attrs<64>();
   if (e != hipSuccess) return e;
   const int sm = dh == 128 ? attn_smem_bytes<128>() : attn_smem_bytes<64>();
-  if (stage == 1) {
-    if (dh == 128)
-      hipLaunchKernelGGL(flash_dkdv_kernel<128>, grid, dim3(512), sm, s, q, dO, lse2, delta, dq, S,
-                         H, D, causal, sl2, scale);
-    else
-      hipLaunchKernelGGL(flash_dkdv_kernel<64>, grid, dim3(512), sm, s, q, dO, lse2, delta, dq, S,
-                         H, D, causal, sl2, scale);
-  } else {
-    if (dh == 128)
-      hipLaunchKernelGGL(flash_dq_kernel<128>, grid, dim3(512), sm, s, q, o, dO, lse2, delta, dq, S,
-                         H, D, causal, sl2, scale);
-    else
-      hipLaunchKernelGGL(flash_dq_kernel<64>, grid, dim3(512), sm, s, q, o, dO, lse2, delta, dq, S,
-                         H, D, causal, sl2, scale);
-  }
+  // (sequence, head) along x: workgroups go to the XCDs round-robin by linear
+  // id, so with B*H a multiple of 8 every block of one (sequence, head) --
+  // which all read the same keys and values -- shares one XCD's L2
+  const dim3 grid(B * H, 2 * nb);
+  if (dh == 128)
+    hipLaunchKernelGGL(flash_bwd_kernel<128>, grid, dim3(512), sm, s, q, o, dO, lse2, dq, S, H, D,
+                       causal, sl2, scale);
+  else
+    hipLaunchKernelGGL(flash_bwd_kernel<64>, grid, dim3(512), sm, s, q, o, dO, lse2, dq, S, H, D,
+                       causal, sl2, scale);
   return hipGetLastError();
 }
 

@@ -26,8 +26,8 @@ namespace {
 //   sets:   remat ? 1 : M micro-batch sets; each set holds, for every layer,
 //           the saved tensors of gpipe_saved (layer 0 has no X slot)
 //   yre:    output of the re-materialized forward [T, D] (remat only)
-//   scores: float32 [B*H, S, ldS]  (forward scores, backward dP); with fused
-//           attention float32 [B*H, S], the row sums of dO * O
+//   scores: float32 [B*H, S, ldS]  (forward scores, backward dP; unfused
+//           attention only)
 //   ds:     act [B*H, S, ldS] (unfused attention only)
 //   r0, r1, dm: float32 [T, D]   (residual-stream gradients, LN input grads)
 //   a0, a1, dctx: act [T, D]
@@ -105,8 +105,8 @@ bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
     return at;
   };
   p->yre = take(remat ? T * D * eb : 0);
-  // unfused attention: scores / dP (f32) and dS; fused: the row sums of dO * O
-  p->scores = take(p->flash ? B * H * S * 4 : pbytes * 4);
+  // unfused attention: scores / dP (f32) and dS
+  p->scores = take(p->flash ? 0 : pbytes * 4);
   p->ds = take(p->flash ? 0 : pbytes * eb);
   p->r0 = take(T * D * 4);
   p->r1 = take(T * D * 4);
@@ -531,9 +531,8 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, const WgradDone& above, W
   if (!ss.join(above.qkv)) return GPIPE_ERR_DEVICE;  // the layer above's QKV weight gradient read dqkv
   if (p.flash) {
     const float* lse2 = static_cast<const float*>(P);
-    // dQ first: it also writes the row sums of dO * O that dK / dV read
-    GP_RUN(x, GPIPE_ROLE_ATTN_DQ, flash_bwd(qkv, ctx, dctx, lse2, dP, dqkv, p.B, H, S, D, cz, x.s, 2));
-    GP_RUN(x, GPIPE_ROLE_ATTN_DKDV, flash_bwd(qkv, ctx, dctx, lse2, dP, dqkv, p.B, H, S, D, cz, x.s, 1));
+    // dQ, dK and dV in one launch
+    GP_RUN(x, GPIPE_ROLE_ATTN_DQ, flash_bwd(qkv, ctx, dctx, lse2, dqkv, p.B, H, S, D, cz, x.s));
   } else {
     GP_RUN(x, GPIPE_ROLE_DP, bmm(x, GPIPE_ROLE_DP, S, S, dh, DC, V, DP,
                  cz ? CAUSAL_SKIP_UPPER : CAUSAL_NONE, 1.0f));

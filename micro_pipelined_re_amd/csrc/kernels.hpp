@@ -161,10 +161,9 @@ hipError_t bn_running(const float* rec, int M, int nbn, int C, int64_t n_total, 
 bool flash_ok(bool bf16, int dh);
 hipError_t flash_fwd(const void* qkv, void* ctx, float* lse2, int B, int H, int S, int D,
                      int causal, hipStream_t s);
-// stage 2: dQ, and delta = rowsum(dctx * ctx) (written); then stage 1: dK, dV (reads delta)
+// dQ, dK and dV in one launch (each block computes the row sums rowsum(dctx * ctx) it needs)
 hipError_t flash_bwd(const void* qkv, const void* ctx, const void* dctx, const float* lse2,
-                     float* delta, void* dqkv, int B, int H, int S, int D, int causal,
-                     hipStream_t s, int stage);
+                     void* dqkv, int B, int H, int S, int D, int causal, hipStream_t s);
 
 // Tap-flipped, transposed 3 x 3 weights: dst[c][t][o] = src[o][8 - t][c] (bf16, C x C x 9);
 // the input gradient of a convolution is the convolution of its output gradient with them.
