@@ -47,6 +47,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # dominant kernel and mfma_util_gemm come from those launches of the forward
 # roles.
 SECOND_STREAM_ROLES = ("ffn2_wgrad", "ffn1_wgrad", "out_wgrad", "qkv_wgrad")
+CONV_FORWARD_ROLES = ("conv_fwd_implicit", "bn_stats", "bn_apply")
 ALONE_ROLES = ("ln1_fwd", "qkv_fwd", "scores_fwd", "softmax_fwd", "pv_fwd", "attn_fwd", "out_fwd",
                "ln2_fwd", "ffn1_fwd", "ffn2_fwd", "mse")
 
@@ -440,8 +441,15 @@ def main():
     # (ranked by the role's time in a whole step: its average launch times its
     # launches per step -- the forward roles are timed in one micro-batch's
     # re-materialization but launch 2 L M times)
+    # (the conv cell's forward phase runs on lanes too, bf16 with implicit
+    # convolutions: its forward roles are timed in the re-materializations,
+    # half of their launches)
+    conv_lanes = (conv and remat and cfg.precision == "bf16" and cfg.channels % 64 == 0
+                  and cfg.blocks >= 2)
     def step_launches(name, cnt):
-        if conv or name not in ALONE_ROLES or name == "mse":
+        if conv:
+            return 2 * cnt if conv_lanes and name in CONV_FORWARD_ROLES else cnt
+        if name not in ALONE_ROLES or name == "mse":
             return cnt
         return 2 * cfg.layers * m
     dominant = max((k for k in prof if single_kernel(k)),
@@ -490,6 +498,9 @@ def main():
         if not conv and name in ALONE_ROLES and name != "mse":
             e["timed"] = "micro-batch 0's re-materialization, caller's stream alone"
             e["launches_per_step_all"] = 2 * cfg.layers * m
+        if conv_lanes and name in CONV_FORWARD_ROLES:
+            e["timed"] = "re-materializations only (the forward phase runs on three streams)"
+            e["launches_per_step_all"] = 2 * cnt
         if kind == "mfma":
             tf = per / (ms_tot / cnt * 1e-3) / 1e12
             pk = PEAK_BF16_TFLOPS if cfg.precision == "bf16" else PEAK_FP32_TFLOPS

@@ -32,6 +32,10 @@ struct CPlan {
   size_t block_bytes, set_bytes;
   int nsets;
   size_t yre, col, dcol, r0, r1, dz, part, sums, rec, msepart, splitk, wflip;
+  // forward-phase lanes (see conv_cell_step): count, and the BN / split-K
+  // partials of lanes 1 and 2 (lane 0 uses part and splitk)
+  int lanes;
+  size_t lane_part[3], lane_splitk[3];
   int mse_nblk;
   size_t total;
 };
@@ -88,6 +92,17 @@ bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
                               gemm_partial_floats(GPIPE_ROLE_CONV_DGRAD_IMPLICIT, bf, Pi, Ci, 9 * Ci, 1),
                               gemm_partial_floats(GPIPE_ROLE_CONV_WGRAD_IMPLICIT, bf, Ci, 9 * Ci, Pi, 1)});
   p->splitk = take(sk * 4);
+  // lanes of the forward phase: implicit convolutions and at least two
+  // blocks (their partials are laid out with or without re-materialization,
+  // so that the two workspaces differ by the saved sets only)
+  p->lanes = p->implicit && c->L >= 2 ? std::min(3, c->L) : 1;
+  const size_t skf = gemm_partial_floats(GPIPE_ROLE_CONV_FWD_IMPLICIT, bf, Pi, Ci, 9 * Ci, 1);
+  p->lane_part[0] = p->part;
+  p->lane_splitk[0] = p->splitk;
+  for (int k = 1; k < 3; ++k) {
+    p->lane_part[k] = take(k < p->lanes ? size_t(bn_chunks(int64_t(P))) * 2 * C * 4 : 0);
+    p->lane_splitk[k] = take(k < p->lanes ? skf * 4 : 0);
+  }
   p->total = o;
   return true;
 }
@@ -103,6 +118,7 @@ struct CCtx {
   char* ws;
   hipStream_t s;
   bool bf16;
+  size_t part, splitk;  // workspace offsets of this stream's BN and split-K partials
   const void* wmat(int block, int t) const {
     const size_t off = size_t(block) * c->per_layer + c->rel_off[t];
     if (bf16) return static_cast<const uint16_t*>(c->w_lowp) + off;
@@ -137,7 +153,7 @@ hipError_t cmm(const CCtx& x, int role, int M, int N, int K, const void* A, int6
   g.B = B; g.ldb = ldb;
   g.C = C; g.ldc = ldc;
   g.beta = beta;
-  g.P = x.f(x.p->splitk);
+  g.P = x.f(x.splitk);
   return gemm(x.bf16, role, g, 1, x.s);
 }
 
@@ -155,7 +171,7 @@ hipError_t cconv(const CCtx& x, int role, const void* img, const void* w, void* 
   g.C = out; g.ldc = C;
   g.beta = beta;
   g.conv_h = x.c->Hc; g.conv_w = x.c->Wc; g.conv_c = C;
-  g.P = x.f(x.p->splitk);
+  g.P = x.f(x.splitk);
   return gemm(true, role, g, 1, x.s);
 }
 
@@ -181,25 +197,28 @@ gpipe_status cwgrad(const CCtx& x, const void* img, const void* dz, float* grad,
   g.C = grad; g.ldc = 9 * C;
   g.beta = beta;
   g.conv_h = c->Hc; g.conv_w = c->Wc; g.conv_c = C;
-  g.P = x.f(x.p->splitk);
+  g.P = x.f(x.splitk);
   GP_RUN(x, GPIPE_ROLE_CONV_WGRAD_IMPLICIT, gemm(true, GPIPE_ROLE_CONV_WGRAD_IMPLICIT, g, 1, x.s));
   return GPIPE_OK;
 }
 
 // One block forward of one micro-batch; rec (nullable) receives the BN
 // moments [2][2][C] of this block (forward phase only).
-gpipe_status block_forward(const CCtx& x, int set, int l, const void* xin, void* xout, float* rec) {
+// (slot: the block slot of `set` that receives the saved tensors; l: the
+// block whose weights apply -- the same except in the forward phase's lanes)
+gpipe_status block_forward(const CCtx& x, int set, int slot, int l, const void* xin, void* xout,
+                           float* rec) {
   const gpipe_cell* c = x.c;
   const CPlan& p = *x.p;
   const int C = c->C, B = p.B, H = c->Hc, W = c->Wc;
   const int64_t P = p.P;
   void* col = x.at(p.col);
-  void* a = x.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_A));
-  float* st1 = x.f(csaved_at(p, set, l, GPIPE_CONV_SAVED_ST1));
-  void* r = x.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_R));
-  void* z = x.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_Z));
-  float* st2 = x.f(csaved_at(p, set, l, GPIPE_CONV_SAVED_ST2));
-  float* part = x.f(p.part);
+  void* a = x.at(csaved_at(p, set, slot, GPIPE_CONV_SAVED_A));
+  float* st1 = x.f(csaved_at(p, set, slot, GPIPE_CONV_SAVED_ST1));
+  void* r = x.at(csaved_at(p, set, slot, GPIPE_CONV_SAVED_R));
+  void* z = x.at(csaved_at(p, set, slot, GPIPE_CONV_SAVED_Z));
+  float* st2 = x.f(csaved_at(p, set, slot, GPIPE_CONV_SAVED_ST2));
+  float* part = x.f(x.part);
   if (p.implicit) {
     GP_RUN(x, GPIPE_ROLE_CONV_FWD_IMPLICIT,
            cconv(x, GPIPE_ROLE_CONV_FWD_IMPLICIT, xin, x.wmat(l, GPIPE_CONV_W1), a, 0));
@@ -231,7 +250,7 @@ gpipe_status cell_forward(const CCtx& x, int set, const void* xin, void* yout, f
   for (int l = 0; l < L; ++l) {
     const void* in = l == 0 ? xin : x.at(csaved_at(*x.p, set, l, GPIPE_CONV_SAVED_X));
     void* out = l == L - 1 ? yout : x.at(csaved_at(*x.p, set, l + 1, GPIPE_CONV_SAVED_X));
-    gpipe_status st = block_forward(x, set, l, in, out, rec ? rec + size_t(l) * 4 * C : nullptr);
+    gpipe_status st = block_forward(x, set, l, l, in, out, rec ? rec + size_t(l) * 4 * C : nullptr);
     if (st != GPIPE_OK) return st;
   }
   return GPIPE_OK;
@@ -365,7 +384,7 @@ gpipe_status conv_cell_step(gpipe_cell* c, const void* x, const void* target, vo
       !aligned16(workspace))
     return GPIPE_ERR_INVALID;
   CCtx cx{c, c->prof_mask ? c : nullptr, &p, static_cast<char*>(workspace), stream,
-          c->prec == GPIPE_BF16};
+          c->prec == GPIPE_BF16, p.part, p.splitk};
   const size_t mb = size_t(p.P) * c->C;
   const float inv_denom = float(1.0 / (double(N) * c->Hc * c->Wc * c->C));
   float* rec = cx.f(p.rec);
@@ -378,11 +397,51 @@ gpipe_status conv_cell_step(gpipe_cell* c, const void* x, const void* target, vo
       GP_CHECK(conv_flip_weights(cx.wmat(l, GPIPE_CONV_W2), const_cast<void*>(cx.flipped(l, 1)),
                                  c->C, stream));
     }
-  // phase 1: forward; each micro-batch normalised with its own statistics
-  for (int m = 0; m < M; ++m) {
-    gpipe_status st = cell_forward(cx, remat ? 0 : m, cx.act(x, m * mb), cx.act(y, m * mb),
-                                   rec + m * rec_mb);
-    if (st != GPIPE_OK) return st;
+  // phase 1: forward; each micro-batch normalised with its own statistics.
+  // With re-materialization only the boundary output is kept, so a
+  // micro-batch needs one block's saved tensors, reused block after block
+  // (the block's output overwrites its input, last read by the residual add
+  // of its final BatchNorm apply).  The micro-batches are independent:
+  // micro-batch m runs on lane m mod K (up to 3 streams: the caller's and the
+  // cell's two) in block slot m mod K of set 0, with its own BN and split-K
+  // partials, enqueued block by block so that every stream has work queued.
+  // Launches on the lanes are not role-timed (their times would include the
+  // other streams').
+  if (remat && p.lanes > 1) {
+    {
+      const gpipe_status st = ensure_streams(c);
+      if (st != GPIPE_OK) return st;
+    }
+    Streams ss{c, stream, c->aux, c->aux2};
+    const int K = p.lanes;
+    CCtx lane[3] = {cx, cx, cx};
+    for (int k = 0; k < 3; ++k) {
+      lane[k].prof = nullptr;
+      lane[k].part = p.lane_part[k];
+      lane[k].splitk = p.lane_splitk[k];
+    }
+    lane[1].s = ss.s2;
+    lane[2].s = ss.s3;
+    // (the flipped weights, inputs and weights exist)
+    if (!ss.fork() || (K == 3 && !ss.fork3())) return GPIPE_ERR_DEVICE;
+    for (int m0 = 0; m0 < M; m0 += K)
+      for (int l = 0; l < c->L; ++l)
+        for (int m = m0; m < std::min(M, m0 + K); ++m) {
+          const int k = m % K;
+          void* xs = cx.at(csaved_at(p, 0, k, GPIPE_CONV_SAVED_X));
+          const void* in = l == 0 ? cx.act(x, m * mb) : xs;
+          void* out = l == c->L - 1 ? cx.act(y, m * mb) : xs;
+          gpipe_status st = block_forward(lane[k], 0, k, l, in, out,
+                                          rec + m * rec_mb + size_t(l) * 4 * c->C);
+          if (st != GPIPE_OK) return st;
+        }
+    if (!ss.join_all() || (K == 3 && !ss.join3())) return GPIPE_ERR_DEVICE;
+  } else {
+    for (int m = 0; m < M; ++m) {
+      gpipe_status st = cell_forward(cx, remat ? 0 : m, cx.act(x, m * mb), cx.act(y, m * mb),
+                                     rec + m * rec_mb);
+      if (st != GPIPE_OK) return st;
+    }
   }
   // the moving averages, once per step, from the forward phase's moments
   GP_RUN(cx, GPIPE_ROLE_BN_RUNNING, bn_running(rec, M, 2 * c->L, c->C,

@@ -204,69 +204,6 @@ struct Ctx {
   }
 };
 
-// Ordering of the backward phase's two streams.  The weight gradients do not
-// feed the input-gradient chain, so they run on the cell's second stream
-// (s2) and overlap the chain on the caller's stream (s1): each is enqueued
-// after a fork (s2 waits for everything s1 has enqueued: its operands
-// exist), and s1 joins (waits for the event recorded after a weight
-// gradient) before it overwrites a buffer that weight gradient reads.  s2
-// runs the weight gradients in issue order, so every gradient still sums the
-// micro-batches in order 0 .. M-1.
-struct Streams {
-  gpipe_cell* c;
-  hipStream_t s1, s2, s3;
-  hipEvent_t next() { return c->sync_events[c->sync_next++ % c->sync_events.size()]; }
-  // s2 waits for the work enqueued so far on s1
-  bool fork() {
-    const hipEvent_t e = next();
-    return hipEventRecord(e, s1) == hipSuccess && hipStreamWaitEvent(s2, e, 0) == hipSuccess;
-  }
-  // event recorded on s2 after the work enqueued so far on it
-  bool mark(hipEvent_t* out) {
-    *out = next();
-    return hipEventRecord(*out, s2) == hipSuccess;
-  }
-  // s1 waits for an event of s2 (nullptr: nothing to wait for).  A ring
-  // event recorded again since only makes the wait longer, never shorter.
-  bool join(hipEvent_t e) { return !e || hipStreamWaitEvent(s1, e, 0) == hipSuccess; }
-  bool join_all() {
-    hipEvent_t e;
-    return mark(&e) && join(e);
-  }
-  // s3 waits for the work enqueued so far on s1 and on s2
-  bool fork3() {
-    const hipEvent_t e1 = next(), e2 = next();
-    return hipEventRecord(e1, s1) == hipSuccess && hipEventRecord(e2, s2) == hipSuccess &&
-           hipStreamWaitEvent(s3, e1, 0) == hipSuccess && hipStreamWaitEvent(s3, e2, 0) == hipSuccess;
-  }
-  // s1 waits for the work enqueued so far on s3
-  bool join3() {
-    const hipEvent_t e = next();
-    return hipEventRecord(e, s3) == hipSuccess && hipStreamWaitEvent(s1, e, 0) == hipSuccess;
-  }
-};
-
-// Events of s2 after the weight gradients of one layer's backward.
-struct WgradDone {
-  hipEvent_t ffn2 = nullptr, ffn1 = nullptr, out = nullptr, qkv = nullptr;
-};
-
-// Creates the second stream and the event ring at the first step.
-gpipe_status ensure_streams(gpipe_cell* c) {
-  int dev = -1;
-  GP_CHECK(hipGetDevice(&dev));
-  if (c->aux) return dev == c->aux_device ? GPIPE_OK : GPIPE_ERR_STATE;
-  GP_CHECK(hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking));
-  GP_CHECK(hipStreamCreateWithFlags(&c->aux2, hipStreamNonBlocking));
-  c->aux_device = dev;
-  for (int i = 0; i < 64; ++i) {
-    hipEvent_t e;
-    GP_CHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-    c->sync_events.push_back(e);
-  }
-  return GPIPE_OK;
-}
-
 GemmParams gp0() {
   GemmParams g;
   memset(&g, 0, sizeof(g));
