@@ -432,23 +432,42 @@ def main():
             prof[name] = (ms_tot, cnt)
     # the dominant kernel: the role with the most time whose launch is a single kernel
     # (a split-K GEMM role is two kernels: the split products and their ordered sum)
+    # The conv cell (bf16, implicit convolutions, re-materialization) runs its
+    # forward phase on lanes (not role-timed); with the implicit weight
+    # gradient its backward is pipelined too (weight gradients on a second
+    # stream, micro-batch m+1's re-materialization on a third, not
+    # role-timed), leaving micro-batch 0's re-materialization alone on the
+    # caller's stream.
+    conv_lanes = (conv and remat and cfg.precision == "bf16" and cfg.channels % 64 == 0
+                  and cfg.blocks >= 2)
+    conv_px = (n // m) * cfg.height * cfg.width if conv else 0
+    conv_piped = (conv_lanes and conv_px % 64 == 0 and conv_px < (1 << 21)
+                  and (conv_px + 64) * cfg.channels < (1 << 31))
+
+    def alone(name):
+        if not conv:
+            return name in ALONE_ROLES
+        if conv_piped:
+            return name in CONV_FORWARD_ROLES or name == "mse"
+        return True
+
     def single_kernel(name):
         if name not in work or name in ("bias_grad", "norm_grad", "loss_reduce"):
             return False
-        if not conv and name not in ALONE_ROLES:
+        if not alone(name):
             return False
         return gpipe.gpipe_cell_gemm_plan(cell.handle, n, m, gpipe.ROLES.index(name))[2] <= 1
+
     # (ranked by the role's time in a whole step: its average launch times its
-    # launches per step -- the forward roles are timed in one micro-batch's
-    # re-materialization but launch 2 L M times)
-    # (the conv cell's forward phase runs on lanes too, bf16 with implicit
-    # convolutions: its forward roles are timed in the re-materializations,
-    # half of their launches)
-    conv_lanes = (conv and remat and cfg.precision == "bf16" and cfg.channels % 64 == 0
-                  and cfg.blocks >= 2)
+    # launches per step -- the Transformer's forward roles are timed in one
+    # micro-batch's re-materialization but launch 2 L M times; the conv
+    # cell's forward roles in the re-materializations (all M, or micro-batch
+    # 0's when pipelined) of the 2 M passes)
     def step_launches(name, cnt):
         if conv:
-            return 2 * cnt if conv_lanes and name in CONV_FORWARD_ROLES else cnt
+            if conv_lanes and name in CONV_FORWARD_ROLES:
+                return cnt * (2 * m if conv_piped else 2)
+            return cnt
         if name not in ALONE_ROLES or name == "mse":
             return cnt
         return 2 * cfg.layers * m
@@ -499,8 +518,12 @@ def main():
             e["timed"] = "micro-batch 0's re-materialization, caller's stream alone"
             e["launches_per_step_all"] = 2 * cfg.layers * m
         if conv_lanes and name in CONV_FORWARD_ROLES:
-            e["timed"] = "re-materializations only (the forward phase runs on three streams)"
-            e["launches_per_step_all"] = 2 * cnt
+            e["timed"] = ("micro-batch 0's re-materialization, caller's stream alone" if conv_piped
+                          else "re-materializations only (the forward phase runs on three streams)")
+            e["launches_per_step_all"] = cnt * (2 * m if conv_piped else 2)
+        if conv_piped and not alone(name) and name not in ("loss_reduce", "rmsprop",
+                                                           "bn_running"):
+            e["overlapped"] = "concurrent with the other streams"
         if kind == "mfma":
             tf = per / (ms_tot / cnt * 1e-3) / 1e12
             pk = PEAK_BF16_TFLOPS if cfg.precision == "bf16" else PEAK_FP32_TFLOPS
@@ -534,11 +557,12 @@ def main():
     roof["work_per_launch"] = per
 
     def clean(k):
-        return work.get(k, ("", 0))[0] == "mfma" and (conv or k in ALONE_ROLES)
+        return work.get(k, ("", 0))[0] == "mfma" and alone(k)
     gemm_flops = sum(work[k][1] * src[k][1] for k in src if clean(k))
     gemm_ms = sum(src[k][0] for k in src if clean(k))
     # (the Transformer cell's forward-phase launches are not role-timed: count its work directly)
-    step_flops = (sum(work[k][1] * src[k][1] for k in src if work.get(k, ("", 0))[0] == "mfma")
+    step_flops = (sum(work[k][1] * step_launches(k, src[k][1]) for k in src
+                      if work.get(k, ("", 0))[0] == "mfma")
                   if conv else step_mfma_flops(cfg, n, m))
     keep_bytes = gpipe.gpipe_cell_workspace_bytes(cell.handle, n, m, False)
     act_bytes = x.numel() * x.element_size()

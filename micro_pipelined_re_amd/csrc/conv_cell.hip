@@ -36,6 +36,11 @@ struct CPlan {
   // partials of lanes 1 and 2 (lane 0 uses part and splitk)
   int lanes;
   size_t lane_part[3], lane_splitk[3];
+  // pipelined backward (see conv_cell_step): with re-materialization and the
+  // implicit weight gradient on at least two blocks; wsplitk: the split-K
+  // partials of the weight gradients on the second stream
+  bool piped;
+  size_t wsplitk;
   int mse_nblk;
   size_t total;
 };
@@ -103,6 +108,10 @@ bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
     p->lane_part[k] = take(k < p->lanes ? size_t(bn_chunks(int64_t(P))) * 2 * C * 4 : 0);
     p->lane_splitk[k] = take(k < p->lanes ? skf * 4 : 0);
   }
+  p->piped = remat && p->implicit_wgrad && c->L >= 2;
+  p->wsplitk = take(p->implicit_wgrad && c->L >= 2
+                        ? gemm_partial_floats(GPIPE_ROLE_CONV_WGRAD_IMPLICIT, bf, Ci, 9 * Ci, Pi, 1) * 4
+                        : 0);
   p->total = o;
   return true;
 }
@@ -259,16 +268,28 @@ gpipe_status cell_forward(const CCtx& x, int set, const void* xin, void* yout, f
 // Backward of block l.  r0 holds the gradient w.r.t. the block output and is
 // overwritten in place with the gradient w.r.t. its input (dx_out, if given,
 // receives the act copy).
-gpipe_status block_backward(const CCtx& x, int set, int l, const void* xin, int beta, void* dx_out) {
+// With ss (pipelined backward) the two weight gradients run on the second
+// stream: each is enqueued after a fork (dz exists), and the caller's stream
+// waits for the W2 gradient before BN1's backward overwrites dz, and for the
+// block above's W1 gradient (*dz_reader) before BN2's does; *dz_reader
+// becomes this block's W1 gradient event.
+gpipe_status block_backward(const CCtx& x, Streams* ss, hipEvent_t* dz_reader, int set, int slot,
+                            int l, const void* xin, int beta, void* dx_out) {
   const gpipe_cell* c = x.c;
   const CPlan& p = *x.p;
   const int C = c->C, B = p.B, H = c->Hc, W = c->Wc;
   const int64_t P = p.P;
-  const void* a = x.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_A));
-  const float* st1 = x.f(csaved_at(p, set, l, GPIPE_CONV_SAVED_ST1));
-  const void* r = x.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_R));
-  const void* z = x.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_Z));
-  const float* st2 = x.f(csaved_at(p, set, l, GPIPE_CONV_SAVED_ST2));
+  const void* a = x.at(csaved_at(p, set, slot, GPIPE_CONV_SAVED_A));
+  const float* st1 = x.f(csaved_at(p, set, slot, GPIPE_CONV_SAVED_ST1));
+  const void* r = x.at(csaved_at(p, set, slot, GPIPE_CONV_SAVED_R));
+  const void* z = x.at(csaved_at(p, set, slot, GPIPE_CONV_SAVED_Z));
+  const float* st2 = x.f(csaved_at(p, set, slot, GPIPE_CONV_SAVED_ST2));
+  CCtx w = x;  // the weight gradients' context
+  if (ss) {
+    w.s = ss->s2;
+    w.splitk = p.wsplitk;
+    if (!ss->join(*dz_reader)) return GPIPE_ERR_DEVICE;
+  }
   float* dcol = x.f(p.dcol);
   float* r0 = x.f(p.r0);
   float* r1 = x.f(p.r1);
@@ -281,9 +302,12 @@ gpipe_status block_backward(const CCtx& x, int set, int l, const void* xin, int 
                                       part, sums, x.grad(l, GPIPE_CONV_BN2_G), beta, dz, P, C,
                                       &nch, x.s));
   // z = conv(r, W2)
+  hipEvent_t w2 = nullptr;
   {
-    const gpipe_status st = cwgrad(x, r, dz, x.grad(l, GPIPE_CONV_W2), beta);
+    if (ss && !ss->fork()) return GPIPE_ERR_DEVICE;
+    const gpipe_status st = cwgrad(w, r, dz, x.grad(l, GPIPE_CONV_W2), beta);
     if (st != GPIPE_OK) return st;
+    if (ss && !ss->mark(&w2)) return GPIPE_ERR_DEVICE;
   }
   if (p.implicit) {
     GP_RUN(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT,
@@ -294,13 +318,16 @@ gpipe_status block_backward(const CCtx& x, int set, int l, const void* xin, int 
     GP_RUN(x, GPIPE_ROLE_COL2IM, col2im(x.bf16, dcol, nullptr, r1, nullptr, B, H, W, C, x.s));
   }
   // r = ReLU(BN1(a))
+  if (ss && !ss->join(w2)) return GPIPE_ERR_DEVICE;
   GP_RUN(x, GPIPE_ROLE_BN_BWD, bn_bwd(x.bf16, 1, r1, r, a, st1, x.wf32(l, GPIPE_CONV_BN1_G), part,
                                       sums, x.grad(l, GPIPE_CONV_BN1_G), beta, dz, P, C, &nch,
                                       x.s));
   // a = conv(x, W1); the residual gradient r0 is added in col2im (in place)
   {
-    const gpipe_status st = cwgrad(x, xin, dz, x.grad(l, GPIPE_CONV_W1), beta);
+    if (ss && !ss->fork()) return GPIPE_ERR_DEVICE;
+    const gpipe_status st = cwgrad(w, xin, dz, x.grad(l, GPIPE_CONV_W1), beta);
     if (st != GPIPE_OK) return st;
+    if (ss && !ss->mark(dz_reader)) return GPIPE_ERR_DEVICE;
   }
   if (p.implicit) {
     // the residual gradient already in r0 gets the convolution's input gradient added
@@ -447,12 +474,50 @@ gpipe_status conv_cell_step(gpipe_cell* c, const void* x, const void* target, vo
   GP_RUN(cx, GPIPE_ROLE_BN_RUNNING, bn_running(rec, M, 2 * c->L, c->C,
                                               int64_t(N) * c->Hc * c->Wc, c->bn_momentum,
                                               c->running, stream));
-  // phase 2: re-materialize and backpropagate each micro-batch
+  // phase 2: re-materialize and backpropagate each micro-batch.  Pipelined
+  // (p.piped): the weight gradients run on the second stream, and micro-batch
+  // m+1 re-materializes on the third while micro-batch m's backward frees the
+  // saved set's block slots, from the top block down: m+1 puts block j in the
+  // slot m's block L-1-j held (odd micro-batches take the slots in reverse
+  // order), each block enqueued after that slot's backward and weight
+  // gradients; a block's output goes to its own slot's X tensor (the next
+  // block's input).  Micro-batch 0 re-materializes on the caller's stream.
+  const int L = c->L;
+  std::vector<int> slots(L), next_slots(L);  // block -> slot, this / next micro-batch
+  for (int j = 0; j < L; ++j) slots[j] = j;
+  Streams ss{c, stream, c->aux, c->aux2};
+  CCtx cr = cx;  // the re-materialization's context on the third stream
+  if (p.piped) {
+    const gpipe_status st = ensure_streams(c);
+    if (st != GPIPE_OK) return st;
+    ss = Streams{c, stream, c->aux, c->aux2};
+    cr.s = ss.s3;
+    cr.prof = nullptr;
+    cr.part = p.lane_part[1];
+    cr.splitk = p.lane_splitk[1];
+  }
+  auto remat_block = [&](const CCtx& z, int m, int j, const std::vector<int>& sl) {
+    const void* in = j == 0 ? cx.act(x, m * mb) : z.at(csaved_at(p, 0, sl[j - 1], GPIPE_CONV_SAVED_X));
+    void* out = j == L - 1 ? z.at(p.yre) : z.at(csaved_at(p, 0, sl[j], GPIPE_CONV_SAVED_X));
+    return block_forward(z, 0, sl[j], j, in, out, nullptr);
+  };
+  hipEvent_t dz_reader = nullptr;  // the last weight gradient that read dz
   for (int m = 0; m < M; ++m) {
     const int set = remat ? 0 : m;
     const void* xm = cx.act(x, m * mb);
     const void* ym = cx.act(y, m * mb);
-    if (remat) {
+    if (p.piped) {
+      // the previous micro-batch's weight gradients have read dz and their
+      // slots; this micro-batch's re-materialization is done
+      if (m > 0 && (!ss.join_all() || !ss.join3())) return GPIPE_ERR_DEVICE;
+      dz_reader = nullptr;
+      if (m == 0)
+        for (int j = 0; j < L; ++j) {
+          gpipe_status st = remat_block(cx, 0, j, slots);
+          if (st != GPIPE_OK) return st;
+        }
+      ym = cx.at(p.yre);
+    } else if (remat) {
       gpipe_status st = cell_forward(cx, set, xm, cx.at(p.yre), nullptr);
       if (st != GPIPE_OK) return st;
       ym = cx.at(p.yre);
@@ -461,13 +526,28 @@ gpipe_status conv_cell_step(gpipe_cell* c, const void* x, const void* target, vo
     GP_RUN(cx, GPIPE_ROLE_MSE, mse_fwd_bwd(cx.bf16, ym, cx.act(target, m * mb), cx.f(p.r0),
                                            cx.at(p.dz), msepart + size_t(m) * p.mse_nblk,
                                            int64_t(mb), inv_denom, &nblk, stream));
-    for (int l = c->L - 1; l >= 0; --l) {
-      const void* xin = l == 0 ? xm : cx.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_X));
+    const bool next = p.piped && m + 1 < M;
+    for (int l = L - 1; l >= 0; --l) {
+      const void* xin = l == 0 ? xm
+                        : p.piped ? cx.at(csaved_at(p, set, slots[l - 1], GPIPE_CONV_SAVED_X))
+                                  : cx.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_X));
       void* dxo = (l == 0 && dx) ? cx.act(dx, m * mb) : nullptr;
-      gpipe_status st = block_backward(cx, set, l, xin, m > 0 ? 1 : 0, dxo);
+      gpipe_status st = block_backward(cx, p.piped ? &ss : nullptr, &dz_reader, set, slots[l], l,
+                                       xin, m > 0 ? 1 : 0, dxo);
       if (st != GPIPE_OK) return st;
+      if (next) {
+        // block l's slot is free once its backward (s1) and weight gradients
+        // (s2) are done
+        next_slots[L - 1 - l] = slots[l];
+        if (!ss.fork3()) return GPIPE_ERR_DEVICE;
+        st = remat_block(cr, m + 1, L - 1 - l, next_slots);
+        if (st != GPIPE_OK) return st;
+      }
     }
+    if (next) slots.swap(next_slots);
   }
+  // the weight gradients are complete
+  if (p.piped && !ss.join_all()) return GPIPE_ERR_DEVICE;
   GP_RUN(cx, GPIPE_ROLE_LOSS_REDUCE, sum_partials(msepart, M * p.mse_nblk, 1, 1, loss_dev, 0, stream));
   return GPIPE_OK;
 }
