@@ -77,27 +77,28 @@ constexpr int kCUs = 256;
 }  // namespace
 
 // Tile and split choice, from per-role timings on MI355X with random
-// operands.  The linear layers' products (forward, input gradient, weight
-// gradient) take the specialised-wave kernel: 256 x 128 tiles (128 x 256
-// when both operands are k-contiguous and the output is wider than tall)
-// when the output has at least 192 of them; else, outside the weight
-// gradients and for k < 4096, 128 x 64 tiles when 128 x 128 ones would
-// number at most half the CUs and 128 x 64 ones at least 192 (a 1024 x 2048
-// output at k = 2048, inside the cell's step: 21.0 us against 24.6 us for
-// 128 x 128 tiles; at k = 8192 the narrow tiles re-read the operand that
-// the step brings in cold twice as often and took 60 us against 51 us for
-// 128 x 128 tiles split in two); else 128 x 128 tiles, split in two for
-// k >= 4096 in the forward products only (the input-gradient products run
-// while the weight gradients occupy the second stream, which fills the idle
-// CUs: unsplit, the step takes as long and the split-K reduction, which then
-// contends with the weight gradients' read-modify-write, disappears).  Against 128 x 128 tiles with two workgroups
-// per CU the specialised kernel ran 5-37% faster on every role of the
-// 2048-wide layer.  Weight gradients never split (their fp32 partials would
-// double the accumulator traffic).  The
-// attention products (K = 128 or 512, 32 batches) take 64 x 64 tiles, the
-// convolutions and small products 128 x 128 tiles, where split-K pays only
-// when the output has fewer tiles than CUs; it then aims at about two
-// workgroups per CU with splits at least 512 deep.
+// operands and A/B runs of the whole step.  The linear layers' products
+// (forward, input gradient, weight gradient) take the specialised-wave
+// kernel: 256 x 128 tiles (128 x 256 when both operands are k-contiguous and
+// the output is wider than tall) when the output has at least 192 of them,
+// else 128 x 128 tiles, unsplit.  The step runs these products beside other
+// streams' work (the forward lanes, the weight gradients, the next
+// re-materialization), which fills the CUs a small grid leaves idle, so what
+// pays alone does not in the step: the 1024 x 2048 x 8192 down-projection
+// split in two took 49 us alone against ~60 us unsplit, yet the step ran
+// 166.0 ms with the split and 162.1 ms without; 128 x 64 tiles for the 1024
+// x 2048 outputs at k = 2048 (256 tiles instead of 64) took 21.0 against
+// 24.6 us in the step's own timing, yet the step ran 161.6 ms with them and
+// 160.6 ms without (A/B on one box each).  Against 128 x 128 tiles with two
+// workgroups per CU the specialised kernel ran 5-37% faster on every role of
+// the 2048-wide layer.  Weight gradients never split (their fp32 partials
+// would double the accumulator traffic).  The attention products (K = 128 or
+// 512, 32 batches) take 64 x 64 tiles; the explicit convolutions and small
+// products 128 x 128 tiles of the two-workgroup kernel, where split-K pays
+// only when the output has fewer tiles than CUs: it then aims at about two
+// workgroups per CU with splits at least 512 deep.  The implicit
+// convolutions take 128 x 128 specialised tiles (the weight gradient split
+// to about one workgroup per CU).
 GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch) {
   GemmPlan p{is_attention(role) ? CFG_64x64_K64 : CFG_128x128_K64, 1, K};
   if (!bf16) {
@@ -125,18 +126,9 @@ GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch) {
       return p;
     }
     const long t128 = long((M + 127) / 128) * ((N + 127) / 128);
-    const long t64 = long((M + 127) / 128) * ((N + 63) / 64);
-    if (!is_wgrad(role) && K < 4096 && t128 <= kCUs / 2 && t64 >= 192) {
-      // 128 x 128 tiles would leave half the CUs idle: 128 x 64 tiles fill
-      // the chip (without split-K partials)
-      p.cfg = CFG_128x64_SPEC;
-      return p;
-    }
     if (t128 >= 64) {
-      // fewer big tiles than 3/4 of the CUs: 128 x 128 tiles, and for deep k
-      // two splits (the partial sums cost less than the idle CUs)
+      // fewer big tiles than 3/4 of the CUs: 128 x 128 tiles
       p.cfg = CFG_128x128_SPEC;
-      if (group_of(role) == 0 && K >= 4096 && t128 < 192) split_of(2, 1024);
       return p;
     }
   }
@@ -188,8 +180,7 @@ hipError_t gemm(bool bf16, int role, const GemmParams& g0, int batch, hipStream_
 
 namespace {
 bool spec_cfg(int cfg) {
-  return cfg == CFG_256x128_K64 || cfg == CFG_128x256_K64 || cfg == CFG_128x128_SPEC ||
-         cfg == CFG_128x64_SPEC;
+  return cfg == CFG_256x128_K64 || cfg == CFG_128x256_K64 || cfg == CFG_128x128_SPEC;
 }
 }  // namespace
 

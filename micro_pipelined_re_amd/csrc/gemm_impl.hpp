@@ -537,11 +537,10 @@ enum {
   CFG_128x128_K64 = 2,   // 2 stages x 32 KB, two workgroups per CU
   CFG_128x128_SPEC = 3,  // specialised waves: 3 stages x 32 KB, one workgroup per CU
   CFG_64x64_K64 = 4,     // 3 stages x 16 KB
-  CFG_128x64_SPEC = 5,   // specialised waves: 3 stages x 24 KB, one workgroup per CU
   CFG_N
 };
-constexpr int kCfgBM[CFG_N] = {256, 128, 128, 128, 64, 128};
-constexpr int kCfgBN[CFG_N] = {128, 256, 128, 128, 64, 64};
+constexpr int kCfgBM[CFG_N] = {256, 128, 128, 128, 64};
+constexpr int kCfgBN[CFG_N] = {128, 256, 128, 128, 64};
 
 // Launches one instance (defined in gemm_dma.hpp).
 template <class DC, class RC, int LA, int LB, int EPI, int ROLE>
@@ -607,7 +606,6 @@ hipError_t launch_role(int path, int cfg, const GemmParams& g, int batch, int sp
     switch (cfg) {
       case CFG_256x128_K64: return launch_bf16<DCfg<256, 128, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
       case CFG_128x128_SPEC: return launch_bf16<DCfg<128, 128, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
-      case CFG_128x64_SPEC: return launch_bf16<DCfg<128, 64, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
     }
     return hipErrorInvalidValue;
   } else {
@@ -617,7 +615,6 @@ hipError_t launch_role(int path, int cfg, const GemmParams& g, int batch, int sp
     case CFG_128x128_K64: return launch_bf16<DCfg<128, 128, 64, 2, 2>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
     case CFG_128x128_SPEC: return launch_bf16<DCfg<128, 128, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
     case CFG_64x64_K64: return launch_bf16<DCfg<64, 64, 64, 3, 3>, Cfg<64, 64>, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
-    case CFG_128x64_SPEC: return launch_bf16<DCfg<128, 64, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
   }
   return hipErrorInvalidValue;
   }

@@ -217,10 +217,10 @@ def test_ragged_tiles_specialised_kernel_bf16():
     check(cfg)
 
 
-def test_ragged_narrow_tiles_specialised_kernel_bf16():
-    """128 x 64 tiles of the specialised-wave GEMM with ragged M and N (T = 576,
-    D = 2528, F = 2112: ffn2_fwd and ffn1_dgrad, k-contiguous and m-contiguous B
-    operands), unfused attention (head_dim 632)."""
+def test_ragged_wide_tiles_specialised_kernel_bf16():
+    """128 x 128 tiles of the specialised-wave GEMM with ragged M and N on a wide
+    output (T = 576, D = 2528, F = 2112: ffn2_fwd and ffn1_dgrad, k-contiguous and
+    m-contiguous B operands), unfused attention (head_dim 632)."""
     cfg = configs.SMALL.with_(name="spec_ragged_narrow_bf16", layers=1, d_model=2528, heads=4,
                               d_ff=2112, seq=288, batch=2, micro=1)
     check(cfg)

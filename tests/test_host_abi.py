@@ -380,34 +380,31 @@ def _cell_plans(cfg, N, M, names):
 
 def test_gemm_plan_of_the_2048_cell():
     """Micro-batches of 1024 tokens: the linear products take 256 x 128 / 128 x 256
-    tiles (one workgroup per CU) where the output has at least 192 of them; the
-    1024 x 2048 outputs of the forward and input-gradient products take 128 x 64
-    tiles (256 of them) at k = 2048; at k >= 4096 128 x 128 tiles, split in two
-    for the forward products only (the input-gradient products overlap the
-    weight gradients on the second stream, which fill the idle CUs); weight
-    gradients never split."""
+    tiles (one workgroup per CU) where the output has at least 192 of them, else
+    128 x 128 tiles, unsplit (the step's other streams fill the CUs they leave
+    idle); weight gradients never split."""
     p = _cell_plans(configs.CELL_2048, 64, 32,
                     ["qkv_fwd", "out_fwd", "ffn1_fwd", "ffn2_fwd", "ffn2_dgrad", "ffn1_dgrad",
                      "out_dgrad", "qkv_dgrad", "ffn1_wgrad", "ffn2_wgrad", "qkv_wgrad",
                      "out_wgrad"])
     assert p["qkv_fwd"] == (128, 256, 1) and p["ffn1_fwd"] == (128, 256, 1)
-    assert p["out_fwd"] == (128, 64, 1) and p["ffn2_fwd"] == (128, 128, 2)
+    assert p["out_fwd"] == (128, 128, 1) and p["ffn2_fwd"] == (128, 128, 1)
     assert p["ffn2_dgrad"] == (256, 128, 1)
     assert p["ffn1_dgrad"] == (128, 128, 1) and p["qkv_dgrad"] == (128, 128, 1)
-    assert p["out_dgrad"] == (128, 64, 1)
+    assert p["out_dgrad"] == (128, 128, 1)
     for w in ("ffn1_wgrad", "ffn2_wgrad", "qkv_wgrad"):
         assert p[w] == (256, 128, 1)
     assert p["out_wgrad"] == (128, 128, 1)
 
 
-def test_gemm_plan_of_the_ragged_narrow_tile_case():
-    """The GPU test of the 128 x 64 tiles' ragged edges reaches them: T = 576 and
-    D = 2528 (neither a multiple of the tile), F = 2112, on a k-contiguous (ffn2_fwd)
-    and an m-contiguous (ffn1_dgrad) B operand."""
+def test_gemm_plan_of_the_ragged_wide_case():
+    """The GPU test of ragged 128 x 128 specialised tiles with a wide output reaches
+    them: T = 576 and D = 2528 (neither a multiple of the tile), F = 2112, on a
+    k-contiguous (ffn2_fwd) and an m-contiguous (ffn1_dgrad) B operand."""
     cfg = configs.SMALL.with_(layers=1, d_model=2528, heads=4, d_ff=2112, seq=288)
     p = _cell_plans(cfg, 2, 1, ["ffn2_fwd", "ffn1_dgrad"])
     for n in p:
-        assert p[n] == (128, 64, 1), (n, p[n])
+        assert p[n] == (128, 128, 1), (n, p[n])
 
 
 def test_gemm_plan_of_the_ragged_specialised_case():
