@@ -510,21 +510,21 @@ __device__ __forceinline__ float frag_sum(const bf16x8_t& v, float acc) {
 
 template <class C>
 constexpr int spec_smem_bytes() {
-  constexpr int pipe = 3 * (C::BM + C::BN) * 64 * 2, tile = C::BM * (C::BN + 4) * 4;
+  constexpr int pipe = C::STAGES * (C::BM + C::BN) * 64 * 2, tile = C::BM * (C::BN + 4) * 4;
   return pipe > tile ? pipe : tile;
 }
 
 template <class C, int LA, int LB, int EPI, int ROLE>
 __global__ __launch_bounds__(kSpecThreads, 1) void gemm_spec_kernel(GemmParams g) {
-  constexpr int BM = C::BM, BN = C::BN, BK = 64, FM = C::FM, FN = C::FN;
-  static_assert(C::BK == 64 && C::STAGES == 3, "specialised kernel: 64-deep k-tiles, 3 stages");
+  constexpr int BM = C::BM, BN = C::BN, BK = 64, FM = C::FM, FN = C::FN, S = C::STAGES;
+  static_assert(C::BK == 64 && S >= 3 && S <= 5, "specialised kernel: 64-deep k-tiles, 3-5 stages");
   // (A may be the gathered column matrix of a 3x3 convolution)
   using OA = typename std::conditional<LA == LAY_CONV, DmaConvOperand<BM, BK>,
                                        DmaOperand<BM, BK, LA>>::type;
   using OB = typename std::conditional<LB == LAY_CONV_MN, DmaConvMnOperand<BN, BK>,
                                        DmaOperand<BN, BK, LB>>::type;
   constexpr int LPT = OA::PER_WAVE + OB::PER_WAVE;  // loads per loader wave per k-tile
-  static_assert(LPT * 2 < 64, "vmcnt range");
+  static_assert(LPT * (S - 1) < 64, "vmcnt range");
   constexpr int RA = LA == LAY_MN ? 2 : 1, RB = LB == LAY_MN || LB == LAY_CONV_MN ? 2 : 1;  // LDS reads per fragment
   constexpr int STAGE = (BM + BN) * BK, TP = BN + 4;
   // Weight gradients can also sum A over k (the bias gradient).  The loader
@@ -570,12 +570,12 @@ __global__ __launch_bounds__(kSpecThreads, 1) void gemm_spec_kernel(GemmParams g
     else oa.init(g.lda, m0, g.M, kbeg, cw, lane);
     if constexpr (LB == LAY_CONV_MN) ob.init(g, n0, g.N, kbeg, cw, lane);
     else ob.init(g.ldb, n0, g.N, kbeg, cw, lane);
-    const int pre = min(3, nkt);
+    const int pre = min(S, nkt);
     for (int t = 0; t < pre; ++t) {
       oa.issue(A, t, sa(t), cw);
       ob.issue(B, t, sb(t), cw);
     }
-    wait_tiles<LPT, 2>(pre - 1);  // tile 0 has landed
+    wait_tiles<LPT, S - 1>(pre - 1);  // tile 0 has landed
     barrier_nofence();
     // row sums (RS): tile t is in LDS from barrier t-1 (the prologue barrier
     // for t = 0) until barrier t; this wave's reads end before it arrives there
@@ -597,13 +597,14 @@ __global__ __launch_bounds__(kSpecThreads, 1) void gemm_spec_kernel(GemmParams g
     };
     if (do_rs && rs_lo <= 0 && 0 < rs_hi) add_rows(0);
     for (int kt = 0; kt < nkt; ++kt) {
-      wait_tiles<LPT, 1>(min(1, nkt - 2 - kt));  // tile kt + 1 has landed
+      wait_tiles<LPT, S - 2>(min(S - 2, nkt - 2 - kt));  // tile kt + 1 has landed
       barrier_nofence();
-      if (do_rs && rs_lo <= kt + 1 && kt + 1 < rs_hi) add_rows((kt + 1) % 3);
-      if (kt + 3 < nkt) {
-        const int st = kt % 3;
-        oa.issue(A, kt + 3, sa(st), cw);
-        ob.issue(B, kt + 3, sb(st), cw);
+      if (do_rs && rs_lo <= kt + 1 && kt + 1 < rs_hi) add_rows((kt + 1) % S);
+      // after barrier kt every wave is done with tile kt's stage: refill it
+      if (kt + S < nkt) {
+        const int st = kt % S;
+        oa.issue(A, kt + S, sa(st), cw);
+        ob.issue(B, kt + S, sb(st), cw);
       }
     }
     wait_vmcnt<0>();
@@ -635,7 +636,7 @@ __global__ __launch_bounds__(kSpecThreads, 1) void gemm_spec_kernel(GemmParams g
     constexpr int PER_A = REST / FM;
     int s_cur = 0;
     for (int kt = 0; kt < nkt; ++kt) {
-      const int s_nxt = s_cur == 2 ? 0 : s_cur + 1;
+      const int s_nxt = s_cur == S - 1 ? 0 : s_cur + 1;
       {  // k-step 0 of tile kt; read k-step 1
         const bf16_t* as = sa(s_cur);
         const bf16_t* bs = sb(s_cur);
@@ -810,7 +811,7 @@ hipError_t launch_bf16(int path, const GemmParams& g, int batch, int splits, hip
   if ((LA == LAY_CONV || LB == LAY_CONV_MN) && path != 0) {
     return hipErrorInvalidValue;  // the gathered operands exist only on the direct-to-LDS path
   } else if (path == 0) {
-    if constexpr (DC::OCC == 1 && DC::BK == 64 && DC::STAGES == 3) {
+    if constexpr (DC::OCC == 1 && DC::BK == 64 && DC::STAGES >= 3) {
       constexpr int smem = spec_smem_bytes<DC>();
       static const hipError_t attr = hipFuncSetAttribute(
           reinterpret_cast<const void*>(&gemm_spec_kernel<DC, LA, LB, EPI, ROLE>),

@@ -535,7 +535,7 @@ enum {
   CFG_256x128_K64 = 0,   // specialised waves: 3 stages x 48 KB, one workgroup per CU
   CFG_128x256_K64 = 1,
   CFG_128x128_K64 = 2,   // 2 stages x 32 KB, two workgroups per CU
-  CFG_128x128_SPEC = 3,  // specialised waves: 3 stages x 32 KB, one workgroup per CU
+  CFG_128x128_SPEC = 3,  // specialised waves: 4 stages x 32 KB, one workgroup per CU
   CFG_64x64_K64 = 4,     // 3 stages x 16 KB
   CFG_N
 };
@@ -596,7 +596,7 @@ hipError_t launch_role(int path, int cfg, const GemmParams& g, int batch, int sp
   if constexpr (R::LA == LAY_CONV) {
     // two tile configurations for the gathered operand
     if (cfg == CFG_128x128_SPEC)
-      return launch_bf16<DCfg<128, 128, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch,
+      return launch_bf16<DCfg<128, 128, 64, 4, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch,
                                                                                   splits, s);
     if (cfg != CFG_128x128_K64) return hipErrorInvalidValue;
     return launch_bf16<DCfg<128, 128, 64, 2, 2>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch,
@@ -605,7 +605,7 @@ hipError_t launch_role(int path, int cfg, const GemmParams& g, int batch, int sp
     // the specialised-wave tile configurations for the gathered B operand
     switch (cfg) {
       case CFG_256x128_K64: return launch_bf16<DCfg<256, 128, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
-      case CFG_128x128_SPEC: return launch_bf16<DCfg<128, 128, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
+      case CFG_128x128_SPEC: return launch_bf16<DCfg<128, 128, 64, 4, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
     }
     return hipErrorInvalidValue;
   } else {
@@ -613,7 +613,7 @@ hipError_t launch_role(int path, int cfg, const GemmParams& g, int batch, int sp
     case CFG_256x128_K64: return launch_bf16<DCfg<256, 128, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
     case CFG_128x256_K64: return launch_bf16<DCfg<128, 256, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
     case CFG_128x128_K64: return launch_bf16<DCfg<128, 128, 64, 2, 2>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
-    case CFG_128x128_SPEC: return launch_bf16<DCfg<128, 128, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
+    case CFG_128x128_SPEC: return launch_bf16<DCfg<128, 128, 64, 4, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
     case CFG_64x64_K64: return launch_bf16<DCfg<64, 64, 64, 3, 3>, Cfg<64, 64>, R::LA, R::LB, R::EPI, ROLE>(path, g, batch, splits, s);
   }
   return hipErrorInvalidValue;
