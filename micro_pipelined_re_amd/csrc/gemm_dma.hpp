@@ -353,7 +353,7 @@ __device__ __forceinline__ void epi_store8(const GemmParams& g, int row, int col
         u[e] = a[e] + b[e];
         o[e] = gelu_f(u[e]);
       }
-      st8(static_cast<bf16_t*>(g.U) + int64_t(row) * g.ldu + col, u);
+      if (g.U) st8(static_cast<bf16_t*>(g.U) + int64_t(row) * g.ldu + col, u);
     } else if constexpr (EPI == EPI_GELU_BWD) {
       float u[8];
       ld8(static_cast<const bf16_t*>(g.U) + int64_t(row) * g.ldu + col, u);

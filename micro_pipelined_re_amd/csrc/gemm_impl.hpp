@@ -72,7 +72,7 @@ __device__ __forceinline__ void epi_store(const GemmParams& g, int row, int col,
     static_cast<T*>(g.C)[ci] = from_f<T>(a + g.bias[col] + r);
   } else if constexpr (EPI == EPI_BIAS_GELU) {
     const float u = a + g.bias[col];
-    static_cast<T*>(g.U)[int64_t(row) * g.ldu + col] = from_f<T>(u);
+    if (g.U) static_cast<T*>(g.U)[int64_t(row) * g.ldu + col] = from_f<T>(u);
     static_cast<T*>(g.C)[ci] = from_f<T>(gelu_f(u));
   } else if constexpr (EPI == EPI_GELU_BWD) {
     const float u = to_f<T>(static_cast<const T*>(g.U)[int64_t(row) * g.ldu + col]);

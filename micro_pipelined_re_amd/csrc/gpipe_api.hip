@@ -288,7 +288,9 @@ hipError_t colsum_into(const Ctx& x, int xtype, const void* src, int64_t ld, int
 // (slot: the layer slot of `set` that receives the intermediates; l: the
 // layer whose weights are applied -- the same except in the forward phase's
 // one-slot scratch)
-gpipe_status layer_forward(const Ctx& x, int set, int slot, int l, const void* xin, void* xout) {
+// (keep_u: store the FFN pre-activation u, which only the backward reads)
+gpipe_status layer_forward(const Ctx& x, int set, int slot, int l, const void* xin, void* xout,
+                           bool keep_u = true) {
   const gpipe_cell* c = x.c;
   const Plan& p = *x.p;
   const int T = p.T, D = c->D, F = c->F, S = c->S, H = c->H, dh = D / H;
@@ -331,7 +333,7 @@ gpipe_status layer_forward(const Ctx& x, int set, int slot, int l, const void* x
   GP_RUN(x, GPIPE_ROLE_LN2_FWD, layernorm_fwd(x.bf16, x1, h2, st2, x.wf32(l, GPIPE_LN2_G), x.wf32(l, GPIPE_LN2_B), T, D,
                          c->ln_eps, x.s));
   GP_RUN(x, GPIPE_ROLE_FFN1_FWD, mm(x, GPIPE_ROLE_FFN1_FWD, T, F, D, h2, D, x.wmat(l, GPIPE_W_1), D, g, F,
-              x.wf32(l, GPIPE_B_1), nullptr, 0, u, F));
+              x.wf32(l, GPIPE_B_1), nullptr, 0, keep_u ? u : nullptr, F));
   GP_RUN(x, GPIPE_ROLE_FFN2_FWD, mm(x, GPIPE_ROLE_FFN2_FWD, T, D, F, g, F, x.wmat(l, GPIPE_W_2), F, xout, D,
               x.wf32(l, GPIPE_B_2), x1, D));
   return GPIPE_OK;
@@ -382,7 +384,8 @@ gpipe_status overlapped_forward(const Ctx& cx, Streams& ss, const void* x, void*
         void* xs = z.at(saved_at(p, 0, slot, GPIPE_SAVED_X));
         const void* in = l == 0 ? cx.act(x, m * mb) : xs;
         void* out = l == L - 1 ? cx.act(y, m * mb) : xs;
-        gpipe_status st = layer_forward(z, 0, slot, l, in, out);
+        // (nothing of the layer but its output is read again)
+        gpipe_status st = layer_forward(z, 0, slot, l, in, out, false);
         if (st != GPIPE_OK) return st;
       }
   return ss.join_all() && (K < 3 || ss.join3()) ? GPIPE_OK : GPIPE_ERR_DEVICE;

@@ -18,7 +18,7 @@ enum {
   EPI_STORE = 0,       // C(act) = alpha * acc
   EPI_BIAS = 1,        // C(act) = acc + bias[n]
   EPI_BIAS_RESID = 2,  // C(act) = acc + bias[n] + R(act)[m, n]
-  EPI_BIAS_GELU = 3,   // U(act) = acc + bias[n];  C(act) = gelu(U)
+  EPI_BIAS_GELU = 3,   // U(act) = acc + bias[n] (unless U is null);  C(act) = gelu(U)
   EPI_GELU_BWD = 4,    // C(act) = acc * gelu'(U(act)[m, n])
   EPI_STORE_F32 = 5,   // C(f32) = alpha * acc
   EPI_ACC_F32 = 6,     // C(f32) = (beta ? C : 0) + acc

@@ -197,6 +197,19 @@ __global__ __launch_bounds__(256) void ln_bwd_wave_kernel(const float* __restric
   extern __shared__ float lds[];  // [4][d]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nch = d >> 3;
+  float* out = part + int64_t(blockIdx.x) * 2 * d;
+  // the block's partial row, to be added to (beta), is loaded before the rows
+  // (its own memory round trip overlaps theirs)
+  constexpr int CPT = (NV * 64 + 255) / 256;  // chunks per thread in the fold
+  float prev[2][CPT][8];
+  if (beta)
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int c = threadIdx.x + 256 * j;
+        if (c < nch) load8<float>(out + half * d + c * 8, prev[half][j]);
+      }
   float pg[NV][8], pb[NV][8];
 #pragma unroll
   for (int i = 0; i < NV; ++i)
@@ -242,7 +255,6 @@ __global__ __launch_bounds__(256) void ln_bwd_wave_kernel(const float* __restric
       }
     }
   }
-  float* out = part + int64_t(blockIdx.x) * 2 * d;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -251,7 +263,10 @@ __global__ __launch_bounds__(256) void ln_bwd_wave_kernel(const float* __restric
       if (c < nch) store8<float>(lds + w * d + c * 8, half ? pb[i] : pg[i]);
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < nch; c += 256) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = threadIdx.x + 256 * j;
+      if (c >= nch) continue;
       float s[8], v[8];
       load8<float>(lds + c * 8, s);
 #pragma unroll
@@ -261,9 +276,8 @@ __global__ __launch_bounds__(256) void ln_bwd_wave_kernel(const float* __restric
         for (int e = 0; e < 8; ++e) s[e] += v[e];
       }
       if (beta) {
-        load8<float>(out + half * d + c * 8, v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s[e] += v[e];
+        for (int e = 0; e < 8; ++e) s[e] += prev[half][j][e];
       }
       store8<float>(out + half * d + c * 8, s);
     }
