@@ -214,12 +214,13 @@ gpipe_status gpipe_cell_saved_offset(const gpipe_cell *cell, int N, int M, int r
  * `stream` and the call returns after enqueueing; synchronising `stream`
  * covers the whole step.  A Transformer cell also uses two streams of its
  * own (created at its first step, default priority, on the device current
- * then; a later step on another device returns GPIPE_ERR_STATE).  The second
- * runs the odd micro-batches of the forward phase (remat != 0, bf16 with
- * head dim 64 or 128, at least two layers) and the weight-gradient GEMMs of
- * the backward phase; the third (same conditions) re-materializes micro-
- * batch m+1 layer by layer while micro-batch m's backward frees the saved
- * set's layer slots.  Events order them against `stream` both ways, the
+ * then; a later step on another device returns GPIPE_ERR_STATE).  With
+ * remat != 0, bf16, head dim 64 or 128 and at least two layers, the forward
+ * phase runs groups of consecutive micro-batches (one launch per layer for the
+ * whole group) alternately on `stream` and the cell's streams; the second
+ * stream then runs the weight-gradient GEMMs of the backward phase and the
+ * third re-materializes micro-batch m+1 layer by layer while micro-batch m's
+ * backward frees the saved set's layer slots.  Events order them against `stream` both ways, the
  * weight gradients still accumulate the micro-batches in order and the step
  * is bitwise reproducible.  A cell must not run two steps at once. */
 gpipe_status gpipe_cell_step(gpipe_cell *cell, const void *x, const void *target, void *y,

@@ -351,20 +351,63 @@ gpipe_status cell_forward(const Ctx& x, int set, const void* xin, void* yout) {
 }
 
 // The forward phase with re-materialization keeps nothing but the boundary
-// output, so each micro-batch needs only one layer's intermediates, reused
-// layer after layer (the layer's output overwrites its input, which is last
-// read by the out-projection's residual add).  The micro-batches are
-// independent: micro-batch m runs on lane m mod K (K = 3 streams with at
-// least three layers, else 2) in slot m mod K of the saved set, the lanes
-// after the first with their own split-K partials, so each stream's kernels
-// fill the CUs and launch gaps the others leave; the set is free until the
-// backward phase re-materializes into it, after the streams join.  Launches
-// here are not role-timed (their times would include the other streams').
+// output, so a micro-batch needs only one layer's intermediates, reused layer
+// after layer (the layer's output overwrites its input, which is last read by
+// the out-projection's residual add).  The micro-batches are independent: they
+// run in groups of G consecutive ones (rows contiguous in x and y) per launch,
+// group i on lane i mod K -- the caller's stream and the cell's others, the
+// lanes after the first with their own split-K partials -- in that lane's
+// share of the saved set, so each stream's kernels fill the CUs and launch
+// gaps the others leave; the set is free until the backward phase
+// re-materializes into it, after the streams join.  Launches here are not
+// role-timed (their times would include the other streams').
+// Micro-batches per launch (G) and lanes (K) of the forward phase: two lanes
+// of up to four micro-batches, about 4096 tokens, per launch (each lane takes G
+// layer slots of the set); G = 1 on three lanes when the set has fewer than
+// four slots.  Per row the arithmetic does not depend on G (per-row LayerNorm,
+// per-sequence attention, unsplit products whose k order is the same for every
+// tile shape), so the boundary outputs are bitwise those of one micro-batch per
+// launch.  Two lanes of four 1024-token micro-batches ran the 8-layer 2048-wide
+// step in 156.4 ms against 158.8 (three lanes of one), 157.4 (one lane of
+// eight) and 159.9 (three lanes of two) -- A/B on one box.
+void forward_groups(int L, int M, int T, int* lanes, int* group) {
+  const int G = std::min({L / 2, std::max(1, 4096 / std::max(T, 1)), M});
+  *lanes = G >= 2 ? 2 : std::min(L, 3);
+  *group = std::max(G, 1);
+}
+
+// Layout of one layer slot for g micro-batches at once (every per-row tensor
+// g times longer), with the slot stride `stride`.
+bool group_plan(const gpipe_cell* c, const Plan& p, int g, size_t stride, Plan* q) {
+  Plan t;
+  if (!make_plan(c, g * p.B, 1, 1, &t) || t.layer_bytes > stride) return false;
+  *q = p;
+  q->B = t.B;
+  q->T = t.T;
+  for (int i = 0; i < GPIPE_N_SAVED; ++i) {
+    q->saved_off[i] = t.saved_off[i];
+    q->saved_bytes[i] = t.saved_bytes[i];
+  }
+  q->layer_bytes = stride;
+  return true;
+}
+
 gpipe_status overlapped_forward(const Ctx& cx, Streams& ss, const void* x, void* y, int M,
                                 size_t mb) {
   const Plan& p = *cx.p;
   const int L = cx.c->L;
-  const int K = L >= 3 ? 3 : 2;  // lanes (one layer slot each)
+  int K, G;
+  forward_groups(L, M, p.T, &K, &G);
+  // a group's rows are contiguous in x and y, and its intermediates take
+  // lane k's share of the set: [k, k+1) x the full group's slot size
+  Plan pg[2];
+  {
+    Plan t;
+    if (!make_plan(cx.c, G * p.B, 1, 1, &t) || size_t(K) * t.layer_bytes > p.set_bytes ||
+        !group_plan(cx.c, p, G, t.layer_bytes, &pg[0]) ||
+        !group_plan(cx.c, p, M % G ? M % G : G, t.layer_bytes, &pg[1]))
+      return GPIPE_ERR_INVALID;
+  }
   Ctx lane[3] = {cx, cx, cx};
   for (Ctx& z : lane) z.prof = nullptr;
   lane[1].s = ss.s2;
@@ -372,23 +415,25 @@ gpipe_status overlapped_forward(const Ctx& cx, Streams& ss, const void* x, void*
   lane[2].s = ss.s3;
   lane[2].splitk = p.splitk3;
   // the inputs and weights exist
-  if (!ss.fork() || (K == 3 && !ss.fork3())) return GPIPE_ERR_DEVICE;
-  // K micro-batches are enqueued layer by layer, alternating the streams, so
-  // that all always have work queued (enqueueing a whole micro-batch per
-  // stream let each run dry while the host fed the others)
-  for (int m0 = 0; m0 < M; m0 += K)
+  if ((K >= 2 && !ss.fork()) || (K == 3 && !ss.fork3())) return GPIPE_ERR_DEVICE;
+  // K groups are enqueued layer by layer, alternating the streams, so that
+  // all always have work queued (enqueueing a whole group per stream let each
+  // run dry while the host fed the others)
+  const int ng = (M + G - 1) / G;
+  for (int g0 = 0; g0 < ng; g0 += K)
     for (int l = 0; l < L; ++l)
-      for (int m = m0; m < std::min(M, m0 + K); ++m) {
-        const int slot = m % K;
-        const Ctx& z = lane[slot];
-        void* xs = z.at(saved_at(p, 0, slot, GPIPE_SAVED_X));
+      for (int gi = g0; gi < std::min(ng, g0 + K); ++gi) {
+        const int k = gi % K, m = gi * G;
+        Ctx z = lane[k];
+        z.p = m + G > M ? &pg[1] : &pg[0];
+        void* xs = z.at(saved_at(*z.p, 0, k, GPIPE_SAVED_X));
         const void* in = l == 0 ? cx.act(x, m * mb) : xs;
         void* out = l == L - 1 ? cx.act(y, m * mb) : xs;
         // (nothing of the layer but its output is read again)
-        gpipe_status st = layer_forward(z, 0, slot, l, in, out, false);
+        gpipe_status st = layer_forward(z, 0, k, l, in, out, false);
         if (st != GPIPE_OK) return st;
       }
-  return ss.join_all() && (K < 3 || ss.join3()) ? GPIPE_OK : GPIPE_ERR_DEVICE;
+  return (K < 2 || ss.join_all()) && (K < 3 || ss.join3()) ? GPIPE_OK : GPIPE_ERR_DEVICE;
 }
 
 // Backward of layer l (its saved tensors in layer slot `slot` of `set`).  On

@@ -264,6 +264,26 @@ def test_remat_with_split_products_bitwise_bf16(batch):
     check(cfg)
 
 
+@pytest.mark.parametrize("layers,micro", [(4, 5), (8, 7)])
+def test_grouped_forward_phase_bitwise_bf16(layers, micro):
+    """The forward phase runs several micro-batches per launch (with a shorter
+    last group when they do not divide evenly); its boundary outputs, and the
+    re-materialized intermediates behind every gradient, equal the
+    stored-activation run bit for bit."""
+    cfg = configs.SMALL.with_(name=f"grouped_fwd_l{layers}_m{micro}", layers=layers, d_model=256,
+                              heads=2, d_ff=512, seq=100, batch=2 * micro, micro=micro,
+                              causal=True)
+    params = inputs.cell_params(cfg)
+    x, t = inputs.cell_data(cfg)
+    a = run_gpu(cfg, params, x, t, cfg.batch, cfg.micro, remat=True, update=False)
+    b = run_gpu(cfg, params, x, t, cfg.batch, cfg.micro, remat=False, update=False)
+    assert np.array_equal(a["y"], b["y"])
+    assert np.array_equal(a["dx"], b["dx"])
+    for ga, gb in zip(a["grad"], b["grad"]):
+        for n in gpipe.TENSORS:
+            assert np.array_equal(ga[n], gb[n]), n
+
+
 def test_fused_attention_remat_bitwise_bf16():
     """Remat through the fused attention equals stored activations bit for bit."""
     cfg = configs.SMALL.with_(name="fused_remat", layers=2, d_model=256, heads=2, d_ff=512,
