@@ -460,7 +460,8 @@ def main():
 
     # (ranked by the role's time in a whole step: its average launch times its
     # launches per step -- the Transformer's forward roles are timed in one
-    # micro-batch's re-materialization but launch 2 L M times; the conv
+    # micro-batch's re-materialization but run 2 L M micro-batch passes (the
+    # forward phase's launches take several micro-batches at once); the conv
     # cell's forward roles in the re-materializations (all M, or micro-batch
     # 0's when pipelined) of the 2 M passes)
     def step_launches(name, cnt):
@@ -516,7 +517,8 @@ def main():
                                else "caller's stream") + ", concurrent with the other streams"
         if not conv and name in ALONE_ROLES and name != "mse":
             e["timed"] = "micro-batch 0's re-materialization, caller's stream alone"
-            e["launches_per_step_all"] = 2 * cfg.layers * m
+            # (the forward phase runs these for several micro-batches per launch)
+            e["micro_batch_passes_per_step"] = 2 * cfg.layers * m
         if conv_lanes and name in CONV_FORWARD_ROLES:
             e["timed"] = ("micro-batch 0's re-materialization, caller's stream alone" if conv_piped
                           else "re-materializations only (the forward phase runs on three streams)")
