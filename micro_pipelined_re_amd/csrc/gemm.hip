@@ -89,7 +89,10 @@ constexpr int kCUs = 256;
 // 166.0 ms with the split and 162.1 ms without; 128 x 64 tiles for the 1024
 // x 2048 outputs at k = 2048 (256 tiles instead of 64) took 21.0 against
 // 24.6 us in the step's own timing, yet the step ran 161.6 ms with them and
-// 160.6 ms without (A/B on one box each).  Against 128 x 128 tiles with two
+// 160.6 ms without (A/B on one box each); the input-gradient products of
+// the backward's critical stream split in two (FFN1 1024 x 2048 x 8192, and
+// with it QKV 1024 x 2048 x 6144) ran the step in 160.1 and 162.8 ms
+// against 160.1 unsplit.  Against 128 x 128 tiles with two
 // workgroups per CU the specialised kernel ran 5-37% faster on every role of
 // the 2048-wide layer.  Weight gradients never split (their fp32 partials
 // would double the accumulator traffic).  The attention products (K = 128 or
