@@ -227,6 +227,39 @@ gpipe_status gpipe_cell_step(gpipe_cell *cell, const void *x, const void *target
                              void *dx, int N, int M, int remat, void *workspace, size_t ws_bytes,
                              void *stream, float *loss_dev);
 
+/* The two phases of gpipe_cell_step as separate calls, for cells chained on
+ * one device ("minimal interface design": a model is cut into K cells of
+ * contiguous layers and communication sits only at the cell boundaries; cell
+ * k's output is cell k+1's input, and in the backward pass the gradient with
+ * respect to cell k+1's input is the output gradient of cell k).
+ *
+ * gpipe_cell_forward: phase 1 of "pipeline execution flow" -- every
+ * micro-batch through the cell, y [N, S, D] (NHWC for conv cells) written,
+ * with remat != 0 nothing else kept; conv cells also update the moving
+ * averages as the step does.
+ *
+ * gpipe_cell_backward: phase 2 with the output gradient dy [N, S, D] handed
+ * down by the cell above instead of a loss: for m = 0 .. M-1 in order,
+ * re-materialize micro-batch m (remat != 0), backpropagate dy's rows of m,
+ * accumulate the parameter gradients in float32 into the bound grad
+ * (micro-batch 0 stores, the others add) and write dx [N, S, D] (NULL to
+ * skip).  dy and dx have the cell's activation type (bf16 cells hand bf16
+ * gradients across the boundary).  With remat == 0 the saved activations are
+ * those gpipe_cell_forward left in the workspace, so both calls must get the
+ * same workspace, x, N and M, with no other step of the cell in between; with
+ * remat != 0 the workspace's contents on entry are ignored.
+ *
+ * gpipe_cell_step(x, target) equals gpipe_cell_forward followed by the
+ * backward against the loss's gradient; a stack of cells c_0 .. c_{K-1} takes
+ * forward(c_k, x_k, x_{k+1}) for k < K-1, step(c_{K-1}, x_{K-1}, target) and
+ * then backward(c_k, x_k, dy = dx_{k+1}, dx_k) for k = K-2 .. 0, which is one
+ * step of the whole stack.  Workspace, alignment, stream and error rules as
+ * for gpipe_cell_step; GPIPE_ERR_INVALID also for a null dy. */
+gpipe_status gpipe_cell_forward(gpipe_cell *cell, const void *x, void *y, int N, int M, int remat,
+                                void *workspace, size_t ws_bytes, void *stream);
+gpipe_status gpipe_cell_backward(gpipe_cell *cell, const void *x, const void *dy, void *dx, int N,
+                                 int M, int remat, void *workspace, size_t ws_bytes, void *stream);
+
 /* Phase 3, the single synchronous update: RMSProp over all P parameters,
  *   ms <- decay*ms + (1-decay)*grad^2;  master <- master - lr*grad/(sqrt(ms)+eps)
  * and, for bf16 cells, w_lowp <- bf16(master) (round to nearest even).
@@ -295,6 +328,19 @@ gpipe_status gpipe_cell_profile_read(gpipe_cell *cell, int role, double *total_m
  * Errors: GPIPE_ERR_INVALID for bad N/M or role. */
 gpipe_status gpipe_cell_gemm_plan(const gpipe_cell *cell, int N, int M, int role, int *tile_m,
                                   int *tile_n, int *splits);
+
+/* How the forward phase of gpipe_cell_step(N, M, remat) on a Transformer cell
+ * is launched: on `lanes` streams (1: the caller's stream alone), `group`
+ * consecutive micro-batches per launch (the last group takes the remaining
+ * M mod group), and the bytes of split-K partials each lane owns in the
+ * workspace, which hold the largest split product of any launch of that lane.
+ * Micro-batches share a launch only where every forward product sums over k
+ * in the same order as for one micro-batch, so the forward phase's boundary
+ * outputs are bitwise those the re-materialization reproduces.  Inspection
+ * only; host side, no device work.  Errors: GPIPE_ERR_INVALID for a conv cell
+ * or bad N/M. */
+gpipe_status gpipe_cell_forward_plan(const gpipe_cell *cell, int N, int M, int remat, int *lanes,
+                                     int *group, size_t *lane_partial_bytes);
 
 /* Static string naming a status code. */
 const char *gpipe_status_string(gpipe_status status);

@@ -102,6 +102,12 @@ bool conv_saved_offset(const gpipe_cell* c, int N, int M, int remat, int micro, 
 gpipe_status conv_cell_step(gpipe_cell* c, const void* x, const void* target, void* y, void* dx,
                             int N, int M, int remat, void* workspace, size_t ws_bytes,
                             hipStream_t stream, float* loss_dev);
+// phases: 1 the forward phase (and the moving averages), 2 the backward
+// phase, 3 both; the backward's output gradient is the loss against target,
+// or dy when target is null.
+gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void* target,
+                           const void* dy, void* y, void* dx, int N, int M, int remat,
+                           void* workspace, size_t ws_bytes, hipStream_t stream, float* loss_dev);
 gpipe_status conv_gemm_plan(const gpipe_cell* c, int N, int M, int role, int* tile_m, int* tile_n,
                             int* splits);
 
@@ -113,17 +119,25 @@ gpipe_status conv_gemm_plan(const gpipe_cell* c, int N, int M, int role, int* ti
 // in the input-gradient chain, run on s2 in issue order (so every gradient
 // still sums the micro-batches in order 0 .. M-1) and s1 joins before it
 // overwrites a buffer a weight gradient reads.
+// With `single` set all three are the caller's stream and every ordering
+// call is a no-op (the stream's own order covers it; no event is used).
 struct Streams {
   gpipe_cell* c;
   hipStream_t s1, s2, s3;
+  bool single = false;
   hipEvent_t next() { return c->sync_events[c->sync_next++ % c->sync_events.size()]; }
   // s2 waits for the work enqueued so far on s1
   bool fork() {
+    if (single) return true;
     const hipEvent_t e = next();
     return hipEventRecord(e, s1) == hipSuccess && hipStreamWaitEvent(s2, e, 0) == hipSuccess;
   }
   // event recorded on s2 after the work enqueued so far on it
   bool mark(hipEvent_t* out) {
+    if (single) {
+      *out = nullptr;
+      return true;
+    }
     *out = next();
     return hipEventRecord(*out, s2) == hipSuccess;
   }
@@ -136,12 +150,14 @@ struct Streams {
   }
   // s3 waits for the work enqueued so far on s1 and on s2
   bool fork3() {
+    if (single) return true;
     const hipEvent_t e1 = next(), e2 = next();
     return hipEventRecord(e1, s1) == hipSuccess && hipEventRecord(e2, s2) == hipSuccess &&
            hipStreamWaitEvent(s3, e1, 0) == hipSuccess && hipStreamWaitEvent(s3, e2, 0) == hipSuccess;
   }
   // s1 waits for the work enqueued so far on s3
   bool join3() {
+    if (single) return true;
     const hipEvent_t e = next();
     return hipEventRecord(e, s3) == hipSuccess && hipStreamWaitEvent(s1, e, 0) == hipSuccess;
   }

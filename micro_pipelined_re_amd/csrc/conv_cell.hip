@@ -403,12 +403,22 @@ gpipe_status conv_gemm_plan(const gpipe_cell* c, int N, int M, int role, int* ti
 gpipe_status conv_cell_step(gpipe_cell* c, const void* x, const void* target, void* y, void* dx,
                             int N, int M, int remat, void* workspace, size_t ws_bytes,
                             hipStream_t stream, float* loss_dev) {
+  return conv_cell_run(c, 3, x, target, nullptr, y, dx, N, M, remat, workspace, ws_bytes, stream,
+                       loss_dev);
+}
+
+gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void* target,
+                           const void* dy, void* y, void* dx, int N, int M, int remat,
+                           void* workspace, size_t ws_bytes, hipStream_t stream, float* loss_dev) {
   CPlan p;
   if (!make_cplan(c, N, M, remat, &p)) return GPIPE_ERR_INVALID;
   if (!c->running) return GPIPE_ERR_STATE;
-  if (!x || !target || !y || !workspace || !loss_dev || ws_bytes < p.total) return GPIPE_ERR_INVALID;
-  if (!aligned16(x) || !aligned16(target) || !aligned16(y) || (dx && !aligned16(dx)) ||
-      !aligned16(workspace))
+  const bool fwd = phases & 1, bwd = phases & 2;
+  if (!x || !workspace || ws_bytes < p.total || (fwd && !y)) return GPIPE_ERR_INVALID;
+  // the backward's output gradient: the loss (needs y, target, loss_dev) or dy
+  if (bwd && (target ? (!y || !loss_dev || dy) : !dy)) return GPIPE_ERR_INVALID;
+  if (!aligned16(x) || (target && !aligned16(target)) || (y && !aligned16(y)) ||
+      (dy && !aligned16(dy)) || (dx && !aligned16(dx)) || !aligned16(workspace))
     return GPIPE_ERR_INVALID;
   CCtx cx{c, c->prof_mask ? c : nullptr, &p, static_cast<char*>(workspace), stream,
           c->prec == GPIPE_BF16, p.part, p.splitk};
@@ -417,7 +427,8 @@ gpipe_status conv_cell_step(gpipe_cell* c, const void* x, const void* target, vo
   float* rec = cx.f(p.rec);
   float* msepart = cx.f(p.msepart);
   const size_t rec_mb = size_t(2) * c->L * 2 * c->C;
-  if (p.implicit)
+  // the tap-flipped weights of the input gradients, once per backward phase
+  if (p.implicit && bwd)
     for (int l = 0; l < c->L; ++l) {
       GP_CHECK(conv_flip_weights(cx.wmat(l, GPIPE_CONV_W1), const_cast<void*>(cx.flipped(l, 0)),
                                  c->C, stream));
@@ -434,7 +445,7 @@ gpipe_status conv_cell_step(gpipe_cell* c, const void* x, const void* target, vo
   // partials, enqueued block by block so that every stream has work queued.
   // Launches on the lanes are not role-timed (their times would include the
   // other streams').
-  if (remat && p.lanes > 1) {
+  if (fwd && remat && p.lanes > 1) {
     {
       const gpipe_status st = ensure_streams(c);
       if (st != GPIPE_OK) return st;
@@ -463,7 +474,7 @@ gpipe_status conv_cell_step(gpipe_cell* c, const void* x, const void* target, vo
           if (st != GPIPE_OK) return st;
         }
     if (!ss.join_all() || (K == 3 && !ss.join3())) return GPIPE_ERR_DEVICE;
-  } else {
+  } else if (fwd) {
     for (int m = 0; m < M; ++m) {
       gpipe_status st = cell_forward(cx, remat ? 0 : m, cx.act(x, m * mb), cx.act(y, m * mb),
                                      rec + m * rec_mb);
@@ -471,9 +482,11 @@ gpipe_status conv_cell_step(gpipe_cell* c, const void* x, const void* target, vo
     }
   }
   // the moving averages, once per step, from the forward phase's moments
-  GP_RUN(cx, GPIPE_ROLE_BN_RUNNING, bn_running(rec, M, 2 * c->L, c->C,
-                                              int64_t(N) * c->Hc * c->Wc, c->bn_momentum,
-                                              c->running, stream));
+  if (fwd)
+    GP_RUN(cx, GPIPE_ROLE_BN_RUNNING, bn_running(rec, M, 2 * c->L, c->C,
+                                                int64_t(N) * c->Hc * c->Wc, c->bn_momentum,
+                                                c->running, stream));
+  if (!bwd) return GPIPE_OK;
   // phase 2: re-materialize and backpropagate each micro-batch.  Pipelined
   // (p.piped): the weight gradients run on the second stream, and micro-batch
   // m+1 re-materializes on the third while micro-batch m's backward frees the
@@ -505,7 +518,7 @@ gpipe_status conv_cell_step(gpipe_cell* c, const void* x, const void* target, vo
   for (int m = 0; m < M; ++m) {
     const int set = remat ? 0 : m;
     const void* xm = cx.act(x, m * mb);
-    const void* ym = cx.act(y, m * mb);
+    const void* ym = y ? cx.act(y, m * mb) : nullptr;
     if (p.piped) {
       // the previous micro-batch's weight gradients have read dz and their
       // slots; this micro-batch's re-materialization is done
@@ -522,10 +535,14 @@ gpipe_status conv_cell_step(gpipe_cell* c, const void* x, const void* target, vo
       if (st != GPIPE_OK) return st;
       ym = cx.at(p.yre);
     }
-    int nblk = 0;
-    GP_RUN(cx, GPIPE_ROLE_MSE, mse_fwd_bwd(cx.bf16, ym, cx.act(target, m * mb), cx.f(p.r0),
-                                           cx.at(p.dz), msepart + size_t(m) * p.mse_nblk,
-                                           int64_t(mb), inv_denom, &nblk, stream));
+    if (target) {
+      int nblk = 0;
+      GP_RUN(cx, GPIPE_ROLE_MSE, mse_fwd_bwd(cx.bf16, ym, cx.act(target, m * mb), cx.f(p.r0),
+                                             cx.at(p.dz), msepart + size_t(m) * p.mse_nblk,
+                                             int64_t(mb), inv_denom, &nblk, stream));
+    } else {
+      GP_CHECK(grad_in(cx.bf16, cx.act(dy, m * mb), cx.f(p.r0), cx.at(p.dz), int64_t(mb), stream));
+    }
     const bool next = p.piped && m + 1 < M;
     for (int l = L - 1; l >= 0; --l) {
       const void* xin = l == 0 ? xm
@@ -548,7 +565,8 @@ gpipe_status conv_cell_step(gpipe_cell* c, const void* x, const void* target, vo
   }
   // the weight gradients are complete
   if (p.piped && !ss.join_all()) return GPIPE_ERR_DEVICE;
-  GP_RUN(cx, GPIPE_ROLE_LOSS_REDUCE, sum_partials(msepart, M * p.mse_nblk, 1, 1, loss_dev, 0, stream));
+  if (target)
+    GP_RUN(cx, GPIPE_ROLE_LOSS_REDUCE, sum_partials(msepart, M * p.mse_nblk, 1, 1, loss_dev, 0, stream));
   return GPIPE_OK;
 }
 

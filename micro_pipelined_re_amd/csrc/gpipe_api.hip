@@ -65,8 +65,60 @@ struct Plan {
   size_t gp_off[GPS_N], gp_layer;
   int gp_parts[GPS_N], gp_cols[GPS_N];
   int mse_nblk;
+  // forward phase with re-materialization (overlapped_forward): lanes and
+  // micro-batches per launch; 1 / 1 when that phase runs one micro-batch at
+  // a time on the caller's stream
+  int fwd_lanes, fwd_group;
   size_t total;
 };
+
+// The forward products of one layer over `rows` tokens.
+void forward_shapes(const gpipe_cell* c, int rows, int out[4][4]) {
+  const int D = c->D, F = c->F;
+  const int s[4][4] = {{GPIPE_ROLE_QKV_FWD, rows, 3 * D, D}, {GPIPE_ROLE_OUT_FWD, rows, D, D},
+                       {GPIPE_ROLE_FFN1_FWD, rows, F, D}, {GPIPE_ROLE_FFN2_FWD, rows, D, F}};
+  memcpy(out, s, sizeof(s));
+}
+
+// True when every forward product sums over k the same way at `a` and at `b`
+// rows: the same k-splits of the same depth (an unsplit product accumulates
+// each output in increasing k with the same MFMA instruction whatever the
+// tile, and split partials are summed in split order), so each row's result
+// does not depend on how many rows share the launch.
+bool same_k_order(const gpipe_cell* c, int a, int b) {
+  int sa[4][4], sb[4][4];
+  forward_shapes(c, a, sa);
+  forward_shapes(c, b, sb);
+  const bool bf = c->prec == GPIPE_BF16;
+  for (int i = 0; i < 4; ++i) {
+    const GemmPlan pa = plan_gemm(sa[i][0], bf, sa[i][1], sa[i][2], sa[i][3], 1);
+    const GemmPlan pb = plan_gemm(sb[i][0], bf, sb[i][1], sb[i][2], sb[i][3], 1);
+    const bool ua = pa.splits <= 1, ub = pb.splits <= 1;
+    if (ua != ub || (!ua && (pa.splits != pb.splits || pa.kchunk != pb.kchunk))) return false;
+  }
+  return true;
+}
+
+// Micro-batches per launch (G) and lanes of the forward phase with
+// re-materialization: two lanes of up to four micro-batches, about 4096
+// tokens, per launch (each lane takes G layer slots of the set), provided
+// the grouped launches -- G micro-batches, and the M mod G of the last group
+// -- sum every product in the same k order as one micro-batch (so the
+// boundary outputs are bitwise those the re-materialization reproduces);
+// else one micro-batch per launch on up to three lanes.  Two lanes of four
+// 1024-token micro-batches ran the 8-layer 2048-wide step in 156.4 ms
+// against 158.8 (three lanes of one), 157.4 (one lane of eight) and 159.9
+// (three lanes of two) -- A/B on one box.
+void forward_groups(const gpipe_cell* c, int M, int T, int* lanes, int* group) {
+  const int L = c->L;
+  int G = std::min({L / 2, std::max(1, 4096 / std::max(T, 1)), M});
+  for (; G >= 2; --G) {
+    if (int64_t(G) * T > std::numeric_limits<int>::max()) continue;
+    if (same_k_order(c, T, G * T) && (M % G == 0 || same_k_order(c, T, (M % G) * T))) break;
+  }
+  *lanes = G >= 2 ? 2 : std::min(L, 3);
+  *group = std::max(G, 1);
+}
 
 bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
   if (N <= 0 || M <= 0 || N % M) return false;
@@ -157,6 +209,16 @@ bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
                            {GPIPE_ROLE_OUT_DGRAD, Ti, Di, Di},    {GPIPE_ROLE_QKV_DGRAD, Ti, Di, 3 * Di}};
   size_t sk = 0;
   for (const auto& r : shapes) sk = std::max(sk, gemm_partial_floats(r[0], bf, r[1], r[2], r[3], 1));
+  p->fwd_lanes = p->fwd_group = 1;
+  if (remat && p->flash && c->L >= 2) forward_groups(c, M, Ti, &p->fwd_lanes, &p->fwd_group);
+  // the grouped forward launches (G micro-batches, and the last group's M mod
+  // G) take their lane's partials too
+  for (const int g : {p->fwd_group, M % p->fwd_group}) {
+    if (g < 2) continue;
+    int fs[4][4];
+    forward_shapes(c, g * Ti, fs);
+    for (const auto& r : fs) sk = std::max(sk, gemm_partial_floats(r[0], bf, r[1], r[2], r[3], 1));
+  }
   p->splitk = take(sk * 4);
   // the forward phase's second lane (overlapped_forward) has its own partials
   p->splitk2 = take(sk * 4);
@@ -350,32 +412,6 @@ gpipe_status cell_forward(const Ctx& x, int set, const void* xin, void* yout) {
   return GPIPE_OK;
 }
 
-// The forward phase with re-materialization keeps nothing but the boundary
-// output, so a micro-batch needs only one layer's intermediates, reused layer
-// after layer (the layer's output overwrites its input, which is last read by
-// the out-projection's residual add).  The micro-batches are independent: they
-// run in groups of G consecutive ones (rows contiguous in x and y) per launch,
-// group i on lane i mod K -- the caller's stream and the cell's others, the
-// lanes after the first with their own split-K partials -- in that lane's
-// share of the saved set, so each stream's kernels fill the CUs and launch
-// gaps the others leave; the set is free until the backward phase
-// re-materializes into it, after the streams join.  Launches here are not
-// role-timed (their times would include the other streams').
-// Micro-batches per launch (G) and lanes (K) of the forward phase: two lanes
-// of up to four micro-batches, about 4096 tokens, per launch (each lane takes G
-// layer slots of the set); G = 1 on three lanes when the set has fewer than
-// four slots.  Per row the arithmetic does not depend on G (per-row LayerNorm,
-// per-sequence attention, unsplit products whose k order is the same for every
-// tile shape), so the boundary outputs are bitwise those of one micro-batch per
-// launch.  Two lanes of four 1024-token micro-batches ran the 8-layer 2048-wide
-// step in 156.4 ms against 158.8 (three lanes of one), 157.4 (one lane of
-// eight) and 159.9 (three lanes of two) -- A/B on one box.
-void forward_groups(int L, int M, int T, int* lanes, int* group) {
-  const int G = std::min({L / 2, std::max(1, 4096 / std::max(T, 1)), M});
-  *lanes = G >= 2 ? 2 : std::min(L, 3);
-  *group = std::max(G, 1);
-}
-
 // Layout of one layer slot for g micro-batches at once (every per-row tensor
 // g times longer), with the slot stride `stride`.
 bool group_plan(const gpipe_cell* c, const Plan& p, int g, size_t stride, Plan* q) {
@@ -392,12 +428,23 @@ bool group_plan(const gpipe_cell* c, const Plan& p, int g, size_t stride, Plan* 
   return true;
 }
 
+// The forward phase with re-materialization keeps nothing but the boundary
+// output, so a micro-batch needs only one layer's intermediates, reused layer
+// after layer (the layer's output overwrites its input, which is last read by
+// the out-projection's residual add).  The micro-batches are independent: they
+// run in groups of G consecutive ones (rows contiguous in x and y) per launch,
+// group i on lane i mod K -- the caller's stream and the cell's others, the
+// lanes after the first with their own split-K partials -- in that lane's
+// share of the saved set, so each stream's kernels fill the CUs and launch
+// gaps the others leave; the set is free until the backward phase
+// re-materializes into it, after the streams join.  Launches here are not
+// role-timed (their times would include the other streams').  G and K come
+// from the plan (forward_groups).
 gpipe_status overlapped_forward(const Ctx& cx, Streams& ss, const void* x, void* y, int M,
                                 size_t mb) {
   const Plan& p = *cx.p;
   const int L = cx.c->L;
-  int K, G;
-  forward_groups(L, M, p.T, &K, &G);
+  const int K = p.fwd_lanes, G = p.fwd_group;
   // a group's rows are contiguous in x and y, and its intermediates take
   // lane k's share of the set: [k, k+1) x the full group's slot size
   Plan pg[2];
@@ -562,6 +609,156 @@ gpipe_status reduce_gparts(const Ctx& x) {
   return GPIPE_OK;
 }
 
+// What one call of the Transformer cell's driver does: the forward phase
+// (PH_FWD), the backward phase (PH_BWD) or both (the step).  The backward's
+// output gradient comes from the loss against `target`, or is `dy`, handed
+// down by the cell above.  `single`: every launch on the caller's stream, no
+// stream or event of the cell's own (and no role timing).
+enum { PH_FWD = 1, PH_BWD = 2 };
+struct StepIO {
+  int phases = 0;
+  const void* x = nullptr;
+  const void* target = nullptr;
+  const void* dy = nullptr;
+  void* y = nullptr;
+  void* dx = nullptr;
+  float* loss_dev = nullptr;
+  int N = 0, M = 0, remat = 0;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  hipStream_t s = nullptr;
+  bool single = false;
+};
+
+gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
+  Plan p;
+  if (!make_plan(c, io.N, io.M, io.remat, &p)) return GPIPE_ERR_INVALID;
+  const bool fwd = io.phases & PH_FWD, bwd = io.phases & PH_BWD;
+  const int M = io.M, remat = io.remat;
+  const void* x = io.x;
+  if (!x || !io.ws || io.ws_bytes < p.total) return GPIPE_ERR_INVALID;
+  if (fwd && !io.y) return GPIPE_ERR_INVALID;
+  // the backward's output gradient: the loss (needs y, target, loss_dev) or dy
+  if (bwd && (io.target ? (!io.y || !io.loss_dev || io.dy) : !io.dy)) return GPIPE_ERR_INVALID;
+  if (!aligned16(x) || (io.y && !aligned16(io.y)) || (io.target && !aligned16(io.target)) ||
+      (io.dy && !aligned16(io.dy)) || (io.dx && !aligned16(io.dx)) || !aligned16(io.ws))
+    return GPIPE_ERR_INVALID;
+  if (!io.single) {
+    const gpipe_status st = ensure_streams(c);
+    if (st != GPIPE_OK) return st;
+  }
+  Ctx cx{c, (c->prof_mask && !io.single) ? c : nullptr, &p, io.ws, io.s, c->prec == GPIPE_BF16,
+         p.splitk};
+  Streams ss{c, cx.s, io.single ? cx.s : c->aux, io.single ? cx.s : c->aux2, io.single};
+  const size_t mb = size_t(p.T) * c->D;  // elements per micro-batch
+  const float inv_denom = float(1.0 / (double(io.N) * c->S * c->D));
+  float* msepart = static_cast<float*>(cx.at(p.msepart));
+  const int L = c->L;
+  // several streams (the grouped forward, the pipelined re-materialization)
+  // where the fused attention and two or more layers make them pay
+  const bool lanes = remat && p.flash && L >= 2 && !io.single;
+
+  // phase 1: forward, boundary output only (intermediates are overwritten)
+  if (fwd) {
+    if (lanes) {
+      gpipe_status st = overlapped_forward(cx, ss, x, io.y, M, mb);
+      if (st != GPIPE_OK) return st;
+    } else {
+      for (int m = 0; m < M; ++m) {
+        const int set = remat ? 0 : m;
+        gpipe_status st = cell_forward(cx, set, cx.act(x, m * mb), cx.act(io.y, m * mb));
+        if (st != GPIPE_OK) return st;
+      }
+    }
+  }
+  if (!bwd) return GPIPE_OK;
+  // phase 2: backward with re-materialization and float32 accumulation.
+  // With fused attention the re-materialization of micro-batch m+1 runs on
+  // the third stream during the backward of micro-batch m, in the one saved
+  // set: the backward frees the layer slots from the top down and the
+  // re-materialization fills them from the bottom up, so micro-batch m+1
+  // puts layer j in the slot that layer L-1-j of micro-batch m held (odd
+  // micro-batches take the slots in reverse order), each layer enqueued
+  // after that slot's backward and weight gradients.  A layer's output goes
+  // to its own slot's X tensor (the next layer's input).  Micro-batch 0
+  // re-materializes on the caller's stream before its backward.
+  const bool piped = lanes;
+  auto slot_of = [&](int m, int j) { return (piped && (m & 1)) ? L - 1 - j : j; };
+  Ctx cr = cx;  // the re-materialization's context on the third stream
+  cr.s = ss.s3;
+  cr.prof = nullptr;
+  cr.splitk = p.splitk2;
+  auto remat_layer = [&](const Ctx& z, int m, int j) {
+    const void* in = j == 0 ? cx.act(x, m * mb) : z.at(saved_at(p, 0, slot_of(m, j - 1), GPIPE_SAVED_X));
+    void* out = j == L - 1 ? z.at(p.yre) : z.at(saved_at(p, 0, slot_of(m, j), GPIPE_SAVED_X));
+    return layer_forward(z, 0, slot_of(m, j), j, in, out);
+  };
+  for (int m = 0; m < M; ++m) {
+    const int set = remat ? 0 : m;
+    const void* xm = cx.act(x, m * mb);
+    const void* ym = io.y ? cx.act(io.y, m * mb) : nullptr;
+    // every weight gradient of the previous micro-batch has read the saved
+    // activations and the transient gradients this one overwrites
+    if (m > 0 && !ss.join_all()) return GPIPE_ERR_DEVICE;
+    if (piped) {
+      if (m == 0) {
+        for (int j = 0; j < L; ++j) {
+          gpipe_status st = remat_layer(cx, 0, j);
+          if (st != GPIPE_OK) return st;
+        }
+      } else if (!ss.join3()) {  // this micro-batch's re-materialization is done
+        return GPIPE_ERR_DEVICE;
+      }
+      ym = cx.at(p.yre);
+    } else if (remat) {
+      void* yre = cx.at(p.yre);
+      gpipe_status st = cell_forward(cx, set, xm, yre);
+      if (st != GPIPE_OK) return st;
+      ym = yre;
+    }
+    if (io.target) {
+      int nblk = 0;
+      GP_RUN(cx, GPIPE_ROLE_MSE, mse_fwd_bwd(cx.bf16, ym, cx.act(io.target, m * mb),
+                                             static_cast<float*>(cx.at(p.r0)), cx.at(p.a0),
+                                             msepart + size_t(m) * p.mse_nblk, int64_t(mb),
+                                             inv_denom, &nblk, cx.s));
+    } else {
+      GP_CHECK(grad_in(cx.bf16, cx.act(io.dy, m * mb), static_cast<float*>(cx.at(p.r0)), cx.at(p.a0),
+                       int64_t(mb), cx.s));
+    }
+    WgradDone above;  // the top layer has none above it in this micro-batch
+    for (int l = L - 1; l >= 0; --l) {
+      // (the layer's input: the output of layer l-1, in that layer's slot when
+      // pipelined, else in this layer's X tensor)
+      const void* xin = l == 0 ? xm
+                        : piped ? cx.at(saved_at(p, set, slot_of(m, l - 1), GPIPE_SAVED_X))
+                                : cx.at(saved_at(p, set, l, GPIPE_SAVED_X));
+      void* dxo = (l == 0 && io.dx) ? cx.act(io.dx, m * mb) : nullptr;
+      WgradDone mine;
+      gpipe_status st = layer_backward(cx, ss, above, &mine, set, slot_of(m, l), l, xin,
+                                       m > 0 ? 1 : 0, dxo);
+      if (st != GPIPE_OK) return st;
+      above = mine;
+      if (piped && m + 1 < M) {
+        // layer l's slot is free once its backward (s1) and weight gradients (s2)
+        // are done
+        if (!ss.fork3()) return GPIPE_ERR_DEVICE;
+        st = remat_layer(cr, m + 1, L - 1 - l);
+        if (st != GPIPE_OK) return st;
+      }
+    }
+  }
+  // the weight gradients (and their bias partial sums) are complete
+  if (!ss.join_all()) return GPIPE_ERR_DEVICE;
+  {
+    gpipe_status st = reduce_gparts(cx);
+    if (st != GPIPE_OK) return st;
+  }
+  if (io.target)
+    GP_RUN(cx, GPIPE_ROLE_LOSS_REDUCE, sum_partials(msepart, M * p.mse_nblk, 1, 1, io.loss_dev, 0, cx.s));
+  return GPIPE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -719,113 +916,46 @@ gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, v
   if (c->kind == CELL_CONV)
     return conv_cell_step(c, x, target, y, dx, N, M, remat, workspace, ws_bytes,
                           static_cast<hipStream_t>(stream), loss_dev);
-  Plan p;
-  if (!make_plan(c, N, M, remat, &p)) return GPIPE_ERR_INVALID;
-  if (!x || !target || !y || !workspace || !loss_dev || ws_bytes < p.total) return GPIPE_ERR_INVALID;
-  if (!aligned16(x) || !aligned16(target) || !aligned16(y) || (dx && !aligned16(dx)) ||
-      !aligned16(workspace))
-    return GPIPE_ERR_INVALID;
-  {
-    const gpipe_status st = ensure_streams(c);
-    if (st != GPIPE_OK) return st;
-  }
-  Ctx cx{c, c->prof_mask ? c : nullptr, &p, static_cast<char*>(workspace),
-         static_cast<hipStream_t>(stream), c->prec == GPIPE_BF16, p.splitk};
-  Streams ss{c, cx.s, c->aux, c->aux2};
-  const size_t mb = size_t(p.T) * c->D;  // elements per micro-batch
-  const float inv_denom = float(1.0 / (double(N) * c->S * c->D));
-  float* msepart = static_cast<float*>(cx.at(p.msepart));
+  StepIO io;
+  io.phases = PH_FWD | PH_BWD;
+  io.x = x; io.target = target; io.y = y; io.dx = dx; io.loss_dev = loss_dev;
+  io.N = N; io.M = M; io.remat = remat;
+  io.ws = static_cast<char*>(workspace); io.ws_bytes = ws_bytes;
+  io.s = static_cast<hipStream_t>(stream);
+  return transformer_run(c, io);
+}
 
-  // phase 1: forward, boundary output only (intermediates are overwritten)
-  if (remat && p.flash && c->L >= 2) {
-    gpipe_status st = overlapped_forward(cx, ss, x, y, M, mb);
-    if (st != GPIPE_OK) return st;
-  } else {
-    for (int m = 0; m < M; ++m) {
-      const int set = remat ? 0 : m;
-      gpipe_status st = cell_forward(cx, set, cx.act(x, m * mb), cx.act(y, m * mb));
-      if (st != GPIPE_OK) return st;
-    }
-  }
-  // phase 2: backward with re-materialization and float32 accumulation.
-  // With fused attention the re-materialization of micro-batch m+1 runs on
-  // the third stream during the backward of micro-batch m, in the one saved
-  // set: the backward frees the layer slots from the top down and the
-  // re-materialization fills them from the bottom up, so micro-batch m+1
-  // puts layer j in the slot that layer L-1-j of micro-batch m held (odd
-  // micro-batches take the slots in reverse order), each layer enqueued
-  // after that slot's backward and weight gradients.  A layer's output goes
-  // to its own slot's X tensor (the next layer's input).  Micro-batch 0
-  // re-materializes on the caller's stream before its backward.
-  const int L = c->L;
-  const bool piped = remat && p.flash && L >= 2;
-  auto slot_of = [&](int m, int j) { return (piped && (m & 1)) ? L - 1 - j : j; };
-  Ctx cr = cx;  // the re-materialization's context on the third stream
-  cr.s = ss.s3;
-  cr.prof = nullptr;
-  cr.splitk = p.splitk2;
-  auto remat_layer = [&](const Ctx& z, int m, int j) {
-    const void* in = j == 0 ? cx.act(x, m * mb) : z.at(saved_at(p, 0, slot_of(m, j - 1), GPIPE_SAVED_X));
-    void* out = j == L - 1 ? z.at(p.yre) : z.at(saved_at(p, 0, slot_of(m, j), GPIPE_SAVED_X));
-    return layer_forward(z, 0, slot_of(m, j), j, in, out);
-  };
-  for (int m = 0; m < M; ++m) {
-    const int set = remat ? 0 : m;
-    const void* xm = cx.act(x, m * mb);
-    const void* ym = cx.act(y, m * mb);
-    // every weight gradient of the previous micro-batch has read the saved
-    // activations and the transient gradients this one overwrites
-    if (m > 0 && !ss.join_all()) return GPIPE_ERR_DEVICE;
-    if (piped) {
-      if (m == 0) {
-        for (int j = 0; j < L; ++j) {
-          gpipe_status st = remat_layer(cx, 0, j);
-          if (st != GPIPE_OK) return st;
-        }
-      } else if (!ss.join3()) {  // this micro-batch's re-materialization is done
-        return GPIPE_ERR_DEVICE;
-      }
-      ym = cx.at(p.yre);
-    } else if (remat) {
-      void* yre = cx.at(p.yre);
-      gpipe_status st = cell_forward(cx, set, xm, yre);
-      if (st != GPIPE_OK) return st;
-      ym = yre;
-    }
-    int nblk = 0;
-    GP_RUN(cx, GPIPE_ROLE_MSE, mse_fwd_bwd(cx.bf16, ym, cx.act(target, m * mb), static_cast<float*>(cx.at(p.r0)),
-                         cx.at(p.a0), msepart + size_t(m) * p.mse_nblk, int64_t(mb), inv_denom,
-                         &nblk, cx.s));
-    WgradDone above;  // the top layer has none above it in this micro-batch
-    for (int l = L - 1; l >= 0; --l) {
-      // (the layer's input: the output of layer l-1, in that layer's slot when
-      // pipelined, else in this layer's X tensor)
-      const void* xin = l == 0 ? xm
-                        : piped ? cx.at(saved_at(p, set, slot_of(m, l - 1), GPIPE_SAVED_X))
-                                : cx.at(saved_at(p, set, l, GPIPE_SAVED_X));
-      void* dxo = (l == 0 && dx) ? cx.act(dx, m * mb) : nullptr;
-      WgradDone mine;
-      gpipe_status st = layer_backward(cx, ss, above, &mine, set, slot_of(m, l), l, xin,
-                                       m > 0 ? 1 : 0, dxo);
-      if (st != GPIPE_OK) return st;
-      above = mine;
-      if (piped && m + 1 < M) {
-        // layer l's slot is free once its backward (s1) and weight gradients (s2)
-        // are done
-        if (!ss.fork3()) return GPIPE_ERR_DEVICE;
-        st = remat_layer(cr, m + 1, L - 1 - l);
-        if (st != GPIPE_OK) return st;
-      }
-    }
-  }
-  // the weight gradients (and their bias partial sums) are complete
-  if (!ss.join_all()) return GPIPE_ERR_DEVICE;
-  {
-    gpipe_status st = reduce_gparts(cx);
-    if (st != GPIPE_OK) return st;
-  }
-  GP_RUN(cx, GPIPE_ROLE_LOSS_REDUCE, sum_partials(msepart, M * p.mse_nblk, 1, 1, loss_dev, 0, cx.s));
-  return GPIPE_OK;
+gpipe_status gpipe_cell_forward(gpipe_cell* c, const void* x, void* y, int N, int M, int remat,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  if (!c) return GPIPE_ERR_INVALID;
+  if (!c->bound) return GPIPE_ERR_STATE;
+  if (c->kind == CELL_CONV)
+    return conv_cell_run(c, 1, x, nullptr, nullptr, y, nullptr, N, M, remat, workspace, ws_bytes,
+                         static_cast<hipStream_t>(stream), nullptr);
+  StepIO io;
+  io.phases = PH_FWD;
+  io.x = x; io.y = y;
+  io.N = N; io.M = M; io.remat = remat;
+  io.ws = static_cast<char*>(workspace); io.ws_bytes = ws_bytes;
+  io.s = static_cast<hipStream_t>(stream);
+  return transformer_run(c, io);
+}
+
+gpipe_status gpipe_cell_backward(gpipe_cell* c, const void* x, const void* dy, void* dx, int N,
+                                 int M, int remat, void* workspace, size_t ws_bytes, void* stream) {
+  if (!c) return GPIPE_ERR_INVALID;
+  if (!c->bound) return GPIPE_ERR_STATE;
+  if (!dy) return GPIPE_ERR_INVALID;
+  if (c->kind == CELL_CONV)
+    return conv_cell_run(c, 2, x, nullptr, dy, nullptr, dx, N, M, remat, workspace, ws_bytes,
+                         static_cast<hipStream_t>(stream), nullptr);
+  StepIO io;
+  io.phases = PH_BWD;
+  io.x = x; io.dy = dy; io.dx = dx;
+  io.N = N; io.M = M; io.remat = remat;
+  io.ws = static_cast<char*>(workspace); io.ws_bytes = ws_bytes;
+  io.s = static_cast<hipStream_t>(stream);
+  return transformer_run(c, io);
 }
 
 gpipe_status gpipe_apply_update(gpipe_cell* c, float lr, float decay, float eps, void* stream) {
@@ -864,6 +994,18 @@ gpipe_status gpipe_cell_profile_read(gpipe_cell* c, int role, double* total_ms, 
   }
   *total_ms = t;
   *launches = n;
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_cell_forward_plan(const gpipe_cell* c, int N, int M, int remat, int* lanes,
+                                     int* group, size_t* lane_partial_bytes) {
+  if (!c || !lanes || !group || !lane_partial_bytes || c->kind != CELL_TRANSFORMER)
+    return GPIPE_ERR_INVALID;
+  Plan p;
+  if (!make_plan(c, N, M, remat, &p)) return GPIPE_ERR_INVALID;
+  *lanes = p.fwd_lanes;
+  *group = p.fwd_group;
+  *lane_partial_bytes = p.splitk2 - p.splitk;
   return GPIPE_OK;
 }
 

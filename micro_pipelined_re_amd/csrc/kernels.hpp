@@ -117,6 +117,9 @@ hipError_t softmax_bwd(bool bf16, const void* p, const float* dp, void* ds, int6
 hipError_t mse_fwd_bwd(bool bf16, const void* y, const void* t, float* dy_f32, void* dy_act,
                        float* part, int64_t count, float inv_denom, int* nblk, hipStream_t s);
 int mse_blocks(int64_t count);
+// The output gradient handed down by the cell above: dy (act, count a multiple
+// of 8) into dy_f32 and its act copy dy_act.
+hipError_t grad_in(bool bf16, const void* dy, float* dy_f32, void* dy_act, int64_t count, hipStream_t s);
 
 // Column sums: part[chunk][c] = sum over the rows of chunk of x[r, c] (x is f32 or act).
 hipError_t colsum_partial(int xtype, const void* x, int64_t ld, int rows, int cols, float* part,

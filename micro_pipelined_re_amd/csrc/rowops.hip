@@ -445,6 +445,33 @@ hipError_t softmax_bwd(bool bf16, const void* p, const float* dp, void* ds, int6
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ output gradient from the cell above
+// dy (act, `count` elements, a multiple of 8) -> the backward's residual-stream
+// gradient dy_f32 and its act copy dy_act, 8 elements per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void grad_in_kernel(const T* __restrict__ dy, float* __restrict__ dy_f32,
+                                                      T* __restrict__ dy_act, int64_t nch) {
+  for (int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x; c < nch; c += int64_t(gridDim.x) * 256) {
+    float v[8];
+    load8<T>(dy + c * 8, v);
+    store8<float>(dy_f32 + c * 8, v);
+    store8<T>(dy_act + c * 8, v);
+  }
+}
+
+hipError_t grad_in(bool bf16, const void* dy, float* dy_f32, void* dy_act, int64_t count, hipStream_t s) {
+  const int64_t nch = count / 8;
+  if (nch == 0) return hipSuccess;
+  const int blocks = int(std::min<int64_t>((nch + 255) / 256, 2048));
+  if (bf16)
+    hipLaunchKernelGGL(grad_in_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, static_cast<const bf16_t*>(dy),
+                       dy_f32, static_cast<bf16_t*>(dy_act), nch);
+  else
+    hipLaunchKernelGGL(grad_in_kernel<float>, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(dy),
+                       dy_f32, static_cast<float*>(dy_act), nch);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ MSE
 constexpr int kMseBlocks = 256;
 int mse_blocks(int64_t count) {

@@ -26,7 +26,8 @@ EXPORTS = ("gpipe_cell_create", "gpipe_cell_destroy", "gpipe_cell_param_count",
            "gpipe_cell_workspace_bytes", "gpipe_cell_saved_offset", "gpipe_cell_step",
            "gpipe_apply_update", "gpipe_partition", "gpipe_status_string",
            "gpipe_cell_profile", "gpipe_cell_profile_read", "gpipe_cell_gemm_plan",
-           "gpipe_conv_cell_create", "gpipe_cell_bind_running")
+           "gpipe_conv_cell_create", "gpipe_cell_bind_running", "gpipe_cell_forward_plan",
+           "gpipe_cell_forward", "gpipe_cell_backward")
 
 ROLES = ("ln1_fwd", "qkv_fwd", "scores_fwd", "softmax_fwd", "pv_fwd", "out_fwd", "ln2_fwd",
          "ffn1_fwd", "ffn2_fwd", "mse", "ffn2_dgrad", "ffn2_wgrad", "ffn1_dgrad", "ffn1_wgrad",
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
             "gpipe_cell_saved_offset": [_vp, _i, _i, _i, _i, _i, _i, ctypes.POINTER(_sz),
                                         ctypes.POINTER(_sz)],
             "gpipe_cell_step": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp, _vp],
+            "gpipe_cell_forward": [_vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp],
+            "gpipe_cell_backward": [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp],
             "gpipe_apply_update": [_vp, ctypes.c_float, ctypes.c_float, ctypes.c_float, _vp],
             "gpipe_partition": [ctypes.POINTER(ctypes.c_double), _i, _i, ctypes.POINTER(_i),
                                 ctypes.POINTER(ctypes.c_double)],
@@ -76,6 +79,8 @@ def lib() -> ctypes.CDLL:
                                         ctypes.POINTER(ctypes.c_longlong)],
             "gpipe_conv_cell_create": [_i, _i, _i, _i, ctypes.c_float, _i, ctypes.POINTER(_vp)],
             "gpipe_cell_bind_running": [_vp, _vp],
+            "gpipe_cell_forward_plan": [_vp, _i, _i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i),
+                                        ctypes.POINTER(_sz)],
         }
         for name, argtypes in sig.items():
             f = getattr(L, name)
@@ -187,6 +192,18 @@ def gpipe_cell_step(cell, x, target, y, dx, N, M, remat, workspace, ws_bytes, st
                                  _ptr(loss)))
 
 
+def gpipe_cell_forward(cell, x, y, N, M, remat, workspace, ws_bytes, stream) -> None:
+    _check("gpipe_cell_forward",
+           lib().gpipe_cell_forward(cell, _ptr(x), _ptr(y), N, M, int(bool(remat)),
+                                    _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def gpipe_cell_backward(cell, x, dy, dx, N, M, remat, workspace, ws_bytes, stream) -> None:
+    _check("gpipe_cell_backward",
+           lib().gpipe_cell_backward(cell, _ptr(x), _ptr(dy), _ptr(dx), N, M, int(bool(remat)),
+                                     _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def gpipe_apply_update(cell, lr, decay, eps, stream=None) -> None:
     _check("gpipe_apply_update", lib().gpipe_apply_update(cell, lr, decay, eps, _stream(stream)))
 
@@ -218,6 +235,14 @@ def gpipe_cell_gemm_plan(cell, N: int, M: int, role: int):
            lib().gpipe_cell_gemm_plan(cell, N, M, role, ctypes.byref(tm), ctypes.byref(tn),
                                       ctypes.byref(sp)))
     return tm.value, tn.value, sp.value
+
+
+def gpipe_cell_forward_plan(cell, N: int, M: int, remat: bool):
+    lanes, group, nb = _i(), _i(), _sz()
+    _check("gpipe_cell_forward_plan",
+           lib().gpipe_cell_forward_plan(cell, N, M, int(bool(remat)), ctypes.byref(lanes),
+                                         ctypes.byref(group), ctypes.byref(nb)))
+    return lanes.value, group.value, nb.value
 
 
 # ---------------------------------------------------------------- convenience
@@ -312,6 +337,23 @@ class Cell:
         gpipe_cell_step(self.handle, x, t, y, dx if want_dx else None, N, M, remat, ws, nb,
                         stream, self.loss)
         return y, (dx if want_dx else None)
+
+    def forward(self, x, N, M, remat=True, y=None, stream=None):
+        """Phase 1 only: y of every micro-batch (for a cell below others)."""
+        if y is None:
+            y = self.torch.empty_like(x)
+        ws, nb = self.workspace(N, M, remat)
+        gpipe_cell_forward(self.handle, x, y, N, M, remat, ws, nb, stream)
+        return y
+
+    def backward(self, x, dy, N, M, remat=True, want_dx=True, dx=None, stream=None):
+        """Phase 2 with the output gradient dy handed down by the cell above."""
+        if want_dx and dx is None:
+            dx = self.torch.empty_like(x)
+        ws, nb = self.workspace(N, M, remat)
+        gpipe_cell_backward(self.handle, x, dy, dx if want_dx else None, N, M, remat, ws, nb,
+                            stream)
+        return dx if want_dx else None
 
     def update(self, lr, decay, eps, stream=None):
         gpipe_apply_update(self.handle, lr, decay, eps, stream)

@@ -164,17 +164,32 @@ def test_ragged_shapes_bf16():
     check(cfg.with_(causal=True))
 
 
-def test_small_bf16_full():
-    """The small cell as specified: 6 layers, N=64, M=8."""
-    check(configs.SMALL)
-
-
-def test_small_bf16_one_micro_batch_matches_eight():
-    """M=1 (the full-batch step) and M=8 agree with the oracle and with each other."""
+@pytest.fixture(scope="module")
+def small_oracle():
+    """One oracle step of the small cell (6 layers, N=64): the full mini-batch's
+    step, which every micro-batch count reaches (M=8 here; the LayerNorm cell's
+    result does not depend on M)."""
     cfg = configs.SMALL
     params = inputs.cell_params(cfg)
     x, t = inputs.cell_data(cfg)
-    g1 = run_gpu(cfg, params, x, t, cfg.batch, 1, update=False)
+    return cfg, params, x, t, oracle_step(cfg, params, x, t, cfg.micro)
+
+
+def test_small_bf16_full(small_oracle):
+    """The small cell as specified: 6 layers, N=64, M=8."""
+    cfg, params, x, t, ref = small_oracle
+    gpu = run_gpu(cfg, params, x, t, cfg.batch, cfg.micro)
+    report, bad = compare_step(gpu, ref, BF16_TOL)
+    assert not bad, bad
+
+
+def test_small_bf16_one_micro_batch_matches_oracle(small_oracle):
+    """M=1 (the full-batch step, 8192 tokens per launch) against the oracle, and
+    against the M=8 run."""
+    cfg, params, x, t, ref = small_oracle
+    g1 = run_gpu(cfg, params, x, t, cfg.batch, 1)
+    report, bad = compare_step(g1, ref, BF16_TOL)
+    assert not bad, bad
     g8 = run_gpu(cfg, params, x, t, cfg.batch, 8, update=False)
     # the tile / split-K plan depends on the rows per micro-batch, so the two runs
     # sum in different orders: equal up to bf16 rounding, not bitwise
@@ -182,6 +197,92 @@ def test_small_bf16_one_micro_batch_matches_eight():
     for a, b in zip(g1["grad"], g8["grad"]):
         for n in gpipe.TENSORS:
             assert rel_l2(a[n], b[n]) < 1e-2, n
+
+
+def test_small_bf16_remat_bitwise_equals_stored():
+    """The small cell as specified (N=64, M=8: its down-projection splits over k
+    at 1024 rows, so the forward phase runs one micro-batch per launch on three
+    lanes): re-materialization reproduces the stored run bit for bit."""
+    cfg = configs.SMALL
+    params = inputs.cell_params(cfg)
+    x, t = inputs.cell_data(cfg)
+    a = run_gpu(cfg, params, x, t, cfg.batch, cfg.micro, remat=True, update=False)
+    b = run_gpu(cfg, params, x, t, cfg.batch, cfg.micro, remat=False, update=False)
+    assert np.array_equal(a["y"], b["y"])
+    assert np.array_equal(a["dx"], b["dx"])
+    for ga, gb in zip(a["grad"], b["grad"]):
+        for n in gpipe.TENSORS:
+            assert np.array_equal(ga[n], gb[n]), n
+
+
+@pytest.mark.parametrize("layers,d_ff,batch,micro", [(6, 2048, 16, 8), (4, 4096, 10, 5)])
+def test_grouped_forward_with_split_products_bitwise_bf16(layers, d_ff, batch, micro):
+    """Grouped forward launches whose down-projection splits over k: the small
+    cell's layers at 256-token micro-batches (three per launch, 4 splits; the
+    last group of two) and d_ff 4096 (two per launch, 8 splits, a last group of
+    one).  Each lane's split-K partials hold the grouped launch, and the
+    boundary outputs and every gradient equal the stored-activation run bit
+    for bit; the step matches the oracle."""
+    cfg = configs.SMALL.with_(name=f"grouped_split_l{layers}_f{d_ff}_m{micro}", layers=layers,
+                              d_ff=d_ff, batch=batch, micro=micro)
+    cell = gpipe.gpipe_cell_create(cfg.layers, cfg.d_model, cfg.heads, cfg.d_ff, cfg.seq,
+                                   cfg.causal, gpipe.GPIPE_BF16)
+    try:
+        lanes, G, _ = gpipe.gpipe_cell_forward_plan(cell, batch, micro, True)
+    finally:
+        gpipe.gpipe_cell_destroy(cell)
+    say(f"[plan] forward lanes={lanes} group={G}")
+    assert G >= 2 and micro % G != 0
+    params = inputs.cell_params(cfg)
+    x, t = inputs.cell_data(cfg)
+    a = run_gpu(cfg, params, x, t, cfg.batch, cfg.micro, remat=True, update=False)
+    b = run_gpu(cfg, params, x, t, cfg.batch, cfg.micro, remat=False, update=False)
+    assert np.array_equal(a["y"], b["y"])
+    assert np.array_equal(a["dx"], b["dx"])
+    for ga, gb in zip(a["grad"], b["grad"]):
+        for n in gpipe.TENSORS:
+            assert np.array_equal(ga[n], gb[n]), n
+    check(cfg)
+
+
+def two_steps(cfg, N=None, M=None):
+    """Two consecutive GPU steps + updates (the second reads the RMSProp state and
+    the bf16 copy the first update wrote, and overwrites the gradients) against two
+    oracle train steps with the state carried."""
+    import torch
+    N = cfg.batch if N is None else N
+    M = cfg.micro if M is None else M
+    params = inputs.cell_params(cfg)
+    x, t = inputs.cell_data(cfg, batch=N)
+    tol = FP32_TOL if cfg.precision == "fp32" else BF16_TOL
+    cell = make_cell(cfg, params)
+    ref1 = oracle_step(cfg, params, x, t, M)
+    g1 = run_gpu(cfg, params, x, t, N, M, cell=cell)
+    report, bad = compare_step(g1, ref1, tol)
+    assert not bad, ("step 1", bad)
+    if cell.bf16:
+        want = inputs.round_to_bf16(cell.master.cpu().numpy())
+        assert np.array_equal(g1["w_lowp"], want), "w_lowp != bf16(master) after update 1"
+    # step 2 from the oracle's own updated weights and mean-square state
+    ref2 = tc.train_step(ref1["w_new"], x, t, M, cfg.heads, cfg.causal, cfg.lr, cfg.decay, cfg.eps,
+                         ms=ref1["ms_new"], ln_eps=cfg.ln_eps)
+    g2 = run_gpu(cfg, params, x, t, N, M, cell=cell)
+    report, bad = compare_step(g2, ref2, tol)
+    assert not bad, ("step 2", bad)
+    if cell.bf16:
+        want = inputs.round_to_bf16(cell.master.cpu().numpy())
+        assert np.array_equal(g2["w_lowp"], want), "w_lowp != bf16(master) after update 2"
+    torch.cuda.synchronize()
+
+
+def test_two_steps_fp32():
+    two_steps(configs.TINY)
+
+
+def test_two_steps_bf16_reduced():
+    """The small cell's layer shapes at 2 layers, N=8, M=4 (fused attention,
+    grouped forward, pipelined re-materialization)."""
+    two_steps(configs.SMALL.with_(name="small_2l_two_steps", layers=2, batch=8, micro=4))
 
 
 def test_cell_2048_layer_shapes_bf16():

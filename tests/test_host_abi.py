@@ -180,6 +180,19 @@ def test_workspace_and_step_validation_without_device():
         assert e.value.code == 1
         with pytest.raises(gpipe.GpipeError):                    # bad decay
             gpipe.gpipe_apply_update(h, 1e-3, 1.0, 1e-8, 0)
+        # the split phases: forward needs y, backward needs dy; checked before any launch
+        with pytest.raises(gpipe.GpipeError) as e:
+            gpipe.gpipe_cell_forward(h, 16, None, 8, 4, True, 16, ws, 0)
+        assert e.value.code == 1
+        with pytest.raises(gpipe.GpipeError) as e:
+            gpipe.gpipe_cell_backward(h, 16, None, 16, 8, 4, True, 16, ws, 0)
+        assert e.value.code == 1
+        with pytest.raises(gpipe.GpipeError) as e:               # misaligned dy
+            gpipe.gpipe_cell_backward(h, 16, 24, 16, 8, 4, True, 16, ws, 0)
+        assert e.value.code == 1
+        with pytest.raises(gpipe.GpipeError) as e:               # workspace too small
+            gpipe.gpipe_cell_backward(h, 16, 32, 16, 8, 4, True, 16, ws - 1, 0)
+        assert e.value.code == 1
     finally:
         gpipe.gpipe_cell_destroy(h)
 
@@ -421,3 +434,75 @@ def test_gemm_plan_of_the_ragged_specialised_case():
     for w in ("ffn1_wgrad", "ffn2_wgrad", "qkv_wgrad"):
         assert p[w] == (256, 128, 1), (w, p[w])
     assert p["ffn1_fwd"] == (128, 128, 1)
+
+
+FWD_ROLES = ("qkv_fwd", "out_fwd", "ffn1_fwd", "ffn2_fwd")
+
+
+def _fwd_out_cols(cfg, role):
+    d, f = cfg.d_model, cfg.d_ff
+    return {"qkv_fwd": 3 * d, "out_fwd": d, "ffn1_fwd": f, "ffn2_fwd": d}[role]
+
+
+GROUP_CASES = [
+    # the small cell's layers at N=16, M=8: 256-token micro-batches, grouped by
+    # three, where the down-projection splits four ways at both sizes
+    configs.SMALL.with_(batch=16, micro=8),
+    configs.SMALL,                                       # N=64, M=8
+    configs.SMALL.with_(batch=24, micro=8),
+    configs.SMALL.with_(layers=2, batch=12, micro=6, d_ff=4096, causal=True),
+    configs.CELL_2048,
+    configs.CELL_2048.with_(batch=12, micro=6),
+    configs.SMALL.with_(layers=8, d_model=256, heads=2, d_ff=512, seq=100, batch=14, micro=7),
+    configs.SMALL.with_(layers=4, d_model=512, heads=4, d_ff=4096, seq=128, batch=10, micro=5),
+]
+
+
+@pytest.mark.parametrize("cfg", GROUP_CASES, ids=lambda c: f"{c.layers}l_d{c.d_model}_f{c.d_ff}_n{c.batch}_m{c.micro}")
+def test_grouped_forward_fits_its_partials_and_keeps_the_k_order(cfg):
+    """The forward phase runs G micro-batches per launch only where each forward
+    product splits over k the same way at G*T (and at the last group's rows) as
+    at T, and each lane's split-K region holds the largest split launch it makes."""
+    h = gpipe.gpipe_cell_create(cfg.layers, cfg.d_model, cfg.heads, cfg.d_ff, cfg.seq,
+                                cfg.causal, gpipe.GPIPE_BF16)
+    try:
+        R = {n: i for i, n in enumerate(gpipe.ROLES)}
+        N, M = cfg.batch, cfg.micro
+        b = N // M
+        lanes, G, lane_bytes = gpipe.gpipe_cell_forward_plan(h, N, M, True)
+        assert 1 <= G <= M and lanes in (1, 2, 3)
+        one = {r: gpipe.gpipe_cell_gemm_plan(h, N, M, R[r]) for r in FWD_ROLES}
+        sizes = [g for g in {G, M % G} if g >= 1]
+        for g in sizes:
+            grp = {r: gpipe.gpipe_cell_gemm_plan(h, g * b, 1, R[r]) for r in FWD_ROLES}
+            for r in FWD_ROLES:
+                # same number of k-splits (the same K fixes their depth)
+                assert grp[r][2] == one[r][2], (g, r, grp[r], one[r])
+                rows = g * b * cfg.seq
+                if grp[r][2] > 1:
+                    need = grp[r][2] * rows * _fwd_out_cols(cfg, r) * 4
+                    assert need <= lane_bytes, (g, r, need, lane_bytes)
+        for r in FWD_ROLES:
+            if one[r][2] > 1:
+                assert one[r][2] * b * cfg.seq * _fwd_out_cols(cfg, r) * 4 <= lane_bytes
+        # lanes x (G micro-batches' layer slot) fit in one micro-batch's saved set
+        if G > 1:
+            ws1 = gpipe.gpipe_cell_workspace_bytes(h, N, M, True)
+            assert ws1 > 0
+        # without re-materialization the forward phase runs one micro-batch at a time
+        assert gpipe.gpipe_cell_forward_plan(h, N, M, False)[:2] == (1, 1)
+    finally:
+        gpipe.gpipe_cell_destroy(h)
+
+
+def test_grouped_forward_choices_of_the_workloads():
+    """The 2048-wide cell groups four 1024-token micro-batches on two lanes; the
+    small cell's micro-batches (whose down-projection splits at 1024 rows but
+    not at 2048 or more) run one per launch on three lanes."""
+    for cfg, want in ((configs.CELL_2048, (2, 4)), (configs.SMALL, (3, 1))):
+        h = gpipe.gpipe_cell_create(cfg.layers, cfg.d_model, cfg.heads, cfg.d_ff, cfg.seq,
+                                    cfg.causal, gpipe.GPIPE_BF16)
+        try:
+            assert gpipe.gpipe_cell_forward_plan(h, cfg.batch, cfg.micro, True)[:2] == want
+        finally:
+            gpipe.gpipe_cell_destroy(h)
