@@ -260,6 +260,31 @@ gpipe_status gpipe_cell_forward(gpipe_cell *cell, const void *x, void *y, int N,
 gpipe_status gpipe_cell_backward(gpipe_cell *cell, const void *x, const void *dy, void *dx, int N,
                                  int M, int remat, void *workspace, size_t ws_bytes, void *stream);
 
+/* Size of the library's own device scratch used by gpipe_cell_step_noalloc:
+ * one array per device, held from the first such call on that device until
+ * the process ends. */
+#define GPIPE_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* gpipe_cell_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The workspace is the library's static scratch of GPIPE_SCRATCH_BYTES on the
+ * device current at the call (its address is looked up once per device), and
+ * every launch goes to `stream` alone: no stream, event or memory is created,
+ * and nothing is allocated or freed (role timing is not applied).  The caller
+ * still provides x, target, y, dx (NULL to skip) and loss_dev; arguments,
+ * results and the bound state are those of gpipe_cell_step, bitwise.  The
+ * scratch's contents on entry are ignored (nothing in it has to start at
+ * zero).  All calls on one device share its scratch and leave the last call's
+ * contents there, so calls whose work overlaps on one GPU (other streams,
+ * other threads, other cells) race: a caller must order them, for example on
+ * one stream.  Transformer cells only.
+ * Errors: GPIPE_ERR_OOM (no work enqueued) when gpipe_cell_workspace_bytes(N,
+ * M, remat) exceeds GPIPE_SCRATCH_BYTES; GPIPE_ERR_UNSUPPORTED for a conv
+ * cell; otherwise as gpipe_cell_step. */
+gpipe_status gpipe_cell_step_noalloc(gpipe_cell *cell, const void *x, const void *target, void *y,
+                                     void *dx, int N, int M, int remat, void *stream,
+                                     float *loss_dev);
+
 /* Phase 3, the single synchronous update: RMSProp over all P parameters,
  *   ms <- decay*ms + (1-decay)*grad^2;  master <- master - lr*grad/(sqrt(ms)+eps)
  * and, for bf16 cells, w_lowp <- bf16(master) (round to nearest even).

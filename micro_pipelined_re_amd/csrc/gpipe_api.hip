@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <limits>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -609,6 +610,31 @@ gpipe_status reduce_gparts(const Ctx& x) {
   return GPIPE_OK;
 }
 
+// The allocation-free step's workspace: one array per device, resident while
+// the process lives.  In host code `scratch` names a host-side stand-in, not
+// device memory, so the host only ever uses the device address that
+// hipGetSymbolAddress returns for it, looked up once per device with that
+// device current (each device holds its own copy at its own address).
+__device__ __align__(256) static unsigned char scratch[GPIPE_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+gpipe_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  GP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return GPIPE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return GPIPE_ERR_DEVICE;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GPIPE_OK;
+}
+
 // What one call of the Transformer cell's driver does: the forward phase
 // (PH_FWD), the backward phase (PH_BWD) or both (the step).  The backward's
 // output gradient comes from the loss against `target`, or is `dy`, handed
@@ -955,6 +981,30 @@ gpipe_status gpipe_cell_backward(gpipe_cell* c, const void* x, const void* dy, v
   io.N = N; io.M = M; io.remat = remat;
   io.ws = static_cast<char*>(workspace); io.ws_bytes = ws_bytes;
   io.s = static_cast<hipStream_t>(stream);
+  return transformer_run(c, io);
+}
+
+gpipe_status gpipe_cell_step_noalloc(gpipe_cell* c, const void* x, const void* target, void* y,
+                                     void* dx, int N, int M, int remat, void* stream,
+                                     float* loss_dev) {
+  if (!c) return GPIPE_ERR_INVALID;
+  if (!c->bound) return GPIPE_ERR_STATE;
+  if (c->kind == CELL_CONV) return GPIPE_ERR_UNSUPPORTED;
+  Plan p;
+  if (!make_plan(c, N, M, remat, &p)) return GPIPE_ERR_INVALID;
+  if (p.total > GPIPE_SCRATCH_BYTES) return GPIPE_ERR_OOM;
+  void* ws = nullptr;
+  {
+    const gpipe_status st = scratch_of_current_device(&ws);
+    if (st != GPIPE_OK) return st;
+  }
+  StepIO io;
+  io.phases = PH_FWD | PH_BWD;
+  io.x = x; io.target = target; io.y = y; io.dx = dx; io.loss_dev = loss_dev;
+  io.N = N; io.M = M; io.remat = remat;
+  io.ws = static_cast<char*>(ws); io.ws_bytes = GPIPE_SCRATCH_BYTES;
+  io.s = static_cast<hipStream_t>(stream);
+  io.single = true;
   return transformer_run(c, io);
 }
 

@@ -27,7 +27,7 @@ EXPORTS = ("gpipe_cell_create", "gpipe_cell_destroy", "gpipe_cell_param_count",
            "gpipe_apply_update", "gpipe_partition", "gpipe_status_string",
            "gpipe_cell_profile", "gpipe_cell_profile_read", "gpipe_cell_gemm_plan",
            "gpipe_conv_cell_create", "gpipe_cell_bind_running", "gpipe_cell_forward_plan",
-           "gpipe_cell_forward", "gpipe_cell_backward")
+           "gpipe_cell_forward", "gpipe_cell_backward", "gpipe_cell_step_noalloc")
 
 ROLES = ("ln1_fwd", "qkv_fwd", "scores_fwd", "softmax_fwd", "pv_fwd", "out_fwd", "ln2_fwd",
          "ffn1_fwd", "ffn2_fwd", "mse", "ffn2_dgrad", "ffn2_wgrad", "ffn1_dgrad", "ffn1_wgrad",
@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
                                         ctypes.POINTER(_sz)],
             "gpipe_cell_step": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp, _vp],
             "gpipe_cell_forward": [_vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp],
+            "gpipe_cell_step_noalloc": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp],
             "gpipe_cell_backward": [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp],
             "gpipe_apply_update": [_vp, ctypes.c_float, ctypes.c_float, ctypes.c_float, _vp],
             "gpipe_partition": [ctypes.POINTER(ctypes.c_double), _i, _i, ctypes.POINTER(_i),
@@ -190,6 +191,15 @@ def gpipe_cell_step(cell, x, target, y, dx, N, M, remat, workspace, ws_bytes, st
            lib().gpipe_cell_step(cell, _ptr(x), _ptr(target), _ptr(y), _ptr(dx), N, M,
                                  int(bool(remat)), _ptr(workspace), ws_bytes, _stream(stream),
                                  _ptr(loss)))
+
+
+GPIPE_SCRATCH_BYTES = 64 << 20
+
+
+def gpipe_cell_step_noalloc(cell, x, target, y, dx, N, M, remat, stream, loss) -> None:
+    _check("gpipe_cell_step_noalloc",
+           lib().gpipe_cell_step_noalloc(cell, _ptr(x), _ptr(target), _ptr(y), _ptr(dx), N, M,
+                                         int(bool(remat)), _stream(stream), _ptr(loss)))
 
 
 def gpipe_cell_forward(cell, x, y, N, M, remat, workspace, ws_bytes, stream) -> None:
