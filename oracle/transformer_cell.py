@@ -76,8 +76,17 @@ def gelu_derivative(u):
     return 0.5 * (1.0 + erf(u / math.sqrt(2.0))) + u * phi
 
 
-def softmax_rows(s, causal):
-    """Row softmax over the last axis with max subtraction; causal masks j > i."""
+def clip_logits(s, clip):
+    """Logit clipping ("training stability challenges of deep models": the
+    activations in front of a softmax are clipped when they exceed a
+    threshold): s limited to [-clip, clip]; clip None leaves s as it is."""
+    return s if clip is None else np.clip(s, -clip, clip)
+
+
+def softmax_rows(s, causal, clip=None):
+    """Row softmax over the last axis with max subtraction; causal masks j > i.
+    With clip, the scores are clipped first (clip_logits)."""
+    s = clip_logits(s, clip)
     if causal:
         n = s.shape[-1]
         keep = np.tril(np.ones((s.shape[-2], n), dtype=bool))
@@ -112,8 +121,9 @@ def _merge_heads(a):
     return a.transpose(0, 2, 1, 3).reshape(b, s, h * dh)
 
 
-def layer_forward(p, x, heads, causal, ln_eps=LN_EPS):
-    """One pre-LN layer on x [B, S, D]; returns (x_out, saved intermediates)."""
+def layer_forward(p, x, heads, causal, ln_eps=LN_EPS, clip=None):
+    """One pre-LN layer on x [B, S, D]; returns (x_out, saved intermediates).
+    clip: the attention logit-clipping threshold (None: off)."""
     d = x.shape[-1]
     dh = d // heads
     h1, mu1, rstd1 = layer_norm(x, p["ln1_g"], p["ln1_b"], ln_eps)
@@ -122,7 +132,7 @@ def layer_forward(p, x, heads, causal, ln_eps=LN_EPS):
     k = _split_heads(qkv[..., d:2 * d], heads)
     v = _split_heads(qkv[..., 2 * d:3 * d], heads)
     scores = (q @ k.transpose(0, 1, 3, 2)) / math.sqrt(dh)
-    prob = softmax_rows(scores, causal)
+    prob = softmax_rows(scores, causal, clip)
     ctx = _merge_heads(prob @ v)
     x1 = x + linear(ctx, p["w_o"], p["b_o"])
     h2, mu2, rstd2 = layer_norm(x1, p["ln2_g"], p["ln2_b"], ln_eps)
@@ -131,6 +141,10 @@ def layer_forward(p, x, heads, causal, ln_eps=LN_EPS):
     x_out = x1 + linear(g, p["w_2"], p["b_2"])
     saved = dict(x=x, h1=h1, mu1=mu1, rstd1=rstd1, qkv=qkv, prob=prob, ctx=ctx,
                  x1=x1, h2=h2, mu2=mu2, rstd2=rstd2, u=u, g=g)
+    if clip is not None:
+        # where the clip is active its output does not move with the score:
+        # d clip(s) / ds is 1 for |s| <= clip and 0 beyond
+        saved["keep"] = np.abs(scores) <= clip
     return x_out, saved
 
 
@@ -170,6 +184,8 @@ def layer_backward(p, saved, d_out, heads, causal):
     dprob = dctx @ v.transpose(0, 1, 3, 2)
     dv = prob.transpose(0, 1, 3, 2) @ dctx
     dscores = softmax_backward(prob, dprob) / math.sqrt(dh)
+    if "keep" in saved:
+        dscores = dscores * saved["keep"]
     dq = dscores @ k
     dk = dscores.transpose(0, 1, 3, 2) @ q
     dqkv = np.concatenate([_merge_heads(dq), _merge_heads(dk), _merge_heads(dv)], axis=-1)
@@ -185,12 +201,12 @@ def layer_backward(p, saved, d_out, heads, causal):
 # the cell, the loss and the step
 # --------------------------------------------------------------------------
 
-def cell_forward(params, x, heads, causal, ln_eps=LN_EPS, keep=False):
+def cell_forward(params, x, heads, causal, ln_eps=LN_EPS, keep=False, clip=None):
     """Run every layer of the cell; returns (y, saved list or None)."""
     saved = [] if keep else None
     h = x
     for p in params:
-        h, s = layer_forward(p, h, heads, causal, ln_eps)
+        h, s = layer_forward(p, h, heads, causal, ln_eps, clip)
         if keep:
             saved.append(s)
     return h, saved
@@ -215,7 +231,7 @@ def cast_params(params, dtype):
 
 
 def cell_step(params, x, t, micro, heads, causal, ln_eps=LN_EPS, remat=True,
-              dtype=np.float64, record=False, denom=None):
+              dtype=np.float64, record=False, denom=None, clip=None):
     """One GPipe training step of the cell without the update (phases 1 and 2).
 
     x, t: [N, S, D].  micro: M, must divide N.  remat=True drops the layer
@@ -224,6 +240,7 @@ def cell_step(params, x, t, micro, heads, causal, ln_eps=LN_EPS, remat=True,
     Micro-batches are processed in order m = 0 .. M-1 in both phases.
     denom is the loss normaliser, N*S*D of x unless given (a caller taking
     some sequences of a larger mini-batch passes that mini-batch's N*S*D).
+    clip is the attention logit-clipping threshold (None: off).
     Returns dict(y, loss, dx, grads) plus, if record, the forward phase's and
     the backward phase's intermediates for each micro-batch.
     """
@@ -241,7 +258,7 @@ def cell_step(params, x, t, micro, heads, causal, ln_eps=LN_EPS, remat=True,
     for m in range(micro):
         sl = slice(m * b, (m + 1) * b)
         y[sl], s = cell_forward(params, x[sl], heads, causal, ln_eps,
-                                keep=(not remat) or record)
+                                keep=(not remat) or record, clip=clip)
         kept.append(s)
     # phase 2: backward, re-materializing each micro-batch's intermediates
     loss = 0.0
@@ -251,7 +268,7 @@ def cell_step(params, x, t, micro, heads, causal, ln_eps=LN_EPS, remat=True,
     for m in range(micro):
         sl = slice(m * b, (m + 1) * b)
         if remat:
-            y_m, saved = cell_forward(params, x[sl], heads, causal, ln_eps, keep=True)
+            y_m, saved = cell_forward(params, x[sl], heads, causal, ln_eps, keep=True, clip=clip)
             if record:
                 rebuilt.append((y_m, saved))
         else:
@@ -280,9 +297,9 @@ def rmsprop(w, g, ms, lr, decay, eps):
 
 
 def train_step(params, x, t, micro, heads, causal, lr, decay, eps, ms=None,
-               ln_eps=LN_EPS, remat=True, dtype=np.float64):
+               ln_eps=LN_EPS, remat=True, dtype=np.float64, clip=None):
     """Phases 1-3: the step plus one synchronous RMSProp update of every tensor."""
-    out = cell_step(params, x, t, micro, heads, causal, ln_eps, remat, dtype)
+    out = cell_step(params, x, t, micro, heads, causal, ln_eps, remat, dtype, clip=clip)
     p64 = cast_params(params, dtype)
     if ms is None:
         ms = [{k: np.zeros_like(v) for k, v in p.items()} for p in p64]
@@ -295,4 +312,20 @@ def train_step(params, x, t, micro, heads, causal, lr, decay, eps, ms=None,
         new_ms.append(m_l)
     out["w_new"] = new_w
     out["ms_new"] = new_ms
+    return out
+
+
+def depth_scaled_ffn_init(params, total_layers, dtype=np.float64):
+    """Scaled initialisation ("training stability challenges of deep models":
+    the feed-forward layers' initialisation is scaled down by the number of
+    layers L): every layer's FFN matrices w_1 and w_2 divided by L, the
+    stack's total depth (not the cell's L/K); everything else unchanged."""
+    if total_layers < 1:
+        raise ValueError("total_layers must be positive")
+    out = []
+    for p in params:
+        q = {k: np.asarray(v, dtype=dtype) for k, v in p.items()}
+        for k in ("w_1", "w_2"):
+            q[k] = q[k] / dtype(total_layers)
+        out.append(q)
     return out
