@@ -175,10 +175,19 @@ gpipe_status gpipe_cell_sync_lowp(gpipe_cell *cell, void *stream);
 
 /* Exact device workspace needed by gpipe_cell_step(N, M, remat): one
  * micro-batch's saved activations of all layers when remat != 0 (the pages'
- * O(N + L/K * N/M) activation bound: the boundary tensors are the caller's
- * x / y), all M micro-batches' when remat == 0, plus one layer's backward
- * transients and the reduction partials.  GPIPE_ERR_INVALID unless
- * N > 0, M > 0 and N % M == 0. */
+ * O(N + L/K * N/M) activation bound, "preliminaries 5": the boundary tensors
+ * are the caller's x / y), all M micro-batches' when remat == 0, plus one
+ * layer's backward transients and the reduction partials.
+ * It also tells whether that fits: GPIPE_ERR_OOM when the plan -- plus the
+ * parameter state (12 B/param for fp32 cells, 14 for bf16) while the cell is
+ * not bound yet -- exceeds the free memory of the current device
+ * (hipMemGetInfo); *bytes still receives the plan then, so the caller can
+ * report the bytes it would need.  Query before allocating the workspace: a
+ * query made while that workspace is allocated counts it as used.  Without a
+ * visible device only the plan is reported.  Nothing is enqueued either way.
+ * GPIPE_ERR_INVALID unless N > 0, M > 0 and N % M == 0.
+ * (gpipe_cell_step allocates nothing, so it has no OOM of its own: it takes
+ * the workspace the caller allocated after this query.) */
 gpipe_status gpipe_cell_workspace_bytes(const gpipe_cell *cell, int N, int M, int remat,
                                         size_t *bytes);
 
@@ -292,6 +301,30 @@ gpipe_status gpipe_cell_step_noalloc(gpipe_cell *cell, const void *x, const void
  * GPIPE_ERR_INVALID if decay is outside [0, 1) or lr/eps are negative or
  * not finite. */
 gpipe_status gpipe_apply_update(gpipe_cell *cell, float lr, float decay, float eps, void *stream);
+
+/* Stability options for deep stacks ("training stability challenges of deep
+ * models": sharp predictions and exploding gradients, fixed by scaling the
+ * feed-forward initialisation down with the depth and by clipping the
+ * activations in front of a softmax that exceed a threshold).
+ *
+ * gpipe_cell_set_logit_clip: with threshold > 0 every attention score
+ * s = q.k / sqrt(d_model/heads) is clipped to [-threshold, threshold] before
+ * the softmax, in the forward, re-materialized and backward passes alike; a
+ * clipped score (|s| > threshold) passes no gradient back to q and k.  The
+ * attention softmax is the cell's only softmax.  0 switches clipping off (the
+ * default).  Takes effect at the next step; host side only.
+ * Errors: GPIPE_ERR_INVALID for a negative or non-finite threshold or a conv
+ * cell.
+ *
+ * gpipe_cell_scale_ffn_init: divides the FFN matrices w_1 and w_2 of every
+ * layer of the bound master weights by total_layers -- the depth L of the
+ * whole stack the cell belongs to, not the cell's L/K -- with correctly
+ * rounded float32 division, and rewrites their bf16 copy in bf16 cells.  Meant
+ * right after the caller has written the initial weights; enqueued on
+ * `stream`.  Errors: GPIPE_ERR_STATE if not bound; GPIPE_ERR_INVALID for
+ * total_layers < 1 or a conv cell. */
+gpipe_status gpipe_cell_set_logit_clip(gpipe_cell *cell, float threshold);
+gpipe_status gpipe_cell_scale_ffn_init(gpipe_cell *cell, int total_layers, void *stream);
 
 /* The cell partition of "minimal interface design": split L layers with
  * estimated costs costs[0..L-1] (finite, >= 0) into K contiguous non-empty

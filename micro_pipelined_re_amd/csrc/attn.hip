@@ -11,6 +11,9 @@
 // order (no atomics) and the result is reproducible.
 //
 // Scores live in base 2: x = (q . k) * scale * log2(e), p = 2^(x - lse2).
+// With logit clipping (CLIP) the raw product q . k is first limited to
+// [-craw, craw], craw = threshold / scale, and in the backward a clipped
+// score passes no gradient (d clip(s)/ds = 0 for |s| > threshold).
 //
 // MFMA v_mfma_f32_16x16x32_bf16: A lane l holds row l%16, k 8*(l/16)+e;
 // B lane l holds k 8*(l/16)+e of column l%16; C lane l holds rows
@@ -148,11 +151,11 @@ extern __shared__ __attribute__((aligned(16))) bf16_t attn_smem[];
 
 // ------------------------------------------------------------------ forward
 // grid (B*H, query blocks); qkv [B*S][3D], ctx [B*S][D], lse2 [B*H][S].
-template <int DH>
+template <int DH, bool CLIP>
 __global__ __launch_bounds__(512) void flash_fwd_kernel(const bf16_t* __restrict__ qkv,
                                                         bf16_t* __restrict__ ctx,
                                                         float* __restrict__ lse2, int S, int H,
-                                                        int D, int causal, float sl2) {
+                                                        int D, int causal, float sl2, float craw) {
   constexpr int KS = DH / 32;   // k steps over the head dimension
   constexpr int DT = DH / 16;   // 16-column output tiles
   constexpr int TE = attn_tile_elems<DH>();
@@ -216,6 +219,11 @@ __global__ __launch_bounds__(512) void flash_fwd_kernel(const bf16_t* __restrict
       for (int t = 0; t < 4; ++t) st[t] = mfma(kfr[t][ks], qf[ks], st[t]);
     __builtin_amdgcn_sched_group_barrier(0x100, 4 * KS + 2 * DT, 0);  // the LDS reads
     __builtin_amdgcn_sched_group_barrier(0x008, 4 * KS, 0);           // then the MFMAs
+    if constexpr (CLIP)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) st[t][v] = fminf(fmaxf(st[t][v], -craw), craw);
     const int k0 = kb * kBlk;
     const bool full = (k0 + kBlk <= S) && (!causal || k0 + kBlk - 1 <= qb * kBlk);
     if (!full)
@@ -322,11 +330,11 @@ __global__ __launch_bounds__(512) void flash_fwd_kernel(const bf16_t* __restrict
 // dK, dV for key block kbk of (sequence, head) bh; the groups split the
 // query blocks, and each computes the row sums delta = rowsum(dO * O) of the
 // query blocks it visits from the dO and O tiles it loads.
-template <int DH>
+template <int DH, bool CLIP>
 __device__ __forceinline__ void flash_dkdv_body(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ ctx,
     const bf16_t* __restrict__ dctx, const float* __restrict__ lse2, bf16_t* __restrict__ dqkv,
-    int S, int H, int D, int causal, float sl2, float scale, int bh, int kbk) {
+    int S, int H, int D, int causal, float sl2, float scale, float craw, int bh, int kbk) {
   constexpr int KS = DH / 32;
   constexpr int DT = DH / 16;
   constexpr int TE = attn_tile_elems<DH>();
@@ -420,10 +428,12 @@ __device__ __forceinline__ void flash_dkdv_body(
       for (int v = 0; v < 4; ++v) {
         const int r = t * 16 + 4 * g + v;
         const int qq = q0 + r;
-        float p = exp2_raw(fmaf(sp[t][v], sl2, -ls_s[r]));
+        const float s0 = sp[t][v];
+        float p = exp2_raw(fmaf(CLIP ? fminf(fmaxf(s0, -craw), craw) : s0, sl2, -ls_s[r]));
         if (key >= S || (causal && key > qq)) p = 0.f;
         sp[t][v] = p;                                   // P
         dp[t][v] = p * (dp[t][v] - dl_s[r]);            // dS (unscaled)
+        if (CLIP && !(fabsf(s0) <= craw)) dp[t][v] = 0.f;
       }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
@@ -470,11 +480,11 @@ __device__ __forceinline__ void flash_dkdv_body(
 
 // dQ for query block qb of (sequence, head) bh; the groups split the key
 // blocks.  Each computes the block's row sums delta = rowsum(dO * O) itself.
-template <int DH>
+template <int DH, bool CLIP>
 __device__ __forceinline__ void flash_dq_body(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ ctx,
     const bf16_t* __restrict__ dctx, const float* __restrict__ lse2, bf16_t* __restrict__ dqkv,
-    int S, int H, int D, int causal, float sl2, float scale, int bh, int qb) {
+    int S, int H, int D, int causal, float sl2, float scale, float craw, int bh, int qb) {
   constexpr int KS = DH / 32;
   constexpr int DT = DH / 16;
   constexpr int TE = attn_tile_elems<DH>();
@@ -550,9 +560,11 @@ __device__ __forceinline__ void flash_dq_body(
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int key = k0 + t * 16 + 4 * g + v;
-        float p = exp2_raw(fmaf(st[t][v], sl2, -lq));
+        const float s0 = st[t][v];
+        float p = exp2_raw(fmaf(CLIP ? fminf(fmaxf(s0, -craw), craw) : s0, sl2, -lq));
         if (key >= S || (causal && key > q)) p = 0.f;
         st[t][v] = p * (dpt[t][v] - dq_);   // dS^T (unscaled)
+        if (CLIP && !(fabsf(s0) <= craw)) st[t][v] = 0.f;
       }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
@@ -590,17 +602,19 @@ __device__ __forceinline__ void flash_dq_body(
 // dV of key block y-blocks (key block 0, the longest, first).  The dQ and the
 // dK/dV blocks are independent, so a CU that finishes a short one takes the
 // next.
-template <int DH>
+template <int DH, bool CLIP>
 __global__ __launch_bounds__(512) void flash_bwd_kernel(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ ctx,
     const bf16_t* __restrict__ dctx, const float* __restrict__ lse2, bf16_t* __restrict__ dqkv,
-    int S, int H, int D, int causal, float sl2, float scale) {
+    int S, int H, int D, int causal, float sl2, float scale, float craw) {
   const int nb = (S + kBlk - 1) / kBlk;
   const int y = int(blockIdx.y), bh = int(blockIdx.x);
   if (y < nb)
-    flash_dq_body<DH>(qkv, ctx, dctx, lse2, dqkv, S, H, D, causal, sl2, scale, bh, nb - 1 - y);
+    flash_dq_body<DH, CLIP>(qkv, ctx, dctx, lse2, dqkv, S, H, D, causal, sl2, scale, craw, bh,
+                            nb - 1 - y);
   else
-    flash_dkdv_body<DH>(qkv, ctx, dctx, lse2, dqkv, S, H, D, causal, sl2, scale, bh, y - nb);
+    flash_dkdv_body<DH, CLIP>(qkv, ctx, dctx, lse2, dqkv, S, H, D, causal, sl2, scale, craw, bh,
+                              y - nb);
 }
 
 // Sets the dynamic-LDS limit of a kernel once.
@@ -614,21 +628,28 @@ template <int DH>
 hipError_t attn_attrs() {
   static const hipError_t e = [] {
     constexpr int sm = attn_smem_bytes<DH>();
-    hipError_t r = allow_smem(flash_fwd_kernel<DH>, sm);
-    if (r == hipSuccess) r = allow_smem(flash_bwd_kernel<DH>, sm);
+    hipError_t r = allow_smem(flash_fwd_kernel<DH, false>, sm);
+    if (r == hipSuccess) r = allow_smem(flash_bwd_kernel<DH, false>, sm);
+    if (r == hipSuccess) r = allow_smem(flash_fwd_kernel<DH, true>, sm);
+    if (r == hipSuccess) r = allow_smem(flash_bwd_kernel<DH, true>, sm);
     return r;
   }();
   return e;
 }
+
+// The clip threshold in units of the raw product q . k (INFINITY: no clipping).
+float raw_clip(float clip, float scale) { return clip > 0.f ? clip / scale : INFINITY; }
 
 }  // namespace
 
 bool flash_ok(bool bf16, int dh) { return bf16 && (dh == 64 || dh == 128); }
 
 hipError_t flash_fwd(const void* qkv, void* ctx, float* lse2, int B, int H, int S, int D,
-                     int causal, hipStream_t s) {
+                     int causal, float clip, hipStream_t s) {
   const int dh = D / H;
+  const float scale = 1.0f / sqrtf(float(dh));
   const float sl2 = kLog2e / sqrtf(float(dh));
+  const float craw = raw_clip(clip, scale);
   // (sequence, head) along x: workgroups go to the XCDs round-robin by linear
   // id, so with B*H a multiple of 8 every block of one (sequence, head) --
   // which all read the same keys and values -- shares one XCD's L2
@@ -636,23 +657,27 @@ hipError_t flash_fwd(const void* qkv, void* ctx, float* lse2, int B, int H, int 
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
   const bf16_t* q = static_cast<const bf16_t*>(qkv);
   bf16_t* c = static_cast<bf16_t*>(ctx);
-  if (dh == 128) {
-    if (hipError_t e = attn_attrs<128>(); e != hipSuccess) return e;
-    hipLaunchKernelGGL(flash_fwd_kernel<128>, grid, dim3(512), attn_smem_bytes<128>(), s, q, c, lse2, S, H, D, causal, sl2);
-  } else if (dh == 64) {
-    if (hipError_t e = attn_attrs<64>(); e != hipSuccess) return e;
-    hipLaunchKernelGGL(flash_fwd_kernel<64>, grid, dim3(512), attn_smem_bytes<64>(), s, q, c, lse2, S, H, D, causal, sl2);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  if (dh != 128 && dh != 64) return hipErrorInvalidValue;
+  if (hipError_t e = dh == 128 ? attn_attrs<128>() : attn_attrs<64>(); e != hipSuccess) return e;
+  const int sm = dh == 128 ? attn_smem_bytes<128>() : attn_smem_bytes<64>();
+  const bool cl = craw < INFINITY;
+  if (dh == 128 && cl)
+    hipLaunchKernelGGL((flash_fwd_kernel<128, true>), grid, dim3(512), sm, s, q, c, lse2, S, H, D, causal, sl2, craw);
+  else if (dh == 128)
+    hipLaunchKernelGGL((flash_fwd_kernel<128, false>), grid, dim3(512), sm, s, q, c, lse2, S, H, D, causal, sl2, craw);
+  else if (cl)
+    hipLaunchKernelGGL((flash_fwd_kernel<64, true>), grid, dim3(512), sm, s, q, c, lse2, S, H, D, causal, sl2, craw);
+  else
+    hipLaunchKernelGGL((flash_fwd_kernel<64, false>), grid, dim3(512), sm, s, q, c, lse2, S, H, D, causal, sl2, craw);
   return hipGetLastError();
 }
 
 hipError_t flash_bwd(const void* qkv, const void* ctx, const void* dctx, const float* lse2,
-                     void* dqkv, int B, int H, int S, int D, int causal, hipStream_t s) {
+                     void* dqkv, int B, int H, int S, int D, int causal, float clip, hipStream_t s) {
   const int dh = D / H;
   const float scale = 1.0f / sqrtf(float(dh));
   const float sl2 = kLog2e * scale;
+  const float craw = raw_clip(clip, scale);
   const int nb = (S + kBlk - 1) / kBlk;
   if (B * H == 0 || nb == 0) return hipSuccess;
   const bf16_t* q = static_cast<const bf16_t*>(qkv);
@@ -667,12 +692,15 @@ hipError_t flash_bwd(const void* qkv, const void* ctx, const void* dctx, const f
   // id, so with B*H a multiple of 8 every block of one (sequence, head) --
   // which all read the same keys and values -- shares one XCD's L2
   const dim3 grid(B * H, 2 * nb);
-  if (dh == 128)
-    hipLaunchKernelGGL(flash_bwd_kernel<128>, grid, dim3(512), sm, s, q, o, dO, lse2, dq, S, H, D,
-                       causal, sl2, scale);
+  const bool cl = craw < INFINITY;
+  if (dh == 128 && cl)
+    hipLaunchKernelGGL((flash_bwd_kernel<128, true>), grid, dim3(512), sm, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
+  else if (dh == 128)
+    hipLaunchKernelGGL((flash_bwd_kernel<128, false>), grid, dim3(512), sm, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
+  else if (cl)
+    hipLaunchKernelGGL((flash_bwd_kernel<64, true>), grid, dim3(512), sm, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
   else
-    hipLaunchKernelGGL(flash_bwd_kernel<64>, grid, dim3(512), sm, s, q, o, dO, lse2, dq, S, H, D,
-                       causal, sl2, scale);
+    hipLaunchKernelGGL((flash_bwd_kernel<64, false>), grid, dim3(512), sm, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@ struct gpipe_cell {
   float* running;  // conv cells: moving averages [L][2][2][C]
   gpipe_precision prec;
   float ln_eps;
+  float logit_clip = 0.f;  // attention logit clipping threshold (0: off)
   size_t n_params;
   size_t per_layer;
   size_t rel_off[GPIPE_N_TENSORS];  // offsets inside one layer / block

@@ -383,11 +383,12 @@ gpipe_status layer_forward(const Ctx& x, int set, int slot, int l, const void* x
   Bat CX{ctx, D, int64_t(S) * D, dh};
   if (p.flash) {
     GP_RUN(x, GPIPE_ROLE_ATTN_FWD, flash_fwd(qkv, ctx, static_cast<float*>(P), p.B, H, S, D,
-                                             c->causal, x.s));
+                                             c->causal, c->logit_clip, x.s));
   } else {
     GP_RUN(x, GPIPE_ROLE_SCORES_FWD, bmm(x, GPIPE_ROLE_SCORES_FWD, S, S, dh, Q, K, SC,
                  c->causal ? CAUSAL_SKIP_UPPER : CAUSAL_NONE, scale));
-    GP_RUN(x, GPIPE_ROLE_SOFTMAX_FWD, softmax_fwd(x.bf16, scores, P, int64_t(p.B) * H * S, S, ldS, c->causal, x.s));
+    GP_RUN(x, GPIPE_ROLE_SOFTMAX_FWD, softmax_fwd(x.bf16, scores, P, int64_t(p.B) * H * S, S, ldS, c->causal,
+                                                  c->logit_clip, x.s));
     GP_RUN(x, GPIPE_ROLE_PV_FWD, bmm(x, GPIPE_ROLE_PV_FWD, S, dh, S, PP, V, CX,
                  c->causal ? CAUSAL_K_UPTO_M : CAUSAL_NONE, 1.0f));
   }
@@ -565,13 +566,25 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, const WgradDone& above, W
   if (p.flash) {
     const float* lse2 = static_cast<const float*>(P);
     // dQ, dK and dV in one launch
-    GP_RUN(x, GPIPE_ROLE_ATTN_DQ, flash_bwd(qkv, ctx, dctx, lse2, dqkv, p.B, H, S, D, cz, x.s));
+    GP_RUN(x, GPIPE_ROLE_ATTN_DQ, flash_bwd(qkv, ctx, dctx, lse2, dqkv, p.B, H, S, D, cz,
+                                            c->logit_clip, x.s));
   } else {
+    const bool clip = c->logit_clip > 0.f;
+    if (clip) {
+      // the clip's keep mask from the recomputed scores, into dS's buffer
+      // (softmax_bwd reads it there before writing dS); then dP takes the
+      // scores' buffer
+      Bat SC{dP, ldS, sp, int64_t(S) * ldS};
+      GP_RUN(x, GPIPE_ROLE_SCORES_FWD, bmm(x, GPIPE_ROLE_SCORES_FWD, S, S, dh, Q, K, SC,
+                   cz ? CAUSAL_SKIP_UPPER : CAUSAL_NONE, scale));
+      GP_CHECK(clip_keep(bf, dP, dS, int64_t(p.B) * H * S, S, ldS, cz, c->logit_clip, x.s));
+    }
     GP_RUN(x, GPIPE_ROLE_DP, bmm(x, GPIPE_ROLE_DP, S, S, dh, DC, V, DP,
                  cz ? CAUSAL_SKIP_UPPER : CAUSAL_NONE, 1.0f));
     GP_RUN(x, GPIPE_ROLE_DV, bmm(x, GPIPE_ROLE_DV, S, dh, S, PP, DC, dV,
                  cz ? CAUSAL_K_FROM_M : CAUSAL_NONE, 1.0f));
-    GP_RUN(x, GPIPE_ROLE_SOFTMAX_BWD, softmax_bwd(bf, P, dP, dS, int64_t(p.B) * H * S, S, ldS, cz, scale, x.s));
+    GP_RUN(x, GPIPE_ROLE_SOFTMAX_BWD, softmax_bwd(bf, P, dP, dS, int64_t(p.B) * H * S, S, ldS, cz, scale,
+                                                  clip ? 1 : 0, x.s));
     GP_RUN(x, GPIPE_ROLE_DQ, bmm(x, GPIPE_ROLE_DQ, S, dh, S, DS, K, dQ,
                  cz ? CAUSAL_K_UPTO_M : CAUSAL_NONE, 1.0f));
     GP_RUN(x, GPIPE_ROLE_DK, bmm(x, GPIPE_ROLE_DK, S, dh, S, DS, Q, dK,
@@ -910,12 +923,26 @@ gpipe_status gpipe_cell_sync_lowp(gpipe_cell* c, void* stream) {
 
 gpipe_status gpipe_cell_workspace_bytes(const gpipe_cell* c, int N, int M, int remat, size_t* bytes) {
   if (!c || !bytes) return GPIPE_ERR_INVALID;
-  if (c->kind == CELL_CONV)
-    return conv_workspace_bytes(c, N, M, remat, bytes) ? GPIPE_OK : GPIPE_ERR_INVALID;
-  Plan p;
-  if (!make_plan(c, N, M, remat, &p)) return GPIPE_ERR_INVALID;
-  *bytes = p.total;
-  return GPIPE_OK;
+  size_t plan = 0;
+  if (c->kind == CELL_CONV) {
+    if (!conv_workspace_bytes(c, N, M, remat, &plan)) return GPIPE_ERR_INVALID;
+  } else {
+    Plan p;
+    if (!make_plan(c, N, M, remat, &p)) return GPIPE_ERR_INVALID;
+    plan = p.total;
+  }
+  *bytes = plan;
+  // The fit: the plan, plus the parameter state while the cell is unbound
+  // (it must be allocated too), against the free memory of the current
+  // device.  Without a device (a host-only process) there is nothing to
+  // compare with and the plan is only reported.
+  size_t free_b = 0, total_b = 0;
+  if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) {
+    (void)hipGetLastError();
+    return GPIPE_OK;
+  }
+  const size_t state = c->bound ? 0 : c->n_params * (c->prec == GPIPE_BF16 ? 14 : 12);
+  return plan + state > free_b ? GPIPE_ERR_OOM : GPIPE_OK;
 }
 
 gpipe_status gpipe_cell_saved_offset(const gpipe_cell* c, int N, int M, int remat, int micro,
@@ -1006,6 +1033,28 @@ gpipe_status gpipe_cell_step_noalloc(gpipe_cell* c, const void* x, const void* t
   io.s = static_cast<hipStream_t>(stream);
   io.single = true;
   return transformer_run(c, io);
+}
+
+gpipe_status gpipe_cell_set_logit_clip(gpipe_cell* c, float threshold) {
+  if (!c || c->kind != CELL_TRANSFORMER || !(threshold >= 0.f) || !isfinite(threshold))
+    return GPIPE_ERR_INVALID;
+  c->logit_clip = threshold;
+  return GPIPE_OK;
+}
+
+gpipe_status gpipe_cell_scale_ffn_init(gpipe_cell* c, int total_layers, void* stream) {
+  if (!c || c->kind != CELL_TRANSFORMER || total_layers < 1) return GPIPE_ERR_INVALID;
+  if (!c->bound) return GPIPE_ERR_STATE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int l = 0; l < c->L; ++l)
+    for (const int t : {GPIPE_W_1, GPIPE_W_2}) {
+      const size_t off = size_t(l) * c->per_layer + c->rel_off[t];
+      GP_CHECK(div_scalar(c->master + off, int64_t(c->count[t]), float(total_layers), s));
+      if (c->prec == GPIPE_BF16)
+        GP_CHECK(to_bf16(c->master + off, static_cast<uint16_t*>(c->w_lowp) + off,
+                         int64_t(c->count[t]), s));
+    }
+  return GPIPE_OK;
 }
 
 gpipe_status gpipe_apply_update(gpipe_cell* c, float lr, float decay, float eps, void* stream) {

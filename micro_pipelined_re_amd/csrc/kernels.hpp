@@ -106,11 +106,18 @@ int layernorm_bwd_blocks(int rows, int d);
 
 // Softmax forward of scores (f32, already scaled) into P(act); rows of length n, row pitch ld,
 // optional causal mask (key j > row index i within its [n x n] block); masked entries -> 0.
+// clip > 0: the scores are clipped to [-clip, clip] first (logit clipping).
 hipError_t softmax_fwd(bool bf16, const float* scores, void* p, int64_t rows, int n, int64_t ld,
-                       int causal, hipStream_t s);
-// Softmax backward: dS(act) = scale * P * (dP - rowsum(P*dP)); masked entries -> 0.
+                       int causal, float clip, hipStream_t s);
+// Softmax backward: dS(act) = scale * P * (dP - rowsum(P*dP)); masked entries -> 0.  With
+// keep_in_ds, ds holds the clip's keep mask on entry (clip_keep) and clipped entries get 0.
 hipError_t softmax_bwd(bool bf16, const void* p, const float* dp, void* ds, int64_t rows, int n,
-                       int64_t ld, int causal, float scale, hipStream_t s);
+                       int64_t ld, int causal, float scale, int keep_in_ds, hipStream_t s);
+// keep(act) = 1 where |scores| <= clip, else 0 (same row layout as softmax_fwd).
+hipError_t clip_keep(bool bf16, const float* scores, void* keep, int64_t rows, int n, int64_t ld,
+                     int causal, float clip, hipStream_t s);
+// w[i] = w[i] / d over n floats (correctly rounded fp32 division).
+hipError_t div_scalar(float* w, int64_t n, float d, hipStream_t s);
 
 // MSE: r = y - t over `count` elements; dy = 2 r / denom into dy_f32 and dy_act;
 // per-block partial sums of r^2 / denom into part[nblk].
@@ -162,11 +169,13 @@ hipError_t bn_running(const float* rec, int M, int nbn, int C, int64_t n_total, 
 // bf16 cells with head dim 64 or 128.  qkv [B*S][3D], ctx/dctx [B*S][D],
 // lse2/delta [B*H][S] float32, dqkv [B*S][3D].
 bool flash_ok(bool bf16, int dh);
+// clip > 0: logit clipping, every score q.k/sqrt(dh) limited to [-clip, clip]
+// before the softmax; in the backward a clipped score passes no gradient.
 hipError_t flash_fwd(const void* qkv, void* ctx, float* lse2, int B, int H, int S, int D,
-                     int causal, hipStream_t s);
+                     int causal, float clip, hipStream_t s);
 // dQ, dK and dV in one launch (each block computes the row sums rowsum(dctx * ctx) it needs)
 hipError_t flash_bwd(const void* qkv, const void* ctx, const void* dctx, const float* lse2,
-                     void* dqkv, int B, int H, int S, int D, int causal, hipStream_t s);
+                     void* dqkv, int B, int H, int S, int D, int causal, float clip, hipStream_t s);
 
 // Tap-flipped, transposed 3 x 3 weights: dst[c][t][o] = src[o][8 - t][c] (bf16, C x C x 9);
 // the input gradient of a convolution is the convolution of its output gradient with them.

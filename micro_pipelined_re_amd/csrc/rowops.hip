@@ -326,10 +326,11 @@ hipError_t layernorm_bwd(bool bf16, const float* dh, const void* x, const float*
 // grouped in [n x n] blocks, so the query index of a row is row % n.  Causal
 // rows keep keys j <= i; the other entries of P, and the row padding, are
 // written as zeros.
+// clip > 0: every score is first clipped to [-clip, clip] (logit clipping).
 template <typename T, int NV>
 __global__ __launch_bounds__(256) void softmax_fwd_kernel(const float* __restrict__ sc,
                                                           T* __restrict__ p, int64_t rows, int n,
-                                                          int64_t ld, int causal) {
+                                                          int64_t ld, int causal, float clip) {
   const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
@@ -343,6 +344,9 @@ __global__ __launch_bounds__(256) void softmax_fwd_kernel(const float* __restric
     const int c = lane + 64 * i;
     if (c < nch && c * 8 < valid) {
       load8<float>(sr + c * 8, v[i]);
+      if (clip > 0.f)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[i][e] = fminf(fmaxf(v[i][e], -clip), clip);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (c * 8 + e >= valid) v[i][e] = -INFINITY;
@@ -378,11 +382,16 @@ __global__ __launch_bounds__(256) void softmax_fwd_kernel(const float* __restric
   }
 }
 
+// keep_in_ds: ds holds on entry the clip's keep mask (clip_keep_kernel: 1 where
+// the score passed the clip unchanged, 0 where it was clipped); a clipped
+// score gets no gradient.  Each thread reads its own chunk of the mask
+// before it overwrites it with dS.
 template <typename T, int NV>
 __global__ __launch_bounds__(256) void softmax_bwd_kernel(const T* __restrict__ p,
                                                           const float* __restrict__ dp,
-                                                          T* __restrict__ ds, int64_t rows, int n,
-                                                          int64_t ld, int causal, float scale) {
+                                                          T* ds, int64_t rows, int n,
+                                                          int64_t ld, int causal, float scale,
+                                                          int keep_in_ds) {
   const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
@@ -409,11 +418,39 @@ __global__ __launch_bounds__(256) void softmax_bwd_kernel(const T* __restrict__ 
   for (int i = 0; i < NV; ++i) {
     const int c = lane + 64 * i;
     if (c < nch) {
-      float o[8];
+      float o[8], kv[8];
       const bool live = c * 8 < valid;
+      if (keep_in_ds && live) load8<T>(dr + c * 8, kv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = live ? scale * pv[i][e] * (gv[i][e] - r) : 0.f;
+      for (int e = 0; e < 8; ++e) {
+        o[e] = live ? scale * pv[i][e] * (gv[i][e] - r) : 0.f;
+        if (keep_in_ds && live && kv[e] == 0.f) o[e] = 0.f;
+      }
       store8<T>(dr + c * 8, o);
+    }
+  }
+}
+
+// The logit clip's keep mask of scores sc: 1 where |s| <= clip, else 0 (the
+// causal mask's and the padding's entries are written as 0 too).
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void clip_keep_kernel(const float* __restrict__ sc,
+                                                        T* __restrict__ keep, int64_t rows, int n,
+                                                        int64_t ld, int causal, float clip) {
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int valid = causal ? int(row % n) + 1 : n;
+  const int nch = (n + 7) >> 3;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, o[8];
+      if (c * 8 < valid) load8<float>(sc + row * ld + c * 8, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (c * 8 + e < valid && fabsf(v[e]) <= clip) ? 1.f : 0.f;
+      store8<T>(keep + row * ld + c * 8, o);
     }
   }
 }
@@ -430,18 +467,39 @@ __global__ __launch_bounds__(256) void softmax_bwd_kernel(const T* __restrict__ 
   } while (0)
 
 hipError_t softmax_fwd(bool bf16, const float* scores, void* p, int64_t rows, int n, int64_t ld,
-                       int causal, hipStream_t s) {
+                       int causal, float clip, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  if (bf16) GP_SOFTMAX_DISPATCH(softmax_fwd_kernel, bf16_t, scores, static_cast<bf16_t*>(p), rows, n, ld, causal);
-  else GP_SOFTMAX_DISPATCH(softmax_fwd_kernel, float, scores, static_cast<float*>(p), rows, n, ld, causal);
+  if (bf16) GP_SOFTMAX_DISPATCH(softmax_fwd_kernel, bf16_t, scores, static_cast<bf16_t*>(p), rows, n, ld, causal, clip);
+  else GP_SOFTMAX_DISPATCH(softmax_fwd_kernel, float, scores, static_cast<float*>(p), rows, n, ld, causal, clip);
   return hipGetLastError();
 }
 
 hipError_t softmax_bwd(bool bf16, const void* p, const float* dp, void* ds, int64_t rows, int n,
-                       int64_t ld, int causal, float scale, hipStream_t s) {
+                       int64_t ld, int causal, float scale, int keep_in_ds, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  if (bf16) GP_SOFTMAX_DISPATCH(softmax_bwd_kernel, bf16_t, static_cast<const bf16_t*>(p), dp, static_cast<bf16_t*>(ds), rows, n, ld, causal, scale);
-  else GP_SOFTMAX_DISPATCH(softmax_bwd_kernel, float, static_cast<const float*>(p), dp, static_cast<float*>(ds), rows, n, ld, causal, scale);
+  if (bf16) GP_SOFTMAX_DISPATCH(softmax_bwd_kernel, bf16_t, static_cast<const bf16_t*>(p), dp, static_cast<bf16_t*>(ds), rows, n, ld, causal, scale, keep_in_ds);
+  else GP_SOFTMAX_DISPATCH(softmax_bwd_kernel, float, static_cast<const float*>(p), dp, static_cast<float*>(ds), rows, n, ld, causal, scale, keep_in_ds);
+  return hipGetLastError();
+}
+
+hipError_t clip_keep(bool bf16, const float* scores, void* keep, int64_t rows, int n, int64_t ld,
+                     int causal, float clip, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (bf16) GP_SOFTMAX_DISPATCH(clip_keep_kernel, bf16_t, scores, static_cast<bf16_t*>(keep), rows, n, ld, causal, clip);
+  else GP_SOFTMAX_DISPATCH(clip_keep_kernel, float, scores, static_cast<float*>(keep), rows, n, ld, causal, clip);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ w /= d (IEEE division)
+__global__ __launch_bounds__(256) void div_scalar_kernel(float* __restrict__ w, int64_t n, float d) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256)
+    w[i] = w[i] / d;
+}
+
+hipError_t div_scalar(float* w, int64_t n, float d, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int blocks = int(std::min<int64_t>((n + 255) / 256, 4096));
+  hipLaunchKernelGGL(div_scalar_kernel, dim3(blocks), dim3(256), 0, s, w, n, d);
   return hipGetLastError();
 }
 

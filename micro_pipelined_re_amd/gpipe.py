@@ -27,7 +27,8 @@ EXPORTS = ("gpipe_cell_create", "gpipe_cell_destroy", "gpipe_cell_param_count",
            "gpipe_apply_update", "gpipe_partition", "gpipe_status_string",
            "gpipe_cell_profile", "gpipe_cell_profile_read", "gpipe_cell_gemm_plan",
            "gpipe_conv_cell_create", "gpipe_cell_bind_running", "gpipe_cell_forward_plan",
-           "gpipe_cell_forward", "gpipe_cell_backward", "gpipe_cell_step_noalloc")
+           "gpipe_cell_forward", "gpipe_cell_backward", "gpipe_cell_step_noalloc",
+           "gpipe_cell_set_logit_clip", "gpipe_cell_scale_ffn_init")
 
 ROLES = ("ln1_fwd", "qkv_fwd", "scores_fwd", "softmax_fwd", "pv_fwd", "out_fwd", "ln2_fwd",
          "ffn1_fwd", "ffn2_fwd", "mse", "ffn2_dgrad", "ffn2_wgrad", "ffn1_dgrad", "ffn1_wgrad",
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
                                         ctypes.POINTER(_sz)],
             "gpipe_cell_step": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp, _vp],
             "gpipe_cell_forward": [_vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp],
+            "gpipe_cell_set_logit_clip": [_vp, ctypes.c_float],
+            "gpipe_cell_scale_ffn_init": [_vp, _i, _vp],
             "gpipe_cell_step_noalloc": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp],
             "gpipe_cell_backward": [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp],
             "gpipe_apply_update": [_vp, ctypes.c_float, ctypes.c_float, ctypes.c_float, _vp],
@@ -178,6 +181,16 @@ def gpipe_cell_workspace_bytes(cell, N: int, M: int, remat: bool) -> int:
     return b.value
 
 
+def gpipe_cell_workspace_fit(cell, N: int, M: int, remat: bool):
+    """(plan bytes, fits): gpipe_cell_workspace_bytes with GPIPE_ERR_OOM as fits=False."""
+    b = _sz()
+    code = lib().gpipe_cell_workspace_bytes(cell, N, M, int(bool(remat)), ctypes.byref(b))
+    if code == 2:
+        return b.value, False
+    _check("gpipe_cell_workspace_bytes", code)
+    return b.value, True
+
+
 def gpipe_cell_saved_offset(cell, N, M, remat, micro, layer, which):
     off, nb = _sz(), _sz()
     _check("gpipe_cell_saved_offset",
@@ -212,6 +225,15 @@ def gpipe_cell_backward(cell, x, dy, dx, N, M, remat, workspace, ws_bytes, strea
     _check("gpipe_cell_backward",
            lib().gpipe_cell_backward(cell, _ptr(x), _ptr(dy), _ptr(dx), N, M, int(bool(remat)),
                                      _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def gpipe_cell_set_logit_clip(cell, threshold: float) -> None:
+    _check("gpipe_cell_set_logit_clip", lib().gpipe_cell_set_logit_clip(cell, float(threshold)))
+
+
+def gpipe_cell_scale_ffn_init(cell, total_layers: int, stream=None) -> None:
+    _check("gpipe_cell_scale_ffn_init",
+           lib().gpipe_cell_scale_ffn_init(cell, int(total_layers), _stream(stream)))
 
 
 def gpipe_apply_update(cell, lr, decay, eps, stream=None) -> None:
@@ -282,6 +304,7 @@ class Cell:
         gpipe_cell_bind(self.handle, self.master, self.w_lowp, self.grad, self.ms)
         self.loss = torch.zeros(1, dtype=torch.float32, device=device)
         self._ws = None
+        self._plans = {}
 
     @classmethod
     def from_config(cls, cfg, device="cuda"):
@@ -331,7 +354,21 @@ class Cell:
         return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(self.device)
 
     def workspace(self, N, M, remat=True):
-        nb = gpipe_cell_workspace_bytes(self.handle, N, M, remat)
+        """The workspace for (N, M, remat).  Each plan is queried once, before
+        anything is allocated for it (the query's fit check counts a workspace
+        already held as used memory); a refused plan that the held workspace
+        cannot cover releases it and is asked again, raising GpipeError (OOM)
+        if it still does not fit."""
+        key = (N, M, bool(remat))
+        nb = self._plans.get(key)
+        if nb is None:
+            nb, fits = gpipe_cell_workspace_fit(self.handle, N, M, remat)
+            held = 0 if self._ws is None else self._ws.numel()
+            if not fits and nb > held:
+                self._ws = None
+                self.torch.cuda.empty_cache()
+                nb = gpipe_cell_workspace_bytes(self.handle, N, M, remat)
+            self._plans[key] = nb
         if self._ws is None or self._ws.numel() < nb:
             self._ws = None
             self._ws = self.torch.empty(max(nb, 1), dtype=self.torch.uint8, device=self.device)
@@ -396,6 +433,7 @@ class ConvCell(Cell):
         gpipe_cell_bind_running(self.handle, self.running)
         self.loss = torch.zeros(1, dtype=torch.float32, device=device)
         self._ws = None
+        self._plans = {}
 
     @classmethod
     def from_config(cls, cfg, device="cuda"):

@@ -15,6 +15,11 @@ from oracle.partition import partition_bruteforce
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def ws_plan(h, n, m, remat):
+    """The planned workspace bytes, whether or not the current device would fit them."""
+    return gpipe.gpipe_cell_workspace_fit(h, n, m, remat)[0]
+
+
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "gpipe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -92,8 +97,8 @@ def test_workspace_tracks_the_activation_bound(cfg):
                                 cfg.causal, prec)
     try:
         n, m = cfg.batch, cfg.micro
-        remat = gpipe.gpipe_cell_workspace_bytes(h, n, m, True)
-        keep = gpipe.gpipe_cell_workspace_bytes(h, n, m, False)
+        remat = ws_plan(h, n, m, True)
+        keep = ws_plan(h, n, m, False)
         formula = saved_set_bytes_formula(cfg, n, m, eb)
         set_bytes = (gpipe.gpipe_cell_saved_offset(h, n, m, False, 1, 0, 1)[0]
                      - gpipe.gpipe_cell_saved_offset(h, n, m, False, 0, 0, 1)[0])
@@ -109,7 +114,7 @@ def test_workspace_tracks_the_activation_bound(cfg):
             assert transient < 0.6 * set_bytes
         # halving the micro-batch halves the set
         if n % (2 * m) == 0:
-            assert gpipe.gpipe_cell_workspace_bytes(h, n, 2 * m, True) < 0.6 * remat + transient
+            assert ws_plan(h, n, 2 * m, True) < 0.6 * remat + transient
     finally:
         gpipe.gpipe_cell_destroy(h)
 
@@ -124,8 +129,8 @@ def test_memory_cell_at_one_micro_batch_exceeds_one_gpu():
     h = gpipe.gpipe_cell_create(cfg.layers, cfg.d_model, cfg.heads, cfg.d_ff, cfg.seq, False,
                                 gpipe.GPIPE_BF16)
     try:
-        m1 = gpipe.gpipe_cell_workspace_bytes(h, 32, 1, True)
-        m32 = gpipe.gpipe_cell_workspace_bytes(h, 32, 32, True)
+        m1 = ws_plan(h, 32, 1, True)
+        m32 = ws_plan(h, 32, 32, True)
         state = gpipe.gpipe_cell_param_count(h) * 14
         assert m1 + state > 288e9
         assert m1 > 200e9
@@ -154,9 +159,9 @@ def test_workspace_and_step_validation_without_device():
     h = gpipe.gpipe_cell_create(2, 64, 4, 256, 32, 0, gpipe.GPIPE_FP32)
     try:
         with pytest.raises(gpipe.GpipeError):
-            gpipe.gpipe_cell_workspace_bytes(h, 8, 3, True)      # N % M != 0
+            ws_plan(h, 8, 3, True)      # N % M != 0
         with pytest.raises(gpipe.GpipeError):
-            gpipe.gpipe_cell_workspace_bytes(h, 0, 1, True)
+            ws_plan(h, 0, 1, True)
         # stepping an unbound cell is a state error; nothing is launched
         with pytest.raises(gpipe.GpipeError) as e:
             gpipe.gpipe_cell_step(h, 16, 16, 16, None, 8, 4, True, 16, 1 << 30, 0, 16)
@@ -171,7 +176,7 @@ def test_workspace_and_step_validation_without_device():
         with pytest.raises(gpipe.GpipeError):
             gpipe.gpipe_cell_bind(h, 258, None, 256, 256)
         gpipe.gpipe_cell_bind(h, 256, None, 512, 768)            # host-side bookkeeping only
-        ws = gpipe.gpipe_cell_workspace_bytes(h, 8, 4, True)
+        ws = ws_plan(h, 8, 4, True)
         with pytest.raises(gpipe.GpipeError) as e:               # workspace too small
             gpipe.gpipe_cell_step(h, 16, 16, 16, None, 8, 4, True, 16, ws - 1, 0, 16)
         assert e.value.code == 1
@@ -202,7 +207,7 @@ def test_saved_offsets_are_disjoint_and_inside_the_workspace():
     h = gpipe.gpipe_cell_create(cfg.layers, cfg.d_model, cfg.heads, cfg.d_ff, cfg.seq, 0, 0)
     try:
         for remat in (True, False):
-            ws = gpipe.gpipe_cell_workspace_bytes(h, 8, 4, remat)
+            ws = ws_plan(h, 8, 4, remat)
             spans = []
             for m in range(1 if remat else 4):
                 for l in range(cfg.layers):
@@ -295,7 +300,7 @@ def test_conv_create_and_bind_validation():
     h = gpipe.gpipe_conv_cell_create(cfg.blocks, cfg.channels, cfg.height, cfg.width, 0.9, 0)
     try:
         gpipe.gpipe_cell_bind(h, 256, None, 512, 768)            # host-side bookkeeping only
-        ws = gpipe.gpipe_cell_workspace_bytes(h, 8, 4, True)
+        ws = ws_plan(h, 8, 4, True)
         with pytest.raises(E) as e:                               # moving averages not bound
             gpipe.gpipe_cell_step(h, 16, 16, 16, None, 8, 4, True, 16, ws, 0, 16)
         assert e.value.code == 5
@@ -318,7 +323,7 @@ def test_conv_saved_offsets_and_workspace_scaling():
     try:
         P = (8 // 4) * cfg.height * cfg.width
         for remat in (True, False):
-            ws = gpipe.gpipe_cell_workspace_bytes(h, 8, 4, remat)
+            ws = ws_plan(h, 8, 4, remat)
             spans = []
             for m in range(1 if remat else 4):
                 for l in range(cfg.blocks):
@@ -337,8 +342,8 @@ def test_conv_saved_offsets_and_workspace_scaling():
                 assert a[1] <= b[0]
         # re-materialization keeps one micro-batch's set (plus the re-computed
         # output); without it every micro-batch's set is kept
-        r = [gpipe.gpipe_cell_workspace_bytes(h, 64, m, True) for m in (1, 2, 4)]
-        s = [gpipe.gpipe_cell_workspace_bytes(h, 64, m, False) for m in (1, 2, 4)]
+        r = [ws_plan(h, 64, m, True) for m in (1, 2, 4)]
+        s = [ws_plan(h, 64, m, False) for m in (1, 2, 4)]
         assert r[0] > r[1] > r[2]
         set_bytes = (gpipe.gpipe_cell_saved_offset(h, 64, 4, False, 1, 0, 1)[0]
                      - gpipe.gpipe_cell_saved_offset(h, 64, 4, False, 0, 0, 1)[0])
@@ -355,7 +360,7 @@ def test_conv_workspace_drops_the_column_matrix_with_the_gathered_weight_gradien
     def ws(h, w, n, m):
         hd = gpipe.gpipe_conv_cell_create(2, 64, h, w, 0.9, gpipe.GPIPE_BF16)
         try:
-            return gpipe.gpipe_cell_workspace_bytes(hd, n, m, True)
+            return ws_plan(hd, n, m, True)
         finally:
             gpipe.gpipe_cell_destroy(hd)
     row = 9 * 64 * 2                         # one pixel's column-matrix row, bf16
@@ -487,7 +492,7 @@ def test_grouped_forward_fits_its_partials_and_keeps_the_k_order(cfg):
                 assert one[r][2] * b * cfg.seq * _fwd_out_cols(cfg, r) * 4 <= lane_bytes
         # lanes x (G micro-batches' layer slot) fit in one micro-batch's saved set
         if G > 1:
-            ws1 = gpipe.gpipe_cell_workspace_bytes(h, N, M, True)
+            ws1 = ws_plan(h, N, M, True)
             assert ws1 > 0
         # without re-materialization the forward phase runs one micro-batch at a time
         assert gpipe.gpipe_cell_forward_plan(h, N, M, False)[:2] == (1, 1)
