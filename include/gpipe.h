@@ -110,12 +110,20 @@ typedef enum {
   GPIPE_CONV_N_TENSORS
 } gpipe_conv_tensor;
 
+/* Saved tensors of one block for one micro-batch of P = (N/M)*H*W pixels.
+ * Micro-batch BatchNorm makes the cell's gradients small remainders of
+ * near-cancellations, so a bf16 conv cell keeps its forward activations exact
+ * to about 2^-17: x and r as split pairs of bf16, [P, 2C] with hi = bf16(v) in
+ * channels 0..C-1 and lo = bf16(v - hi) in channels C..2C-1 (v ~ hi + lo; the
+ * forward convolutions take them as 2C-channel inputs with the weights
+ * repeated over both halves), a and z in float32; only the backward's
+ * operands are bf16.  In fp32 cells x and r are float32 [P, C]. */
 typedef enum {
-  GPIPE_CONV_SAVED_X = 0, /* block input [P, C], P = (N/M)*H*W (block 0: the caller's x) */
-  GPIPE_CONV_SAVED_A,     /* conv1 output [P, C] */
+  GPIPE_CONV_SAVED_X = 0, /* block input (block 0: the caller's x, not saved) */
+  GPIPE_CONV_SAVED_A,     /* conv1 output [P, C] float32 */
   GPIPE_CONV_SAVED_ST1,   /* BN1 (mean[C], rstd[C]) float32 */
-  GPIPE_CONV_SAVED_R,     /* ReLU(BN1(a)) [P, C] */
-  GPIPE_CONV_SAVED_Z,     /* conv2 output [P, C] */
+  GPIPE_CONV_SAVED_R,     /* ReLU(BN1(a)) */
+  GPIPE_CONV_SAVED_Z,     /* conv2 output [P, C] float32 */
   GPIPE_CONV_SAVED_ST2,   /* BN2 (mean[C], rstd[C]) float32 */
   GPIPE_CONV_N_SAVED
 } gpipe_conv_saved;

@@ -11,13 +11,28 @@
 namespace gp {
 namespace {
 
+// Storage.  Micro-batch BatchNorm makes this cell's gradients the small
+// remainder of near-cancellations: a relative rounding of 2^-9 in any forward
+// activation (block output, conv output, ReLU output) moves dx and the weight
+// gradients by 2-5% (measured on the float64 oracle at the 64- and
+// 256-channel shapes), while the same rounding of the backward's gradients
+// moves them by 0.1-0.4%.  So bf16 cells keep the forward exact to float32
+// level: the convolution outputs a and z (the BatchNorm inputs) in float32,
+// the block outputs and ReLU outputs -- the convolutions' input operands -- as
+// split bf16 pairs [P][2C] (SK_SPLIT: hi + lo), convolved with the weights
+// repeated over both halves; the backward's operands (dz, da) stay bf16, and
+// the weight gradients read the hi halves.  Every saved tensor is then 4 bytes
+// per element in both precisions.
+//
 // Byte layout of a conv-cell workspace for one (N, M, remat):
 //   sets:  remat ? 1 : M micro-batch sets, each L blocks of the saved tensors
 //          of gpipe_conv_saved (block 0 has no X slot in use)
-//   yre:   output of the re-materialized forward [P, C] (remat only)
-//   col:   im2col matrix [P, 9C] (act; explicit weight gradient and explicit path)
-//   dcol:  its gradient [P, 9C] (f32, explicit path)
+//   yre:   output of the re-materialized forward [P, C] (act; remat only)
+//   col:   im2col matrix (act): [P, 9 Cin] for the explicit forward (Cin = 2C
+//          for split inputs), [P, 9C] for the explicit weight gradient
+//   dcol:  [P, 9C] input-gradient columns (f32, explicit path)
 //   wflip: tap-flipped transposed weights [L][2][C][9][C] (implicit path)
+//   wdup:  weights repeated over split inputs [L][2][C][9][2C] (bf16 cells)
 //   r0:    residual-stream gradient [P, C] (f32);  r1: ReLU-input gradient (f32)
 //   dz:    BN input gradient [P, C] (act, GEMM operand)
 //   part, sums: BN reduction partials;  rec: forward-phase moments [M][2L][2][C]
@@ -31,7 +46,8 @@ struct CPlan {
   size_t saved_off[GPIPE_CONV_N_SAVED], saved_bytes[GPIPE_CONV_N_SAVED];
   size_t block_bytes, set_bytes;
   int nsets;
-  size_t yre, col, dcol, r0, r1, dz, part, sums, rec, msepart, splitk, wflip;
+  size_t yre, col, dcol, r0, r1, dz, part, sums, rec, msepart, splitk, wflip, wdup;
+  bool split;  // bf16 cells: split forward activations (see above)
   // forward-phase lanes (see conv_cell_step): count, and the BN / split-K
   // partials of lanes 1 and 2 (lane 0 uses part and splitk)
   int lanes;
@@ -56,8 +72,10 @@ bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
   p->P = int64_t(P);
   const size_t eb = c->prec == GPIPE_BF16 ? 2 : 4;
   p->eb = eb;
-  const size_t sizes[GPIPE_CONV_N_SAVED] = {P * C * eb, P * C * eb, 2 * C * 4,
-                                            P * C * eb, P * C * eb, 2 * C * 4};
+  p->split = c->prec == GPIPE_BF16;
+  // x, r: f32 [P][C] or split [P][2C] bf16; a, z: f32 -- 4 bytes per element
+  const size_t sizes[GPIPE_CONV_N_SAVED] = {P * C * 4, P * C * 4, 2 * C * 4,
+                                            P * C * 4, P * C * 4, 2 * C * 4};
   size_t off = 0;
   for (int i = 0; i < GPIPE_CONV_N_SAVED; ++i) {
     p->saved_off[i] = off;
@@ -76,10 +94,12 @@ bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
   p->implicit = c->prec == GPIPE_BF16 && C % 64 == 0;
   p->implicit_wgrad = p->implicit && P % 64 == 0 && P < (size_t(1) << 21) &&
                       (P + 64) * C < (size_t(1) << 31);
+  const size_t cin = p->split ? 2 * C : C;  // channels of a forward convolution's input
   p->yre = take(remat ? P * C * eb : 0);
-  p->col = take(p->implicit_wgrad ? 0 : P * 9 * C * eb);
+  p->col = take(!p->implicit ? P * 9 * cin * eb : p->implicit_wgrad ? 0 : P * 9 * C * eb);
   p->dcol = take(p->implicit ? 0 : P * 9 * C * 4);
   p->wflip = take(p->implicit ? size_t(c->L) * 2 * 9 * C * C * 2 : 0);
+  p->wdup = take(p->split ? size_t(c->L) * 2 * 9 * C * cin * 2 : 0);
   p->r0 = take(P * C * 4);
   p->r1 = take(P * C * 4);
   p->dz = take(P * C * eb);
@@ -90,10 +110,14 @@ bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
   p->msepart = take(size_t(M) * p->mse_nblk * 4);
   const bool bf = c->prec == GPIPE_BF16;
   const int Pi = int(P), Ci = int(C);
-  const size_t sk = std::max({gemm_partial_floats(GPIPE_ROLE_CONV_FWD, bf, Pi, Ci, 9 * Ci, 1),
+  const int Ki = int(9 * cin);  // k extent of a forward convolution of a split input
+  const size_t skf = std::max({gemm_partial_floats(GPIPE_ROLE_CONV_FWD, bf, Pi, Ci, 9 * Ci, 1),
+                               gemm_partial_floats(GPIPE_ROLE_CONV_FWD, bf, Pi, Ci, Ki, 1),
+                               gemm_partial_floats(GPIPE_ROLE_CONV_FWD_IMPLICIT, bf, Pi, Ci, 9 * Ci, 1),
+                               gemm_partial_floats(GPIPE_ROLE_CONV_FWD_IMPLICIT, bf, Pi, Ci, Ki, 1)});
+  const size_t sk = std::max({skf,
                               gemm_partial_floats(GPIPE_ROLE_CONV_DGRAD, bf, Pi, 9 * Ci, Ci, 1),
                               gemm_partial_floats(GPIPE_ROLE_CONV_WGRAD, bf, Ci, 9 * Ci, Pi, 1),
-                              gemm_partial_floats(GPIPE_ROLE_CONV_FWD_IMPLICIT, bf, Pi, Ci, 9 * Ci, 1),
                               gemm_partial_floats(GPIPE_ROLE_CONV_DGRAD_IMPLICIT, bf, Pi, Ci, 9 * Ci, 1),
                               gemm_partial_floats(GPIPE_ROLE_CONV_WGRAD_IMPLICIT, bf, Ci, 9 * Ci, Pi, 1)});
   p->splitk = take(sk * 4);
@@ -101,7 +125,6 @@ bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
   // blocks (their partials are laid out with or without re-materialization,
   // so that the two workspaces differ by the saved sets only)
   p->lanes = p->implicit && c->L >= 2 ? std::min(3, c->L) : 1;
-  const size_t skf = gemm_partial_floats(GPIPE_ROLE_CONV_FWD_IMPLICIT, bf, Pi, Ci, 9 * Ci, 1);
   p->lane_part[0] = p->part;
   p->lane_splitk[0] = p->splitk;
   for (int k = 1; k < 3; ++k) {
@@ -149,6 +172,14 @@ struct CCtx {
     const size_t n = size_t(9) * c->C * c->C;
     return ws + p->wflip + (size_t(block) * 2 + which) * n * 2;
   }
+  // the same convolution's weights repeated over a split input's halves
+  const void* dup(int block, int which) const {
+    const size_t n = size_t(9) * c->C * 2 * c->C;
+    return ws + p->wdup + (size_t(block) * 2 + which) * n * 2;
+  }
+  // storage of the caller's activations and of the block boundaries / ReLU outputs
+  int act_kind() const { return bf16 ? SK_BF16 : SK_F32; }
+  int xs_kind() const { return p->split ? SK_SPLIT : SK_F32; }
 };
 
 hipError_t cmm(const CCtx& x, int role, int M, int N, int K, const void* A, int64_t lda,
@@ -166,32 +197,36 @@ hipError_t cmm(const CCtx& x, int role, int M, int N, int K, const void* A, int6
   return gemm(x.bf16, role, g, 1, x.s);
 }
 
-// Implicit-GEMM convolution of an NHWC image [P, C] with [C][9C] weights
-// (k-contiguous): out[P, C] (beta: accumulate into an f32 output).
-hipError_t cconv(const CCtx& x, int role, const void* img, const void* w, void* out, int beta) {
+// Implicit-GEMM convolution of an NHWC image [P, cin] with [C][9 cin] weights
+// (k-contiguous): out[P, C] f32 (beta: accumulate).
+hipError_t cconv(const CCtx& x, int role, const void* img, int cin, const void* w, void* out,
+                 int beta) {
   GemmParams g;
   memset(&g, 0, sizeof(g));
   const int C = x.c->C;
   g.hdiv = 1;
   g.alpha = 1.0f;
-  g.M = int(x.p->P); g.N = C; g.K = 9 * C;
-  g.A = img; g.lda = C;
-  g.B = w; g.ldb = 9 * C;
+  g.M = int(x.p->P); g.N = C; g.K = 9 * cin;
+  g.A = img; g.lda = cin;
+  g.B = w; g.ldb = 9 * cin;
   g.C = out; g.ldc = C;
   g.beta = beta;
-  g.conv_h = x.c->Hc; g.conv_w = x.c->Wc; g.conv_c = C;
+  g.conv_h = x.c->Hc; g.conv_w = x.c->Wc; g.conv_c = cin;
   g.P = x.f(x.splitk);
   return gemm(true, role, g, 1, x.s);
 }
 
-// Weight gradient of a convolution: grad (+)= dz^T im2col(img), [C][9C] f32.
-gpipe_status cwgrad(const CCtx& x, const void* img, const void* dz, float* grad, int beta) {
+// Weight gradient of a convolution: grad (+)= dz^T im2col(img), [C][9C] f32,
+// img the first C channels of an image of pixel stride img_ld (the hi half of
+// a split activation).
+gpipe_status cwgrad(const CCtx& x, const void* img, int img_ld, const void* dz, float* grad,
+                    int beta) {
   const gpipe_cell* c = x.c;
   const int C = c->C;
   const int P = int(x.p->P);
   if (!x.p->implicit_wgrad) {
     void* col = x.at(x.p->col);
-    GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, img, col, x.p->B, c->Hc, c->Wc, C, x.s));
+    GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, img, img_ld, col, x.p->B, c->Hc, c->Wc, C, x.s));
     GP_RUN(x, GPIPE_ROLE_CONV_WGRAD,
            cmm(x, GPIPE_ROLE_CONV_WGRAD, C, 9 * C, P, dz, C, col, 9 * C, grad, 9 * C, beta));
     return GPIPE_OK;
@@ -206,6 +241,7 @@ gpipe_status cwgrad(const CCtx& x, const void* img, const void* dz, float* grad,
   g.C = grad; g.ldc = 9 * C;
   g.beta = beta;
   g.conv_h = c->Hc; g.conv_w = c->Wc; g.conv_c = C;
+  g.conv_ld = img_ld;
   g.P = x.f(x.splitk);
   GP_RUN(x, GPIPE_ROLE_CONV_WGRAD_IMPLICIT, gemm(true, GPIPE_ROLE_CONV_WGRAD_IMPLICIT, g, 1, x.s));
   return GPIPE_OK;
@@ -221,36 +257,51 @@ gpipe_status block_forward(const CCtx& x, int set, int slot, int l, const void* 
   const CPlan& p = *x.p;
   const int C = c->C, B = p.B, H = c->Hc, W = c->Wc;
   const int64_t P = p.P;
-  void* col = x.at(p.col);
   void* a = x.at(csaved_at(p, set, slot, GPIPE_CONV_SAVED_A));
   float* st1 = x.f(csaved_at(p, set, slot, GPIPE_CONV_SAVED_ST1));
   void* r = x.at(csaved_at(p, set, slot, GPIPE_CONV_SAVED_R));
   void* z = x.at(csaved_at(p, set, slot, GPIPE_CONV_SAVED_Z));
   float* st2 = x.f(csaved_at(p, set, slot, GPIPE_CONV_SAVED_ST2));
   float* part = x.f(x.part);
-  if (p.implicit) {
-    GP_RUN(x, GPIPE_ROLE_CONV_FWD_IMPLICIT,
-           cconv(x, GPIPE_ROLE_CONV_FWD_IMPLICIT, xin, x.wmat(l, GPIPE_CONV_W1), a, 0));
-  } else {
-    GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, xin, col, B, H, W, C, x.s));
-    GP_RUN(x, GPIPE_ROLE_CONV_FWD, cmm(x, GPIPE_ROLE_CONV_FWD, int(P), C, 9 * C, col, 9 * C,
-                                       x.wmat(l, GPIPE_CONV_W1), 9 * C, a, C));
+  // block 0 reads the caller's x, the last block writes the caller's y (or
+  // the re-materialized output), both in the cell's activation type; the
+  // boundaries between blocks and the ReLU outputs are split in bf16 cells
+  const int in_kind = l == 0 ? x.act_kind() : x.xs_kind();
+  const int out_kind = l == c->L - 1 ? x.act_kind() : x.xs_kind();
+  const int r_kind = x.xs_kind();
+  // conv(img, W_which): a split image meets the repeated weights over 2C channels
+  auto conv = [&](const void* img, int kind, int which, float* out) -> gpipe_status {
+    const int cin = kind == SK_SPLIT ? 2 * C : C;
+    const void* w = kind == SK_SPLIT ? x.dup(l, which)
+                                     : x.wmat(l, which == 0 ? GPIPE_CONV_W1 : GPIPE_CONV_W2);
+    if (p.implicit) {
+      GP_RUN(x, GPIPE_ROLE_CONV_FWD_IMPLICIT,
+             cconv(x, GPIPE_ROLE_CONV_FWD_IMPLICIT, img, cin, w, out, 0));
+    } else {
+      void* col = x.at(p.col);
+      GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, img, cin, col, B, H, W, cin, x.s));
+      GP_RUN(x, GPIPE_ROLE_CONV_FWD, cmm(x, GPIPE_ROLE_CONV_FWD, int(P), C, 9 * cin, col, 9 * cin,
+                                         w, 9 * cin, out, C));
+    }
+    return GPIPE_OK;
+  };
+  {
+    const gpipe_status st = conv(xin, in_kind, 0, static_cast<float*>(a));
+    if (st != GPIPE_OK) return st;
   }
-  GP_RUN(x, GPIPE_ROLE_BN_STATS, bn_stats(x.bf16, a, P, C, c->bn_eps, part, st1, rec, x.s));
-  GP_RUN(x, GPIPE_ROLE_BN_APPLY, bn_apply(x.bf16, 0, a, st1, x.wf32(l, GPIPE_CONV_BN1_G),
-                                          x.wf32(l, GPIPE_CONV_BN1_B), nullptr, r, P, C, x.s));
-  if (p.implicit) {
-    GP_RUN(x, GPIPE_ROLE_CONV_FWD_IMPLICIT,
-           cconv(x, GPIPE_ROLE_CONV_FWD_IMPLICIT, r, x.wmat(l, GPIPE_CONV_W2), z, 0));
-  } else {
-    GP_RUN(x, GPIPE_ROLE_IM2COL, im2col(x.bf16, r, col, B, H, W, C, x.s));
-    GP_RUN(x, GPIPE_ROLE_CONV_FWD, cmm(x, GPIPE_ROLE_CONV_FWD, int(P), C, 9 * C, col, 9 * C,
-                                       x.wmat(l, GPIPE_CONV_W2), 9 * C, z, C));
+  GP_RUN(x, GPIPE_ROLE_BN_STATS, bn_stats(false, a, P, C, c->bn_eps, part, st1, rec, x.s));
+  GP_RUN(x, GPIPE_ROLE_BN_APPLY, bn_apply(0, static_cast<const float*>(a), st1,
+                                          x.wf32(l, GPIPE_CONV_BN1_G), x.wf32(l, GPIPE_CONV_BN1_B),
+                                          nullptr, SK_F32, r, r_kind, P, C, x.s));
+  {
+    const gpipe_status st = conv(r, r_kind, 1, static_cast<float*>(z));
+    if (st != GPIPE_OK) return st;
   }
   GP_RUN(x, GPIPE_ROLE_BN_STATS,
-         bn_stats(x.bf16, z, P, C, c->bn_eps, part, st2, rec ? rec + 2 * C : nullptr, x.s));
-  GP_RUN(x, GPIPE_ROLE_BN_APPLY, bn_apply(x.bf16, 1, z, st2, x.wf32(l, GPIPE_CONV_BN2_G),
-                                          x.wf32(l, GPIPE_CONV_BN2_B), xin, xout, P, C, x.s));
+         bn_stats(false, z, P, C, c->bn_eps, part, st2, rec ? rec + 2 * C : nullptr, x.s));
+  GP_RUN(x, GPIPE_ROLE_BN_APPLY, bn_apply(1, static_cast<const float*>(z), st2,
+                                          x.wf32(l, GPIPE_CONV_BN2_G), x.wf32(l, GPIPE_CONV_BN2_B),
+                                          xin, in_kind, xout, out_kind, P, C, x.s));
   return GPIPE_OK;
 }
 
@@ -279,10 +330,13 @@ gpipe_status block_backward(const CCtx& x, Streams* ss, hipEvent_t* dz_reader, i
   const CPlan& p = *x.p;
   const int C = c->C, B = p.B, H = c->Hc, W = c->Wc;
   const int64_t P = p.P;
-  const void* a = x.at(csaved_at(p, set, slot, GPIPE_CONV_SAVED_A));
+  const float* a = x.f(csaved_at(p, set, slot, GPIPE_CONV_SAVED_A));
   const float* st1 = x.f(csaved_at(p, set, slot, GPIPE_CONV_SAVED_ST1));
   const void* r = x.at(csaved_at(p, set, slot, GPIPE_CONV_SAVED_R));
-  const void* z = x.at(csaved_at(p, set, slot, GPIPE_CONV_SAVED_Z));
+  const float* z = x.f(csaved_at(p, set, slot, GPIPE_CONV_SAVED_Z));
+  // pixel strides of the weight gradients' images: the hi halves of split ones
+  const int r_ld = x.xs_kind() == SK_SPLIT ? 2 * C : C;
+  const int x_ld = (l == 0 || x.xs_kind() != SK_SPLIT) ? C : 2 * C;
   const float* st2 = x.f(csaved_at(p, set, slot, GPIPE_CONV_SAVED_ST2));
   CCtx w = x;  // the weight gradients' context
   if (ss) {
@@ -298,20 +352,20 @@ gpipe_status block_backward(const CCtx& x, Streams* ss, hipEvent_t* dz_reader, i
   float* sums = x.f(p.sums);
   int nch = 0;
   // y = x + BN2(z) (the gain and shift gradients, adjacent, accumulate in the same pass)
-  GP_RUN(x, GPIPE_ROLE_BN_BWD, bn_bwd(x.bf16, 0, r0, nullptr, z, st2, x.wf32(l, GPIPE_CONV_BN2_G),
-                                      part, sums, x.grad(l, GPIPE_CONV_BN2_G), beta, dz, P, C,
-                                      &nch, x.s));
+  GP_RUN(x, GPIPE_ROLE_BN_BWD, bn_bwd(x.act_kind(), 0, r0, nullptr, SK_F32, z, st2,
+                                      x.wf32(l, GPIPE_CONV_BN2_G), part, sums,
+                                      x.grad(l, GPIPE_CONV_BN2_G), beta, dz, P, C, &nch, x.s));
   // z = conv(r, W2)
   hipEvent_t w2 = nullptr;
   {
     if (ss && !ss->fork()) return GPIPE_ERR_DEVICE;
-    const gpipe_status st = cwgrad(w, r, dz, x.grad(l, GPIPE_CONV_W2), beta);
+    const gpipe_status st = cwgrad(w, r, r_ld, dz, x.grad(l, GPIPE_CONV_W2), beta);
     if (st != GPIPE_OK) return st;
     if (ss && !ss->mark(&w2)) return GPIPE_ERR_DEVICE;
   }
   if (p.implicit) {
     GP_RUN(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT,
-           cconv(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT, dz, x.flipped(l, 1), r1, 0));
+           cconv(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT, dz, C, x.flipped(l, 1), r1, 0));
   } else {
     GP_RUN(x, GPIPE_ROLE_CONV_DGRAD, cmm(x, GPIPE_ROLE_CONV_DGRAD, int(P), 9 * C, C, dz, C,
                                          x.wmat(l, GPIPE_CONV_W2), 9 * C, dcol, 9 * C));
@@ -319,20 +373,20 @@ gpipe_status block_backward(const CCtx& x, Streams* ss, hipEvent_t* dz_reader, i
   }
   // r = ReLU(BN1(a))
   if (ss && !ss->join(w2)) return GPIPE_ERR_DEVICE;
-  GP_RUN(x, GPIPE_ROLE_BN_BWD, bn_bwd(x.bf16, 1, r1, r, a, st1, x.wf32(l, GPIPE_CONV_BN1_G), part,
-                                      sums, x.grad(l, GPIPE_CONV_BN1_G), beta, dz, P, C, &nch,
-                                      x.s));
+  GP_RUN(x, GPIPE_ROLE_BN_BWD, bn_bwd(x.act_kind(), 1, r1, r, x.xs_kind(), a, st1,
+                                      x.wf32(l, GPIPE_CONV_BN1_G), part, sums,
+                                      x.grad(l, GPIPE_CONV_BN1_G), beta, dz, P, C, &nch, x.s));
   // a = conv(x, W1); the residual gradient r0 is added in col2im (in place)
   {
     if (ss && !ss->fork()) return GPIPE_ERR_DEVICE;
-    const gpipe_status st = cwgrad(w, xin, dz, x.grad(l, GPIPE_CONV_W1), beta);
+    const gpipe_status st = cwgrad(w, xin, x_ld, dz, x.grad(l, GPIPE_CONV_W1), beta);
     if (st != GPIPE_OK) return st;
     if (ss && !ss->mark(dz_reader)) return GPIPE_ERR_DEVICE;
   }
   if (p.implicit) {
     // the residual gradient already in r0 gets the convolution's input gradient added
     GP_RUN(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT,
-           cconv(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT, dz, x.flipped(l, 0), r0, 1));
+           cconv(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT, dz, C, x.flipped(l, 0), r0, 1));
     if (dx_out) GP_CHECK(to_bf16(r0, dx_out, P * C, x.s));
   } else {
     GP_RUN(x, GPIPE_ROLE_CONV_DGRAD, cmm(x, GPIPE_ROLE_CONV_DGRAD, int(P), 9 * C, C, dz, C,
@@ -382,13 +436,14 @@ gpipe_status conv_gemm_plan(const gpipe_cell* c, int N, int M, int role, int* ti
   CPlan p;
   if (!make_cplan(c, N, M, 1, &p)) return GPIPE_ERR_INVALID;
   const int P = int(p.P), C = c->C;
+  const int cin = p.split ? 2 * C : C;  // a forward convolution's input channels (blocks > 0)
   int m = 0, n = 0, k = 0;
   switch (role) {
-    case GPIPE_ROLE_CONV_FWD: m = P; n = C; k = 9 * C; break;
+    case GPIPE_ROLE_CONV_FWD: m = P; n = C; k = 9 * cin; break;
     case GPIPE_ROLE_CONV_DGRAD: m = P; n = 9 * C; k = C; break;
     case GPIPE_ROLE_CONV_WGRAD: case GPIPE_ROLE_CONV_WGRAD_IMPLICIT: m = C; n = 9 * C; k = P; break;
-    case GPIPE_ROLE_CONV_FWD_IMPLICIT: case GPIPE_ROLE_CONV_DGRAD_IMPLICIT:
-      m = P; n = C; k = 9 * C; break;
+    case GPIPE_ROLE_CONV_FWD_IMPLICIT: m = P; n = C; k = 9 * cin; break;
+    case GPIPE_ROLE_CONV_DGRAD_IMPLICIT: m = P; n = C; k = 9 * C; break;
     default:
       *tile_m = *tile_n = *splits = 0;
       return GPIPE_OK;
@@ -427,6 +482,15 @@ gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void*
   float* rec = cx.f(p.rec);
   float* msepart = cx.f(p.msepart);
   const size_t rec_mb = size_t(2) * c->L * 2 * c->C;
+  // the weights repeated over split inputs, for every forward and
+  // re-materialized convolution of the call
+  if (p.split && (fwd || remat))
+    for (int l = 0; l < c->L; ++l) {
+      GP_CHECK(conv_dup_weights(cx.wmat(l, GPIPE_CONV_W1), const_cast<void*>(cx.dup(l, 0)), c->C,
+                                stream));
+      GP_CHECK(conv_dup_weights(cx.wmat(l, GPIPE_CONV_W2), const_cast<void*>(cx.dup(l, 1)), c->C,
+                                stream));
+    }
   // the tap-flipped weights of the input gradients, once per backward phase
   if (p.implicit && bwd)
     for (int l = 0; l < c->L; ++l) {

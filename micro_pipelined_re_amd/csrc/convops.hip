@@ -12,10 +12,53 @@
 
 namespace gp {
 
+// ------------------------------------------------------------ activation storage
+// Eight channels c0 .. c0+7 of pixel p of a tensor of C channels, stored as
+// SK_F32 (float [P][C]), SK_BF16 ([P][C] bf16) or SK_SPLIT: a pair of bf16
+// values per element, hi = bf16(v) in channels 0 .. C-1 and lo = bf16(v - hi)
+// in channels C .. 2C-1 of a [P][2C] tensor, v ~ hi + lo to about 2^-17
+// relative (v - hi is exact in float32).  A convolution over the [P][2C]
+// tensor with the weights repeated over both halves is the convolution of
+// hi + lo.
+template <int K>
+__device__ __forceinline__ void ld8k(const void* base, int64_t p, int C, int c0, float* v) {
+  if constexpr (K == SK_F32) {
+    load8<float>(static_cast<const float*>(base) + p * C + c0, v);
+  } else if constexpr (K == SK_BF16) {
+    load8<bf16_t>(static_cast<const bf16_t*>(base) + p * C + c0, v);
+  } else {
+    const bf16_t* b = static_cast<const bf16_t*>(base) + p * 2 * C + c0;
+    float lo[8];
+    load8<bf16_t>(b, v);
+    load8<bf16_t>(b + C, lo);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] += lo[e];
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void st8k(void* base, int64_t p, int C, int c0, const float* v) {
+  if constexpr (K == SK_F32) {
+    store8<float>(static_cast<float*>(base) + p * C + c0, v);
+  } else if constexpr (K == SK_BF16) {
+    store8<bf16_t>(static_cast<bf16_t*>(base) + p * C + c0, v);
+  } else {
+    bf16_t* b = static_cast<bf16_t*>(base) + p * 2 * C + c0;
+    float hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      hi[e] = bf2f(f2bf(v[e]));
+      lo[e] = v[e] - hi[e];
+    }
+    store8<bf16_t>(b, hi);
+    store8<bf16_t>(b + C, lo);
+  }
+}
+
 // ------------------------------------------------------------ im2col / col2im
 template <typename T, typename I>
 __global__ __launch_bounds__(256) void im2col_kernel(const T* __restrict__ x, T* __restrict__ col,
-                                                     int B, int H, int W, int C) {
+                                                     int B, int H, int W, int C, int ldx) {
   // one 8-element chunk per thread, copied as raw 16-byte words (no
   // conversion); I is the index type (32-bit whenever the count fits)
   constexpr int WORDS = sizeof(T) * 8 / 16;
@@ -34,7 +77,7 @@ __global__ __launch_bounds__(256) void im2col_kernel(const T* __restrict__ x, T*
 #pragma unroll
   for (int k = 0; k < WORDS; ++k) v[k] = make_uint4(0, 0, 0, 0);
   if (hs >= 0 && hs < H && ws >= 0 && ws < W) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + ((int64_t(b) * H + hs) * W + ws) * C + cc * 8);
+    const uint4* src = reinterpret_cast<const uint4*>(x + ((int64_t(b) * H + hs) * W + ws) * ldx + cc * 8);
 #pragma unroll
     for (int k = 0; k < WORDS; ++k) v[k] = src[k];
   }
@@ -43,14 +86,15 @@ __global__ __launch_bounds__(256) void im2col_kernel(const T* __restrict__ x, T*
   for (int k = 0; k < WORDS; ++k) dst[k] = v[k];
 }
 
-hipError_t im2col(bool bf16, const void* x, void* col, int B, int H, int W, int C, hipStream_t s) {
+hipError_t im2col(bool bf16, const void* x, int ldx, void* col, int B, int H, int W, int C,
+                  hipStream_t s) {
   const int64_t total = int64_t(B) * H * W * 9 * (C / 8);
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + 255) / 256;
   if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const bool small = total < (int64_t(1) << 31);
 #define GP_IM2COL(T, I) hipLaunchKernelGGL((im2col_kernel<T, I>), dim3(unsigned(blocks)), dim3(256), 0, s, \
-                                           static_cast<const T*>(x), static_cast<T*>(col), B, H, W, C)
+                                           static_cast<const T*>(x), static_cast<T*>(col), B, H, W, C, ldx)
   if (bf16) {
     if (small) GP_IM2COL(bf16_t, uint32_t);
     else GP_IM2COL(bf16_t, uint64_t);
@@ -251,61 +295,78 @@ hipError_t bn_stats(bool bf16, const void* x, int64_t rows, int C, float eps, fl
 }
 
 // ------------------------------------------------------------ BatchNorm apply
-// y = gamma * (a - mean) * rstd + beta;  MODE 0: out = max(y, 0);  MODE 1: out = res + y.
-template <typename T, int MODE>
-__global__ __launch_bounds__(256) void bn_apply_kernel(const T* __restrict__ a,
+// y = gamma * (a - mean) * rstd + beta from the float32 input a;  MODE 0:
+// out = max(y, 0);  MODE 1: out = res + y.  res and out are stored as KR / KO
+// (they may be the same tensor: each thread reads its elements of res before
+// it writes them).
+template <int MODE, int KR, int KO>
+__global__ __launch_bounds__(256) void bn_apply_kernel(const float* __restrict__ a,
                                                        const float* __restrict__ stats,
                                                        const float* __restrict__ gamma,
                                                        const float* __restrict__ beta,
-                                                       const T* __restrict__ res,
-                                                       T* __restrict__ out, int64_t rows, int C) {
+                                                       const void* res, void* out, int64_t rows,
+                                                       int C) {
   const int cc8 = C >> 3;
   const int64_t total = rows * cc8;
   const int64_t stride = int64_t(gridDim.x) * 256;
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += stride) {
     const int c0 = int(i % cc8) * 8;
-    const int64_t off = (i / cc8) * C + c0;
-    float v[8], o[8];
-    load8<T>(a + off, v);
-    float rv[8];
-    if (MODE == 1) load8<T>(res + off, rv);
+    const int64_t p = i / cc8;
+    float v[8], o[8], rv[8];
+    load8<float>(a + p * C + c0, v);
+    if constexpr (MODE == 1) ld8k<KR>(res, p, C, c0, rv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int c = c0 + e;
       const float y = gamma[c] * (v[e] - stats[c]) * stats[C + c] + beta[c];
       o[e] = MODE == 0 ? fmaxf(y, 0.f) : rv[e] + y;
     }
-    store8<T>(out + off, o);
+    st8k<KO>(out, p, C, c0, o);
   }
 }
 
-hipError_t bn_apply(bool bf16, int mode, const void* a, const float* stats, const float* gamma,
-                    const float* beta, const void* res, void* out, int64_t rows, int C,
-                    hipStream_t s) {
+hipError_t bn_apply(int mode, const float* a, const float* stats, const float* gamma,
+                    const float* beta, const void* res, int res_kind, void* out, int out_kind,
+                    int64_t rows, int C, hipStream_t s) {
   const int64_t total = rows * (C / 8);
   if (total == 0) return hipSuccess;
   const int64_t want = (total + 255) / 256;
   const int blocks = int(want < 16384 ? want : 16384);
-#define GP_BN_APPLY(T, M)                                                                      \
-  hipLaunchKernelGGL((bn_apply_kernel<T, M>), dim3(blocks), dim3(256), 0, s,                  \
-                     static_cast<const T*>(a), stats, gamma, beta, static_cast<const T*>(res), \
-                     static_cast<T*>(out), rows, C)
-  if (bf16) {
-    if (mode == 0) GP_BN_APPLY(bf16_t, 0); else GP_BN_APPLY(bf16_t, 1);
+#define GP_BN_APPLY(M, KR, KO)                                                                 \
+  hipLaunchKernelGGL((bn_apply_kernel<M, KR, KO>), dim3(blocks), dim3(256), 0, s, a, stats,   \
+                     gamma, beta, res, out, rows, C)
+  if (mode == 0) {
+    if (out_kind == SK_F32) GP_BN_APPLY(0, SK_F32, SK_F32);
+    else if (out_kind == SK_SPLIT) GP_BN_APPLY(0, SK_F32, SK_SPLIT);
+    else return hipErrorInvalidValue;
   } else {
-    if (mode == 0) GP_BN_APPLY(float, 0); else GP_BN_APPLY(float, 1);
+    if (res_kind == SK_F32 && out_kind == SK_F32) GP_BN_APPLY(1, SK_F32, SK_F32);
+    else if (res_kind == SK_BF16 && out_kind == SK_SPLIT) GP_BN_APPLY(1, SK_BF16, SK_SPLIT);
+    else if (res_kind == SK_SPLIT && out_kind == SK_SPLIT) GP_BN_APPLY(1, SK_SPLIT, SK_SPLIT);
+    else if (res_kind == SK_SPLIT && out_kind == SK_BF16) GP_BN_APPLY(1, SK_SPLIT, SK_BF16);
+    else if (res_kind == SK_BF16 && out_kind == SK_BF16) GP_BN_APPLY(1, SK_BF16, SK_BF16);
+    else return hipErrorInvalidValue;
   }
 #undef GP_BN_APPLY
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ BatchNorm backward
-// dy = dy_src (MASK: times [r > 0], r the ReLU output), xhat = (a - mean) * rstd.
+// dy = dy_src (MASK: times [r > 0], r the ReLU output stored as KR; of a split
+// r the hi half decides), xhat = (a - mean) * rstd with a float32.
 // part[chunk][0:C] = sum dy*xhat, part[chunk][C:2C] = sum dy (gamma, beta order).
-template <typename T, int MASK>
+template <int KR>
+__device__ __forceinline__ void relu_mask8(const void* r, int64_t row, int C, int c0, float* g) {
+  float rv[8];
+  ld8k<KR == SK_SPLIT ? SK_BF16 : KR>(r, row * (KR == SK_SPLIT ? 2 : 1), C, c0, rv);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) g[e] = rv[e] > 0.f ? g[e] : 0.f;
+}
+
+template <int KR, int MASK>
 __global__ __launch_bounds__(256) void bn_bwd_partial_kernel(const float* __restrict__ dy_src,
-                                                             const T* __restrict__ r,
-                                                             const T* __restrict__ a,
+                                                             const void* __restrict__ r,
+                                                             const float* __restrict__ a,
                                                              const float* __restrict__ stats,
                                                              float* __restrict__ part,
                                                              int64_t rows, int C) {
@@ -322,13 +383,8 @@ __global__ __launch_bounds__(256) void bn_bwd_partial_kernel(const float* __rest
     for (int64_t row = r0 + rg; row < r1; row += 8) {
       float g[8], av[8];
       load8<float>(dy_src + row * C + c0, g);
-      load8<T>(a + row * C + c0, av);
-      if (MASK) {
-        float rv[8];
-        load8<T>(r + row * C + c0, rv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) g[e] = rv[e] > 0.f ? g[e] : 0.f;
-      }
+      load8<float>(a + row * C + c0, av);
+      if (MASK) relu_mask8<KR>(r, row, C, c0, g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         sg[e] += g[e] * (av[e] - mu[e]) * rs[e];
@@ -355,31 +411,28 @@ __global__ __launch_bounds__(256) void bn_bwd_partial_kernel(const float* __rest
   }
 }
 
-// da = gamma * rstd * (dy - sum(dy)/n - xhat * sum(dy*xhat)/n);  sums = [2][C] as in the partials.
-template <typename T, int MASK>
+// da (stored as KD) = gamma * rstd * (dy - sum(dy)/n - xhat * sum(dy*xhat)/n);
+// sums = [2][C] as in the partials.
+template <int KD, int KR, int MASK>
 __global__ __launch_bounds__(256) void bn_bwd_apply_kernel(const float* __restrict__ dy_src,
-                                                           const T* __restrict__ r,
-                                                           const T* __restrict__ a,
+                                                           const void* __restrict__ r,
+                                                           const float* __restrict__ a,
                                                            const float* __restrict__ stats,
                                                            const float* __restrict__ gamma,
                                                            const float* __restrict__ sums,
-                                                           T* __restrict__ da, int64_t rows, int C,
-                                                           float inv_n) {
+                                                           void* __restrict__ da, int64_t rows,
+                                                           int C, float inv_n) {
   const int cc8 = C >> 3;
   const int64_t total = rows * cc8;
   const int64_t stride = int64_t(gridDim.x) * 256;
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += stride) {
     const int c0 = int(i % cc8) * 8;
-    const int64_t off = (i / cc8) * C + c0;
+    const int64_t row = i / cc8;
+    const int64_t off = row * C + c0;
     float g[8], av[8], o[8];
     load8<float>(dy_src + off, g);
-    load8<T>(a + off, av);
-    if (MASK) {
-      float rv[8];
-      load8<T>(r + off, rv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) g[e] = rv[e] > 0.f ? g[e] : 0.f;
-    }
+    load8<float>(a + off, av);
+    if (MASK) relu_mask8<KR>(r, row, C, c0, g);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int c = c0 + e;
@@ -387,24 +440,25 @@ __global__ __launch_bounds__(256) void bn_bwd_apply_kernel(const float* __restri
       const float xh = (av[e] - stats[c]) * rs;
       o[e] = gamma[c] * rs * (g[e] - sums[C + c] * inv_n - xh * sums[c] * inv_n);
     }
-    store8<T>(da + off, o);
+    st8k<KD>(da, row, C, c0, o);
   }
 }
 
-hipError_t bn_bwd(bool bf16, int mask, const float* dy_src, const void* r, const void* a,
-                  const float* stats, const float* gamma, float* part, float* sums, float* grad,
-                  int grad_beta, void* da, int64_t rows, int C, int* nchunk, hipStream_t s) {
+hipError_t bn_bwd(int da_kind, int mask, const float* dy_src, const void* r, int r_kind,
+                  const float* a, const float* stats, const float* gamma, float* part, float* sums,
+                  float* grad, int grad_beta, void* da, int64_t rows, int C, int* nchunk,
+                  hipStream_t s) {
   *nchunk = bn_chunks(rows);
   if (rows == 0 || C == 0) return hipSuccess;
+  if ((da_kind != SK_F32 && da_kind != SK_BF16) || (mask && r_kind != SK_F32 && r_kind != SK_SPLIT))
+    return hipErrorInvalidValue;
   dim3 grid((C + 255) / 256, *nchunk);
-#define GP_BN_BWD_P(T, MK)                                                                    \
-  hipLaunchKernelGGL((bn_bwd_partial_kernel<T, MK>), grid, dim3(256), 0, s, dy_src,          \
-                     static_cast<const T*>(r), static_cast<const T*>(a), stats, part, rows, C)
-  if (bf16) {
-    if (mask) GP_BN_BWD_P(bf16_t, 1); else GP_BN_BWD_P(bf16_t, 0);
-  } else {
-    if (mask) GP_BN_BWD_P(float, 1); else GP_BN_BWD_P(float, 0);
-  }
+#define GP_BN_BWD_P(KR, MK)                                                                   \
+  hipLaunchKernelGGL((bn_bwd_partial_kernel<KR, MK>), grid, dim3(256), 0, s, dy_src, r, a,   \
+                     stats, part, rows, C)
+  if (!mask) GP_BN_BWD_P(SK_F32, 0);
+  else if (r_kind == SK_F32) GP_BN_BWD_P(SK_F32, 1);
+  else GP_BN_BWD_P(SK_SPLIT, 1);
 #undef GP_BN_BWD_P
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -414,14 +468,17 @@ hipError_t bn_bwd(bool bf16, int mask, const float* dy_src, const void* r, const
   const int64_t want = (total + 255) / 256;
   const int blocks = int(want < 16384 ? want : 16384);
   const float inv_n = float(1.0 / double(rows));
-#define GP_BN_BWD_A(T, MK)                                                                   \
-  hipLaunchKernelGGL((bn_bwd_apply_kernel<T, MK>), dim3(blocks), dim3(256), 0, s, dy_src,   \
-                     static_cast<const T*>(r), static_cast<const T*>(a), stats, gamma, sums, \
-                     static_cast<T*>(da), rows, C, inv_n)
-  if (bf16) {
-    if (mask) GP_BN_BWD_A(bf16_t, 1); else GP_BN_BWD_A(bf16_t, 0);
+#define GP_BN_BWD_A(KD, KR, MK)                                                              \
+  hipLaunchKernelGGL((bn_bwd_apply_kernel<KD, KR, MK>), dim3(blocks), dim3(256), 0, s, dy_src, \
+                     r, a, stats, gamma, sums, da, rows, C, inv_n)
+  if (da_kind == SK_F32) {
+    if (!mask) GP_BN_BWD_A(SK_F32, SK_F32, 0);
+    else if (r_kind == SK_F32) GP_BN_BWD_A(SK_F32, SK_F32, 1);
+    else GP_BN_BWD_A(SK_F32, SK_SPLIT, 1);
   } else {
-    if (mask) GP_BN_BWD_A(float, 1); else GP_BN_BWD_A(float, 0);
+    if (!mask) GP_BN_BWD_A(SK_BF16, SK_F32, 0);
+    else if (r_kind == SK_F32) GP_BN_BWD_A(SK_BF16, SK_F32, 1);
+    else GP_BN_BWD_A(SK_BF16, SK_SPLIT, 1);
   }
 #undef GP_BN_BWD_A
   return hipGetLastError();
@@ -447,6 +504,33 @@ hipError_t conv_flip_weights(const void* src, void* dst, int C, hipStream_t s) {
   const int64_t want = (n + 255) / 256;
   const int blocks = int(want < 4096 ? want : 4096);
   hipLaunchKernelGGL(conv_flip_kernel, dim3(blocks), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(src), static_cast<bf16_t*>(dst), C);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ repeated weights
+// dst[o][t][c'] = src[o][t][c' mod C], c' < 2C: the weights of a convolution
+// over a split [P][2C] tensor (its hi and lo halves meet the same weights).
+__global__ __launch_bounds__(256) void conv_dup_kernel(const bf16_t* __restrict__ src,
+                                                       bf16_t* __restrict__ dst, int C) {
+  const int64_t n = int64_t(9) * C * C;  // in 8-element chunks of the source: n / 8
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n / 8; i += int64_t(gridDim.x) * 256) {
+    const int64_t e = i * 8;
+    const int64_t ot = e / C;  // o * 9 + t
+    const int c = int(e - ot * C);
+    const uint4 v = *reinterpret_cast<const uint4*>(src + e);
+    bf16_t* d = dst + ot * 2 * C + c;
+    *reinterpret_cast<uint4*>(d) = v;
+    *reinterpret_cast<uint4*>(d + C) = v;
+  }
+}
+
+hipError_t conv_dup_weights(const void* src, void* dst, int C, hipStream_t s) {
+  const int64_t n = int64_t(9) * C * C / 8;
+  if (n == 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  const int blocks = int(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(conv_dup_kernel, dim3(blocks), dim3(256), 0, s,
                      static_cast<const bf16_t*>(src), static_cast<bf16_t*>(dst), C);
   return hipGetLastError();
 }

@@ -65,7 +65,8 @@ bool dma_ok(int role, const GemmParams& g) {
   // 2^21, element offsets within 32 bits
   if (role == GPIPE_ROLE_CONV_WGRAD_IMPLICIT &&
       (g.conv_c % 8 || g.N != 9 * g.conv_c || g.K >= (1 << 21) || g.conv_h < 1 || g.conv_w < 1 ||
-       g.K % (g.conv_h * g.conv_w) || int64_t(g.K + 64) * g.conv_c >= (int64_t(1) << 31)))
+       g.K % (g.conv_h * g.conv_w) || (g.conv_ld && (g.conv_ld < g.conv_c || g.conv_ld % 8)) ||
+       int64_t(g.K + 64) * (g.conv_ld ? g.conv_ld : g.conv_c) >= (int64_t(1) << 31)))
     return false;
   if (a_mn && g.M % 8) return false;
   if (b_mn && g.N % 8) return false;

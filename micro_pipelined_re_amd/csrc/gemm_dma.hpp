@@ -221,7 +221,8 @@ struct DmaConvMnOperand : DmaOperand<ROWS, BK, LAY_MN> {
     H = g.conv_h;
     W = g.conv_w;
     const int C = g.conv_c;
-    step = BK * C;
+    const int LD = g.conv_ld ? g.conv_ld : C;  // the image's pixel stride
+    step = BK * LD;
     dh64 = (BK / W) % H;
     dw64 = BK % W;
     const float inv_w = 1.0f / float(W), inv_h = 1.0f / float(H);
@@ -241,7 +242,7 @@ struct DmaConvMnOperand : DmaOperand<ROWS, BK, LAY_MN> {
       const int ph = int((float(pw) + 0.5f) * inv_h);  // (p / W) / H
       w[q] = p - pw * W;
       h[q] = pw - ph * H;
-      src[q] = (p + dh * W + dw) * C + (gn - tap * C);
+      src[q] = (p + dh * W + dw) * LD + (gn - tap * C);
       hlo[q] = dh < 0 ? 1 : 0;
       wlo[q] = dw < 0 ? 1 : 0;
       hcnt[q] = unsigned(H - (dh != 0 ? 1 : 0));

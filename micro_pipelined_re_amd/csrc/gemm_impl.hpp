@@ -574,13 +574,14 @@ GP_SPEC(GPIPE_ROLE_DK, LAY_MN, LAY_MN, EPI_STORE)
 GP_SPEC(GPIPE_ROLE_QKV_DGRAD, LAY_K, LAY_MN, EPI_STORE_F32)
 GP_SPEC(GPIPE_ROLE_QKV_WGRAD, LAY_MN, LAY_MN, EPI_ACC_F32)
 // 3x3 convolutions as GEMMs over the im2col matrix [P, 9C]:
-//   forward  a = col W^T;  input gradient dcol = da W (f32);  weight gradient G (+)= da^T col
-GP_SPEC(GPIPE_ROLE_CONV_FWD, LAY_K, LAY_K, EPI_STORE)
+//   forward  a = col W^T (f32: the BatchNorm input);  input gradient dcol = da W (f32);
+//   weight gradient G (+)= da^T col
+GP_SPEC(GPIPE_ROLE_CONV_FWD, LAY_K, LAY_K, EPI_STORE_F32)
 GP_SPEC(GPIPE_ROLE_CONV_DGRAD, LAY_K, LAY_MN, EPI_STORE_F32)
 GP_SPEC(GPIPE_ROLE_CONV_WGRAD, LAY_MN, LAY_MN, EPI_ACC_F32)
 // implicit GEMM: a = im2col(x) W^T with the column matrix gathered by the loads;
 // the input gradient (+)= im2col(dz) Wflip^T, Wflip the tap-flipped transposed weights
-GP_SPEC(GPIPE_ROLE_CONV_FWD_IMPLICIT, LAY_CONV, LAY_K, EPI_STORE)
+GP_SPEC(GPIPE_ROLE_CONV_FWD_IMPLICIT, LAY_CONV, LAY_K, EPI_STORE_F32)
 GP_SPEC(GPIPE_ROLE_CONV_DGRAD_IMPLICIT, LAY_CONV, LAY_K, EPI_ACC_F32)
 // and the weight gradient G (+)= da^T im2col(x), the column matrix gathered along k
 GP_SPEC(GPIPE_ROLE_CONV_WGRAD_IMPLICIT, LAY_MN, LAY_CONV_MN, EPI_ACC_F32)

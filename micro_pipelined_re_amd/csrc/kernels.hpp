@@ -47,6 +47,7 @@ struct GemmParams {
   float* P;     // split-K partials [splits][M][N] (f32), required when the plan splits
   int kchunk;   // split-K: k extent of one split (set by gemm())
   int conv_h, conv_w, conv_c;  // image geometry of a LAY_CONV operand
+  int conv_ld;  // pixel stride of a LAY_CONV_MN image in elements (0: conv_c)
   // Optional (weight-gradient roles, where gemm_rowsum_parts() > 0): partial
   // sums of A over k, rowsum[t * M + m] for tile column t, written (beta = 0)
   // or added (beta = 1) like C; summed over t they
@@ -142,8 +143,13 @@ hipError_t rmsprop(float* w, const float* g, float* ms, void* w_lowp, int64_t n,
                    float decay, float eps, hipStream_t s);
 
 // ---------------------------------------------------------------- conv cell
-// col [B*H*W, 9*C] from x [B, H, W, C] (pad 1); column (kh*3 + kw)*C + c.
-hipError_t im2col(bool bf16, const void* x, void* col, int B, int H, int W, int C, hipStream_t s);
+// Storage of a conv-cell activation: float32 [P][C], bf16 [P][C], or a split
+// pair of bf16 [P][2C] (hi = bf16(v) in channels 0 .. C-1, lo = bf16(v - hi)
+// in C .. 2C-1; v ~ hi + lo to about 2^-17 relative).
+enum { SK_F32 = 0, SK_BF16 = 1, SK_SPLIT = 2 };
+// col [B*H*W, 9*C] from x [B, H, W, ldx] (its first C channels; pad 1); column (kh*3 + kw)*C + c.
+hipError_t im2col(bool bf16, const void* x, int ldx, void* col, int B, int H, int W, int C,
+                  hipStream_t s);
 // dx = res (optional) + adjoint of im2col applied to dcol (f32); writes f32 and (optional) act.
 hipError_t col2im(bool bf16, const float* dcol, const float* res, float* dx_f32, void* dx_act,
                   int B, int H, int W, int C, hipStream_t s);
@@ -151,19 +157,25 @@ int bn_chunks(int64_t rows);
 // Per-channel statistics over `rows` rows: stats = (mean[C], rstd[C]); rec (optional) = (mean, biased var).
 hipError_t bn_stats(bool bf16, const void* x, int64_t rows, int C, float eps, float* part,
                     float* stats, float* rec, hipStream_t s);
-// mode 0: out = relu(bn(a));  mode 1: out = res + bn(a).
-hipError_t bn_apply(bool bf16, int mode, const void* a, const float* stats, const float* gamma,
-                    const float* beta, const void* res, void* out, int64_t rows, int C,
-                    hipStream_t s);
-// Backward of bn (mask: dy is multiplied by [r > 0]); sums = (sum dy*xhat, sum dy) of this
-// batch (part: [chunks][2C] scratch), also stored (grad_beta = 0) or added into grad
-// [2C] (the gain and shift gradients); da = input gradient (act).
-hipError_t bn_bwd(bool bf16, int mask, const float* dy_src, const void* r, const void* a,
-                  const float* stats, const float* gamma, float* part, float* sums, float* grad,
-                  int grad_beta, void* da, int64_t rows, int C, int* nchunk, hipStream_t s);
+// From float32 a:  mode 0: out = relu(bn(a));  mode 1: out = res + bn(a); res and out
+// stored as the given SK_* kinds (mode 0: out f32 or split; mode 1: res/out f32/f32,
+// bf16/split, split/split, split/bf16 or bf16/bf16; res may be out).
+hipError_t bn_apply(int mode, const float* a, const float* stats, const float* gamma,
+                    const float* beta, const void* res, int res_kind, void* out, int out_kind,
+                    int64_t rows, int C, hipStream_t s);
+// Backward of bn over float32 a (mask: dy is multiplied by [r > 0], r stored f32 or split);
+// sums = (sum dy*xhat, sum dy) of this batch (part: [chunks][2C] scratch), also stored
+// (grad_beta = 0) or added into grad [2C] (the gain and shift gradients); da = input gradient
+// stored as da_kind (f32 or bf16).
+hipError_t bn_bwd(int da_kind, int mask, const float* dy_src, const void* r, int r_kind,
+                  const float* a, const float* stats, const float* gamma, float* part, float* sums,
+                  float* grad, int grad_beta, void* da, int64_t rows, int C, int* nchunk,
+                  hipStream_t s);
 // Moving averages from the M micro-batches' recorded moments.
 hipError_t bn_running(const float* rec, int M, int nbn, int C, int64_t n_total, float momentum,
                       float* running, hipStream_t s);
+// [C][9][2C] weights repeating [C][9][C] over both halves of a split input (bf16).
+hipError_t conv_dup_weights(const void* src, void* dst, int C, hipStream_t s);
 
 // ---------------------------------------------------------------- fused attention
 // bf16 cells with head dim 64 or 128.  qkv [B*S][3D], ctx/dctx [B*S][D],

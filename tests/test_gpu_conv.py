@@ -3,19 +3,17 @@
 Relative L2 per tensor for y, dx, every gradient and the moving averages;
 on the whole vector for the updated weights and RMSProp state.
 
-fp32 mode: <= 1e-4 for everything at the small shapes.
+  * fp32 mode: <= 1e-4 at the small shapes;
+  * bf16 mode (bf16 MFMA operands, float32 accumulation): <= 2e-2 at every
+    shape.  The cell's gradients are the small remainder of near-
+    cancellations, so the bf16 path keeps its forward activations exact to
+    about 2^-17 (float32 BatchNorm inputs, split hi + lo bf16 convolution
+    operands) and rounds only the backward's operands to bf16
+    (tests/conv_bf16_model.py measures why on the oracle).
 
-The gradients of this cell are ill-conditioned: micro-batch BatchNorm over
-residual blocks makes them the small remainder of near-cancellations, so a
-tiny perturbation of the arithmetic moves them by much more
-(tests/conv_bf16_model.py).  Where that matters one bar for dx, the
-gradients and the update is derived from the oracle itself on the same
-inputs: max(stated bar, 1.5 x the largest deviation among them from the
-float64 oracle of the same definitions evaluated in the path's precision):
-  * fp32 at the full shape: the oracle evaluated in float32;
-  * bf16: the oracle with the bf16 storage policy (conv_bf16_model).
-y, the loss and the moving averages (forward quantities) keep the stated
-bar (1e-4 fp32, 2e-2 bf16) everywhere.
+At the full 256-channel shape the fp32 bar is the conditioning floor of
+test_gpu_conv_full.py: the oracle's own definitions evaluated in float32 move
+dx and the gradients by ~2e-3 there, so no float32 evaluation meets 1e-4.
 """
 import numpy as np
 import pytest
@@ -23,7 +21,6 @@ import pytest
 from micro_pipelined_re_amd import configs, gpipe, inputs
 from oracle import conv_cell as cc
 from oracle.transformer_cell import rmsprop
-from tests.conv_bf16_model import model_step
 from tests.gpu_common import rel_l2, say, to_host
 
 pytestmark = pytest.mark.gpu
@@ -136,8 +133,9 @@ def compare_conv(gpu, ref, tol):
     return report, over(report, tol)
 
 
-def derived_tol(dev, bar):
-    """bar for the forward quantities; max(bar, 1.5 x the largest backward deviation) for the rest."""
+def conditioning_tol(dev, bar):
+    """bar for the forward quantities; max(bar, 1.5 x the largest backward deviation
+    of the float32-evaluated oracle) for the rest."""
     worst = max(v for k, v in dev.items() if k not in FORWARD_KEYS)
     back = max(bar, 1.5 * worst)
     say(f"[tol] forward {bar:.1e}, backward {back:.2e}")
@@ -146,17 +144,13 @@ def derived_tol(dev, bar):
     return tol
 
 
-def check_derived(cfg, params, x, t, M, gpu, ref):
-    """gpu against the float64 oracle with the derived bar of the module docstring."""
-    if cfg.precision == "fp32":
-        same = oracle_conv_step(cfg, params, x, t, M, dtype=np.float32)
-        bar, label = FP32_TOL, "oracle in float32"
-    else:
-        same = add_update(cfg, params, model_step(params, x, t, M, cfg.bn_eps))
-        bar, label = BF16_TOL, "bf16 policy"
-    dev = conv_report(same, ref, f"{label} vs oracle")
+def check_fp32_conditioning(cfg, params, x, t, M, gpu, ref):
+    """An fp32 run against the float64 oracle, dx / gradients / update bounded by the
+    conditioning floor: 1.5 x the deviation of the oracle evaluated in float32."""
+    same = oracle_conv_step(cfg, params, x, t, M, dtype=np.float32)
+    dev = conv_report(same, ref, "oracle in float32 vs oracle")
     report = conv_report(gpu, ref, "gpu vs oracle")
-    bad = over(report, derived_tol(dev, bar))
+    bad = over(report, conditioning_tol(dev, FP32_TOL))
     assert not bad, bad
     return report
 
@@ -168,11 +162,8 @@ def check_conv(cfg, N=None, M=None, remat=True):
     x, t = inputs.conv_cell_data(cfg, batch=N)
     gpu = run_conv_gpu(cfg, params, x, t, N, M, remat=remat)
     ref = oracle_conv_step(cfg, params, x, t, M)
-    if cfg.precision == "fp32":
-        _, bad = compare_conv(gpu, ref, FP32_TOL)
-        assert not bad, bad
-    else:
-        check_derived(cfg, params, x, t, M, gpu, ref)
+    _, bad = compare_conv(gpu, ref, FP32_TOL if cfg.precision == "fp32" else BF16_TOL)
+    assert not bad, bad
     return gpu, ref
 
 

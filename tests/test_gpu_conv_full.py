@@ -1,10 +1,11 @@
 """The conv cell at its full shape: 8 blocks of 256 channels on 32 x 32 images.
 
 * One micro-batch (N = 16, M = 1) runs every kernel at exactly the launch
-  shapes of the full workload's micro-batches (16384 pixels, K = 2304); the
-  oracle checks all of it, with the derived bar of test_gpu_conv for dx, the
-  gradients and the update (at this shape the oracle evaluated in float32
-  itself deviates from float64 by about 2e-3).
+  shapes of the full workload's micro-batches (16384 pixels, K = 2304, 4608
+  for the split forward operands); the oracle checks all of it: bf16 at the
+  flat 2e-2; fp32 with its conditioning floor for dx, the gradients and the
+  update (at this shape the oracle evaluated in float32 itself deviates from
+  float64 by about 2e-3, from the cancellations in the BatchNorm backward).
 * The full step (N = 256, M = 16, the timed workload) is checked on what the
   oracle can compute piecewise: the outputs of sampled micro-batches (each
   normalised with its own statistics, so a micro-batch is the unit), block
@@ -19,8 +20,8 @@ import pytest
 from micro_pipelined_re_amd import configs, inputs
 from oracle import conv_cell as cc
 from tests.gpu_common import rel_l2, say
-from tests.test_gpu_conv import (BF16_TOL, _concat, check_derived, oracle_conv_step,
-                                 run_conv_gpu)
+from tests.test_gpu_conv import (BF16_TOL, _concat, check_fp32_conditioning, compare_conv,
+                                 oracle_conv_step, run_conv_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +42,7 @@ def test_conv_full_shape_fp32_one_micro_batch():
     x, t = inputs.conv_cell_data(cfg)
     gpu = run_conv_gpu(cfg, params, x, t, 16, 1)
     ref = oracle_conv_step(cfg, params, x, t, 1)
-    check_derived(cfg, params, x, t, 1, gpu, ref)
+    check_fp32_conditioning(cfg, params, x, t, 1, gpu, ref)
 
 
 def test_conv_full_shape_bf16_one_micro_batch():
@@ -50,7 +51,8 @@ def test_conv_full_shape_bf16_one_micro_batch():
     x, t = inputs.conv_cell_data(cfg)
     gpu = run_conv_gpu(cfg, params, x, t, 16, 1)
     ref = oracle_conv_step(cfg, params, x, t, 1)
-    check_derived(cfg, params, x, t, 1, gpu, ref)
+    _, bad = compare_conv(gpu, ref, BF16_TOL)
+    assert not bad, bad
 
 
 def test_conv_full_workload_sampled():
