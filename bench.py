@@ -37,19 +37,18 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
-# The Transformer cell's step runs several streams: in the forward phase even
-# and odd micro-batches, in the backward phase the weight-gradient GEMMs beside
-# the input-gradient chain and the next micro-batch's re-materialization on a
-# third stream (the launches of the forward phase and of those
-# re-materializations are not role-timed), so the times of every backward-
-# phase launch include time shared with other kernels: they are not per-kernel
-# figures.  Micro-batch 0 re-materializes on the caller's stream alone: the
-# dominant kernel and mfma_util_gemm come from those launches of the forward
-# roles.
-SECOND_STREAM_ROLES = ("ffn2_wgrad", "ffn1_wgrad", "out_wgrad", "qkv_wgrad")
-CONV_FORWARD_ROLES = ("conv_fwd_implicit", "bn_stats", "bn_apply")
-ALONE_ROLES = ("ln1_fwd", "qkv_fwd", "scores_fwd", "softmax_fwd", "pv_fwd", "attn_fwd", "out_fwd",
-               "ln2_fwd", "ffn1_fwd", "ffn2_fwd", "mse")
+# Roles of the Transformer cell's step by how many micro-batch passes of one
+# layer they make per step: the forward roles run in the forward phase and in
+# the re-materialization (2 L M passes), the backward roles once (L M).  The
+# step runs several streams (the forward phase's lanes, the weight gradients
+# beside the input-gradient chain, the next micro-batch's re-materialization),
+# so a launch's timed span is its time in the step, sharing the CUs with the
+# other streams' kernels.
+FWD_ROLES = ("ln1_fwd", "qkv_fwd", "scores_fwd", "softmax_fwd", "pv_fwd", "attn_fwd", "out_fwd",
+             "ln2_fwd", "ffn1_fwd", "ffn2_fwd")
+BWD_ROLES = ("ffn2_dgrad", "ffn2_wgrad", "ffn1_dgrad", "ffn1_wgrad", "ln2_bwd", "out_dgrad",
+             "out_wgrad", "dp", "dv", "softmax_bwd", "dq", "dk", "attn_dq", "qkv_dgrad",
+             "qkv_wgrad", "ln1_bwd")
 
 
 def log(*a):
@@ -65,6 +64,22 @@ GEMM_SOURCES = ("common.hpp", "kernels.hpp", "gemm_impl.hpp", "gemm_dma.hpp", "g
                 "gemm_fwd.hip", "gemm_dgrad.hip", "gemm_wgrad.hip")
 
 
+def gemm_source_digest():
+    """sha256 of the GEMM sources with comments and blank lines removed (edits of
+    comments alone keep the measured figures)."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "micro_pipelined_re_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode())
+    return h.hexdigest()
+
+
 def measured_traffic(role):
     """(fetch_bytes, write_bytes) per launch of `role`, or None if not measured for these sources."""
     import hashlib
@@ -73,12 +88,8 @@ def measured_traffic(role):
         text = open(TRAFFIC_FILE).read()
     except OSError:
         return None
-    h = hashlib.sha256()
-    for f in GEMM_SOURCES:
-        with open(os.path.join(ROOT, "micro_pipelined_re_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
     m = re.search(r"gemm_source_digest: ([0-9a-f]+)", text)
-    if not m or m.group(1) != h.hexdigest():
+    if not m or m.group(1) != gemm_source_digest():
         return None
     m = re.search(rf"traffic {re.escape(role)}: fetch_bytes=(\d+) write_bytes=(\d+)", text)
     return (int(m.group(1)), int(m.group(2))) if m else None
@@ -86,7 +97,8 @@ def measured_traffic(role):
 
 # ------------------------------------------------------------------ algorithmic work per role
 def role_work(cfg, n, m):
-    """Per launch: ('mfma', flops) for the contractions, ('hbm', bytes) for the rest."""
+    """Per micro-batch pass of one layer: ('mfma', flops) for the contractions,
+    ('hbm', bytes) for the rest (rmsprop: the whole update)."""
     b = n // m
     S, D, H, F = cfg.seq, cfg.d_model, cfg.heads, cfg.d_ff
     dh = D // H
@@ -103,6 +115,8 @@ def role_work(cfg, n, m):
         "ffn1_dgrad": ("mfma", 2 * T * D * F), "ffn1_wgrad": ("mfma", 2 * F * D * T),
         "out_dgrad": ("mfma", 2 * T * D * D), "out_wgrad": ("mfma", 2 * D * D * T),
         "dp": ("mfma", attn), "dv": ("mfma", attn), "dq": ("mfma", attn), "dk": ("mfma", attn),
+        # fused attention: the forward's two products, the backward's four (dP, dV, dQ, dK)
+        "attn_fwd": ("mfma", 2 * attn), "attn_dq": ("mfma", 4 * attn),
         "qkv_dgrad": ("mfma", 2 * T * D * 3 * D), "qkv_wgrad": ("mfma", 2 * 3 * D * D * T),
         # LayerNorm forward: read x, write y (act) and (mean, rstd)
         "ln1_fwd": ("hbm", 2 * T * D * eb + 8 * T), "ln2_fwd": ("hbm", 2 * T * D * eb + 8 * T),
@@ -132,7 +146,11 @@ def step_mfma_flops(cfg, n, m):
 
 
 def conv_role_work(cfg, n, m):
-    """conv cell: ('mfma', flops) or ('hbm', bytes) per launch."""
+    """conv cell, per micro-batch pass of one block's convolution or BatchNorm:
+    ('mfma', flops) or ('hbm', bytes).  The convolutions' algorithmic work is
+    2 P C 9C whatever the operand storage (a bf16 cell's split forward operands
+    double the forward's MFMA work, not its algorithmic work).  Activations
+    are float32 or split bf16 pairs (4 B per element) in the forward."""
     P = (n // m) * cfg.height * cfg.width          # pixels per micro-batch
     C = cfg.channels
     eb = 2 if cfg.precision == "bf16" else 4
@@ -141,24 +159,48 @@ def conv_role_work(cfg, n, m):
         "conv_fwd": ("mfma", g), "conv_dgrad": ("mfma", g), "conv_wgrad": ("mfma", g),
         "conv_fwd_implicit": ("mfma", g), "conv_dgrad_implicit": ("mfma", g),
         "conv_wgrad_implicit": ("mfma", g),
-        # im2col: read the image once, write the nine shifted copies
-        "im2col": ("hbm", P * C * eb * 10),
-        # col2im: read the f32 column gradient (and the f32 residual), write f32 (+ act)
-        "col2im": ("hbm", P * C * (36 + 4 + 4)),
-        # statistics: two passes over the input
-        "bn_stats": ("hbm", 2 * P * C * eb),
-        # apply: read the input (+ the residual half the time), write the output
-        "bn_apply": ("hbm", P * C * eb * 2.5),
-        # backward: two passes over dy (f32) and the input (+ the ReLU output), write da
-        "bn_bwd": ("hbm", P * C * (2 * 4 + 2 * eb + eb + eb)),
+        # statistics: one pass over the float32 input
+        "bn_stats": ("hbm", P * C * 4),
+        # apply: read the input, the residual half the time, write the output
+        "bn_apply": ("hbm", P * C * 10),
+        # backward: two passes over dy and the input (+ the ReLU mask), write da
+        "bn_bwd": ("hbm", P * C * (2 * (4 + 4 + 1) + eb)),
         "mse": ("hbm", P * C * (3 * eb + 4)),
         "rmsprop": ("hbm", cfg.param_count() * (20 + (2 if eb == 2 else 0))),
     }
 
 
+def role_passes(cfg, m, name, conv):
+    """Micro-batch passes of one layer (block) a role makes per step, or None."""
+    L = cfg.blocks if conv else cfg.layers
+    if name == "mse":
+        return m
+    if name == "rmsprop":
+        return 1
+    if conv:
+        return {"conv_fwd": 4, "conv_fwd_implicit": 4, "conv_dgrad": 2, "conv_dgrad_implicit": 2,
+                "conv_wgrad": 2, "conv_wgrad_implicit": 2, "bn_stats": 4, "bn_apply": 4,
+                "bn_bwd": 2}.get(name, 0) * L * m or None
+    if name in FWD_ROLES:
+        return 2 * L * m
+    if name in BWD_ROLES:
+        return L * m
+    return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 # ------------------------------------------------------------------ CPU baseline (oracle)
 def cpu_baseline(cfg, n, m):
-    """The oracle on one micro-batch of one layer (fwd + remat + bwd, fp64) plus that
+    """The oracle on one micro-batch of one layer (fwd + remat + bwd, float32) plus that
     layer's RMSProp, scaled to the full step: M micro-batches x L layers + L updates."""
     from micro_pipelined_re_amd import inputs
     from oracle import transformer_cell as tc
@@ -169,12 +211,13 @@ def cpu_baseline(cfg, n, m):
     reps, t_step, t_upd, t_start = 0, 0.0, 0.0, time.perf_counter()
     while reps == 0 or time.perf_counter() - t_start < 10.0:
         t0 = time.perf_counter()
-        out = tc.cell_step(p, x, t, 1, cfg.heads, cfg.causal, remat=True)
+        out = tc.cell_step(p, x, t, 1, cfg.heads, cfg.causal, remat=True, dtype=np.float32,
+                           denom=n * cfg.seq * cfg.d_model)
         t1 = time.perf_counter()
-        ms = {k: np.zeros(v.shape) for k, v in p[0].items()}
+        ms = {k: np.zeros(v.shape, np.float32) for k, v in p[0].items()}
         for k in p[0]:
-            tc.rmsprop(p[0][k].astype(np.float64), out["grads"][0][k], ms[k], cfg.lr, cfg.decay,
-                       cfg.eps)
+            tc.rmsprop(p[0][k], out["grads"][0][k], ms[k], np.float32(cfg.lr),
+                       np.float32(cfg.decay), np.float32(cfg.eps))
         t2 = time.perf_counter()
         t_step += t1 - t0
         t_upd += t2 - t1
@@ -188,16 +231,16 @@ def cpu_baseline(cfg, n, m):
     except Exception:
         pass
     return {"value": n * cfg.seq / step_s, "unit": "tokens/s",
-            "cores": threads or os.cpu_count(), "kind": "oracle",
+            "cores": threads or os.cpu_count(), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": (f"one micro-batch ({b} sequences, {b * cfg.seq} tokens) through one layer "
-                       f"(forward, re-materialized forward, backward; numpy float64) plus that "
+                       f"(forward, re-materialized forward, backward; numpy float32) plus that "
                        f"layer's RMSProp, {reps} repetitions of {t2:.2f} s, scaled by {m} "
                        f"micro-batches x {cfg.layers} layers"),
             "sample_seconds": round(t2 * reps, 2)}
 
 
 def conv_cpu_baseline(cfg, n, m):
-    """The oracle on one micro-batch through one block (fwd + remat + bwd, fp64) plus
+    """The oracle on one micro-batch through one block (fwd + remat + bwd, float32) plus
     that block's RMSProp, scaled to the full step: M micro-batches x blocks + updates."""
     from micro_pipelined_re_amd import inputs
     from oracle import conv_cell as cc
@@ -208,11 +251,12 @@ def conv_cpu_baseline(cfg, n, m):
     reps, t_step, t_upd, t_start = 0, 0.0, 0.0, time.perf_counter()
     while reps == 0 or time.perf_counter() - t_start < 10.0:
         t0 = time.perf_counter()
-        out = cc.cell_step(p, x, t, 1, eps=cfg.bn_eps, remat=True)
+        out = cc.cell_step(p, x, t, 1, eps=cfg.bn_eps, remat=True, dtype=np.float32)
         t1 = time.perf_counter()
         for k in p[0]:
-            w = p[0][k].astype(np.float64)
-            tc.rmsprop(w, out["grads"][0][k], np.zeros_like(w), cfg.lr, cfg.decay, cfg.eps)
+            w = p[0][k]
+            tc.rmsprop(w, out["grads"][0][k], np.zeros_like(w), np.float32(cfg.lr),
+                       np.float32(cfg.decay), np.float32(cfg.eps))
         t2 = time.perf_counter()
         t_step += t1 - t0
         t_upd += t2 - t1
@@ -226,10 +270,10 @@ def conv_cpu_baseline(cfg, n, m):
     except Exception:
         pass
     return {"value": n / step_s, "unit": "images/s",
-            "cores": threads or os.cpu_count(), "kind": "oracle",
+            "cores": threads or os.cpu_count(), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": (f"one micro-batch ({b} images of {cfg.height}x{cfg.width}x{cfg.channels}) "
                        f"through one block (forward, re-materialized forward, backward; numpy "
-                       f"float64) plus that block's RMSProp, {reps} repetitions of {t2:.2f} s, "
+                       f"float32) plus that block's RMSProp, {reps} repetitions of {t2:.2f} s, "
                        f"scaled by {m} micro-batches x {cfg.blocks} blocks"),
             "sample_seconds": round(t2 * reps, 2)}
 
@@ -306,7 +350,7 @@ def run_memory(args):
         x.normal_(0.0, 1.0, generator=gen)
         t.normal_(0.0, 1.0, generator=gen)
         y, dx = torch.empty_like(x), torch.empty_like(x)
-        plan = gpipe.gpipe_cell_workspace_bytes(cell.handle, n, m, remat)
+        plan = gpipe.gpipe_cell_workspace_bytes(cell.handle, n, m, remat)   # raises if it does not fit
         ws = torch.empty(plan, dtype=torch.uint8, device="cuda")
         stream = torch.cuda.current_stream()
         torch.cuda.synchronize()
@@ -334,28 +378,46 @@ def run_memory(args):
         torch.cuda.empty_cache()
         return r
 
-    runs = []
+    def fit(xs, ys):
+        """Least-squares line ys ~ a xs + b; returns slope, intercept, R^2."""
+        xs, ys = np.asarray(xs, np.float64), np.asarray(ys, np.float64)
+        a, b0 = np.polyfit(xs, ys, 1)
+        pred = a * xs + b0
+        ss = float(((ys - ys.mean()) ** 2).sum())
+        r2 = 1.0 - float(((ys - pred) ** 2).sum()) / ss if ss > 0 else 1.0
+        return {"slope_bytes": float(a), "intercept_bytes": float(b0), "r2": round(r2, 6)}
+
+    # N sweep at fixed M = 8, M sweep at fixed N = 32 (re-materialization)
+    by_n = [one(nn, 8, True) for nn in (8, 16, 32)]
+    by_m = [one(32, mm, True) for mm in (4, 32)] + [by_n[-1]]
+    by_m.sort(key=lambda r: r["M"])
     n = cfg.batch
-    for m in (32, 8, 4):
-        runs.append(one(n, m, True))
-    # M = 1: the planner's figure alone (it does not fit next to the parameter state)
-    m1 = gpipe.gpipe_cell_workspace_bytes(cell.handle, n, 1, True)
+    # M = 1: the planner's figure, refused by the library's fit check
+    m1, m1_fits = gpipe.gpipe_cell_workspace_fit(cell.handle, n, 1, True)
+    log(f"[bench] N={n} M=1: plan {m1 / 1e9:.1f} GB, fits={m1_fits}")
     # without re-materialization at the largest N (multiple of 8) that fits
-    per_seq_keep = gpipe.gpipe_cell_workspace_bytes(cell.handle, 16, 16, False) / 16
+    per_seq_keep = gpipe.gpipe_cell_workspace_fit(cell.handle, 16, 16, False)[0] / 16
     n_keep = int((0.97 * total_mem - state) // (per_seq_keep + 4 * per_seq_io)) // 8 * 8
     keep = None
     if n_keep >= 8:
         keep = [one(n_keep, n_keep // 2, False), one(n_keep, n_keep // 2, True)]
+    act = lambda rs: [r["activation_bytes_measured"] for r in rs]
     out = {
         "metric": "peak activation bytes vs O(N + L/K*N/M), 48-layer d4096 cell",
-        "value": runs[0]["activation_bytes_measured"], "unit": "bytes",
+        "value": by_m[-1]["activation_bytes_measured"], "unit": "bytes",
         "higher_is_better": False, "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "layers": cfg.layers, "d_model": cfg.d_model,
                    "heads": cfg.heads, "d_ff": cfg.d_ff, "seq_len": cfg.seq,
                    "global_batch": n, "causal": cfg.causal},
         "parameter_state_bytes": state, "device_bytes": total_mem,
-        "remat_runs": runs,
-        "m1_workspace_plan": m1, "m1_fits": bool(state + m1 + 4 * n * per_seq_io < total_mem),
+        "remat_runs_n_sweep_m8": by_n,
+        "remat_runs_m_sweep_n32": by_m,
+        # activations against N at fixed M (the boundary and the set grow with N),
+        # and against L N / M at fixed N (one micro-batch's saved set)
+        "fit_activation_vs_n_at_m8": fit([r["N"] for r in by_n], act(by_n)),
+        "fit_activation_vs_l_n_over_m_at_n32": fit([cfg.layers * r["N"] / r["M"] for r in by_m],
+                                                   act(by_m)),
+        "m1_workspace_plan": m1, "m1_refused_oom": not m1_fits,
         "no_remat_vs_remat_at_largest_n": keep,
     }
     print(json.dumps(out), flush=True)
@@ -416,7 +478,7 @@ def main():
         gpipe.gpipe_cell_step(cell.handle, x, t, y, dx, n, m, remat, ws, ws_bytes, stream, cell.loss)
         gpipe.gpipe_apply_update(cell.handle, cfg.lr, cfg.decay, cfg.eps, stream)
 
-    # warmup; the last warmup step times every role to find the dominant kernel
+    # warmup; the last warmup step times every launch of every role (all streams)
     all_roles = (1 << len(gpipe.ROLES)) - 1
     for i in range(max(args.warmup, 1)):
         if i == max(args.warmup, 1) - 1:
@@ -430,53 +492,26 @@ def main():
         ms_tot, cnt = gpipe.gpipe_cell_profile_read(cell.handle, r)
         if cnt:
             prof[name] = (ms_tot, cnt)
-    # the dominant kernel: the role with the most time whose launch is a single kernel
-    # (a split-K GEMM role is two kernels: the split products and their ordered sum)
-    # The conv cell (bf16, implicit convolutions, re-materialization) runs its
-    # forward phase on lanes (not role-timed); with the implicit weight
-    # gradient its backward is pipelined too (weight gradients on a second
-    # stream, micro-batch m+1's re-materialization on a third, not
-    # role-timed), leaving micro-batch 0's re-materialization alone on the
-    # caller's stream.
-    conv_lanes = (conv and remat and cfg.precision == "bf16" and cfg.channels % 64 == 0
-                  and cfg.blocks >= 2)
-    conv_px = (n // m) * cfg.height * cfg.width if conv else 0
-    conv_piped = (conv_lanes and conv_px % 64 == 0 and conv_px < (1 << 21)
-                  and (conv_px + 64) * cfg.channels < (1 << 31))
 
-    def alone(name):
-        if not conv:
-            return name in ALONE_ROLES
-        if conv_piped:
-            return name in CONV_FORWARD_ROLES or name == "mse"
-        return True
+    def step_work(name):
+        """Algorithmic work of the role in one step, or None."""
+        p_ = role_passes(cfg, m, name, conv)
+        return work[name][1] * p_ if (p_ and name in work) else None
 
     def single_kernel(name):
-        if name not in work or name in ("bias_grad", "norm_grad", "loss_reduce"):
-            return False
-        if not alone(name):
-            return False
+        # a split-K GEMM role is two kernels: the split products and their ordered sum
         return gpipe.gpipe_cell_gemm_plan(cell.handle, n, m, gpipe.ROLES.index(name))[2] <= 1
 
-    # (ranked by the role's time in a whole step: its average launch times its
-    # launches per step -- the Transformer's forward roles are timed in one
-    # micro-batch's re-materialization but run 2 L M micro-batch passes (the
-    # forward phase's launches take several micro-batches at once); the conv
-    # cell's forward roles in the re-materializations (all M, or micro-batch
-    # 0's when pipelined) of the 2 M passes)
-    def step_launches(name, cnt):
-        if conv:
-            if conv_lanes and name in CONV_FORWARD_ROLES:
-                return cnt * (2 * m if conv_piped else 2)
-            return cnt
-        if name not in ALONE_ROLES or name == "mse":
-            return cnt
-        return 2 * cfg.layers * m
-    dominant = max((k for k in prof if single_kernel(k)),
-                   key=lambda k: prof[k][0] / prof[k][1] * step_launches(k, prof[k][1]))
+    # the dominant kernel: the role with the most kernel time in a whole step,
+    # over every stream (forward lanes, backward, re-materializations)
+    ranked = sorted((k for k in prof if step_work(k) and single_kernel(k)),
+                    key=lambda k: -prof[k][0])
+    dominant = ranked[0]
     dom_idx = gpipe.ROLES.index(dominant)
+    log("[bench] kernel time per step (warmup step, all streams): " +
+        ", ".join(f"{k} {prof[k][0]:.1f} ms" for k in ranked[:6]))
 
-    # timed region: K steps; the dominant role's launches are bracketed by events
+    # timed region: K steps; the dominant role's launches are timed by events
     gpipe.gpipe_cell_profile(cell.handle, all_roles if args.profile_all else (1 << dom_idx))
     torch.cuda.reset_peak_memory_stats()
     base_alloc = torch.cuda.memory_allocated()
@@ -494,52 +529,40 @@ def main():
     loss = cell.loss.item()
     peak_alloc = torch.cuda.max_memory_allocated()
 
-    kernels = {}
-    timed = gpipe.ROLES if args.profile_all else (dominant,)
+    # per role: time and launches per step (from the timed region where timed
+    # there, else from the warmup step), algorithmic rate over its kernel time
     src = {}
-    for name in timed:
+    for name in (gpipe.ROLES if args.profile_all else (dominant,)):
         ms_tot, cnt = gpipe.gpipe_cell_profile_read(cell.handle, gpipe.ROLES.index(name))
         if cnt:
-            src[name] = (ms_tot / args.steps, cnt // args.steps)
+            src[name] = (ms_tot / args.steps, cnt // args.steps, "timed steps")
     for name, (ms_tot, cnt) in prof.items():
         if name not in src:
-            src[name] = (ms_tot, cnt)
-    for name, (ms_tot, cnt) in src.items():
-        kind, per = work.get(name, (None, None))
+            src[name] = (ms_tot, cnt, "warmup step")
+    peak_mfma = PEAK_BF16_TFLOPS if cfg.precision == "bf16" else PEAK_FP32_TFLOPS
+    kernels = {}
+    for name, (ms_tot, cnt, when) in sorted(src.items(), key=lambda kv: -kv[1][0]):
         e = {"ms_per_step": round(ms_tot, 4), "launches_per_step": cnt,
-             "avg_us": round(ms_tot / cnt * 1e3, 3)}
-        if name in gpipe.ROLES:
-            _, _, sp_ = gpipe.gpipe_cell_gemm_plan(cell.handle, n, m, gpipe.ROLES.index(name))
-            if sp_ > 1:
-                e["split_k"] = sp_
-        if not conv and name not in ALONE_ROLES and name not in ("loss_reduce", "rmsprop"):
-            e["overlapped"] = ("second stream" if name in SECOND_STREAM_ROLES
-                               else "caller's stream") + ", concurrent with the other streams"
-        if not conv and name in ALONE_ROLES and name != "mse":
-            e["timed"] = "micro-batch 0's re-materialization, caller's stream alone"
-            # (the forward phase runs these for several micro-batches per launch)
-            e["micro_batch_passes_per_step"] = 2 * cfg.layers * m
-        if conv_lanes and name in CONV_FORWARD_ROLES:
-            e["timed"] = ("micro-batch 0's re-materialization, caller's stream alone" if conv_piped
-                          else "re-materializations only (the forward phase runs on three streams)")
-            e["launches_per_step_all"] = cnt * (2 * m if conv_piped else 2)
-        if conv_piped and not alone(name) and name not in ("loss_reduce", "rmsprop",
-                                                           "bn_running"):
-            e["overlapped"] = "concurrent with the other streams"
-        if kind == "mfma":
-            tf = per / (ms_tot / cnt * 1e-3) / 1e12
-            pk = PEAK_BF16_TFLOPS if cfg.precision == "bf16" else PEAK_FP32_TFLOPS
-            e.update(tflops=round(tf, 1), frac_mfma_peak=round(tf / pk, 4))
-        elif kind == "hbm":
-            gb = per / (ms_tot / cnt * 1e-3) / 1e9
-            e.update(gbs=round(gb, 1), frac_hbm_peak=round(gb / PEAK_HBM_GBS, 4))
+             "avg_us": round(ms_tot / cnt * 1e3, 3), "from": when}
+        _, _, sp_ = gpipe.gpipe_cell_gemm_plan(cell.handle, n, m, gpipe.ROLES.index(name))
+        if sp_ > 1:
+            e["split_k"] = sp_
+        sw = step_work(name)
+        if sw:
+            kind = work[name][0]
+            rate = sw / (ms_tot * 1e-3)
+            if kind == "mfma":
+                e.update(tflops=round(rate / 1e12, 1), frac_mfma_peak=round(rate / 1e12 / peak_mfma, 4))
+            else:
+                e.update(gbs=round(rate / 1e9, 1), frac_hbm_peak=round(rate / 1e9 / PEAK_HBM_GBS, 4))
         kernels[name] = e
 
-    # dominant kernel roofline, from the events inside the timed region
-    kind, per = work[dominant]
-    d_ms, d_cnt = src[dominant]
+    # dominant kernel roofline: its algorithmic work per step over its kernel
+    # time per step (= the mean work per launch over the mean launch duration)
+    kind = work[dominant][0]
+    d_ms, d_cnt, _ = src[dominant]
+    per = step_work(dominant) / d_cnt          # mean algorithmic work per launch
     avg_s = d_ms / d_cnt * 1e-3
-    peak_mfma = PEAK_BF16_TFLOPS if cfg.precision == "bf16" else PEAK_FP32_TFLOPS
     if kind == "mfma":
         roof = {"bound": "mfma", "achieved": round(per / avg_s / 1e12, 2), "peak": peak_mfma,
                 "unit": "TFLOP/s"}
@@ -556,17 +579,19 @@ def main():
     tm_, tn_, sp_ = gpipe.gpipe_cell_gemm_plan(cell.handle, n, m, dom_idx)
     roof["kernel_tile"] = [tm_, tn_] if tm_ else None
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
+    roof["launches_per_step"] = d_cnt
     roof["work_per_launch"] = per
+    roof["kernel_ms_per_step"] = round(d_ms, 3)
 
-    def clean(k):
-        return work.get(k, ("", 0))[0] == "mfma" and alone(k)
-    gemm_flops = sum(work[k][1] * src[k][1] for k in src if clean(k))
-    gemm_ms = sum(src[k][0] for k in src if clean(k))
-    # (the Transformer cell's forward-phase launches are not role-timed: count its work directly)
-    step_flops = (sum(work[k][1] * step_launches(k, src[k][1]) for k in src
-                      if work.get(k, ("", 0))[0] == "mfma")
-                  if conv else step_mfma_flops(cfg, n, m))
-    keep_bytes = gpipe.gpipe_cell_workspace_bytes(cell.handle, n, m, False)
+    # the GEMM roles' algorithmic work over their summed kernel time, and the
+    # step's whole algorithmic MFMA work over its wall time
+    gemm = [k for k in src if work.get(k, ("", 0))[0] == "mfma" and step_work(k)]
+    gemm_flops = sum(step_work(k) for k in gemm)
+    gemm_ms = sum(src[k][0] for k in gemm)
+    step_flops = gemm_flops if conv else step_mfma_flops(cfg, n, m)
+    keep_bytes = gpipe.gpipe_cell_workspace_fit(cell.handle, n, m, False)[0]
+    state_bytes = sum(v.numel() * v.element_size()
+                      for v in (cell.master, cell.w_lowp, cell.grad, cell.ms) if v is not None)
     act_bytes = x.numel() * x.element_size()
     if conv:
         units, unit = n, "images/s"
@@ -594,11 +619,16 @@ def main():
         "roofline": roof,
         "mfma_util_gemm": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak_mfma, 4)
         if gemm_ms else None,
+        "mfma_util_gemm_note": "the GEMM roles' algorithmic flops over their summed kernel "
+                               "time (kernels of different streams overlap)",
         "mfma_util_step": round(step_flops / (ms_step * 1e-3) / 1e12 / peak_mfma, 4),
-        "peak_act_bytes": {"workspace_plan": ws_bytes, "boundary_x_y_dx": 3 * act_bytes,
-                           "total": ws_bytes + 3 * act_bytes,
-                           "no_remat_workspace_plan": keep_bytes,
-                           "torch_max_allocated": peak_alloc, "torch_base_allocated": base_alloc},
+        # the library allocates nothing: the step's device memory is what the
+        # caller allocated from the plan; the measured peak above the parameter
+        # state is the workspace plus the boundary tensors x, target, y, dx
+        "peak_act_bytes": {"workspace_plan": ws_bytes, "boundary_x_t_y_dx": 4 * act_bytes,
+                           "total_planned": ws_bytes + 4 * act_bytes,
+                           "measured_peak_above_state": peak_alloc - state_bytes,
+                           "no_remat_workspace_plan": keep_bytes},
         "loss": loss,
         "kernels": kernels,
     }

@@ -375,10 +375,15 @@ typedef enum {
 } gpipe_role;
 
 /* Event timing of selected kernel roles.  With bit r of role_mask set, every
- * later launch of role r by gpipe_cell_step / gpipe_apply_update is
- * bracketed by two HIP events recorded on the call's stream.  Calling it
- * again (any mask, 0 switches timing off) discards what was recorded.  The
+ * later launch of role r by gpipe_cell_step / forward / backward /
+ * gpipe_apply_update, on whichever of the step's streams it runs, is timed
+ * by two HIP events: a GEMM role's events are recorded in its own dispatch
+ * (the span of its kernels), any other role's on its stream right before and
+ * after the launch.  With several streams a launch's span may share the CUs
+ * with other kernels: it is the time the launch took in the step.  Calling
+ * it again (any mask, 0 switches timing off) discards what was recorded.  The
  * cell creates the events it needs and destroys them in gpipe_cell_destroy.
+ * gpipe_cell_step_noalloc never times.
  * Errors: GPIPE_ERR_DEVICE if events cannot be created. */
 gpipe_status gpipe_cell_profile(gpipe_cell *cell, unsigned long long role_mask);
 

@@ -507,8 +507,8 @@ gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void*
   // micro-batch m runs on lane m mod K (up to 3 streams: the caller's and the
   // cell's two) in block slot m mod K of set 0, with its own BN and split-K
   // partials, enqueued block by block so that every stream has work queued.
-  // Launches on the lanes are not role-timed (their times would include the
-  // other streams').
+  // Role timing covers every stream (a launch's time is its own span, which
+  // may share the CUs with the other streams' kernels).
   if (fwd && remat && p.lanes > 1) {
     {
       const gpipe_status st = ensure_streams(c);
@@ -518,7 +518,6 @@ gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void*
     const int K = p.lanes;
     CCtx lane[3] = {cx, cx, cx};
     for (int k = 0; k < 3; ++k) {
-      lane[k].prof = nullptr;
       lane[k].part = p.lane_part[k];
       lane[k].splitk = p.lane_splitk[k];
     }
@@ -569,7 +568,6 @@ gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void*
     if (st != GPIPE_OK) return st;
     ss = Streams{c, stream, c->aux, c->aux2};
     cr.s = ss.s3;
-    cr.prof = nullptr;
     cr.part = p.lane_part[1];
     cr.splitk = p.lane_splitk[1];
   }

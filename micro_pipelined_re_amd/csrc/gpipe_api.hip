@@ -439,9 +439,9 @@ bool group_plan(const gpipe_cell* c, const Plan& p, int g, size_t stride, Plan* 
 // lanes after the first with their own split-K partials -- in that lane's
 // share of the saved set, so each stream's kernels fill the CUs and launch
 // gaps the others leave; the set is free until the backward phase
-// re-materializes into it, after the streams join.  Launches here are not
-// role-timed (their times would include the other streams').  G and K come
-// from the plan (forward_groups).
+// re-materializes into it, after the streams join.  Role timing covers these
+// launches too (each one's own span, which may share the CUs with the other
+// streams' kernels).  G and K come from the plan (forward_groups).
 gpipe_status overlapped_forward(const Ctx& cx, Streams& ss, const void* x, void* y, int M,
                                 size_t mb) {
   const Plan& p = *cx.p;
@@ -458,7 +458,6 @@ gpipe_status overlapped_forward(const Ctx& cx, Streams& ss, const void* x, void*
       return GPIPE_ERR_INVALID;
   }
   Ctx lane[3] = {cx, cx, cx};
-  for (Ctx& z : lane) z.prof = nullptr;
   lane[1].s = ss.s2;
   lane[1].splitk = p.splitk2;
   lane[2].s = ss.s3;
@@ -725,7 +724,6 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
   auto slot_of = [&](int m, int j) { return (piped && (m & 1)) ? L - 1 - j : j; };
   Ctx cr = cx;  // the re-materialization's context on the third stream
   cr.s = ss.s3;
-  cr.prof = nullptr;
   cr.splitk = p.splitk2;
   auto remat_layer = [&](const Ctx& z, int m, int j) {
     const void* in = j == 0 ? cx.act(x, m * mb) : z.at(saved_at(p, 0, slot_of(m, j - 1), GPIPE_SAVED_X));
