@@ -59,7 +59,7 @@ def log(*a):
 # WRITE_SIZE counters (calibrated on a streaming kernel of known size) and
 # stored in a profile summary together with a digest of the GEMM sources; the
 # figures are used only while the sources still hash to that digest.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_cell_d2048_L8_causal.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "counters_cell_d2048_L8_causal.md")
 GEMM_SOURCES = ("common.hpp", "kernels.hpp", "gemm_impl.hpp", "gemm_dma.hpp", "gemm.hip",
                 "gemm_fwd.hip", "gemm_dgrad.hip", "gemm_wgrad.hip")
 
@@ -423,6 +423,107 @@ def run_memory(args):
     print(json.dumps(out), flush=True)
 
 
+# ------------------------------------------------------------------ counter summaries
+def _kernel_class(name):
+    """The step role of a GEMM dispatch (its last template argument) or the
+    family of another kernel; None for kernels the summary leaves out."""
+    import re
+    from micro_pipelined_re_amd import gpipe
+    m = re.search(r"gemm_(?:spec|dma|bf16)_kernel<.*, (\d+)>\(gp::GemmParams\)", name)
+    if m:
+        return gpipe.ROLES[int(m.group(1))]
+    for key, cls in (("ln_fwd_kernel", "ln_fwd"), ("ln_bwd", "ln_bwd"), ("flash_fwd_kernel", "attn_fwd"),
+                     ("flash_bwd_kernel", "attn_bwd"), ("mse_kernel", "mse"),
+                     ("rmsprop_kernel", "rmsprop"), ("to_bf16_kernel", "to_bf16"),
+                     ("sum_partials_kernel", "sum_partials"), ("splitk_reduce", "splitk_reduce")):
+        if key in name:
+            return cls
+    return None
+
+
+def _read_counters(d):
+    """{dispatch: (class, grid, duration_ns, {counter: value})} of one rocprofv3
+    --pmc run (csv output) in directory d."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(d, "*counter_collection.csv")):
+        for r in csv.DictReader(open(path)):
+            cls = _kernel_class(r["Kernel_Name"])
+            if cls is None:
+                continue
+            k = int(r["Dispatch_Id"])
+            if k not in out:
+                out[k] = (cls, int(r["Grid_Size"]),
+                          int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), {})
+            out[k][3][r["Counter_Name"]] = float(r["Counter_Value"])
+    return out
+
+
+def counter_summary(fetch_dir, write_dir, sq_dir=None):
+    """Markdown tables of the counter passes over one step of the native
+    driver: HBM bytes per dispatch (FETCH_SIZE and WRITE_SIZE, calibrated on
+    the to_bf16 stream of the parameters), and for the GEMM roles the MFMA
+    busy fraction and the clock implied by GRBM_GUI_ACTIVE.  Durations are
+    those of the counter runs, whose dispatches run one at a time."""
+    from micro_pipelined_re_amd import configs
+    cfg = configs.CELL_2048
+    nparam = cfg.param_count()
+    fe, wr = _read_counters(fetch_dir), _read_counters(write_dir)
+    cal = [v for v in fe.values() if v[0] == "to_bf16"], [v for v in wr.values() if v[0] == "to_bf16"]
+    f_fetch = 4.0 * nparam / (cal[0][0][3]["FETCH_SIZE"] * 1024.0)
+    f_write = 2.0 * nparam / (cal[1][0][3]["WRITE_SIZE"] * 1024.0)
+    lines = [f"Calibration (to_bf16 over {nparam:,} parameters: {4 * nparam:,} B read, "
+             f"{2 * nparam:,} B written): FETCH_SIZE x {f_fetch:.4f}, WRITE_SIZE x {f_write:.4f}.", ""]
+
+    def groups(runs, key):
+        g = {}
+        for cls, grid, dur, c in runs.values():
+            g.setdefault(key(cls, grid), []).append((dur, c))
+        return g
+    by = lambda cls, grid: (cls, grid)
+    gf, gw = groups(fe, by), groups(wr, by)
+    work = role_work(cfg, cfg.batch, cfg.micro)
+    lines += ["| kernel (role) | grid | dispatches | mean us | fetch MB | write MB | GB/s |",
+              "|---|---|---|---|---|---|---|"]
+    for key in sorted(gf, key=lambda k: -sum(d for d, _ in gf[k])):
+        f = gf[key]
+        w = gw.get(key, [])
+        us = sum(d for d, _ in f) / len(f) / 1e3
+        fb = sum(c["FETCH_SIZE"] for _, c in f) / len(f) * 1024 * f_fetch
+        wb = sum(c["WRITE_SIZE"] for _, c in w) / len(w) * 1024 * f_write if w else 0.0
+        lines.append(f"| {key[0]} | {key[1]} | {len(f)} | {us:.2f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} "
+                     f"| {(fb + wb) / us / 1e3:.0f} |")
+    lines.append("")
+    # per role over all its dispatches (the mix of one step), as bench.py reads them
+    gfr, gwr = groups(fe, lambda cls, grid: cls), groups(wr, lambda cls, grid: cls)
+    mach = [f"gemm_source_digest: {gemm_source_digest()}"]
+    for role in sorted(gfr):
+        if work.get(role, ("", 0))[0] != "mfma" or role.startswith("attn"):
+            continue
+        fb = sum(c["FETCH_SIZE"] for _, c in gfr[role]) / len(gfr[role]) * 1024 * f_fetch
+        wb = sum(c["WRITE_SIZE"] for _, c in gwr[role]) / len(gwr[role]) * 1024 * f_write
+        mach.append(f"traffic {role}: fetch_bytes={int(round(fb))} write_bytes={int(round(wb))}")
+    if sq_dir:
+        sq = groups(_read_counters(sq_dir), by)
+        lines += ["| GEMM role | grid | dispatches | mean us | MFMA busy | flops (MOPS x 512) / algorithmic "
+                  "| clock GHz (GRBM_GUI_ACTIVE per XCD / duration) |", "|---|---|---|---|---|---|---|"]
+        for key in sorted(sq, key=lambda k: -sum(d for d, _ in sq[k])):
+            if work.get(key[0], ("", 0))[0] != "mfma" or key[0].startswith("attn"):
+                continue
+            rows = sq[key]
+            us = sum(d for d, _ in rows) / len(rows) / 1e3
+            gui = sum(c["GRBM_GUI_ACTIVE"] for _, c in rows) / 8.0      # summed over 8 XCDs
+            busy = sum(c["SQ_VALU_MFMA_BUSY_CYCLES"] for _, c in rows) / (gui * 1024)  # 1024 SIMDs
+            fl = sum(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for _, c in rows) * 512 / len(rows)
+            lines.append(f"| {key[0]} | {key[1]} | {len(rows)} | {us:.2f} | {busy:.3f} | "
+                         f"{fl:.4g} | {gui / len(rows) / (us * 1e3):.2f} |")
+        lines.append("")
+    lines += ["Machine-readable lines read by bench.py (the figures hold only while the GEMM "
+              "sources hash to the digest; comments excluded):", "", "```", *mach, "```"]
+    return "\n".join(lines)
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -436,9 +537,15 @@ def main():
     ap.add_argument("--precision", default=None, choices=("bf16", "fp32"),
                     help="override the workload's precision")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="print the summary of rocprofv3 --pmc runs (csv) of the native driver: "
+                         "FETCH_SIZE dir, WRITE_SIZE dir [, SQ/GRBM dir]")
     ap.add_argument("--profile-all", action="store_true",
                     help="time every kernel role inside the timed region")
     args = ap.parse_args()
+    if args.counter_summary:
+        print(counter_summary(*args.counter_summary[:3]))
+        return 0
     if args.workload == "memory_4096" and args.gpus == 1:
         return run_memory(args)
     if args.gpus != 1:
