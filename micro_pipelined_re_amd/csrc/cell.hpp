@@ -164,11 +164,6 @@ struct Streams {
   }
 };
 
-// Events of s2 after the weight gradients of one Transformer layer's backward.
-struct WgradDone {
-  hipEvent_t ffn2 = nullptr, ffn1 = nullptr, out = nullptr, qkv = nullptr;
-};
-
 // Creates the cell's two streams and the event ring at its first step.
 inline gpipe_status ensure_streams(gpipe_cell* c) {
   int dev = -1;
@@ -177,7 +172,9 @@ inline gpipe_status ensure_streams(gpipe_cell* c) {
   GP_CHECK(hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking));
   GP_CHECK(hipStreamCreateWithFlags(&c->aux2, hipStreamNonBlocking));
   c->aux_device = dev;
-  for (int i = 0; i < 64; ++i) {
+  // (a ring: an event is recorded again ~20 layers of the backward phase
+  // later, well after its last wait)
+  for (int i = 0; i < 256; ++i) {
     hipEvent_t e;
     GP_CHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
     c->sync_events.push_back(e);

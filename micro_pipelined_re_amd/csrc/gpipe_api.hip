@@ -30,9 +30,14 @@ namespace {
 //   scores: float32 [B*H, S, ldS]  (forward scores, backward dP; unfused
 //           attention only)
 //   ds:     act [B*H, S, ldS] (unfused attention only)
+//   spare:  one more layer slot after the set (pipelined backward phase: the
+//           next micro-batch's top layer is re-materialized there while the
+//           current one's backward still holds every slot of the set)
 //   r0, r1, dm: float32 [T, D]   (residual-stream gradients, LN input grads)
-//   a0, a1, dctx: act [T, D]
-//   du: act [T, F];  dqkv: act [T, 3D]
+//   a0, a1: act [T, D], two copies each;  dctx: act [T, D]
+//   du: act [T, F];  dqkv: act [T, 3D], two copies each (the weight-gradient
+//           stream reads them: the input-gradient chain writes one copy while
+//           the other's readers may still run)
 //   colpart: float32 [colsum chunks, max(3D, F)] (bias gradients summed by
 //            column sums: fp32 cells, or shapes the weight-gradient kernel
 //            does not sum)
@@ -59,8 +64,9 @@ struct Plan {
   size_t saved_bytes[GPIPE_N_SAVED];
   size_t layer_bytes, set_bytes;
   int nsets;
-  size_t yre, scores, ds, r0, r1, dm, a0, a1, dctx, du, dqkv, colpart, gpart, msepart, splitk, splitk2,
-      splitk3;
+  bool spare;  // a spare layer slot after set 0 (slot index L)
+  size_t yre, scores, ds, r0, r1, dm, a0[2], a1[2], dctx, du[2], dqkv[2], colpart, gpart, msepart,
+      splitk, splitk2, splitk3;
   size_t colpart_floats;
   // gpart slots (GPS_*): offset inside a layer's block, partial rows, row length
   size_t gp_off[GPS_N], gp_layer;
@@ -151,7 +157,10 @@ bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
   // layer 0 has no X slot: the set is L layer slots minus one X slot
   p->set_bytes = size_t(c->L) * p->layer_bytes;
   p->nsets = remat ? 1 : M;
-  size_t o = size_t(p->nsets) * p->set_bytes;
+  // the backward phase is pipelined (transformer_run) with re-materialization,
+  // fused attention and two or more layers
+  p->spare = remat && p->flash && c->L >= 2;
+  size_t o = size_t(p->nsets) * p->set_bytes + (p->spare ? p->layer_bytes : 0);
   auto take = [&](size_t bytes) {
     const size_t at = o;
     o += align_up(bytes, kAlign);
@@ -164,11 +173,13 @@ bool make_plan(const gpipe_cell* c, int N, int M, int remat, Plan* p) {
   p->r0 = take(T * D * 4);
   p->r1 = take(T * D * 4);
   p->dm = take(T * D * 4);
-  p->a0 = take(T * D * eb);
-  p->a1 = take(T * D * eb);
+  for (int k = 0; k < 2; ++k) {
+    p->a0[k] = take(T * D * eb);
+    p->a1[k] = take(T * D * eb);
+    p->du[k] = take(T * F * eb);
+    p->dqkv[k] = take(T * 3 * D * eb);
+  }
   p->dctx = take(T * D * eb);
-  p->du = take(T * F * eb);
-  p->dqkv = take(T * 3 * D * eb);
   p->colpart_floats = size_t(colsum_chunks(int(T))) * std::max(3 * D, F);
   p->colpart = take(p->colpart_floats * 4);
   {
@@ -484,13 +495,38 @@ gpipe_status overlapped_forward(const Ctx& cx, Streams& ss, const void* x, void*
   return (K < 2 || ss.join_all()) && (K < 3 || ss.join3()) ? GPIPE_OK : GPIPE_ERR_DEVICE;
 }
 
+// A transient gradient of the backward phase that a weight gradient on the
+// second stream reads: two copies used in turn, each with the event recorded
+// after the last weight gradient that read it.  The input-gradient chain
+// writes the other copy than the one just read, waiting only for that copy's
+// readers -- from two writes earlier, long done -- instead of for the
+// weight-gradient stream to catch up.
+struct Transient {
+  size_t off[2];
+  hipEvent_t read[2] = {nullptr, nullptr};
+  int cur = 0;
+  void* now(const Ctx& x) const { return x.at(off[cur]); }
+  // the copy to write next, once its last readers are done
+  bool next(const Ctx& x, Streams& ss, void** out) {
+    cur ^= 1;
+    if (!ss.join(read[cur])) return false;
+    read[cur] = nullptr;
+    *out = x.at(off[cur]);
+    return true;
+  }
+  // the weight gradients enqueued so far on the second stream read this copy
+  bool read_by_s2(Streams& ss) { return ss.mark(&read[cur]); }
+};
+struct Transients {
+  Transient a0, a1, du, dqkv;
+};
+
 // Backward of layer l (its saved tensors in layer slot `slot` of `set`).  On
-// entry r0 (f32) / a0 (act) hold the gradient w.r.t.
-// the layer output; on exit they hold the gradient w.r.t. its input (a0, or
-// dx_out when given, receives the act copy).
-gpipe_status layer_backward(const Ctx& x, Streams& ss, const WgradDone& above, WgradDone* mine,
-                            int set, int slot, int l, const void* xin, int beta,
-                            void* dx_out) {
+// entry r0 (f32) / the current a0 copy (act) hold the gradient w.r.t. the
+// layer output; on exit they hold the gradient w.r.t. its input (the next a0
+// copy, or dx_out when given, receives the act copy).
+gpipe_status layer_backward(const Ctx& x, Streams& ss, Transients& tb, int set, int slot, int l,
+                            const void* xin, int beta, void* dx_out) {
   Ctx w = x;  // the weight gradients' context: the second stream
   w.s = ss.s2;
   const gpipe_cell* c = x.c;
@@ -512,11 +548,11 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, const WgradDone& above, W
   float* r0 = static_cast<float*>(x.at(p.r0));
   float* r1 = static_cast<float*>(x.at(p.r1));
   float* dm = static_cast<float*>(x.at(p.dm));
-  void* a0 = x.at(p.a0);
-  void* a1 = x.at(p.a1);
+  void* a0 = tb.a0.now(x);
   void* dctx = x.at(p.dctx);
-  void* du = x.at(p.du);
-  void* dqkv = x.at(p.dqkv);
+  void* a1 = nullptr;
+  void* du = nullptr;
+  void* dqkv = nullptr;
   float* dP = static_cast<float*>(x.at(p.scores));
   void* dS = x.at(p.ds);
   float* ln1part = static_cast<float*>(x.at(gpart_at(p, l, GPS_LN1)));
@@ -531,26 +567,27 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, const WgradDone& above, W
   // launch by ~7 us (measured in the kernel trace), and the two batches keep
   // the weight gradients in the same order on the second stream.
   bool fused = false;
-  if (!ss.join(above.ffn1)) return GPIPE_ERR_DEVICE;  // the layer above's FFN1 weight gradient read du
+  if (!tb.du.next(x, ss, &du)) return GPIPE_ERR_DEVICE;
   GP_RUN(x, GPIPE_ROLE_FFN2_DGRAD, mm(x, GPIPE_ROLE_FFN2_DGRAD, T, F, D, a0, D, x.wmat(l, GPIPE_W_2), F, du, F,
               nullptr, nullptr, 0, u, F));
   if (!ss.fork()) return GPIPE_ERR_DEVICE;  // a0, g and du exist
   GP_RUN(w, GPIPE_ROLE_FFN2_WGRAD, mm_wgrad(w, GPIPE_ROLE_FFN2_WGRAD, l, GPS_B2, D, F, T, a0, D, g, F,
               x.grad(l, GPIPE_W_2), F, beta, &fused));
-  if (!ss.mark(&mine->ffn2)) return GPIPE_ERR_DEVICE;
+  if (!tb.a0.read_by_s2(ss)) return GPIPE_ERR_DEVICE;
   if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r0, D, D, x.grad(l, GPIPE_B_2), beta));
   GP_RUN(w, GPIPE_ROLE_FFN1_WGRAD, mm_wgrad(w, GPIPE_ROLE_FFN1_WGRAD, l, GPS_B1, F, D, T, du, F, h2, D,
               x.grad(l, GPIPE_W_1), D, beta, &fused));
-  if (!ss.mark(&mine->ffn1)) return GPIPE_ERR_DEVICE;
+  if (!tb.du.read_by_s2(ss)) return GPIPE_ERR_DEVICE;
   GP_RUN(x, GPIPE_ROLE_FFN1_DGRAD, mm(x, GPIPE_ROLE_FFN1_DGRAD, T, D, F, du, F, x.wmat(l, GPIPE_W_1), D, dm, D));
   if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, du, F, F, x.grad(l, GPIPE_B_1), beta));
   int nblk = 0;
-  if (!ss.join(above.out)) return GPIPE_ERR_DEVICE;  // the layer above's out-projection weight gradient read a1
+  if (!tb.a1.next(x, ss, &a1)) return GPIPE_ERR_DEVICE;
   GP_RUN(x, GPIPE_ROLE_LN2_BWD, layernorm_bwd(bf, dm, x1, st2, x.wf32(l, GPIPE_LN2_G), r0, r1, a1, ln2part, T, D,
                          beta, &nblk, x.s));
 
   // attention: x1 = x + ctx Wo^T + bo
   GP_RUN(x, GPIPE_ROLE_OUT_DGRAD, mm(x, GPIPE_ROLE_OUT_DGRAD, T, D, D, a1, D, x.wmat(l, GPIPE_W_O), D, dctx, D));
+  if (!tb.dqkv.next(x, ss, &dqkv)) return GPIPE_ERR_DEVICE;
   const int64_t sq = int64_t(S) * 3 * D;
   const int64_t sp = int64_t(H) * S * ldS;
   const int64_t sd = int64_t(S) * D;
@@ -560,7 +597,6 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, const WgradDone& above, W
   Bat PP{P, ldS, sp, int64_t(S) * ldS}, DP{dP, ldS, sp, int64_t(S) * ldS}, DS{dS, ldS, sp, int64_t(S) * ldS};
   Bat DC{dctx, D, sd, dh};
   const int cz = c->causal;
-  if (!ss.join(above.qkv)) return GPIPE_ERR_DEVICE;  // the layer above's QKV weight gradient read dqkv
   if (p.flash) {
     const float* lse2 = static_cast<const float*>(P);
     // dQ, dK and dV in one launch
@@ -593,17 +629,18 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, const WgradDone& above, W
   if (!ss.fork()) return GPIPE_ERR_DEVICE;  // a1 and dqkv exist
   GP_RUN(w, GPIPE_ROLE_OUT_WGRAD, mm_wgrad(w, GPIPE_ROLE_OUT_WGRAD, l, GPS_BO, D, D, T, a1, D, ctx, D,
               x.grad(l, GPIPE_W_O), D, beta, &fused));
-  if (!ss.mark(&mine->out)) return GPIPE_ERR_DEVICE;
+  if (!tb.a1.read_by_s2(ss)) return GPIPE_ERR_DEVICE;
   if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r1, D, D, x.grad(l, GPIPE_B_O), beta));
   GP_RUN(w, GPIPE_ROLE_QKV_WGRAD, mm_wgrad(w, GPIPE_ROLE_QKV_WGRAD, l, GPS_BQKV, 3 * D, D, T, dqkv, 3 * D, h1,
               D, x.grad(l, GPIPE_W_QKV), D, beta, &fused));
-  if (!ss.mark(&mine->qkv)) return GPIPE_ERR_DEVICE;
+  if (!tb.dqkv.read_by_s2(ss)) return GPIPE_ERR_DEVICE;
   GP_RUN(x, GPIPE_ROLE_QKV_DGRAD, mm(x, GPIPE_ROLE_QKV_DGRAD, T, D, 3 * D, dqkv, 3 * D, x.wmat(l, GPIPE_W_QKV), D,
               dm, D));
   if (!fused)
     GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, dqkv, 3 * D, 3 * D, x.grad(l, GPIPE_B_QKV), beta));
-  if (!ss.join(mine->ffn2)) return GPIPE_ERR_DEVICE;  // this layer's FFN2 weight gradient read a0
-  GP_RUN(x, GPIPE_ROLE_LN1_BWD, layernorm_bwd(bf, dm, xin, st1, x.wf32(l, GPIPE_LN1_G), r1, r0, dx_out ? dx_out : a0,
+  void* a0_in = dx_out;  // the gradient w.r.t. the layer input (act)
+  if (!a0_in && !tb.a0.next(x, ss, &a0_in)) return GPIPE_ERR_DEVICE;
+  GP_RUN(x, GPIPE_ROLE_LN1_BWD, layernorm_bwd(bf, dm, xin, st1, x.wf32(l, GPIPE_LN1_G), r1, r0, a0_in,
                          ln1part, T, D, beta, &nblk, x.s));
   return GPIPE_OK;
 }
@@ -715,35 +752,49 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
   if (!bwd) return GPIPE_OK;
   // phase 2: backward with re-materialization and float32 accumulation.
   // With fused attention the re-materialization of micro-batch m+1 runs on
-  // the third stream during the backward of micro-batch m, in the one saved
-  // set: the backward frees the layer slots from the top down and the
-  // re-materialization fills them from the bottom up, so micro-batch m+1
-  // puts layer j in the slot that layer L-1-j of micro-batch m held (odd
-  // micro-batches take the slots in reverse order), each layer enqueued
-  // after that slot's backward and weight gradients.  A layer's output goes
-  // to its own slot's X tensor (the next layer's input).  Micro-batch 0
-  // re-materializes on the caller's stream before its backward.
+  // the third stream during the backward of micro-batch m, in the saved set
+  // and one spare layer slot: the backward frees the layer slots from the top
+  // down and the re-materialization fills them from the bottom up, micro-batch
+  // m+1 putting layer j in the slot that layer L-1-j of micro-batch m held,
+  // each layer enqueued after that slot's backward and weight gradients; its
+  // top layer goes to the spare slot, right after layer L-2 (so it does not
+  // wait for micro-batch m's last layer), and the slot micro-batch m's layer 0
+  // frees is the next spare.  A layer's output goes to its own slot's X
+  // tensor (the next layer's input).  Micro-batch 0 re-materializes on the
+  // caller's stream before its backward.
   const bool piped = lanes;
-  auto slot_of = [&](int m, int j) { return (piped && (m & 1)) ? L - 1 - j : j; };
+  if (piped && !p.spare) return GPIPE_ERR_STATE;
+  std::vector<int> cur(L), nxt(L);  // layer -> slot, this micro-batch and the next
+  for (int l = 0; l < L; ++l) cur[l] = l;
+  int spare = L;
   Ctx cr = cx;  // the re-materialization's context on the third stream
   cr.s = ss.s3;
   cr.splitk = p.splitk2;
-  auto remat_layer = [&](const Ctx& z, int m, int j) {
-    const void* in = j == 0 ? cx.act(x, m * mb) : z.at(saved_at(p, 0, slot_of(m, j - 1), GPIPE_SAVED_X));
-    void* out = j == L - 1 ? z.at(p.yre) : z.at(saved_at(p, 0, slot_of(m, j), GPIPE_SAVED_X));
-    return layer_forward(z, 0, slot_of(m, j), j, in, out);
+  auto remat_layer = [&](const Ctx& z, const std::vector<int>& sl, int m, int j) {
+    const void* in = j == 0 ? cx.act(x, m * mb) : z.at(saved_at(p, 0, sl[j - 1], GPIPE_SAVED_X));
+    void* out = j == L - 1 ? z.at(p.yre) : z.at(saved_at(p, 0, sl[j], GPIPE_SAVED_X));
+    return layer_forward(z, 0, sl[j], j, in, out);
   };
+  Transients tb;
+  for (int k = 0; k < 2; ++k) {
+    tb.a0.off[k] = p.a0[k];
+    tb.a1.off[k] = p.a1[k];
+    tb.du.off[k] = p.du[k];
+    tb.dqkv.off[k] = p.dqkv[k];
+  }
   for (int m = 0; m < M; ++m) {
     const int set = remat ? 0 : m;
     const void* xm = cx.act(x, m * mb);
     const void* ym = io.y ? cx.act(io.y, m * mb) : nullptr;
-    // every weight gradient of the previous micro-batch has read the saved
-    // activations and the transient gradients this one overwrites
-    if (m > 0 && !ss.join_all()) return GPIPE_ERR_DEVICE;
+    // unpipelined, the re-materialization below overwrites the saved
+    // activations the previous micro-batch's weight gradients read
+    // (pipelined, the third stream's forks order those reads, and the
+    // transients the weight gradients read wait per copy)
+    if (m > 0 && !piped && !ss.join_all()) return GPIPE_ERR_DEVICE;
     if (piped) {
       if (m == 0) {
         for (int j = 0; j < L; ++j) {
-          gpipe_status st = remat_layer(cx, 0, j);
+          gpipe_status st = remat_layer(cx, cur, 0, j);
           if (st != GPIPE_OK) return st;
         }
       } else if (!ss.join3()) {  // this micro-batch's re-materialization is done
@@ -756,36 +807,45 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
       if (st != GPIPE_OK) return st;
       ym = yre;
     }
+    void* a0 = nullptr;  // the loss gradient's act copy
+    if (!tb.a0.next(cx, ss, &a0)) return GPIPE_ERR_DEVICE;
     if (io.target) {
       int nblk = 0;
       GP_RUN(cx, GPIPE_ROLE_MSE, mse_fwd_bwd(cx.bf16, ym, cx.act(io.target, m * mb),
-                                             static_cast<float*>(cx.at(p.r0)), cx.at(p.a0),
+                                             static_cast<float*>(cx.at(p.r0)), a0,
                                              msepart + size_t(m) * p.mse_nblk, int64_t(mb),
                                              inv_denom, &nblk, cx.s));
     } else {
-      GP_CHECK(grad_in(cx.bf16, cx.act(io.dy, m * mb), static_cast<float*>(cx.at(p.r0)), cx.at(p.a0),
+      GP_CHECK(grad_in(cx.bf16, cx.act(io.dy, m * mb), static_cast<float*>(cx.at(p.r0)), a0,
                        int64_t(mb), cx.s));
     }
-    WgradDone above;  // the top layer has none above it in this micro-batch
     for (int l = L - 1; l >= 0; --l) {
       // (the layer's input: the output of layer l-1, in that layer's slot when
       // pipelined, else in this layer's X tensor)
       const void* xin = l == 0 ? xm
-                        : piped ? cx.at(saved_at(p, set, slot_of(m, l - 1), GPIPE_SAVED_X))
+                        : piped ? cx.at(saved_at(p, set, cur[l - 1], GPIPE_SAVED_X))
                                 : cx.at(saved_at(p, set, l, GPIPE_SAVED_X));
       void* dxo = (l == 0 && io.dx) ? cx.act(io.dx, m * mb) : nullptr;
-      WgradDone mine;
-      gpipe_status st = layer_backward(cx, ss, above, &mine, set, slot_of(m, l), l, xin,
-                                       m > 0 ? 1 : 0, dxo);
+      gpipe_status st = layer_backward(cx, ss, tb, set, piped ? cur[l] : l, l, xin, m > 0 ? 1 : 0, dxo);
       if (st != GPIPE_OK) return st;
-      above = mine;
-      if (piped && m + 1 < M) {
+      if (piped && m + 1 < M && l >= 1) {
         // layer l's slot is free once its backward (s1) and weight gradients (s2)
         // are done
         if (!ss.fork3()) return GPIPE_ERR_DEVICE;
-        st = remat_layer(cr, m + 1, L - 1 - l);
+        const int j = L - 1 - l;
+        nxt[j] = cur[l];
+        st = remat_layer(cr, nxt, m + 1, j);
         if (st != GPIPE_OK) return st;
+        if (l == 1) {  // the top layer, in the spare slot
+          nxt[L - 1] = spare;
+          st = remat_layer(cr, nxt, m + 1, L - 1);
+          if (st != GPIPE_OK) return st;
+        }
       }
+    }
+    if (piped && m + 1 < M) {
+      spare = cur[0];
+      cur.swap(nxt);
     }
   }
   // the weight gradients (and their bias partial sums) are complete

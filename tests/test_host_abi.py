@@ -86,7 +86,9 @@ def saved_set_bytes_formula(cfg, n, m, eb):
 
 @pytest.mark.parametrize("cfg", [configs.TINY, configs.SMALL, configs.CELL_2048, configs.MEMORY_4096])
 def test_workspace_tracks_the_activation_bound(cfg):
-    """Remat keeps one micro-batch's saved set, no-remat keeps M of them.
+    """Remat keeps one micro-batch's saved set (and, where the backward phase
+    is pipelined -- fused attention, two or more layers -- one spare layer
+    slot for the next micro-batch's top layer), no-remat keeps M of them.
 
     The pages put re-materialized peak activations at O(N + L/K * N/M): the N
     term is the boundary (the caller's x / y), the second term one saved set.
@@ -105,12 +107,15 @@ def test_workspace_tracks_the_activation_bound(cfg):
         # the set is the formula up to 256-byte padding of its 11 tensors per layer
         assert formula <= set_bytes <= formula + 256 * 11 * cfg.layers
         yre = -(-(n // m) * cfg.seq * cfg.d_model * eb // 256) * 256
-        assert keep - remat == (m - 1) * set_bytes - yre
-        # transients are one layer's worth plus each stream's split-K partials,
-        # small next to the set for the big cells
+        spare = set_bytes // cfg.layers if fused_attention(cfg) and cfg.layers >= 2 else 0
+        assert keep - remat == (m - 1) * set_bytes - yre - spare
+        # transients are about one layer's worth (the spare layer slot, two
+        # copies of the gradients the weight-gradient stream reads, the other
+        # backward buffers) plus each stream's split-K partials, small next to
+        # the set for the deep cells
         transient = remat - set_bytes
         assert transient > 0
-        if cfg.layers >= 6:
+        if cfg.layers >= 8:
             assert transient < 0.6 * set_bytes
         # halving the micro-batch halves the set
         if n % (2 * m) == 0:
