@@ -164,6 +164,28 @@ struct Streams {
   }
 };
 
+// A transient gradient of a backward phase that weight gradients on the
+// second stream read: two copies used in turn (workspace offsets), each with
+// the event recorded after the last weight gradient that read it.  The
+// input-gradient chain writes the other copy than the one just read, waiting
+// only for that copy's readers -- from two writes earlier, long done --
+// instead of for the weight-gradient stream to catch up.
+struct Transient {
+  size_t off[2];
+  hipEvent_t read[2] = {nullptr, nullptr};
+  int cur = 0;
+  // switches to the other copy, once its last readers are done (ss null: one
+  // stream, nothing to wait for)
+  bool next(Streams* ss) {
+    cur ^= 1;
+    if (ss && !ss->join(read[cur])) return false;
+    read[cur] = nullptr;
+    return true;
+  }
+  // the weight gradients enqueued so far on the second stream read copy k
+  bool read_by_s2(Streams* ss, int k) { return !ss || ss->mark(&read[k]); }
+};
+
 // Creates the cell's two streams and the event ring at its first step.
 inline gpipe_status ensure_streams(gpipe_cell* c) {
   int dev = -1;

@@ -34,7 +34,9 @@ namespace {
 //   wflip: tap-flipped transposed weights [L][2][C][9][C] (implicit path)
 //   wdup:  weights repeated over split inputs [L][2][C][9][2C] (bf16 cells)
 //   r0:    residual-stream gradient [P, C] (f32);  r1: ReLU-input gradient (f32)
-//   dz:    BN input gradient [P, C] (act, GEMM operand)
+//   dz:    BN input gradient [P, C] (act, GEMM operand), two copies (the
+//          weight gradients on the second stream read one while the
+//          input-gradient chain writes the other)
 //   part, sums: BN reduction partials;  rec: forward-phase moments [M][2L][2][C]
 //   msepart, splitk
 struct CPlan {
@@ -46,7 +48,7 @@ struct CPlan {
   size_t saved_off[GPIPE_CONV_N_SAVED], saved_bytes[GPIPE_CONV_N_SAVED];
   size_t block_bytes, set_bytes;
   int nsets;
-  size_t yre, col, dcol, r0, r1, dz, part, sums, rec, msepart, splitk, wflip, wdup;
+  size_t yre, col, dcol, r0, r1, dz[2], part, sums, rec, msepart, splitk, wflip, wdup;
   bool split;  // bf16 cells: split forward activations (see above)
   // forward-phase lanes (see conv_cell_step): count, and the BN / split-K
   // partials of lanes 1 and 2 (lane 0 uses part and splitk)
@@ -102,7 +104,8 @@ bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
   p->wdup = take(p->split ? size_t(c->L) * 2 * 9 * C * cin * 2 : 0);
   p->r0 = take(P * C * 4);
   p->r1 = take(P * C * 4);
-  p->dz = take(P * C * eb);
+  p->dz[0] = take(P * C * eb);
+  p->dz[1] = take(P * C * eb);
   p->part = take(size_t(bn_chunks(int64_t(P))) * 2 * C * 4);
   p->sums = take(2 * C * 4);
   p->rec = take(size_t(M) * 2 * c->L * 2 * C * 4);
@@ -316,16 +319,16 @@ gpipe_status cell_forward(const CCtx& x, int set, const void* xin, void* yout, f
   return GPIPE_OK;
 }
 
-// Backward of block l.  r0 holds the gradient w.r.t. the block output and is
-// overwritten in place with the gradient w.r.t. its input (dx_out, if given,
-// receives the act copy).
-// With ss (pipelined backward) the two weight gradients run on the second
-// stream: each is enqueued after a fork (dz exists), and the caller's stream
-// waits for the W2 gradient before BN1's backward overwrites dz, and for the
-// block above's W1 gradient (*dz_reader) before BN2's does; *dz_reader
-// becomes this block's W1 gradient event.
-gpipe_status block_backward(const CCtx& x, Streams* ss, hipEvent_t* dz_reader, int set, int slot,
-                            int l, const void* xin, int beta, void* dx_out) {
+// Backward of block l (saved tensors in `slot` of `set`).  On entry r0 holds
+// the gradient w.r.t. the block output (f32); on exit the gradient w.r.t.
+// its input (r0, and dx_out when given).  With streams (ss) the two weight
+// gradients run on the second stream, handed over together after BN1's
+// backward (an event recorded on the caller's stream delays its next launch
+// by several microseconds): W2's reads the copy of dz that BN2's backward
+// wrote, W1's the copy BN1's wrote, and each BatchNorm backward writes the
+// other copy than the last one, waiting only for that copy's readers.
+gpipe_status block_backward(const CCtx& x, Streams* ss, Transient* tdz, int set, int slot, int l,
+                            const void* xin, int beta, void* dx_out) {
   const gpipe_cell* c = x.c;
   const CPlan& p = *x.p;
   const int C = c->C, B = p.B, H = c->Hc, W = c->Wc;
@@ -342,54 +345,54 @@ gpipe_status block_backward(const CCtx& x, Streams* ss, hipEvent_t* dz_reader, i
   if (ss) {
     w.s = ss->s2;
     w.splitk = p.wsplitk;
-    if (!ss->join(*dz_reader)) return GPIPE_ERR_DEVICE;
   }
   float* dcol = x.f(p.dcol);
   float* r0 = x.f(p.r0);
   float* r1 = x.f(p.r1);
-  void* dz = x.at(p.dz);
   float* part = x.f(p.part);
   float* sums = x.f(p.sums);
   int nch = 0;
   // y = x + BN2(z) (the gain and shift gradients, adjacent, accumulate in the same pass)
+  if (!tdz->next(ss)) return GPIPE_ERR_DEVICE;
+  const int k2 = tdz->cur;
+  void* dz2 = x.at(tdz->off[k2]);
   GP_RUN(x, GPIPE_ROLE_BN_BWD, bn_bwd(x.act_kind(), 0, r0, nullptr, SK_F32, z, st2,
                                       x.wf32(l, GPIPE_CONV_BN2_G), part, sums,
-                                      x.grad(l, GPIPE_CONV_BN2_G), beta, dz, P, C, &nch, x.s));
+                                      x.grad(l, GPIPE_CONV_BN2_G), beta, dz2, P, C, &nch, x.s));
   // z = conv(r, W2)
-  hipEvent_t w2 = nullptr;
-  {
-    if (ss && !ss->fork()) return GPIPE_ERR_DEVICE;
-    const gpipe_status st = cwgrad(w, r, r_ld, dz, x.grad(l, GPIPE_CONV_W2), beta);
-    if (st != GPIPE_OK) return st;
-    if (ss && !ss->mark(&w2)) return GPIPE_ERR_DEVICE;
-  }
   if (p.implicit) {
     GP_RUN(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT,
-           cconv(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT, dz, C, x.flipped(l, 1), r1, 0));
+           cconv(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT, dz2, C, x.flipped(l, 1), r1, 0));
   } else {
-    GP_RUN(x, GPIPE_ROLE_CONV_DGRAD, cmm(x, GPIPE_ROLE_CONV_DGRAD, int(P), 9 * C, C, dz, C,
+    GP_RUN(x, GPIPE_ROLE_CONV_DGRAD, cmm(x, GPIPE_ROLE_CONV_DGRAD, int(P), 9 * C, C, dz2, C,
                                          x.wmat(l, GPIPE_CONV_W2), 9 * C, dcol, 9 * C));
     GP_RUN(x, GPIPE_ROLE_COL2IM, col2im(x.bf16, dcol, nullptr, r1, nullptr, B, H, W, C, x.s));
   }
   // r = ReLU(BN1(a))
-  if (ss && !ss->join(w2)) return GPIPE_ERR_DEVICE;
+  if (!tdz->next(ss)) return GPIPE_ERR_DEVICE;
+  const int k1 = tdz->cur;
+  void* dz1 = x.at(tdz->off[k1]);
   GP_RUN(x, GPIPE_ROLE_BN_BWD, bn_bwd(x.act_kind(), 1, r1, r, x.xs_kind(), a, st1,
                                       x.wf32(l, GPIPE_CONV_BN1_G), part, sums,
-                                      x.grad(l, GPIPE_CONV_BN1_G), beta, dz, P, C, &nch, x.s));
-  // a = conv(x, W1); the residual gradient r0 is added in col2im (in place)
+                                      x.grad(l, GPIPE_CONV_BN1_G), beta, dz1, P, C, &nch, x.s));
+  // the weight gradients of W2 and W1 (in that order on the second stream)
+  if (ss && !ss->fork()) return GPIPE_ERR_DEVICE;
   {
-    if (ss && !ss->fork()) return GPIPE_ERR_DEVICE;
-    const gpipe_status st = cwgrad(w, xin, x_ld, dz, x.grad(l, GPIPE_CONV_W1), beta);
+    gpipe_status st = cwgrad(w, r, r_ld, dz2, x.grad(l, GPIPE_CONV_W2), beta);
     if (st != GPIPE_OK) return st;
-    if (ss && !ss->mark(dz_reader)) return GPIPE_ERR_DEVICE;
+    if (!tdz->read_by_s2(ss, k2)) return GPIPE_ERR_DEVICE;
+    st = cwgrad(w, xin, x_ld, dz1, x.grad(l, GPIPE_CONV_W1), beta);
+    if (st != GPIPE_OK) return st;
+    if (!tdz->read_by_s2(ss, k1)) return GPIPE_ERR_DEVICE;
   }
+  // a = conv(x, W1); the residual gradient r0 is added in col2im (in place)
   if (p.implicit) {
     // the residual gradient already in r0 gets the convolution's input gradient added
     GP_RUN(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT,
-           cconv(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT, dz, C, x.flipped(l, 0), r0, 1));
+           cconv(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT, dz1, C, x.flipped(l, 0), r0, 1));
     if (dx_out) GP_CHECK(to_bf16(r0, dx_out, P * C, x.s));
   } else {
-    GP_RUN(x, GPIPE_ROLE_CONV_DGRAD, cmm(x, GPIPE_ROLE_CONV_DGRAD, int(P), 9 * C, C, dz, C,
+    GP_RUN(x, GPIPE_ROLE_CONV_DGRAD, cmm(x, GPIPE_ROLE_CONV_DGRAD, int(P), 9 * C, C, dz1, C,
                                          x.wmat(l, GPIPE_CONV_W1), 9 * C, dcol, 9 * C));
     GP_RUN(x, GPIPE_ROLE_COL2IM, col2im(x.bf16, dcol, r0, r0, dx_out, B, H, W, C, x.s));
   }
@@ -576,16 +579,19 @@ gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void*
     void* out = j == L - 1 ? z.at(p.yre) : z.at(csaved_at(p, 0, sl[j], GPIPE_CONV_SAVED_X));
     return block_forward(z, 0, sl[j], j, in, out, nullptr);
   };
-  hipEvent_t dz_reader = nullptr;  // the last weight gradient that read dz
+  Transient tdz;  // the BatchNorm input gradients the weight gradients read
+  tdz.off[0] = p.dz[0];
+  tdz.off[1] = p.dz[1];
+  Streams* sp = p.piped ? &ss : nullptr;
   for (int m = 0; m < M; ++m) {
     const int set = remat ? 0 : m;
     const void* xm = cx.act(x, m * mb);
     const void* ym = y ? cx.act(y, m * mb) : nullptr;
     if (p.piped) {
-      // the previous micro-batch's weight gradients have read dz and their
-      // slots; this micro-batch's re-materialization is done
-      if (m > 0 && (!ss.join_all() || !ss.join3())) return GPIPE_ERR_DEVICE;
-      dz_reader = nullptr;
+      // this micro-batch's re-materialization is done (the third stream's
+      // forks ordered it after the previous micro-batch's weight gradients
+      // read their slots; dz waits per copy)
+      if (m > 0 && !ss.join3()) return GPIPE_ERR_DEVICE;
       if (m == 0)
         for (int j = 0; j < L; ++j) {
           gpipe_status st = remat_block(cx, 0, j, slots);
@@ -597,13 +603,16 @@ gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void*
       if (st != GPIPE_OK) return st;
       ym = cx.at(p.yre);
     }
+    // (the loss gradient's act copy goes to the next dz copy; the backward reads r0)
+    if (!tdz.next(sp)) return GPIPE_ERR_DEVICE;
     if (target) {
       int nblk = 0;
       GP_RUN(cx, GPIPE_ROLE_MSE, mse_fwd_bwd(cx.bf16, ym, cx.act(target, m * mb), cx.f(p.r0),
-                                             cx.at(p.dz), msepart + size_t(m) * p.mse_nblk,
+                                             cx.at(tdz.off[tdz.cur]), msepart + size_t(m) * p.mse_nblk,
                                              int64_t(mb), inv_denom, &nblk, stream));
     } else {
-      GP_CHECK(grad_in(cx.bf16, cx.act(dy, m * mb), cx.f(p.r0), cx.at(p.dz), int64_t(mb), stream));
+      GP_CHECK(grad_in(cx.bf16, cx.act(dy, m * mb), cx.f(p.r0), cx.at(tdz.off[tdz.cur]), int64_t(mb),
+                       stream));
     }
     const bool next = p.piped && m + 1 < M;
     for (int l = L - 1; l >= 0; --l) {
@@ -611,7 +620,7 @@ gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void*
                         : p.piped ? cx.at(csaved_at(p, set, slots[l - 1], GPIPE_CONV_SAVED_X))
                                   : cx.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_X));
       void* dxo = (l == 0 && dx) ? cx.act(dx, m * mb) : nullptr;
-      gpipe_status st = block_backward(cx, p.piped ? &ss : nullptr, &dz_reader, set, slots[l], l,
+      gpipe_status st = block_backward(cx, sp, &tdz, set, slots[l], l,
                                        xin, m > 0 ? 1 : 0, dxo);
       if (st != GPIPE_OK) return st;
       if (next) {

@@ -495,28 +495,7 @@ gpipe_status overlapped_forward(const Ctx& cx, Streams& ss, const void* x, void*
   return (K < 2 || ss.join_all()) && (K < 3 || ss.join3()) ? GPIPE_OK : GPIPE_ERR_DEVICE;
 }
 
-// A transient gradient of the backward phase that a weight gradient on the
-// second stream reads: two copies used in turn, each with the event recorded
-// after the last weight gradient that read it.  The input-gradient chain
-// writes the other copy than the one just read, waiting only for that copy's
-// readers -- from two writes earlier, long done -- instead of for the
-// weight-gradient stream to catch up.
-struct Transient {
-  size_t off[2];
-  hipEvent_t read[2] = {nullptr, nullptr};
-  int cur = 0;
-  void* now(const Ctx& x) const { return x.at(off[cur]); }
-  // the copy to write next, once its last readers are done
-  bool next(const Ctx& x, Streams& ss, void** out) {
-    cur ^= 1;
-    if (!ss.join(read[cur])) return false;
-    read[cur] = nullptr;
-    *out = x.at(off[cur]);
-    return true;
-  }
-  // the weight gradients enqueued so far on the second stream read this copy
-  bool read_by_s2(Streams& ss) { return ss.mark(&read[cur]); }
-};
+// The four gradients of a layer's backward that weight gradients read.
 struct Transients {
   Transient a0, a1, du, dqkv;
 };
@@ -548,7 +527,7 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, Transients& tb, int set, 
   float* r0 = static_cast<float*>(x.at(p.r0));
   float* r1 = static_cast<float*>(x.at(p.r1));
   float* dm = static_cast<float*>(x.at(p.dm));
-  void* a0 = tb.a0.now(x);
+  void* a0 = x.at(tb.a0.off[tb.a0.cur]);
   void* dctx = x.at(p.dctx);
   void* a1 = nullptr;
   void* du = nullptr;
@@ -567,27 +546,30 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, Transients& tb, int set, 
   // launch by ~7 us (measured in the kernel trace), and the two batches keep
   // the weight gradients in the same order on the second stream.
   bool fused = false;
-  if (!tb.du.next(x, ss, &du)) return GPIPE_ERR_DEVICE;
+  if (!tb.du.next(&ss)) return GPIPE_ERR_DEVICE;
+  du = x.at(tb.du.off[tb.du.cur]);
   GP_RUN(x, GPIPE_ROLE_FFN2_DGRAD, mm(x, GPIPE_ROLE_FFN2_DGRAD, T, F, D, a0, D, x.wmat(l, GPIPE_W_2), F, du, F,
               nullptr, nullptr, 0, u, F));
   if (!ss.fork()) return GPIPE_ERR_DEVICE;  // a0, g and du exist
   GP_RUN(w, GPIPE_ROLE_FFN2_WGRAD, mm_wgrad(w, GPIPE_ROLE_FFN2_WGRAD, l, GPS_B2, D, F, T, a0, D, g, F,
               x.grad(l, GPIPE_W_2), F, beta, &fused));
-  if (!tb.a0.read_by_s2(ss)) return GPIPE_ERR_DEVICE;
+  if (!tb.a0.read_by_s2(&ss, tb.a0.cur)) return GPIPE_ERR_DEVICE;
   if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r0, D, D, x.grad(l, GPIPE_B_2), beta));
   GP_RUN(w, GPIPE_ROLE_FFN1_WGRAD, mm_wgrad(w, GPIPE_ROLE_FFN1_WGRAD, l, GPS_B1, F, D, T, du, F, h2, D,
               x.grad(l, GPIPE_W_1), D, beta, &fused));
-  if (!tb.du.read_by_s2(ss)) return GPIPE_ERR_DEVICE;
+  if (!tb.du.read_by_s2(&ss, tb.du.cur)) return GPIPE_ERR_DEVICE;
   GP_RUN(x, GPIPE_ROLE_FFN1_DGRAD, mm(x, GPIPE_ROLE_FFN1_DGRAD, T, D, F, du, F, x.wmat(l, GPIPE_W_1), D, dm, D));
   if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, du, F, F, x.grad(l, GPIPE_B_1), beta));
   int nblk = 0;
-  if (!tb.a1.next(x, ss, &a1)) return GPIPE_ERR_DEVICE;
+  if (!tb.a1.next(&ss)) return GPIPE_ERR_DEVICE;
+  a1 = x.at(tb.a1.off[tb.a1.cur]);
   GP_RUN(x, GPIPE_ROLE_LN2_BWD, layernorm_bwd(bf, dm, x1, st2, x.wf32(l, GPIPE_LN2_G), r0, r1, a1, ln2part, T, D,
                          beta, &nblk, x.s));
 
   // attention: x1 = x + ctx Wo^T + bo
   GP_RUN(x, GPIPE_ROLE_OUT_DGRAD, mm(x, GPIPE_ROLE_OUT_DGRAD, T, D, D, a1, D, x.wmat(l, GPIPE_W_O), D, dctx, D));
-  if (!tb.dqkv.next(x, ss, &dqkv)) return GPIPE_ERR_DEVICE;
+  if (!tb.dqkv.next(&ss)) return GPIPE_ERR_DEVICE;
+  dqkv = x.at(tb.dqkv.off[tb.dqkv.cur]);
   const int64_t sq = int64_t(S) * 3 * D;
   const int64_t sp = int64_t(H) * S * ldS;
   const int64_t sd = int64_t(S) * D;
@@ -629,17 +611,20 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, Transients& tb, int set, 
   if (!ss.fork()) return GPIPE_ERR_DEVICE;  // a1 and dqkv exist
   GP_RUN(w, GPIPE_ROLE_OUT_WGRAD, mm_wgrad(w, GPIPE_ROLE_OUT_WGRAD, l, GPS_BO, D, D, T, a1, D, ctx, D,
               x.grad(l, GPIPE_W_O), D, beta, &fused));
-  if (!tb.a1.read_by_s2(ss)) return GPIPE_ERR_DEVICE;
+  if (!tb.a1.read_by_s2(&ss, tb.a1.cur)) return GPIPE_ERR_DEVICE;
   if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r1, D, D, x.grad(l, GPIPE_B_O), beta));
   GP_RUN(w, GPIPE_ROLE_QKV_WGRAD, mm_wgrad(w, GPIPE_ROLE_QKV_WGRAD, l, GPS_BQKV, 3 * D, D, T, dqkv, 3 * D, h1,
               D, x.grad(l, GPIPE_W_QKV), D, beta, &fused));
-  if (!tb.dqkv.read_by_s2(ss)) return GPIPE_ERR_DEVICE;
+  if (!tb.dqkv.read_by_s2(&ss, tb.dqkv.cur)) return GPIPE_ERR_DEVICE;
   GP_RUN(x, GPIPE_ROLE_QKV_DGRAD, mm(x, GPIPE_ROLE_QKV_DGRAD, T, D, 3 * D, dqkv, 3 * D, x.wmat(l, GPIPE_W_QKV), D,
               dm, D));
   if (!fused)
     GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, dqkv, 3 * D, 3 * D, x.grad(l, GPIPE_B_QKV), beta));
   void* a0_in = dx_out;  // the gradient w.r.t. the layer input (act)
-  if (!a0_in && !tb.a0.next(x, ss, &a0_in)) return GPIPE_ERR_DEVICE;
+  if (!a0_in) {
+    if (!tb.a0.next(&ss)) return GPIPE_ERR_DEVICE;
+    a0_in = x.at(tb.a0.off[tb.a0.cur]);
+  }
   GP_RUN(x, GPIPE_ROLE_LN1_BWD, layernorm_bwd(bf, dm, xin, st1, x.wf32(l, GPIPE_LN1_G), r1, r0, a0_in,
                          ln1part, T, D, beta, &nblk, x.s));
   return GPIPE_OK;
@@ -807,8 +792,8 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
       if (st != GPIPE_OK) return st;
       ym = yre;
     }
-    void* a0 = nullptr;  // the loss gradient's act copy
-    if (!tb.a0.next(cx, ss, &a0)) return GPIPE_ERR_DEVICE;
+    if (!tb.a0.next(&ss)) return GPIPE_ERR_DEVICE;
+    void* a0 = cx.at(tb.a0.off[tb.a0.cur]);  // the loss gradient's act copy
     if (io.target) {
       int nblk = 0;
       GP_RUN(cx, GPIPE_ROLE_MSE, mse_fwd_bwd(cx.bf16, ym, cx.act(io.target, m * mb),
