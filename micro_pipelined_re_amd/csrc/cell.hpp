@@ -165,19 +165,20 @@ struct Streams {
 };
 
 // A transient gradient of a backward phase that weight gradients on the
-// second stream read: two copies used in turn (workspace offsets), each with
-// the event recorded after the last weight gradient that read it.  The
-// input-gradient chain writes the other copy than the one just read, waiting
-// only for that copy's readers -- from two writes earlier, long done --
-// instead of for the weight-gradient stream to catch up.
+// second stream read: n copies (2 to 4) used in turn (workspace offsets),
+// each with the event recorded after the last weight gradient that read it.
+// The input-gradient chain writes the copy after the one just written,
+// waiting only for that copy's readers -- from n writes earlier -- instead of
+// for the weight-gradient stream to catch up.
 struct Transient {
-  size_t off[2];
-  hipEvent_t read[2] = {nullptr, nullptr};
-  int cur = 0;
-  // switches to the other copy, once its last readers are done (ss null: one
+  static constexpr int kMax = 4;
+  size_t off[kMax];
+  hipEvent_t read[kMax] = {nullptr, nullptr, nullptr, nullptr};
+  int n = 2, cur = 0;
+  // switches to the next copy, once its last readers are done (ss null: one
   // stream, nothing to wait for)
   bool next(Streams* ss) {
-    cur ^= 1;
+    cur = cur + 1 == n ? 0 : cur + 1;
     if (ss && !ss->join(read[cur])) return false;
     read[cur] = nullptr;
     return true;

@@ -34,11 +34,16 @@ namespace {
 //   wflip: tap-flipped transposed weights [L][2][C][9][C] (implicit path)
 //   wdup:  weights repeated over split inputs [L][2][C][9][2C] (bf16 cells)
 //   r0:    residual-stream gradient [P, C] (f32);  r1: ReLU-input gradient (f32)
-//   dz:    BN input gradient [P, C] (act, GEMM operand), two copies (the
-//          weight gradients on the second stream read one while the
-//          input-gradient chain writes the other)
+//   dz:    BN input gradient [P, C] (act, GEMM operand), kDzCopies copies
+//          used in turn (the weight gradients on the second stream read the
+//          two of a block while the input-gradient chain writes the next)
 //   part, sums: BN reduction partials;  rec: forward-phase moments [M][2L][2][C]
 //   msepart, splitk
+// Copies of dz: a block's two BatchNorm backwards each write one, so with four
+// the copy written was last read by the weight gradients of the block two
+// above, which have long finished.
+constexpr int kDzCopies = 4;
+
 struct CPlan {
   int N, M, B;
   bool implicit;  // bf16, channels a multiple of 64: implicit-GEMM convolutions
@@ -48,7 +53,7 @@ struct CPlan {
   size_t saved_off[GPIPE_CONV_N_SAVED], saved_bytes[GPIPE_CONV_N_SAVED];
   size_t block_bytes, set_bytes;
   int nsets;
-  size_t yre, col, dcol, r0, r1, dz[2], part, sums, rec, msepart, splitk, wflip, wdup;
+  size_t yre, col, dcol, r0, r1, dz[4], part, sums, rec, msepart, splitk, wflip, wdup;
   bool split;  // bf16 cells: split forward activations (see above)
   // forward-phase lanes (see conv_cell_step): count, and the BN / split-K
   // partials of lanes 1 and 2 (lane 0 uses part and splitk)
@@ -87,15 +92,18 @@ bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
   p->block_bytes = off;
   p->set_bytes = size_t(c->L) * off;
   p->nsets = remat ? 1 : M;
-  size_t o = size_t(p->nsets) * p->set_bytes;
+  p->implicit = c->prec == GPIPE_BF16 && C % 64 == 0;
+  p->implicit_wgrad = p->implicit && P % 64 == 0 && P < (size_t(1) << 21) &&
+                      (P + 64) * C < (size_t(1) << 31);
+  p->piped = remat && p->implicit_wgrad && c->L >= 2;
+  // pipelined, one spare block slot after the set (block index L): the next
+  // micro-batch's top block is re-materialized there (conv_cell_run)
+  size_t o = size_t(p->nsets) * p->set_bytes + (p->piped ? p->block_bytes : 0);
   auto take = [&](size_t bytes) {
     const size_t at = o;
     o += align_up(bytes, kAlign);
     return at;
   };
-  p->implicit = c->prec == GPIPE_BF16 && C % 64 == 0;
-  p->implicit_wgrad = p->implicit && P % 64 == 0 && P < (size_t(1) << 21) &&
-                      (P + 64) * C < (size_t(1) << 31);
   const size_t cin = p->split ? 2 * C : C;  // channels of a forward convolution's input
   p->yre = take(remat ? P * C * eb : 0);
   p->col = take(!p->implicit ? P * 9 * cin * eb : p->implicit_wgrad ? 0 : P * 9 * C * eb);
@@ -104,8 +112,7 @@ bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
   p->wdup = take(p->split ? size_t(c->L) * 2 * 9 * C * cin * 2 : 0);
   p->r0 = take(P * C * 4);
   p->r1 = take(P * C * 4);
-  p->dz[0] = take(P * C * eb);
-  p->dz[1] = take(P * C * eb);
+  for (int k = 0; k < kDzCopies; ++k) p->dz[k] = take(P * C * eb);
   p->part = take(size_t(bn_chunks(int64_t(P))) * 2 * C * 4);
   p->sums = take(2 * C * 4);
   p->rec = take(size_t(M) * 2 * c->L * 2 * C * 4);
@@ -134,7 +141,6 @@ bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
     p->lane_part[k] = take(k < p->lanes ? size_t(bn_chunks(int64_t(P))) * 2 * C * 4 : 0);
     p->lane_splitk[k] = take(k < p->lanes ? skf * 4 : 0);
   }
-  p->piped = remat && p->implicit_wgrad && c->L >= 2;
   p->wsplitk = take(p->implicit_wgrad && c->L >= 2
                         ? gemm_partial_floats(GPIPE_ROLE_CONV_WGRAD_IMPLICIT, bf, Ci, 9 * Ci, Pi, 1) * 4
                         : 0);
@@ -556,14 +562,16 @@ gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void*
   // phase 2: re-materialize and backpropagate each micro-batch.  Pipelined
   // (p.piped): the weight gradients run on the second stream, and micro-batch
   // m+1 re-materializes on the third while micro-batch m's backward frees the
-  // saved set's block slots, from the top block down: m+1 puts block j in the
-  // slot m's block L-1-j held (odd micro-batches take the slots in reverse
-  // order), each block enqueued after that slot's backward and weight
-  // gradients; a block's output goes to its own slot's X tensor (the next
-  // block's input).  Micro-batch 0 re-materializes on the caller's stream.
+  // saved set's block slots, from the top block down: m+1 puts block j < L-1
+  // in the slot m's block L-1-j held, each block enqueued after that slot's
+  // backward and weight gradients, and its top block in a spare slot right
+  // after block L-2 (the slot m's block 0 frees is the next spare); a block's
+  // output goes to its own slot's X tensor (the next block's input).
+  // Micro-batch 0 re-materializes on the caller's stream.
   const int L = c->L;
   std::vector<int> slots(L), next_slots(L);  // block -> slot, this / next micro-batch
   for (int j = 0; j < L; ++j) slots[j] = j;
+  int spare = L;  // the slot the next micro-batch's top block takes
   Streams ss{c, stream, c->aux, c->aux2};
   CCtx cr = cx;  // the re-materialization's context on the third stream
   if (p.piped) {
@@ -580,8 +588,8 @@ gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void*
     return block_forward(z, 0, sl[j], j, in, out, nullptr);
   };
   Transient tdz;  // the BatchNorm input gradients the weight gradients read
-  tdz.off[0] = p.dz[0];
-  tdz.off[1] = p.dz[1];
+  tdz.n = kDzCopies;
+  for (int k = 0; k < kDzCopies; ++k) tdz.off[k] = p.dz[k];
   Streams* sp = p.piped ? &ss : nullptr;
   for (int m = 0; m < M; ++m) {
     const int set = remat ? 0 : m;
@@ -623,16 +631,25 @@ gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void*
       gpipe_status st = block_backward(cx, sp, &tdz, set, slots[l], l,
                                        xin, m > 0 ? 1 : 0, dxo);
       if (st != GPIPE_OK) return st;
-      if (next) {
+      if (next && l >= 1) {
         // block l's slot is free once its backward (s1) and weight gradients
         // (s2) are done
-        next_slots[L - 1 - l] = slots[l];
+        const int j = L - 1 - l;
+        next_slots[j] = slots[l];
         if (!ss.fork3()) return GPIPE_ERR_DEVICE;
-        st = remat_block(cr, m + 1, L - 1 - l, next_slots);
+        st = remat_block(cr, m + 1, j, next_slots);
         if (st != GPIPE_OK) return st;
+        if (l == 1) {  // the top block, in the spare slot
+          next_slots[L - 1] = spare;
+          st = remat_block(cr, m + 1, L - 1, next_slots);
+          if (st != GPIPE_OK) return st;
+        }
       }
     }
-    if (next) slots.swap(next_slots);
+    if (next) {
+      spare = slots[0];  // freed by this micro-batch's block 0
+      slots.swap(next_slots);
+    }
   }
   // the weight gradients are complete
   if (p.piped && !ss.join_all()) return GPIPE_ERR_DEVICE;
