@@ -91,13 +91,15 @@ __device__ __forceinline__ bf16x8_t pack8(const float* v) {
 // probabilities that are negligible next to the row's largest one (1).
 __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// A 64 x DH tile of a [rows][ld] bf16 matrix, staged through registers by
-// the 256 threads of one wave group (t = thread index inside the group).
-// Rows >= nrows read as zeros.  (Clamping the row instead, which removes the
-// branches, made the kernels 50% slower on gfx950: the compiler then waited
-// for each tile's loads right after issuing them.)
+// This thread's 16-byte chunks of a 64 x DH tile of a [rows][ld] bf16
+// matrix, held in registers (256 threads of one wave group: chunk t + 256 i
+// is column chunk (t + 256 i) % CPR of row (t + 256 i) / CPR).  Rows at or
+// past nrows read row nrows - 1: the loads need no branch, so the compiler
+// keeps an exact count of the loads in flight and does not wait for them
+// before their first use (rows past the sequence carry a zero probability
+// wherever these values enter).
 template <int DH>
-struct TileLoad {
+struct TileRows {
   static constexpr int CPR = DH / 8;                 // 16-byte chunks per row
   static constexpr int PER = kBlk * CPR / 256;       // per thread
   uint4 v[PER];
@@ -105,17 +107,108 @@ struct TileLoad {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int cid = t + 256 * i;
-      const int r = cid / CPR, c = cid % CPR;
-      v[i] = make_uint4(0, 0, 0, 0);
-      if (r0 + r < nrows) v[i] = *reinterpret_cast<const uint4*>(base + int64_t(r0 + r) * ld + c * 8);
+      const int r = min(r0 + cid / CPR, nrows - 1), c = cid % CPR;
+      v[i] = *reinterpret_cast<const uint4*>(base + int64_t(r) * ld + c * 8);
     }
   }
-  __device__ __forceinline__ void store(bf16_t* tl, int t) const {
+};
+
+// An integer the optimizer cannot look into (an empty asm that may change it).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Per-lane byte offsets of the fragment reads inside a 64 x DH tile.  With
+// them every read in a loop is tile + offset + constant: the compiler then
+// still knows which LDS variable the read touches (it follows only a few
+// address steps), so a read of one buffer does not wait for the loads
+// streaming into the other.  row[ks]: frag_row(t * 16 + ln, ks * 4 + g) at
+// row[ks] + 32 t DH bytes.  tr[i]: the transposing reads of frag_tr(rlo,
+// rhi, 16 i) at tr[i] + 2 rlo DH and tr[i] + 2 rhi DH bytes (rlo, rhi
+// multiples of 8, where the swizzle of a row repeats).
+template <int DH>
+struct FragOffsets {
+  static constexpr int KS = DH / 32, DT = DH / 16;
+  int row[KS], tr[DT];
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 4, s = lane & 15;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int cid = t + 256 * i;
-      const int r = cid / CPR, c = cid % CPR;
-      *reinterpret_cast<uint4*>(tl + toff<DH>(r, c * 8)) = v[i];
+    for (int ks = 0; ks < KS; ++ks) row[ks] = opaque(2 * toff<DH>(s, (ks * 4 + g) * 8));
+#pragma unroll
+    for (int i = 0; i < DT; ++i) tr[i] = opaque(2 * toff<DH>(4 * g + (s >> 2), i * 16 + 4 * (s & 3)));
+  }
+};
+
+template <int DH>
+__device__ __forceinline__ bf16x8_t frag_row_at(const bf16_t* tile, int off, int t) {
+  return *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const char*>(tile) + off + 32 * t * DH);
+}
+
+template <int DH>
+__device__ __forceinline__ bf16x8_t frag_tr_at(const bf16_t* tile, int off, int rlo, int rhi) {
+  const char* p = reinterpret_cast<const char*>(tile) + off;
+  const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p + 2 * rlo * DH));
+  const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p + 2 * rhi * DH));
+  const short8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// s_waitcnt vmcnt(0), the other counters left alone (gfx9 encoding).  Loads
+// guarded by a branch leave the compiler unsure how many are in flight, so
+// its first use of a register loaded before a loop waits for every load,
+// the loop's own prefetch of the next block included; waiting once for the
+// loads issued before the loop clears them from that count.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// A wave group's share of a 64 x DH tile of a [rows][ld] bf16 matrix loaded
+// straight into LDS (global_load_lds_dwordx4, no registers in between).
+// Instruction i of group wave wl fills 1 KB of the tile: its 64 lanes write
+// consecutive 16-byte chunks, i.e. RPI whole rows, lane l chunk position
+// l % CPR of row l / CPR.  Each lane fetches the chunk of global columns
+// that the tile's granule swizzle places at that position.  Rows at or past
+// nrows read row nrows - 1 (valid memory): keys past the sequence get a
+// masked score and a zero probability, so their finite values never count.
+template <int DH>
+struct TileDma {
+  static constexpr int CPR = DH / 8;           // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;         // rows per instruction
+  static constexpr int IPW = kBlk / RPI / 4;   // instructions per wave and tile
+  static constexpr int NG = DH / 16;           // 32-byte granules per row
+  int row[IPW], col[IPW];
+  uint32_t off[IPW];  // byte offset of the lane's chunk from the tile's first row
+  int64_t ld;         // row stride (elements) of the matrices this loader reads
+  __device__ __forceinline__ void init(int wl, int lane, int64_t ld_) {
+    ld = ld_;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int r = (wl * IPW + i) * RPI + lane / CPR, pc = lane % CPR;
+      const int f = (DH >= 128) ? (r & 7) : ((r >> 1) & 3);
+      row[i] = r;
+      col[i] = ((((pc >> 1) ^ f) & (NG - 1)) << 4) + (pc & 1) * 8;
+      off[i] = uint32_t(r * int(ld_) + col[i]) * 2u;
+    }
+  }
+  // rows r0 .. r0+63 of base (row stride ld); wl must be wave-uniform (the
+  // LDS address of a load is)
+  __device__ __forceinline__ void load(const bf16_t* base, int r0, int nrows, bf16_t* tile,
+                                       int wl) const {
+    if (r0 + kBlk <= nrows) {
+      const char* b0 = reinterpret_cast<const char*>(base + int64_t(r0) * ld);
+#pragma unroll
+      for (int i = 0; i < IPW; ++i)
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(b0 + off[i]),
+                                         (lds_void_t*)(tile + (wl * IPW + i) * 512), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int r = min(r0 + row[i], nrows - 1);
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + int64_t(r) * ld + col[i]),
+                                         (lds_void_t*)(tile + (wl * IPW + i) * 512), 16, 0, 0);
+      }
     }
   }
 };
@@ -138,19 +231,22 @@ __device__ __forceinline__ bf16x8_t gfrag(const bf16_t* base, int64_t ld, int ro
 // joins the barrier), so every barrier is reached by all 512 threads.
 constexpr int kGroups = 2;
 
-// dynamic LDS of the kernels: [group][buffer][2 tiles] bf16, then (dK/dV
-// kernel) [group][buffer][2][64] float row statistics
+// LDS of the kernels (static, declared in each kernel): two tile buffers,
+// each [group][2 tiles] bf16, and for the dK/dV blocks two [group][2][64]
+// float row-statistics buffers.  Each buffer is a variable of its own (see
+// FragOffsets).
 template <int DH>
 constexpr int attn_tile_elems() { return kBlk * DH; }
-template <int DH>
-constexpr int attn_smem_bytes() {
-  return kGroups * 2 * 2 * attn_tile_elems<DH>() * 2 + kGroups * 2 * 2 * kBlk * 4;
-}
-
-extern __shared__ __attribute__((aligned(16))) bf16_t attn_smem[];
 
 // ------------------------------------------------------------------ forward
 // grid (B*H, query blocks); qkv [B*S][3D], ctx [B*S][D], lse2 [B*H][S].
+//
+// The key/value tiles go straight from memory into LDS, one block ahead:
+// while a group computes on one buffer, its next tiles stream into the
+// other.  The two buffers are separate LDS variables and the loop body is
+// written out once per buffer, so the compiler can see that the reads of
+// one buffer do not depend on the loads into the other (with one array and
+// a computed buffer index it waits for every load before the first read).
 template <int DH, bool CLIP>
 __global__ __launch_bounds__(512) void flash_fwd_kernel(const bf16_t* __restrict__ qkv,
                                                         bf16_t* __restrict__ ctx,
@@ -159,9 +255,12 @@ __global__ __launch_bounds__(512) void flash_fwd_kernel(const bf16_t* __restrict
   constexpr int KS = DH / 32;   // k steps over the head dimension
   constexpr int DT = DH / 16;   // 16-column output tiles
   constexpr int TE = attn_tile_elems<DH>();
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, ln = lane & 15;
-  const int grp = w >> 2, wl = w & 3, gt = threadIdx.x & 255;
-  bf16_t* gbase = attn_smem + grp * 4 * TE;  // [buffer][K, V]
+  // [group][K, V] tiles of buffer 0 and of buffer 1
+  __shared__ __attribute__((aligned(16))) bf16_t buf0[kGroups * 2 * TE];
+  __shared__ __attribute__((aligned(16))) bf16_t buf1[kGroups * 2 * TE];
+  const int lane = threadIdx.x & 63, g = lane >> 4, ln = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int grp = w >> 2, wl = w & 3;
   const int nqb = (S + kBlk - 1) / kBlk;
   const int qb = nqb - 1 - int(blockIdx.y);  // longest causal rows first
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
@@ -170,6 +269,16 @@ __global__ __launch_bounds__(512) void flash_fwd_kernel(const bf16_t* __restrict
   const bf16_t* Kg = Qg + D;
   const bf16_t* Vg = Qg + 2 * D;
   const int q = qb * kBlk + wl * 16 + ln;  // this lane's query (column of S^T)
+  const int nkb = causal ? min(qb + 1, (S + kBlk - 1) / kBlk) : (S + kBlk - 1) / kBlk;
+  const int iters = (nkb + kGroups - 1) / kGroups;
+  // the first key/value tiles are requested before the queries, so the two
+  // memory round trips overlap
+  TileDma<DH> dm;
+  dm.init(wl, lane, ld);
+  if (grp < nkb) {
+    dm.load(Kg, grp * kBlk, S, buf0 + grp * 2 * TE, wl);
+    dm.load(Vg, grp * kBlk, S, buf0 + grp * 2 * TE + TE, wl);
+  }
   bf16x8_t qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qf[ks] = gfrag(Qg, ld, q, S, ks * 32 + 8 * g);
@@ -178,47 +287,42 @@ __global__ __launch_bounds__(512) void flash_fwd_kernel(const bf16_t* __restrict
 #pragma unroll
   for (int i = 0; i < DT; ++i) o[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  const int nkb = causal ? min(qb + 1, (S + kBlk - 1) / kBlk) : (S + kBlk - 1) / kBlk;
-  const int iters = (nkb + kGroups - 1) / kGroups;
-  TileLoad<DH> lk, lv;
-  if (grp < nkb) {
-    lk.load(Kg, ld, grp * kBlk, S, gt);
-    lv.load(Vg, ld, grp * kBlk, S, gt);
-  }
-  for (int it = 0; it < iters; ++it) {
+  // iteration `it` on this group's tiles in `cur`, the next ones into `nxt`
+  auto step = [&](int it, bf16_t* cur, bf16_t* nxt) __attribute__((always_inline)) {
     const int kb = kGroups * it + grp;
-    const bool have = kb < nkb;
-    bf16_t* kt = gbase + (it & 1) * 2 * TE;
-    bf16_t* vt = kt + TE;
-    if (have) {
-      lk.store(kt, gt);
-      lv.store(vt, gt);
-    }
+    const bf16_t* kt = cur;
+    const bf16_t* vt = cur + TE;
+    // this wave's share of the tiles has landed; after the barrier every
+    // share has, and every wave is done with the other buffer
+    wait_vm_all();
     __syncthreads();
-    if (kb + kGroups < nkb) {
-      lk.load(Kg, ld, (kb + kGroups) * kBlk, S, gt);
-      lv.load(Vg, ld, (kb + kGroups) * kBlk, S, gt);
-    }
-    if (!have) continue;
-    // S^T tile t: keys 16t + 4g + v, query q.  Every LDS read of the score
-    // product, and of the first 32 keys' V fragments, is issued before the
-    // first MFMA (otherwise each MFMA waits for its own read's round trip).
+    const bool more = kb + kGroups < nkb;
+    if (kb >= nkb) return;
+    // S^T tile t: keys 16t + 4g + v, query q.  Every LDS read of the block
+    // is issued before the first MFMA (otherwise each MFMA waits for its own
+    // read's round trip), and before the next tiles are requested: the
+    // transposing reads carry no alias information, so one issued after the
+    // request would wait for it.
     floatx4_t st[4];
-    bf16x8_t kfr[4][KS], vfr[DT];
+    bf16x8_t kfr[4][KS], vfr[DT], vfr1[DT];
+#pragma unroll
+    for (int i = 0; i < DT; ++i) vfr[i] = frag_tr<DH>(vt, 0, 16, i * 16, lane);
+#pragma unroll
+    for (int i = 0; i < DT; ++i) vfr1[i] = frag_tr<DH>(vt, 32, 48, i * 16, lane);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kfr[t][ks] = frag_row<DH>(kt, t * 16 + ln, ks * 4 + g);
-#pragma unroll
-    for (int i = 0; i < DT; ++i) vfr[i] = frag_tr<DH>(vt, 0, 16, i * 16, lane);
+    if (more) {
+      dm.load(Kg, (kb + kGroups) * kBlk, S, nxt, wl);
+      dm.load(Vg, (kb + kGroups) * kBlk, S, nxt + TE, wl);
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) st[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int t = 0; t < 4; ++t) st[t] = mfma(kfr[t][ks], qf[ks], st[t]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * KS + 2 * DT, 0);  // the LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * KS, 0);           // then the MFMAs
     if constexpr (CLIP)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -268,23 +372,23 @@ __global__ __launch_bounds__(512) void flash_fwd_kernel(const bf16_t* __restrict
     for (int i = 0; i < DT; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) o[i][v] *= av[v];
-    // O += P V over two 32-key halves (the second half's V fragments are
-    // read before the first half's MFMAs)
+    // O += P V over the two 32-key halves
     const float pv0[8] = {st[0][0], st[0][1], st[0][2], st[0][3], st[1][0], st[1][1], st[1][2], st[1][3]};
     const float pv1[8] = {st[2][0], st[2][1], st[2][2], st[2][3], st[3][0], st[3][1], st[3][2], st[3][3]};
     const bf16x8_t pa0 = pack8(pv0), pa1 = pack8(pv1);
-    bf16x8_t vfr1[DT];
-#pragma unroll
-    for (int i = 0; i < DT; ++i) vfr1[i] = frag_tr<DH>(vt, 32, 48, i * 16, lane);
 #pragma unroll
     for (int i = 0; i < DT; ++i) o[i] = mfma(pa0, vfr[i], o[i]);
 #pragma unroll
     for (int i = 0; i < DT; ++i) o[i] = mfma(pa1, vfr1[i], o[i]);
+  };
+  for (int it = 0; it < iters; it += 2) {
+    step(it, buf0 + grp * 2 * TE, buf1 + grp * 2 * TE);
+    if (it + 1 < iters) step(it + 1, buf1 + grp * 2 * TE, buf0 + grp * 2 * TE);
   }
   // combine the groups: per wave slot [DT*4][64] group 1's output, then
   // m[group][16], l[group][16] of the wave's 16 queries
   __syncthreads();
-  float* slot = reinterpret_cast<float*>(attn_smem) + wl * (DT * 256 + 64);
+  float* slot = reinterpret_cast<float*>(buf0) + wl * (DT * 256 + 64);
   float* stat = slot + DT * 256;
   if (grp == 1)
 #pragma unroll
@@ -327,21 +431,25 @@ __global__ __launch_bounds__(512) void flash_fwd_kernel(const bf16_t* __restrict
 }
 
 // ------------------------------------------------------------------ backward
+// The tiles a block's loop visits go straight from memory into LDS, one
+// block ahead, into the buffer the group is not reading (as in the forward);
+// the loop body is written out once per buffer.
+
 // dK, dV for key block kbk of (sequence, head) bh; the groups split the
 // query blocks, and each computes the row sums delta = rowsum(dO * O) of the
-// query blocks it visits from the dO and O tiles it loads.
+// query blocks it visits from dO and O rows it holds in registers.
 template <int DH, bool CLIP>
 __device__ __forceinline__ void flash_dkdv_body(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ ctx,
     const bf16_t* __restrict__ dctx, const float* __restrict__ lse2, bf16_t* __restrict__ dqkv,
-    int S, int H, int D, int causal, float sl2, float scale, float craw, int bh, int kbk) {
+    int S, int H, int D, int causal, float sl2, float scale, float craw, int bh, int kbk,
+    bf16_t* buf0, bf16_t* buf1, float* sta0, float* sta1) {
   constexpr int KS = DH / 32;
   constexpr int DT = DH / 16;
   constexpr int TE = attn_tile_elems<DH>();
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, ln = lane & 15;
+  const int lane = threadIdx.x & 63, g = lane >> 4, ln = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int grp = w >> 2, wl = w & 3, gt = threadIdx.x & 255;
-  bf16_t* gbase = attn_smem + grp * 4 * TE;  // [buffer][Q, dO]
-  float* sbase = reinterpret_cast<float*>(attn_smem + kGroups * 4 * TE) + grp * 4 * kBlk;  // [buffer][lse, delta][64]
   const int nb = (S + kBlk - 1) / kBlk;
   const int b = bh / H, h = bh % H;
   const int64_t ld = 3 * int64_t(D);
@@ -352,50 +460,53 @@ __device__ __forceinline__ void flash_dkdv_body(
   const float* Lg = lse2 + int64_t(bh) * S;
   const bf16_t* Cg = ctx + int64_t(b) * S * D + h * DH;
   const int key = kbk * kBlk + wl * 16 + ln;  // this lane's key (column of S)
+  const int q_first = causal ? kbk : 0;
+  const int nqb = nb - q_first;
+  const int iters = (nqb + kGroups - 1) / kGroups;
+  TileDma<DH> dmq, dmo;  // Q (row stride 3D) and dO (row stride D) tiles
+  dmq.init(wl, lane, ld);
+  dmo.init(wl, lane, D);
+  TileRows<DH> ro, rc;  // dO and O rows of a query block (for delta)
+  float lsv = 0.f;      // lse of row gt of the block (wave 0 of each group)
+  // requests query block qb: Q and dO tiles into `tiles`, dO, O rows and the
+  // block's lse values into registers
+  auto request = [&](int qb, bf16_t* tiles) __attribute__((always_inline)) {
+    dmq.load(Qg, qb * kBlk, S, tiles, wl);
+    dmo.load(Og, qb * kBlk, S, tiles + TE, wl);
+    ro.load(Og, D, qb * kBlk, S, gt);
+    rc.load(Cg, D, qb * kBlk, S, gt);
+    if (wl == 0) lsv = Lg[min(qb * kBlk + gt, S - 1)];
+  };
+  if (grp < nqb) request(q_first + grp, buf0 + grp * 2 * TE);
   bf16x8_t kf[KS], vf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     kf[ks] = gfrag(Kg, ld, key, S, ks * 32 + 8 * g);
     vf[ks] = gfrag(Vg, ld, key, S, ks * 32 + 8 * g);
   }
+  FragOffsets<DH> fo;
+  fo.init(lane);
   floatx4_t dk[DT], dv[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) dk[i] = dv[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  const int q_first = causal ? kbk : 0;
-  const int nqb = nb - q_first;
-  const int iters = (nqb + kGroups - 1) / kGroups;
-  TileLoad<DH> lq, lo, lc;  // Q, dO and O of a query block
-  float lsv = 0.f;
-  auto load_blk = [&](int qb) {
-    lq.load(Qg, ld, qb * kBlk, S, gt);
-    lo.load(Og, D, qb * kBlk, S, gt);
-    lc.load(Cg, D, qb * kBlk, S, gt);
-    if (gt < kBlk) {
-      const int qq = qb * kBlk + gt;
-      lsv = qq < S ? Lg[qq] : INFINITY;
-    }
-  };
-  if (grp < nqb) load_blk(q_first + grp);
-  for (int it = 0; it < iters; ++it) {
+  auto step = [&](int it, bf16_t* cur, bf16_t* nxt, float* ls_s) __attribute__((always_inline)) {
     const int qi = kGroups * it + grp;  // index into this key block's query blocks
     const bool have = qi < nqb;
     const int qb = q_first + qi;
-    bf16_t* qt = gbase + (it & 1) * 2 * TE;
-    bf16_t* ot = qt + TE;
-    float* ls_s = sbase + (it & 1) * 2 * kBlk;
+    const bf16_t* qt = cur;
+    const bf16_t* ot = cur + TE;
     float* dl_s = ls_s + kBlk;
+    wait_vm_all();  // this wave's requests for the block have landed
     if (have) {
-      lq.store(qt, gt);
-      lo.store(ot, gt);
-      if (gt < kBlk) ls_s[gt] = lsv;
+      if (wl == 0) ls_s[gt] = qb * kBlk + gt < S ? lsv : INFINITY;
       // delta = rowsum(dO * O) of the block's rows: chunk i of this thread is
       // 8 columns of row (gt + 256 i) / CPR, the CPR consecutive threads of a
       // row add their dot products in a fixed butterfly
-      constexpr int CPR = TileLoad<DH>::CPR;
+      constexpr int CPR = TileRows<DH>::CPR;
 #pragma unroll
-      for (int i = 0; i < TileLoad<DH>::PER; ++i) {
-        const uint32_t av[4] = {lo.v[i].x, lo.v[i].y, lo.v[i].z, lo.v[i].w};
-        const uint32_t cv[4] = {lc.v[i].x, lc.v[i].y, lc.v[i].z, lc.v[i].w};
+      for (int i = 0; i < TileRows<DH>::PER; ++i) {
+        const uint32_t av[4] = {ro.v[i].x, ro.v[i].y, ro.v[i].z, ro.v[i].w};
+        const uint32_t cv[4] = {rc.v[i].x, rc.v[i].y, rc.v[i].z, rc.v[i].w};
         float dsum = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -408,8 +519,8 @@ __device__ __forceinline__ void flash_dkdv_body(
       }
     }
     __syncthreads();
-    if (qi + kGroups < nqb) load_blk(qb + kGroups);
-    if (!have) continue;
+    if (qi + kGroups < nqb) request(qb + kGroups, nxt);
+    if (!have) return;
     // S and dP tiles t: rows (queries) 16t + 4g + v, column (key) `key`
     floatx4_t sp[4], dp[4];
 #pragma unroll
@@ -417,8 +528,8 @@ __device__ __forceinline__ void flash_dkdv_body(
       sp[t] = dp[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        sp[t] = mfma(frag_row<DH>(qt, t * 16 + ln, ks * 4 + g), kf[ks], sp[t]);
-        dp[t] = mfma(frag_row<DH>(ot, t * 16 + ln, ks * 4 + g), vf[ks], dp[t]);
+        sp[t] = mfma(frag_row_at<DH>(qt, fo.row[ks], t), kf[ks], sp[t]);
+        dp[t] = mfma(frag_row_at<DH>(ot, fo.row[ks], t), vf[ks], dp[t]);
       }
     }
     const int q0 = qb * kBlk;
@@ -444,14 +555,18 @@ __device__ __forceinline__ void flash_dkdv_body(
       const bf16x8_t pa = pack8(pv), sa = pack8(sv);
 #pragma unroll
       for (int i = 0; i < DT; ++i) {
-        dv[i] = mfma(pa, frag_tr<DH>(ot, 32 * k2, 32 * k2 + 16, i * 16, lane), dv[i]);
-        dk[i] = mfma(sa, frag_tr<DH>(qt, 32 * k2, 32 * k2 + 16, i * 16, lane), dk[i]);
+        dv[i] = mfma(pa, frag_tr_at<DH>(ot, fo.tr[i], 32 * k2, 32 * k2 + 16), dv[i]);
+        dk[i] = mfma(sa, frag_tr_at<DH>(qt, fo.tr[i], 32 * k2, 32 * k2 + 16), dk[i]);
       }
     }
+  };
+  for (int it = 0; it < iters; it += 2) {
+    step(it, buf0 + grp * 2 * TE, buf1 + grp * 2 * TE, sta0 + grp * 2 * kBlk);
+    if (it + 1 < iters) step(it + 1, buf1 + grp * 2 * TE, buf0 + grp * 2 * TE, sta1 + grp * 2 * kBlk);
   }
   // combine: group 1's dK, dV through LDS (per wave [2][DT*4][64]), added to group 0's
   __syncthreads();
-  float* slot = reinterpret_cast<float*>(attn_smem) + wl * (2 * DT * 256);
+  float* slot = reinterpret_cast<float*>(buf0) + wl * (2 * DT * 256);
   if (grp == 1)
 #pragma unroll
     for (int i = 0; i < DT; ++i)
@@ -484,13 +599,14 @@ template <int DH, bool CLIP>
 __device__ __forceinline__ void flash_dq_body(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ ctx,
     const bf16_t* __restrict__ dctx, const float* __restrict__ lse2, bf16_t* __restrict__ dqkv,
-    int S, int H, int D, int causal, float sl2, float scale, float craw, int bh, int qb) {
+    int S, int H, int D, int causal, float sl2, float scale, float craw, int bh, int qb,
+    bf16_t* buf0, bf16_t* buf1) {
   constexpr int KS = DH / 32;
   constexpr int DT = DH / 16;
   constexpr int TE = attn_tile_elems<DH>();
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, ln = lane & 15;
-  const int grp = w >> 2, wl = w & 3, gt = threadIdx.x & 255;
-  bf16_t* gbase = attn_smem + grp * 4 * TE;  // [buffer][K, V]
+  const int lane = threadIdx.x & 63, g = lane >> 4, ln = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int grp = w >> 2, wl = w & 3;
   const int nb = (S + kBlk - 1) / kBlk;
   const int b = bh / H, h = bh % H;
   const int64_t ld = 3 * int64_t(D);
@@ -499,6 +615,14 @@ __device__ __forceinline__ void flash_dq_body(
   const bf16_t* Vg = Qg + 2 * D;
   const bf16_t* Og = dctx + int64_t(b) * S * D + h * DH;
   const int q = qb * kBlk + wl * 16 + ln;  // this lane's query (column of S^T)
+  const int nkb = causal ? min(qb + 1, nb) : nb;
+  const int iters = (nkb + kGroups - 1) / kGroups;
+  TileDma<DH> dm;
+  dm.init(wl, lane, ld);
+  if (grp < nkb) {
+    dm.load(Kg, grp * kBlk, S, buf0 + grp * 2 * TE, wl);
+    dm.load(Vg, grp * kBlk, S, buf0 + grp * 2 * TE + TE, wl);
+  }
   bf16x8_t qf[KS], of[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -518,31 +642,22 @@ __device__ __forceinline__ void flash_dq_body(
     dq_ += __shfl_xor(dq_, 16, 64);
     dq_ += __shfl_xor(dq_, 32, 64);
   }
+  FragOffsets<DH> fo;
+  fo.init(lane);
   floatx4_t acc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  const int nkb = causal ? min(qb + 1, nb) : nb;
-  const int iters = (nkb + kGroups - 1) / kGroups;
-  TileLoad<DH> lk, lv;
-  if (grp < nkb) {
-    lk.load(Kg, ld, grp * kBlk, S, gt);
-    lv.load(Vg, ld, grp * kBlk, S, gt);
-  }
-  for (int it = 0; it < iters; ++it) {
+  auto step = [&](int it, bf16_t* cur, bf16_t* nxt) __attribute__((always_inline)) {
     const int kb = kGroups * it + grp;
-    const bool have = kb < nkb;
-    bf16_t* kt = gbase + (it & 1) * 2 * TE;
-    bf16_t* vt = kt + TE;
-    if (have) {
-      lk.store(kt, gt);
-      lv.store(vt, gt);
-    }
+    const bf16_t* kt = cur;
+    const bf16_t* vt = cur + TE;
+    wait_vm_all();  // this wave's share of the tiles has landed
     __syncthreads();
     if (kb + kGroups < nkb) {
-      lk.load(Kg, ld, (kb + kGroups) * kBlk, S, gt);
-      lv.load(Vg, ld, (kb + kGroups) * kBlk, S, gt);
+      dm.load(Kg, (kb + kGroups) * kBlk, S, nxt, wl);
+      dm.load(Vg, (kb + kGroups) * kBlk, S, nxt + TE, wl);
     }
-    if (!have) continue;
+    if (kb >= nkb) return;
     // S^T and dP^T tiles t: rows (keys) 16t + 4g + v, column (query) q
     floatx4_t st[4], dpt[4];
 #pragma unroll
@@ -550,8 +665,8 @@ __device__ __forceinline__ void flash_dq_body(
       st[t] = dpt[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        st[t] = mfma(frag_row<DH>(kt, t * 16 + ln, ks * 4 + g), qf[ks], st[t]);
-        dpt[t] = mfma(frag_row<DH>(vt, t * 16 + ln, ks * 4 + g), of[ks], dpt[t]);
+        st[t] = mfma(frag_row_at<DH>(kt, fo.row[ks], t), qf[ks], st[t]);
+        dpt[t] = mfma(frag_row_at<DH>(vt, fo.row[ks], t), of[ks], dpt[t]);
       }
     }
     const int k0 = kb * kBlk;
@@ -573,12 +688,16 @@ __device__ __forceinline__ void flash_dq_body(
       const bf16x8_t sa = pack8(sv);
 #pragma unroll
       for (int i = 0; i < DT; ++i)
-        acc[i] = mfma(sa, frag_tr<DH>(kt, 32 * k2, 32 * k2 + 16, i * 16, lane), acc[i]);
+        acc[i] = mfma(sa, frag_tr_at<DH>(kt, fo.tr[i], 32 * k2, 32 * k2 + 16), acc[i]);
     }
+  };
+  for (int it = 0; it < iters; it += 2) {
+    step(it, buf0 + grp * 2 * TE, buf1 + grp * 2 * TE);
+    if (it + 1 < iters) step(it + 1, buf1 + grp * 2 * TE, buf0 + grp * 2 * TE);
   }
   // combine: group 1's dQ through LDS (per wave [DT*4][64]), added to group 0's
   __syncthreads();
-  float* slot = reinterpret_cast<float*>(attn_smem) + wl * (DT * 256);
+  float* slot = reinterpret_cast<float*>(buf0) + wl * (DT * 256);
   if (grp == 1)
 #pragma unroll
     for (int i = 0; i < DT; ++i)
@@ -607,34 +726,19 @@ __global__ __launch_bounds__(512) void flash_bwd_kernel(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ ctx,
     const bf16_t* __restrict__ dctx, const float* __restrict__ lse2, bf16_t* __restrict__ dqkv,
     int S, int H, int D, int causal, float sl2, float scale, float craw) {
+  constexpr int TE = attn_tile_elems<DH>();
+  __shared__ __attribute__((aligned(16))) bf16_t buf0[kGroups * 2 * TE];
+  __shared__ __attribute__((aligned(16))) bf16_t buf1[kGroups * 2 * TE];
+  __shared__ float sta0[kGroups * 2 * kBlk];  // [group][lse, delta][64]
+  __shared__ float sta1[kGroups * 2 * kBlk];
   const int nb = (S + kBlk - 1) / kBlk;
   const int y = int(blockIdx.y), bh = int(blockIdx.x);
   if (y < nb)
     flash_dq_body<DH, CLIP>(qkv, ctx, dctx, lse2, dqkv, S, H, D, causal, sl2, scale, craw, bh,
-                            nb - 1 - y);
+                            nb - 1 - y, buf0, buf1);
   else
     flash_dkdv_body<DH, CLIP>(qkv, ctx, dctx, lse2, dqkv, S, H, D, causal, sl2, scale, craw, bh,
-                              y - nb);
-}
-
-// Sets the dynamic-LDS limit of a kernel once.
-template <class K>
-hipError_t allow_smem(K kernel, int bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
-
-template <int DH>
-hipError_t attn_attrs() {
-  static const hipError_t e = [] {
-    constexpr int sm = attn_smem_bytes<DH>();
-    hipError_t r = allow_smem(flash_fwd_kernel<DH, false>, sm);
-    if (r == hipSuccess) r = allow_smem(flash_bwd_kernel<DH, false>, sm);
-    if (r == hipSuccess) r = allow_smem(flash_fwd_kernel<DH, true>, sm);
-    if (r == hipSuccess) r = allow_smem(flash_bwd_kernel<DH, true>, sm);
-    return r;
-  }();
-  return e;
+                              y - nb, buf0, buf1, sta0, sta1);
 }
 
 // The clip threshold in units of the raw product q . k (INFINITY: no clipping).
@@ -658,17 +762,16 @@ hipError_t flash_fwd(const void* qkv, void* ctx, float* lse2, int B, int H, int 
   const bf16_t* q = static_cast<const bf16_t*>(qkv);
   bf16_t* c = static_cast<bf16_t*>(ctx);
   if (dh != 128 && dh != 64) return hipErrorInvalidValue;
-  if (hipError_t e = dh == 128 ? attn_attrs<128>() : attn_attrs<64>(); e != hipSuccess) return e;
-  const int sm = dh == 128 ? attn_smem_bytes<128>() : attn_smem_bytes<64>();
+  // (the forward kernel's LDS is static)
   const bool cl = craw < INFINITY;
   if (dh == 128 && cl)
-    hipLaunchKernelGGL((flash_fwd_kernel<128, true>), grid, dim3(512), sm, s, q, c, lse2, S, H, D, causal, sl2, craw);
+    hipLaunchKernelGGL((flash_fwd_kernel<128, true>), grid, dim3(512), 0, s, q, c, lse2, S, H, D, causal, sl2, craw);
   else if (dh == 128)
-    hipLaunchKernelGGL((flash_fwd_kernel<128, false>), grid, dim3(512), sm, s, q, c, lse2, S, H, D, causal, sl2, craw);
+    hipLaunchKernelGGL((flash_fwd_kernel<128, false>), grid, dim3(512), 0, s, q, c, lse2, S, H, D, causal, sl2, craw);
   else if (cl)
-    hipLaunchKernelGGL((flash_fwd_kernel<64, true>), grid, dim3(512), sm, s, q, c, lse2, S, H, D, causal, sl2, craw);
+    hipLaunchKernelGGL((flash_fwd_kernel<64, true>), grid, dim3(512), 0, s, q, c, lse2, S, H, D, causal, sl2, craw);
   else
-    hipLaunchKernelGGL((flash_fwd_kernel<64, false>), grid, dim3(512), sm, s, q, c, lse2, S, H, D, causal, sl2, craw);
+    hipLaunchKernelGGL((flash_fwd_kernel<64, false>), grid, dim3(512), 0, s, q, c, lse2, S, H, D, causal, sl2, craw);
   return hipGetLastError();
 }
 
@@ -685,22 +788,20 @@ hipError_t flash_bwd(const void* qkv, const void* ctx, const void* dctx, const f
   const bf16_t* dO = static_cast<const bf16_t*>(dctx);
   bf16_t* dq = static_cast<bf16_t*>(dqkv);
   if (dh != 128 && dh != 64) return hipErrorInvalidValue;
-  hipError_t e = dh == 128 ? attn_attrs<128>() : attn_attrs<64>();
-  if (e != hipSuccess) return e;
-  const int sm = dh == 128 ? attn_smem_bytes<128>() : attn_smem_bytes<64>();
+  // (the kernel's LDS is static)
   // (sequence, head) along x: workgroups go to the XCDs round-robin by linear
   // id, so with B*H a multiple of 8 every block of one (sequence, head) --
   // which all read the same keys and values -- shares one XCD's L2
   const dim3 grid(B * H, 2 * nb);
   const bool cl = craw < INFINITY;
   if (dh == 128 && cl)
-    hipLaunchKernelGGL((flash_bwd_kernel<128, true>), grid, dim3(512), sm, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
+    hipLaunchKernelGGL((flash_bwd_kernel<128, true>), grid, dim3(512), 0, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
   else if (dh == 128)
-    hipLaunchKernelGGL((flash_bwd_kernel<128, false>), grid, dim3(512), sm, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
+    hipLaunchKernelGGL((flash_bwd_kernel<128, false>), grid, dim3(512), 0, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
   else if (cl)
-    hipLaunchKernelGGL((flash_bwd_kernel<64, true>), grid, dim3(512), sm, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
+    hipLaunchKernelGGL((flash_bwd_kernel<64, true>), grid, dim3(512), 0, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
   else
-    hipLaunchKernelGGL((flash_bwd_kernel<64, false>), grid, dim3(512), sm, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
+    hipLaunchKernelGGL((flash_bwd_kernel<64, false>), grid, dim3(512), 0, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
   return hipGetLastError();
 }
 
