@@ -501,7 +501,7 @@ __device__ __forceinline__ void flash_dkdv_body(
       if (wl == 0) ls_s[gt] = qb * kBlk + gt < S ? lsv : INFINITY;
       // delta = rowsum(dO * O) of the block's rows: chunk i of this thread is
       // 8 columns of row (gt + 256 i) / CPR, the CPR consecutive threads of a
-      // row add their dot products in a fixed order
+      // row add their dot products in a fixed butterfly
       constexpr int CPR = TileRows<DH>::CPR;
 #pragma unroll
       for (int i = 0; i < TileRows<DH>::PER; ++i) {
@@ -513,14 +513,8 @@ __device__ __forceinline__ void flash_dkdv_body(
           dsum = fmaf(__uint_as_float(av[e] << 16), __uint_as_float(cv[e] << 16), dsum);
           dsum = fmaf(__uint_as_float(av[e] & 0xffff0000u), __uint_as_float(cv[e] & 0xffff0000u), dsum);
         }
-        // the CPR threads of a row are one aligned DPP row (16) or half row (8)
-        if constexpr (CPR == 16) {
-          dsum = row16_sum(dsum);
-        } else {
-          dsum += dpp_f<0xB1>(dsum);   // quad_perm [1,0,3,2]
-          dsum += dpp_f<0x4E>(dsum);   // quad_perm [2,3,0,1]
-          dsum += dpp_f<0x141>(dsum);  // row_half_mirror
-        }
+#pragma unroll
+        for (int m = CPR / 2; m > 0; m >>= 1) dsum += __shfl_xor(dsum, m, 64);
         if (gt % CPR == 0) dl_s[(gt + 256 * i) / CPR] = dsum;
       }
     }
@@ -722,12 +716,11 @@ __device__ __forceinline__ void flash_dq_body(
   }
 }
 
-// The backward of the attention in one launch: grid (B*H, 2 * blocks); even
-// y: dK / dV of key block y/2, odd y: dQ of query block blocks-1-y/2.  With
-// a causal mask both lists then run from the longest block to the shortest
-// and the two interleave, so the longest blocks of either kind start first
-// (workgroups start in order of y).  The dQ and the dK/dV blocks are
-// independent, so a CU that finishes a short one takes the next.
+// The backward of the attention in one launch: grid (B*H, 2 * blocks); y <
+// blocks: dQ of query block blocks-1-y (longest causal rows first), else dK /
+// dV of key block y-blocks (key block 0, the longest, first).  The dQ and the
+// dK/dV blocks are independent, so a CU that finishes a short one takes the
+// next.
 template <int DH, bool CLIP>
 __global__ __launch_bounds__(512) void flash_bwd_kernel(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ ctx,
@@ -740,12 +733,12 @@ __global__ __launch_bounds__(512) void flash_bwd_kernel(
   __shared__ float sta1[kGroups * 2 * kBlk];
   const int nb = (S + kBlk - 1) / kBlk;
   const int y = int(blockIdx.y), bh = int(blockIdx.x);
-  if (y & 1)
+  if (y < nb)
     flash_dq_body<DH, CLIP>(qkv, ctx, dctx, lse2, dqkv, S, H, D, causal, sl2, scale, craw, bh,
-                            nb - 1 - (y >> 1), buf0, buf1);
+                            nb - 1 - y, buf0, buf1);
   else
     flash_dkdv_body<DH, CLIP>(qkv, ctx, dctx, lse2, dqkv, S, H, D, causal, sl2, scale, craw, bh,
-                              y >> 1, buf0, buf1, sta0, sta1);
+                              y - nb, buf0, buf1, sta0, sta1);
 }
 
 // The clip threshold in units of the raw product q . k (INFINITY: no clipping).
