@@ -31,7 +31,7 @@ namespace {
 //           attention only)
 //   ds:     act [B*H, S, ldS] (unfused attention only)
 //   spare:  one more layer slot after the set (pipelined backward phase: the
-//           next micro-batch's top layer is re-materialized there while the
+//           next micro-batch's first layer is re-materialized there while the
 //           current one's backward still holds every slot of the set)
 //   r0, r1, dm: float32 [T, D]   (residual-stream gradients, LN input grads)
 //   a0, a1: act [T, D], two copies each;  dctx: act [T, D]
@@ -739,14 +739,16 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
   // With fused attention the re-materialization of micro-batch m+1 runs on
   // the third stream during the backward of micro-batch m, in the saved set
   // and one spare layer slot: the backward frees the layer slots from the top
-  // down and the re-materialization fills them from the bottom up, micro-batch
-  // m+1 putting layer j in the slot that layer L-1-j of micro-batch m held,
-  // each layer enqueued after that slot's backward and weight gradients; its
-  // top layer goes to the spare slot, right after layer L-2 (so it does not
-  // wait for micro-batch m's last layer), and the slot micro-batch m's layer 0
-  // frees is the next spare.  A layer's output goes to its own slot's X
-  // tensor (the next layer's input).  Micro-batch 0 re-materializes on the
-  // caller's stream before its backward.
+  // down and the re-materialization fills them from the bottom up.  Micro-batch
+  // m+1 puts layer 0 in the spare slot as soon as micro-batch m's backward
+  // starts (after its loss, which reads the re-materialized output), and layer
+  // j >= 1 in the slot that layer L-j of micro-batch m held, enqueued after
+  // that slot's backward and weight gradients; so its last layer can start
+  // after micro-batch m's layer 1 and is done about when layer 0 is.  The slot
+  // micro-batch m's layer 0 frees is the next spare.  A layer's output goes to
+  // its own slot's X tensor (the next layer's input), the top layer's to the
+  // re-materialized output.  Micro-batch 0 re-materializes on the caller's
+  // stream before its backward.
   const bool piped = lanes;
   if (piped && !p.spare) return GPIPE_ERR_STATE;
   std::vector<int> cur(L), nxt(L);  // layer -> slot, this micro-batch and the next
@@ -804,6 +806,15 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
       GP_CHECK(grad_in(cx.bf16, cx.act(io.dy, m * mb), static_cast<float*>(cx.at(p.r0)), a0,
                        int64_t(mb), cx.s));
     }
+    if (piped && m + 1 < M) {
+      // the spare slot (micro-batch m-1's layer 0, whose backward and weight
+      // gradients are enqueued before this point) takes micro-batch m+1's
+      // layer 0
+      if (!ss.fork3()) return GPIPE_ERR_DEVICE;
+      nxt[0] = spare;
+      gpipe_status st = remat_layer(cr, nxt, m + 1, 0);
+      if (st != GPIPE_OK) return st;
+    }
     for (int l = L - 1; l >= 0; --l) {
       // (the layer's input: the output of layer l-1, in that layer's slot when
       // pipelined, else in this layer's X tensor)
@@ -817,15 +828,10 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
         // layer l's slot is free once its backward (s1) and weight gradients (s2)
         // are done
         if (!ss.fork3()) return GPIPE_ERR_DEVICE;
-        const int j = L - 1 - l;
+        const int j = L - l;
         nxt[j] = cur[l];
         st = remat_layer(cr, nxt, m + 1, j);
         if (st != GPIPE_OK) return st;
-        if (l == 1) {  // the top layer, in the spare slot
-          nxt[L - 1] = spare;
-          st = remat_layer(cr, nxt, m + 1, L - 1);
-          if (st != GPIPE_OK) return st;
-        }
       }
     }
     if (piped && m + 1 < M) {
