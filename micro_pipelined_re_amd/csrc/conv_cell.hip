@@ -97,7 +97,7 @@ bool make_cplan(const gpipe_cell* c, int N, int M, int remat, CPlan* p) {
                       (P + 64) * C < (size_t(1) << 31);
   p->piped = remat && p->implicit_wgrad && c->L >= 2;
   // pipelined, one spare block slot after the set (block index L): the next
-  // micro-batch's top block is re-materialized there (conv_cell_run)
+  // micro-batch's block 0 is re-materialized there (conv_cell_run)
   size_t o = size_t(p->nsets) * p->set_bytes + (p->piped ? p->block_bytes : 0);
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -562,16 +562,18 @@ gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void*
   // phase 2: re-materialize and backpropagate each micro-batch.  Pipelined
   // (p.piped): the weight gradients run on the second stream, and micro-batch
   // m+1 re-materializes on the third while micro-batch m's backward frees the
-  // saved set's block slots, from the top block down: m+1 puts block j < L-1
-  // in the slot m's block L-1-j held, each block enqueued after that slot's
-  // backward and weight gradients, and its top block in a spare slot right
-  // after block L-2 (the slot m's block 0 frees is the next spare); a block's
-  // output goes to its own slot's X tensor (the next block's input).
-  // Micro-batch 0 re-materializes on the caller's stream.
+  // saved set's block slots, from the top block down: m+1 puts block 0 in a
+  // spare slot as soon as m's backward starts (after its loss, which reads
+  // the re-materialized output) and block j >= 1 in the slot m's block L-j
+  // held, each enqueued after that slot's backward and weight gradients (the
+  // slot m's block 0 frees is the next spare); a block's output goes to its
+  // own slot's X tensor (the next block's input), the top block's to the
+  // re-materialized output.  Micro-batch 0 re-materializes on the caller's
+  // stream.
   const int L = c->L;
   std::vector<int> slots(L), next_slots(L);  // block -> slot, this / next micro-batch
   for (int j = 0; j < L; ++j) slots[j] = j;
-  int spare = L;  // the slot the next micro-batch's top block takes
+  int spare = L;  // the slot the next micro-batch's block 0 takes
   Streams ss{c, stream, c->aux, c->aux2};
   CCtx cr = cx;  // the re-materialization's context on the third stream
   if (p.piped) {
@@ -623,6 +625,14 @@ gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void*
                        stream));
     }
     const bool next = p.piped && m + 1 < M;
+    if (next) {
+      // the spare slot (micro-batch m-1's block 0, whose backward and weight
+      // gradients are enqueued before this point) takes micro-batch m+1's block 0
+      next_slots[0] = spare;
+      if (!ss.fork3()) return GPIPE_ERR_DEVICE;
+      gpipe_status st = remat_block(cr, m + 1, 0, next_slots);
+      if (st != GPIPE_OK) return st;
+    }
     for (int l = L - 1; l >= 0; --l) {
       const void* xin = l == 0 ? xm
                         : p.piped ? cx.at(csaved_at(p, set, slots[l - 1], GPIPE_CONV_SAVED_X))
@@ -634,16 +644,11 @@ gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void*
       if (next && l >= 1) {
         // block l's slot is free once its backward (s1) and weight gradients
         // (s2) are done
-        const int j = L - 1 - l;
+        const int j = L - l;
         next_slots[j] = slots[l];
         if (!ss.fork3()) return GPIPE_ERR_DEVICE;
         st = remat_block(cr, m + 1, j, next_slots);
         if (st != GPIPE_OK) return st;
-        if (l == 1) {  // the top block, in the spare slot
-          next_slots[L - 1] = spare;
-          st = remat_block(cr, m + 1, L - 1, next_slots);
-          if (st != GPIPE_OK) return st;
-        }
       }
     }
     if (next) {
