@@ -137,10 +137,13 @@ GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch) {
     }
   }
   // implicit-GEMM convolutions with at least 192 tiles of 128 x 128: the
-  // specialised-wave kernel with the gathered-operand loader
+  // specialised-wave kernel with the gathered-operand loader.  The forward
+  // convolution (the forward phase's lanes and the re-materialization) takes
+  // 128 x 256 tiles where they cover the output channels, so one launch
+  // holds about half the CUs and leaves the rest to the caller's stream.
   if ((role == GPIPE_ROLE_CONV_FWD_IMPLICIT || role == GPIPE_ROLE_CONV_DGRAD_IMPLICIT) &&
       batch == 1 && long((M + 127) / 128) * ((N + 127) / 128) >= 192) {
-    p.cfg = CFG_128x128_SPEC;
+    p.cfg = role == GPIPE_ROLE_CONV_FWD_IMPLICIT && N % 256 == 0 ? CFG_128x256_K64 : CFG_128x128_SPEC;
     return p;
   }
   // the weight gradient with the gathered column matrix: C x 9C outputs

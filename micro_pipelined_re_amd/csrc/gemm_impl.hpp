@@ -595,9 +595,12 @@ hipError_t launch_role(int path, int cfg, const GemmParams& g, int batch, int sp
   using R = RoleSpec<ROLE>;
   using RB = Cfg<128, 128>;
   if constexpr (R::LA == LAY_CONV) {
-    // two tile configurations for the gathered operand
+    // three tile configurations for the gathered operand
     if (cfg == CFG_128x128_SPEC)
       return launch_bf16<DCfg<128, 128, 64, 4, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch,
+                                                                                  splits, s);
+    if (cfg == CFG_128x256_K64)
+      return launch_bf16<DCfg<128, 256, 64, 3, 1>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch,
                                                                                   splits, s);
     if (cfg != CFG_128x128_K64) return hipErrorInvalidValue;
     return launch_bf16<DCfg<128, 128, 64, 2, 2>, RB, R::LA, R::LB, R::EPI, ROLE>(path, g, batch,
