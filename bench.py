@@ -22,6 +22,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -542,6 +543,10 @@ def main():
                          "FETCH_SIZE dir, WRITE_SIZE dir [, SQ/GRBM dir]")
     ap.add_argument("--profile-all", action="store_true",
                     help="time every kernel role inside the timed region")
+    ap.add_argument("--time-every", type=int, default=5,
+                    help="inside the timed region, time every k-th launch of the dominant "
+                         "kernel (raised to the next k coprime with its launches per step, so "
+                         "that the sample moves over every launch position of a step)")
     args = ap.parse_args()
     if args.counter_summary:
         print(counter_summary(*args.counter_summary[:3]))
@@ -618,8 +623,15 @@ def main():
     log("[bench] kernel time per step (warmup step, all streams): " +
         ", ".join(f"{k} {prof[k][0]:.1f} ms" for k in ranked[:6]))
 
-    # timed region: K steps; the dominant role's launches are timed by events
-    gpipe.gpipe_cell_profile(cell.handle, all_roles if args.profile_all else (1 << dom_idx))
+    # timed region: K steps; a regular sample of the dominant role's launches
+    # (every k-th) is timed by events, which keeps the events' own cost (each
+    # timed launch delays the next kernel of its stream) a fraction of timing
+    # every launch
+    every = 1 if args.profile_all else max(args.time_every, 1)
+    while every > 1 and math.gcd(every, prof[dominant][1]) != 1:
+        every += 1
+    gpipe.gpipe_cell_profile_sampled(cell.handle, all_roles if args.profile_all else (1 << dom_idx),
+                                     every)
     torch.cuda.reset_peak_memory_stats()
     base_alloc = torch.cuda.memory_allocated()
     torch.cuda.synchronize()
@@ -641,8 +653,16 @@ def main():
     src = {}
     for name in (gpipe.ROLES if args.profile_all else (dominant,)):
         ms_tot, cnt = gpipe.gpipe_cell_profile_read(cell.handle, gpipe.ROLES.index(name))
-        if cnt:
+        if not cnt:
+            continue
+        if every == 1:
             src[name] = (ms_tot / args.steps, cnt // args.steps, "timed steps")
+        else:
+            # mean over the sampled launches times the launches of a step (the
+            # warmup step timed them all)
+            per_step = prof[name][1]
+            src[name] = (ms_tot / cnt * per_step, per_step,
+                         f"timed steps, every {every}th launch ({cnt} launches)")
     for name, (ms_tot, cnt) in prof.items():
         if name not in src:
             src[name] = (ms_tot, cnt, "warmup step")

@@ -387,6 +387,16 @@ typedef enum {
  * Errors: GPIPE_ERR_DEVICE if events cannot be created. */
 gpipe_status gpipe_cell_profile(gpipe_cell *cell, unsigned long long role_mask);
 
+/* gpipe_cell_profile timing only every `every`-th launch of each selected
+ * role (the first, the every+1-th, ...; counted per role from this call), so
+ * that the events' own cost (each timed launch delays the next kernel of its
+ * stream by several microseconds) stays a fraction of it; every = 1 is
+ * gpipe_cell_profile.  gpipe_cell_profile_read then reports the timed
+ * launches only.
+ * Errors: GPIPE_ERR_INVALID for a null cell or every < 1. */
+gpipe_status gpipe_cell_profile_sampled(gpipe_cell *cell, unsigned long long role_mask,
+                                        int every);
+
 /* Total milliseconds and number of launches of `role` recorded since the last
  * gpipe_cell_profile call; waits for the recorded events to complete. */
 gpipe_status gpipe_cell_profile_read(gpipe_cell *cell, int role, double *total_ms,

@@ -43,6 +43,8 @@ struct gpipe_cell {
   size_t sync_next = 0;
   // event timing of selected kernel roles (gpipe_cell_profile)
   unsigned long long prof_mask = 0;
+  int prof_every = 1;                    // time every prof_every-th launch of a role
+  std::vector<long long> prof_seen;      // launches of each role since the profile call
   std::vector<hipEvent_t> prof_events;  // pool, pairs (start, end), reused
   std::vector<int> prof_roles;          // role of each recorded pair
 };
@@ -72,14 +74,24 @@ inline bool prof_pair(gpipe_cell* c, int role, hipEvent_t* e0, hipEvent_t* e1) {
   return true;
 }
 
-// Launches `expr`; when `role` is being timed, a GEMM role's launch records
-// two events in its own dispatch (launch_events()), any other role is
-// bracketed by two events recorded on the context's stream.
+// Whether this launch of a timed role is one of the sampled ones (every
+// prof_every-th launch of the role, counting from the first).
+inline bool prof_take(gpipe_cell* c, int role) {
+  if (c->prof_every <= 1) return true;
+  if (c->prof_seen.size() <= size_t(role)) c->prof_seen.resize(role + 1, 0);
+  return c->prof_seen[role]++ % c->prof_every == 0;
+}
+
+// Launches `expr`; when `role` is being timed (and this launch is sampled), a
+// GEMM role's launch records two events in its own dispatch
+// (launch_events()), any other role is bracketed by two events recorded on
+// the context's stream.
 #define GP_RUN(ctx, role, expr)                                                         \
   do {                                                                                 \
     hipEvent_t e0_ = nullptr, e1_ = nullptr;                                           \
     const bool in_launch_ = gemm_role(role);                                           \
-    if ((ctx).prof && (((ctx).prof->prof_mask >> (role)) & 1ull)) {                   \
+    if ((ctx).prof && (((ctx).prof->prof_mask >> (role)) & 1ull) &&                   \
+        prof_take((ctx).prof, (role))) {                                               \
       if (!prof_pair((ctx).prof, (role), &e0_, &e1_)) return GPIPE_ERR_DEVICE;          \
       if (in_launch_)                                                                  \
         launch_events() = LaunchEvents{e0_, e1_};                                      \

@@ -1123,11 +1123,17 @@ gpipe_status gpipe_apply_update(gpipe_cell* c, float lr, float decay, float eps,
   return GPIPE_OK;
 }
 
-gpipe_status gpipe_cell_profile(gpipe_cell* c, unsigned long long role_mask) {
-  if (!c) return GPIPE_ERR_INVALID;
+gpipe_status gpipe_cell_profile_sampled(gpipe_cell* c, unsigned long long role_mask, int every) {
+  if (!c || every < 1) return GPIPE_ERR_INVALID;
   c->prof_mask = role_mask;
+  c->prof_every = every;
+  c->prof_seen.assign(GPIPE_N_ROLES, 0);
   c->prof_roles.clear();
   return GPIPE_OK;
+}
+
+gpipe_status gpipe_cell_profile(gpipe_cell* c, unsigned long long role_mask) {
+  return gpipe_cell_profile_sampled(c, role_mask, 1);
 }
 
 gpipe_status gpipe_cell_profile_read(gpipe_cell* c, int role, double* total_ms, long long* launches) {

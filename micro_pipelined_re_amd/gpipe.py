@@ -25,7 +25,8 @@ EXPORTS = ("gpipe_cell_create", "gpipe_cell_destroy", "gpipe_cell_param_count",
            "gpipe_cell_param_offset", "gpipe_cell_bind", "gpipe_cell_sync_lowp",
            "gpipe_cell_workspace_bytes", "gpipe_cell_saved_offset", "gpipe_cell_step",
            "gpipe_apply_update", "gpipe_partition", "gpipe_status_string",
-           "gpipe_cell_profile", "gpipe_cell_profile_read", "gpipe_cell_gemm_plan",
+           "gpipe_cell_profile", "gpipe_cell_profile_sampled", "gpipe_cell_profile_read",
+           "gpipe_cell_gemm_plan",
            "gpipe_conv_cell_create", "gpipe_cell_bind_running", "gpipe_cell_forward_plan",
            "gpipe_cell_forward", "gpipe_cell_backward", "gpipe_cell_step_noalloc",
            "gpipe_cell_set_logit_clip", "gpipe_cell_scale_ffn_init")
@@ -77,6 +78,7 @@ def lib() -> ctypes.CDLL:
             "gpipe_partition": [ctypes.POINTER(ctypes.c_double), _i, _i, ctypes.POINTER(_i),
                                 ctypes.POINTER(ctypes.c_double)],
             "gpipe_cell_profile": [_vp, ctypes.c_ulonglong],
+            "gpipe_cell_profile_sampled": [_vp, ctypes.c_ulonglong, _i],
             "gpipe_cell_gemm_plan": [_vp, _i, _i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i),
                                      ctypes.POINTER(_i)],
             "gpipe_cell_profile_read": [_vp, _i, ctypes.POINTER(ctypes.c_double),
@@ -252,6 +254,10 @@ def gpipe_partition(costs, K: int):
 
 def gpipe_cell_profile(cell, role_mask: int) -> None:
     _check("gpipe_cell_profile", lib().gpipe_cell_profile(cell, role_mask))
+
+
+def gpipe_cell_profile_sampled(cell, role_mask: int, every: int) -> None:
+    _check("gpipe_cell_profile_sampled", lib().gpipe_cell_profile_sampled(cell, role_mask, every))
 
 
 def gpipe_cell_profile_read(cell, role: int):

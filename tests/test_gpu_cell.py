@@ -398,3 +398,37 @@ def test_fused_attention_remat_bitwise_bf16():
     for ga, gb in zip(a["grad"], b["grad"]):
         for n in gpipe.TENSORS:
             assert np.array_equal(ga[n], gb[n]), n
+
+
+def test_profiled_step_bitwise_and_sampled_launch_counts():
+    """Timing roles with events changes no result, and timing every k-th launch
+    of a role records ceil(n / k) of its n launches."""
+    import math
+    cfg = configs.SMALL.with_(name="small_2l", layers=2, batch=8, micro=4)
+    params = inputs.cell_params(cfg)
+    x, t = inputs.cell_data(cfg, batch=8)
+    plain = run_gpu(cfg, params, x, t, 8, 4, update=False)
+    cell = make_cell(cfg, params)
+    all_roles = (1 << len(gpipe.ROLES)) - 1
+    gpipe.gpipe_cell_profile(cell.handle, all_roles)
+    timed = run_gpu(cfg, params, x, t, 8, 4, update=False, cell=cell)
+    assert np.array_equal(plain["y"], timed["y"]) and np.array_equal(plain["dx"], timed["dx"])
+    for ga, gb in zip(plain["grad"], timed["grad"]):
+        for n in gpipe.TENSORS:
+            assert np.array_equal(ga[n], gb[n]), n
+    full = {}
+    for r, name in enumerate(gpipe.ROLES):
+        ms, cnt = gpipe.gpipe_cell_profile_read(cell.handle, r)
+        if cnt:
+            assert ms > 0, name
+            full[name] = cnt
+    assert full.get("ffn1_fwd", 0) >= cfg.layers * 4, full
+    for every in (3, 7):
+        gpipe.gpipe_cell_profile_sampled(cell.handle, all_roles, every)
+        run_gpu(cfg, params, x, t, 8, 4, update=False, cell=cell)
+        for r, name in enumerate(gpipe.ROLES):
+            ms, cnt = gpipe.gpipe_cell_profile_read(cell.handle, r)
+            assert cnt == math.ceil(full.get(name, 0) / every), (name, every, cnt, full.get(name))
+    with pytest.raises(RuntimeError):
+        gpipe.gpipe_cell_profile_sampled(cell.handle, all_roles, 0)
+    gpipe.gpipe_cell_profile(cell.handle, 0)
