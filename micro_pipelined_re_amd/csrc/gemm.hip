@@ -80,17 +80,21 @@ constexpr int kCUs = 256;
 // Tile and split choice, from per-role timings on MI355X with random
 // operands and A/B runs of the whole step.  The linear layers' products
 // (forward, input gradient, weight gradient) take the specialised-wave
-// kernel: 256 x 128 tiles (128 x 256 when both operands are k-contiguous and
-// the output is wider than tall) when the output has at least 192 of them
-// -- at least 64 for the input-gradient products -- else 128 x 128 tiles,
-// unsplit.  The input gradients run on the backward's critical stream beside
-// the weight gradients and the next re-materialization: with 64 big tiles
-// for its 1024 x 2048 outputs (the FFN1, QKV and out-projection input
-// gradients) instead of 128 tiles of 128 x 128 the 8-layer 2048-wide step
-// ran 146.0 ms against 149.5 (both A/B runs on one box); big tiles for the
-// 64- and 128-tile forward and weight-gradient outputs as well ran 146.7,
-// for the forward products alone 148.5, and the input gradients in 128 x 256
-// tiles 148.0.  The step runs these products beside other
+// kernel: 256 x 128 tiles (128 x 256 for outputs wider than tall where both
+// operands are k-contiguous, and for weight gradients wider than tall) when
+// the output has at least 192 of them -- at least 64 for the backward's
+// products -- else 128 x 128 tiles, unsplit.  The input gradients run on the
+// backward's critical stream beside the weight gradients and the next
+// re-materialization: with 64 big tiles for its 1024 x 2048 outputs (the
+// FFN1, QKV and out-projection input gradients) instead of 128 tiles of
+// 128 x 128 the 8-layer 2048-wide step ran 146.0 ms against 149.5 (both A/B
+// runs on one box); big tiles for the 64- and 128-tile forward outputs as
+// well ran 146.7, for the forward products alone 148.5, and the input
+// gradients in 128 x 256 tiles 148.0.  Then 128 x 256 tiles for the 2048 x
+// 8192 FFN2 weight gradient with 256 x 128 tiles for the 2048 x 2048
+// out-projection one (128 instead of 256 tiles of 128 x 128) ran 143.8-144.1
+// against 144.9-145.0, and 147.8-147.9 against 149.6-149.7 on a slower box
+// (three A/B rounds each); either change alone gained 0.3 ms or less.  The step runs these products beside other
 // streams' work (the forward lanes, the weight gradients, the next
 // re-materialization), which fills the CUs a small grid leaves idle, so what
 // pays alone does not in the step: the 1024 x 2048 x 8192 down-projection
@@ -131,9 +135,10 @@ GemmPlan plan_gemm(int role, bool bf16, int M, int N, int K, int batch) {
   };
   const bool linear = group_of(role) >= 0 && group_of(role) <= 2 && !is_conv(role);
   if (linear && batch == 1 && K >= 512) {
-    const int cfg = (b_k_contiguous(role) && N > M) ? CFG_128x256_K64 : CFG_256x128_K64;
+    const int cfg = ((b_k_contiguous(role) || is_wgrad(role)) && N > M) ? CFG_128x256_K64
+                                                                         : CFG_256x128_K64;
     const long tiles = long((M + kCfgBM[cfg] - 1) / kCfgBM[cfg]) * ((N + kCfgBN[cfg] - 1) / kCfgBN[cfg]);
-    if (tiles >= 192 || (tiles >= 64 && group_of(role) == 1)) {
+    if (tiles >= 192 || (tiles >= 64 && group_of(role) != 0)) {
       p.cfg = cfg;
       return p;
     }

@@ -309,10 +309,11 @@ def test_ragged_tiles_direct_lds_path_bf16():
 
 
 def test_ragged_tiles_specialised_kernel_bf16():
-    """The specialised-wave GEMM (loader and MFMA waves) with 128 x 128 tiles and
-    ragged M / N edges on k-contiguous and m-contiguous operands: T = 576 rows per
-    micro-batch, D = 1152, F = 4160, S = 288, head_dim 128 (the plans are checked
-    on the host)."""
+    """The specialised-wave GEMM (loader and MFMA waves) with ragged M / N edges on
+    k-contiguous and m-contiguous operands: 128 x 128 tiles (forward products, the
+    out-projection weight gradient) and 256 x 128 / 128 x 256 tiles (the other
+    backward products); T = 576 rows per micro-batch, D = 1152, F = 4160, S = 288,
+    head_dim 128 (the plans are checked on the host)."""
     cfg = configs.SMALL.with_(name="spec_ragged_bf16", layers=1, d_model=1152, heads=9,
                               d_ff=4160, seq=288, batch=2, micro=1)
     check(cfg)
@@ -328,8 +329,9 @@ def test_ragged_wide_tiles_specialised_kernel_bf16():
 
 
 def test_ragged_big_tiles_specialised_kernel_bf16():
-    """256 x 128 tiles of the specialised-wave GEMM with ragged M and N (the weight
-    gradients and their fused bias sums: F = 4160, D = 1600, T = 640), head_dim 64."""
+    """256 x 128 and 128 x 256 tiles of the specialised-wave GEMM with ragged M and N
+    (the weight gradients and their fused bias sums: F = 4160, D = 1600, T = 640),
+    head_dim 64."""
     cfg = configs.SMALL.with_(name="spec_ragged_big_bf16", layers=1, d_model=1600, heads=25,
                               d_ff=4160, seq=320, batch=2, micro=1)
     check(cfg)

@@ -404,8 +404,9 @@ def _cell_plans(cfg, N, M, names):
 def test_gemm_plan_of_the_2048_cell():
     """Micro-batches of 1024 tokens: the linear products take 256 x 128 / 128 x 256
     tiles (one workgroup per CU) where the output has at least 192 of them (at
-    least 64 for the input gradients), else 128 x 128 tiles, unsplit (the step's
-    other streams fill the CUs they leave idle); weight gradients never split."""
+    least 64 for the backward's products), else 128 x 128 tiles, unsplit (the
+    step's other streams fill the CUs they leave idle); weight gradients never
+    split; 128 x 256 for the weight gradient wider than tall."""
     p = _cell_plans(configs.CELL_2048, 64, 32,
                     ["qkv_fwd", "out_fwd", "ffn1_fwd", "ffn2_fwd", "ffn2_dgrad", "ffn1_dgrad",
                      "out_dgrad", "qkv_dgrad", "ffn1_wgrad", "ffn2_wgrad", "qkv_wgrad",
@@ -415,9 +416,9 @@ def test_gemm_plan_of_the_2048_cell():
     assert p["ffn2_dgrad"] == (256, 128, 1)
     assert p["ffn1_dgrad"] == (256, 128, 1) and p["qkv_dgrad"] == (256, 128, 1)
     assert p["out_dgrad"] == (256, 128, 1)
-    for w in ("ffn1_wgrad", "ffn2_wgrad", "qkv_wgrad"):
+    for w in ("ffn1_wgrad", "qkv_wgrad", "out_wgrad"):
         assert p[w] == (256, 128, 1)
-    assert p["out_wgrad"] == (128, 128, 1)
+    assert p["ffn2_wgrad"] == (128, 256, 1)
 
 
 def test_gemm_plan_of_the_ragged_wide_case():
@@ -432,18 +433,24 @@ def test_gemm_plan_of_the_ragged_wide_case():
 
 def test_gemm_plan_of_the_ragged_specialised_case():
     """The shapes of the GPU tests of the specialised kernel's ragged edges do reach it:
-    128 x 128 tiles for T = 576, D = 1152, F = 4160 (256 x 128 for the input
-    gradient, whose output has 99 of them); 256 x 128 tiles for the weight
-    gradients of T = 640, D = 1600, F = 4160."""
+    for T = 576, D = 1152, F = 4160, 128 x 128 tiles for the forward products and
+    the out-projection weight gradient (45 big tiles), big tiles for the backward
+    products with at least 64 of them -- 128 x 256 for the FFN2 weight gradient,
+    wider than tall; 256 x 128 tiles for the taller weight gradients of T = 640,
+    D = 1600, F = 4160 (128 x 256 for FFN2's)."""
     cfg = configs.SMALL.with_(layers=1, d_model=1152, heads=9, d_ff=4160, seq=288)
     p = _cell_plans(cfg, 2, 1, ["qkv_fwd", "ffn1_fwd", "ffn2_dgrad", "ffn1_wgrad", "ffn2_wgrad",
                                 "qkv_wgrad", "out_wgrad"])
+    want = {"qkv_fwd": (128, 128, 1), "ffn1_fwd": (128, 128, 1), "out_wgrad": (128, 128, 1),
+            "ffn2_dgrad": (256, 128, 1), "ffn1_wgrad": (256, 128, 1), "qkv_wgrad": (256, 128, 1),
+            "ffn2_wgrad": (128, 256, 1)}
     for n in p:
-        assert p[n] == ((256, 128, 1) if n == "ffn2_dgrad" else (128, 128, 1)), (n, p[n])
+        assert p[n] == want[n], (n, p[n])
     cfg = configs.SMALL.with_(layers=1, d_model=1600, heads=25, d_ff=4160, seq=320)
     p = _cell_plans(cfg, 2, 1, ["ffn1_wgrad", "ffn2_wgrad", "qkv_wgrad", "ffn1_fwd"])
-    for w in ("ffn1_wgrad", "ffn2_wgrad", "qkv_wgrad"):
+    for w in ("ffn1_wgrad", "qkv_wgrad"):
         assert p[w] == (256, 128, 1), (w, p[w])
+    assert p["ffn2_wgrad"] == (128, 256, 1)
     assert p["ffn1_fwd"] == (128, 128, 1)
 
 
