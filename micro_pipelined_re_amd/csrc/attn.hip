@@ -795,13 +795,13 @@ hipError_t flash_bwd(const void* qkv, const void* ctx, const void* dctx, const f
   const dim3 grid(B * H, 2 * nb);
   const bool cl = craw < INFINITY;
   if (dh == 128 && cl)
-    hipLaunchKernelGGL((flash_bwd_kernel<128, true>), grid, dim3(512), 0, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
+    launch_k((flash_bwd_kernel<128, true>), grid, dim3(512), 0, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
   else if (dh == 128)
-    hipLaunchKernelGGL((flash_bwd_kernel<128, false>), grid, dim3(512), 0, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
+    launch_k((flash_bwd_kernel<128, false>), grid, dim3(512), 0, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
   else if (cl)
-    hipLaunchKernelGGL((flash_bwd_kernel<64, true>), grid, dim3(512), 0, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
+    launch_k((flash_bwd_kernel<64, true>), grid, dim3(512), 0, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
   else
-    hipLaunchKernelGGL((flash_bwd_kernel<64, false>), grid, dim3(512), 0, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
+    launch_k((flash_bwd_kernel<64, false>), grid, dim3(512), 0, s, q, o, dO, lse2, dq, S, H, D, causal, sl2, scale, craw);
   return hipGetLastError();
 }
 

@@ -168,6 +168,35 @@ struct Streams {
     return hipEventRecord(e1, s1) == hipSuccess && hipEventRecord(e2, s2) == hipSuccess &&
            hipStreamWaitEvent(s3, e1, 0) == hipSuccess && hipStreamWaitEvent(s3, e2, 0) == hipSuccess;
   }
+  // fork() with its event recorded in the dispatch of the next kernel launched
+  // on s1 (next_done_event: no packet of its own on s1): fork_begin right
+  // before the call whose last kernel ends the work s2 waits for, fork_end
+  // after it (it records the event on s1 if no launch took it)
+  hipEvent_t pending = nullptr;
+  void fork_begin() {
+    if (single) return;
+    pending = next();
+    next_done_event() = pending;
+  }
+  bool fork_end() {
+    if (single) return true;
+    const hipEvent_t e = pending;
+    pending = nullptr;
+    if (next_done_event() == e) {
+      next_done_event() = nullptr;
+      if (hipEventRecord(e, s1) != hipSuccess) return false;
+    }
+    return hipStreamWaitEvent(s2, e, 0) == hipSuccess;
+  }
+  // fork3 where the work enqueued so far on s1 ends at event e1 (recorded in a
+  // kernel's dispatch); null e1: plain fork3
+  bool fork3_after(hipEvent_t e1) {
+    if (single) return true;
+    if (!e1) return fork3();
+    const hipEvent_t e2 = next();
+    return hipEventRecord(e2, s2) == hipSuccess && hipStreamWaitEvent(s3, e1, 0) == hipSuccess &&
+           hipStreamWaitEvent(s3, e2, 0) == hipSuccess;
+  }
   // s1 waits for the work enqueued so far on s3
   bool join3() {
     if (single) return true;

@@ -183,6 +183,11 @@ LaunchEvents& launch_events() {
   return e;
 }
 
+hipEvent_t& next_done_event() {
+  static thread_local hipEvent_t e = nullptr;
+  return e;
+}
+
 bool gemm_role(int role) { return group_of(role) >= 0; }
 
 int gemm_cfg_bm(int cfg) { return kCfgBM[cfg]; }

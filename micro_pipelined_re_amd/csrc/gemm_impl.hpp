@@ -639,14 +639,27 @@ template <typename K, typename... A>
 hipError_t launch_timed(K kernel, dim3 grid, dim3 block, uint32_t smem, hipStream_t s, bool first,
                         bool last, A... args) {
   LaunchEvents& le = launch_events();
-  const hipEvent_t e0 = first ? le.start : nullptr, e1 = last ? le.stop : nullptr;
+  hipEvent_t e0 = first ? le.start : nullptr, e1 = last ? le.stop : nullptr;
   if (first) le.start = nullptr;
   if (last) le.stop = nullptr;
+  // the pending end event (next_done_event) goes to the last kernel's dispatch
+  // unless role timing holds its stop slot; then it is recorded after it
+  hipEvent_t done = nullptr;
+  if (last) {
+    done = next_done_event();
+    next_done_event() = nullptr;
+    if (!e1) {
+      e1 = done;
+      done = nullptr;
+    }
+  }
   if (e0 || e1)
     hipExtLaunchKernelGGL(kernel, grid, block, smem, s, e0, e1, 0, args...);
   else
     hipLaunchKernelGGL(kernel, grid, block, smem, s, args...);
-  return hipGetLastError();
+  hipError_t err = hipGetLastError();
+  if (err == hipSuccess && done) err = hipEventRecord(done, s);
+  return err;
 }
 
 // A GEMM launch with nothing to compute still takes the pending events:
@@ -656,7 +669,9 @@ inline hipError_t launch_nothing(hipStream_t s) {
   hipError_t e = hipSuccess;
   if (le.start) e = hipEventRecord(le.start, s);
   if (le.stop && e == hipSuccess) e = hipEventRecord(le.stop, s);
+  if (next_done_event() && e == hipSuccess) e = hipEventRecord(next_done_event(), s);
   le.start = le.stop = nullptr;
+  next_done_event() = nullptr;
   return e;
 }
 

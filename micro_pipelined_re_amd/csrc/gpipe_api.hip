@@ -505,7 +505,7 @@ struct Transients {
 // layer output; on exit they hold the gradient w.r.t. its input (the next a0
 // copy, or dx_out when given, receives the act copy).
 gpipe_status layer_backward(const Ctx& x, Streams& ss, Transients& tb, int set, int slot, int l,
-                            const void* xin, int beta, void* dx_out) {
+                            const void* xin, int beta, void* dx_out, hipEvent_t* s1_done = nullptr) {
   Ctx w = x;  // the weight gradients' context: the second stream
   w.s = ss.s2;
   const gpipe_cell* c = x.c;
@@ -548,9 +548,10 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, Transients& tb, int set, 
   bool fused = false;
   if (!tb.du.next(&ss)) return GPIPE_ERR_DEVICE;
   du = x.at(tb.du.off[tb.du.cur]);
+  ss.fork_begin();
   GP_RUN(x, GPIPE_ROLE_FFN2_DGRAD, mm(x, GPIPE_ROLE_FFN2_DGRAD, T, F, D, a0, D, x.wmat(l, GPIPE_W_2), F, du, F,
               nullptr, nullptr, 0, u, F));
-  if (!ss.fork()) return GPIPE_ERR_DEVICE;  // a0, g and du exist
+  if (!ss.fork_end()) return GPIPE_ERR_DEVICE;  // a0, g and du exist
   GP_RUN(w, GPIPE_ROLE_FFN2_WGRAD, mm_wgrad(w, GPIPE_ROLE_FFN2_WGRAD, l, GPS_B2, D, F, T, a0, D, g, F,
               x.grad(l, GPIPE_W_2), F, beta, &fused));
   if (!tb.a0.read_by_s2(&ss, tb.a0.cur)) return GPIPE_ERR_DEVICE;
@@ -582,6 +583,7 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, Transients& tb, int set, 
   if (p.flash) {
     const float* lse2 = static_cast<const float*>(P);
     // dQ, dK and dV in one launch
+    ss.fork_begin();
     GP_RUN(x, GPIPE_ROLE_ATTN_DQ, flash_bwd(qkv, ctx, dctx, lse2, dqkv, p.B, H, S, D, cz,
                                             c->logit_clip, x.s));
   } else {
@@ -603,12 +605,13 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, Transients& tb, int set, 
                                                   clip ? 1 : 0, x.s));
     GP_RUN(x, GPIPE_ROLE_DQ, bmm(x, GPIPE_ROLE_DQ, S, dh, S, DS, K, dQ,
                  cz ? CAUSAL_K_UPTO_M : CAUSAL_NONE, 1.0f));
+    ss.fork_begin();
     GP_RUN(x, GPIPE_ROLE_DK, bmm(x, GPIPE_ROLE_DK, S, dh, S, DS, Q, dK,
                  cz ? CAUSAL_K_FROM_M : CAUSAL_NONE, 1.0f));
   }
 
   // qkv = h1 Wqkv^T + bqkv,  h1 = LN1(x)
-  if (!ss.fork()) return GPIPE_ERR_DEVICE;  // a1 and dqkv exist
+  if (!ss.fork_end()) return GPIPE_ERR_DEVICE;  // a1 and dqkv exist
   GP_RUN(w, GPIPE_ROLE_OUT_WGRAD, mm_wgrad(w, GPIPE_ROLE_OUT_WGRAD, l, GPS_BO, D, D, T, a1, D, ctx, D,
               x.grad(l, GPIPE_W_O), D, beta, &fused));
   if (!tb.a1.read_by_s2(&ss, tb.a1.cur)) return GPIPE_ERR_DEVICE;
@@ -625,8 +628,15 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, Transients& tb, int set, 
     if (!tb.a0.next(&ss)) return GPIPE_ERR_DEVICE;
     a0_in = x.at(tb.a0.off[tb.a0.cur]);
   }
+  // (s1_done: an event the LayerNorm backward, the layer's last kernel on the
+  // caller's stream, records in its dispatch)
+  if (s1_done && !ss.single) next_done_event() = *s1_done = ss.next();
   GP_RUN(x, GPIPE_ROLE_LN1_BWD, layernorm_bwd(bf, dm, xin, st1, x.wf32(l, GPIPE_LN1_G), r1, r0, a0_in,
                          ln1part, T, D, beta, &nblk, x.s));
+  if (s1_done && *s1_done && next_done_event() == *s1_done) {
+    next_done_event() = nullptr;
+    GP_CHECK(hipEventRecord(*s1_done, x.s));
+  }
   return GPIPE_OK;
 }
 
@@ -712,6 +722,7 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
   }
   Ctx cx{c, (c->prof_mask && !io.single) ? c : nullptr, &p, io.ws, io.s, c->prec == GPIPE_BF16,
          p.splitk};
+  next_done_event() = nullptr;  // (nothing pending from an earlier call that failed)
   Streams ss{c, cx.s, io.single ? cx.s : c->aux, io.single ? cx.s : c->aux2, io.single};
   const size_t mb = size_t(p.T) * c->D;  // elements per micro-batch
   const float inv_denom = float(1.0 / (double(io.N) * c->S * c->D));
@@ -822,12 +833,15 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
                         : piped ? cx.at(saved_at(p, set, cur[l - 1], GPIPE_SAVED_X))
                                 : cx.at(saved_at(p, set, l, GPIPE_SAVED_X));
       void* dxo = (l == 0 && io.dx) ? cx.act(io.dx, m * mb) : nullptr;
-      gpipe_status st = layer_backward(cx, ss, tb, set, piped ? cur[l] : l, l, xin, m > 0 ? 1 : 0, dxo);
+      const bool refill = piped && m + 1 < M && l >= 1;
+      hipEvent_t s1_done = nullptr;
+      gpipe_status st = layer_backward(cx, ss, tb, set, piped ? cur[l] : l, l, xin, m > 0 ? 1 : 0, dxo,
+                                       refill ? &s1_done : nullptr);
       if (st != GPIPE_OK) return st;
-      if (piped && m + 1 < M && l >= 1) {
+      if (refill) {
         // layer l's slot is free once its backward (s1) and weight gradients (s2)
         // are done
-        if (!ss.fork3()) return GPIPE_ERR_DEVICE;
+        if (!ss.fork3_after(s1_done)) return GPIPE_ERR_DEVICE;
         const int j = L - l;
         nxt[j] = cur[l];
         st = remat_layer(cr, nxt, m + 1, j);

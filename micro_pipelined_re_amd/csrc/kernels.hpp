@@ -1,5 +1,6 @@
 // Host-callable launchers of the cell's HIP kernels (internal to the library).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -88,6 +89,25 @@ struct LaunchEvents {
   hipEvent_t start = nullptr, stop = nullptr;
 };
 LaunchEvents& launch_events();
+// An event the next launch through launch_k() (or a GEMM's last kernel) records
+// when its kernel ends, in that kernel's own dispatch packet -- no packet of
+// its own on the stream, which would hold back the stream's next kernel by a
+// few microseconds -- and clears.  Set only right before a call whose last
+// kernel should take it; the caller records it on the stream if it is still
+// pending afterwards.
+hipEvent_t& next_done_event();
+template <typename K, typename... A>
+hipError_t launch_k(K kernel, dim3 grid, dim3 block, uint32_t smem, hipStream_t s, A... args) {
+  hipEvent_t& d = next_done_event();
+  if (d) {
+    const hipEvent_t e = d;
+    d = nullptr;
+    hipExtLaunchKernelGGL(kernel, grid, block, smem, s, nullptr, e, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, smem, s, args...);
+  }
+  return hipGetLastError();
+}
 // true for the roles whose launch is a gemm() call (they take the events)
 bool gemm_role(int role);
 

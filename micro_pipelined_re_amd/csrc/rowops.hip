@@ -299,15 +299,15 @@ static hipError_t ln_bwd_t(const float* dh, const void* x, const float* stats, c
   const T* xp = static_cast<const T*>(x);
   T* op = static_cast<T*>(dx_act);
   const size_t sh = size_t(kLnWaveRows) * d * 4;
-#define GP_LNW(NV) hipLaunchKernelGGL((ln_bwd_wave_kernel<T, NV>), grid, blk, sh, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d, beta)
+#define GP_LNW(NV) launch_k((ln_bwd_wave_kernel<T, NV>), grid, blk, sh, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d, beta)
   if (nch <= 64) GP_LNW(1);
   else if (nch <= 128) GP_LNW(2);
   else if (nch <= 256) GP_LNW(4);
   else if (nch <= 512) GP_LNW(8);
 #undef GP_LNW
-  else if (nch <= 256) hipLaunchKernelGGL((ln_bwd_kernel<T, 1>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d, beta);
-  else if (nch <= 512) hipLaunchKernelGGL((ln_bwd_kernel<T, 2>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d, beta);
-  else if (nch <= 1024) hipLaunchKernelGGL((ln_bwd_kernel<T, 4>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d, beta);
+  else if (nch <= 256) launch_k((ln_bwd_kernel<T, 1>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d, beta);
+  else if (nch <= 512) launch_k((ln_bwd_kernel<T, 2>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d, beta);
+  else if (nch <= 1024) launch_k((ln_bwd_kernel<T, 4>), grid, blk, 0, s, dh, xp, stats, gamma, res_in, dx_f32, op, part, rows, d, beta);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
