@@ -188,14 +188,33 @@ struct Streams {
     }
     return hipStreamWaitEvent(s2, e, 0) == hipSuccess;
   }
-  // fork3 where the work enqueued so far on s1 ends at event e1 (recorded in a
-  // kernel's dispatch); null e1: plain fork3
-  bool fork3_after(hipEvent_t e1) {
+  // mark() with the event recorded in the dispatch of the next kernel launched
+  // on s2: mark_begin right before that launch (null in single mode),
+  // mark_end after it
+  hipEvent_t mark_begin() {
+    if (single) return nullptr;
+    const hipEvent_t e = next();
+    next_done_event() = e;
+    return e;
+  }
+  bool mark_end(hipEvent_t e) {
+    if (!e || next_done_event() != e) return true;
+    next_done_event() = nullptr;
+    return hipEventRecord(e, s2) == hipSuccess;
+  }
+  // fork3 where the work enqueued so far on s1 ends at event e1 and that on s2
+  // at e2 (events recorded in kernels' dispatches; a null one is recorded now)
+  bool fork3_after(hipEvent_t e1, hipEvent_t e2) {
     if (single) return true;
-    if (!e1) return fork3();
-    const hipEvent_t e2 = next();
-    return hipEventRecord(e2, s2) == hipSuccess && hipStreamWaitEvent(s3, e1, 0) == hipSuccess &&
-           hipStreamWaitEvent(s3, e2, 0) == hipSuccess;
+    if (!e1) {
+      e1 = next();
+      if (hipEventRecord(e1, s1) != hipSuccess) return false;
+    }
+    if (!e2) {
+      e2 = next();
+      if (hipEventRecord(e2, s2) != hipSuccess) return false;
+    }
+    return hipStreamWaitEvent(s3, e1, 0) == hipSuccess && hipStreamWaitEvent(s3, e2, 0) == hipSuccess;
   }
   // s1 waits for the work enqueued so far on s3
   bool join3() {
@@ -226,6 +245,12 @@ struct Transient {
   }
   // the weight gradients enqueued so far on the second stream read copy k
   bool read_by_s2(Streams* ss, int k) { return !ss || ss->mark(&read[k]); }
+  // the same, with e the event the last of them recorded (Streams::mark_begin)
+  bool read_by_s2_at(Streams* ss, int k, hipEvent_t e) {
+    if (!ss || !ss->mark_end(e)) return !ss;
+    read[k] = e;
+    return true;
+  }
 };
 
 // Creates the cell's two streams and the event ring at its first step.

@@ -552,13 +552,16 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, Transients& tb, int set, 
   GP_RUN(x, GPIPE_ROLE_FFN2_DGRAD, mm(x, GPIPE_ROLE_FFN2_DGRAD, T, F, D, a0, D, x.wmat(l, GPIPE_W_2), F, du, F,
               nullptr, nullptr, 0, u, F));
   if (!ss.fork_end()) return GPIPE_ERR_DEVICE;  // a0, g and du exist
+  // (the events after the weight gradients are recorded in their dispatches)
+  hipEvent_t ev = ss.mark_begin();
   GP_RUN(w, GPIPE_ROLE_FFN2_WGRAD, mm_wgrad(w, GPIPE_ROLE_FFN2_WGRAD, l, GPS_B2, D, F, T, a0, D, g, F,
               x.grad(l, GPIPE_W_2), F, beta, &fused));
-  if (!tb.a0.read_by_s2(&ss, tb.a0.cur)) return GPIPE_ERR_DEVICE;
+  if (!tb.a0.read_by_s2_at(&ss, tb.a0.cur, ev)) return GPIPE_ERR_DEVICE;
   if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r0, D, D, x.grad(l, GPIPE_B_2), beta));
+  ev = ss.mark_begin();
   GP_RUN(w, GPIPE_ROLE_FFN1_WGRAD, mm_wgrad(w, GPIPE_ROLE_FFN1_WGRAD, l, GPS_B1, F, D, T, du, F, h2, D,
               x.grad(l, GPIPE_W_1), D, beta, &fused));
-  if (!tb.du.read_by_s2(&ss, tb.du.cur)) return GPIPE_ERR_DEVICE;
+  if (!tb.du.read_by_s2_at(&ss, tb.du.cur, ev)) return GPIPE_ERR_DEVICE;
   GP_RUN(x, GPIPE_ROLE_FFN1_DGRAD, mm(x, GPIPE_ROLE_FFN1_DGRAD, T, D, F, du, F, x.wmat(l, GPIPE_W_1), D, dm, D));
   if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, xt_act, du, F, F, x.grad(l, GPIPE_B_1), beta));
   int nblk = 0;
@@ -612,13 +615,15 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, Transients& tb, int set, 
 
   // qkv = h1 Wqkv^T + bqkv,  h1 = LN1(x)
   if (!ss.fork_end()) return GPIPE_ERR_DEVICE;  // a1 and dqkv exist
+  ev = ss.mark_begin();
   GP_RUN(w, GPIPE_ROLE_OUT_WGRAD, mm_wgrad(w, GPIPE_ROLE_OUT_WGRAD, l, GPS_BO, D, D, T, a1, D, ctx, D,
               x.grad(l, GPIPE_W_O), D, beta, &fused));
-  if (!tb.a1.read_by_s2(&ss, tb.a1.cur)) return GPIPE_ERR_DEVICE;
+  if (!tb.a1.read_by_s2_at(&ss, tb.a1.cur, ev)) return GPIPE_ERR_DEVICE;
   if (!fused) GP_RUN(x, GPIPE_ROLE_BIAS_GRAD, colsum_into(x, XT_F32, r1, D, D, x.grad(l, GPIPE_B_O), beta));
+  ev = ss.mark_begin();
   GP_RUN(w, GPIPE_ROLE_QKV_WGRAD, mm_wgrad(w, GPIPE_ROLE_QKV_WGRAD, l, GPS_BQKV, 3 * D, D, T, dqkv, 3 * D, h1,
               D, x.grad(l, GPIPE_W_QKV), D, beta, &fused));
-  if (!tb.dqkv.read_by_s2(&ss, tb.dqkv.cur)) return GPIPE_ERR_DEVICE;
+  if (!tb.dqkv.read_by_s2_at(&ss, tb.dqkv.cur, ev)) return GPIPE_ERR_DEVICE;
   GP_RUN(x, GPIPE_ROLE_QKV_DGRAD, mm(x, GPIPE_ROLE_QKV_DGRAD, T, D, 3 * D, dqkv, 3 * D, x.wmat(l, GPIPE_W_QKV), D,
               dm, D));
   if (!fused)
@@ -841,7 +846,9 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
       if (refill) {
         // layer l's slot is free once its backward (s1) and weight gradients (s2)
         // are done
-        if (!ss.fork3_after(s1_done)) return GPIPE_ERR_DEVICE;
+        // (the weight gradients' last event: after the layer's QKV weight
+        // gradient, the last launch on s2)
+        if (!ss.fork3_after(s1_done, tb.dqkv.read[tb.dqkv.cur])) return GPIPE_ERR_DEVICE;
         const int j = L - l;
         nxt[j] = cur[l];
         st = remat_layer(cr, nxt, m + 1, j);
