@@ -334,7 +334,7 @@ gpipe_status cell_forward(const CCtx& x, int set, const void* xin, void* yout, f
 // wrote, W1's the copy BN1's wrote, and each BatchNorm backward writes the
 // other copy than the last one, waiting only for that copy's readers.
 gpipe_status block_backward(const CCtx& x, Streams* ss, Transient* tdz, int set, int slot, int l,
-                            const void* xin, int beta, void* dx_out) {
+                            const void* xin, int beta, void* dx_out, hipEvent_t* s1_done = nullptr) {
   const gpipe_cell* c = x.c;
   const CPlan& p = *x.p;
   const int C = c->C, B = p.B, H = c->Hc, W = c->Wc;
@@ -378,20 +378,29 @@ gpipe_status block_backward(const CCtx& x, Streams* ss, Transient* tdz, int set,
   if (!tdz->next(ss)) return GPIPE_ERR_DEVICE;
   const int k1 = tdz->cur;
   void* dz1 = x.at(tdz->off[k1]);
+  // (the hand-off events are recorded in the dispatches of the kernels they
+  // follow: BN1's backward on the caller's stream, the weight gradients)
+  if (ss) ss->fork_begin();
   GP_RUN(x, GPIPE_ROLE_BN_BWD, bn_bwd(x.act_kind(), 1, r1, r, x.xs_kind(), a, st1,
                                       x.wf32(l, GPIPE_CONV_BN1_G), part, sums,
                                       x.grad(l, GPIPE_CONV_BN1_G), beta, dz1, P, C, &nch, x.s));
   // the weight gradients of W2 and W1 (in that order on the second stream)
-  if (ss && !ss->fork()) return GPIPE_ERR_DEVICE;
+  if (ss && !ss->fork_end()) return GPIPE_ERR_DEVICE;
   {
+    hipEvent_t ev = ss ? ss->mark_begin() : nullptr;
     gpipe_status st = cwgrad(w, r, r_ld, dz2, x.grad(l, GPIPE_CONV_W2), beta);
     if (st != GPIPE_OK) return st;
-    if (!tdz->read_by_s2(ss, k2)) return GPIPE_ERR_DEVICE;
+    if (!tdz->read_by_s2_at(ss, k2, ev)) return GPIPE_ERR_DEVICE;
+    ev = ss ? ss->mark_begin() : nullptr;
     st = cwgrad(w, xin, x_ld, dz1, x.grad(l, GPIPE_CONV_W1), beta);
     if (st != GPIPE_OK) return st;
-    if (!tdz->read_by_s2(ss, k1)) return GPIPE_ERR_DEVICE;
+    if (!tdz->read_by_s2_at(ss, k1, ev)) return GPIPE_ERR_DEVICE;
   }
   // a = conv(x, W1); the residual gradient r0 is added in col2im (in place)
+  // (s1_done: an event the implicit input-gradient convolution, then the
+  // block's last kernel on the caller's stream, records in its dispatch)
+  const bool tail = s1_done && ss && !ss->single && p.implicit && !dx_out;
+  if (tail) next_done_event() = *s1_done = ss->next();
   if (p.implicit) {
     // the residual gradient already in r0 gets the convolution's input gradient added
     GP_RUN(x, GPIPE_ROLE_CONV_DGRAD_IMPLICIT,
@@ -401,6 +410,10 @@ gpipe_status block_backward(const CCtx& x, Streams* ss, Transient* tdz, int set,
     GP_RUN(x, GPIPE_ROLE_CONV_DGRAD, cmm(x, GPIPE_ROLE_CONV_DGRAD, int(P), 9 * C, C, dz1, C,
                                          x.wmat(l, GPIPE_CONV_W1), 9 * C, dcol, 9 * C));
     GP_RUN(x, GPIPE_ROLE_COL2IM, col2im(x.bf16, dcol, r0, r0, dx_out, B, H, W, C, x.s));
+  }
+  if (tail && next_done_event() == *s1_done) {
+    next_done_event() = nullptr;
+    GP_CHECK(hipEventRecord(*s1_done, x.s));
   }
   return GPIPE_OK;
 }
@@ -486,6 +499,7 @@ gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void*
     return GPIPE_ERR_INVALID;
   CCtx cx{c, c->prof_mask ? c : nullptr, &p, static_cast<char*>(workspace), stream,
           c->prec == GPIPE_BF16, p.part, p.splitk};
+  next_done_event() = nullptr;  // (nothing pending from an earlier call that failed)
   const size_t mb = size_t(p.P) * c->C;
   const float inv_denom = float(1.0 / (double(N) * c->Hc * c->Wc * c->C));
   float* rec = cx.f(p.rec);
@@ -638,15 +652,16 @@ gpipe_status conv_cell_run(gpipe_cell* c, int phases, const void* x, const void*
                         : p.piped ? cx.at(csaved_at(p, set, slots[l - 1], GPIPE_CONV_SAVED_X))
                                   : cx.at(csaved_at(p, set, l, GPIPE_CONV_SAVED_X));
       void* dxo = (l == 0 && dx) ? cx.act(dx, m * mb) : nullptr;
+      hipEvent_t s1_done = nullptr;
       gpipe_status st = block_backward(cx, sp, &tdz, set, slots[l], l,
-                                       xin, m > 0 ? 1 : 0, dxo);
+                                       xin, m > 0 ? 1 : 0, dxo, next && l >= 1 ? &s1_done : nullptr);
       if (st != GPIPE_OK) return st;
       if (next && l >= 1) {
         // block l's slot is free once its backward (s1) and weight gradients
-        // (s2) are done
+        // (s2) are done (the latter end with W1's, whose event is the dz copy's)
         const int j = L - l;
         next_slots[j] = slots[l];
-        if (!ss.fork3()) return GPIPE_ERR_DEVICE;
+        if (!ss.fork3_after(s1_done, tdz.read[tdz.cur])) return GPIPE_ERR_DEVICE;
         st = remat_block(cr, m + 1, j, next_slots);
         if (st != GPIPE_OK) return st;
       }

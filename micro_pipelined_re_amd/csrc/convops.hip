@@ -469,8 +469,8 @@ hipError_t bn_bwd(int da_kind, int mask, const float* dy_src, const void* r, int
   const int blocks = int(want < 16384 ? want : 16384);
   const float inv_n = float(1.0 / double(rows));
 #define GP_BN_BWD_A(KD, KR, MK)                                                              \
-  hipLaunchKernelGGL((bn_bwd_apply_kernel<KD, KR, MK>), dim3(blocks), dim3(256), 0, s, dy_src, \
-                     r, a, stats, gamma, sums, da, rows, C, inv_n)
+  launch_k((bn_bwd_apply_kernel<KD, KR, MK>), dim3(blocks), dim3(256), 0, s, dy_src, r, a,    \
+           stats, gamma, sums, da, rows, C, inv_n)
   if (da_kind == SK_F32) {
     if (!mask) GP_BN_BWD_A(SK_F32, SK_F32, 0);
     else if (r_kind == SK_F32) GP_BN_BWD_A(SK_F32, SK_F32, 1);
