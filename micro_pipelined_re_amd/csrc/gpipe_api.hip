@@ -363,8 +363,9 @@ hipError_t colsum_into(const Ctx& x, int xtype, const void* src, int64_t ld, int
 // layer whose weights are applied -- the same except in the forward phase's
 // one-slot scratch)
 // (keep_u: store the FFN pre-activation u, which only the backward reads)
+// (end_event: recorded when the layer's last kernel ends, in its dispatch)
 gpipe_status layer_forward(const Ctx& x, int set, int slot, int l, const void* xin, void* xout,
-                           bool keep_u = true) {
+                           bool keep_u = true, hipEvent_t end_event = nullptr) {
   const gpipe_cell* c = x.c;
   const Plan& p = *x.p;
   const int T = p.T, D = c->D, F = c->F, S = c->S, H = c->H, dh = D / H;
@@ -409,8 +410,13 @@ gpipe_status layer_forward(const Ctx& x, int set, int slot, int l, const void* x
                          c->ln_eps, x.s));
   GP_RUN(x, GPIPE_ROLE_FFN1_FWD, mm(x, GPIPE_ROLE_FFN1_FWD, T, F, D, h2, D, x.wmat(l, GPIPE_W_1), D, g, F,
               x.wf32(l, GPIPE_B_1), nullptr, 0, keep_u ? u : nullptr, F));
+  next_done_event() = end_event;
   GP_RUN(x, GPIPE_ROLE_FFN2_FWD, mm(x, GPIPE_ROLE_FFN2_FWD, T, D, F, g, F, x.wmat(l, GPIPE_W_2), F, xout, D,
               x.wf32(l, GPIPE_B_2), x1, D));
+  if (end_event && next_done_event() == end_event) {
+    next_done_event() = nullptr;
+    GP_CHECK(hipEventRecord(end_event, x.s));
+  }
   return GPIPE_OK;
 }
 
@@ -651,14 +657,16 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, Transients& tb, int set, 
 gpipe_status reduce_gparts(const Ctx& x) {
   const Plan& p = *x.p;
   const int grad_of[GPS_N] = {GPIPE_LN1_G, GPIPE_LN2_G, GPIPE_B_QKV, GPIPE_B_O, GPIPE_B_1, GPIPE_B_2};
+  // (all of them in one launch: each is its own row of the grid)
+  std::vector<SumJob> jobs;
   for (int l = 0; l < x.c->L; ++l)
     for (int k = 0; k < GPS_N; ++k) {
       if (!p.gp_parts[k]) continue;
       const int cols = p.gp_cols[k];
-      const float* part = static_cast<const float*>(x.at(gpart_at(p, l, k)));
-      GP_RUN(x, k <= GPS_LN2 ? GPIPE_ROLE_NORM_GRAD : GPIPE_ROLE_BIAS_GRAD,
-             sum_partials(part, p.gp_parts[k], cols, cols, x.grad(l, grad_of[k]), 0, x.s));
+      jobs.push_back(SumJob{static_cast<const float*>(x.at(gpart_at(p, l, k))), x.grad(l, grad_of[k]),
+                            cols, p.gp_parts[k], cols});
     }
+  GP_RUN(x, GPIPE_ROLE_NORM_GRAD, sum_partials_batch(jobs.data(), int(jobs.size()), x.s));
   return GPIPE_OK;
 }
 
@@ -773,10 +781,16 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
   Ctx cr = cx;  // the re-materialization's context on the third stream
   cr.s = ss.s3;
   cr.splitk = p.splitk2;
+  // (the third stream's re-materialization of a micro-batch ends with its top
+  // layer's last kernel, which records remat_done in its dispatch; the caller's
+  // stream waits for that event before the micro-batch's backward)
+  hipEvent_t remat_done = nullptr;
   auto remat_layer = [&](const Ctx& z, const std::vector<int>& sl, int m, int j) {
     const void* in = j == 0 ? cx.act(x, m * mb) : z.at(saved_at(p, 0, sl[j - 1], GPIPE_SAVED_X));
     void* out = j == L - 1 ? z.at(p.yre) : z.at(saved_at(p, 0, sl[j], GPIPE_SAVED_X));
-    return layer_forward(z, 0, sl[j], j, in, out);
+    hipEvent_t end = nullptr;
+    if (j == L - 1 && z.s != cx.s && !ss.single) end = remat_done = ss.next();
+    return layer_forward(z, 0, sl[j], j, in, out, true, end);
   };
   Transients tb;
   for (int k = 0; k < 2; ++k) {
@@ -800,8 +814,8 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
           gpipe_status st = remat_layer(cx, cur, 0, j);
           if (st != GPIPE_OK) return st;
         }
-      } else if (!ss.join3()) {  // this micro-batch's re-materialization is done
-        return GPIPE_ERR_DEVICE;
+      } else if (remat_done ? !ss.join(remat_done) : !ss.join3()) {
+        return GPIPE_ERR_DEVICE;  // (this micro-batch's re-materialization is done)
       }
       ym = cx.at(p.yre);
     } else if (remat) {
@@ -812,6 +826,10 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
     }
     if (!tb.a0.next(&ss)) return GPIPE_ERR_DEVICE;
     void* a0 = cx.at(tb.a0.off[tb.a0.cur]);  // the loss gradient's act copy
+    // (the loss kernel records loss_done in its dispatch: the next micro-batch's
+    // first layer, re-materialized on the third stream, waits for it)
+    hipEvent_t loss_done = nullptr;
+    if (piped && m + 1 < M && !ss.single) next_done_event() = loss_done = ss.next();
     if (io.target) {
       int nblk = 0;
       GP_RUN(cx, GPIPE_ROLE_MSE, mse_fwd_bwd(cx.bf16, ym, cx.act(io.target, m * mb),
@@ -822,11 +840,17 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
       GP_CHECK(grad_in(cx.bf16, cx.act(io.dy, m * mb), static_cast<float*>(cx.at(p.r0)), a0,
                        int64_t(mb), cx.s));
     }
+    if (loss_done && next_done_event() == loss_done) {
+      next_done_event() = nullptr;
+      GP_CHECK(hipEventRecord(loss_done, cx.s));
+    }
     if (piped && m + 1 < M) {
       // the spare slot (micro-batch m-1's layer 0, whose backward and weight
       // gradients are enqueued before this point) takes micro-batch m+1's
-      // layer 0
-      if (!ss.fork3()) return GPIPE_ERR_DEVICE;
+      // layer 0 (the last work on the second stream is micro-batch m-1's
+      // layer-0 QKV weight gradient, whose event tb.dqkv holds; none yet for
+      // micro-batch 0)
+      if (!ss.fork3_after(loss_done, tb.dqkv.read[tb.dqkv.cur])) return GPIPE_ERR_DEVICE;
       nxt[0] = spare;
       gpipe_status st = remat_layer(cr, nxt, m + 1, 0);
       if (st != GPIPE_OK) return st;

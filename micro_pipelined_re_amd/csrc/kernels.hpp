@@ -157,6 +157,16 @@ int colsum_chunks(int rows);
 // acc (optional) receives the same sum the same way under acc_beta.
 hipError_t sum_partials(const float* part, int nparts, int64_t stride, int cols, float* out,
                         int beta, hipStream_t s, float* acc = nullptr, int acc_beta = 0);
+// Several such sums (beta 0, no acc) in one launch, each bitwise what
+// sum_partials computes; jobs of fewer than 32 columns are launched one by one.
+struct SumJob {
+  const float* part;
+  float* out;
+  int64_t stride;
+  int nparts, cols;
+};
+constexpr int kSumJobsMax = 64;  // per launch (the jobs travel in the kernel arguments)
+hipError_t sum_partials_batch(const SumJob* jobs, int njobs, hipStream_t s);
 
 // RMSProp over n parameters; writes the bf16 copy when w_lowp is non-null.
 hipError_t rmsprop(float* w, const float* g, float* ms, void* w_lowp, int64_t n, float lr,

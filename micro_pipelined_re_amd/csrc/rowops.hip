@@ -567,10 +567,10 @@ hipError_t mse_fwd_bwd(bool bf16, const void* y, const void* t, float* dy_f32, v
   if (count == 0) return hipSuccess;
   const float k = 2.0f * inv_denom;
   if (bf16)
-    hipLaunchKernelGGL(mse_kernel<bf16_t>, dim3(*nblk), dim3(256), 0, s, static_cast<const bf16_t*>(y),
+    launch_k(mse_kernel<bf16_t>, dim3(*nblk), dim3(256), 0, s, static_cast<const bf16_t*>(y),
                        static_cast<const bf16_t*>(t), dy_f32, static_cast<bf16_t*>(dy_act), part, count / 8, inv_denom, k);
   else
-    hipLaunchKernelGGL(mse_kernel<float>, dim3(*nblk), dim3(256), 0, s, static_cast<const float*>(y),
+    launch_k(mse_kernel<float>, dim3(*nblk), dim3(256), 0, s, static_cast<const float*>(y),
                        static_cast<const float*>(t), dy_f32, static_cast<float*>(dy_act), part, count / 8, inv_denom, k);
   return hipGetLastError();
 }
@@ -626,11 +626,9 @@ hipError_t colsum_partial(int xtype, const void* x, int64_t ld, int rows, int co
 // threads per column each summing every (256/CW)-th part, then a fixed-order
 // combination in LDS.
 template <int CW>
-__global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restrict__ part, int nparts,
-                                                           int64_t stride, int cols,
-                                                           float* __restrict__ out, int beta,
-                                                           float* __restrict__ acc,
-                                                           int acc_beta) {
+__device__ __forceinline__ void sum_partials_block(const float* __restrict__ part, int nparts,
+                                                   int64_t stride, int cols, float* __restrict__ out,
+                                                   int beta, float* __restrict__ acc, int acc_beta) {
   constexpr int G = 256 / CW;
   __shared__ float red[256];
   const int cl = threadIdx.x % CW, pg = threadIdx.x / CW;
@@ -651,6 +649,51 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restri
     out[c] = beta ? out[c] + red[cl] : red[cl];
     if (acc) acc[c] = acc_beta ? acc[c] + red[cl] : red[cl];
   }
+}
+
+template <int CW>
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restrict__ part, int nparts,
+                                                           int64_t stride, int cols,
+                                                           float* __restrict__ out, int beta,
+                                                           float* __restrict__ acc,
+                                                           int acc_beta) {
+  sum_partials_block<CW>(part, nparts, stride, cols, out, beta, acc, acc_beta);
+}
+
+struct SumJobs {
+  SumJob j[kSumJobsMax];
+};
+// job blockIdx.y, its columns along x (blocks past a job's columns store nothing)
+__global__ __launch_bounds__(256) void sum_partials_batch_kernel(SumJobs jobs) {
+  const SumJob& jb = jobs.j[blockIdx.y];
+  sum_partials_block<32>(jb.part, jb.nparts, jb.stride, jb.cols, jb.out, 0, nullptr, 0);
+}
+
+hipError_t sum_partials_batch(const SumJob* jobs, int njobs, hipStream_t s) {
+  SumJobs b;
+  int n = 0, xmax = 0;
+  auto flush = [&]() -> hipError_t {
+    if (!n) return hipSuccess;
+    hipLaunchKernelGGL(sum_partials_batch_kernel, dim3(xmax, n), dim3(256), 0, s, b);
+    n = xmax = 0;
+    return hipGetLastError();
+  };
+  for (int i = 0; i < njobs; ++i) {
+    const SumJob& jb = jobs[i];
+    if (jb.cols == 0) continue;
+    if (jb.cols < 32) {
+      const hipError_t e = sum_partials(jb.part, jb.nparts, jb.stride, jb.cols, jb.out, 0, s);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    b.j[n++] = jb;
+    xmax = std::max(xmax, (jb.cols + 31) / 32);
+    if (n == kSumJobsMax) {
+      const hipError_t e = flush();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return flush();
 }
 
 hipError_t sum_partials(const float* part, int nparts, int64_t stride, int cols, float* out,
