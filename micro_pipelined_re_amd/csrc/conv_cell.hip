@@ -329,8 +329,8 @@ gpipe_status cell_forward(const CCtx& x, int set, const void* xin, void* yout, f
 // the gradient w.r.t. the block output (f32); on exit the gradient w.r.t.
 // its input (r0, and dx_out when given).  With streams (ss) the two weight
 // gradients run on the second stream, handed over together after BN1's
-// backward (an event recorded on the caller's stream delays its next launch
-// by several microseconds): W2's reads the copy of dz that BN2's backward
+// backward (one hand-off event, recorded in the dispatch of that backward's
+// last kernel): W2's reads the copy of dz that BN2's backward
 // wrote, W1's the copy BN1's wrote, and each BatchNorm backward writes the
 // other copy than the last one, waiting only for that copy's readers.
 gpipe_status block_backward(const CCtx& x, Streams* ss, Transient* tdz, int set, int slot, int l,

@@ -548,9 +548,10 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, Transients& tb, int set, 
   // over the bf16 copy of the output gradient it reads -- else summed here)
   // The weight gradients are handed to the second stream in two batches per
   // layer, each after the input-gradient kernel that produces the last of
-  // their operands: an event recorded on the caller's stream delays its next
-  // launch by ~7 us (measured in the kernel trace), and the two batches keep
-  // the weight gradients in the same order on the second stream.
+  // their operands, whose dispatch records the hand-off event (an event
+  // recorded as a packet of its own delays the caller's next launch by a few
+  // microseconds); the two batches keep the weight gradients in the same
+  // order on the second stream.
   bool fused = false;
   if (!tb.du.next(&ss)) return GPIPE_ERR_DEVICE;
   du = x.at(tb.du.off[tb.du.cur]);
