@@ -94,7 +94,10 @@ constexpr int kCUs = 256;
 // 8192 FFN2 weight gradient with 256 x 128 tiles for the 2048 x 2048
 // out-projection one (128 instead of 256 tiles of 128 x 128) ran 143.8-144.1
 // against 144.9-145.0, and 147.8-147.9 against 149.6-149.7 on a slower box
-// (three A/B rounds each); either change alone gained 0.3 ms or less.  The step runs these products beside other
+// (three A/B rounds each); either change alone gained 0.3 ms or less.  The
+// backward's long input gradients (K >= 4096) split in two over k ran the
+// step 0.3 ms slower, in four 6 ms slower: the step is bound by the CUs'
+// work, not by the critical stream's latency.  The step runs these products beside other
 // streams' work (the forward lanes, the weight gradients, the next
 // re-materialization), which fills the CUs a small grid leaves idle, so what
 // pays alone does not in the step: the 1024 x 2048 x 8192 down-projection
