@@ -587,8 +587,10 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        gpipe.gpipe_cell_step(cell.handle, x, t, y, dx, n, m, remat, ws, ws_bytes, stream, cell.loss)
-        gpipe.gpipe_apply_update(cell.handle, cfg.lr, cfg.decay, cfg.eps, stream)
+        # the step and its update in one call: each layer's update starts as
+        # soon as that layer's gradients are complete
+        gpipe.gpipe_cell_step_update(cell.handle, x, t, y, dx, n, m, remat, ws, ws_bytes, stream,
+                                     cell.loss, cfg.lr, cfg.decay, cfg.eps)
 
     # warmup; the last warmup step times every launch of every role (all streams)
     all_roles = (1 << len(gpipe.ROLES)) - 1

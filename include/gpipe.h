@@ -310,6 +310,22 @@ gpipe_status gpipe_cell_step_noalloc(gpipe_cell *cell, const void *x, const void
  * not finite. */
 gpipe_status gpipe_apply_update(gpipe_cell *cell, float lr, float decay, float eps, void *stream);
 
+/* gpipe_cell_step followed by gpipe_apply_update(lr, decay, eps): the same
+ * work and the same results, bit for bit, in one call.  The update stays the
+ * pages' single synchronous one -- every parameter moves once, after the
+ * gradients of all M micro-batches are summed -- but on a Transformer cell
+ * each layer's update is enqueued as soon as that layer's gradients are
+ * complete (after the last micro-batch's backward of the layer and its
+ * weight gradients), on the cell's second stream, beside the backward of the
+ * layers below it; the call's work on `stream` still ends after every
+ * update.  A conv cell runs the two calls one after the other.
+ * Errors: those of gpipe_cell_step and of gpipe_apply_update (checked before
+ * any work is enqueued). */
+gpipe_status gpipe_cell_step_update(gpipe_cell *cell, const void *x, const void *target, void *y,
+                                    void *dx, int N, int M, int remat, void *workspace,
+                                    size_t workspace_bytes, void *stream, float *loss_dev,
+                                    float lr, float decay, float eps);
+
 /* Stability options for deep stacks ("training stability challenges of deep
  * models": sharp predictions and exploding gradients, fixed by scaling the
  * feed-forward initialisation down with the depth and by clipping the

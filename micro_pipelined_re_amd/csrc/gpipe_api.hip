@@ -655,12 +655,13 @@ gpipe_status layer_backward(const Ctx& x, Streams& ss, Transients& tb, int set, 
 // After the backward phase: reduce each layer's in-place partial sums (LN
 // gains and shifts -- adjacent in the parameter layout, so one pass over 2D
 // columns -- and the biases the weight-gradient kernels summed) into G.
-gpipe_status reduce_gparts(const Ctx& x) {
+gpipe_status reduce_gparts(const Ctx& x, int l_begin = 0, int l_end = -1) {
   const Plan& p = *x.p;
   const int grad_of[GPS_N] = {GPIPE_LN1_G, GPIPE_LN2_G, GPIPE_B_QKV, GPIPE_B_O, GPIPE_B_1, GPIPE_B_2};
+  if (l_end < 0) l_end = x.c->L;
   // (all of them in one launch: each is its own row of the grid)
   std::vector<SumJob> jobs;
-  for (int l = 0; l < x.c->L; ++l)
+  for (int l = l_begin; l < l_end; ++l)
     for (int k = 0; k < GPS_N; ++k) {
       if (!p.gp_parts[k]) continue;
       const int cols = p.gp_cols[k];
@@ -715,7 +716,18 @@ struct StepIO {
   size_t ws_bytes = 0;
   hipStream_t s = nullptr;
   bool single = false;
+  // the RMSProp update follows the step (gpipe_cell_step_update)
+  bool update = false;
+  float lr = 0.f, decay = 0.f, eps = 0.f;
 };
+
+// RMSProp over layer l's parameters (contiguous in master, grad, ms and the
+// bf16 copy), as gpipe_apply_update does over all of them.
+hipError_t rmsprop_layer(const gpipe_cell* c, int l, float lr, float decay, float eps, hipStream_t s) {
+  const size_t off = size_t(l) * c->per_layer;
+  void* wl = c->prec == GPIPE_BF16 ? static_cast<void*>(static_cast<uint16_t*>(c->w_lowp) + off) : nullptr;
+  return rmsprop(c->master + off, c->grad + off, c->ms + off, wl, int64_t(c->per_layer), lr, decay, eps, s);
+}
 
 gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
   Plan p;
@@ -775,6 +787,9 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
   // re-materialized output.  Micro-batch 0 re-materializes on the caller's
   // stream before its backward.
   const bool piped = lanes;
+  // layer-wise update (gpipe_cell_step_update), where every layer's parameter
+  // range starts 16-byte aligned (RMSProp takes four parameters per thread)
+  const bool upd = io.update && c->per_layer % 4 == 0;
   if (piped && !p.spare) return GPIPE_ERR_STATE;
   std::vector<int> cur(L), nxt(L);  // layer -> slot, this micro-batch and the next
   for (int l = 0; l < L; ++l) cur[l] = l;
@@ -864,10 +879,26 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
                                 : cx.at(saved_at(p, set, l, GPIPE_SAVED_X));
       void* dxo = (l == 0 && io.dx) ? cx.act(io.dx, m * mb) : nullptr;
       const bool refill = piped && m + 1 < M && l >= 1;
+      // (layer-wise update: after the last micro-batch's backward of layer l
+      // nothing reads its parameters or writes its gradients but the weight
+      // gradients already enqueued on the second stream)
+      const bool upd_l = upd && m == M - 1;
       hipEvent_t s1_done = nullptr;
       gpipe_status st = layer_backward(cx, ss, tb, set, piped ? cur[l] : l, l, xin, m > 0 ? 1 : 0, dxo,
-                                       refill ? &s1_done : nullptr);
+                                       refill || upd_l ? &s1_done : nullptr);
       if (st != GPIPE_OK) return st;
+      if (upd_l) {
+        // on the third stream (idle in the last micro-batch: nothing is left to
+        // re-materialize), after this layer's backward on the caller's stream
+        // (s1_done) and its weight gradients on the second (the event after the
+        // last of them, the QKV one)
+        if (!ss.fork3_after(s1_done, tb.dqkv.read[tb.dqkv.cur])) return GPIPE_ERR_DEVICE;
+        Ctx w = cx;
+        w.s = ss.s3;
+        st = reduce_gparts(w, l, l + 1);
+        if (st != GPIPE_OK) return st;
+        GP_RUN(w, GPIPE_ROLE_RMSPROP, rmsprop_layer(c, l, io.lr, io.decay, io.eps, w.s));
+      }
       if (refill) {
         // layer l's slot is free once its backward (s1) and weight gradients (s2)
         // are done
@@ -885,11 +916,16 @@ gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {
       cur.swap(nxt);
     }
   }
-  // the weight gradients (and their bias partial sums) are complete
-  if (!ss.join_all()) return GPIPE_ERR_DEVICE;
-  {
+  // the weight gradients (and their bias partial sums; with the layer-wise
+  // update, on the third stream, the updates) are complete
+  if (!ss.join_all() || (upd && !ss.join3())) return GPIPE_ERR_DEVICE;
+  if (!upd) {
     gpipe_status st = reduce_gparts(cx);
     if (st != GPIPE_OK) return st;
+    if (io.update)
+      GP_RUN(cx, GPIPE_ROLE_RMSPROP,
+             rmsprop(c->master, c->grad, c->ms, c->prec == GPIPE_BF16 ? c->w_lowp : nullptr,
+                     int64_t(c->n_params), io.lr, io.decay, io.eps, cx.s));
   }
   if (io.target)
     GP_RUN(cx, GPIPE_ROLE_LOSS_REDUCE, sum_partials(msepart, M * p.mse_nblk, 1, 1, io.loss_dev, 0, cx.s));
@@ -1076,6 +1112,33 @@ gpipe_status gpipe_cell_step(gpipe_cell* c, const void* x, const void* target, v
   return transformer_run(c, io);
 }
 
+static bool update_args_ok(float lr, float decay, float eps) {
+  return decay >= 0.f && decay < 1.f && lr >= 0.f && eps >= 0.f && isfinite(lr) && isfinite(eps);
+}
+
+gpipe_status gpipe_cell_step_update(gpipe_cell* c, const void* x, const void* target, void* y,
+                                    void* dx, int N, int M, int remat, void* workspace,
+                                    size_t ws_bytes, void* stream, float* loss_dev, float lr,
+                                    float decay, float eps) {
+  if (!c) return GPIPE_ERR_INVALID;
+  if (!c->bound) return GPIPE_ERR_STATE;
+  if (!update_args_ok(lr, decay, eps)) return GPIPE_ERR_INVALID;
+  if (c->kind == CELL_CONV) {
+    const gpipe_status st = gpipe_cell_step(c, x, target, y, dx, N, M, remat, workspace, ws_bytes,
+                                            stream, loss_dev);
+    return st != GPIPE_OK ? st : gpipe_apply_update(c, lr, decay, eps, stream);
+  }
+  StepIO io;
+  io.phases = PH_FWD | PH_BWD;
+  io.x = x; io.target = target; io.y = y; io.dx = dx; io.loss_dev = loss_dev;
+  io.N = N; io.M = M; io.remat = remat;
+  io.ws = static_cast<char*>(workspace); io.ws_bytes = ws_bytes;
+  io.s = static_cast<hipStream_t>(stream);
+  io.update = true;
+  io.lr = lr; io.decay = decay; io.eps = eps;
+  return transformer_run(c, io);
+}
+
 gpipe_status gpipe_cell_forward(gpipe_cell* c, const void* x, void* y, int N, int M, int remat,
                                 void* workspace, size_t ws_bytes, void* stream) {
   if (!c) return GPIPE_ERR_INVALID;
@@ -1158,9 +1221,7 @@ gpipe_status gpipe_cell_scale_ffn_init(gpipe_cell* c, int total_layers, void* st
 gpipe_status gpipe_apply_update(gpipe_cell* c, float lr, float decay, float eps, void* stream) {
   if (!c) return GPIPE_ERR_INVALID;
   if (!c->bound) return GPIPE_ERR_STATE;
-  if (!(decay >= 0.f && decay < 1.f) || !(lr >= 0.f) || !(eps >= 0.f) || !isfinite(lr) ||
-      !isfinite(eps))
-    return GPIPE_ERR_INVALID;
+  if (!update_args_ok(lr, decay, eps)) return GPIPE_ERR_INVALID;
   Ctx cx{c, c->prof_mask ? c : nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream),
          c->prec == GPIPE_BF16, 0};
   GP_RUN(cx, GPIPE_ROLE_RMSPROP,

@@ -29,6 +29,7 @@ EXPORTS = ("gpipe_cell_create", "gpipe_cell_destroy", "gpipe_cell_param_count",
            "gpipe_cell_gemm_plan",
            "gpipe_conv_cell_create", "gpipe_cell_bind_running", "gpipe_cell_forward_plan",
            "gpipe_cell_forward", "gpipe_cell_backward", "gpipe_cell_step_noalloc",
+           "gpipe_cell_step_update",
            "gpipe_cell_set_logit_clip", "gpipe_cell_scale_ffn_init")
 
 ROLES = ("ln1_fwd", "qkv_fwd", "scores_fwd", "softmax_fwd", "pv_fwd", "out_fwd", "ln2_fwd",
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
             "gpipe_cell_set_logit_clip": [_vp, ctypes.c_float],
             "gpipe_cell_scale_ffn_init": [_vp, _i, _vp],
             "gpipe_cell_step_noalloc": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp],
+            "gpipe_cell_step_update": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp, _vp,
+                                       ctypes.c_float, ctypes.c_float, ctypes.c_float],
             "gpipe_cell_backward": [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp],
             "gpipe_apply_update": [_vp, ctypes.c_float, ctypes.c_float, ctypes.c_float, _vp],
             "gpipe_partition": [ctypes.POINTER(ctypes.c_double), _i, _i, ctypes.POINTER(_i),
@@ -206,6 +209,14 @@ def gpipe_cell_step(cell, x, target, y, dx, N, M, remat, workspace, ws_bytes, st
            lib().gpipe_cell_step(cell, _ptr(x), _ptr(target), _ptr(y), _ptr(dx), N, M,
                                  int(bool(remat)), _ptr(workspace), ws_bytes, _stream(stream),
                                  _ptr(loss)))
+
+
+def gpipe_cell_step_update(cell, x, target, y, dx, N, M, remat, workspace, ws_bytes, stream, loss,
+                           lr, decay, eps) -> None:
+    _check("gpipe_cell_step_update",
+           lib().gpipe_cell_step_update(cell, _ptr(x), _ptr(target), _ptr(y), _ptr(dx), N, M,
+                                        int(bool(remat)), _ptr(workspace), ws_bytes,
+                                        _stream(stream), _ptr(loss), lr, decay, eps))
 
 
 GPIPE_SCRATCH_BYTES = 64 << 20
@@ -389,6 +400,19 @@ class Cell:
         ws, nb = self.workspace(N, M, remat)
         gpipe_cell_step(self.handle, x, t, y, dx if want_dx else None, N, M, remat, ws, nb,
                         stream, self.loss)
+        return y, (dx if want_dx else None)
+
+    def step_update(self, x, t, N, M, lr, decay, eps, remat=True, want_dx=True, y=None, dx=None,
+                    stream=None):
+        """step() and update() in one call (each layer updated once its gradients are complete)."""
+        torch = self.torch
+        if y is None:
+            y = torch.empty_like(x)
+        if want_dx and dx is None:
+            dx = torch.empty_like(x)
+        ws, nb = self.workspace(N, M, remat)
+        gpipe_cell_step_update(self.handle, x, t, y, dx if want_dx else None, N, M, remat, ws, nb,
+                               stream, self.loss, lr, decay, eps)
         return y, (dx if want_dx else None)
 
     def forward(self, x, N, M, remat=True, y=None, stream=None):

@@ -434,3 +434,36 @@ def test_profiled_step_bitwise_and_sampled_launch_counts():
     with pytest.raises(RuntimeError):
         gpipe.gpipe_cell_profile_sampled(cell.handle, all_roles, 0)
     gpipe.gpipe_cell_profile(cell.handle, 0)
+
+
+@pytest.mark.parametrize("cfg", [configs.TINY,
+                                 configs.SMALL.with_(name="small_3l", layers=3, batch=8, micro=4)],
+                         ids=["tiny_fp32", "small_3l_bf16"])
+def test_step_update_equals_step_then_update(cfg):
+    """gpipe_cell_step_update (each layer's RMSProp update enqueued once its gradients are
+    complete, beside the backward of the layers below it) leaves bitwise what
+    gpipe_cell_step followed by gpipe_apply_update leaves: outputs, loss, gradients,
+    weights, mean squares and the bf16 copy -- over two calls in a row (the second reads
+    the first's update), with re-materialization (pipelined for the bf16 cell) and
+    without."""
+    import torch
+    params = inputs.cell_params(cfg)
+    x, t = inputs.cell_data(cfg, batch=cfg.batch)
+    N, M = cfg.batch, cfg.micro
+    for remat in (True, False):
+        a, b = make_cell(cfg, params), make_cell(cfg, params)
+        xd, td = a.to_device(x), a.to_device(t)
+        say(f"[gpu] step_update {cfg.name} N={N} M={M} remat={remat}")
+        for k in range(2):
+            ya, dxa = a.step(xd, td, N, M, remat=remat)
+            a.update(cfg.lr, cfg.decay, cfg.eps)
+            yb, dxb = b.step_update(xd, td, N, M, cfg.lr, cfg.decay, cfg.eps, remat=remat)
+            torch.cuda.synchronize()
+            assert torch.equal(ya, yb) and torch.equal(dxa, dxb), (remat, k)
+            assert a.loss.item() == b.loss.item(), (remat, k)
+            for name in ("grad", "master", "ms"):
+                assert torch.equal(getattr(a, name), getattr(b, name)), (remat, k, name)
+            if a.bf16:
+                assert torch.equal(a.w_lowp, b.w_lowp), (remat, k)
+    with pytest.raises(RuntimeError):
+        b.step_update(xd, td, N, M, cfg.lr, 1.5, cfg.eps)
