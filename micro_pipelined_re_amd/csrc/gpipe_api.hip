@@ -722,11 +722,16 @@ struct StepIO {
 };
 
 // RMSProp over layer l's parameters (contiguous in master, grad, ms and the
-// bf16 copy), as gpipe_apply_update does over all of them.
+// bf16 copy), as gpipe_apply_update does over all of them.  It runs beside
+// the backward of the layers below, so its grid is capped at one workgroup
+// per CU (each looping over its share): 140.0-140.1 ms/step against
+// 140.2-140.3 uncapped, 140.4-140.7 at 128 workgroups and ~143 at 64 (three
+// A/B rounds on one box).
 hipError_t rmsprop_layer(const gpipe_cell* c, int l, float lr, float decay, float eps, hipStream_t s) {
   const size_t off = size_t(l) * c->per_layer;
   void* wl = c->prec == GPIPE_BF16 ? static_cast<void*>(static_cast<uint16_t*>(c->w_lowp) + off) : nullptr;
-  return rmsprop(c->master + off, c->grad + off, c->ms + off, wl, int64_t(c->per_layer), lr, decay, eps, s);
+  return rmsprop(c->master + off, c->grad + off, c->ms + off, wl, int64_t(c->per_layer), lr, decay, eps, s,
+                 256);
 }
 
 gpipe_status transformer_run(gpipe_cell* c, const StepIO& io) {

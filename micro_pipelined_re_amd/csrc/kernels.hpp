@@ -170,7 +170,7 @@ hipError_t sum_partials_batch(const SumJob* jobs, int njobs, hipStream_t s);
 
 // RMSProp over n parameters; writes the bf16 copy when w_lowp is non-null.
 hipError_t rmsprop(float* w, const float* g, float* ms, void* w_lowp, int64_t n, float lr,
-                   float decay, float eps, hipStream_t s);
+                   float decay, float eps, hipStream_t s, int max_blocks = 0);
 
 // ---------------------------------------------------------------- conv cell
 // Storage of a conv-cell activation: float32 [P][C], bf16 [P][C], or a split

@@ -748,7 +748,7 @@ __global__ __launch_bounds__(256) void rmsprop_kernel(float* __restrict__ w, con
 }
 
 hipError_t rmsprop(float* w, const float* g, float* ms, void* w_lowp, int64_t n, float lr,
-                   float decay, float eps, hipStream_t s) {
+                   float decay, float eps, hipStream_t s, int max_blocks) {
   if (n == 0) return hipSuccess;
   // one thread per group of four parameters: measured on 403 M parameters,
   // 1.58 ms (5.6 TB/s) against 1.91 ms with the grid capped at 8192 blocks
@@ -756,7 +756,10 @@ hipError_t rmsprop(float* w, const float* g, float* ms, void* w_lowp, int64_t n,
   // non-temporal accesses did not help
   const int64_t n4 = (n + 3) / 4;
   const int64_t want = (n4 + 255) / 256;
-  const int blocks = int(want < (int64_t(1) << 30) ? want : (int64_t(1) << 30));
+  // (max_blocks > 0: at most that many blocks, each looping over the groups;
+  // the same per-element arithmetic)
+  const int64_t cap = max_blocks > 0 ? max_blocks : (int64_t(1) << 30);
+  const int blocks = int(want < cap ? want : cap);
   hipLaunchKernelGGL(rmsprop_kernel, dim3(blocks), dim3(256), 0, s, w, g, ms,
                      static_cast<bf16_t*>(w_lowp), n, lr, decay, eps);
   return hipGetLastError();
