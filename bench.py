@@ -616,13 +616,17 @@ def main():
         # a split-K GEMM role is two kernels: the split products and their ordered sum
         return gpipe.gpipe_cell_gemm_plan(cell.handle, n, m, gpipe.ROLES.index(name))[2] <= 1
 
-    # the dominant kernel: the role with the most kernel time in a whole step,
-    # over every stream (forward lanes, backward, re-materializations)
+    # the dominant kernel: the role with the most algorithmic work in a step,
+    # among equals the first in role order (ffn1_fwd and ffn2_fwd carry the
+    # same flops).  Kernel time is no stable rank here: the three streams share
+    # the chip, so a launch of 64 tiles on the caller's stream stretches with
+    # whatever runs beside it, and the order of the top roles by time changed
+    # from run to run.
     ranked = sorted((k for k in prof if step_work(k) and single_kernel(k)),
-                    key=lambda k: -prof[k][0])
+                    key=lambda k: (-step_work(k), gpipe.ROLES.index(k)))
     dominant = ranked[0]
     dom_idx = gpipe.ROLES.index(dominant)
-    log("[bench] kernel time per step (warmup step, all streams): " +
+    log("[bench] roles by work per step; their kernel time (warmup step, all streams): " +
         ", ".join(f"{k} {prof[k][0]:.1f} ms" for k in ranked[:6]))
 
     # timed region: K steps; a regular sample of the dominant role's launches
