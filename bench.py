@@ -189,6 +189,17 @@ def role_passes(cfg, m, name, conv):
     return None
 
 
+def rank_roles(names, step_work):
+    """`names` in roofline order; the first is the dominant kernel.  The rank is
+    the role's algorithmic work per step, among equals the role order
+    (ffn1_fwd and ffn2_fwd carry the same flops).  Kernel time is no stable
+    rank: the step's three streams share the chip, so a launch of 64 tiles on
+    the caller's stream stretches with whatever runs beside it, and the order
+    of the top roles by time changed from run to run."""
+    from micro_pipelined_re_amd import gpipe
+    return sorted(names, key=lambda k: (-step_work(k), gpipe.ROLES.index(k)))
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -555,7 +566,8 @@ def main():
         return run_memory(args)
     if args.gpus != 1:
         print(f"bench.py runs one cell on one GPU; --gpus {args.gpus} is not supported "
-              f"(the multi-GPU pipeline schedule is not part of this build)", file=sys.stderr)
+              f"(the library steps one pipeline cell per GPU; scheduling cells across GPUs "
+              f"is outside it)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -616,14 +628,7 @@ def main():
         # a split-K GEMM role is two kernels: the split products and their ordered sum
         return gpipe.gpipe_cell_gemm_plan(cell.handle, n, m, gpipe.ROLES.index(name))[2] <= 1
 
-    # the dominant kernel: the role with the most algorithmic work in a step,
-    # among equals the first in role order (ffn1_fwd and ffn2_fwd carry the
-    # same flops).  Kernel time is no stable rank here: the three streams share
-    # the chip, so a launch of 64 tiles on the caller's stream stretches with
-    # whatever runs beside it, and the order of the top roles by time changed
-    # from run to run.
-    ranked = sorted((k for k in prof if step_work(k) and single_kernel(k)),
-                    key=lambda k: (-step_work(k), gpipe.ROLES.index(k)))
+    ranked = rank_roles([k for k in prof if step_work(k) and single_kernel(k)], step_work)
     dominant = ranked[0]
     dom_idx = gpipe.ROLES.index(dominant)
     log("[bench] roles by work per step; their kernel time (warmup step, all streams): " +
