@@ -126,8 +126,12 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int b
   }
   const int xcd = bid % 8, j = bid / 8;
   const int rm = tiles_m / best, rn = tiles_n / (8 / best);
-  *tm = (xcd / (8 / best)) * rm + j % rm;
-  *tn = (xcd % (8 / best)) * rn + j / rm;
+  // within the region, column-major over bands of at most 8 tile rows: the
+  // 32 workgroups an XCD runs at once cover 8 x 4 tiles rather than 16 x 2
+  const int gm = (rm > 8 && rm % 8 == 0) ? 8 : rm;
+  const int band = j / (gm * rn), r = j % (gm * rn);
+  *tm = (xcd / (8 / best)) * rm + band * gm + r % gm;
+  *tn = (xcd % (8 / best)) * rn + r / gm;
 }
 
 // Tile and k-split of a workgroup.  Workgroups go to the 8 XCDs round-robin
