@@ -126,12 +126,24 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int b
   }
   const int xcd = bid % 8, j = bid / 8;
   const int rm = tiles_m / best, rn = tiles_n / (8 / best);
-  // within the region, column-major over bands of at most 8 tile rows: the
-  // 32 workgroups an XCD runs at once cover 8 x 4 tiles rather than 16 x 2
-  const int gm = (rm > 8 && rm % 8 == 0) ? 8 : rm;
-  const int band = j / (gm * rn), r = j % (gm * rn);
-  *tm = (xcd / (8 / best)) * rm + band * gm + r % gm;
-  *tn = (xcd % (8 / best)) * rn + r / gm;
+  // Within the region, column-major over bands of gm tile rows (the last band
+  // may be shorter), so that the 32 workgroups an XCD runs at once share few
+  // operand panels: 8 x 4 tiles of 128 x 256, 4 x 8 of 256 x 128 (an A panel
+  // of BM rows against a B panel of BN columns, both K deep).
+  const int gm = min(bm > bn ? 4 : 8, rm);
+  const int full = rm / gm, jb = full * gm * rn;
+  int r, c;
+  if (j < jb) {
+    const int band = j / (gm * rn), q = j % (gm * rn);
+    r = band * gm + q % gm;
+    c = q / gm;
+  } else {
+    const int h = rm - full * gm, q = j - jb;
+    r = full * gm + q % h;
+    c = q / h;
+  }
+  *tm = (xcd / (8 / best)) * rm + r;
+  *tn = (xcd % (8 / best)) * rn + c;
 }
 
 // Tile and k-split of a workgroup.  Workgroups go to the 8 XCDs round-robin
